@@ -1,0 +1,201 @@
+/*
+ * msk.h -- C ABI of libmsk.so: one decode/verify step of a mixture-of-experts
+ * decoder layer (or a short stack of them) on an AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one the pages on "Optimizing Muse Spark Open on TPU v7
+ * with SGLang-TorchTPU" describe: every decoder layer is a mixture-of-experts
+ * layer that routes each token to 8 of 256 experts and mixes sliding-window
+ * (2,048 tokens) with full-context attention (ainewsbites page, section "One
+ * program replaces many kernel boundaries"); QK-norm lets softmax run without
+ * a running maximum, so context chunks reduce independently (brifing.si page,
+ * section "Removing Attention Bottlenecks"); the KV cache is fp8 (aitop.news
+ * page, opening paragraphs); expert weights are NVFP4 with one scale per 16
+ * values (brifing.si page, "Expert Weight Quantization"); a verify step checks
+ * the draft tokens of each request in one pass (brifing.si page, "Speculative
+ * Decoding Integration").  The serving stack keeps embedding, draft model, LM
+ * head and sampling (ainewsbites page, "One program replaces many kernel
+ * boundaries"), so the step maps hidden states in to hidden states out.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *   allocates no device memory and keeps no state between calls; scratch space
+ *   comes from the caller's workspace (see msk_workspace_size).
+ * - Row-major, innermost dimension last.  T = n_req * tokens_per_req tokens,
+ *   request-major: token t of request b is row b * tokens_per_req + t and sits
+ *   at cache position p = kv_len[b] + t.
+ * - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
+ *   return without waiting.  Nothing is synchronised implicitly.
+ * - Argument errors return before anything is enqueued; msk_last_error()
+ *   then describes them.  A failed launch returns MSK_ERR_DEVICE.
+ * - A workspace must not be used by two calls that may run at the same time.
+ *   It must be zero-filled before its first use; every call leaves the
+ *   synchronisation words in it zero again when it completes normally.
+ * - The KV cache is written at positions [kv_len[b], kv_len[b] + tokens_per_req)
+ *   only; lengths are never changed by the library (accepting or rejecting
+ *   drafts is the caller's business).
+ */
+#ifndef MSK_H
+#define MSK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSK_ABI_VERSION 1
+#define MSK_MAX_REQ 64       /* requests per call                          */
+#define MSK_MAX_TOKENS 64    /* T = n_req * tokens_per_req per call         */
+#define MSK_MAX_STACK 4      /* layers per msk_layer_step call             */
+
+typedef enum {
+  MSK_OK = 0,
+  MSK_ERR_INVALID_ARG = 1, /* null pointer, inconsistent shape, bad length   */
+  MSK_ERR_UNSUPPORTED = 2, /* valid but outside what this library handles   */
+  MSK_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
+  MSK_ERR_DEVICE = 4,      /* a HIP call or launch failed                   */
+  MSK_ERR_TIMEOUT = 5      /* a device-side wait gave up (see msk_workspace_status) */
+} msk_status;
+
+typedef enum {
+  MSK_F32 = 0,   /* IEEE binary32                                              */
+  MSK_BF16 = 1,  /* bfloat16 bit patterns (uint16)                             */
+  MSK_E4M3 = 2,  /* OCP FP8 E4M3FN bytes, no scale (KV cache only)             */
+  MSK_NVFP4 = 3  /* e2m1 codes, 2 per byte (even element in the low nibble),
+                    one e4m3 scale per 16 consecutive elements along the
+                    reduction dimension, one fp32 scale per matrix (experts only) */
+} msk_dtype;
+
+/* Shape and numeric configuration of one layer. */
+typedef struct {
+  int32_t hidden;      /* H: hidden size; multiple of 256                       */
+  int32_t n_q_heads;   /* Hq: query heads; multiple of n_kv_heads                */
+  int32_t n_kv_heads;  /* Hkv: key/value heads; query head h uses kv head
+                          h / (Hq / Hkv) (contiguous groups)                      */
+  int32_t head_dim;    /* D: 32, 64 or 128                                       */
+  int32_t n_experts;   /* E: 1..256                                              */
+  int32_t top_k;       /* k: experts per token, 1..min(E, 16)                   */
+  int32_t ffn_dim;     /* F: expert FFN width; multiple of 32                    */
+  int32_t window;      /* 0 = full context; W > 0 = sliding window of the W
+                          positions ending at the token itself: [p-W+1, p]       */
+  float rms_eps;       /* eps of all RMSNorms: x / sqrt(mean(x^2) + eps) * g     */
+  float softmax_shift; /* c: fixed score bound; attention weights are
+                          exp(s - c) summed without a running maximum.  Any c
+                          with s - c < 88 for every score gives the same result
+                          up to rounding; sqrt(D)*max|g_q|*max|g_k| bounds the
+                          scores of QK-normalised keys                            */
+  int32_t dense_dtype;  /* MSK_F32 | MSK_BF16: wq, wk, wv, wo, w_router          */
+  int32_t expert_dtype; /* MSK_F32 | MSK_BF16 | MSK_NVFP4: w_gate, w_up, w_down  */
+  int32_t kv_dtype;     /* MSK_F32 | MSK_BF16 | MSK_E4M3                         */
+} msk_layer_cfg;
+
+/* Weights of one layer (device pointers, caller-owned, read only). */
+typedef struct {
+  const float *attn_norm;  /* [H]  gain of the attention RMSNorm                 */
+  const float *q_norm;     /* [D]  QK-norm gain for queries (shared by heads)    */
+  const float *k_norm;     /* [D]  QK-norm gain for keys                         */
+  const float *ffn_norm;   /* [H]  gain of the FFN RMSNorm                       */
+  const void *wq;          /* [Hq*D][H]  row h*D+d produces query head h, dim d  */
+  const void *wk;          /* [Hkv*D][H]                                         */
+  const void *wv;          /* [Hkv*D][H]                                         */
+  const void *wo;          /* [H][Hq*D]                                          */
+  const void *w_router;    /* [E][H]  logits = w_router . u, no bias             */
+  const void *w_gate;      /* [E][F][H]  (NVFP4: uint8 [E][F][H/2])              */
+  const void *w_up;        /* [E][F][H]  (NVFP4: uint8 [E][F][H/2])              */
+  const void *w_down;      /* [E][H][F]  (NVFP4: uint8 [E][H][F/2])              */
+  const uint8_t *s_gate;   /* NVFP4 only: e4m3 [E][F][H/16]                      */
+  const uint8_t *s_up;     /* NVFP4 only: e4m3 [E][F][H/16]                      */
+  const uint8_t *s_down;   /* NVFP4 only: e4m3 [E][H][F/16]                      */
+  const float *g_gate;     /* NVFP4 only: fp32 per-matrix scale [E]              */
+  const float *g_up;       /* NVFP4 only: [E]                                    */
+  const float *g_down;     /* NVFP4 only: [E]                                    */
+} msk_layer_weights;
+
+/* KV cache of one layer: k, v are [n_req][Hkv][cap][D] in kv_dtype.  Positions
+ * [0, kv_len[b]) hold request b's cached keys (already QK-normalised) and
+ * values; the step appends at [kv_len[b], kv_len[b] + tokens_per_req). */
+typedef struct {
+  void *k;
+  void *v;
+  int64_t cap;
+} msk_kv;
+
+/* Batch description.  kv_len_host is a HOST array [n_req]: positions cached
+ * per request before this step. */
+typedef struct {
+  int32_t n_req;           /* 1..MSK_MAX_REQ                                     */
+  int32_t tokens_per_req;  /* Tr: 1 for decode, the draft length for verify      */
+  const int32_t *kv_len_host;
+} msk_batch;
+
+/* ABI version of the loaded library (MSK_ABI_VERSION). */
+int32_t msk_abi_version(void);
+
+/* Text of the last error returned on this thread; valid until the next call. */
+const char *msk_last_error(void);
+
+/* Bytes of workspace the calls below need for these layers and this batch
+ * (the largest need over the entry points, so one workspace serves all of
+ * them).  Returns 0 and sets msk_last_error() on invalid arguments. */
+size_t msk_workspace_size(const msk_layer_cfg *cfg, int32_t n_layers,
+                          const msk_batch *batch);
+
+/* Synchronises `stream`, then reports whether a device-side wait in a call
+ * that used `ws` gave up (MSK_ERR_TIMEOUT; the flag is cleared and the
+ * workspace's synchronisation words reset) or MSK_OK.  MSK_ERR_DEVICE if the
+ * stream reports an error. */
+msk_status msk_workspace_status(void *ws, size_t ws_bytes, void *stream);
+
+/* Attention half of a layer (steps: attention RMSNorm, QKV projection,
+ * QK-norm, KV append, windowed no-max split-KV attention, output projection
+ * with residual).
+ *   x      [T][H] fp32 in
+ *   h      [T][H] fp32 out: x + wo . attn
+ *   attn_o [T][Hq*D] fp32 out, nullable: attention output before wo
+ *   win    [T][2] int32 out, nullable: visible cache positions [lo, hi] of each
+ *          token (hi = its own position)
+ * Writes the appended K/V into kv (in kv_dtype, round to nearest even; e4m3
+ * saturates to +-448).  x and h must not overlap. */
+msk_status msk_attn_step(const msk_layer_cfg *cfg, const msk_layer_weights *w,
+                         const msk_kv *kv, const msk_batch *batch, const float *x,
+                         float *h, float *attn_o, int32_t *win, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/* Router: u = RMSNorm(h) * ffn_norm; logits = w_router . u (fp32); per token the
+ * top_k experts by logit (descending; the lower index wins a tie) and their
+ * weights (softmax over the selected logits).
+ *   h [T][H] in; u [T][H] out; topk_idx [T][k] int32 out; topk_w [T][k] out;
+ *   logits [T][E] out, nullable. */
+msk_status msk_moe_route(const msk_layer_cfg *cfg, const msk_layer_weights *w,
+                         int32_t n_tokens, const float *h, float *u,
+                         int32_t *topk_idx, float *topk_w, float *logits,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* Experts: out[t] = h[t] + sum_j topk_w[t][j] * down_e(silu(gate_e u[t]) * up_e u[t])
+ * with e = topk_idx[t][j], summed in slot order j = 0..k-1.  Only the distinct
+ * selected experts are read, each once for all tokens routed to it.
+ *   u, h [T][H] in; topk_idx, topk_w [T][k] in; out [T][H] out (may equal h). */
+msk_status msk_expert_ffn(const msk_layer_cfg *cfg, const msk_layer_weights *w,
+                          int32_t n_tokens, const float *u, const int32_t *topk_idx,
+                          const float *topk_w, const float *h, float *out, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* A whole decode/verify step through n_layers (1..MSK_MAX_STACK) layers as one
+ * persistent kernel: layer l's output is layer l+1's input.  cfg, w and kv are
+ * arrays of n_layers entries (shapes must agree; window and dtypes may differ).
+ *   x         [T][H] fp32 in/out: the step's input, replaced by its output
+ *   layer_out [n_layers][T][H] out, nullable: each layer's output
+ *   topk_idx  [n_layers][T][k] out, nullable
+ *   win       [n_layers][T][2] out, nullable */
+msk_status msk_layer_step(const msk_layer_cfg *cfg, const msk_layer_weights *w,
+                          const msk_kv *kv, int32_t n_layers, const msk_batch *batch,
+                          float *x, float *layer_out, int32_t *topk_idx, int32_t *win,
+                          void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSK_H */

@@ -1,0 +1,145 @@
+"""Shared helpers of the parity tests: run the oracle on the same bytes the GPU
+path consumed, and compare with the stated tolerances.
+
+Tolerances (per checked tensor, against that tensor's oracle RMS):
+* all-fp32 layers: max|err| <= 1e-5 * RMS(reference);
+* layers with any bf16 / e4m3 / NVFP4 storage: max|err| <= 2e-2 * RMS(reference).
+Routing indices are compared exactly wherever the oracle's gap between the
+k-th and (k+1)-th logit exceeds a margin that fp32 rounding cannot cross.
+"""
+import numpy as np
+import torch
+
+import synth
+import verify_step_amd as msk
+from oracle import formats as fm
+from oracle import layer as ol
+
+FP32_TOL = 1e-5
+LOWP_TOL = 2e-2
+
+
+def tol_for(spec):
+    return FP32_TOL if (spec["dense_dtype"], spec["expert_dtype"], spec["kv_dtype"]) == \
+        ("f32", "f32", "f32") else LOWP_TOL
+
+
+def rel_err(gpu, ref, floor=None):
+    """max over elements of |gpu - ref| / RMS(ref), after subtracting an
+    element-wise allowance `floor` (clipped at zero)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), "GPU result has non-finite values"
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(gpu - ref)
+    if floor is not None:
+        err = np.maximum(err - floor, 0.0)
+    return float(np.max(err)) / max(rms, 1e-30)
+
+
+def assert_close(name, gpu, ref, tol, floor=None):
+    e = rel_err(gpu, ref, floor)
+    assert e <= tol, f"{name}: max|err|/RMS = {e:.3e} > {tol:.1e}"
+    return e
+
+
+def fp32_store_floor(out):
+    """Allowance for a difference of fp32 values: the stored fp32 output
+    carries up to half an ulp of its own magnitude (<= 2^-24 |out|), which
+    a delta out - h inherits in full; 2^-23 |out| covers it with margin."""
+    return np.abs(np.asarray(out, dtype=np.float64)) * 2.0 ** -23
+
+
+def fill_shift(p):
+    """Fixed softmax shift of every layer from its QK-norm gains."""
+    for spec, w in zip(p.specs, p.weights):
+        spec["softmax_shift"] = msk.softmax_shift(w["q_norm"], w["k_norm"], spec["head_dim"])
+
+
+def snapshot_kv(p):
+    """Host copies of the cache slots the step appends to (for restoring and
+    for checking the untouched slots)."""
+    snaps = []
+    for c in p.kv:
+        s = {}
+        for name in ("k", "v"):
+            s[name] = [c[name][b, :, L:L + p.tokens_per_req].clone() for b, L in enumerate(p.kv_len)]
+        snaps.append(s)
+    return snaps
+
+
+def restore_kv(p, snaps):
+    for c, s in zip(p.kv, snaps):
+        for name in ("k", "v"):
+            for b, L in enumerate(p.kv_len):
+                c[name][b, :, L:L + p.tokens_per_req].copy_(s[name][b])
+
+
+def oracle_inputs(p, layer):
+    return (p.specs[layer], synth.host_weights(p.weights[layer]), synth.host_kv(p.kv[layer]))
+
+
+def code_distance(a, b, dtype):
+    """|a - b| in units of the format's codes (sign-magnitude order)."""
+    a = np.asarray(a)
+    b = np.asarray(b)
+    if dtype == "f32":
+        raise ValueError
+    bits = 16 if dtype == "bf16" else 8
+    a = a.astype(np.int64)
+    b = b.astype(np.int64)
+    sign = 1 << (bits - 1)
+
+    def ordered(x):
+        return np.where(x & sign, -(x & (sign - 1)), x)
+
+    return np.abs(ordered(a) - ordered(b))
+
+
+def check_appended(p, layer, ref, tol):
+    """K/V written at [L_b, L_b + Tr) equal the oracle's cast values, up to one
+    code of the format where the fp32 and fp64 values straddle a rounding
+    boundary."""
+    spec = p.specs[layer]
+    kd = spec["kv_dtype"]
+    Tr = p.tokens_per_req
+    for name, bits_key in (("k", "k_new_bits"), ("v", "v_new_bits")):
+        cache = p.kv[layer][name]
+        for b, L in enumerate(p.kv_len):
+            got = synth.to_numpy(cache[b, :, L:L + Tr])                 # [Hkv][Tr][D]
+            want = np.asarray(ref[bits_key])[b * Tr:(b + 1) * Tr]      # [Tr][Hkv][D]
+            want = np.transpose(want, (1, 0, 2))
+            if kd == "f32":
+                np.testing.assert_allclose(got, want, rtol=2e-6, atol=2e-6 * np.abs(want).max())
+            else:
+                d = code_distance(got, want, kd)
+                assert d.max() <= 1, f"{name} append: {int((d > 0).sum())} codes differ, max {d.max()}"
+
+
+def routing_margin(logits_ref, k, scale=1e-4):
+    """Per token: gap between the k-th and (k+1)-th largest oracle logits."""
+    s = -np.sort(-np.asarray(logits_ref), axis=1)
+    if s.shape[1] == k:
+        return np.full(s.shape[0], np.inf)
+    return s[:, k - 1] - s[:, k]
+
+
+def check_routing(idx_gpu, logits_ref, idx_ref, k, delta):
+    """Bit-exact indices for every token whose top-k boundary gap exceeds
+    delta; returns the number of tokens inside the margin (not compared)."""
+    idx_gpu = np.asarray(idx_gpu)
+    gap = routing_margin(logits_ref, k)
+    near = gap <= delta
+    far = ~near
+    assert np.array_equal(idx_gpu[far], np.asarray(idx_ref)[far]), \
+        f"routing differs on {int((idx_gpu[far] != np.asarray(idx_ref)[far]).any(1).sum())} tokens"
+    return int(near.sum())
+
+
+def check_topk_of_gpu_logits(idx_gpu, logits_gpu, k):
+    """The GPU's selection is exactly the top-k of its own fp32 logits under
+    (value descending, index ascending): the integer decision is taken in the
+    same precision on both sides."""
+    want = ol.topk_desc_index_asc(np.asarray(logits_gpu, dtype=np.float32).astype(np.float64), k)
+    assert np.array_equal(np.asarray(idx_gpu), want)

@@ -1,0 +1,443 @@
+// C ABI of libmsk.so: argument checks, workspace layout, attention planning
+// and the calls into the kernel launchers.  Every check runs before any HIP
+// call, so invalid arguments return with nothing enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/msk.h"
+#include "launch.h"
+#include "params.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+msk_status fail(msk_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+msk_status ok() {
+  g_err.clear();
+  return MSK_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Target number of attention work items (one wave each) per layer: about
+// two rounds of the waves that fit on the chip at once.
+constexpr long long kTargetItems = 2048;
+
+struct AttnSplit {
+  int chunk, n_items, nrg;
+};
+
+AttnSplit plan_attention(const msk_layer_cfg& c, const msk_batch& b) {
+  const int G = c.n_q_heads / c.n_kv_heads;
+  const int nrg = cdiv((long long)G * b.tokens_per_req, msk::kRowGroup);
+  long long total = 0;
+  for (int r = 0; r < b.n_req; ++r) {
+    int base, end;
+    const int L = b.kv_len_host[r], W = c.window;
+    const int lo = W > 0 ? (L - W + 1 > 0 ? L - W + 1 : 0) : 0;
+    base = lo & ~63;
+    end = L + b.tokens_per_req;
+    total += (long long)(end - base) * c.n_kv_heads * nrg;
+  }
+  long long chunk = (total + kTargetItems - 1) / kTargetItems;
+  chunk = (chunk + 63) / 64 * 64;
+  if (chunk < 64) chunk = 64;
+  if (chunk > (1 << 20)) chunk = 1 << 20;
+  long long items = 0;
+  for (int r = 0; r < b.n_req; ++r) {
+    const int L = b.kv_len_host[r], W = c.window;
+    const int lo = W > 0 ? (L - W + 1 > 0 ? L - W + 1 : 0) : 0;
+    const int base = lo & ~63, end = L + b.tokens_per_req;
+    items += (long long)cdiv(end - base, chunk) * c.n_kv_heads * nrg;
+  }
+  return AttnSplit{(int)chunk, (int)items, nrg};
+}
+
+struct Layout {
+  size_t sync, qkv, part, attn_o, h, u, logits, idx, wts, act, xa, xb, total;
+};
+
+Layout layout(const msk_layer_cfg* cfg, int n_layers, const msk_batch& b) {
+  const msk_layer_cfg& c = cfg[0];
+  const size_t T = (size_t)b.n_req * b.tokens_per_req;
+  const size_t H = c.hidden, D = c.head_dim;
+  const size_t NR = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * D;
+  size_t max_items = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const AttnSplit a = plan_attention(cfg[l], b);
+    if ((size_t)a.n_items > max_items) max_items = a.n_items;
+  }
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += up(bytes);
+    return at;
+  };
+  L.sync = take(kAlign);
+  L.qkv = take(T * NR * 4);
+  L.part = take(max_items * msk::kRowGroup * (D + 1) * 4);
+  L.attn_o = take(T * c.n_q_heads * D * 4);
+  L.h = take(T * H * 4);
+  L.u = take(T * H * 4);
+  L.logits = take(T * c.n_experts * 4);
+  L.idx = take(T * c.top_k * 4);
+  L.wts = take(T * c.top_k * 4);
+  L.act = take(T * c.top_k * (size_t)c.ffn_dim * 4);
+  L.xa = take(T * H * 4);
+  L.xb = take(T * H * 4);
+  L.total = o;
+  return L;
+}
+
+bool dtype_in(int v, std::initializer_list<int> set) {
+  for (int s : set)
+    if (v == s) return true;
+  return false;
+}
+
+msk_status check_cfg(const msk_layer_cfg* c, int l) {
+  if (!c) return fail(MSK_ERR_INVALID_ARG, "layer %d: cfg is null", l);
+  if (c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->n_experts <= 0 || c->top_k <= 0 || c->ffn_dim <= 0)
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: every dimension must be positive", l);
+  if (c->n_q_heads % c->n_kv_heads != 0)
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: n_q_heads %d is not a multiple of n_kv_heads %d", l,
+                c->n_q_heads, c->n_kv_heads);
+  if (c->top_k > c->n_experts)
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: top_k %d > n_experts %d", l, c->top_k, c->n_experts);
+  if (c->window < 0) return fail(MSK_ERR_INVALID_ARG, "layer %d: window %d < 0", l, c->window);
+  if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps))
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: rms_eps must be positive and finite", l);
+  if (!std::isfinite(c->softmax_shift))
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: softmax_shift must be finite", l);
+  if (!dtype_in(c->dense_dtype, {MSK_F32, MSK_BF16}))
+    return fail(MSK_ERR_UNSUPPORTED, "layer %d: dense_dtype %d unsupported (F32, BF16)", l,
+                c->dense_dtype);
+  if (!dtype_in(c->expert_dtype, {MSK_F32, MSK_BF16, MSK_NVFP4}))
+    return fail(MSK_ERR_UNSUPPORTED, "layer %d: expert_dtype %d unsupported (F32, BF16, NVFP4)", l,
+                c->expert_dtype);
+  if (!dtype_in(c->kv_dtype, {MSK_F32, MSK_BF16, MSK_E4M3}))
+    return fail(MSK_ERR_UNSUPPORTED, "layer %d: kv_dtype %d unsupported (F32, BF16, E4M3)", l,
+                c->kv_dtype);
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(MSK_ERR_UNSUPPORTED, "layer %d: head_dim %d unsupported (32, 64, 128)", l, c->head_dim);
+  if (c->hidden % 32 != 0 || c->ffn_dim % 32 != 0)
+    return fail(MSK_ERR_UNSUPPORTED, "layer %d: hidden and ffn_dim must be multiples of 32", l);
+  if (c->n_experts > msk::kMaxExperts)
+    return fail(MSK_ERR_UNSUPPORTED, "layer %d: n_experts %d > %d", l, c->n_experts, msk::kMaxExperts);
+  if (c->top_k > msk::kMaxTopK)
+    return fail(MSK_ERR_UNSUPPORTED, "layer %d: top_k %d > %d", l, c->top_k, msk::kMaxTopK);
+  return ok();
+}
+
+msk_status check_same_shape(const msk_layer_cfg* a, const msk_layer_cfg* b, int l) {
+  if (a->hidden != b->hidden || a->n_q_heads != b->n_q_heads || a->n_kv_heads != b->n_kv_heads ||
+      a->head_dim != b->head_dim || a->n_experts != b->n_experts || a->top_k != b->top_k ||
+      a->ffn_dim != b->ffn_dim)
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: shape differs from layer 0", l);
+  return ok();
+}
+
+msk_status check_batch(const msk_batch* b) {
+  if (!b) return fail(MSK_ERR_INVALID_ARG, "batch is null");
+  if (b->n_req < 1 || b->n_req > MSK_MAX_REQ)
+    return fail(MSK_ERR_INVALID_ARG, "n_req %d outside [1, %d]", b->n_req, MSK_MAX_REQ);
+  if (b->tokens_per_req < 1)
+    return fail(MSK_ERR_INVALID_ARG, "tokens_per_req %d < 1", b->tokens_per_req);
+  if ((long long)b->n_req * b->tokens_per_req > MSK_MAX_TOKENS)
+    return fail(MSK_ERR_UNSUPPORTED, "n_req * tokens_per_req = %lld > %d",
+                (long long)b->n_req * b->tokens_per_req, MSK_MAX_TOKENS);
+  if (!b->kv_len_host) return fail(MSK_ERR_INVALID_ARG, "kv_len_host is null");
+  for (int r = 0; r < b->n_req; ++r) {
+    if (b->kv_len_host[r] < 0)
+      return fail(MSK_ERR_INVALID_ARG, "kv_len[%d] = %d < 0", r, b->kv_len_host[r]);
+    if ((long long)b->kv_len_host[r] + b->tokens_per_req > (1LL << 30))
+      return fail(MSK_ERR_UNSUPPORTED, "kv_len[%d] + tokens_per_req exceeds 2^30", r);
+  }
+  return ok();
+}
+
+msk_status check_kv(const msk_kv* kv, const msk_batch* b, int l) {
+  if (!kv || !kv->k || !kv->v) return fail(MSK_ERR_INVALID_ARG, "layer %d: kv cache pointer is null", l);
+  for (int r = 0; r < b->n_req; ++r)
+    if ((long long)b->kv_len_host[r] + b->tokens_per_req > kv->cap)
+      return fail(MSK_ERR_INVALID_ARG, "layer %d: kv_len[%d] + tokens_per_req = %lld > cap %lld", l, r,
+                  (long long)b->kv_len_host[r] + b->tokens_per_req, (long long)kv->cap);
+  return ok();
+}
+
+msk_status check_attn_weights(const msk_layer_weights* w, int l) {
+  if (!w) return fail(MSK_ERR_INVALID_ARG, "layer %d: weights are null", l);
+  if (!w->attn_norm || !w->q_norm || !w->k_norm || !w->wq || !w->wk || !w->wv || !w->wo)
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: an attention weight pointer is null", l);
+  return ok();
+}
+
+msk_status check_route_weights(const msk_layer_weights* w, int l) {
+  if (!w) return fail(MSK_ERR_INVALID_ARG, "layer %d: weights are null", l);
+  if (!w->ffn_norm || !w->w_router)
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: ffn_norm or w_router is null", l);
+  return ok();
+}
+
+msk_status check_expert_weights(const msk_layer_cfg* c, const msk_layer_weights* w, int l) {
+  if (!w) return fail(MSK_ERR_INVALID_ARG, "layer %d: weights are null", l);
+  if (!w->w_gate || !w->w_up || !w->w_down)
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: an expert weight pointer is null", l);
+  if (c->expert_dtype == MSK_NVFP4 &&
+      (!w->s_gate || !w->s_up || !w->s_down || !w->g_gate || !w->g_up || !w->g_down))
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: NVFP4 experts need block and matrix scales", l);
+  return ok();
+}
+
+#define CHECK(x)                       \
+  do {                                 \
+    msk_status s_ = (x);               \
+    if (s_ != MSK_OK) return s_;       \
+  } while (0)
+
+msk::LayerArgs make_layer(const msk_layer_cfg& c, const msk_layer_weights* w, const msk_kv* kv,
+                          const msk_batch* b) {
+  msk::LayerArgs L{};
+  L.H = c.hidden;
+  L.Hq = c.n_q_heads;
+  L.Hkv = c.n_kv_heads;
+  L.D = c.head_dim;
+  L.E = c.n_experts;
+  L.K = c.top_k;
+  L.F = c.ffn_dim;
+  L.window = c.window;
+  L.eps = c.rms_eps;
+  L.shift = c.softmax_shift;
+  L.qscale = (float)(1.0 / std::sqrt((double)c.head_dim));
+  L.ddt = c.dense_dtype;
+  L.edt = c.expert_dtype;
+  L.kdt = c.kv_dtype;
+  if (w) {
+    L.attn_norm = w->attn_norm;
+    L.q_norm = w->q_norm;
+    L.k_norm = w->k_norm;
+    L.ffn_norm = w->ffn_norm;
+    L.wq = static_cast<const uint8_t*>(w->wq);
+    L.wk = static_cast<const uint8_t*>(w->wk);
+    L.wv = static_cast<const uint8_t*>(w->wv);
+    L.wo = static_cast<const uint8_t*>(w->wo);
+    L.wr = static_cast<const uint8_t*>(w->w_router);
+    L.wg = static_cast<const uint8_t*>(w->w_gate);
+    L.wu = static_cast<const uint8_t*>(w->w_up);
+    L.wd = static_cast<const uint8_t*>(w->w_down);
+    L.sg = w->s_gate;
+    L.su = w->s_up;
+    L.sd = w->s_down;
+    L.gg = w->g_gate;
+    L.gu = w->g_up;
+    L.gd = w->g_down;
+  }
+  if (kv) {
+    L.kc = static_cast<uint8_t*>(kv->k);
+    L.vc = static_cast<uint8_t*>(kv->v);
+    L.cap = kv->cap;
+  }
+  if (b) {
+    const AttnSplit a = plan_attention(c, *b);
+    L.chunk = a.chunk;
+    L.n_items = a.n_items;
+    L.nrg = a.nrg;
+  }
+  return L;
+}
+
+msk::StepArgs make_step(const Layout& lay, void* ws, int n_req, int Tr, const int32_t* kv_len) {
+  msk::StepArgs S{};
+  S.n_req = n_req;
+  S.Tr = Tr;
+  S.T = n_req * Tr;
+  for (int r = 0; r < n_req && kv_len; ++r) S.kv_len[r] = kv_len[r];
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  S.sync = reinterpret_cast<unsigned*>(base + lay.sync);
+  S.qkv = reinterpret_cast<float*>(base + lay.qkv);
+  S.part = reinterpret_cast<float*>(base + lay.part);
+  S.attn_o = reinterpret_cast<float*>(base + lay.attn_o);
+  S.h = reinterpret_cast<float*>(base + lay.h);
+  S.u = reinterpret_cast<float*>(base + lay.u);
+  S.logits = reinterpret_cast<float*>(base + lay.logits);
+  S.idx = reinterpret_cast<int*>(base + lay.idx);
+  S.wts = reinterpret_cast<float*>(base + lay.wts);
+  S.act = reinterpret_cast<float*>(base + lay.act);
+  S.xa = reinterpret_cast<float*>(base + lay.xa);
+  S.xb = reinterpret_cast<float*>(base + lay.xb);
+  return S;
+}
+
+msk_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MSK_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// A one-token batch description for the calls that take only a token count.
+struct FlatBatch {
+  int32_t zero[MSK_MAX_TOKENS] = {};
+  msk_batch b{};
+  explicit FlatBatch(int T) {
+    b.n_req = T;
+    b.tokens_per_req = 1;
+    b.kv_len_host = zero;
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int32_t msk_abi_version(void) { return MSK_ABI_VERSION; }
+
+const char* msk_last_error(void) { return g_err.c_str(); }
+
+size_t msk_workspace_size(const msk_layer_cfg* cfg, int32_t n_layers, const msk_batch* batch) {
+  if (!cfg || n_layers < 1 || n_layers > MSK_MAX_STACK) {
+    fail(MSK_ERR_INVALID_ARG, "n_layers %d outside [1, %d] or cfg null", n_layers, MSK_MAX_STACK);
+    return 0;
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    if (check_cfg(&cfg[l], l) != MSK_OK) return 0;
+    if (l > 0 && check_same_shape(&cfg[0], &cfg[l], l) != MSK_OK) return 0;
+  }
+  if (check_batch(batch) != MSK_OK) return 0;
+  ok();
+  return layout(cfg, n_layers, *batch).total;
+}
+
+msk_status msk_workspace_status(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || ws_bytes < kAlign) return fail(MSK_ERR_WORKSPACE, "workspace missing or too small");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return device_status(e, "hipStreamSynchronize");
+  unsigned words[4] = {0, 0, 0, 0};
+  e = hipMemcpy(words, ws, sizeof(words), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return device_status(e, "hipMemcpy");
+  if (words[2] != 0 || words[0] != 0 || words[1] != 0) {
+    e = hipMemset(ws, 0, kAlign);
+    if (e != hipSuccess) return device_status(e, "hipMemset");
+    if (words[2] != 0) return fail(MSK_ERR_TIMEOUT, "a device-side wait gave up (barrier watchdog)");
+    return fail(MSK_ERR_TIMEOUT, "synchronisation words were left non-zero");
+  }
+  return ok();
+}
+
+msk_status msk_attn_step(const msk_layer_cfg* cfg, const msk_layer_weights* w, const msk_kv* kv,
+                         const msk_batch* batch, const float* x, float* h, float* attn_o,
+                         int32_t* win, void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(cfg, 0));
+  CHECK(check_batch(batch));
+  CHECK(check_kv(kv, batch, 0));
+  CHECK(check_attn_weights(w, 0));
+  if (!x || !h) return fail(MSK_ERR_INVALID_ARG, "x or h is null");
+  if (x == h) return fail(MSK_ERR_INVALID_ARG, "x and h must not overlap");
+  const Layout lay = layout(cfg, 1, *batch);
+  if (!ws || ws_bytes < lay.total)
+    return fail(MSK_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, lay.total);
+  msk::LayerArgs L = make_layer(*cfg, w, kv, batch);
+  msk::StepArgs S = make_step(lay, ws, batch->n_req, batch->tokens_per_req, batch->kv_len_host);
+  S.n_layers = 1;
+  if (attn_o) S.attn_o = attn_o;
+  S.win_out = win;
+  return device_status(msk::launch_attn(L, S, x, h, static_cast<hipStream_t>(stream)),
+                       "attention launch");
+}
+
+msk_status msk_moe_route(const msk_layer_cfg* cfg, const msk_layer_weights* w, int32_t n_tokens,
+                         const float* h, float* u, int32_t* topk_idx, float* topk_w, float* logits,
+                         void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(cfg, 0));
+  CHECK(check_route_weights(w, 0));
+  if (n_tokens < 1 || n_tokens > MSK_MAX_TOKENS)
+    return fail(MSK_ERR_INVALID_ARG, "n_tokens %d outside [1, %d]", n_tokens, MSK_MAX_TOKENS);
+  if (!h || !u || !topk_idx || !topk_w) return fail(MSK_ERR_INVALID_ARG, "an output or h is null");
+  FlatBatch fb(n_tokens);
+  const Layout lay = layout(cfg, 1, fb.b);
+  if (!ws || ws_bytes < lay.total)
+    return fail(MSK_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, lay.total);
+  msk::LayerArgs L = make_layer(*cfg, w, nullptr, nullptr);
+  msk::StepArgs S = make_step(lay, ws, n_tokens, 1, nullptr);
+  S.u = u;
+  S.idx = topk_idx;
+  S.wts = topk_w;
+  if (logits) S.logits = logits;
+  return device_status(msk::launch_route(L, S, h, nullptr, static_cast<hipStream_t>(stream)),
+                       "router launch");
+}
+
+msk_status msk_expert_ffn(const msk_layer_cfg* cfg, const msk_layer_weights* w, int32_t n_tokens,
+                          const float* u, const int32_t* topk_idx, const float* topk_w,
+                          const float* h, float* out, void* ws, size_t ws_bytes, void* stream) {
+  CHECK(check_cfg(cfg, 0));
+  CHECK(check_expert_weights(cfg, w, 0));
+  if (n_tokens < 1 || n_tokens > MSK_MAX_TOKENS)
+    return fail(MSK_ERR_INVALID_ARG, "n_tokens %d outside [1, %d]", n_tokens, MSK_MAX_TOKENS);
+  if (!u || !topk_idx || !topk_w || !h || !out)
+    return fail(MSK_ERR_INVALID_ARG, "an input or output pointer is null");
+  FlatBatch fb(n_tokens);
+  const Layout lay = layout(cfg, 1, fb.b);
+  if (!ws || ws_bytes < lay.total)
+    return fail(MSK_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, lay.total);
+  msk::LayerArgs L = make_layer(*cfg, w, nullptr, nullptr);
+  msk::StepArgs S = make_step(lay, ws, n_tokens, 1, nullptr);
+  S.u = const_cast<float*>(u);
+  S.idx = const_cast<int*>(topk_idx);
+  S.wts = const_cast<float*>(topk_w);
+  return device_status(msk::launch_ffn(L, S, h, out, static_cast<hipStream_t>(stream)),
+                       "expert launch");
+}
+
+msk_status msk_layer_step(const msk_layer_cfg* cfg, const msk_layer_weights* w, const msk_kv* kv,
+                          int32_t n_layers, const msk_batch* batch, float* x, float* layer_out,
+                          int32_t* topk_idx, int32_t* win, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!cfg || !w || !kv) return fail(MSK_ERR_INVALID_ARG, "cfg, w or kv is null");
+  if (n_layers < 1 || n_layers > MSK_MAX_STACK)
+    return fail(MSK_ERR_INVALID_ARG, "n_layers %d outside [1, %d]", n_layers, MSK_MAX_STACK);
+  CHECK(check_batch(batch));
+  for (int l = 0; l < n_layers; ++l) {
+    CHECK(check_cfg(&cfg[l], l));
+    if (l > 0) CHECK(check_same_shape(&cfg[0], &cfg[l], l));
+    CHECK(check_kv(&kv[l], batch, l));
+    CHECK(check_attn_weights(&w[l], l));
+    CHECK(check_route_weights(&w[l], l));
+    CHECK(check_expert_weights(&cfg[l], &w[l], l));
+  }
+  if (!x) return fail(MSK_ERR_INVALID_ARG, "x is null");
+  const Layout lay = layout(cfg, n_layers, *batch);
+  if (!ws || ws_bytes < lay.total)
+    return fail(MSK_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, lay.total);
+  msk::LayerArgs Ls[msk::kMaxLayers];
+  for (int l = 0; l < n_layers; ++l) Ls[l] = make_layer(cfg[l], &w[l], &kv[l], batch);
+  msk::StepArgs S = make_step(lay, ws, batch->n_req, batch->tokens_per_req, batch->kv_len_host);
+  S.n_layers = n_layers;
+  S.x_in = x;
+  S.x_out = x;
+  S.layer_out = layer_out;
+  S.topk_out = topk_idx;
+  S.win_out = win;
+  return device_status(msk::launch_step_fused(Ls, S, static_cast<hipStream_t>(stream)),
+                       "layer-step launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Kernel parameter blocks shared by the host planner and the device code.
+#pragma once
+#include <stdint.h>
+
+namespace msk {
+
+constexpr int kMaxReq = 64;
+constexpr int kMaxTok = 64;
+constexpr int kMaxLayers = 4;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxExperts = 256;
+constexpr int kRowGroup = 8;       // query rows handled together by attention
+constexpr int kBlockThreads = 256; // every kernel uses 4 waves of 64
+constexpr int kWaves = kBlockThreads / 64;
+
+enum Dt : int { kF32 = 0, kBF16 = 1, kE4M3 = 2, kNVFP4 = 3 };
+
+// One layer's shapes, weights, cache and attention plan.
+struct LayerArgs {
+  int H, Hq, Hkv, D, E, K, F, window;
+  float eps, shift, qscale;  // qscale = 1/sqrt(D)
+  int ddt, edt, kdt;
+  const float *attn_norm, *q_norm, *k_norm, *ffn_norm;
+  const uint8_t *wq, *wk, *wv, *wo, *wr, *wg, *wu, *wd;
+  const uint8_t *sg, *su, *sd;
+  const float *gg, *gu, *gd;
+  uint8_t *kc, *vc;
+  long long cap;
+  int chunk;    // cache positions per attention work item (multiple of 64)
+  int n_items;  // attention work items of this layer
+  int nrg;      // query row groups per kv head: ceil(G * Tr / kRowGroup)
+};
+
+// Buffers of one step; the per-layer arrays follow the layer index.
+struct StepArgs {
+  int n_req, Tr, T, n_layers;
+  int kv_len[kMaxReq];
+  const float *x_in;    // layer 0 input [T][H]
+  float *x_out;         // last layer output [T][H] (may equal x_in)
+  float *layer_out;     // [n_layers][T][H] or null
+  int *topk_out;        // [n_layers][T][K] or null
+  int *win_out;         // [n_layers][T][2] or null
+  float *attn_o_out;    // [T][Hq*D] or null (single layer calls)
+  // workspace
+  float *qkv;           // [T][Hq*D + 2*Hkv*D]
+  float *part;          // attention partials [items][kRowGroup][D + 1]
+  float *attn_o;        // [T][Hq*D]
+  float *h;             // [T][H]
+  float *u;             // [T][H]
+  float *logits;        // [T][E]
+  int *idx;             // [T][K]
+  float *wts;           // [T][K]
+  float *act;           // [T*K][F]
+  float *xa, *xb;       // [T][H] layer ping-pong
+  unsigned *sync;       // grid barrier words; sync[0] arrive, sync[1] depart, sync[2] error
+};
+
+}  // namespace msk

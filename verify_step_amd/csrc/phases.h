@@ -1,0 +1,797 @@
+// The phases of one MoE layer step, written as grid-stride device functions
+// so that the same code runs as separate kernels (one launch per phase) and
+// inside the persistent whole-step kernel (phases separated by grid barriers).
+//
+// Every phase takes the "virtual block" index vb and count nvb it runs on.
+#pragma once
+#include "device.h"
+
+namespace msk {
+
+template <int N> struct IC { static constexpr int value = N; };
+
+// Calls f(IC<NV>) with the smallest power of two NV >= n, n <= NVMAX.
+template <int NVMAX, class F>
+__device__ __forceinline__ void nv_dispatch(int n, F&& f) {
+  if (NVMAX <= 1 || n <= 1) f(IC<1>{});
+  else if (NVMAX <= 2 || n <= 2) f(IC<(NVMAX < 2 ? NVMAX : 2)>{});
+  else if (NVMAX <= 4 || n <= 4) f(IC<(NVMAX < 4 ? NVMAX : 4)>{});
+  else if (NVMAX <= 8 || n <= 8) f(IC<(NVMAX < 8 ? NVMAX : 8)>{});
+  else if (NVMAX <= 16 || n <= 16) f(IC<(NVMAX < 16 ? NVMAX : 16)>{});
+  else f(IC<NVMAX>{});
+}
+
+// Rows per wave of the dense projections for NV token vectors: fewer rows
+// when many tokens share them, so the accumulators stay in registers.
+template <int NV> struct DenseRows { static constexpr int R = NV >= 16 ? 2 : 4; };
+
+__host__ __device__ inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Cache range one request's tokens read in one layer: from the window start of
+// its first draft token (rounded down to 64 positions) to one past its last
+// draft token's own position.
+__host__ __device__ inline void req_span(int L, int Tr, int W, int& base, int& end) {
+  const int lo = W > 0 ? (L - W + 1 > 0 ? L - W + 1 : 0) : 0;
+  base = lo & ~63;
+  end = L + Tr;
+}
+
+// Attention work split of one layer, kept in LDS by every workgroup.
+struct AttnPlan {
+  int item0[kMaxReq + 1];  // first item of request b; item0[n_req] = all items
+  int nch[kMaxReq];        // chunks per (kv head, row group) of request b
+  int base[kMaxReq];
+  int end[kMaxReq];
+};
+
+__device__ inline void build_plan(const LayerArgs& L, const StepArgs& S, AttnPlan* P) {
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int b = 0; b < S.n_req; ++b) {
+      int base, end;
+      req_span(S.kv_len[b], S.Tr, L.window, base, end);
+      const int n = ceil_div(end - base, L.chunk);
+      P->base[b] = base;
+      P->end[b] = end;
+      P->nch[b] = n;
+      P->item0[b] = acc;
+      acc += n * L.Hkv * L.nrg;
+    }
+    P->item0[S.n_req] = acc;
+  }
+  __syncthreads();
+}
+
+// 1/sqrt(mean(x^2) + eps) of T rows of length H, into rs[0..T).
+__device__ inline void block_rstd(const float* x, int T, int H, float eps, float* rs) {
+  for (int t = wave_id(); t < T; t += kWaves) {
+    const float* row = x + (size_t)t * H;
+    float s = 0.f;
+    for (int c = lane_id() * 4; c < H; c += 256) {
+      v4f a = *reinterpret_cast<const v4f*>(row + c);
+      s += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    }
+    s = wave_sum(s);
+    if (lane_id() == 0) rs[t] = 1.0f / sqrtf(s / (float)H + eps);
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ size_t dense_row_bytes(int dt, int n) {
+  return (size_t)n * (dt == kBF16 ? 2 : 4);
+}
+__device__ __forceinline__ size_t expert_row_bytes(int dt, int n) {
+  return dt == kNVFP4 ? (size_t)n / 2 : (size_t)n * (dt == kBF16 ? 2 : 4);
+}
+
+// Lane (r * NV + v) % 64 stores value acc[r][v]; all lanes hold all values.
+template <int R, int NV, class F>
+__device__ __forceinline__ void store_results(const float (&acc)[R][NV], int nv, F&& st) {
+  const int ln = lane_id();
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      if (v < nv && ln == ((r * NV + v) & 63)) st(r, v, acc[r][v]);
+}
+
+// ------------------------------------------------------------- QKV
+// qkv[t][r] = rstd[t] * sum_c W[r][c] * attn_norm[c] * x[t][c] for the rows of
+// wq, wk, wv stacked (r < Hq*D: wq; then wk; then wv).
+template <int DT, int NV>
+__device__ void phase_qkv(const LayerArgs& L, const StepArgs& S, const float* x,
+                          const float* rs, int vb, int nvb) {
+  constexpr int R = DenseRows<NV>::R;
+  const int NQ = L.Hq * L.D, NK = L.Hkv * L.D, NR = NQ + 2 * NK;
+  const size_t rb = dense_row_bytes(DT, L.H);
+  const int gw = vb * kWaves + wave_id(), nw = nvb * kWaves;
+  for (int t0 = 0; t0 < S.T; t0 += NV) {
+    const int nt = S.T - t0 < NV ? S.T - t0 : NV;
+    const float* vin[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) vin[v] = x + (size_t)(t0 + (v < nt ? v : 0)) * L.H;
+    const uint8_t* srow[R] = {};
+    for (int blk = gw; blk * R < NR; blk += nw) {
+      const int r0 = blk * R;
+      const uint8_t* base;
+      int rr;
+      if (r0 < NQ) { base = L.wq; rr = r0; }
+      else if (r0 < NQ + NK) { base = L.wk; rr = r0 - NQ; }
+      else { base = L.wv; rr = r0 - NQ - NK; }
+      const uint8_t* wrow[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) wrow[r] = base + (size_t)(rr + r) * rb;
+      float acc[R][NV];
+      wave_gemv<DT, R, NV>(wrow, srow, L.H, vin, nt, L.attn_norm, acc);
+      store_results<R, NV>(acc, nt, [&](int r, int v, float val) {
+        S.qkv[(size_t)(t0 + v) * NR + r0 + r] = val * rs[t0 + v];
+      });
+    }
+  }
+}
+
+// ------------------------------------------------------- attention
+// One wave per work item (request b, kv head j, query row group rg, chunk c).
+// Rows of a group are (draft token t, query head g of the group) pairs,
+// m = t * G + g, eight at a time.  For each 64-position block of the chunk:
+//  - K rows are staged in a wave-private LDS tile; a lane then owns one
+//    cache position and computes its eight scores in-lane;
+//  - e = exp(s - shift) inside the token's window, else 0 (no running max);
+//  - V is read straight from the cache, each lane owning a slice of head_dim
+//    for a few positions, and o += e * V.
+// Positions at or past kv_len[b] are the step's own draft tokens: their K/V
+// are rebuilt from the QKV output (QK-norm on k, cast to the cache format),
+// and the row-group-0 item also writes them into the cache.
+// The item writes its plain partial sums (o[8][D], l[8]).
+template <int KDT> struct KV;
+template <> struct KV<kF32> { enum { ES = 4, EPLV = 4 }; };
+template <> struct KV<kBF16> { enum { ES = 2, EPLV = 8 }; };
+template <> struct KV<kE4M3> { enum { ES = 1, EPLV = 8 }; };
+
+template <int KDT, int D>
+struct AttnGeom {
+  static constexpr int ES = KV<KDT>::ES;
+  static constexpr int RB = D * ES;           // cache row bytes
+  static constexpr int RBP = RB + 16;         // padded LDS row
+  static constexpr int CPR = RB / 16;         // 16-B chunks per row
+  static constexpr int EPLV = KV<KDT>::EPLV;  // V elements per lane load
+  static constexpr int VB = EPLV * ES;        // V bytes per lane load
+  static constexpr int LPP = D / EPLV;        // lanes per position (V)
+  static constexpr int PPI = 64 / LPP;        // positions per V load
+  static constexpr int NVL = 64 / PPI;        // V loads per lane per block
+  // per-wave LDS: q rows, K tile, weights tile, new-key norms, row windows
+  static constexpr int LDS_Q = kRowGroup * D * 4;
+  static constexpr int LDS_K = 64 * RBP;
+  static constexpr int LDS_E = kRowGroup * 64 * 4;
+  static constexpr int LDS_RK = kMaxTok * 4;
+  static constexpr int LDS_WIN = kRowGroup * 8;
+  static constexpr int LDS_WAVE = LDS_Q + LDS_K + LDS_E + LDS_RK + LDS_WIN;
+};
+
+template <int KDT>
+__device__ __forceinline__ v4u encode16(const float* f);
+template <>
+__device__ __forceinline__ v4u encode16<kF32>(const float* f) {
+  return v4u{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+             __float_as_uint(f[3])};
+}
+template <>
+__device__ __forceinline__ v4u encode16<kBF16>(const float* f) {
+  return v4u{f2bf16(f[0]) | (f2bf16(f[1]) << 16), f2bf16(f[2]) | (f2bf16(f[3]) << 16),
+             f2bf16(f[4]) | (f2bf16(f[5]) << 16), f2bf16(f[6]) | (f2bf16(f[7]) << 16)};
+}
+template <>
+__device__ __forceinline__ v4u encode16<kE4M3>(const float* f) {
+  return v4u{f2e4m3x2(f[0], f[1]) | (f2e4m3x2(f[2], f[3]) << 16),
+             f2e4m3x2(f[4], f[5]) | (f2e4m3x2(f[6], f[7]) << 16),
+             f2e4m3x2(f[8], f[9]) | (f2e4m3x2(f[10], f[11]) << 16),
+             f2e4m3x2(f[12], f[13]) | (f2e4m3x2(f[14], f[15]) << 16)};
+}
+
+// Decode the first EPLV elements held in a 16-B register value.
+template <int KDT>
+__device__ __forceinline__ void decode_reg(const v4u& w, float* f) {
+  if constexpr (KDT == kF32) {
+    f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
+    f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
+  } else if constexpr (KDT == kBF16) {
+    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+  } else {
+    e4m3x4(w.x, f);
+    e4m3x4(w.y, f + 4);
+  }
+}
+
+// Decode 8 consecutive cache elements starting at p (LDS or registers).
+template <int KDT>
+__device__ __forceinline__ void decode8(const uint8_t* p, float* f) {
+  if constexpr (KDT == kF32) {
+    v4f a = *reinterpret_cast<const v4f*>(p);
+    v4f b = *reinterpret_cast<const v4f*>(p + 16);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  } else if constexpr (KDT == kBF16) {
+    v4u w = *reinterpret_cast<const v4u*>(p);
+    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+  } else {
+    v2u w = *reinterpret_cast<const v2u*>(p);
+    e4m3x4(w.x, f);
+    e4m3x4(w.y, f + 4);
+  }
+}
+
+template <int KDT, int D>
+__device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int item,
+                          uint8_t* wl) {
+  using Gm = AttnGeom<KDT, D>;
+  constexpr int ES = Gm::ES, RB = Gm::RB, RBP = Gm::RBP, CPR = Gm::CPR;
+  constexpr int EPLV = Gm::EPLV, VB = Gm::VB, LPP = Gm::LPP, PPI = Gm::PPI, NVL = Gm::NVL;
+  float* qs = reinterpret_cast<float*>(wl);
+  uint8_t* kt = wl + Gm::LDS_Q;
+  float* et = reinterpret_cast<float*>(kt + Gm::LDS_K);
+  float* rk = et + kRowGroup * 64;
+  int* win = reinterpret_cast<int*>(rk + kMaxTok);
+
+  const int ln = lane_id();
+  int b = 0;
+  while (b + 1 < S.n_req && P->item0[b + 1] <= item) ++b;
+  const int nch = P->nch[b];
+  int rem = item - P->item0[b];
+  const int j = rem / (L.nrg * nch);
+  rem -= j * L.nrg * nch;
+  const int rg = rem / nch;
+  const int c = rem - rg * nch;
+  const int p0 = P->base[b] + c * L.chunk;
+  const int p1 = p0 + L.chunk < P->end[b] ? p0 + L.chunk : P->end[b];
+  const int Lb = S.kv_len[b];
+  const int G = L.Hq / L.Hkv;
+  const int M = G * S.Tr;
+  const int m0 = rg * kRowGroup;
+  const int NQ = L.Hq * L.D, NK = L.Hkv * L.D, NR = NQ + 2 * NK;
+  const size_t head_off = ((size_t)b * L.Hkv + j) * (size_t)L.cap;  // in rows
+  uint8_t* kc = L.kc + head_off * RB;
+  uint8_t* vc = L.vc + head_off * RB;
+  const bool writer = (rg == 0);
+
+  // normalised, pre-scaled query rows and their windows
+  for (int mm = 0; mm < kRowGroup; ++mm) {
+    const int m = m0 + mm;
+    if (m < M) {
+      const int t = m / G, g = m - (m / G) * G;
+      const float* q = S.qkv + (size_t)(b * S.Tr + t) * NR + (size_t)(j * G + g) * D;
+      float qv[(D + 63) / 64];
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < (D + 63) / 64; ++i) {
+        const int d = ln + 64 * i;
+        qv[i] = d < D ? q[d] : 0.f;
+        ss += qv[i] * qv[i];
+      }
+      ss = wave_sum(ss);
+      const float r = 1.0f / sqrtf(ss / (float)D + L.eps);
+#pragma unroll
+      for (int i = 0; i < (D + 63) / 64; ++i) {
+        const int d = ln + 64 * i;
+        if (d < D) qs[mm * D + d] = qv[i] * r * L.q_norm[d] * L.qscale;
+      }
+      if (ln == 0) {
+        const int p = Lb + t;
+        win[2 * mm] = L.window > 0 ? (p - L.window + 1 > 0 ? p - L.window + 1 : 0) : 0;
+        win[2 * mm + 1] = p;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < (D + 63) / 64; ++i) {
+        const int d = ln + 64 * i;
+        if (d < D) qs[mm * D + d] = 0.f;
+      }
+      if (ln == 0) { win[2 * mm] = 1; win[2 * mm + 1] = 0; }
+    }
+  }
+  wave_lds_sync();
+  // positions before the group's earliest window start are never visible
+  const int lo_min = win[0];
+  // 1/rms of the step's new keys that fall in this chunk
+  int tn0 = p0 - Lb > 0 ? p0 - Lb : 0;
+  int tn1 = p1 - Lb < S.Tr ? p1 - Lb : S.Tr;
+  for (int t = tn0; t < tn1; ++t) {
+    const float* k = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + (size_t)j * D;
+    float ss = 0.f;
+    for (int d = ln; d < D; d += 64) ss += k[d] * k[d];
+    ss = wave_sum(ss);
+    if (ln == 0) rk[t] = 1.0f / sqrtf(ss / (float)D + L.eps);
+  }
+  wave_lds_sync();
+
+  float lsum[kRowGroup];
+  float o[kRowGroup][EPLV];
+#pragma unroll
+  for (int mm = 0; mm < kRowGroup; ++mm) {
+    lsum[mm] = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPLV; ++i) o[mm][i] = 0.f;
+  }
+  const int pg = ln / LPP, dc = ln - (ln / LPP) * LPP;
+
+  for (int pb = p0; pb < p1; pb += 64) {
+    const int npos = p1 - pb < 64 ? p1 - pb : 64;
+    // V rows of old positions, straight to registers
+    v4u vraw[NVL];
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int pp = pg + i * PPI;
+      const int pos = pb + pp;
+      vraw[i] = v4u{0u, 0u, 0u, 0u};
+      if (pp < npos && pos >= lo_min && pos < Lb) {
+        const uint8_t* src = vc + (size_t)pos * RB + dc * VB;
+        if constexpr (VB == 16) {
+          vraw[i] = *reinterpret_cast<const v4u*>(src);
+        } else {
+          v2u t2 = *reinterpret_cast<const v2u*>(src);
+          vraw[i].x = t2.x;
+          vraw[i].y = t2.y;
+        }
+      }
+    }
+    // K rows into the LDS tile (new positions rebuilt from the QKV output)
+#pragma unroll
+    for (int i = 0; i < CPR; ++i) {
+      const int q = ln + 64 * i;
+      const int row = q / CPR, col = q - (q / CPR) * CPR;
+      const int pos = pb + row;
+      if (row < npos) {
+        uint8_t* dst = kt + row * RBP + col * 16;
+        if (pos < Lb) {
+          *reinterpret_cast<v4u*>(dst) = *reinterpret_cast<const v4u*>(kc + (size_t)pos * RB + col * 16);
+        } else {
+          const int t = pos - Lb;
+          constexpr int EP = 16 / ES;
+          const int d0 = col * EP;
+          const float* k = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + (size_t)j * D + d0;
+          float f[EP];
+#pragma unroll
+          for (int e = 0; e < EP; ++e) f[e] = k[e] * rk[t] * L.k_norm[d0 + e];
+          const v4u enc = encode16<KDT>(f);
+          *reinterpret_cast<v4u*>(dst) = enc;
+          if (writer) *reinterpret_cast<v4u*>(kc + (size_t)pos * RB + col * 16) = enc;
+        }
+      }
+    }
+    wave_lds_sync();
+    // scores: lane = position
+    {
+      float s[kRowGroup];
+#pragma unroll
+      for (int mm = 0; mm < kRowGroup; ++mm) s[mm] = 0.f;
+      const uint8_t* krow = kt + ln * RBP;
+#pragma unroll 4
+      for (int d0 = 0; d0 < D; d0 += 8) {
+        float kf[8];
+        decode8<KDT>(krow + d0 * ES, kf);
+#pragma unroll
+        for (int mm = 0; mm < kRowGroup; ++mm) {
+          v4f qa = *reinterpret_cast<const v4f*>(qs + mm * D + d0);
+          v4f qb = *reinterpret_cast<const v4f*>(qs + mm * D + d0 + 4);
+          s[mm] = fmaf(qa.x, kf[0], s[mm]);
+          s[mm] = fmaf(qa.y, kf[1], s[mm]);
+          s[mm] = fmaf(qa.z, kf[2], s[mm]);
+          s[mm] = fmaf(qa.w, kf[3], s[mm]);
+          s[mm] = fmaf(qb.x, kf[4], s[mm]);
+          s[mm] = fmaf(qb.y, kf[5], s[mm]);
+          s[mm] = fmaf(qb.z, kf[6], s[mm]);
+          s[mm] = fmaf(qb.w, kf[7], s[mm]);
+        }
+      }
+      const int pos = pb + ln;
+#pragma unroll
+      for (int mm = 0; mm < kRowGroup; ++mm) {
+        const bool ok = ln < npos && pos >= win[2 * mm] && pos <= win[2 * mm + 1];
+        const float e = ok ? __expf(s[mm] - L.shift) : 0.f;
+        et[mm * 64 + ln] = e;
+        lsum[mm] += e;
+      }
+    }
+    wave_lds_sync();
+    // o += e * V
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int pp = pg + i * PPI;
+      const int pos = pb + pp;
+      if (pp < npos && pos >= lo_min) {
+        float vf[EPLV];
+        if (pos < Lb) {
+          decode_reg<KDT>(vraw[i], vf);
+        } else {
+          const int t = pos - Lb;
+          const float* v = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + NK + (size_t)j * D + dc * EPLV;
+          float raw[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) raw[e] = e < EPLV ? v[e] : 0.f;
+          const v4u enc = encode16<KDT>(raw);
+          if (writer) {
+            uint8_t* dst = vc + (size_t)pos * RB + dc * VB;
+            if constexpr (VB == 16)
+              *reinterpret_cast<v4u*>(dst) = enc;
+            else
+              *reinterpret_cast<v2u*>(dst) = v2u{enc.x, enc.y};
+          }
+          decode_reg<KDT>(enc, vf);
+        }
+#pragma unroll
+        for (int mm = 0; mm < kRowGroup; ++mm) {
+          const float e = et[mm * 64 + pp];
+#pragma unroll
+          for (int k = 0; k < EPLV; ++k) o[mm][k] = fmaf(e, vf[k], o[mm][k]);
+        }
+      }
+    }
+    wave_lds_sync();
+  }
+  // reduce over lanes and write the partial sums
+  float* part = S.part + (size_t)item * kRowGroup * (D + 1);
+#pragma unroll
+  for (int mm = 0; mm < kRowGroup; ++mm) {
+    const float l = wave_sum(lsum[mm]);
+#pragma unroll
+    for (int k = 0; k < EPLV; ++k) {
+      float v = o[mm][k];
+#pragma unroll
+      for (int off = LPP; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+      o[mm][k] = v;
+    }
+    if (pg == 0) {
+#pragma unroll
+      for (int k = 0; k < EPLV; ++k) part[mm * (D + 1) + dc * EPLV + k] = o[mm][k];
+    }
+    if (ln == 0) part[mm * (D + 1) + D] = l;
+  }
+}
+
+template <int KDT, int D>
+__device__ void phase_attn(const LayerArgs& L, const StepArgs& S, const AttnPlan* P,
+                           uint8_t* lds_waves, int vb, int nvb) {
+  using Gm = AttnGeom<KDT, D>;
+  uint8_t* wl = lds_waves + wave_id() * Gm::LDS_WAVE;
+  const int n_items = P->item0[S.n_req];
+  for (int item = vb * kWaves + wave_id(); item < n_items; item += nvb * kWaves)
+    attn_item<KDT, D>(L, S, P, item, wl);
+}
+
+// ---------------------------------------------------------- combine
+// attn_o[t][h] = sum_chunks o / sum_chunks l (plain sums, fixed order).
+__device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int vb,
+                              int nvb) {
+  const int D = L.D, G = L.Hq / L.Hkv;
+  const int rows = S.T * L.Hq;
+  const int ln = lane_id();
+  for (int row = vb * kWaves + wave_id(); row < rows; row += nvb * kWaves) {
+    const int tok = row / L.Hq, hh = row - (row / L.Hq) * L.Hq;
+    const int b = tok / S.Tr, tt = tok - (tok / S.Tr) * S.Tr;
+    const int j = hh / G, g = hh - (hh / G) * G;
+    const int m = tt * G + g, rg = m / kRowGroup, mm = m - rg * kRowGroup;
+    const int nch = P->nch[b];
+    const int it0 = P->item0[b] + (j * L.nrg + rg) * nch;
+    const float* base = S.part + (size_t)it0 * kRowGroup * (D + 1) + mm * (D + 1);
+    const size_t stride = (size_t)kRowGroup * (D + 1);
+    float l = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int c = 0; c < nch; ++c) {
+      const float* p = base + c * stride;
+      l += p[D];
+      if (ln < D) o0 += p[ln];
+      if (ln + 64 < D) o1 += p[ln + 64];
+    }
+    float* dst = S.attn_o + (size_t)tok * L.Hq * D + (size_t)hh * D;
+    if (ln < D) dst[ln] = o0 / l;
+    if (ln + 64 < D) dst[ln + 64] = o1 / l;
+  }
+  if (S.win_out != nullptr && vb == 0) {
+    for (int tok = threadIdx.x; tok < S.T; tok += blockDim.x) {
+      const int b = tok / S.Tr, t = tok - (tok / S.Tr) * S.Tr;
+      const int p = S.kv_len[b] + t;
+      S.win_out[2 * tok] = L.window > 0 ? (p - L.window + 1 > 0 ? p - L.window + 1 : 0) : 0;
+      S.win_out[2 * tok + 1] = p;
+    }
+  }
+}
+
+// ------------------------------------------------------------- Wo
+// h[t][r] = x[t][r] + sum_c wo[r][c] * attn_o[t][c]
+template <int DT, int NV>
+__device__ void phase_wo(const LayerArgs& L, const StepArgs& S, const float* x, float* h, int vb,
+                         int nvb) {
+  constexpr int R = DenseRows<NV>::R;
+  const int NI = L.Hq * L.D;
+  const size_t rb = dense_row_bytes(DT, NI);
+  const int gw = vb * kWaves + wave_id(), nw = nvb * kWaves;
+  for (int t0 = 0; t0 < S.T; t0 += NV) {
+    const int nt = S.T - t0 < NV ? S.T - t0 : NV;
+    const float* vin[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) vin[v] = S.attn_o + (size_t)(t0 + (v < nt ? v : 0)) * NI;
+    const uint8_t* srow[R] = {};
+    for (int blk = gw; blk * R < L.H; blk += nw) {
+      const int r0 = blk * R;
+      const uint8_t* wrow[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) wrow[r] = L.wo + (size_t)(r0 + r) * rb;
+      float acc[R][NV];
+      wave_gemv<DT, R, NV>(wrow, srow, NI, vin, nt, nullptr, acc);
+      store_results<R, NV>(acc, nt, [&](int r, int v, float val) {
+        const size_t o = (size_t)(t0 + v) * L.H + r0 + r;
+        h[o] = x[o] + val;
+      });
+    }
+  }
+}
+
+// ----------------------------------------------------------- router
+// u = h * rstd * ffn_norm (written), logits[t][e] = rstd[t] * sum_c wr[e][c] h[t][c] g[c]
+template <int DT, int NV>
+__device__ void phase_router(const LayerArgs& L, const StepArgs& S, const float* h, const float* rs,
+                             int vb, int nvb) {
+  constexpr int R = DenseRows<NV>::R;
+  // u, split over blocks by float4 groups
+  const int n4 = S.T * L.H / 4;
+  for (int i = vb * blockDim.x + threadIdx.x; i < n4; i += nvb * blockDim.x) {
+    const int t = (i * 4) / L.H, c = i * 4 - ((i * 4) / L.H) * L.H;
+    v4f a = *reinterpret_cast<const v4f*>(h + (size_t)t * L.H + c);
+    v4f g = *reinterpret_cast<const v4f*>(L.ffn_norm + c);
+    const float r = rs[t];
+    *reinterpret_cast<v4f*>(S.u + (size_t)t * L.H + c) =
+        v4f{a.x * r * g.x, a.y * r * g.y, a.z * r * g.z, a.w * r * g.w};
+  }
+  const size_t rb = dense_row_bytes(DT, L.H);
+  const int gw = vb * kWaves + wave_id(), nw = nvb * kWaves;
+  for (int t0 = 0; t0 < S.T; t0 += NV) {
+    const int nt = S.T - t0 < NV ? S.T - t0 : NV;
+    const float* vin[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) vin[v] = h + (size_t)(t0 + (v < nt ? v : 0)) * L.H;
+    const uint8_t* srow[R] = {};
+    for (int blk = gw; blk * R < L.E; blk += nw) {
+      const int r0 = blk * R;
+      const uint8_t* wrow[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) wrow[r] = L.wr + (size_t)(r0 + r < L.E ? r0 + r : r0) * rb;
+      float acc[R][NV];
+      wave_gemv<DT, R, NV>(wrow, srow, L.H, vin, nt, L.ffn_norm, acc);
+      store_results<R, NV>(acc, nt, [&](int r, int v, float val) {
+        if (r0 + r < L.E) S.logits[(size_t)(t0 + v) * L.E + r0 + r] = val * rs[t0 + v];
+      });
+    }
+  }
+}
+
+// ------------------------------------------------------------- top-k
+// One wave per token: k rounds of a wave-wide arg-max under the order
+// (logit descending, expert index ascending); weights = softmax over the
+// selected logits.
+__device__ inline bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__device__ void phase_topk(const LayerArgs& L, const StepArgs& S, int* topk_out, int vb, int nvb) {
+  const int ln = lane_id();
+  for (int t = vb * kWaves + wave_id(); t < S.T; t += nvb * kWaves) {
+    float v[4];
+    bool taken[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = ln + 64 * i;
+      v[i] = e < L.E ? S.logits[(size_t)t * L.E + e] : 0.f;
+      taken[i] = !(e < L.E) || (v[i] != v[i]);  // absent or NaN
+    }
+    float v0 = 0.f, den = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+      if (k >= L.K) break;
+      float bv = 0.f;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = ln + 64 * i;
+        if (!taken[i] && (bi == 0x7fffffff || better(v[i], e, bv, bi))) { bv = v[i]; bi = e; }
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) { bv = ov; bi = oi; }
+      }
+      if (bi == 0x7fffffff) { bi = 0; bv = -INFINITY; }  // fewer valid logits than k
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (ln + 64 * i == bi) taken[i] = true;
+      if (k == 0) v0 = bv;
+      const float ex = __expf(bv - v0);
+      den += ex;
+      if (ln == 0) {
+        S.idx[t * L.K + k] = bi;
+        S.wts[t * L.K + k] = ex;
+        if (topk_out) topk_out[t * L.K + k] = bi;
+      }
+    }
+    if (ln == 0) {
+      const float inv = 1.0f / den;
+      for (int k = 0; k < L.K; ++k) S.wts[t * L.K + k] *= inv;
+    }
+  }
+}
+
+// ------------------------------------------------------ expert union
+// Distinct selected experts in ascending order, and per expert the slots
+// (t * K + j) routed to it in ascending order.  Built identically by every
+// workgroup from idx.
+struct Union {
+  int n;                       // distinct experts
+  int list[kMaxExperts];       // expert ids
+  int off[kMaxExperts + 1];    // slot ranges in `slots`
+  int start[kMaxExperts];      // per expert id: first position in slots
+  int slots[kMaxTok * kMaxTopK];
+};
+
+__device__ inline void build_union(const int* idx, int T, int K, int E, Union* U) {
+  const int S = T * K;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) U->start[e] = 0;
+  __syncthreads();
+  for (int s = threadIdx.x; s < S; s += blockDim.x) {
+    const int e = idx[s];
+    if (e >= 0 && e < E) atomicAdd(&U->start[e], 1);
+  }
+  __syncthreads();
+  if (wave_id() == 0) {
+    const int ln = lane_id();
+    int c[4], nz = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = ln * 4 + i;
+      c[i] = e < E ? U->start[e] : 0;
+      nz += c[i] > 0;
+      tot += c[i];
+    }
+    int inz = nz, itot = tot;  // inclusive scans over lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int a = __shfl_up(inz, off, 64), bsum = __shfl_up(itot, off, 64);
+      if (ln >= off) { inz += a; itot += bsum; }
+    }
+    int pnz = inz - nz, ptot = itot - tot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = ln * 4 + i;
+      if (e < E) {
+        if (c[i] > 0) {
+          U->list[pnz] = e;
+          U->off[pnz] = ptot;
+          ++pnz;
+        }
+        U->start[e] = ptot;
+        ptot += c[i];
+      }
+    }
+    if (ln == 63) { U->n = inz; U->off[inz] = itot; }
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < S; s += blockDim.x) {
+    const int e = idx[s];
+    if (e < 0 || e >= E) continue;
+    int rank = 0;
+    for (int q = 0; q < s; ++q) rank += idx[q] == e;
+    U->slots[U->start[e] + rank] = s;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// ------------------------------------------------------------ gate/up
+// act[s][f] = silu(gate_e[f] . u[t]) * (up_e[f] . u[t]) for slot s = t*K + j
+// routed to expert e.  Work items: (expert of the union, block of R rows);
+// both matrices' rows stream once for all of the expert's tokens.
+template <int DT, int NVMAX>
+__device__ void phase_gateup(const LayerArgs& L, const StepArgs& S, const Union* U, int vb, int nvb) {
+  constexpr int R = 4;
+  const int nrb = L.F / R;
+  const int n_items = U->n * nrb;
+  const size_t rb = expert_row_bytes(DT, L.H);
+  const size_t sb = (size_t)L.H / 16;
+  for (int item = vb * kWaves + wave_id(); item < n_items; item += nvb * kWaves) {
+    const int ui = item / nrb, rblk = item - (item / nrb) * nrb;
+    const int e = U->list[ui];
+    const int s0 = U->off[ui], ns = U->off[ui + 1] - s0;
+    const int f0 = rblk * R;
+    const float ggs = DT == kNVFP4 ? L.gg[e] : 1.f;
+    const float gus = DT == kNVFP4 ? L.gu[e] : 1.f;
+    for (int sg = 0; sg < ns; sg += NVMAX) {
+      const int nv = ns - sg < NVMAX ? ns - sg : NVMAX;
+      nv_dispatch<NVMAX>(nv, [&](auto nvc) {
+        constexpr int NV = decltype(nvc)::value;
+        const float* vin[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          vin[v] = S.u + (size_t)(U->slots[s0 + sg + (v < nv ? v : 0)] / L.K) * L.H;
+        const uint8_t* wrow[2 * R];
+        const uint8_t* srow[2 * R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const size_t row = (size_t)e * L.F + f0 + r;
+          wrow[r] = L.wg + row * rb;
+          wrow[R + r] = L.wu + row * rb;
+          srow[r] = DT == kNVFP4 ? L.sg + row * sb : nullptr;
+          srow[R + r] = DT == kNVFP4 ? L.su + row * sb : nullptr;
+        }
+        float acc[2 * R][NV];
+        wave_gemv<DT, 2 * R, NV>(wrow, srow, L.H, vin, nv, nullptr, acc);
+        float res[R][NV];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int v = 0; v < NV; ++v) res[r][v] = silu(acc[r][v] * ggs) * (acc[R + r][v] * gus);
+        store_results<R, NV>(res, nv, [&](int r, int v, float val) {
+          S.act[(size_t)U->slots[s0 + sg + v] * L.F + f0 + r] = val;
+        });
+      });
+    }
+  }
+}
+
+// -------------------------------------------------------------- down
+// out[t][c] = h[t][c] + sum_j wts[t][j] * (down_e[c] . act[t*K + j]), e = idx[t][j],
+// summed in slot order.  Work items: blocks of R output rows; each streams
+// those rows of every expert in the union once.
+template <int DT, int NVMAX>
+__device__ void phase_down(const LayerArgs& L, const StepArgs& S, const Union* U, const float* h,
+                           float* out, float* ybuf_all, int vb, int nvb) {
+  constexpr int R = 4;
+  const int TK = S.T * L.K;
+  float* ybuf = ybuf_all + (size_t)wave_id() * TK * R;
+  const size_t rb = expert_row_bytes(DT, L.F);
+  const size_t sb = (size_t)L.F / 16;
+  const int ln = lane_id();
+  for (int blk = vb * kWaves + wave_id(); blk * R < L.H; blk += nvb * kWaves) {
+    const int c0 = blk * R;
+    for (int i = ln; i < TK * R; i += 64) ybuf[i] = 0.f;
+    wave_lds_sync();
+    for (int ui = 0; ui < U->n; ++ui) {
+      const int e = U->list[ui];
+      const int s0 = U->off[ui], ns = U->off[ui + 1] - s0;
+      const float gds = DT == kNVFP4 ? L.gd[e] : 1.f;
+      for (int sg = 0; sg < ns; sg += NVMAX) {
+        const int nv = ns - sg < NVMAX ? ns - sg : NVMAX;
+        nv_dispatch<NVMAX>(nv, [&](auto nvc) {
+          constexpr int NV = decltype(nvc)::value;
+          const float* vin[NV];
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            vin[v] = S.act + (size_t)U->slots[s0 + sg + (v < nv ? v : 0)] * L.F;
+          const uint8_t* wrow[R];
+          const uint8_t* srow[R];
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const size_t row = (size_t)e * L.H + c0 + r;
+            wrow[r] = L.wd + row * rb;
+            srow[r] = DT == kNVFP4 ? L.sd + row * sb : nullptr;
+          }
+          float acc[R][NV];
+          wave_gemv<DT, R, NV>(wrow, srow, L.F, vin, nv, nullptr, acc);
+          store_results<R, NV>(acc, nv, [&](int r, int v, float val) {
+            ybuf[U->slots[s0 + sg + v] * R + r] = val * gds;
+          });
+        });
+      }
+    }
+    wave_lds_sync();
+    for (int i = ln; i < S.T * R; i += 64) {
+      const int t = i / R, r = i - (i / R) * R;
+      const size_t o = (size_t)t * L.H + c0 + r;
+      float acc = h[o];
+      for (int j = 0; j < L.K; ++j) acc += S.wts[t * L.K + j] * ybuf[(t * L.K + j) * R + r];
+      out[o] = acc;
+    }
+    wave_lds_sync();
+  }
+}
+
+}  // namespace msk
