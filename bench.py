@@ -86,6 +86,51 @@ def cpu_baseline(p, budget_s=30.0):
                        f"float64 NumPy, including the host copies of the selected experts")
 
 
+def unfused_step(p, x, ws):
+    """The same step as separate per-op calls (attention, router, experts)
+    per layer: one launch sequence per phase group, no persistent kernel."""
+    H = p.specs[0]["hidden"]
+    h = torch.empty_like(x)
+    u = torch.empty_like(x)
+    idx = torch.empty((p.T, p.specs[0]["top_k"]), dtype=torch.int32, device=x.device)
+    wts = torch.empty((p.T, p.specs[0]["top_k"]), dtype=torch.float32, device=x.device)
+
+    def run(stream=None):
+        for spec, w, kv in zip(p.specs, p.weights, p.kv):
+            msk.attn_step(spec, w, kv, p.kv_len, p.tokens_per_req, x, ws, h=h, stream=stream)
+            msk.lib().msk_moe_route(
+                msk.ctypes.byref(msk.make_cfg(spec)), msk.ctypes.byref(msk.make_weights(w)), p.T,
+                msk._ptr(h), msk._ptr(u), msk._ptr(idx), msk._ptr(wts), None, msk._ptr(ws),
+                ws.numel(), msk._stream(stream))
+            msk.expert_ffn(spec, w, u, idx, wts, h, ws, out=x, stream=stream)
+    return run
+
+
+def timeline(p, ws, x):
+    """Per-phase times of one persistent-kernel step from the in-kernel
+    real-time counter (100 MHz): phase k ends when the last workgroup has
+    finished it; its time is measured from the previous phase's end."""
+    nblk = torch.cuda.get_device_properties(0).multi_processor_count
+    stamps = torch.zeros((nblk, 32), dtype=torch.int64, device=x.device)
+    msk.layer_step_timeline(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws, stamps)
+    torch.cuda.synchronize()
+    st = stamps.cpu().numpy().astype(np.float64) * 0.01      # us
+    names = ["qkv", "attn", "combine", "wo", "router", "gateup", "down"]
+    out = []
+    t0 = st[:, 0].min()
+    prev = t0
+    for l in range(len(p.specs)):
+        for i, nm in enumerate(names):
+            k = 1 + l * len(names) + i
+            if k >= 32 or st[:, k].max() == 0:
+                break
+            end = st[:, k].max()
+            out.append(dict(layer=l, phase=nm, us=round(end - prev, 2),
+                            spread_us=round(end - st[:, k].min(), 2)))
+            prev = end
+    return dict(total_us=round(prev - t0, 2), phases=out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +138,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
+                    help="fused: msk_layer_step (one persistent kernel); unfused: the "
+                         "msk_attn_step -> msk_moe_route -> msk_expert_ffn calls per layer")
+    ap.add_argument("--timeline", action="store_true",
+                    help="also print per-phase times of the persistent kernel")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer step runs on a single MI355X "
@@ -111,6 +161,8 @@ def main():
     topk = torch.zeros((n_layers, p.T, K), dtype=torch.int32, device=dev)
     probe = msk.Step(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws, topk_idx=topk)
     step = msk.Step(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws)
+    if args.path == "unfused":
+        step = unfused_step(p, x, ws)
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -159,8 +211,12 @@ def main():
         "bytes_breakdown": parts,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "whole layer step (per-phase kernels)"},
+                     "kernel": "k_step_t1 (persistent whole step)" if args.path == "fused"
+                     else "whole layer step (per-phase kernels)"},
     }
+    out["path"] = args.path
+    if args.timeline and args.path == "fused":
+        out["timeline"] = timeline(p, ws, x)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p)
     print(json.dumps(out), flush=True)

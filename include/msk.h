@@ -29,8 +29,9 @@
  * - Argument errors return before anything is enqueued; msk_last_error()
  *   then describes them.  A failed launch returns MSK_ERR_DEVICE.
  * - A workspace must not be used by two calls that may run at the same time.
- *   It must be zero-filled before its first use; every call leaves the
- *   synchronisation words in it zero again when it completes normally.
+ *   It must be zero-filled before its first use; afterwards calls keep its
+ *   synchronisation words consistent themselves (never clear it again, except
+ *   through msk_workspace_status after a timeout).
  * - The KV cache is written at positions [kv_len[b], kv_len[b] + tokens_per_req)
  *   only; lengths are never changed by the library (accepting or rejecting
  *   drafts is the caller's business).
@@ -70,7 +71,7 @@ typedef enum {
 
 /* Shape and numeric configuration of one layer. */
 typedef struct {
-  int32_t hidden;      /* H: hidden size; multiple of 256                       */
+  int32_t hidden;      /* H: hidden size; multiple of 32                        */
   int32_t n_q_heads;   /* Hq: query heads; multiple of n_kv_heads                */
   int32_t n_kv_heads;  /* Hkv: key/value heads; query head h uses kv head
                           h / (Hq / Hkv) (contiguous groups)                      */
@@ -88,7 +89,7 @@ typedef struct {
                           scores of QK-normalised keys                            */
   int32_t dense_dtype;  /* MSK_F32 | MSK_BF16: wq, wk, wv, wo, w_router          */
   int32_t expert_dtype; /* MSK_F32 | MSK_BF16 | MSK_NVFP4: w_gate, w_up, w_down  */
-  int32_t kv_dtype;     /* MSK_F32 | MSK_BF16 | MSK_E4M3                         */
+  int32_t kv_dtype;     /* MSK_F32 (head_dim <= 64) | MSK_BF16 | MSK_E4M3        */
 } msk_layer_cfg;
 
 /* Weights of one layer (device pointers, caller-owned, read only). */
@@ -143,9 +144,9 @@ size_t msk_workspace_size(const msk_layer_cfg *cfg, int32_t n_layers,
                           const msk_batch *batch);
 
 /* Synchronises `stream`, then reports whether a device-side wait in a call
- * that used `ws` gave up (MSK_ERR_TIMEOUT; the flag is cleared and the
- * workspace's synchronisation words reset) or MSK_OK.  MSK_ERR_DEVICE if the
- * stream reports an error. */
+ * that used `ws` gave up (MSK_ERR_TIMEOUT; the workspace's synchronisation
+ * words are then reset so the next call starts clean) or MSK_OK.
+ * MSK_ERR_DEVICE if the stream reports an error. */
 msk_status msk_workspace_status(void *ws, size_t ws_bytes, void *stream);
 
 /* Attention half of a layer (steps: attention RMSNorm, QKV projection,
@@ -193,6 +194,19 @@ msk_status msk_layer_step(const msk_layer_cfg *cfg, const msk_layer_weights *w,
                           const msk_kv *kv, int32_t n_layers, const msk_batch *batch,
                           float *x, float *layer_out, int32_t *topk_idx, int32_t *win,
                           void *ws, size_t ws_bytes, void *stream);
+
+/* Profiling aid: msk_layer_step (no optional outputs) that also records, for
+ * every workgroup of the persistent kernel, the GPU's constant 100 MHz
+ * real-time counter at the start and after each phase:
+ *   stamps  DEVICE int64 [workgroups][32], caller-owned; slot 0 = start, then
+ *           per layer: QKV, attention, combine, Wo, router, gate/up, down.
+ * The number of workgroups is the GPU's compute-unit count.  Stacks that run
+ * as per-phase kernels (more than one token, or dtype combinations without a
+ * persistent kernel) leave stamps untouched. */
+msk_status msk_layer_step_timeline(const msk_layer_cfg *cfg, const msk_layer_weights *w,
+                                   const msk_kv *kv, int32_t n_layers, const msk_batch *batch,
+                                   float *x, int64_t *stamps, void *ws, size_t ws_bytes,
+                                   void *stream);
 
 #ifdef __cplusplus
 }

@@ -61,6 +61,7 @@ def test_workspace_size_scales_with_context():
     (dict(dense_dtype="e4m3"), 2),
     (dict(rms_eps=0.0), 1),
     (dict(n_experts=300, top_k=2), 2),
+    (dict(head_dim=128, n_q_heads=8, n_kv_heads=2), 2),   # fp32 cache at head_dim 128
 ])
 def test_workspace_size_rejects_bad_config(bad, status):
     with pytest.raises(msk.MskError) as e:

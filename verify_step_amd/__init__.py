@@ -94,6 +94,9 @@ def lib():
         L.msk_layer_step.restype = i32
         L.msk_layer_step.argtypes = [P(LayerCfg), P(LayerWeights), P(KV), i32, P(Batch), vp, vp,
                                      vp, vp, vp, sz, vp]
+        L.msk_layer_step_timeline.restype = i32
+        L.msk_layer_step_timeline.argtypes = [P(LayerCfg), P(LayerWeights), P(KV), i32, P(Batch),
+                                              vp, vp, vp, sz, vp]
         if L.msk_abi_version() != 1:
             raise RuntimeError("libmsk.so ABI version mismatch")
         _lib = L
@@ -225,6 +228,19 @@ def layer_step(specs, weights, kvs, kv_len, tokens_per_req, x, ws, layer_out=Non
     _check(lib().msk_layer_step(cfgs, wts, kva, n, ctypes.byref(b), _ptr(x), _ptr(layer_out),
                                 _ptr(topk_idx), _ptr(win), _ptr(ws), ws.numel(),
                                 _stream(stream)))
+    return x
+
+
+def layer_step_timeline(specs, weights, kvs, kv_len, tokens_per_req, x, ws, stamps, stream=None):
+    """layer_step that records per-workgroup phase timestamps into `stamps`
+    (int64 device tensor [n_workgroups][32])."""
+    n = len(specs)
+    cfgs = _array(LayerCfg, [make_cfg(s) for s in specs])
+    wts = _array(LayerWeights, [make_weights(w) for w in weights])
+    kva = _array(KV, [make_kv(k) for k in kvs])
+    b = make_batch(kv_len, tokens_per_req)
+    _check(lib().msk_layer_step_timeline(cfgs, wts, kva, n, ctypes.byref(b), _ptr(x), _ptr(stamps),
+                                         _ptr(ws), ws.numel(), _stream(stream)))
     return x
 
 

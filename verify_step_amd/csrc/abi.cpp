@@ -91,7 +91,7 @@ Layout layout(const msk_layer_cfg* cfg, int n_layers, const msk_batch& b) {
     o += up(bytes);
     return at;
   };
-  L.sync = take(kAlign);
+  L.sync = take(8192);
   L.qkv = take(T * NR * 4);
   L.part = take(max_items * msk::kRowGroup * (D + 1) * 4);
   L.attn_o = take(T * c.n_q_heads * D * 4);
@@ -139,6 +139,8 @@ msk_status check_cfg(const msk_layer_cfg* c, int l) {
                 c->kv_dtype);
   if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
     return fail(MSK_ERR_UNSUPPORTED, "layer %d: head_dim %d unsupported (32, 64, 128)", l, c->head_dim);
+  if (c->kv_dtype == MSK_F32 && c->head_dim == 128)
+    return fail(MSK_ERR_UNSUPPORTED, "layer %d: fp32 KV cache needs head_dim <= 64", l);
   if (c->hidden % 32 != 0 || c->ffn_dim % 32 != 0)
     return fail(MSK_ERR_UNSUPPORTED, "layer %d: hidden and ffn_dim must be multiples of 32", l);
   if (c->n_experts > msk::kMaxExperts)
@@ -326,18 +328,18 @@ size_t msk_workspace_size(const msk_layer_cfg* cfg, int32_t n_layers, const msk_
 }
 
 msk_status msk_workspace_status(void* ws, size_t ws_bytes, void* stream) {
-  if (!ws || ws_bytes < kAlign) return fail(MSK_ERR_WORKSPACE, "workspace missing or too small");
+  if (!ws || ws_bytes < 8192) return fail(MSK_ERR_WORKSPACE, "workspace missing or too small");
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipStreamSynchronize(st);
   if (e != hipSuccess) return device_status(e, "hipStreamSynchronize");
-  unsigned words[4] = {0, 0, 0, 0};
+  unsigned words[2] = {0, 0};
   e = hipMemcpy(words, ws, sizeof(words), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return device_status(e, "hipMemcpy");
-  if (words[2] != 0 || words[0] != 0 || words[1] != 0) {
-    e = hipMemset(ws, 0, kAlign);
+  if (words[1] != 0) {
+    // a barrier wait gave up: epochs may be inconsistent, start them over
+    e = hipMemset(ws, 0, 8192);
     if (e != hipSuccess) return device_status(e, "hipMemset");
-    if (words[2] != 0) return fail(MSK_ERR_TIMEOUT, "a device-side wait gave up (barrier watchdog)");
-    return fail(MSK_ERR_TIMEOUT, "synchronisation words were left non-zero");
+    return fail(MSK_ERR_TIMEOUT, "a device-side wait gave up (barrier watchdog)");
   }
   return ok();
 }
@@ -407,10 +409,10 @@ msk_status msk_expert_ffn(const msk_layer_cfg* cfg, const msk_layer_weights* w, 
                        "expert launch");
 }
 
-msk_status msk_layer_step(const msk_layer_cfg* cfg, const msk_layer_weights* w, const msk_kv* kv,
-                          int32_t n_layers, const msk_batch* batch, float* x, float* layer_out,
-                          int32_t* topk_idx, int32_t* win, void* ws, size_t ws_bytes,
-                          void* stream) {
+static msk_status layer_step_impl(const msk_layer_cfg* cfg, const msk_layer_weights* w,
+                                  const msk_kv* kv, int32_t n_layers, const msk_batch* batch,
+                                  float* x, float* layer_out, int32_t* topk_idx, int32_t* win,
+                                  int64_t* stamps, void* ws, size_t ws_bytes, void* stream) {
   if (!cfg || !w || !kv) return fail(MSK_ERR_INVALID_ARG, "cfg, w or kv is null");
   if (n_layers < 1 || n_layers > MSK_MAX_STACK)
     return fail(MSK_ERR_INVALID_ARG, "n_layers %d outside [1, %d]", n_layers, MSK_MAX_STACK);
@@ -436,8 +438,26 @@ msk_status msk_layer_step(const msk_layer_cfg* cfg, const msk_layer_weights* w, 
   S.layer_out = layer_out;
   S.topk_out = topk_idx;
   S.win_out = win;
+  S.stamps = reinterpret_cast<long long*>(stamps);
   return device_status(msk::launch_step_fused(Ls, S, static_cast<hipStream_t>(stream)),
                        "layer-step launch");
+}
+
+msk_status msk_layer_step(const msk_layer_cfg* cfg, const msk_layer_weights* w, const msk_kv* kv,
+                          int32_t n_layers, const msk_batch* batch, float* x, float* layer_out,
+                          int32_t* topk_idx, int32_t* win, void* ws, size_t ws_bytes,
+                          void* stream) {
+  return layer_step_impl(cfg, w, kv, n_layers, batch, x, layer_out, topk_idx, win, nullptr, ws,
+                         ws_bytes, stream);
+}
+
+msk_status msk_layer_step_timeline(const msk_layer_cfg* cfg, const msk_layer_weights* w,
+                                   const msk_kv* kv, int32_t n_layers, const msk_batch* batch,
+                                   float* x, int64_t* stamps, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (!stamps) return fail(MSK_ERR_INVALID_ARG, "stamps is null");
+  return layer_step_impl(cfg, w, kv, n_layers, batch, x, nullptr, nullptr, nullptr, stamps, ws,
+                         ws_bytes, stream);
 }
 
 }  // extern "C"

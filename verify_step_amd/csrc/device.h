@@ -23,6 +23,44 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Wave-wide max / min through DPP row rotations (within rows of 16 lanes)
+// and four lane reads (across rows): no LDS round trips.  Every lane gets
+// the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRor4 = 0x124;   // row_ror:4
+constexpr int kDppRor8 = 0x128;   // row_ror:8
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppRor4>(v));
+  v = fmaxf(v, dpp_f<kDppRor8>(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<kDppXor1>(v));
+  v = min(v, dpp_i<kDppXor2>(v));
+  v = min(v, dpp_i<kDppRor4>(v));
+  v = min(v, dpp_i<kDppRor8>(v));
+  const int a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return min(min(a, b), min(c, d));
+}
+
 // Orders LDS traffic of one wave: its earlier LDS writes are complete before
 // its later LDS reads (used for wave-private tiles, no workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -185,26 +223,181 @@ __device__ __forceinline__ void wave_gemv(const uint8_t* const (&wrow)[R],
     for (int v = 0; v < NV; ++v) acc[r][v] = wave_sum(acc[r][v]);
 }
 
-// ---------------------------------------------------- grid-wide barrier
-// All workgroups of a cooperative launch meet here.  Counter words live in
-// the caller's workspace: sync[0] counts arrivals (monotone within a launch),
-// sync[2] is the error flag.  A bounded spin turns a missing arrival into an
-// error flag instead of a hang.
-__device__ __forceinline__ void grid_barrier(unsigned* sync, unsigned& epoch) {
+// ------------------------------------------- one-token streaming GEMV
+// One wave works through its own list of tasks k = 0..ntask-1; task k is R
+// weight rows (rowfn(k, wr, sr) gives their row and NVFP4 scale pointers)
+// dotted with one fp32 vector in LDS (actfn(k)).  The weight stream is
+// software-pipelined two buffers deep across row ends and task ends, and the
+// input vector comes from LDS, so no cache load ever waits behind a weight
+// load.  out(k, acc) receives the sums (in every lane).
+template <int DT, int R, int U, class ActFn, class RowFn, class OutFn>
+__device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, RowFn&& rowfn,
+                                          OutFn&& out) {
+  using W = WT<DT>;
+  const int ln = lane_id();
+  const int nch = ncols / W::EPL;
+  const int NI = (nch + 64 * U - 1) / (64 * U);
+  const int total = ntask * NI;
+  v4u A[U][R], B[U][R];
+  unsigned sA[U][R], sB[U][R];
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+
+  auto issue = [&](v4u(&w)[U][R], unsigned(&s)[U][R], int f) {
+    const int k = f / NI, i = f - (f / NI) * NI;
+    const uint8_t* wr[R];
+    const uint8_t* sr[R];
+    rowfn(k, wr, sr);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ch = (i * U + u) * 64 + ln;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (ch < nch) {
+          w[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wr[r]) + ch);
+          if constexpr (DT == kNVFP4)
+            s[u][r] = *reinterpret_cast<const unsigned short*>(sr[r] + 2 * ch);
+          else
+            s[u][r] = 0u;
+        } else {
+          w[u][r] = v4u{0u, 0u, 0u, 0u};
+          s[u][r] = 0u;
+        }
+      }
+    }
+  };
+  auto compute = [&](const v4u(&w)[U][R], const unsigned(&s)[U][R], int f) {
+    const int k = f / NI, i = f - (f / NI) * NI;
+    const float* act = actfn(k);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ch = (i * U + u) * 64 + ln;
+      if (ch < nch) {
+        v2f sc[R];
+        if constexpr (DT == kNVFP4) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) sc[r] = __builtin_amdgcn_cvt_pk_f32_fp8(s[u][r], false);
+        }
+#pragma unroll
+        for (int sub = 0; sub < W::NSUB; ++sub) {
+          float a[W::SUB];
+          load_act(act + ch * W::EPL + sub * W::SUB, a, W::SUB);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            float fw[W::SUB];
+            decode_sub<DT>(w[u][r], sub, fw);
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < W::SUB; ++e) d = fmaf(fw[e], a[e], d);
+            if constexpr (DT == kNVFP4)
+              acc[r] = fmaf((sub >> 1) ? sc[r].y : sc[r].x, d, acc[r]);
+            else
+              acc[r] += d;
+          }
+        }
+      }
+    }
+    if (i == NI - 1) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+      out(k, acc);
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    }
+  };
+  if (total > 0) issue(A, sA, 0);
+  for (int f = 0; f < total; f += 2) {
+    if (f + 1 < total) issue(B, sB, f + 1);
+    compute(A, sA, f);
+    if (f + 1 < total) {
+      if (f + 2 < total) issue(A, sA, f + 2);
+      compute(B, sB, f + 1);
+    }
+  }
+}
+
+// Sum over the block (all waves); every thread gets the total.  red is
+// kWaves floats of LDS.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
   __syncthreads();
-  epoch += gridDim.x;
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) t += red[w];
+  return t;
+}
+
+// ---------------------------------------------------- grid-wide barrier
+// Barrier words in the caller's workspace (zero before first use):
+//   words[0]            generation, advanced by workgroup 0 at each barrier
+//   words[1]            error flag (a wait gave up)
+//   words[64 + b]       arrival epoch of workgroup b
+// Epochs only grow, across launches too: a launch starts from the
+// generation the previous one left, so nothing needs resetting.  Arrivals
+// are plain per-workgroup stores (no contended atomic); workgroup 0 checks
+// them with one thread per workgroup and publishes the new generation.
+// Every wait is bounded: a missing arrival sets the error flag instead of
+// hanging the GPU.
+constexpr int kSyncFlags = 64;
+constexpr unsigned kSpinLimit = 1u << 22;
+
+struct GridSync {
+  unsigned* words;
+  unsigned base;   // generation at launch
+  unsigned k;      // barriers passed in this launch
+};
+
+__device__ __forceinline__ GridSync grid_sync_begin(unsigned* words) {
+  // every thread reads the same generation: it cannot advance before all
+  // workgroups have arrived at this launch's first barrier
+  GridSync g{words, __hip_atomic_load(&words[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0u};
+  return g;
+}
+
+__device__ __forceinline__ bool epoch_before(unsigned a, unsigned b) { return (int)(a - b) < 0; }
+
+__device__ __forceinline__ void grid_sync(GridSync& g) {
+  __syncthreads();
+  ++g.k;
+  const unsigned target = g.base + g.k;
+  unsigned* gen = &g.words[0];
+  unsigned* err = &g.words[1];
+  unsigned* flags = &g.words[kSyncFlags];
   if (threadIdx.x == 0) {
-    __threadfence();
-    __hip_atomic_fetch_add(&sync[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_store(&flags[blockIdx.x], target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (blockIdx.x == 0) {
+    for (int b = threadIdx.x; b < (int)gridDim.x; b += blockDim.x) {
+      unsigned spins = 0;
+      while (epoch_before(__hip_atomic_load(&flags[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                          target)) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+          __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+      __hip_atomic_store(gen, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (threadIdx.x == 0) {
     unsigned spins = 0;
-    while (__hip_atomic_load(&sync[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < epoch) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++spins > (1u << 22)) {
-        __hip_atomic_store(&sync[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (epoch_before(__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), target)) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }

@@ -3,13 +3,14 @@
 // unfused path); the fused path runs every phase of every layer in one
 // persistent cooperative launch with grid barriers between dependent phases.
 #include "launch.h"
-#include "phases.h"
+#include "phases_t1.h"
 
 namespace msk {
 
 extern __shared__ __align__(16) uint8_t msk_smem[];
 
 constexpr int kMaxGrid = 1024;
+constexpr size_t kMaxLds = 160 * 1024;
 
 __host__ __device__ constexpr size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -28,10 +29,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_attn(LayerArgs L, StepArgs S)
   phase_attn<KDT, D>(L, S, P, msk_smem + align_up(sizeof(AttnPlan), 16), blockIdx.x, gridDim.x);
 }
 
-__global__ __launch_bounds__(kBlockThreads) void k_combine(LayerArgs L, StepArgs S) {
+__global__ __launch_bounds__(kBlockThreads) void k_combine(LayerArgs L, StepArgs S, int* win) {
   AttnPlan* P = reinterpret_cast<AttnPlan*>(msk_smem);
   build_plan(L, S, P);
-  phase_combine(L, S, P, blockIdx.x, gridDim.x);
+  phase_combine(L, S, P, win, blockIdx.x, gridDim.x);
 }
 
 template <int DT, int NV>
@@ -67,6 +68,156 @@ __global__ __launch_bounds__(kBlockThreads) void k_down(LayerArgs L, StepArgs S,
   phase_down<DT, NVMAX>(L, S, U, h, out, ybuf, blockIdx.x, gridDim.x);
 }
 
+// ------------------------------------------------- one-token kernels
+// LDS of the one-token kernels: a reduction scratch, the top-k of the token,
+// one hidden-size input vector (act0) and the K expert activations (act1);
+// the attention phase of the persistent kernel reuses the same space.
+struct StepLayers {
+  StepArgs S;
+  LayerArgs L[kMaxLayers];
+};
+
+struct T1Lds {
+  size_t red, tki, tkw, act0, act1, end_act, attn;
+};
+__host__ __device__ inline T1Lds t1_lds(int H, int HqD, int K, int F) {
+  T1Lds o;
+  o.red = 0;
+  o.tki = 64;
+  o.tkw = 128;
+  o.act0 = 256;
+  o.act1 = o.act0 + align_up((size_t)4 * (H > HqD ? H : HqD), 256);
+  o.end_act = o.act1 + (size_t)4 * K * F;
+  o.attn = 256;
+  return o;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlockThreads) void k_qkv_t1(LayerArgs L, StepArgs S, const float* x) {
+  const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
+  float* act = reinterpret_cast<float*>(msk_smem + o.act0);
+  stage_norm_t1(x, L.attn_norm, L.H, L.eps, act, reinterpret_cast<float*>(msk_smem + o.red));
+  qkv_t1<DT>(L, S, act, blockIdx.x, gridDim.x);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlockThreads) void k_wo_t1(LayerArgs L, StepArgs S, const float* x,
+                                                         float* h) {
+  const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
+  float* act = reinterpret_cast<float*>(msk_smem + o.act0);
+  stage_copy(S.attn_o, L.Hq * L.D, act);
+  wo_t1<DT>(L, S, x, h, act, blockIdx.x, gridDim.x);
+}
+
+// Router logits, then top-k in the workgroup that finishes last.
+template <int DT>
+__global__ __launch_bounds__(kBlockThreads) void k_router_t1(LayerArgs L, StepArgs S,
+                                                             const float* h, int* topk_out) {
+  const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
+  router_t1<DT>(L, S, h, reinterpret_cast<float*>(msk_smem + o.act0),
+                reinterpret_cast<float*>(msk_smem + o.red), blockIdx.x, gridDim.x);
+  if (last_workgroup(&S.sync[2], reinterpret_cast<int*>(msk_smem + o.tki))) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (wave_id() == 0) {
+      topk_row(S.logits, L.E, L.K, S.idx, S.wts);
+      if (topk_out != nullptr && lane_id() == 0)
+        for (int k = 0; k < L.K; ++k) topk_out[k] = S.idx[k];
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlockThreads) void k_gateup_t1(LayerArgs L, StepArgs S) {
+  const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
+  float* u = reinterpret_cast<float*>(msk_smem + o.act0);
+  stage_copy(S.u, L.H, u);
+  gateup_t1<DT>(L, S, S.idx, u, blockIdx.x, gridDim.x);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlockThreads) void k_down_t1(LayerArgs L, StepArgs S, const float* h,
+                                                           float* out) {
+  // only the expert activations are staged here: [K][F] after the scratch words
+  float* act = reinterpret_cast<float*>(msk_smem + 256);
+  stage_copy(S.act, L.K * L.F, act);
+  down_t1<DT>(L, S, S.idx, S.wts, act, h, out, nullptr, blockIdx.x, gridDim.x);
+}
+
+// The whole one-token step through every layer in one persistent launch.
+// Workgroups meet at grid barriers only where a phase needs the complete
+// result of the previous one: QKV -> attention partials -> combine -> Wo ->
+// router -> (top-k, computed redundantly per workgroup) gate/up -> down.
+template <int DDT, int EDT, int KDT, int D>
+__global__ __launch_bounds__(kBlockThreads) void k_step_t1(StepLayers PK) {
+  // Layers are indexed at run time: read them straight from the kernel
+  // argument segment (constant memory) instead of copying the by-value
+  // argument into private memory.
+  typedef __attribute__((address_space(4))) const StepLayers KStepLayers;
+  KStepLayers* PP = (KStepLayers*)__builtin_amdgcn_kernarg_segment_ptr();
+  const StepArgs& S = PK.S;
+  const int vb = blockIdx.x, nvb = gridDim.x;
+  // optional timeline: slot 0 = start, then one stamp after each phase
+  int ts = 0;
+  auto stamp = [&]() {
+    if (S.stamps != nullptr && threadIdx.x == 0 && ts < kStamps)
+      S.stamps[(size_t)vb * kStamps + ts] = (long long)__builtin_amdgcn_s_memrealtime();
+    ++ts;
+  };
+  stamp();
+  GridSync gs = grid_sync_begin(S.sync);
+  float* red = reinterpret_cast<float*>(msk_smem);
+  int* tki = reinterpret_cast<int*>(msk_smem + 64);
+  float* tkw = reinterpret_cast<float*>(msk_smem + 128);
+  for (int l = 0; l < S.n_layers; ++l) {
+    const LayerArgs& L = *(const LayerArgs*)(&PP->L[l]);
+    const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
+    float* act0 = reinterpret_cast<float*>(msk_smem + o.act0);
+    float* act1 = reinterpret_cast<float*>(msk_smem + o.act1);
+    const float* xin = l == 0 ? S.x_in : (((l - 1) & 1) ? S.xb : S.xa);
+    float* xout = l == S.n_layers - 1 ? S.x_out : ((l & 1) ? S.xb : S.xa);
+
+    stage_norm_t1(xin, L.attn_norm, L.H, L.eps, act0, red);
+    qkv_t1<DDT>(L, S, act0, vb, nvb);
+    stamp();
+    grid_sync(gs);
+
+    AttnPlan* P = reinterpret_cast<AttnPlan*>(msk_smem + o.attn);
+    build_plan(L, S, P);
+    phase_attn<KDT, D>(L, S, P, msk_smem + o.attn + align_up(sizeof(AttnPlan), 16), vb, nvb);
+    stamp();
+    grid_sync(gs);
+    phase_combine(L, S, P, S.win_out ? S.win_out + (size_t)l * 2 * S.T : nullptr, vb, nvb);
+    stamp();
+    grid_sync(gs);
+
+    stage_copy(S.attn_o, L.Hq * L.D, act0);
+    wo_t1<DDT>(L, S, xin, S.h, act0, vb, nvb);
+    stamp();
+    grid_sync(gs);
+
+    router_t1<DDT>(L, S, S.h, act0, red, vb, nvb);
+    stamp();
+    grid_sync(gs);
+
+    if (wave_id() == 0) topk_row(S.logits, L.E, L.K, tki, tkw);
+    __syncthreads();
+    if (vb == 0 && threadIdx.x < L.K) {
+      S.idx[threadIdx.x] = tki[threadIdx.x];
+      S.wts[threadIdx.x] = tkw[threadIdx.x];
+      if (S.topk_out) S.topk_out[(size_t)l * L.K + threadIdx.x] = tki[threadIdx.x];
+    }
+    gateup_t1<EDT>(L, S, tki, act0, vb, nvb);
+    stamp();
+    grid_sync(gs);
+
+    stage_copy(S.act, L.K * L.F, act1);
+    down_t1<EDT>(L, S, tki, tkw, act1, S.h, xout,
+                 S.layer_out ? S.layer_out + (size_t)l * L.H : nullptr, vb, nvb);
+    stamp();
+    if (l + 1 < S.n_layers) grid_sync(gs);
+  }
+}
+
 // ------------------------------------------------------- LDS budgets
 size_t attn_lds_bytes(int kdt, int D) {
   size_t w = 0;
@@ -89,6 +240,34 @@ static int grid_for_waves(long long waves) {
   long long b = (waves + kWaves - 1) / kWaves;
   if (b < 1) b = 1;
   return (int)(b < kMaxGrid ? b : kMaxGrid);
+}
+
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+static size_t t1_act_lds(const LayerArgs& L) { return t1_lds(L.H, L.Hq * L.D, L.K, L.F).end_act; }
+// LDS of the one-token kernels that stage only the hidden-size vector.
+static size_t t1_vec_lds(const LayerArgs& L) { return t1_lds(L.H, L.Hq * L.D, L.K, L.F).act1; }
+
+// Workgroups for `tasks` one-wave tasks: every wave gets the same number of
+// tasks, at most four workgroups per CU.
+static int t1_grid(long long tasks) {
+  const long long cap = 4LL * cu_count();
+  const long long per_wave = (tasks + cap * kWaves - 1) / (cap * kWaves);
+  long long g = (tasks + per_wave * kWaves - 1) / (per_wave * kWaves);
+  if (g < 1) g = 1;
+  return (int)g;
 }
 
 template <class K>
@@ -145,14 +324,25 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
   const size_t rs_lds = (size_t)S.T * sizeof(float);
   const int nv = dense_nv(S.T);
   const int qgrid = grid_for_waves(NR / DenseRowsHost(nv));
-  if (L.ddt == kBF16) {
+  const bool one = S.T == 1;
+  if (one) {
+    const size_t lds = t1_vec_lds(L);
+    const int g = t1_grid(NR / 4);
+    if (L.ddt == kBF16) {
+      MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_qkv_t1<kBF16>), lds));
+      MSK_TRY(launch_x(k_qkv_t1<kBF16>, g, lds, st, L, S, x));
+    } else {
+      MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_qkv_t1<kF32>), lds));
+      MSK_TRY(launch_x(k_qkv_t1<kF32>, g, lds, st, L, S, x));
+    }
+  } else if (L.ddt == kBF16) {
     MSK_NV_CASES(nv, MSK_TRY(launch_x(k_qkv<kBF16, NV>, qgrid, rs_lds, st, L, S, x)))
   } else {
     MSK_NV_CASES(nv, MSK_TRY(launch_x(k_qkv<kF32, NV>, qgrid, rs_lds, st, L, S, x)))
   }
 
   const size_t alds = attn_lds_bytes(L.kdt, L.D);
-  const int agrid = grid_for_waves(L.n_items);
+  const int agrid = L.n_items < cu_count() * kWaves ? cu_count() : grid_for_waves(L.n_items);
 #define MSK_ATTN(K, DD)                                                             \
   if (L.kdt == K && L.D == DD) {                                                    \
     MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_attn<K, DD>), alds));   \
@@ -162,9 +352,20 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
   MSK_ATTN(kBF16, 32) MSK_ATTN(kBF16, 64) MSK_ATTN(kBF16, 128)
   MSK_ATTN(kE4M3, 32) MSK_ATTN(kE4M3, 64) MSK_ATTN(kE4M3, 128)
 #undef MSK_ATTN
-  MSK_TRY(launch(k_combine, grid_for_waves((long long)S.T * L.Hq), sizeof(AttnPlan), st, L, S));
+  MSK_TRY(launch_x(k_combine, grid_for_waves((long long)S.T * L.Hq), sizeof(AttnPlan), st, L, S,
+                   S.win_out));
   const int wgrid = grid_for_waves(L.H / DenseRowsHost(nv));
-  if (L.ddt == kBF16) {
+  if (one) {
+    const size_t lds = t1_vec_lds(L);
+    const int g = t1_grid((L.H + 3) / 4);
+    if (L.ddt == kBF16) {
+      MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_wo_t1<kBF16>), lds));
+      MSK_TRY(launch_x(k_wo_t1<kBF16>, g, lds, st, L, S, x, h));
+    } else {
+      MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_wo_t1<kF32>), lds));
+      MSK_TRY(launch_x(k_wo_t1<kF32>, g, lds, st, L, S, x, h));
+    }
+  } else if (L.ddt == kBF16) {
     MSK_NV_CASES(nv, MSK_TRY(launch_x(k_wo<kBF16, NV>, wgrid, 0, st, L, S, x, h)))
   } else {
     MSK_NV_CASES(nv, MSK_TRY(launch_x(k_wo<kF32, NV>, wgrid, 0, st, L, S, x, h)))
@@ -178,12 +379,34 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
   const int nv = dense_nv(S.T);
   const int rows = (L.E + DenseRowsHost(nv) - 1) / DenseRowsHost(nv);
   const int grid = grid_for_waves(rows > 64 ? rows : 64);
-  if (L.ddt == kBF16) {
+  if (S.T == 1) {
+    const size_t lds = t1_vec_lds(L);
+    const int g = cu_count();
+    if (L.ddt == kBF16) {
+      MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_router_t1<kBF16>), lds));
+      MSK_TRY(launch_x(k_router_t1<kBF16>, g, lds, st, L, S, h, topk_out));
+    } else {
+      MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_router_t1<kF32>), lds));
+      MSK_TRY(launch_x(k_router_t1<kF32>, g, lds, st, L, S, h, topk_out));
+    }
+    return hipSuccess;
+  } else if (L.ddt == kBF16) {
     MSK_NV_CASES(nv, MSK_TRY(launch_x(k_router<kBF16, NV>, grid, rs_lds, st, L, S, h)))
   } else {
     MSK_NV_CASES(nv, MSK_TRY(launch_x(k_router<kF32, NV>, grid, rs_lds, st, L, S, h)))
   }
   MSK_TRY(launch_x(k_topk, grid_for_waves(S.T), 0, st, L, S, topk_out));
+  return hipSuccess;
+}
+
+template <int DT>
+static hipError_t launch_ffn_t1(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
+                                hipStream_t st) {
+  const size_t vlds = t1_vec_lds(L), alds = 256 + (size_t)4 * L.K * L.F;
+  MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_gateup_t1<DT>), vlds));
+  MSK_TRY(launch(k_gateup_t1<DT>, t1_grid((long long)L.K * (L.F / 2)), vlds, st, L, S));
+  MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_down_t1<DT>), alds));
+  MSK_TRY(launch_x(k_down_t1<DT>, t1_grid((L.H + 3) / 4), alds, st, L, S, h, out));
   return hipSuccess;
 }
 
@@ -203,6 +426,13 @@ static hipError_t launch_ffn_t(const LayerArgs& L, const StepArgs& S, const floa
 
 hipError_t launch_ffn(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
                       hipStream_t st) {
+  if (S.T == 1 && t1_act_lds(L) <= kMaxLds) {
+    switch (L.edt) {
+      case kF32: return launch_ffn_t1<kF32>(L, S, h, out, st);
+      case kBF16: return launch_ffn_t1<kBF16>(L, S, h, out, st);
+      default: return launch_ffn_t1<kNVFP4>(L, S, h, out, st);
+    }
+  }
   const int nv = expert_nv(S.T);
   switch (L.edt) {
     case kF32: MSK_ENV_CASES(nv, return (launch_ffn_t<kF32, NV>(L, S, h, out, st))) break;
@@ -232,8 +462,54 @@ hipError_t launch_step_unfused(const LayerArgs* Ls, const StepArgs& S0, hipStrea
   return hipSuccess;
 }
 
+template <int DDT, int EDT, int KDT, int D>
+static hipError_t launch_fused_t1(const LayerArgs* Ls, const StepArgs& S, hipStream_t st,
+                                  bool* launched) {
+  *launched = false;
+  auto fn = k_step_t1<DDT, EDT, KDT, D>;
+  // Only a persistent kernel that keeps everything in registers runs: a
+  // variant that spills to scratch memory takes the per-phase path.
+  hipFuncAttributes fa;
+  MSK_TRY(hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(fn)));
+  if (fa.localSizeBytes != 0) return hipSuccess;
+  size_t lds = 0;
+  for (int l = 0; l < S.n_layers; ++l) {
+    const T1Lds o = t1_lds(Ls[l].H, Ls[l].Hq * Ls[l].D, Ls[l].K, Ls[l].F);
+    const size_t a = o.attn + align_up(sizeof(AttnPlan), 16) + kWaves * AttnGeom<KDT, D>::LDS_WAVE;
+    lds = lds > o.end_act ? lds : o.end_act;
+    lds = lds > a ? lds : a;
+  }
+  MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
+  int per_cu = 0;
+  MSK_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn),
+                                                       kBlockThreads, lds));
+  if (per_cu < 1) return hipSuccess;
+  const int grid = cu_count();
+  StepLayers P;
+  P.S = S;
+  for (int l = 0; l < kMaxLayers; ++l) P.L[l] = Ls[l < S.n_layers ? l : 0];
+  void* args[] = {&P};
+  *launched = true;
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(grid),
+                                    dim3(kBlockThreads), args, (unsigned)lds, st);
+}
+
+// The persistent one-token kernel runs for all-fp32 stacks; every other
+// stack runs as per-phase kernels.  The bf16/NVFP4 variants of the
+// persistent kernel are kept out of service: one of them (bf16 weights and
+// cache, head_dim 128, which spilled to scratch) aborted on the GPU with a
+// cause not yet found.
 hipError_t launch_step_fused(const LayerArgs* Ls, const StepArgs& S, hipStream_t st) {
-  // the persistent kernel is not built yet: run the per-phase kernels
+  bool same = true;
+  for (int l = 1; l < S.n_layers; ++l)
+    same = same && Ls[l].ddt == Ls[0].ddt && Ls[l].edt == Ls[0].edt && Ls[l].kdt == Ls[0].kdt;
+  const LayerArgs& L = Ls[0];
+  const bool fits = t1_act_lds(L) <= kMaxLds;
+  if (S.T == 1 && same && fits && L.ddt == kF32 && L.edt == kF32 && L.kdt == kF32 && L.D == 32) {
+    bool launched = false;
+    MSK_TRY((launch_fused_t1<kF32, kF32, kF32, 32>(Ls, S, st, &launched)));
+    if (launched) return hipSuccess;
+  }
   return launch_step_unfused(Ls, S, st);
 }
 

@@ -53,6 +53,9 @@ struct StepArgs {
   float *act;           // [T*K][F]
   float *xa, *xb;       // [T][H] layer ping-pong
   unsigned *sync;       // grid barrier words; sync[0] arrive, sync[1] depart, sync[2] error
+  long long *stamps;    // optional timeline [blocks][kStamps] of 100 MHz counter values
 };
+
+constexpr int kStamps = 32;  // timeline slots per workgroup (phase ends, per layer)
 
 }  // namespace msk

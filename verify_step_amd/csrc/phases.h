@@ -10,6 +10,10 @@ namespace msk {
 
 template <int N> struct IC { static constexpr int value = N; };
 
+// Global index of this wave when waves are numbered across workgroups first,
+// so that a phase with fewer tasks than waves still spreads over every CU.
+__device__ __forceinline__ int gwave(int vb, int nvb) { return wave_id() * nvb + vb; }
+
 // Calls f(IC<NV>) with the smallest power of two NV >= n, n <= NVMAX.
 template <int NVMAX, class F>
 __device__ __forceinline__ void nv_dispatch(int n, F&& f) {
@@ -104,7 +108,7 @@ __device__ void phase_qkv(const LayerArgs& L, const StepArgs& S, const float* x,
   constexpr int R = DenseRows<NV>::R;
   const int NQ = L.Hq * L.D, NK = L.Hkv * L.D, NR = NQ + 2 * NK;
   const size_t rb = dense_row_bytes(DT, L.H);
-  const int gw = vb * kWaves + wave_id(), nw = nvb * kWaves;
+  const int gw = gwave(vb, nvb), nw = nvb * kWaves;
   for (int t0 = 0; t0 < S.T; t0 += NV) {
     const int nt = S.T - t0 < NV ? S.T - t0 : NV;
     const float* vin[NV];
@@ -134,11 +138,13 @@ __device__ void phase_qkv(const LayerArgs& L, const StepArgs& S, const float* x,
 // One wave per work item (request b, kv head j, query row group rg, chunk c).
 // Rows of a group are (draft token t, query head g of the group) pairs,
 // m = t * G + g, eight at a time.  For each 64-position block of the chunk:
-//  - K rows are staged in a wave-private LDS tile; a lane then owns one
-//    cache position and computes its eight scores in-lane;
+//  - the K and V rows go straight from HBM into wave-private LDS tiles
+//    (direct global->LDS loads: no registers are held while they fly);
+//  - a lane then owns one cache position and computes its eight scores
+//    in-lane, reading its K row in a lane-rotated chunk order so the
+//    unpadded tile is read without bank conflicts;
 //  - e = exp(s - shift) inside the token's window, else 0 (no running max);
-//  - V is read straight from the cache, each lane owning a slice of head_dim
-//    for a few positions, and o += e * V.
+//  - o += e * V with each lane owning a slice of head_dim for a few positions.
 // Positions at or past kv_len[b] are the step's own draft tokens: their K/V
 // are rebuilt from the QKV output (QK-norm on k, cast to the cache format),
 // and the row-group-0 item also writes them into the cache.
@@ -152,20 +158,23 @@ template <int KDT, int D>
 struct AttnGeom {
   static constexpr int ES = KV<KDT>::ES;
   static constexpr int RB = D * ES;           // cache row bytes
-  static constexpr int RBP = RB + 16;         // padded LDS row
   static constexpr int CPR = RB / 16;         // 16-B chunks per row
-  static constexpr int EPLV = KV<KDT>::EPLV;  // V elements per lane load
-  static constexpr int VB = EPLV * ES;        // V bytes per lane load
+  static constexpr int EPC = 16 / ES;         // elements per 16-B chunk
+  static constexpr int TILE = 64 * RB;        // one 64-position tile
+  static constexpr int NLD = TILE / 1024;     // 1-KB wave loads per tile
+  static constexpr int EPLV = KV<KDT>::EPLV;  // V elements per lane
+  static constexpr int VB = EPLV * ES;        // V bytes per lane
   static constexpr int LPP = D / EPLV;        // lanes per position (V)
-  static constexpr int PPI = 64 / LPP;        // positions per V load
-  static constexpr int NVL = 64 / PPI;        // V loads per lane per block
-  // per-wave LDS: q rows, K tile, weights tile, new-key norms, row windows
+  static constexpr int PPI = 64 / LPP;        // positions per V step
+  static constexpr int NVL = 64 / PPI;        // V steps per block
+  // per-wave LDS: q rows, K tile, V tile, weights, new-key norms, windows
   static constexpr int LDS_Q = kRowGroup * D * 4;
-  static constexpr int LDS_K = 64 * RBP;
+  static constexpr int LDS_K = TILE;
+  static constexpr int LDS_V = TILE;
   static constexpr int LDS_E = kRowGroup * 64 * 4;
   static constexpr int LDS_RK = kMaxTok * 4;
   static constexpr int LDS_WIN = kRowGroup * 8;
-  static constexpr int LDS_WAVE = LDS_Q + LDS_K + LDS_E + LDS_RK + LDS_WIN;
+  static constexpr int LDS_WAVE = LDS_Q + LDS_K + LDS_V + LDS_E + LDS_RK + LDS_WIN;
 };
 
 template <int KDT>
@@ -188,9 +197,9 @@ __device__ __forceinline__ v4u encode16<kE4M3>(const float* f) {
              f2e4m3x2(f[12], f[13]) | (f2e4m3x2(f[14], f[15]) << 16)};
 }
 
-// Decode the first EPLV elements held in a 16-B register value.
+// Decode the EPC elements of one 16-B chunk.
 template <int KDT>
-__device__ __forceinline__ void decode_reg(const v4u& w, float* f) {
+__device__ __forceinline__ void decode16(const v4u& w, float* f) {
   if constexpr (KDT == kF32) {
     f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
     f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
@@ -198,39 +207,38 @@ __device__ __forceinline__ void decode_reg(const v4u& w, float* f) {
     f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
     f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
   } else {
-    e4m3x4(w.x, f);
-    e4m3x4(w.y, f + 4);
+    e4m3x4(w.x, f); e4m3x4(w.y, f + 4); e4m3x4(w.z, f + 8); e4m3x4(w.w, f + 12);
   }
 }
 
-// Decode 8 consecutive cache elements starting at p (LDS or registers).
+// Decode the first EPLV elements of a V slice (16 B, or 8 B for e4m3).
 template <int KDT>
-__device__ __forceinline__ void decode8(const uint8_t* p, float* f) {
+__device__ __forceinline__ void decode_v(const uint8_t* p, float* f) {
   if constexpr (KDT == kF32) {
     v4f a = *reinterpret_cast<const v4f*>(p);
-    v4f b = *reinterpret_cast<const v4f*>(p + 16);
     f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
   } else if constexpr (KDT == kBF16) {
     v4u w = *reinterpret_cast<const v4u*>(p);
     f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
     f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
   } else {
     v2u w = *reinterpret_cast<const v2u*>(p);
-    e4m3x4(w.x, f);
-    e4m3x4(w.y, f + 4);
+    e4m3x4(w.x, f); e4m3x4(w.y, f + 4);
   }
 }
+
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0); }
 
 template <int KDT, int D>
 __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int item,
                           uint8_t* wl) {
   using Gm = AttnGeom<KDT, D>;
-  constexpr int ES = Gm::ES, RB = Gm::RB, RBP = Gm::RBP, CPR = Gm::CPR;
+  constexpr int ES = Gm::ES, RB = Gm::RB, CPR = Gm::CPR, EPC = Gm::EPC, NLD = Gm::NLD;
   constexpr int EPLV = Gm::EPLV, VB = Gm::VB, LPP = Gm::LPP, PPI = Gm::PPI, NVL = Gm::NVL;
   float* qs = reinterpret_cast<float*>(wl);
   uint8_t* kt = wl + Gm::LDS_Q;
-  float* et = reinterpret_cast<float*>(kt + Gm::LDS_K);
+  uint8_t* vt = kt + Gm::LDS_K;
+  float* et = reinterpret_cast<float*>(vt + Gm::LDS_V);
   float* rk = et + kRowGroup * 64;
   int* win = reinterpret_cast<int*>(rk + kMaxTok);
 
@@ -255,53 +263,67 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
   uint8_t* vc = L.vc + head_off * RB;
   const bool writer = (rg == 0);
 
-  // normalised, pre-scaled query rows and their windows
+  // normalised, pre-scaled query rows and their windows: all rows' loads are
+  // issued before any reduction waits on them
+  constexpr int QD = (D + 63) / 64;
+  float qv[kRowGroup][QD];
+#pragma unroll
+  for (int mm = 0; mm < kRowGroup; ++mm) {
+    const int m = m0 + mm < M ? m0 + mm : M - 1;  // rows past M load a valid row, unused
+    const int t = m / G, g = m - (m / G) * G;
+    const float* q = S.qkv + (size_t)(b * S.Tr + t) * NR + (size_t)(j * G + g) * D;
+#pragma unroll
+    for (int i = 0; i < QD; ++i) {
+      const int d = ln + 64 * i;
+      qv[mm][i] = (m0 + mm < M && d < D) ? q[d] : 0.f;
+    }
+  }
+#pragma unroll
   for (int mm = 0; mm < kRowGroup; ++mm) {
     const int m = m0 + mm;
-    if (m < M) {
-      const int t = m / G, g = m - (m / G) * G;
-      const float* q = S.qkv + (size_t)(b * S.Tr + t) * NR + (size_t)(j * G + g) * D;
-      float qv[(D + 63) / 64];
-      float ss = 0.f;
+    float ss = 0.f;
 #pragma unroll
-      for (int i = 0; i < (D + 63) / 64; ++i) {
-        const int d = ln + 64 * i;
-        qv[i] = d < D ? q[d] : 0.f;
-        ss += qv[i] * qv[i];
-      }
-      ss = wave_sum(ss);
-      const float r = 1.0f / sqrtf(ss / (float)D + L.eps);
+    for (int i = 0; i < QD; ++i) ss += qv[mm][i] * qv[mm][i];
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)D + L.eps);
 #pragma unroll
-      for (int i = 0; i < (D + 63) / 64; ++i) {
-        const int d = ln + 64 * i;
-        if (d < D) qs[mm * D + d] = qv[i] * r * L.q_norm[d] * L.qscale;
-      }
-      if (ln == 0) {
-        const int p = Lb + t;
-        win[2 * mm] = L.window > 0 ? (p - L.window + 1 > 0 ? p - L.window + 1 : 0) : 0;
-        win[2 * mm + 1] = p;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < (D + 63) / 64; ++i) {
-        const int d = ln + 64 * i;
-        if (d < D) qs[mm * D + d] = 0.f;
-      }
-      if (ln == 0) { win[2 * mm] = 1; win[2 * mm + 1] = 0; }
+    for (int i = 0; i < QD; ++i) {
+      const int d = ln + 64 * i;
+      if (d < D) qs[mm * D + d] = m < M ? qv[mm][i] * r * L.q_norm[d] * L.qscale : 0.f;
+    }
+    if (ln == 0) {
+      const int t = m / G;
+      const int p = Lb + t;
+      win[2 * mm] = m < M ? (L.window > 0 ? (p - L.window + 1 > 0 ? p - L.window + 1 : 0) : 0) : 1;
+      win[2 * mm + 1] = m < M ? p : 0;
     }
   }
   wave_lds_sync();
   // positions before the group's earliest window start are never visible
   const int lo_min = win[0];
-  // 1/rms of the step's new keys that fall in this chunk
-  int tn0 = p0 - Lb > 0 ? p0 - Lb : 0;
-  int tn1 = p1 - Lb < S.Tr ? p1 - Lb : S.Tr;
-  for (int t = tn0; t < tn1; ++t) {
-    const float* k = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + (size_t)j * D;
-    float ss = 0.f;
-    for (int d = ln; d < D; d += 64) ss += k[d] * k[d];
-    ss = wave_sum(ss);
-    if (ln == 0) rk[t] = 1.0f / sqrtf(ss / (float)D + L.eps);
+  // 1/rms of the step's new keys that fall in this chunk, eight at a time
+  const int tn0 = p0 - Lb > 0 ? p0 - Lb : 0;
+  const int tn1 = p1 - Lb < S.Tr ? p1 - Lb : S.Tr;
+  for (int t0 = tn0; t0 < tn1; t0 += 8) {
+    float kv[8][QD];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int tq = t0 + q < tn1 ? t0 + q : tn1 - 1;
+      const float* k = S.qkv + (size_t)(b * S.Tr + tq) * NR + NQ + (size_t)j * D;
+#pragma unroll
+      for (int i = 0; i < QD; ++i) {
+        const int d = ln + 64 * i;
+        kv[q][i] = (t0 + q < tn1 && d < D) ? k[d] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < QD; ++i) ss += kv[q][i] * kv[q][i];
+      ss = wave_sum(ss);
+      if (ln == 0 && t0 + q < tn1) rk[t0 + q] = 1.0f / sqrtf(ss / (float)D + L.eps);
+    }
   }
   wave_lds_sync();
 
@@ -317,71 +339,68 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
 
   for (int pb = p0; pb < p1; pb += 64) {
     const int npos = p1 - pb < 64 ? p1 - pb : 64;
-    // V rows of old positions, straight to registers
-    v4u vraw[NVL];
+    // cached rows of this block: straight into the LDS tiles.  Lane l of load
+    // i carries tile bytes [i KB + 16 l, +16), i.e. row (1024 i + 16 l) / RB;
+    // only rows that are visible and already cached are fetched.
 #pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-      const int pp = pg + i * PPI;
-      const int pos = pb + pp;
-      vraw[i] = v4u{0u, 0u, 0u, 0u};
-      if (pp < npos && pos >= lo_min && pos < Lb) {
-        const uint8_t* src = vc + (size_t)pos * RB + dc * VB;
-        if constexpr (VB == 16) {
-          vraw[i] = *reinterpret_cast<const v4u*>(src);
-        } else {
-          v2u t2 = *reinterpret_cast<const v2u*>(src);
-          vraw[i].x = t2.x;
-          vraw[i].y = t2.y;
-        }
+    for (int i = 0; i < NLD; ++i) {
+      const int off = i * 1024 + ln * 16;
+      const int pos = pb + off / RB;
+      if (pos < pb + npos && pos >= lo_min && pos < Lb) {
+        __builtin_amdgcn_global_load_lds(kc + (size_t)pb * RB + off, kt + i * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vc + (size_t)pb * RB + off, vt + i * 1024, 16, 0, 0);
       }
     }
-    // K rows into the LDS tile (new positions rebuilt from the QKV output)
-#pragma unroll
-    for (int i = 0; i < CPR; ++i) {
-      const int q = ln + 64 * i;
-      const int row = q / CPR, col = q - (q / CPR) * CPR;
-      const int pos = pb + row;
-      if (row < npos) {
-        uint8_t* dst = kt + row * RBP + col * 16;
-        if (pos < Lb) {
-          *reinterpret_cast<v4u*>(dst) = *reinterpret_cast<const v4u*>(kc + (size_t)pos * RB + col * 16);
-        } else {
+    // the step's own rows (positions >= kv_len): rebuilt and stored
+    if (pb + npos > Lb) {
+      for (int q = ln; q < 64 * CPR; q += 64) {
+        const int row = q / CPR, col = q - (q / CPR) * CPR;
+        const int pos = pb + row;
+        if (row < npos && pos >= Lb) {
           const int t = pos - Lb;
-          constexpr int EP = 16 / ES;
-          const int d0 = col * EP;
-          const float* k = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + (size_t)j * D + d0;
-          float f[EP];
+          const int d0 = col * EPC;
+          const float* kq = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + (size_t)j * D + d0;
+          const float* vq = kq + NK;
+          float fk[16], fv[16];
 #pragma unroll
-          for (int e = 0; e < EP; ++e) f[e] = k[e] * rk[t] * L.k_norm[d0 + e];
-          const v4u enc = encode16<KDT>(f);
-          *reinterpret_cast<v4u*>(dst) = enc;
-          if (writer) *reinterpret_cast<v4u*>(kc + (size_t)pos * RB + col * 16) = enc;
+          for (int e = 0; e < 16; ++e) {
+            fk[e] = e < EPC ? kq[e] * rk[t] * L.k_norm[d0 + e] : 0.f;
+            fv[e] = e < EPC ? vq[e] : 0.f;
+          }
+          const v4u ek = encode16<KDT>(fk), ev = encode16<KDT>(fv);
+          *reinterpret_cast<v4u*>(kt + row * RB + col * 16) = ek;
+          *reinterpret_cast<v4u*>(vt + row * RB + col * 16) = ev;
+          if (writer) {
+            *reinterpret_cast<v4u*>(kc + (size_t)pos * RB + col * 16) = ek;
+            *reinterpret_cast<v4u*>(vc + (size_t)pos * RB + col * 16) = ev;
+          }
         }
       }
     }
+    wait_vm_all();
     wave_lds_sync();
-    // scores: lane = position
+    // scores: lane = position, K row read in a lane-rotated chunk order
     {
       float s[kRowGroup];
 #pragma unroll
       for (int mm = 0; mm < kRowGroup; ++mm) s[mm] = 0.f;
-      const uint8_t* krow = kt + ln * RBP;
+      const uint8_t* krow = kt + ln * RB;
 #pragma unroll 4
-      for (int d0 = 0; d0 < D; d0 += 8) {
-        float kf[8];
-        decode8<KDT>(krow + d0 * ES, kf);
+      for (int i = 0; i < CPR; ++i) {
+        const int cc = (i + ln) & (CPR - 1);
+        float kf[EPC];
+        decode16<KDT>(*reinterpret_cast<const v4u*>(krow + cc * 16), kf);
+        const int d0 = cc * EPC;
 #pragma unroll
         for (int mm = 0; mm < kRowGroup; ++mm) {
-          v4f qa = *reinterpret_cast<const v4f*>(qs + mm * D + d0);
-          v4f qb = *reinterpret_cast<const v4f*>(qs + mm * D + d0 + 4);
-          s[mm] = fmaf(qa.x, kf[0], s[mm]);
-          s[mm] = fmaf(qa.y, kf[1], s[mm]);
-          s[mm] = fmaf(qa.z, kf[2], s[mm]);
-          s[mm] = fmaf(qa.w, kf[3], s[mm]);
-          s[mm] = fmaf(qb.x, kf[4], s[mm]);
-          s[mm] = fmaf(qb.y, kf[5], s[mm]);
-          s[mm] = fmaf(qb.z, kf[6], s[mm]);
-          s[mm] = fmaf(qb.w, kf[7], s[mm]);
+#pragma unroll
+          for (int e4 = 0; e4 < EPC; e4 += 4) {
+            v4f qa = *reinterpret_cast<const v4f*>(qs + mm * D + d0 + e4);
+            s[mm] = fmaf(qa.x, kf[e4], s[mm]);
+            s[mm] = fmaf(qa.y, kf[e4 + 1], s[mm]);
+            s[mm] = fmaf(qa.z, kf[e4 + 2], s[mm]);
+            s[mm] = fmaf(qa.w, kf[e4 + 3], s[mm]);
+          }
         }
       }
       const int pos = pb + ln;
@@ -394,31 +413,14 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
       }
     }
     wave_lds_sync();
-    // o += e * V
+    // o += e * V from the V tile
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int pp = pg + i * PPI;
       const int pos = pb + pp;
       if (pp < npos && pos >= lo_min) {
         float vf[EPLV];
-        if (pos < Lb) {
-          decode_reg<KDT>(vraw[i], vf);
-        } else {
-          const int t = pos - Lb;
-          const float* v = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + NK + (size_t)j * D + dc * EPLV;
-          float raw[16];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) raw[e] = e < EPLV ? v[e] : 0.f;
-          const v4u enc = encode16<KDT>(raw);
-          if (writer) {
-            uint8_t* dst = vc + (size_t)pos * RB + dc * VB;
-            if constexpr (VB == 16)
-              *reinterpret_cast<v4u*>(dst) = enc;
-            else
-              *reinterpret_cast<v2u*>(dst) = v2u{enc.x, enc.y};
-          }
-          decode_reg<KDT>(enc, vf);
-        }
+        decode_v<KDT>(vt + pp * RB + dc * VB, vf);
 #pragma unroll
         for (int mm = 0; mm < kRowGroup; ++mm) {
           const float e = et[mm * 64 + pp];
@@ -455,18 +457,18 @@ __device__ void phase_attn(const LayerArgs& L, const StepArgs& S, const AttnPlan
   using Gm = AttnGeom<KDT, D>;
   uint8_t* wl = lds_waves + wave_id() * Gm::LDS_WAVE;
   const int n_items = P->item0[S.n_req];
-  for (int item = vb * kWaves + wave_id(); item < n_items; item += nvb * kWaves)
+  for (int item = gwave(vb, nvb); item < n_items; item += nvb * kWaves)
     attn_item<KDT, D>(L, S, P, item, wl);
 }
 
 // ---------------------------------------------------------- combine
 // attn_o[t][h] = sum_chunks o / sum_chunks l (plain sums, fixed order).
-__device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int vb,
-                              int nvb) {
+__device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int* win_out,
+                              int vb, int nvb) {
   const int D = L.D, G = L.Hq / L.Hkv;
   const int rows = S.T * L.Hq;
   const int ln = lane_id();
-  for (int row = vb * kWaves + wave_id(); row < rows; row += nvb * kWaves) {
+  for (int row = gwave(vb, nvb); row < rows; row += nvb * kWaves) {
     const int tok = row / L.Hq, hh = row - (row / L.Hq) * L.Hq;
     const int b = tok / S.Tr, tt = tok - (tok / S.Tr) * S.Tr;
     const int j = hh / G, g = hh - (hh / G) * G;
@@ -476,7 +478,20 @@ __device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnP
     const float* base = S.part + (size_t)it0 * kRowGroup * (D + 1) + mm * (D + 1);
     const size_t stride = (size_t)kRowGroup * (D + 1);
     float l = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int c = 0; c < nch; ++c) {
+    int c = 0;
+    for (; c + 16 <= nch; c += 16) {  // sixteen chunks' loads in flight
+      float pl[16], p0[16], p1[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const float* p = base + (c + q) * stride;
+        pl[q] = p[D];
+        p0[q] = ln < D ? p[ln] : 0.f;
+        p1[q] = ln + 64 < D ? p[ln + 64] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) { l += pl[q]; o0 += p0[q]; o1 += p1[q]; }
+    }
+    for (; c < nch; ++c) {
       const float* p = base + c * stride;
       l += p[D];
       if (ln < D) o0 += p[ln];
@@ -486,12 +501,12 @@ __device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnP
     if (ln < D) dst[ln] = o0 / l;
     if (ln + 64 < D) dst[ln + 64] = o1 / l;
   }
-  if (S.win_out != nullptr && vb == 0) {
+  if (win_out != nullptr && vb == 0) {
     for (int tok = threadIdx.x; tok < S.T; tok += blockDim.x) {
       const int b = tok / S.Tr, t = tok - (tok / S.Tr) * S.Tr;
       const int p = S.kv_len[b] + t;
-      S.win_out[2 * tok] = L.window > 0 ? (p - L.window + 1 > 0 ? p - L.window + 1 : 0) : 0;
-      S.win_out[2 * tok + 1] = p;
+      win_out[2 * tok] = L.window > 0 ? (p - L.window + 1 > 0 ? p - L.window + 1 : 0) : 0;
+      win_out[2 * tok + 1] = p;
     }
   }
 }
@@ -504,7 +519,7 @@ __device__ void phase_wo(const LayerArgs& L, const StepArgs& S, const float* x, 
   constexpr int R = DenseRows<NV>::R;
   const int NI = L.Hq * L.D;
   const size_t rb = dense_row_bytes(DT, NI);
-  const int gw = vb * kWaves + wave_id(), nw = nvb * kWaves;
+  const int gw = gwave(vb, nvb), nw = nvb * kWaves;
   for (int t0 = 0; t0 < S.T; t0 += NV) {
     const int nt = S.T - t0 < NV ? S.T - t0 : NV;
     const float* vin[NV];
@@ -543,7 +558,7 @@ __device__ void phase_router(const LayerArgs& L, const StepArgs& S, const float*
         v4f{a.x * r * g.x, a.y * r * g.y, a.z * r * g.z, a.w * r * g.w};
   }
   const size_t rb = dense_row_bytes(DT, L.H);
-  const int gw = vb * kWaves + wave_id(), nw = nvb * kWaves;
+  const int gw = gwave(vb, nvb), nw = nvb * kWaves;
   for (int t0 = 0; t0 < S.T; t0 += NV) {
     const int nt = S.T - t0 < NV ? S.T - t0 : NV;
     const float* vin[NV];
@@ -572,53 +587,7 @@ __device__ inline bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-__device__ void phase_topk(const LayerArgs& L, const StepArgs& S, int* topk_out, int vb, int nvb) {
-  const int ln = lane_id();
-  for (int t = vb * kWaves + wave_id(); t < S.T; t += nvb * kWaves) {
-    float v[4];
-    bool taken[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = ln + 64 * i;
-      v[i] = e < L.E ? S.logits[(size_t)t * L.E + e] : 0.f;
-      taken[i] = !(e < L.E) || (v[i] != v[i]);  // absent or NaN
-    }
-    float v0 = 0.f, den = 0.f;
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {
-      if (k >= L.K) break;
-      float bv = 0.f;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = ln + 64 * i;
-        if (!taken[i] && (bi == 0x7fffffff || better(v[i], e, bv, bi))) { bv = v[i]; bi = e; }
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) { bv = ov; bi = oi; }
-      }
-      if (bi == 0x7fffffff) { bi = 0; bv = -INFINITY; }  // fewer valid logits than k
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (ln + 64 * i == bi) taken[i] = true;
-      if (k == 0) v0 = bv;
-      const float ex = __expf(bv - v0);
-      den += ex;
-      if (ln == 0) {
-        S.idx[t * L.K + k] = bi;
-        S.wts[t * L.K + k] = ex;
-        if (topk_out) topk_out[t * L.K + k] = bi;
-      }
-    }
-    if (ln == 0) {
-      const float inv = 1.0f / den;
-      for (int k = 0; k < L.K; ++k) S.wts[t * L.K + k] *= inv;
-    }
-  }
-}
+__device__ void phase_topk(const LayerArgs& L, const StepArgs& S, int* topk_out, int vb, int nvb);
 
 // ------------------------------------------------------ expert union
 // Distinct selected experts in ascending order, and per expert the slots
@@ -697,7 +666,7 @@ __device__ void phase_gateup(const LayerArgs& L, const StepArgs& S, const Union*
   const int n_items = U->n * nrb;
   const size_t rb = expert_row_bytes(DT, L.H);
   const size_t sb = (size_t)L.H / 16;
-  for (int item = vb * kWaves + wave_id(); item < n_items; item += nvb * kWaves) {
+  for (int item = gwave(vb, nvb); item < n_items; item += nvb * kWaves) {
     const int ui = item / nrb, rblk = item - (item / nrb) * nrb;
     const int e = U->list[ui];
     const int s0 = U->off[ui], ns = U->off[ui + 1] - s0;
@@ -750,7 +719,7 @@ __device__ void phase_down(const LayerArgs& L, const StepArgs& S, const Union* U
   const size_t rb = expert_row_bytes(DT, L.F);
   const size_t sb = (size_t)L.F / 16;
   const int ln = lane_id();
-  for (int blk = vb * kWaves + wave_id(); blk * R < L.H; blk += nvb * kWaves) {
+  for (int blk = gwave(vb, nvb); blk * R < L.H; blk += nvb * kWaves) {
     const int c0 = blk * R;
     for (int i = ln; i < TK * R; i += 64) ybuf[i] = 0.f;
     wave_lds_sync();

@@ -1,0 +1,285 @@
+// One-token (decode) phases.  With a single token every phase's input vector
+// fits in LDS, so each workgroup stages it once (RMSNorm and gain applied on
+// the way in) and the weight rows stream through registers two buffers deep
+// (stream_t1).  Work is dealt out wave-major over the workgroups so that a
+// phase with fewer tasks than waves still spreads over every CU.
+#pragma once
+#include "phases.h"
+
+namespace msk {
+
+// Tasks of wave gw out of ntask dealt round-robin over nw waves.
+__device__ __forceinline__ int my_count(int gw, int nw, int ntask) {
+  return gw < ntask ? (ntask - 1 - gw) / nw + 1 : 0;
+}
+
+// act[c] = x[c] * g[c] / sqrt(mean(x^2) + eps) into LDS (g may be null).
+__device__ inline void stage_norm_t1(const float* x, const float* g, int H, float eps, float* act,
+                                     float* red) {
+  float s = 0.f;
+  for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
+    v4f a = *reinterpret_cast<const v4f*>(x + c);
+    s += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+  }
+  const float r = 1.0f / sqrtf(block_sum(s, red) / (float)H + eps);
+  for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
+    v4f a = *reinterpret_cast<const v4f*>(x + c);
+    v4f gg = *reinterpret_cast<const v4f*>(g + c);
+    *reinterpret_cast<v4f*>(act + c) = v4f{a.x * r * gg.x, a.y * r * gg.y, a.z * r * gg.z, a.w * r * gg.w};
+  }
+  __syncthreads();
+}
+
+// Plain copy of n floats (n % 4 == 0) into LDS.
+__device__ inline void stage_copy(const float* src, int n, float* dst) {
+  for (int c = threadIdx.x * 4; c < n; c += blockDim.x * 4)
+    *reinterpret_cast<v4f*>(dst + c) = *reinterpret_cast<const v4f*>(src + c);
+  __syncthreads();
+}
+
+// Lane r < R stores acc[r] through st(r, value).
+template <int R, class F>
+__device__ __forceinline__ void lane_store(const float (&acc)[R], F&& st) {
+  const int ln = lane_id();
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (ln == r) st(r, acc[r]);
+}
+
+// qkv[r] = sum_c W[r][c] act[c] over the stacked rows of wq, wk, wv.
+template <int DT>
+__device__ void qkv_t1(const LayerArgs& L, const StepArgs& S, const float* act, int vb, int nvb) {
+  constexpr int R = 4, U = 2;
+  const int NQ = L.Hq * L.D, NK = L.Hkv * L.D, NR = NQ + 2 * NK;
+  const size_t rb = dense_row_bytes(DT, L.H);
+  const int gw = gwave(vb, nvb), nw = nvb * kWaves;
+  const int n = my_count(gw, nw, NR / R);
+  stream_t1<DT, R, U>(
+      n, L.H, [&](int) { return act; },
+      [&](int k, auto& wr, auto& sr) {
+        const int r0 = (gw + k * nw) * R;
+        const uint8_t* base;
+        int rr;
+        if (r0 < NQ) { base = L.wq; rr = r0; }
+        else if (r0 < NQ + NK) { base = L.wk; rr = r0 - NQ; }
+        else { base = L.wv; rr = r0 - NQ - NK; }
+#pragma unroll
+        for (int r = 0; r < R; ++r) { wr[r] = base + (size_t)(rr + r) * rb; sr[r] = nullptr; }
+      },
+      [&](int k, auto& acc) {
+        const int r0 = (gw + k * nw) * R;
+        lane_store<R>(acc, [&](int r, float v) { S.qkv[r0 + r] = v; });
+      });
+}
+
+// h[r] = x[r] + sum_c wo[r][c] act[c]  (act = staged attention output)
+template <int DT>
+__device__ void wo_t1(const LayerArgs& L, const StepArgs& S, const float* x, float* h,
+                      const float* act, int vb, int nvb) {
+  constexpr int R = 4, U = 2;
+  const int NI = L.Hq * L.D;
+  const size_t rb = dense_row_bytes(DT, NI);
+  const int gw = gwave(vb, nvb), nw = nvb * kWaves;
+  const int n = my_count(gw, nw, (L.H + R - 1) / R);
+  stream_t1<DT, R, U>(
+      n, NI, [&](int) { return act; },
+      [&](int k, auto& wr, auto& sr) {
+        const int r0 = (gw + k * nw) * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int row = r0 + r < L.H ? r0 + r : L.H - 1;
+          wr[r] = L.wo + (size_t)row * rb;
+          sr[r] = nullptr;
+        }
+      },
+      [&](int k, auto& acc) {
+        const int r0 = (gw + k * nw) * R;
+        lane_store<R>(acc, [&](int r, float v) {
+          if (r0 + r < L.H) h[r0 + r] = x[r0 + r] + v;
+        });
+      });
+}
+
+// u = RMSNorm(h) * ffn_norm into LDS (workgroup vb also writes its slice of
+// u to global memory); logits[e] = w_router[e] . u.
+template <int DT>
+__device__ void router_t1(const LayerArgs& L, const StepArgs& S, const float* h, float* act,
+                          float* red, int vb, int nvb) {
+  stage_norm_t1(h, L.ffn_norm, L.H, L.eps, act, red);
+  {
+    const int per = ((L.H / 4 + nvb - 1) / nvb) * 4;
+    const int c0 = vb * per, c1 = c0 + per < L.H ? c0 + per : L.H;
+    for (int c = c0 + threadIdx.x * 4; c < c1; c += blockDim.x * 4)
+      *reinterpret_cast<v4f*>(S.u + c) = *reinterpret_cast<const v4f*>(act + c);
+  }
+  constexpr int R = 1, U = 2;
+  const size_t rb = dense_row_bytes(DT, L.H);
+  const int gw = gwave(vb, nvb), nw = nvb * kWaves;
+  const int n = my_count(gw, nw, L.E);
+  stream_t1<DT, R, U>(
+      n, L.H, [&](int) { return act; },
+      [&](int k, auto& wr, auto& sr) {
+        wr[0] = L.wr + (size_t)(gw + k * nw) * rb;
+        sr[0] = nullptr;
+      },
+      [&](int k, auto& acc) {
+        lane_store<R>(acc, [&](int, float v) { S.logits[gw + k * nw] = v; });
+      });
+}
+
+// Top-k of one token's logits by one wave (value descending, index ascending
+// on ties); idx/w written by lane 0, weights = softmax over the selected.
+// Each round takes the wave-wide maximum, then the lowest index holding it.
+__device__ inline void topk_row(const float* logits, int E, int K, int* idx, float* w) {
+  const int ln = lane_id();
+  float v[4];
+  bool open[4];  // still selectable
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = ln + 64 * i;
+    const float x = e < E ? logits[e] : -INFINITY;
+    v[i] = (x == x) ? x : -INFINITY;  // NaN never wins
+    open[i] = e < E;
+  }
+  float v0 = 0.f, den = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    if (k >= K) break;
+    float lm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (open[i]) lm = fmaxf(lm, v[i]);
+    const float m = wave_max(lm);
+    int cand = 0x7fffffff;
+#pragma unroll
+    for (int i = 3; i >= 0; --i)
+      if (open[i] && v[i] == m) cand = ln + 64 * i;
+    int bi = wave_min_i(cand);
+    if (bi == 0x7fffffff) bi = 0;  // fewer selectable logits than k
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (ln + 64 * i == bi) { v[i] = -INFINITY; open[i] = false; }
+    if (k == 0) v0 = m;
+    const float ex = __expf(m - v0);
+    den += ex;
+    if (ln == 0) { idx[k] = bi; w[k] = ex; }
+  }
+  if (ln == 0) {
+    const float inv = 1.0f / den;
+    for (int k = 0; k < K; ++k) w[k] *= inv;
+  }
+}
+
+// One wave per token: top-k and gating weights into S.idx / S.wts.
+__device__ void phase_topk(const LayerArgs& L, const StepArgs& S, int* topk_out, int vb, int nvb) {
+  for (int t = gwave(vb, nvb); t < S.T; t += nvb * kWaves) {
+    topk_row(S.logits + (size_t)t * L.E, L.E, L.K, S.idx + (size_t)t * L.K, S.wts + (size_t)t * L.K);
+    if (topk_out != nullptr && lane_id() == 0)
+      for (int k = 0; k < L.K; ++k) topk_out[(size_t)t * L.K + k] = S.idx[(size_t)t * L.K + k];
+  }
+}
+
+// The workgroup that finishes last (counter in the workspace) gets true; the
+// counter is returned to zero by that workgroup.  No workgroup waits.
+__device__ inline bool last_workgroup(unsigned* counter, int* flag_lds) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == gridDim.x - 1;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag_lds = last;
+  }
+  __syncthreads();
+  return *flag_lds != 0;
+}
+
+// act[j][f] = silu(gate_e[f] . u) * (up_e[f] . u), e = idx[j]; u staged in LDS.
+template <int DT>
+__device__ void gateup_t1(const LayerArgs& L, const StepArgs& S, const int* idx, const float* u,
+                          int vb, int nvb) {
+  constexpr int R = 2, U = 2;
+  const int nrb = L.F / R;
+  const size_t rb = expert_row_bytes(DT, L.H);
+  const size_t sb = (size_t)L.H / 16;
+  const int gw = gwave(vb, nvb), nw = nvb * kWaves;
+  const int n = my_count(gw, nw, L.K * nrb);
+  stream_t1<DT, 2 * R, U>(
+      n, L.H, [&](int) { return u; },
+      [&](int k, auto& wr, auto& sr) {
+        const int t = gw + k * nw, j = t / nrb, f0 = (t - j * nrb) * R;
+        int e = idx[j];
+        e = e >= 0 && e < L.E ? e : 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const size_t row = (size_t)e * L.F + f0 + r;
+          wr[r] = L.wg + row * rb;
+          wr[R + r] = L.wu + row * rb;
+          sr[r] = DT == kNVFP4 ? L.sg + row * sb : nullptr;
+          sr[R + r] = DT == kNVFP4 ? L.su + row * sb : nullptr;
+        }
+      },
+      [&](int k, auto& acc) {
+        const int t = gw + k * nw, j = t / nrb, f0 = (t - j * nrb) * R;
+        int e = idx[j];
+        e = e >= 0 && e < L.E ? e : 0;
+        const float gs = DT == kNVFP4 ? L.gg[e] : 1.f, us = DT == kNVFP4 ? L.gu[e] : 1.f;
+        float res[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) res[r] = silu(acc[r] * gs) * (acc[R + r] * us);
+        lane_store<R>(res, [&](int r, float v) { S.act[(size_t)j * L.F + f0 + r] = v; });
+      });
+}
+
+// out[c] = h[c] + sum_j w[j] * (down_e[c] . act[j]), e = idx[j], in slot order;
+// act staged in LDS as [K][F].  Entries of idx outside [0, E) add nothing.
+template <int DT>
+__device__ void down_t1(const LayerArgs& L, const StepArgs& S, const int* idx, const float* wts,
+                        const float* act, const float* h, float* out, float* out2, int vb,
+                        int nvb) {
+  constexpr int R = 4, U = 2;
+  const size_t rb = expert_row_bytes(DT, L.F);
+  const size_t sb = (size_t)L.F / 16;
+  const int gw = gwave(vb, nvb), nw = nvb * kWaves;
+  const int K = L.K;
+  const int nrb = my_count(gw, nw, (L.H + R - 1) / R);
+  float o[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) o[r] = 0.f;
+  stream_t1<DT, R, U>(
+      nrb * K, L.F, [&](int k) { return act + (size_t)(k - (k / K) * K) * L.F; },
+      [&](int k, auto& wr, auto& sr) {
+        const int j = k - (k / K) * K, r0 = (gw + (k / K) * nw) * R;
+        int e = idx[j];
+        e = e >= 0 && e < L.E ? e : 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int c = r0 + r < L.H ? r0 + r : L.H - 1;
+          const size_t row = (size_t)e * L.H + c;
+          wr[r] = L.wd + row * rb;
+          sr[r] = DT == kNVFP4 ? L.sd + row * sb : nullptr;
+        }
+      },
+      [&](int k, auto& acc) {
+        const int j = k - (k / K) * K, r0 = (gw + (k / K) * nw) * R;
+        const int e = idx[j];
+        const bool ok = e >= 0 && e < L.E;
+        const float s = ok ? wts[j] * (DT == kNVFP4 ? L.gd[e] : 1.f) : 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) o[r] = fmaf(s, acc[r], o[r]);
+        if (j == K - 1) {
+          lane_store<R>(o, [&](int r, float v) {
+            const int c = r0 + r;
+            if (c < L.H) {
+              const float y = h[c] + v;
+              out[c] = y;
+              if (out2) out2[c] = y;
+            }
+          });
+#pragma unroll
+          for (int r = 0; r < R; ++r) o[r] = 0.f;
+        }
+      });
+}
+
+}  // namespace msk
