@@ -16,13 +16,6 @@ typedef unsigned v2u __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
-// Sum over the 64 lanes; every lane gets the total.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // Wave-wide max / min through DPP row rotations (within rows of 16 lanes)
 // and four lane reads (across rows): no LDS round trips.  Every lane gets
 // the result.
@@ -60,6 +53,43 @@ __device__ __forceinline__ int wave_min_i(int v) {
   const int c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
   return min(min(a, b), min(c, d));
 }
+
+// Sum over the 64 lanes; every lane gets the total (fixed order, so the
+// result is reproducible bit for bit).
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppRor4>(v);
+  v += dpp_f<kDppRor8>(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
+// v[l] + v[l ^ 16] and v[l] + v[l ^ 32] through the gfx950 lane swaps.
+__device__ __forceinline__ float add_xor16(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Sum of v over the lanes congruent to this one modulo LPP (LPP = 4, 8, 16
+// or 32): the lanes that hold the same slice for different positions.
+template <int LPP>
+__device__ __forceinline__ float sum_groups(float v) {
+  if constexpr (LPP <= 4) v += dpp_f<kDppRor4>(v);
+  if constexpr (LPP <= 8) v += dpp_f<kDppRor8>(v);
+  if constexpr (LPP <= 16) v = add_xor16(v);
+  v = add_xor32(v);
+  return v;
+}
+
+
 
 // Orders LDS traffic of one wave: its earlier LDS writes are complete before
 // its later LDS reads (used for wave-private tiles, no workgroup barrier).
@@ -229,10 +259,11 @@ __device__ __forceinline__ void wave_gemv(const uint8_t* const (&wrow)[R],
 // dotted with one fp32 vector in LDS (actfn(k)).  The weight stream is
 // software-pipelined two buffers deep across row ends and task ends, and the
 // input vector comes from LDS, so no cache load ever waits behind a weight
-// load.  out(k, acc) receives the sums (in every lane).
-template <int DT, int R, int U, class ActFn, class RowFn, class OutFn>
+// load.  out(k, acc) receives the sums (in every lane); pre() runs once, in
+// every wave, after the first loads are issued.
+template <int DT, int R, int U, class ActFn, class RowFn, class OutFn, class PreFn>
 __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, RowFn&& rowfn,
-                                          OutFn&& out) {
+                                          OutFn&& out, PreFn&& pre) {
   using W = WT<DT>;
   const int ln = lane_id();
   const int nch = ncols / W::EPL;
@@ -306,13 +337,18 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
       for (int r = 0; r < R; ++r) acc[r] = 0.f;
     }
   };
+  // the first two buffers go out before the prologue (typically staging the
+  // input vector into LDS, which every wave of the workgroup joins), so its
+  // latency overlaps the first weight fetches
   if (total > 0) issue(A, sA, 0);
+  if (total > 1) issue(B, sB, 1);
+  pre();
   for (int f = 0; f < total; f += 2) {
-    if (f + 1 < total) issue(B, sB, f + 1);
     compute(A, sA, f);
+    if (f + 2 < total) issue(A, sA, f + 2);
     if (f + 1 < total) {
-      if (f + 2 < total) issue(A, sA, f + 2);
       compute(B, sB, f + 1);
+      if (f + 3 < total) issue(B, sB, f + 3);
     }
   }
 }

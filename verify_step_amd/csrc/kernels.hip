@@ -96,8 +96,9 @@ template <int DT>
 __global__ __launch_bounds__(kBlockThreads) void k_qkv_t1(LayerArgs L, StepArgs S, const float* x) {
   const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
   float* act = reinterpret_cast<float*>(msk_smem + o.act0);
-  stage_norm_t1(x, L.attn_norm, L.H, L.eps, act, reinterpret_cast<float*>(msk_smem + o.red));
-  qkv_t1<DT>(L, S, act, blockIdx.x, gridDim.x);
+  qkv_t1<DT>(L, S, act, blockIdx.x, gridDim.x, [&]() {
+    stage_norm_t1(x, L.attn_norm, L.H, L.eps, act, reinterpret_cast<float*>(msk_smem + o.red));
+  });
 }
 
 template <int DT>
@@ -105,8 +106,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_wo_t1(LayerArgs L, StepArgs S
                                                          float* h) {
   const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
   float* act = reinterpret_cast<float*>(msk_smem + o.act0);
-  stage_copy(S.attn_o, L.Hq * L.D, act);
-  wo_t1<DT>(L, S, x, h, act, blockIdx.x, gridDim.x);
+  wo_t1<DT>(L, S, x, h, act, blockIdx.x, gridDim.x,
+            [&]() { stage_copy(S.attn_o, L.Hq * L.D, act); });
 }
 
 // Router logits, then top-k in the workgroup that finishes last.
@@ -115,7 +116,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_router_t1(LayerArgs L, StepAr
                                                              const float* h, int* topk_out) {
   const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
   router_t1<DT>(L, S, h, reinterpret_cast<float*>(msk_smem + o.act0),
-                reinterpret_cast<float*>(msk_smem + o.red), blockIdx.x, gridDim.x);
+                reinterpret_cast<float*>(msk_smem + o.red),
+                reinterpret_cast<float*>(msk_smem + o.act1), blockIdx.x, gridDim.x);
   if (last_workgroup(&S.sync[2], reinterpret_cast<int*>(msk_smem + o.tki))) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (wave_id() == 0) {
@@ -130,8 +132,7 @@ template <int DT>
 __global__ __launch_bounds__(kBlockThreads) void k_gateup_t1(LayerArgs L, StepArgs S) {
   const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
   float* u = reinterpret_cast<float*>(msk_smem + o.act0);
-  stage_copy(S.u, L.H, u);
-  gateup_t1<DT>(L, S, S.idx, u, blockIdx.x, gridDim.x);
+  gateup_t1<DT>(L, S, S.idx, u, blockIdx.x, gridDim.x, [&]() { stage_copy(S.u, L.H, u); });
 }
 
 template <int DT>
@@ -139,8 +140,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_down_t1(LayerArgs L, StepArgs
                                                            float* out) {
   // only the expert activations are staged here: [K][F] after the scratch words
   float* act = reinterpret_cast<float*>(msk_smem + 256);
-  stage_copy(S.act, L.K * L.F, act);
-  down_t1<DT>(L, S, S.idx, S.wts, act, h, out, nullptr, blockIdx.x, gridDim.x);
+  down_t1<DT>(L, S, S.idx, S.wts, act, h, out, nullptr, blockIdx.x, gridDim.x,
+              [&]() { stage_copy(S.act, L.K * L.F, act); });
 }
 
 // The whole one-token step through every layer in one persistent launch.
@@ -176,8 +177,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_step_t1(StepLayers PK) {
     const float* xin = l == 0 ? S.x_in : (((l - 1) & 1) ? S.xb : S.xa);
     float* xout = l == S.n_layers - 1 ? S.x_out : ((l & 1) ? S.xb : S.xa);
 
-    stage_norm_t1(xin, L.attn_norm, L.H, L.eps, act0, red);
-    qkv_t1<DDT>(L, S, act0, vb, nvb);
+    qkv_t1<DDT>(L, S, act0, vb, nvb,
+                [&]() { stage_norm_t1(xin, L.attn_norm, L.H, L.eps, act0, red); });
     stamp();
     grid_sync(gs);
 
@@ -190,12 +191,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_step_t1(StepLayers PK) {
     stamp();
     grid_sync(gs);
 
-    stage_copy(S.attn_o, L.Hq * L.D, act0);
-    wo_t1<DDT>(L, S, xin, S.h, act0, vb, nvb);
+    wo_t1<DDT>(L, S, xin, S.h, act0, vb, nvb,
+               [&]() { stage_copy(S.attn_o, L.Hq * L.D, act0); });
     stamp();
     grid_sync(gs);
 
-    router_t1<DDT>(L, S, S.h, act0, red, vb, nvb);
+    router_t1<DDT>(L, S, S.h, act0, red, act1, vb, nvb);
     stamp();
     grid_sync(gs);
 
@@ -206,13 +207,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_step_t1(StepLayers PK) {
       S.wts[threadIdx.x] = tkw[threadIdx.x];
       if (S.topk_out) S.topk_out[(size_t)l * L.K + threadIdx.x] = tki[threadIdx.x];
     }
-    gateup_t1<EDT>(L, S, tki, act0, vb, nvb);
+    gateup_t1<EDT>(L, S, tki, act0, vb, nvb, []() {});
     stamp();
     grid_sync(gs);
 
-    stage_copy(S.act, L.K * L.F, act1);
     down_t1<EDT>(L, S, tki, tkw, act1, S.h, xout,
-                 S.layer_out ? S.layer_out + (size_t)l * L.H : nullptr, vb, nvb);
+                 S.layer_out ? S.layer_out + (size_t)l * L.H : nullptr, vb, nvb,
+                 [&]() { stage_copy(S.act, L.K * L.F, act1); });
     stamp();
     if (l + 1 < S.n_layers) grid_sync(gs);
   }
@@ -222,12 +223,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_step_t1(StepLayers PK) {
 size_t attn_lds_bytes(int kdt, int D) {
   size_t w = 0;
 #define MSK_GEOM(K, DD) \
-  if (kdt == K && D == DD) w = AttnGeom<K, DD>::LDS_WAVE;
+  if (kdt == K && D == DD) w = AttnGeom<K, DD>::LDS_ITEM;
   MSK_GEOM(kF32, 32) MSK_GEOM(kF32, 64) MSK_GEOM(kF32, 128)
   MSK_GEOM(kBF16, 32) MSK_GEOM(kBF16, 64) MSK_GEOM(kBF16, 128)
   MSK_GEOM(kE4M3, 32) MSK_GEOM(kE4M3, 64) MSK_GEOM(kE4M3, 128)
 #undef MSK_GEOM
-  return align_up(sizeof(AttnPlan), 16) + kWaves * w;
+  return align_up(sizeof(AttnPlan), 16) + w;
 }
 
 static size_t down_lds_bytes(const LayerArgs& L, const StepArgs& S) {
@@ -342,7 +343,7 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
   }
 
   const size_t alds = attn_lds_bytes(L.kdt, L.D);
-  const int agrid = L.n_items < cu_count() * kWaves ? cu_count() : grid_for_waves(L.n_items);
+  const int agrid = L.n_items < 8 * cu_count() ? L.n_items : 8 * cu_count();
 #define MSK_ATTN(K, DD)                                                             \
   if (L.kdt == K && L.D == DD) {                                                    \
     MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_attn<K, DD>), alds));   \
@@ -380,8 +381,8 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
   const int rows = (L.E + DenseRowsHost(nv) - 1) / DenseRowsHost(nv);
   const int grid = grid_for_waves(rows > 64 ? rows : 64);
   if (S.T == 1) {
-    const size_t lds = t1_vec_lds(L);
-    const int g = cu_count();
+    const size_t lds = t1_vec_lds(L) + (size_t)kWaves * kRouterRows * sizeof(float);
+    const int g = L.E < cu_count() ? L.E : cu_count();
     if (L.ddt == kBF16) {
       MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_router_t1<kBF16>), lds));
       MSK_TRY(launch_x(k_router_t1<kBF16>, g, lds, st, L, S, h, topk_out));
@@ -475,7 +476,7 @@ static hipError_t launch_fused_t1(const LayerArgs* Ls, const StepArgs& S, hipStr
   size_t lds = 0;
   for (int l = 0; l < S.n_layers; ++l) {
     const T1Lds o = t1_lds(Ls[l].H, Ls[l].Hq * Ls[l].D, Ls[l].K, Ls[l].F);
-    const size_t a = o.attn + align_up(sizeof(AttnPlan), 16) + kWaves * AttnGeom<KDT, D>::LDS_WAVE;
+    const size_t a = o.attn + align_up(sizeof(AttnPlan), 16) + AttnGeom<KDT, D>::LDS_ITEM;
     lds = lds > o.end_act ? lds : o.end_act;
     lds = lds > a ? lds : a;
   }

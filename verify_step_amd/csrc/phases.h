@@ -135,11 +135,13 @@ __device__ void phase_qkv(const LayerArgs& L, const StepArgs& S, const float* x,
 }
 
 // ------------------------------------------------------- attention
-// One wave per work item (request b, kv head j, query row group rg, chunk c).
-// Rows of a group are (draft token t, query head g of the group) pairs,
-// m = t * G + g, eight at a time.  For each 64-position block of the chunk:
-//  - the K and V rows go straight from HBM into wave-private LDS tiles
-//    (direct global->LDS loads: no registers are held while they fly);
+// One workgroup per work item (request b, kv head j, query row group rg,
+// chunk c).  Rows of a group are (draft token t, query head g of the group)
+// pairs, m = t * G + g, eight at a time, two per wave.  For each 64-position
+// block of the chunk:
+//  - the K and V rows go straight from HBM into the workgroup's LDS tiles
+//    (direct global->LDS loads, shared by the four waves; no registers are
+//    held while they fly);
 //  - a lane then owns one cache position and computes its eight scores
 //    in-lane, reading its K row in a lane-rotated chunk order so the
 //    unpadded tile is read without bank conflicts;
@@ -167,14 +169,15 @@ struct AttnGeom {
   static constexpr int LPP = D / EPLV;        // lanes per position (V)
   static constexpr int PPI = 64 / LPP;        // positions per V step
   static constexpr int NVL = 64 / PPI;        // V steps per block
-  // per-wave LDS: q rows, K tile, V tile, weights, new-key norms, windows
+  // per-workgroup LDS: q rows, K tile, V tile, weights, new-key norms, windows
   static constexpr int LDS_Q = kRowGroup * D * 4;
   static constexpr int LDS_K = TILE;
   static constexpr int LDS_V = TILE;
   static constexpr int LDS_E = kRowGroup * 64 * 4;
   static constexpr int LDS_RK = kMaxTok * 4;
   static constexpr int LDS_WIN = kRowGroup * 8;
-  static constexpr int LDS_WAVE = LDS_Q + LDS_K + LDS_V + LDS_E + LDS_RK + LDS_WIN;
+  static constexpr int LDS_ITEM = LDS_Q + LDS_K + LDS_V + LDS_E + LDS_RK + LDS_WIN;
+  static constexpr int RPW = kRowGroup / kWaves;  // query rows per wave
 };
 
 template <int KDT>
@@ -233,7 +236,7 @@ template <int KDT, int D>
 __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int item,
                           uint8_t* wl) {
   using Gm = AttnGeom<KDT, D>;
-  constexpr int ES = Gm::ES, RB = Gm::RB, CPR = Gm::CPR, EPC = Gm::EPC, NLD = Gm::NLD;
+  constexpr int RB = Gm::RB, CPR = Gm::CPR, EPC = Gm::EPC, NLD = Gm::NLD, RPW = Gm::RPW;
   constexpr int EPLV = Gm::EPLV, VB = Gm::VB, LPP = Gm::LPP, PPI = Gm::PPI, NVL = Gm::NVL;
   float* qs = reinterpret_cast<float*>(wl);
   uint8_t* kt = wl + Gm::LDS_Q;
@@ -242,7 +245,7 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
   float* rk = et + kRowGroup * 64;
   int* win = reinterpret_cast<int*>(rk + kMaxTok);
 
-  const int ln = lane_id();
+  const int ln = lane_id(), wv = wave_id();
   int b = 0;
   while (b + 1 < S.n_req && P->item0[b + 1] <= item) ++b;
   const int nch = P->nch[b];
@@ -263,97 +266,103 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
   uint8_t* vc = L.vc + head_off * RB;
   const bool writer = (rg == 0);
 
-  // normalised, pre-scaled query rows and their windows: all rows' loads are
-  // issued before any reduction waits on them
+  // this wave's query rows, normalised and pre-scaled, and their windows
   constexpr int QD = (D + 63) / 64;
-  float qv[kRowGroup][QD];
+  {
+    float qv[RPW][QD];
 #pragma unroll
-  for (int mm = 0; mm < kRowGroup; ++mm) {
-    const int m = m0 + mm < M ? m0 + mm : M - 1;  // rows past M load a valid row, unused
-    const int t = m / G, g = m - (m / G) * G;
-    const float* q = S.qkv + (size_t)(b * S.Tr + t) * NR + (size_t)(j * G + g) * D;
-#pragma unroll
-    for (int i = 0; i < QD; ++i) {
-      const int d = ln + 64 * i;
-      qv[mm][i] = (m0 + mm < M && d < D) ? q[d] : 0.f;
-    }
-  }
-#pragma unroll
-  for (int mm = 0; mm < kRowGroup; ++mm) {
-    const int m = m0 + mm;
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < QD; ++i) ss += qv[mm][i] * qv[mm][i];
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)D + L.eps);
-#pragma unroll
-    for (int i = 0; i < QD; ++i) {
-      const int d = ln + 64 * i;
-      if (d < D) qs[mm * D + d] = m < M ? qv[mm][i] * r * L.q_norm[d] * L.qscale : 0.f;
-    }
-    if (ln == 0) {
-      const int t = m / G;
-      const int p = Lb + t;
-      win[2 * mm] = m < M ? (L.window > 0 ? (p - L.window + 1 > 0 ? p - L.window + 1 : 0) : 0) : 1;
-      win[2 * mm + 1] = m < M ? p : 0;
-    }
-  }
-  wave_lds_sync();
-  // positions before the group's earliest window start are never visible
-  const int lo_min = win[0];
-  // 1/rms of the step's new keys that fall in this chunk, eight at a time
-  const int tn0 = p0 - Lb > 0 ? p0 - Lb : 0;
-  const int tn1 = p1 - Lb < S.Tr ? p1 - Lb : S.Tr;
-  for (int t0 = tn0; t0 < tn1; t0 += 8) {
-    float kv[8][QD];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int tq = t0 + q < tn1 ? t0 + q : tn1 - 1;
-      const float* k = S.qkv + (size_t)(b * S.Tr + tq) * NR + NQ + (size_t)j * D;
+    for (int r = 0; r < RPW; ++r) {
+      const int mm = wv * RPW + r;
+      const int m = m0 + mm < M ? m0 + mm : M - 1;  // rows past M load a valid row, unused
+      const int t = m / G, g = m - (m / G) * G;
+      const float* q = S.qkv + (size_t)(b * S.Tr + t) * NR + (size_t)(j * G + g) * D;
 #pragma unroll
       for (int i = 0; i < QD; ++i) {
         const int d = ln + 64 * i;
-        kv[q][i] = (t0 + q < tn1 && d < D) ? k[d] : 0.f;
+        qv[r][i] = (m0 + mm < M && d < D) ? q[d] : 0.f;
       }
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int r = 0; r < RPW; ++r) {
+      const int mm = wv * RPW + r;
+      const int m = m0 + mm;
       float ss = 0.f;
 #pragma unroll
-      for (int i = 0; i < QD; ++i) ss += kv[q][i] * kv[q][i];
+      for (int i = 0; i < QD; ++i) ss += qv[r][i] * qv[r][i];
       ss = wave_sum(ss);
-      if (ln == 0 && t0 + q < tn1) rk[t0 + q] = 1.0f / sqrtf(ss / (float)D + L.eps);
+      const float rr = 1.0f / sqrtf(ss / (float)D + L.eps);
+#pragma unroll
+      for (int i = 0; i < QD; ++i) {
+        const int d = ln + 64 * i;
+        if (d < D) qs[mm * D + d] = m < M ? qv[r][i] * rr * L.q_norm[d] * L.qscale : 0.f;
+      }
+      if (ln == 0) {
+        const int t = m / G;
+        const int p = Lb + t;
+        win[2 * mm] = m < M ? (L.window > 0 ? (p - L.window + 1 > 0 ? p - L.window + 1 : 0) : 0) : 1;
+        win[2 * mm + 1] = m < M ? p : 0;
+      }
     }
   }
-  wave_lds_sync();
+  // 1/rms of the step's new keys that fall in this chunk (wave 0)
+  const int tn0 = p0 - Lb > 0 ? p0 - Lb : 0;
+  const int tn1 = p1 - Lb < S.Tr ? p1 - Lb : S.Tr;
+  if (wv == 0) {
+    for (int t0 = tn0; t0 < tn1; t0 += 8) {
+      float kv[8][QD];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int tq = t0 + q < tn1 ? t0 + q : tn1 - 1;
+        const float* k = S.qkv + (size_t)(b * S.Tr + tq) * NR + NQ + (size_t)j * D;
+#pragma unroll
+        for (int i = 0; i < QD; ++i) {
+          const int d = ln + 64 * i;
+          kv[q][i] = (t0 + q < tn1 && d < D) ? k[d] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < QD; ++i) ss += kv[q][i] * kv[q][i];
+        ss = wave_sum(ss);
+        if (ln == 0 && t0 + q < tn1) rk[t0 + q] = 1.0f / sqrtf(ss / (float)D + L.eps);
+      }
+    }
+  }
+  __syncthreads();
+  // positions before the group's earliest window start are never visible
+  const int lo_min = win[0];
 
-  float lsum[kRowGroup];
-  float o[kRowGroup][EPLV];
+  float lsum[RPW];
+  float o[RPW][EPLV];
 #pragma unroll
-  for (int mm = 0; mm < kRowGroup; ++mm) {
-    lsum[mm] = 0.f;
+  for (int r = 0; r < RPW; ++r) {
+    lsum[r] = 0.f;
 #pragma unroll
-    for (int i = 0; i < EPLV; ++i) o[mm][i] = 0.f;
+    for (int i = 0; i < EPLV; ++i) o[r][i] = 0.f;
   }
   const int pg = ln / LPP, dc = ln - (ln / LPP) * LPP;
 
   for (int pb = p0; pb < p1; pb += 64) {
     const int npos = p1 - pb < 64 ? p1 - pb : 64;
-    // cached rows of this block: straight into the LDS tiles.  Lane l of load
-    // i carries tile bytes [i KB + 16 l, +16), i.e. row (1024 i + 16 l) / RB;
-    // only rows that are visible and already cached are fetched.
+    // cached rows of this block straight into the LDS tiles, the 1-KB loads
+    // dealt over the waves.  Lane l of load i carries tile bytes
+    // [i KB + 16 l, +16), i.e. row (1024 i + 16 l) / RB; only rows that are
+    // visible and already cached are fetched.
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
+    for (int i0 = 0; i0 < NLD; i0 += kWaves) {
+      const int i = i0 + wv;
       const int off = i * 1024 + ln * 16;
       const int pos = pb + off / RB;
-      if (pos < pb + npos && pos >= lo_min && pos < Lb) {
+      if (i < NLD && pos < pb + npos && pos >= lo_min && pos < Lb) {
         __builtin_amdgcn_global_load_lds(kc + (size_t)pb * RB + off, kt + i * 1024, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vc + (size_t)pb * RB + off, vt + i * 1024, 16, 0, 0);
       }
     }
     // the step's own rows (positions >= kv_len): rebuilt and stored
     if (pb + npos > Lb) {
-      for (int q = ln; q < 64 * CPR; q += 64) {
+      for (int q = threadIdx.x; q < 64 * CPR; q += blockDim.x) {
         const int row = q / CPR, col = q - (q / CPR) * CPR;
         const int pos = pb + row;
         if (row < npos && pos >= Lb) {
@@ -378,13 +387,15 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
       }
     }
     wait_vm_all();
-    wave_lds_sync();
-    // scores: lane = position, K row read in a lane-rotated chunk order
+    __syncthreads();
+    // scores of this wave's rows: lane = position, K row read in a
+    // lane-rotated chunk order
     {
-      float s[kRowGroup];
+      float s[RPW];
 #pragma unroll
-      for (int mm = 0; mm < kRowGroup; ++mm) s[mm] = 0.f;
+      for (int r = 0; r < RPW; ++r) s[r] = 0.f;
       const uint8_t* krow = kt + ln * RB;
+      const float* qw = qs + wv * RPW * D;
 #pragma unroll 4
       for (int i = 0; i < CPR; ++i) {
         const int cc = (i + ln) & (CPR - 1);
@@ -392,28 +403,29 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
         decode16<KDT>(*reinterpret_cast<const v4u*>(krow + cc * 16), kf);
         const int d0 = cc * EPC;
 #pragma unroll
-        for (int mm = 0; mm < kRowGroup; ++mm) {
+        for (int r = 0; r < RPW; ++r) {
 #pragma unroll
           for (int e4 = 0; e4 < EPC; e4 += 4) {
-            v4f qa = *reinterpret_cast<const v4f*>(qs + mm * D + d0 + e4);
-            s[mm] = fmaf(qa.x, kf[e4], s[mm]);
-            s[mm] = fmaf(qa.y, kf[e4 + 1], s[mm]);
-            s[mm] = fmaf(qa.z, kf[e4 + 2], s[mm]);
-            s[mm] = fmaf(qa.w, kf[e4 + 3], s[mm]);
+            v4f qa = *reinterpret_cast<const v4f*>(qw + r * D + d0 + e4);
+            s[r] = fmaf(qa.x, kf[e4], s[r]);
+            s[r] = fmaf(qa.y, kf[e4 + 1], s[r]);
+            s[r] = fmaf(qa.z, kf[e4 + 2], s[r]);
+            s[r] = fmaf(qa.w, kf[e4 + 3], s[r]);
           }
         }
       }
       const int pos = pb + ln;
 #pragma unroll
-      for (int mm = 0; mm < kRowGroup; ++mm) {
+      for (int r = 0; r < RPW; ++r) {
+        const int mm = wv * RPW + r;
         const bool ok = ln < npos && pos >= win[2 * mm] && pos <= win[2 * mm + 1];
-        const float e = ok ? __expf(s[mm] - L.shift) : 0.f;
+        const float e = ok ? __expf(s[r] - L.shift) : 0.f;
         et[mm * 64 + ln] = e;
-        lsum[mm] += e;
+        lsum[r] += e;
       }
     }
     wave_lds_sync();
-    // o += e * V from the V tile
+    // o += e * V for this wave's rows, from the V tile
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int pp = pg + i * PPI;
@@ -422,30 +434,26 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
         float vf[EPLV];
         decode_v<KDT>(vt + pp * RB + dc * VB, vf);
 #pragma unroll
-        for (int mm = 0; mm < kRowGroup; ++mm) {
-          const float e = et[mm * 64 + pp];
+        for (int r = 0; r < RPW; ++r) {
+          const float e = et[(wv * RPW + r) * 64 + pp];
 #pragma unroll
-          for (int k = 0; k < EPLV; ++k) o[mm][k] = fmaf(e, vf[k], o[mm][k]);
+          for (int k = 0; k < EPLV; ++k) o[r][k] = fmaf(e, vf[k], o[r][k]);
         }
       }
     }
-    wave_lds_sync();
+    __syncthreads();  // tiles are refilled by the next block
   }
-  // reduce over lanes and write the partial sums
+  // reduce over lanes and write this wave's partial sums
   float* part = S.part + (size_t)item * kRowGroup * (D + 1);
 #pragma unroll
-  for (int mm = 0; mm < kRowGroup; ++mm) {
-    const float l = wave_sum(lsum[mm]);
+  for (int r = 0; r < RPW; ++r) {
+    const int mm = wv * RPW + r;
+    const float l = wave_sum(lsum[r]);
 #pragma unroll
-    for (int k = 0; k < EPLV; ++k) {
-      float v = o[mm][k];
-#pragma unroll
-      for (int off = LPP; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-      o[mm][k] = v;
-    }
+    for (int k = 0; k < EPLV; ++k) o[r][k] = sum_groups<LPP>(o[r][k]);
     if (pg == 0) {
 #pragma unroll
-      for (int k = 0; k < EPLV; ++k) part[mm * (D + 1) + dc * EPLV + k] = o[mm][k];
+      for (int k = 0; k < EPLV; ++k) part[mm * (D + 1) + dc * EPLV + k] = o[r][k];
     }
     if (ln == 0) part[mm * (D + 1) + D] = l;
   }
@@ -453,12 +461,12 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
 
 template <int KDT, int D>
 __device__ void phase_attn(const LayerArgs& L, const StepArgs& S, const AttnPlan* P,
-                           uint8_t* lds_waves, int vb, int nvb) {
-  using Gm = AttnGeom<KDT, D>;
-  uint8_t* wl = lds_waves + wave_id() * Gm::LDS_WAVE;
+                           uint8_t* lds, int vb, int nvb) {
   const int n_items = P->item0[S.n_req];
-  for (int item = gwave(vb, nvb); item < n_items; item += nvb * kWaves)
-    attn_item<KDT, D>(L, S, P, item, wl);
+  for (int item = vb; item < n_items; item += nvb) {
+    attn_item<KDT, D>(L, S, P, item, lds);
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------- combine

@@ -47,8 +47,9 @@ __device__ __forceinline__ void lane_store(const float (&acc)[R], F&& st) {
 }
 
 // qkv[r] = sum_c W[r][c] act[c] over the stacked rows of wq, wk, wv.
-template <int DT>
-__device__ void qkv_t1(const LayerArgs& L, const StepArgs& S, const float* act, int vb, int nvb) {
+template <int DT, class Pre>
+__device__ void qkv_t1(const LayerArgs& L, const StepArgs& S, const float* act, int vb, int nvb,
+                       Pre&& pre) {
   constexpr int R = 4, U = 2;
   const int NQ = L.Hq * L.D, NK = L.Hkv * L.D, NR = NQ + 2 * NK;
   const size_t rb = dense_row_bytes(DT, L.H);
@@ -69,13 +70,14 @@ __device__ void qkv_t1(const LayerArgs& L, const StepArgs& S, const float* act, 
       [&](int k, auto& acc) {
         const int r0 = (gw + k * nw) * R;
         lane_store<R>(acc, [&](int r, float v) { S.qkv[r0 + r] = v; });
-      });
+      },
+      pre);
 }
 
 // h[r] = x[r] + sum_c wo[r][c] act[c]  (act = staged attention output)
-template <int DT>
+template <int DT, class Pre>
 __device__ void wo_t1(const LayerArgs& L, const StepArgs& S, const float* x, float* h,
-                      const float* act, int vb, int nvb) {
+                      const float* act, int vb, int nvb, Pre&& pre) {
   constexpr int R = 4, U = 2;
   const int NI = L.Hq * L.D;
   const size_t rb = dense_row_bytes(DT, NI);
@@ -97,34 +99,48 @@ __device__ void wo_t1(const LayerArgs& L, const StepArgs& S, const float* x, flo
         lane_store<R>(acc, [&](int r, float v) {
           if (r0 + r < L.H) h[r0 + r] = x[r0 + r] + v;
         });
-      });
+      },
+      pre);
 }
 
 // u = RMSNorm(h) * ffn_norm into LDS (workgroup vb also writes its slice of
-// u to global memory); logits[e] = w_router[e] . u.
+// u to global memory); logits[e] = w_router[e] . u.  Workgroup vb owns rows
+// vb, vb + nvb, ...; each of its waves streams one quarter of every row and
+// the quarters are added in fixed order.  part: LDS [kWaves][kRouterRows].
+constexpr int kRouterRows = 16;
+
 template <int DT>
 __device__ void router_t1(const LayerArgs& L, const StepArgs& S, const float* h, float* act,
-                          float* red, int vb, int nvb) {
-  stage_norm_t1(h, L.ffn_norm, L.H, L.eps, act, red);
-  {
-    const int per = ((L.H / 4 + nvb - 1) / nvb) * 4;
-    const int c0 = vb * per, c1 = c0 + per < L.H ? c0 + per : L.H;
-    for (int c = c0 + threadIdx.x * 4; c < c1; c += blockDim.x * 4)
-      *reinterpret_cast<v4f*>(S.u + c) = *reinterpret_cast<const v4f*>(act + c);
-  }
+                          float* red, float* part, int vb, int nvb) {
   constexpr int R = 1, U = 2;
+  const int w = wave_id();
+  const int cols = L.H / kWaves;
   const size_t rb = dense_row_bytes(DT, L.H);
-  const int gw = gwave(vb, nvb), nw = nvb * kWaves;
-  const int n = my_count(gw, nw, L.E);
+  const size_t coff = dense_row_bytes(DT, w * cols);
+  const int n = my_count(vb, nvb, L.E);
   stream_t1<DT, R, U>(
-      n, L.H, [&](int) { return act; },
+      n, cols, [&](int) { return act + w * cols; },
       [&](int k, auto& wr, auto& sr) {
-        wr[0] = L.wr + (size_t)(gw + k * nw) * rb;
+        wr[0] = L.wr + (size_t)(vb + k * nvb) * rb + coff;
         sr[0] = nullptr;
       },
       [&](int k, auto& acc) {
-        lane_store<R>(acc, [&](int, float v) { S.logits[gw + k * nw] = v; });
+        if (lane_id() == 0) part[w * kRouterRows + k] = acc[0];
+      },
+      [&]() {
+        stage_norm_t1(h, L.ffn_norm, L.H, L.eps, act, red);
+        const int per = ((L.H / 4 + nvb - 1) / nvb) * 4;
+        const int c0 = vb * per, c1 = c0 + per < L.H ? c0 + per : L.H;
+        for (int c = c0 + threadIdx.x * 4; c < c1; c += blockDim.x * 4)
+          *reinterpret_cast<v4f*>(S.u + c) = *reinterpret_cast<const v4f*>(act + c);
       });
+  __syncthreads();
+  for (int k = threadIdx.x; k < n; k += blockDim.x) {
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) v += part[q * kRouterRows + k];
+    S.logits[vb + k * nvb] = v;
+  }
 }
 
 // Top-k of one token's logits by one wave (value descending, index ascending
@@ -195,9 +211,9 @@ __device__ inline bool last_workgroup(unsigned* counter, int* flag_lds) {
 }
 
 // act[j][f] = silu(gate_e[f] . u) * (up_e[f] . u), e = idx[j]; u staged in LDS.
-template <int DT>
+template <int DT, class Pre>
 __device__ void gateup_t1(const LayerArgs& L, const StepArgs& S, const int* idx, const float* u,
-                          int vb, int nvb) {
+                          int vb, int nvb, Pre&& pre) {
   constexpr int R = 2, U = 2;
   const int nrb = L.F / R;
   const size_t rb = expert_row_bytes(DT, L.H);
@@ -228,15 +244,16 @@ __device__ void gateup_t1(const LayerArgs& L, const StepArgs& S, const int* idx,
 #pragma unroll
         for (int r = 0; r < R; ++r) res[r] = silu(acc[r] * gs) * (acc[R + r] * us);
         lane_store<R>(res, [&](int r, float v) { S.act[(size_t)j * L.F + f0 + r] = v; });
-      });
+      },
+      pre);
 }
 
 // out[c] = h[c] + sum_j w[j] * (down_e[c] . act[j]), e = idx[j], in slot order;
 // act staged in LDS as [K][F].  Entries of idx outside [0, E) add nothing.
-template <int DT>
+template <int DT, class Pre>
 __device__ void down_t1(const LayerArgs& L, const StepArgs& S, const int* idx, const float* wts,
                         const float* act, const float* h, float* out, float* out2, int vb,
-                        int nvb) {
+                        int nvb, Pre&& pre) {
   constexpr int R = 4, U = 2;
   const size_t rb = expert_row_bytes(DT, L.F);
   const size_t sb = (size_t)L.F / 16;
@@ -279,7 +296,8 @@ __device__ void down_t1(const LayerArgs& L, const StepArgs& S, const int* idx, c
 #pragma unroll
           for (int r = 0; r < R; ++r) o[r] = 0.f;
         }
-      });
+      },
+      pre);
 }
 
 }  // namespace msk
