@@ -3,9 +3,15 @@
 One step = one call of msk_layer_step over the workload's layer stack with
 inputs already resident in HBM.  Prints one JSON line:
   value          microseconds per layer-step (lower is better)
-  roofline       the step kernel's achieved HBM GB/s on its algorithmic bytes
-                 (distinct dense + router + selected-expert + attended-KV bytes)
-                 against MI355X's 8 TB/s
+  hbm_gbs        whole-step algorithmic bytes (distinct dense + router +
+                 selected-expert + attended-KV bytes) per second
+  roofline       the dominant kernel (the phase with the most kernel time in
+                 a second pass of the same steps, each launch bracketed by
+                 dispatch-stamped HIP events): its algorithmic bytes per
+                 launch / its mean launch duration, against MI355X's 8 TB/s;
+                 traffic = HBM bytes per launch from the committed counter
+                 summary, if the kernel sources still match it
+  kernels        the same figures for every phase
   cpu_baseline   the CPU oracle timed on the same workload on this host
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -24,6 +30,7 @@ import torch  # noqa: E402
 
 import synth  # noqa: E402
 import verify_step_amd as msk  # noqa: E402
+from verify_step_amd import profsum  # noqa: E402
 
 METRIC = "µs per MoE layer decode/verify step + achieved HBM GB/s (% of peak)"
 HBM_PEAK_GBS = 8000.0
@@ -31,37 +38,83 @@ ES = {"f32": 4, "bf16": 2, "e4m3": 1}
 
 
 def expert_bytes(spec):
+    """(gate + up, down) bytes of one expert in its storage format."""
     H, F = spec["hidden"], spec["ffn_dim"]
-    n = 3 * H * F
+    n = H * F
     if spec["expert_dtype"] == "nvfp4":
-        return n // 2 + n // 16 + 3 * 4
-    return n * ES[spec["expert_dtype"]]
+        one = n // 2 + n // 16 + 4          # codes, e4m3 block scales, fp32 matrix scale
+    else:
+        one = n * ES[spec["expert_dtype"]]
+    return 2 * one, one
+
+
+def union_kv_positions(spec, kv_len, Tr):
+    """Cache positions the step must read per (request, kv head): the union of
+    its draft tokens' windows, appended positions included."""
+    W = spec["window"]
+    n = 0
+    for L in kv_len:
+        lo = max(0, L - W + 1) if W > 0 else 0
+        n += L + Tr - lo
+    return n
+
+
+def phase_bytes(spec, kv_len, Tr, topk_l):
+    """Algorithmic bytes of one launch of each phase's kernel for one layer:
+    the weights (each distinct selected expert once) or cache rows it must
+    stream, plus its activation inputs and outputs."""
+    T = len(kv_len) * Tr
+    H, Hq, Hkv, D, E, K, F = (spec[k] for k in ("hidden", "n_q_heads", "n_kv_heads", "head_dim",
+                                                 "n_experts", "top_k", "ffn_dim"))
+    es, kes = ES[spec["dense_dtype"]], ES[spec["kv_dtype"]]
+    NR = (Hq + 2 * Hkv) * D
+    n_exp = len(np.unique(topk_l))
+    gu, dn = expert_bytes(spec)
+    kv = union_kv_positions(spec, kv_len, Tr) * Hkv * D * kes * 2
+    return dict(
+        qkv=NR * H * es + (H + 2 * D) * 4 + T * H * 4 + T * NR * 4 + T * 2 * Hkv * D * kes,
+        attn=kv + T * Hq * D * 4,
+        combine=T * Hq * D * 4,
+        wo=H * Hq * D * es + T * Hq * D * 4 + 2 * T * H * 4,
+        router=E * H * es + H * 4 + 2 * T * H * 4 + T * E * 4,
+        topk=T * E * 4 + 2 * T * K * 4,
+        gateup=n_exp * gu + T * H * 4 + T * K * F * 4,
+        down=n_exp * dn + T * K * F * 4 + 2 * T * H * 4,
+    )
 
 
 def algorithmic_bytes(specs, kv_len, Tr, topk):
     """Bytes the step must read at least once: every dense weight, norm gain
     and router row, each distinct selected expert once, and the K and V rows
     of the union of the draft tokens' windows per (request, kv head)."""
-    total = 0
     parts = dict(dense=0, experts=0, kv=0)
     for l, spec in enumerate(specs):
         H, Hq, Hkv, D, E = (spec[k] for k in ("hidden", "n_q_heads", "n_kv_heads", "head_dim",
                                                "n_experts"))
         es = ES[spec["dense_dtype"]]
-        dense = (Hq * D + 2 * Hkv * D) * H * es + H * Hq * D * es + E * H * es + (2 * H + 2 * D) * 4
-        n_exp = len(np.unique(topk[l]))
-        experts = n_exp * expert_bytes(spec)
-        kv = 0
-        W = spec["window"]
-        for L in kv_len:
-            lo = max(0, L - W + 1) if W > 0 else 0
-            hi = L + Tr - 1
-            kv += (hi - lo + 1) * Hkv * D * ES[spec["kv_dtype"]] * 2
-        parts["dense"] += dense
-        parts["experts"] += experts
-        parts["kv"] += kv
-        total += dense + experts + kv
-    return total, parts
+        parts["dense"] += ((Hq * D + 2 * Hkv * D) * H * es + H * Hq * D * es + E * H * es
+                           + (2 * H + 2 * D) * 4)
+        parts["experts"] += len(np.unique(topk[l])) * sum(expert_bytes(spec))
+        parts["kv"] += union_kv_positions(spec, kv_len, Tr) * Hkv * D * ES[spec["kv_dtype"]] * 2
+    return sum(parts.values()), parts
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    calibration) from the committed counter summary of this kernel and
+    workload, or None when there is none or the kernel sources have changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            kv[k.strip()] = v.strip().strip("`")
+    if kv.get("sources_sha256") != profsum.sources_digest():
+        return None
+    return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
 
 
 def cpu_baseline(p, budget_s=30.0):
@@ -131,6 +184,55 @@ def timeline(p, ws, x):
     return dict(total_us=round(prev - t0, 2), phases=out)
 
 
+KERNEL_NAMES = {"qkv": "k_qkv", "attn": "k_attn", "combine": "k_combine", "wo": "k_wo",
+                "router": "k_router", "topk": "k_topk", "gateup": "k_gateup", "down": "k_down",
+                "step": "k_step_t1"}
+ONE_TOKEN_KERNELS = ("qkv", "wo", "router", "gateup", "down")
+
+
+def kernel_name(phase, T):
+    base = KERNEL_NAMES[phase]
+    return base + "_t1" if T == 1 and phase in ONE_TOKEN_KERNELS else base
+
+
+def kernel_pass(p, x, ws, steps, stream):
+    """Run `steps` more steps with every phase kernel bracketed by HIP events
+    (msk_timer_start), each step recording its routing.  Returns per phase
+    the summed kernel time, the launch count and the algorithmic bytes of
+    those launches, plus the mean whole-step bytes."""
+    n_layers, K = len(p.specs), p.specs[0]["top_k"]
+    topk = torch.zeros((steps, n_layers, p.T, K), dtype=torch.int32, device=x.device)
+    runs = [msk.Step(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws,
+                     topk_idx=topk[i]) for i in range(steps)]
+    msk.timer_start()
+    for r in runs:
+        r(stream)
+    torch.cuda.synchronize()
+    res = {ph: dict(ms=0.0, launches=0, bytes=0) for ph in msk.PHASES}
+    for ph in msk.PHASES:
+        res[ph]["ms"], res[ph]["launches"] = msk.timer_read(ph)
+    msk.timer_start(())
+    tk = topk.cpu().numpy()
+    step_bytes = []
+    for i in range(steps):
+        step_bytes.append(algorithmic_bytes(p.specs, p.kv_len, p.tokens_per_req, tk[i]))
+        for l, spec in enumerate(p.specs):
+            for ph, b in phase_bytes(spec, p.kv_len, p.tokens_per_req, tk[i][l]).items():
+                res[ph]["bytes"] += b
+    return res, step_bytes
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device copy of known size, run under the counter passes to
+    scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,15 +241,20 @@ def main():
     ap.add_argument("--workload", default="decode-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
-                    help="fused: msk_layer_step (one persistent kernel); unfused: the "
-                         "msk_attn_step -> msk_moe_route -> msk_expert_ffn calls per layer")
+                    help="fused: msk_layer_step; unfused: the msk_attn_step -> msk_moe_route "
+                         "-> msk_expert_ffn calls per layer")
     ap.add_argument("--timeline", action="store_true",
                     help="also print per-phase times of the persistent kernel")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer step runs on a single MI355X "
               "(no multi-GPU path is built)", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        copy_calibration()
+        return
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -155,11 +262,8 @@ def main():
     for spec, w in zip(p.specs, p.weights):
         spec["softmax_shift"] = msk.softmax_shift(w["q_norm"], w["k_norm"], spec["head_dim"])
     n_layers = len(p.specs)
-    K = p.specs[0]["top_k"]
     ws = msk.new_workspace(p.specs, p.kv_len, p.tokens_per_req, device=dev)
     x = p.x.clone()
-    topk = torch.zeros((n_layers, p.T, K), dtype=torch.int32, device=dev)
-    probe = msk.Step(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws, topk_idx=topk)
     step = msk.Step(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws)
     if args.path == "unfused":
         step = unfused_step(p, x, ws)
@@ -170,6 +274,7 @@ def main():
     torch.cuda.synchronize()
     msk.workspace_status(ws)
 
+    # the timed region: K steps back to back, nothing else on the stream
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -182,11 +287,20 @@ def main():
     ms_step = ms_total / args.steps
     us_layer = ms_step * 1e3 / n_layers
 
-    # one more step that records its routing, for the distinct-expert bytes
-    probe(stream)
-    torch.cuda.synchronize()
-    nbytes, parts = algorithmic_bytes(p.specs, p.kv_len, p.tokens_per_req, topk.cpu().numpy())
+    # the same K steps again, each kernel bracketed by dispatch-stamped events
+    kp, step_bytes = kernel_pass(p, x, ws, args.steps, stream)
+    msk.workspace_status(ws)
+    nbytes = int(np.mean([b for b, _ in step_bytes]))
+    parts = {k: int(np.mean([pp[k] for _, pp in step_bytes])) for k in step_bytes[0][1]}
     gbs = nbytes / (ms_step * 1e-3) / 1e9
+    timed = {ph: r for ph, r in kp.items() if r["launches"]}
+    dom = max(timed, key=lambda ph: timed[ph]["ms"])
+    d = timed[dom]
+    avg_us = d["ms"] * 1e3 / d["launches"]
+    bytes_launch = d["bytes"] / d["launches"] if dom != "step" else nbytes
+    kgbs = bytes_launch / (avg_us * 1e-6) / 1e9
+    kname = kernel_name(dom, p.T)
+    traffic = stored_traffic(kname, args.workload)
 
     out = {
         "metric": METRIC,
@@ -209,12 +323,18 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes": nbytes,
         "bytes_breakdown": parts,
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_step_t1 (persistent whole step)" if args.path == "fused"
-                     else "whole layer step (per-phase kernels)"},
+        "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": kname, "phase": dom,
+                     "bytes_per_launch": int(bytes_launch), "avg_launch_us": round(avg_us, 3),
+                     "launches": d["launches"]},
+        "kernels": {ph: {"avg_us": round(r["ms"] * 1e3 / r["launches"], 3),
+                         "launches": r["launches"],
+                         "gbs": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1)
+                         if ph != "step" else None}
+                    for ph, r in timed.items()},
+        "path": args.path,
     }
-    out["path"] = args.path
     if args.timeline and args.path == "fused":
         out["timeline"] = timeline(p, ws, x)
     if not args.no_cpu_baseline:

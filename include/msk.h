@@ -208,6 +208,34 @@ msk_status msk_layer_step_timeline(const msk_layer_cfg *cfg, const msk_layer_wei
                                    float *x, int64_t *stamps, void *ws, size_t ws_bytes,
                                    void *stream);
 
+/* Kernel timing for measurement harnesses.  The step's kernels fall into
+ * phases:
+ *   MSK_PH_QKV      RMSNorm + QKV projection + QK-norm + KV append
+ *   MSK_PH_ATTN     split-KV no-max attention partials
+ *   MSK_PH_COMBINE  sum of the partials, window bounds
+ *   MSK_PH_WO       output projection + residual
+ *   MSK_PH_ROUTER   FFN RMSNorm + router logits (+ top-k for one token)
+ *   MSK_PH_TOPK     top-k and gating weights (more than one token)
+ *   MSK_PH_GATEUP   expert gate/up + SwiGLU
+ *   MSK_PH_DOWN     expert down + weighted combine + residual
+ *   MSK_PH_STEP     the persistent whole-step kernel, where it runs
+ * msk_timer_start(mask) forgets earlier records and, from then on, brackets
+ * every launch of each phase whose bit (1 << phase) is set in mask with a
+ * pair of HIP events that the dispatch itself stamps (hipExtLaunchKernel),
+ * so a pair measures that kernel alone, on the stream it runs on.  mask 0
+ * stops timing.  msk_timer_read(phase, &ms, &n) waits for the phase's last
+ * recorded launch and returns the summed duration in milliseconds and the
+ * number of launches recorded since the last msk_timer_start.  The library
+ * keeps one process-wide timer: calls on several threads or streams at once
+ * are recorded together.  Errors: MSK_ERR_INVALID_ARG for a phase outside
+ * the list or null outputs, MSK_ERR_DEVICE when an event call fails. */
+enum {
+  MSK_PH_QKV = 0, MSK_PH_ATTN = 1, MSK_PH_COMBINE = 2, MSK_PH_WO = 3, MSK_PH_ROUTER = 4,
+  MSK_PH_TOPK = 5, MSK_PH_GATEUP = 6, MSK_PH_DOWN = 7, MSK_PH_STEP = 8, MSK_N_PHASES = 9
+};
+msk_status msk_timer_start(uint32_t mask);
+msk_status msk_timer_read(int32_t phase, double *total_ms, int64_t *launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -94,6 +94,10 @@ def lib():
         L.msk_layer_step.restype = i32
         L.msk_layer_step.argtypes = [P(LayerCfg), P(LayerWeights), P(KV), i32, P(Batch), vp, vp,
                                      vp, vp, vp, sz, vp]
+        L.msk_timer_start.restype = i32
+        L.msk_timer_start.argtypes = [ctypes.c_uint32]
+        L.msk_timer_read.restype = i32
+        L.msk_timer_read.argtypes = [i32, P(ctypes.c_double), P(ctypes.c_int64)]
         L.msk_layer_step_timeline.restype = i32
         L.msk_layer_step_timeline.argtypes = [P(LayerCfg), P(LayerWeights), P(KV), i32, P(Batch),
                                               vp, vp, vp, sz, vp]
@@ -229,6 +233,25 @@ def layer_step(specs, weights, kvs, kv_len, tokens_per_req, x, ws, layer_out=Non
                                 _ptr(topk_idx), _ptr(win), _ptr(ws), ws.numel(),
                                 _stream(stream)))
     return x
+
+
+PHASES = ("qkv", "attn", "combine", "wo", "router", "topk", "gateup", "down", "step")
+
+
+def timer_start(phases=PHASES):
+    """Time every later launch of the named phases' kernels with HIP events
+    stamped by the dispatch (msk_timer_start); an empty list stops timing."""
+    mask = 0
+    for ph in phases:
+        mask |= 1 << PHASES.index(ph)
+    _check(lib().msk_timer_start(mask))
+
+
+def timer_read(phase):
+    """(summed milliseconds, launches) of one phase since timer_start."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(lib().msk_timer_read(PHASES.index(phase), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def layer_step_timeline(specs, weights, kvs, kv_len, tokens_per_req, x, ws, stamps, stream=None):

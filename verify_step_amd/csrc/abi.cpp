@@ -460,4 +460,22 @@ msk_status msk_layer_step_timeline(const msk_layer_cfg* cfg, const msk_layer_wei
                          ws_bytes, stream);
 }
 
+static_assert(MSK_N_PHASES == msk::kNumPhases && MSK_PH_STEP == msk::kPhStep &&
+                  MSK_PH_GATEUP == msk::kPhGateUp && MSK_PH_ATTN == msk::kPhAttn,
+              "phase numbering of the header and the launchers must agree");
+
+msk_status msk_timer_start(uint32_t mask) {
+  if (mask >> msk::kNumPhases) return fail(MSK_ERR_INVALID_ARG, "timer mask names no phase");
+  return device_status(msk::timer_start(mask), "timer start");
+}
+
+msk_status msk_timer_read(int32_t phase, double* total_ms, int64_t* launches) {
+  if (phase < 0 || phase >= msk::kNumPhases) return fail(MSK_ERR_INVALID_ARG, "no such phase");
+  if (!total_ms || !launches) return fail(MSK_ERR_INVALID_ARG, "null output");
+  long long n = 0;
+  const msk_status st = device_status(msk::timer_read(phase, total_ms, &n), "timer read");
+  *launches = n;
+  return st;
+}
+
 }  // extern "C"

@@ -2,6 +2,12 @@
 // launchers.  Each phase of the step is also a kernel of its own (the
 // unfused path); the fused path runs every phase of every layer in one
 // persistent cooperative launch with grid barriers between dependent phases.
+#include <hip/hip_ext.h>
+
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "launch.h"
 #include "phases_t1.h"
 
@@ -271,17 +277,79 @@ static int t1_grid(long long tasks) {
   return (int)g;
 }
 
-template <class K>
-static hipError_t launch(K kernel, int grid, size_t lds, hipStream_t st, const LayerArgs& L,
-                         const StepArgs& S) {
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlockThreads), lds, st, L, S);
-  return hipGetLastError();
+#define MSK_TRY(x)                          \
+  do {                                      \
+    hipError_t e_ = (x);                    \
+    if (e_ != hipSuccess) return e_;        \
+  } while (0)
+
+// ------------------------------------------------------ kernel timing
+// While a phase's bit is armed, each launch of that phase's kernel takes a
+// pair of HIP events stamped by the dispatch itself (hipExtLaunchKernel), so
+// the pair brackets the kernel and nothing else.  Events are created on
+// first use and reused after msk_timer_start re-arms.
+struct PhaseTimer {
+  std::mutex mu;
+  uint32_t mask = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[kNumPhases];
+  size_t used[kNumPhases] = {};
+};
+static PhaseTimer g_timer;
+
+static hipError_t timer_pair(int ph, hipEvent_t* a, hipEvent_t* b) {
+  *a = *b = nullptr;
+  std::lock_guard<std::mutex> g(g_timer.mu);
+  if (!(g_timer.mask >> ph & 1u)) return hipSuccess;
+  auto& v = g_timer.ev[ph];
+  if (g_timer.used[ph] == v.size()) {
+    hipEvent_t e0, e1;
+    MSK_TRY(hipEventCreate(&e0));
+    MSK_TRY(hipEventCreate(&e1));
+    v.emplace_back(e0, e1);
+  }
+  *a = v[g_timer.used[ph]].first;
+  *b = v[g_timer.used[ph]].second;
+  ++g_timer.used[ph];
+  return hipSuccess;
+}
+
+hipError_t timer_start(uint32_t mask) {
+  std::lock_guard<std::mutex> g(g_timer.mu);
+  g_timer.mask = mask;
+  for (int p = 0; p < kNumPhases; ++p) g_timer.used[p] = 0;
+  return hipSuccess;
+}
+
+hipError_t timer_read(int ph, double* total_ms, long long* launches) {
+  std::lock_guard<std::mutex> g(g_timer.mu);
+  double sum = 0;
+  for (size_t i = 0; i < g_timer.used[ph]; ++i) {
+    float ms = 0;
+    MSK_TRY(hipEventSynchronize(g_timer.ev[ph][i].second));
+    MSK_TRY(hipEventElapsedTime(&ms, g_timer.ev[ph][i].first, g_timer.ev[ph][i].second));
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (long long)g_timer.used[ph];
+  return hipSuccess;
 }
 
 template <class K, class... A>
-static hipError_t launch_x(K kernel, int grid, size_t lds, hipStream_t st, A... args) {
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlockThreads), lds, st, args...);
+static hipError_t launch_x(int ph, K kernel, int grid, size_t lds, hipStream_t st, A... args) {
+  hipEvent_t e0, e1;
+  MSK_TRY(timer_pair(ph, &e0, &e1));
+  if (e0)
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kBlockThreads), (uint32_t)lds, st, e0, e1, 0,
+                          args...);
+  else
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlockThreads), lds, st, args...);
   return hipGetLastError();
+}
+
+template <class K>
+static hipError_t launch(int ph, K kernel, int grid, size_t lds, hipStream_t st,
+                         const LayerArgs& L, const StepArgs& S) {
+  return launch_x(ph, kernel, grid, lds, st, L, S);
 }
 
 static hipError_t set_lds_limit(const void* fn, size_t bytes) {
@@ -289,11 +357,6 @@ static hipError_t set_lds_limit(const void* fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-#define MSK_TRY(x)                          \
-  do {                                      \
-    hipError_t e_ = (x);                    \
-    if (e_ != hipSuccess) return e_;        \
-  } while (0)
 
 // ------------------------------------------------------ launchers
 // Token-group width of the dense projections: the smallest power of two
@@ -331,15 +394,15 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
     const int g = t1_grid(NR / 4);
     if (L.ddt == kBF16) {
       MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_qkv_t1<kBF16>), lds));
-      MSK_TRY(launch_x(k_qkv_t1<kBF16>, g, lds, st, L, S, x));
+      MSK_TRY(launch_x(kPhQkv, k_qkv_t1<kBF16>, g, lds, st, L, S, x));
     } else {
       MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_qkv_t1<kF32>), lds));
-      MSK_TRY(launch_x(k_qkv_t1<kF32>, g, lds, st, L, S, x));
+      MSK_TRY(launch_x(kPhQkv, k_qkv_t1<kF32>, g, lds, st, L, S, x));
     }
   } else if (L.ddt == kBF16) {
-    MSK_NV_CASES(nv, MSK_TRY(launch_x(k_qkv<kBF16, NV>, qgrid, rs_lds, st, L, S, x)))
+    MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhQkv, k_qkv<kBF16, NV>, qgrid, rs_lds, st, L, S, x)))
   } else {
-    MSK_NV_CASES(nv, MSK_TRY(launch_x(k_qkv<kF32, NV>, qgrid, rs_lds, st, L, S, x)))
+    MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhQkv, k_qkv<kF32, NV>, qgrid, rs_lds, st, L, S, x)))
   }
 
   const size_t alds = attn_lds_bytes(L.kdt, L.D);
@@ -347,13 +410,13 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
 #define MSK_ATTN(K, DD)                                                             \
   if (L.kdt == K && L.D == DD) {                                                    \
     MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_attn<K, DD>), alds));   \
-    MSK_TRY(launch(k_attn<K, DD>, agrid, alds, st, L, S));                          \
+    MSK_TRY(launch(kPhAttn, k_attn<K, DD>, agrid, alds, st, L, S));                          \
   }
   MSK_ATTN(kF32, 32) MSK_ATTN(kF32, 64) MSK_ATTN(kF32, 128)
   MSK_ATTN(kBF16, 32) MSK_ATTN(kBF16, 64) MSK_ATTN(kBF16, 128)
   MSK_ATTN(kE4M3, 32) MSK_ATTN(kE4M3, 64) MSK_ATTN(kE4M3, 128)
 #undef MSK_ATTN
-  MSK_TRY(launch_x(k_combine, grid_for_waves((long long)S.T * L.Hq), sizeof(AttnPlan), st, L, S,
+  MSK_TRY(launch_x(kPhCombine, k_combine, grid_for_waves((long long)S.T * L.Hq), sizeof(AttnPlan), st, L, S,
                    S.win_out));
   const int wgrid = grid_for_waves(L.H / DenseRowsHost(nv));
   if (one) {
@@ -361,15 +424,15 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
     const int g = t1_grid((L.H + 3) / 4);
     if (L.ddt == kBF16) {
       MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_wo_t1<kBF16>), lds));
-      MSK_TRY(launch_x(k_wo_t1<kBF16>, g, lds, st, L, S, x, h));
+      MSK_TRY(launch_x(kPhWo, k_wo_t1<kBF16>, g, lds, st, L, S, x, h));
     } else {
       MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_wo_t1<kF32>), lds));
-      MSK_TRY(launch_x(k_wo_t1<kF32>, g, lds, st, L, S, x, h));
+      MSK_TRY(launch_x(kPhWo, k_wo_t1<kF32>, g, lds, st, L, S, x, h));
     }
   } else if (L.ddt == kBF16) {
-    MSK_NV_CASES(nv, MSK_TRY(launch_x(k_wo<kBF16, NV>, wgrid, 0, st, L, S, x, h)))
+    MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhWo, k_wo<kBF16, NV>, wgrid, 0, st, L, S, x, h)))
   } else {
-    MSK_NV_CASES(nv, MSK_TRY(launch_x(k_wo<kF32, NV>, wgrid, 0, st, L, S, x, h)))
+    MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhWo, k_wo<kF32, NV>, wgrid, 0, st, L, S, x, h)))
   }
   return hipSuccess;
 }
@@ -385,18 +448,18 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
     const int g = L.E < cu_count() ? L.E : cu_count();
     if (L.ddt == kBF16) {
       MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_router_t1<kBF16>), lds));
-      MSK_TRY(launch_x(k_router_t1<kBF16>, g, lds, st, L, S, h, topk_out));
+      MSK_TRY(launch_x(kPhRouter, k_router_t1<kBF16>, g, lds, st, L, S, h, topk_out));
     } else {
       MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_router_t1<kF32>), lds));
-      MSK_TRY(launch_x(k_router_t1<kF32>, g, lds, st, L, S, h, topk_out));
+      MSK_TRY(launch_x(kPhRouter, k_router_t1<kF32>, g, lds, st, L, S, h, topk_out));
     }
     return hipSuccess;
   } else if (L.ddt == kBF16) {
-    MSK_NV_CASES(nv, MSK_TRY(launch_x(k_router<kBF16, NV>, grid, rs_lds, st, L, S, h)))
+    MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhRouter, k_router<kBF16, NV>, grid, rs_lds, st, L, S, h)))
   } else {
-    MSK_NV_CASES(nv, MSK_TRY(launch_x(k_router<kF32, NV>, grid, rs_lds, st, L, S, h)))
+    MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhRouter, k_router<kF32, NV>, grid, rs_lds, st, L, S, h)))
   }
-  MSK_TRY(launch_x(k_topk, grid_for_waves(S.T), 0, st, L, S, topk_out));
+  MSK_TRY(launch_x(kPhTopk, k_topk, grid_for_waves(S.T), 0, st, L, S, topk_out));
   return hipSuccess;
 }
 
@@ -405,9 +468,9 @@ static hipError_t launch_ffn_t1(const LayerArgs& L, const StepArgs& S, const flo
                                 hipStream_t st) {
   const size_t vlds = t1_vec_lds(L), alds = 256 + (size_t)4 * L.K * L.F;
   MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_gateup_t1<DT>), vlds));
-  MSK_TRY(launch(k_gateup_t1<DT>, t1_grid((long long)L.K * (L.F / 2)), vlds, st, L, S));
+  MSK_TRY(launch(kPhGateUp, k_gateup_t1<DT>, t1_grid((long long)L.K * (L.F / 2)), vlds, st, L, S));
   MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_down_t1<DT>), alds));
-  MSK_TRY(launch_x(k_down_t1<DT>, t1_grid((L.H + 3) / 4), alds, st, L, S, h, out));
+  MSK_TRY(launch_x(kPhDown, k_down_t1<DT>, t1_grid((L.H + 3) / 4), alds, st, L, S, h, out));
   return hipSuccess;
 }
 
@@ -419,9 +482,9 @@ static hipError_t launch_ffn_t(const LayerArgs& L, const StepArgs& S, const floa
   // the number of distinct experts is known only on the device: size the
   // gate/up grid for the largest possible union, capped
   const long long gu_items = (long long)(S.T * L.K < L.E ? S.T * L.K : L.E) * (L.F / 4);
-  MSK_TRY(launch(k_gateup<DT, NV>, grid_for_waves(gu_items), ulds, st, L, S));
+  MSK_TRY(launch(kPhGateUp, k_gateup<DT, NV>, grid_for_waves(gu_items), ulds, st, L, S));
   MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_down<DT, NV>), dlds));
-  MSK_TRY(launch_x(k_down<DT, NV>, grid_for_waves(L.H / 4), dlds, st, L, S, h, out));
+  MSK_TRY(launch_x(kPhDown, k_down<DT, NV>, grid_for_waves(L.H / 4), dlds, st, L, S, h, out));
   return hipSuccess;
 }
 
@@ -491,8 +554,13 @@ static hipError_t launch_fused_t1(const LayerArgs* Ls, const StepArgs& S, hipStr
   for (int l = 0; l < kMaxLayers; ++l) P.L[l] = Ls[l < S.n_layers ? l : 0];
   void* args[] = {&P};
   *launched = true;
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(grid),
-                                    dim3(kBlockThreads), args, (unsigned)lds, st);
+  hipEvent_t e0, e1;
+  MSK_TRY(timer_pair(kPhStep, &e0, &e1));
+  if (e0) MSK_TRY(hipEventRecord(e0, st));
+  MSK_TRY(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(grid),
+                                     dim3(kBlockThreads), args, (unsigned)lds, st));
+  if (e1) MSK_TRY(hipEventRecord(e1, st));
+  return hipSuccess;
 }
 
 // The persistent one-token kernel runs for all-fp32 stacks; every other

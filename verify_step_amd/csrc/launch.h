@@ -21,6 +21,12 @@ hipError_t launch_step_fused(const LayerArgs* Ls, const StepArgs& S, hipStream_t
 // Whole step as a sequence of per-phase kernels (the unfused comparison path).
 hipError_t launch_step_unfused(const LayerArgs* Ls, const StepArgs& S, hipStream_t st);
 
+// Kernel timing (msk_timer_start / msk_timer_read): arm the phases in
+// `mask`, forget earlier records; read the summed milliseconds and launch
+// count of one phase, waiting for its last recorded launch.
+hipError_t timer_start(uint32_t mask);
+hipError_t timer_read(int phase, double* total_ms, long long* launches);
+
 // LDS bytes a launch needs, for the planner's checks.
 size_t attn_lds_bytes(int kdt, int D);
 

@@ -15,6 +15,12 @@ constexpr int kWaves = kBlockThreads / 64;
 
 enum Dt : int { kF32 = 0, kBF16 = 1, kE4M3 = 2, kNVFP4 = 3 };
 
+// Kernel phases, as numbered by the timing calls of the C ABI.
+enum Phase : int {
+  kPhQkv = 0, kPhAttn, kPhCombine, kPhWo, kPhRouter, kPhTopk, kPhGateUp, kPhDown, kPhStep,
+  kNumPhases
+};
+
 // One layer's shapes, weights, cache and attention plan.
 struct LayerArgs {
   int H, Hq, Hkv, D, E, K, F, window;
