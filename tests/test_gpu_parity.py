@@ -36,6 +36,13 @@ CASES = {
     "d64-bf16kv": ("decode-bf16", dict(dims=dict(_SMALL, head_dim=64, n_q_heads=8),
                                        kv_len=[130, 5], windows=[64], tokens_per_req=3,
                                        n_req=2)),
+    # 96 query rows per kv head (two row groups on the matrix cores), each
+    # draft with its own sliding window, bf16 cache
+    "verify-m96-bf16kv": ("verify-bf16-128k", dict(dims=_SMALL, kv="bf16", kv_len=[300],
+                                                   n_req=1, tokens_per_req=16, windows=[100])),
+    # 12 rows per kv head over a bf16 cache of head_dim 128 (two-wave items)
+    "verify-tr2-bf16kv": ("verify-bf16-128k", dict(dims=_SMALL, kv="bf16", kv_len=[200, 129],
+                                                   tokens_per_req=2)),
 }
 
 

@@ -41,12 +41,24 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 constexpr long long kTargetItems = 2048;
 
 struct AttnSplit {
-  int chunk, n_items, nrg;
+  int chunk, n_items, nrg, rows, nw;
 };
 
+// Query rows of one (request, kv head) pair, G * Tr, go to the matrix cores
+// when they fill more than one row group of the vector path and the cache
+// values are exact in bf16 (bf16 or e4m3 caches); each wave then takes 16
+// rows, at most four waves per item.
 AttnSplit plan_attention(const msk_layer_cfg& c, const msk_batch& b) {
   const int G = c.n_q_heads / c.n_kv_heads;
-  const int nrg = cdiv((long long)G * b.tokens_per_req, msk::kRowGroup);
+  const int M = G * b.tokens_per_req;
+  const bool mfma = (c.kv_dtype == MSK_BF16 || c.kv_dtype == MSK_E4M3) && M > msk::kRowGroup;
+  const int m1 = M < 64 ? M : 64;
+  int nw = mfma ? cdiv(m1, 16) : 0;
+  // a one-wave item over a bf16 cache of head_dim 128 would prefetch a
+  // whole 32-KB tile per wave, more registers than a wave has: two waves
+  if (nw == 1 && c.kv_dtype == MSK_BF16 && c.head_dim == 128) nw = 2;
+  const int rows = mfma ? 16 * nw : msk::kRowGroup;
+  const int nrg = cdiv(M, rows);
   long long total = 0;
   for (int r = 0; r < b.n_req; ++r) {
     int base, end;
@@ -67,7 +79,7 @@ AttnSplit plan_attention(const msk_layer_cfg& c, const msk_batch& b) {
     const int base = lo & ~63, end = L + b.tokens_per_req;
     items += (long long)cdiv(end - base, chunk) * c.n_kv_heads * nrg;
   }
-  return AttnSplit{(int)chunk, (int)items, nrg};
+  return AttnSplit{(int)chunk, (int)items, nrg, rows, nw};
 }
 
 struct Layout {
@@ -79,10 +91,11 @@ Layout layout(const msk_layer_cfg* cfg, int n_layers, const msk_batch& b) {
   const size_t T = (size_t)b.n_req * b.tokens_per_req;
   const size_t H = c.hidden, D = c.head_dim;
   const size_t NR = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * D;
-  size_t max_items = 0;
+  size_t max_rows = 0;
   for (int l = 0; l < n_layers; ++l) {
     const AttnSplit a = plan_attention(cfg[l], b);
-    if ((size_t)a.n_items > max_items) max_items = a.n_items;
+    const size_t rows_total = (size_t)a.n_items * a.rows;
+    if (rows_total > max_rows) max_rows = rows_total;
   }
   Layout L{};
   size_t o = 0;
@@ -93,7 +106,7 @@ Layout layout(const msk_layer_cfg* cfg, int n_layers, const msk_batch& b) {
   };
   L.sync = take(8192);
   L.qkv = take(T * NR * 4);
-  L.part = take(max_items * msk::kRowGroup * (D + 1) * 4);
+  L.part = take(max_rows * (D + 1) * 4);  // item rows of every layer
   L.attn_o = take(T * c.n_q_heads * D * 4);
   L.h = take(T * H * 4);
   L.u = take(T * H * 4);
@@ -263,6 +276,8 @@ msk::LayerArgs make_layer(const msk_layer_cfg& c, const msk_layer_weights* w, co
     L.chunk = a.chunk;
     L.n_items = a.n_items;
     L.nrg = a.nrg;
+    L.rg_rows = a.rows;
+    L.attn_nw = a.nw;
   }
   return L;
 }

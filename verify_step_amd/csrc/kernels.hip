@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "launch.h"
+#include "phases_mfma.h"
 #include "phases_t1.h"
 
 namespace msk {
@@ -33,6 +34,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_attn(LayerArgs L, StepArgs S)
   AttnPlan* P = reinterpret_cast<AttnPlan*>(msk_smem);
   build_plan(L, S, P);
   phase_attn<KDT, D>(L, S, P, msk_smem + align_up(sizeof(AttnPlan), 16), blockIdx.x, gridDim.x);
+}
+
+template <int KDT, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void k_attn_mfma(LayerArgs L, StepArgs S) {
+  AttnPlan* P = reinterpret_cast<AttnPlan*>(msk_smem);
+  build_plan(L, S, P);
+  phase_attn_mfma<KDT, D, NW>(L, S, P, msk_smem + align_up(sizeof(AttnPlan), 16), blockIdx.x,
+                              gridDim.x);
 }
 
 __global__ __launch_bounds__(kBlockThreads) void k_combine(LayerArgs L, StepArgs S, int* win) {
@@ -335,15 +344,20 @@ hipError_t timer_read(int ph, double* total_ms, long long* launches) {
 }
 
 template <class K, class... A>
-static hipError_t launch_x(int ph, K kernel, int grid, size_t lds, hipStream_t st, A... args) {
+static hipError_t launch_b(int ph, K kernel, int grid, int block, size_t lds, hipStream_t st,
+                           A... args) {
   hipEvent_t e0, e1;
   MSK_TRY(timer_pair(ph, &e0, &e1));
   if (e0)
-    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(kBlockThreads), (uint32_t)lds, st, e0, e1, 0,
-                          args...);
+    hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), (uint32_t)lds, st, e0, e1, 0, args...);
   else
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlockThreads), lds, st, args...);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), lds, st, args...);
   return hipGetLastError();
+}
+
+template <class K, class... A>
+static hipError_t launch_x(int ph, K kernel, int grid, size_t lds, hipStream_t st, A... args) {
+  return launch_b(ph, kernel, grid, kBlockThreads, lds, st, args...);
 }
 
 template <class K>
@@ -382,6 +396,48 @@ static int expert_nv(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8; }
     default: { constexpr int NV = 8; BODY; } break;  \
   }
 
+// Matrix-core attention: as many resident workgroups as the CUs hold, each
+// looping over items.
+template <int KDT, int D, int NW>
+static hipError_t launch_attn_mfma_t(const LayerArgs& L, const StepArgs& S, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&k_attn_mfma<KDT, D, NW>);
+  const size_t lds = align_up(sizeof(AttnPlan), 16) + MfmaGeom<KDT, D, NW>::LDS;
+  MSK_TRY(set_lds_limit(fn, lds));
+  static int per_cu = 0;  // one value per instantiation
+  if (per_cu == 0) {
+    int n = 0;
+    MSK_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, NW * 64, lds));
+    per_cu = n > 0 ? n : 1;
+  }
+  const long long cap = (long long)per_cu * cu_count();
+  const int grid = (int)(L.n_items < cap ? L.n_items : cap);
+  return launch_b(kPhAttn, k_attn_mfma<KDT, D, NW>, grid, NW * 64, lds, st, L, S);
+}
+
+template <int KDT, int D>
+static hipError_t launch_attn_mfma_d(const LayerArgs& L, const StepArgs& S, hipStream_t st) {
+  switch (L.attn_nw) {
+    case 1:
+      // the planner gives this pair two waves (register budget)
+      if constexpr (KDT == kBF16 && D == 128) return hipErrorInvalidValue;
+      else return launch_attn_mfma_t<KDT, D, 1>(L, S, st);
+    case 2: return launch_attn_mfma_t<KDT, D, 2>(L, S, st);
+    case 3: return launch_attn_mfma_t<KDT, D, 3>(L, S, st);
+    default: return launch_attn_mfma_t<KDT, D, 4>(L, S, st);
+  }
+}
+
+static hipError_t launch_attn_mfma(const LayerArgs& L, const StepArgs& S, hipStream_t st) {
+  if (L.kdt == kBF16) {
+    if (L.D == 32) return launch_attn_mfma_d<kBF16, 32>(L, S, st);
+    if (L.D == 64) return launch_attn_mfma_d<kBF16, 64>(L, S, st);
+    return launch_attn_mfma_d<kBF16, 128>(L, S, st);
+  }
+  if (L.D == 32) return launch_attn_mfma_d<kE4M3, 32>(L, S, st);
+  if (L.D == 64) return launch_attn_mfma_d<kE4M3, 64>(L, S, st);
+  return launch_attn_mfma_d<kE4M3, 128>(L, S, st);
+}
+
 hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, float* h,
                        hipStream_t st) {
   const int NR = (L.Hq + 2 * L.Hkv) * L.D;
@@ -405,17 +461,21 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
     MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhQkv, k_qkv<kF32, NV>, qgrid, rs_lds, st, L, S, x)))
   }
 
-  const size_t alds = attn_lds_bytes(L.kdt, L.D);
-  const int agrid = L.n_items < 8 * cu_count() ? L.n_items : 8 * cu_count();
+  if (L.attn_nw > 0) {
+    MSK_TRY(launch_attn_mfma(L, S, st));
+  } else {
+    const size_t alds = attn_lds_bytes(L.kdt, L.D);
+    const int agrid = L.n_items < 8 * cu_count() ? L.n_items : 8 * cu_count();
 #define MSK_ATTN(K, DD)                                                             \
-  if (L.kdt == K && L.D == DD) {                                                    \
-    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_attn<K, DD>), alds));   \
-    MSK_TRY(launch(kPhAttn, k_attn<K, DD>, agrid, alds, st, L, S));                          \
-  }
-  MSK_ATTN(kF32, 32) MSK_ATTN(kF32, 64) MSK_ATTN(kF32, 128)
-  MSK_ATTN(kBF16, 32) MSK_ATTN(kBF16, 64) MSK_ATTN(kBF16, 128)
-  MSK_ATTN(kE4M3, 32) MSK_ATTN(kE4M3, 64) MSK_ATTN(kE4M3, 128)
+    if (L.kdt == K && L.D == DD) {                                                  \
+      MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_attn<K, DD>), alds)); \
+      MSK_TRY(launch(kPhAttn, k_attn<K, DD>, agrid, alds, st, L, S));              \
+    }
+    MSK_ATTN(kF32, 32) MSK_ATTN(kF32, 64) MSK_ATTN(kF32, 128)
+    MSK_ATTN(kBF16, 32) MSK_ATTN(kBF16, 64) MSK_ATTN(kBF16, 128)
+    MSK_ATTN(kE4M3, 32) MSK_ATTN(kE4M3, 64) MSK_ATTN(kE4M3, 128)
 #undef MSK_ATTN
+  }
   MSK_TRY(launch_x(kPhCombine, k_combine, grid_for_waves((long long)S.T * L.Hq), sizeof(AttnPlan), st, L, S,
                    S.win_out));
   const int wgrid = grid_for_waves(L.H / DenseRowsHost(nv));

@@ -34,7 +34,10 @@ struct LayerArgs {
   long long cap;
   int chunk;    // cache positions per attention work item (multiple of 64)
   int n_items;  // attention work items of this layer
-  int nrg;      // query row groups per kv head: ceil(G * Tr / kRowGroup)
+  int nrg;      // query row groups per kv head: ceil(G * Tr / rg_rows)
+  int rg_rows;  // query rows per row group (and per partial-sum block)
+  int attn_nw;  // 0: vector attention (rg_rows = kRowGroup); else waves of
+                // the matrix-core attention, rg_rows = 16 * attn_nw
 };
 
 // Buffers of one step; the per-layer arrays follow the layer index.
@@ -49,7 +52,7 @@ struct StepArgs {
   float *attn_o_out;    // [T][Hq*D] or null (single layer calls)
   // workspace
   float *qkv;           // [T][Hq*D + 2*Hkv*D]
-  float *part;          // attention partials [items][kRowGroup][D + 1]
+  float *part;          // attention partials [items][rg_rows][D + 1]
   float *attn_o;        // [T][Hq*D]
   float *h;             // [T][H]
   float *u;             // [T][H]

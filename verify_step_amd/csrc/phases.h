@@ -480,11 +480,11 @@ __device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnP
     const int tok = row / L.Hq, hh = row - (row / L.Hq) * L.Hq;
     const int b = tok / S.Tr, tt = tok - (tok / S.Tr) * S.Tr;
     const int j = hh / G, g = hh - (hh / G) * G;
-    const int m = tt * G + g, rg = m / kRowGroup, mm = m - rg * kRowGroup;
+    const int m = tt * G + g, rg = m / L.rg_rows, mm = m - rg * L.rg_rows;
     const int nch = P->nch[b];
     const int it0 = P->item0[b] + (j * L.nrg + rg) * nch;
-    const float* base = S.part + (size_t)it0 * kRowGroup * (D + 1) + mm * (D + 1);
-    const size_t stride = (size_t)kRowGroup * (D + 1);
+    const float* base = S.part + (size_t)it0 * L.rg_rows * (D + 1) + mm * (D + 1);
+    const size_t stride = (size_t)L.rg_rows * (D + 1);
     float l = 0.f, o0 = 0.f, o1 = 0.f;
     int c = 0;
     for (; c + 16 <= nch; c += 16) {  // sixteen chunks' loads in flight

@@ -1,0 +1,341 @@
+// Split-KV no-max attention partials on the matrix cores, for the verify
+// step's many query rows per kv head.
+//
+// One work item is (request b, kv head j, row group, chunk of cache
+// positions), as for the vector path, but a row group holds up to 64 query
+// rows (rows m = t * G + g in token order) and each wave owns 16 of them.
+// Per 64-position tile:
+//   scores  S^T[pos][m] = sum_d K[pos][d] * qhat[m][d]        (MFMA, k = d)
+//   weights e = exp(s - c) on the row's window, else 0         (VALU)
+//   output  O^T[d][m]  += sum_pos V^T[d][pos] * e[pos][m]      (MFMA, k = pos)
+// with v_mfma_f32_16x16x32_bf16.  Cached K and V are bf16 or e4m3, both
+// exact in bf16.  qhat and e are fp32; each enters as a sum of two bf16
+// terms (hi = rne(x), lo = rne(x - hi)), so a product is exact to about
+// 2^-16 relative and sums stay in fp32.  The score accumulator's layout (lane
+// = column m, four consecutive positions per lane) is used directly as the
+// weight operand of the output product by numbering that product's k index
+// so that a lane's eight k values are its own eight positions of the 32:
+// no shuffle and no LDS round trip for the weights.
+//
+// The tile is fetched into registers one tile ahead (nontemporal 16-B
+// loads) and converted once per workgroup into two bf16 LDS tiles: K
+// row-major [pos][d] and V transposed [d][pos], both padded against bank
+// conflicts.  Positions outside the visible range are zero in both tiles, so
+// masked weights never meet a NaN.  The step's own positions (>= kv_len)
+// are rebuilt from the QKV output as stored (QK-norm on k, cast to the cache
+// format), and the row-group-0 item writes them into the cache.
+//
+// Cite: no-max softmax with a fixed score bound (ainewsbites, "Removing
+// attention bottlenecks"), split-KV partials combined by plain sums.
+#pragma once
+#include "phases.h"
+
+namespace msk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int KDT, int D, int NW>
+struct MfmaGeom {
+  static constexpr int ES = KV<KDT>::ES;
+  static constexpr int RB = D * ES;        // cache row bytes
+  static constexpr int CPR = RB / 16;      // 16-B chunks per cache row
+  static constexpr int EPC = 16 / ES;      // elements per chunk
+  static constexpr int NT = NW * 64;       // threads per workgroup
+  static constexpr int NKC = 64 * CPR;     // K chunks per tile
+  static constexpr int KPT = (NKC + NT - 1) / NT;
+  static constexpr int NVP = 32 * CPR;     // V (position pair, chunk) tasks per tile
+  static constexpr int VPT = (NVP + NT - 1) / NT;
+  static constexpr int KBS = D * 2 + 16;   // bf16 K tile row stride, bytes
+  static constexpr int VTS = 64 * 2 + 8;   // bf16 V^T tile row stride, bytes
+  static constexpr int DS = D / 32;        // k steps of the score product
+  static constexpr int NDT = D / 16;       // d tiles of the output product
+  static constexpr int LDS_KB = 64 * KBS;
+  static constexpr int LDS_VT = D * VTS;
+  static constexpr int LDS = LDS_KB + LDS_VT + kMaxTok * 4;
+  static constexpr int ROWS = 16 * NW;     // query rows per item
+};
+
+__device__ __forceinline__ unsigned pack_bf16_exact(float a, float b) {
+  // a and b are exact in bf16: keep their upper halves
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+
+// One 16-B chunk of cache-format data -> its EPC values as bf16, two per
+// word (exact).
+template <int KDT>
+__device__ __forceinline__ void chunk_to_bf16(const v4u& w, unsigned* o) {
+  if constexpr (KDT == kBF16) {
+    o[0] = w.x; o[1] = w.y; o[2] = w.z; o[3] = w.w;
+  } else {
+    const unsigned ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float f[4];
+      e4m3x4(ws[i], f);
+      o[2 * i] = pack_bf16_exact(f[0], f[1]);
+      o[2 * i + 1] = pack_bf16_exact(f[2], f[3]);
+    }
+  }
+}
+
+// x = hi + lo (+ a residual of at most 2^-16 |x|), both bf16 bits.
+__device__ __forceinline__ void split_bf16(float x, unsigned& hi, unsigned& lo) {
+  hi = f2bf16(x);
+  lo = f2bf16(x - bf16_lo(hi));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const v4u& v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <int KDT, int D, int NW>
+__device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int item,
+                               uint8_t* wl) {
+  using Gm = MfmaGeom<KDT, D, NW>;
+  constexpr int RB = Gm::RB, CPR = Gm::CPR, EPC = Gm::EPC, NT = Gm::NT;
+  constexpr int KPT = Gm::KPT, VPT = Gm::VPT, KBS = Gm::KBS, VTS = Gm::VTS;
+  constexpr int DS = Gm::DS, NDT = Gm::NDT, ROWS = Gm::ROWS;
+  uint8_t* kb = wl;
+  uint8_t* vt = wl + Gm::LDS_KB;
+  float* rk = reinterpret_cast<float*>(vt + Gm::LDS_VT);
+
+  const int tid = threadIdx.x, ln = lane_id(), wv = wave_id();
+  int b = 0;
+  while (b + 1 < S.n_req && P->item0[b + 1] <= item) ++b;
+  const int nch = P->nch[b];
+  int rem = item - P->item0[b];
+  const int j = rem / (L.nrg * nch);
+  rem -= j * L.nrg * nch;
+  const int rg = rem / nch;
+  const int c = rem - rg * nch;
+  const int p0 = P->base[b] + c * L.chunk;
+  const int p1 = p0 + L.chunk < P->end[b] ? p0 + L.chunk : P->end[b];
+  const int Lb = S.kv_len[b];
+  const int G = L.Hq / L.Hkv;
+  const int M = G * S.Tr;
+  const int m0 = rg * ROWS;
+  const int NQ = L.Hq * L.D, NK = L.Hkv * L.D, NR = NQ + 2 * NK;
+  const size_t head_off = ((size_t)b * L.Hkv + j) * (size_t)L.cap;  // in rows
+  uint8_t* kc = L.kc + head_off * RB;
+  uint8_t* vc = L.vc + head_off * RB;
+  const bool writer = (rg == 0);
+
+  // this lane's query row (lanes l, l^16, l^32, l^48 share it) and its window
+  const int mr = m0 + 16 * wv + (ln & 15);
+  const bool live = mr < M;
+  const int t_me = live ? mr / G : 0;
+  const int g_me = live ? mr - t_me * G : 0;
+  const int p_me = Lb + t_me;
+  const int w_lo = live ? (L.window > 0 ? (p_me - L.window + 1 > 0 ? p_me - L.window + 1 : 0) : 0)
+                        : 1;
+  const int w_hi = live ? p_me : 0;
+  // the group's earliest window start: its first row's token
+  const int t_first = m0 / G;
+  const int lo_min = L.window > 0 ? (Lb + t_first - L.window + 1 > 0 ? Lb + t_first - L.window + 1 : 0)
+                                  : 0;
+
+  // qhat as the B operand of the score product: lane holds row m, d = 32 ks + 8 (ln >> 4) + e
+  bf16x8 qh[DS], ql[DS];
+  {
+    const float* q = S.qkv + (size_t)(b * S.Tr + t_me) * NR + (size_t)(j * G + g_me) * D;
+    float qf[DS][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks) {
+      const int d0 = 32 * ks + 8 * (ln >> 4);
+      const v4f a = live ? *reinterpret_cast<const v4f*>(q + d0) : v4f{0.f, 0.f, 0.f, 0.f};
+      const v4f bq = live ? *reinterpret_cast<const v4f*>(q + d0 + 4) : v4f{0.f, 0.f, 0.f, 0.f};
+      qf[ks][0] = a.x; qf[ks][1] = a.y; qf[ks][2] = a.z; qf[ks][3] = a.w;
+      qf[ks][4] = bq.x; qf[ks][5] = bq.y; qf[ks][6] = bq.z; qf[ks][7] = bq.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += qf[ks][e] * qf[ks][e];
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float rr = 1.0f / sqrtf(ss / (float)D + L.eps);
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks) {
+      unsigned h[8], l[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 32 * ks + 8 * (ln >> 4) + e;
+        split_bf16(qf[ks][e] * rr * L.q_norm[d] * L.qscale, h[e], l[e]);
+      }
+      qh[ks] = as_bf16x8(v4u{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16,
+                             h[6] | h[7] << 16});
+      ql[ks] = as_bf16x8(v4u{l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16,
+                             l[6] | l[7] << 16});
+    }
+  }
+  // 1/rms of the step's new keys that fall in this chunk
+  const int tn0 = p0 - Lb > 0 ? p0 - Lb : 0;
+  const int tn1 = p1 - Lb < S.Tr ? p1 - Lb : S.Tr;
+  for (int t = tn0 + wv; t < tn1; t += NW) {
+    const float* k = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + (size_t)j * D;
+    float ss = 0.f;
+    for (int d = ln; d < D; d += 64) ss += k[d] * k[d];
+    ss = wave_sum(ss);
+    if (ln == 0) rk[t] = 1.0f / sqrtf(ss / (float)D + L.eps);
+  }
+
+  // cached rows of a tile into registers; rows outside [lo_min, Lb) are 0
+  v4u kr[KPT], vr[VPT][2];
+  auto fetch = [&](int pb) {
+    const int vlo = pb > lo_min ? pb : lo_min;
+    const int vhi = p1 < Lb ? p1 : Lb;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int q = tid + u * NT;
+      const int pos = pb + q / CPR;
+      kr[u] = v4u{0u, 0u, 0u, 0u};
+      if (q < Gm::NKC && pos >= vlo && pos < vhi)
+        kr[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4u*>(kc + (size_t)pos * RB + (q % CPR) * 16));
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int q = tid + u * NT;
+      const int pos = pb + 2 * (q / CPR);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        vr[u][h] = v4u{0u, 0u, 0u, 0u};
+        if (q < Gm::NVP && pos + h >= vlo && pos + h < vhi)
+          vr[u][h] = __builtin_nontemporal_load(
+              reinterpret_cast<const v4u*>(vc + (size_t)(pos + h) * RB + (q % CPR) * 16));
+      }
+    }
+  };
+  // chunk cc of the step's own row at position pos, as stored in the cache
+  auto new_chunk = [&](int pos, int cc, bool value) -> v4u {
+    const int t = pos - Lb;
+    const int d0 = cc * EPC;
+    const float* kq = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + (size_t)j * D + d0;
+    float f[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      f[e] = e < EPC ? (value ? kq[NK + e] : kq[e] * rk[t] * L.k_norm[d0 + e]) : 0.f;
+    const v4u enc = encode16<KDT>(f);
+    if (writer) *reinterpret_cast<v4u*>((value ? vc : kc) + (size_t)pos * RB + cc * 16) = enc;
+    return enc;
+  };
+
+  f32x4 oacc[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;
+
+  fetch(p0);
+  for (int pb = p0; pb < p1; pb += 64) {
+    __syncthreads();  // the previous tile's readers are done; rk is written
+    // K -> kb[pos][d] (bf16)
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int q = tid + u * NT;
+      if (q < Gm::NKC) {
+        const int row = q / CPR, cc = q % CPR;
+        const int pos = pb + row;
+        v4u raw = kr[u];
+        if (pos >= Lb && pos < p1) raw = new_chunk(pos, cc, false);
+        unsigned o[EPC / 2];
+        chunk_to_bf16<KDT>(raw, o);
+        uint8_t* dst = kb + row * KBS + cc * EPC * 2;
+#pragma unroll
+        for (int w = 0; w < EPC / 2; w += 4)
+          *reinterpret_cast<v4u*>(dst + 4 * w) = v4u{o[w], o[w + 1], o[w + 2], o[w + 3]};
+      }
+    }
+    // V -> vt[d][pos] (bf16), two positions per 32-bit store
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int q = tid + u * NT;
+      if (q < Gm::NVP) {
+        const int pp = q / CPR, cc = q % CPR;
+        unsigned o[2][EPC / 2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int pos = pb + 2 * pp + h;
+          v4u raw = vr[u][h];
+          if (pos >= Lb && pos < p1) raw = new_chunk(pos, cc, true);
+          chunk_to_bf16<KDT>(raw, o[h]);
+        }
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const unsigned a = (e & 1) ? o[0][e >> 1] >> 16 : o[0][e >> 1] & 0xffffu;
+          const unsigned bb = (e & 1) ? o[1][e >> 1] & 0xffff0000u : o[1][e >> 1] << 16;
+          *reinterpret_cast<unsigned*>(vt + (cc * EPC + e) * VTS + 4 * pp) = a | bb;
+        }
+      }
+    }
+    if (pb + 64 < p1) fetch(pb + 64);
+    __syncthreads();
+
+    // scores of this wave's 16 rows against the tile's 64 positions
+    f32x4 sacc[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      sacc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DS; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const v4u*>(
+            kb + (16 * pt + (ln & 15)) * KBS + (32 * ks + 8 * (ln >> 4)) * 2));
+        sacc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], sacc[pt], 0, 0, 0);
+        sacc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[ks], sacc[pt], 0, 0, 0);
+      }
+    }
+    // weights: lane holds row m, positions 16 pt + 4 (ln >> 4) + i
+    unsigned wh[2][4], wlo[2][4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      unsigned hh[4], ll[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = pb + 16 * pt + 4 * (ln >> 4) + i;
+        const bool ok = pos >= w_lo && pos <= w_hi && pos < p1;
+        const float e = ok ? __expf(sacc[pt][i] - L.shift) : 0.f;
+        lsum += e;
+        split_bf16(e, hh[i], ll[i]);
+      }
+      // k index 8 (ln >> 4) + 4 (pt & 1) + i of k step pt / 2
+      wh[pt >> 1][2 * (pt & 1)] = hh[0] | hh[1] << 16;
+      wh[pt >> 1][2 * (pt & 1) + 1] = hh[2] | hh[3] << 16;
+      wlo[pt >> 1][2 * (pt & 1)] = ll[0] | ll[1] << 16;
+      wlo[pt >> 1][2 * (pt & 1) + 1] = ll[2] | ll[3] << 16;
+    }
+    // O^T[d][m] += V^T[d][pos] e[pos][m]; the A operand's k numbering matches
+    // the weights': positions 32 ks + 4 (ln >> 4) + {0..3} and + 16 + {0..3}
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 bh = as_bf16x8(v4u{wh[ks][0], wh[ks][1], wh[ks][2], wh[ks][3]});
+      const bf16x8 bl = as_bf16x8(v4u{wlo[ks][0], wlo[ks][1], wlo[ks][2], wlo[ks][3]});
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint8_t* src = vt + (16 * dt + (ln & 15)) * VTS + (32 * ks + 4 * (ln >> 4)) * 2;
+        const v2u x0 = *reinterpret_cast<const v2u*>(src);
+        const v2u x1 = *reinterpret_cast<const v2u*>(src + 32);
+        const bf16x8 a = as_bf16x8(v4u{x0.x, x0.y, x1.x, x1.y});
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, oacc[dt], 0, 0, 0);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, oacc[dt], 0, 0, 0);
+      }
+    }
+  }
+  // partial sums of this wave's rows: part[item][row][d], part[item][row][D] = l
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  float* part = S.part + ((size_t)item * ROWS + 16 * wv + (ln & 15)) * (D + 1);
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[16 * dt + 4 * (ln >> 4) + i] = oacc[dt][i];
+  if (ln < 16) part[D] = lsum;
+}
+
+template <int KDT, int D, int NW>
+__device__ void phase_attn_mfma(const LayerArgs& L, const StepArgs& S, const AttnPlan* P,
+                                uint8_t* lds, int vb, int nvb) {
+  const int n_items = P->item0[S.n_req];
+  for (int item = vb; item < n_items; item += nvb) {
+    attn_item_mfma<KDT, D, NW>(L, S, P, item, lds);
+    __syncthreads();
+  }
+}
+
+}  // namespace msk
