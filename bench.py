@@ -79,7 +79,11 @@ def phase_bytes(spec, kv_len, Tr, topk_l):
         router=E * H * es + H * 4 + 2 * T * H * 4 + T * E * 4,
         topk=T * E * 4 + 2 * T * K * 4,
         gateup=n_exp * gu + T * H * 4 + T * K * F * 4,
-        down=n_exp * dn + T * K * F * 4 + 2 * T * H * 4,
+        down=n_exp * dn + T * K * F * 4 + (2 * T * H * 4 if T == 1 else T * K * H * 4),
+        union=T * K * 4,
+        prep=2 * (T * H * 4 + H * 4 + 3 * T * H * 2),
+        dense_sum=0,
+        moe_sum=2 * T * H * 4 + T * K * (H * 4 + 8),
     )
 
 
@@ -186,13 +190,18 @@ def timeline(p, ws, x):
 
 KERNEL_NAMES = {"qkv": "k_qkv", "attn": "k_attn", "combine": "k_combine", "wo": "k_wo",
                 "router": "k_router", "topk": "k_topk", "gateup": "k_gateup", "down": "k_down",
-                "step": "k_step_t1"}
+                "step": "k_step_t1", "union": "k_union", "moe_sum": "k_moe_sum",
+                "prep": "k_prep_act", "dense_sum": "k_dense_sum"}
 ONE_TOKEN_KERNELS = ("qkv", "wo", "router", "gateup", "down")
 
 
 def kernel_name(phase, T):
     base = KERNEL_NAMES[phase]
-    return base + "_t1" if T == 1 and phase in ONE_TOKEN_KERNELS else base
+    if T == 1 and phase in ONE_TOKEN_KERNELS:
+        return base + "_t1"
+    if T > 1 and phase in ("gateup", "down"):
+        return base + "_tn"
+    return base
 
 
 def kernel_pass(p, x, ws, steps, stream):

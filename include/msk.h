@@ -219,6 +219,14 @@ msk_status msk_layer_step_timeline(const msk_layer_cfg *cfg, const msk_layer_wei
  *   MSK_PH_GATEUP   expert gate/up + SwiGLU
  *   MSK_PH_DOWN     expert down + weighted combine + residual
  *   MSK_PH_STEP     the persistent whole-step kernel, where it runs
+ *   MSK_PH_UNION    distinct selected experts and their slots (more than
+ *                   one token)
+ *   MSK_PH_MOE_SUM  weighted sum of the per-slot expert outputs + residual
+ *                   (more than one token)
+ *   MSK_PH_PREP     RMSNorm of a projection's input into bf16 terms for the
+ *                   matrix cores (more than one token, bf16 dense weights)
+ *   MSK_PH_DENSE_SUM  sum of a matrix-core projection's K-slice partials
+ *                   (+ residual)
  * msk_timer_start(mask) forgets earlier records and, from then on, brackets
  * every launch of each phase whose bit (1 << phase) is set in mask with a
  * pair of HIP events that the dispatch itself stamps (hipExtLaunchKernel),
@@ -231,7 +239,8 @@ msk_status msk_layer_step_timeline(const msk_layer_cfg *cfg, const msk_layer_wei
  * the list or null outputs, MSK_ERR_DEVICE when an event call fails. */
 enum {
   MSK_PH_QKV = 0, MSK_PH_ATTN = 1, MSK_PH_COMBINE = 2, MSK_PH_WO = 3, MSK_PH_ROUTER = 4,
-  MSK_PH_TOPK = 5, MSK_PH_GATEUP = 6, MSK_PH_DOWN = 7, MSK_PH_STEP = 8, MSK_N_PHASES = 9
+  MSK_PH_TOPK = 5, MSK_PH_GATEUP = 6, MSK_PH_DOWN = 7, MSK_PH_STEP = 8, MSK_PH_UNION = 9,
+  MSK_PH_MOE_SUM = 10, MSK_PH_PREP = 11, MSK_PH_DENSE_SUM = 12, MSK_N_PHASES = 13
 };
 msk_status msk_timer_start(uint32_t mask);
 msk_status msk_timer_read(int32_t phase, double *total_ms, int64_t *launches);

@@ -235,7 +235,8 @@ def layer_step(specs, weights, kvs, kv_len, tokens_per_req, x, ws, layer_out=Non
     return x
 
 
-PHASES = ("qkv", "attn", "combine", "wo", "router", "topk", "gateup", "down", "step")
+PHASES = ("qkv", "attn", "combine", "wo", "router", "topk", "gateup", "down", "step", "union",
+          "moe_sum", "prep", "dense_sum")
 
 
 def timer_start(phases=PHASES):

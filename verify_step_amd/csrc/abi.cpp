@@ -83,7 +83,7 @@ AttnSplit plan_attention(const msk_layer_cfg& c, const msk_batch& b) {
 }
 
 struct Layout {
-  size_t sync, qkv, part, attn_o, h, u, logits, idx, wts, act, xa, xb, total;
+  size_t sync, qkv, part, attn_o, h, u, logits, idx, wts, act, xa, xb, uni, ybuf, a3, dpart, total;
 };
 
 Layout layout(const msk_layer_cfg* cfg, int n_layers, const msk_batch& b) {
@@ -104,7 +104,7 @@ Layout layout(const msk_layer_cfg* cfg, int n_layers, const msk_batch& b) {
     o += up(bytes);
     return at;
   };
-  L.sync = take(8192);
+  L.sync = take(msk::kSyncBytes);
   L.qkv = take(T * NR * 4);
   L.part = take(max_rows * (D + 1) * 4);  // item rows of every layer
   L.attn_o = take(T * c.n_q_heads * D * 4);
@@ -116,6 +116,19 @@ Layout layout(const msk_layer_cfg* cfg, int n_layers, const msk_batch& b) {
   L.act = take(T * c.top_k * (size_t)c.ffn_dim * 4);
   L.xa = take(T * H * 4);
   L.xb = take(T * H * 4);
+  L.uni = take(sizeof(msk::Union));
+  L.ybuf = take(T * c.top_k * H * 4);
+  const size_t HQD = (size_t)c.n_q_heads * D;
+  L.a3 = take(3 * T * (H > HQD ? H : HQD) * 2);
+  size_t dp = 0;
+  const int dense_n[3] = {(int)NR, (int)H, c.n_experts};
+  const int dense_k[3] = {(int)H, (int)HQD, (int)H};
+  for (int i = 0; i < 3; ++i) {
+    const size_t need = (size_t)(dense_n[i] + 63) / 64 * 64 *
+                        msk::dense_slices(dense_n[i], dense_k[i]) * T;
+    dp = dp > need ? dp : need;
+  }
+  L.dpart = take(dp * 4);
   L.total = o;
   return L;
 }
@@ -301,6 +314,10 @@ msk::StepArgs make_step(const Layout& lay, void* ws, int n_req, int Tr, const in
   S.act = reinterpret_cast<float*>(base + lay.act);
   S.xa = reinterpret_cast<float*>(base + lay.xa);
   S.xb = reinterpret_cast<float*>(base + lay.xb);
+  S.uni = reinterpret_cast<msk::Union*>(base + lay.uni);
+  S.ybuf = reinterpret_cast<float*>(base + lay.ybuf);
+  S.a3 = reinterpret_cast<unsigned short*>(base + lay.a3);
+  S.dpart = reinterpret_cast<float*>(base + lay.dpart);
   return S;
 }
 
@@ -343,7 +360,8 @@ size_t msk_workspace_size(const msk_layer_cfg* cfg, int32_t n_layers, const msk_
 }
 
 msk_status msk_workspace_status(void* ws, size_t ws_bytes, void* stream) {
-  if (!ws || ws_bytes < 8192) return fail(MSK_ERR_WORKSPACE, "workspace missing or too small");
+  if (!ws || ws_bytes < (size_t)msk::kSyncBytes)
+    return fail(MSK_ERR_WORKSPACE, "workspace missing or too small");
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipStreamSynchronize(st);
   if (e != hipSuccess) return device_status(e, "hipStreamSynchronize");
@@ -352,7 +370,7 @@ msk_status msk_workspace_status(void* ws, size_t ws_bytes, void* stream) {
   if (e != hipSuccess) return device_status(e, "hipMemcpy");
   if (words[1] != 0) {
     // a barrier wait gave up: epochs may be inconsistent, start them over
-    e = hipMemset(ws, 0, 8192);
+    e = hipMemset(ws, 0, msk::kSyncBytes);
     if (e != hipSuccess) return device_status(e, "hipMemset");
     return fail(MSK_ERR_TIMEOUT, "a device-side wait gave up (barrier watchdog)");
   }
@@ -476,6 +494,8 @@ msk_status msk_layer_step_timeline(const msk_layer_cfg* cfg, const msk_layer_wei
 }
 
 static_assert(MSK_N_PHASES == msk::kNumPhases && MSK_PH_STEP == msk::kPhStep &&
+                  MSK_PH_UNION == msk::kPhUnion && MSK_PH_MOE_SUM == msk::kPhMoeSum &&
+                  MSK_PH_PREP == msk::kPhPrep && MSK_PH_DENSE_SUM == msk::kPhDenseSum &&
                   MSK_PH_GATEUP == msk::kPhGateUp && MSK_PH_ATTN == msk::kPhAttn,
               "phase numbering of the header and the launchers must agree");
 

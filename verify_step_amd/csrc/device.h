@@ -98,6 +98,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Workgroup barrier for hand-offs through LDS only: waits for this wave's LDS
+// operations and meets the other waves, but leaves its global loads in
+// flight.  (__syncthreads() carries a workgroup fence that also waits for
+// every outstanding global load, which would drain any prefetch.)  Data that
+// direct global->LDS loads bring in must be waited for with vmcnt before it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ------------------------------------------------------------ formats
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }

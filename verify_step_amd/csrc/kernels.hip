@@ -9,8 +9,10 @@
 #include <vector>
 
 #include "launch.h"
+#include "phases_dense.h"
 #include "phases_mfma.h"
 #include "phases_t1.h"
+#include "phases_tn.h"
 
 namespace msk {
 
@@ -44,10 +46,50 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(LayerArgs L, StepArgs S) 
                               gridDim.x);
 }
 
-__global__ __launch_bounds__(kBlockThreads) void k_combine(LayerArgs L, StepArgs S, int* win) {
+// Several tokens: the expert union once, then gate/up and down over it,
+// then the weighted sum over each token's slots.
+__global__ __launch_bounds__(kBlockThreads) void k_union(LayerArgs L, StepArgs S) {
+  union_to_global(S.idx, S.T, L.K, L.E, reinterpret_cast<Union*>(msk_smem), S.uni);
+}
+
+template <int DT, int NVMAX>
+__global__ __launch_bounds__(kBlockThreads) void k_gateup_tn(LayerArgs L, StepArgs S) {
+  gateup_tn<DT, NVMAX>(L, S, S.uni, reinterpret_cast<float*>(msk_smem));
+}
+
+template <int DT, int NVMAX>
+__global__ __launch_bounds__(kBlockThreads) void k_down_tn(LayerArgs L, StepArgs S) {
+  down_tn<DT, NVMAX>(L, S, S.uni, reinterpret_cast<float*>(msk_smem), S.ybuf);
+}
+
+__global__ __launch_bounds__(kBlockThreads) void k_moe_sum(LayerArgs L, StepArgs S, const float* h,
+                                                           float* out) {
+  down_combine(L, S, h, S.ybuf, out);
+}
+
+__global__ __launch_bounds__(kBlockThreads) void k_combine(LayerArgs L, StepArgs S, int* win,
+                                                           unsigned short* a3) {
   AttnPlan* P = reinterpret_cast<AttnPlan*>(msk_smem);
   build_plan(L, S, P);
-  phase_combine(L, S, P, win, blockIdx.x, gridDim.x);
+  phase_combine(L, S, P, win, blockIdx.x, gridDim.x, a3);
+}
+
+// Matrix-core dense projections of several tokens and their input terms.
+__global__ __launch_bounds__(kBlockThreads) void k_prep_act(const float* x, const float* g, int T,
+                                                            int H, float eps, float* a32,
+                                                            unsigned short* a3) {
+  prep_act(x, g, T, H, eps, a32, a3, reinterpret_cast<float*>(msk_smem));
+}
+
+template <int CT>
+__global__ __launch_bounds__(kBlockThreads) void k_dense_mfma(DenseArgs A) {
+  dense_mfma<CT>(A, msk_smem);
+}
+
+__global__ __launch_bounds__(kBlockThreads) void k_dense_sum(const float* part, int N, int T,
+                                                             int ks, const float* resid,
+                                                             float* out) {
+  dense_sum(part, N, T, ks, resid, out);
 }
 
 template <int DT, int NV>
@@ -67,21 +109,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_topk(LayerArgs L, StepArgs S,
   phase_topk(L, S, topk_out, blockIdx.x, gridDim.x);
 }
 
-template <int DT, int NVMAX>
-__global__ __launch_bounds__(kBlockThreads) void k_gateup(LayerArgs L, StepArgs S) {
-  Union* U = reinterpret_cast<Union*>(msk_smem);
-  build_union(S.idx, S.T, L.K, L.E, U);
-  phase_gateup<DT, NVMAX>(L, S, U, blockIdx.x, gridDim.x);
-}
-
-template <int DT, int NVMAX>
-__global__ __launch_bounds__(kBlockThreads) void k_down(LayerArgs L, StepArgs S, const float* h,
-                                                        float* out) {
-  Union* U = reinterpret_cast<Union*>(msk_smem);
-  build_union(S.idx, S.T, L.K, L.E, U);
-  float* ybuf = reinterpret_cast<float*>(msk_smem + align_up(sizeof(Union), 16));
-  phase_down<DT, NVMAX>(L, S, U, h, out, ybuf, blockIdx.x, gridDim.x);
-}
 
 // ------------------------------------------------- one-token kernels
 // LDS of the one-token kernels: a reduction scratch, the top-k of the token,
@@ -246,9 +273,6 @@ size_t attn_lds_bytes(int kdt, int D) {
   return align_up(sizeof(AttnPlan), 16) + w;
 }
 
-static size_t down_lds_bytes(const LayerArgs& L, const StepArgs& S) {
-  return align_up(sizeof(Union), 16) + (size_t)kWaves * S.T * L.K * 4 * sizeof(float);
-}
 
 static int DenseRowsHost(int nv) { return nv >= 16 ? 2 : 4; }
 
@@ -376,8 +400,6 @@ static hipError_t set_lds_limit(const void* fn, size_t bytes) {
 // Token-group width of the dense projections: the smallest power of two
 // covering T, at most 32 (more tokens are processed in groups).
 static int dense_nv(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : T <= 8 ? 8 : T <= 16 ? 16 : 32; }
-// Largest token count an expert handles in one pass over its rows.
-static int expert_nv(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8; }
 
 #define MSK_NV_CASES(NVVAL, BODY)   \
   switch (NVVAL) {                  \
@@ -388,13 +410,50 @@ static int expert_nv(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : T <= 4 ? 4 : 8; }
     case 16: { constexpr int NV = 16; BODY; } break; \
     default: { constexpr int NV = 32; BODY; } break; \
   }
-#define MSK_ENV_CASES(NVVAL, BODY)  \
-  switch (NVVAL) {                  \
-    case 1: { constexpr int NV = 1; BODY; } break;   \
-    case 2: { constexpr int NV = 2; BODY; } break;   \
-    case 4: { constexpr int NV = 4; BODY; } break;   \
-    default: { constexpr int NV = 8; BODY; } break;  \
+
+// The matrix-core dense path takes bf16 weights, several tokens, whole
+// 16-row tiles and whole 128-column k-tiles.
+static bool dense_on_mfma(const LayerArgs& L, const StepArgs& S, int N, int K) {
+  return S.T > 1 && L.ddt == kBF16 && N % 16 == 0 && K % 128 == 0;
+}
+
+template <int CT>
+static hipError_t launch_dense_t(const DenseArgs& A, int ph, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&k_dense_mfma<CT>);
+  const size_t lds = DenseLds<CT>::BYTES;
+  MSK_TRY(set_lds_limit(fn, lds));
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    MSK_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kBlockThreads, lds));
+    per_cu = n > 0 ? n : 1;
   }
+  const long long items = (long long)((A.N + 63) / 64) * A.ks;
+  const long long cap = (long long)per_cu * cu_count();
+  return launch_x(ph, k_dense_mfma<CT>, (int)(items < cap ? items : cap), lds, st, A);
+}
+
+// out = resid + W a for the three (QKV) or one weight segments.
+static hipError_t launch_dense(const StepArgs& S, const uint8_t* w0, const uint8_t* w1,
+                               const uint8_t* w2, int seg1, int seg2, int N, int K,
+                               const float* resid, float* out, int ph, hipStream_t st) {
+  DenseArgs A;
+  A.w[0] = w0; A.w[1] = w1 ? w1 : w0; A.w[2] = w2 ? w2 : w0;
+  A.seg[0] = 0; A.seg[1] = seg1; A.seg[2] = seg2;
+  A.N = N; A.K = K; A.T = S.T;
+  A.ks = dense_slices(N, K);
+  A.a3 = S.a3; A.resid = resid; A.out = out; A.part = S.dpart;
+  switch ((S.T + 15) / 16) {
+    case 1: MSK_TRY(launch_dense_t<1>(A, ph, st)); break;
+    case 2: MSK_TRY(launch_dense_t<2>(A, ph, st)); break;
+    case 3: MSK_TRY(launch_dense_t<3>(A, ph, st)); break;
+    default: MSK_TRY(launch_dense_t<4>(A, ph, st)); break;
+  }
+  if (A.ks == 1) return hipSuccess;
+  const long long n = (long long)S.T * N;
+  return launch_x(kPhDenseSum, k_dense_sum, (int)((n + kBlockThreads - 1) / kBlockThreads), 0,
+                  st, (const float*)S.dpart, N, S.T, A.ks, resid, out);
+}
 
 // Matrix-core attention: as many resident workgroups as the CUs hold, each
 // looping over items.
@@ -455,8 +514,11 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
       MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_qkv_t1<kF32>), lds));
       MSK_TRY(launch_x(kPhQkv, k_qkv_t1<kF32>, g, lds, st, L, S, x));
     }
-  } else if (L.ddt == kBF16) {
-    MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhQkv, k_qkv<kBF16, NV>, qgrid, rs_lds, st, L, S, x)))
+  } else if (dense_on_mfma(L, S, NR, L.H)) {
+    MSK_TRY(launch_x(kPhPrep, k_prep_act, S.T, kWaves * sizeof(float), st, x, L.attn_norm, S.T, L.H, L.eps,
+                     (float*)nullptr, S.a3));
+    const int NQ = L.Hq * L.D, NK = L.Hkv * L.D;
+    MSK_TRY(launch_dense(S, L.wq, L.wk, L.wv, NQ, NQ + NK, NR, L.H, nullptr, S.qkv, kPhQkv, st));
   } else {
     MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhQkv, k_qkv<kF32, NV>, qgrid, rs_lds, st, L, S, x)))
   }
@@ -476,8 +538,9 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
     MSK_ATTN(kE4M3, 32) MSK_ATTN(kE4M3, 64) MSK_ATTN(kE4M3, 128)
 #undef MSK_ATTN
   }
-  MSK_TRY(launch_x(kPhCombine, k_combine, grid_for_waves((long long)S.T * L.Hq), sizeof(AttnPlan), st, L, S,
-                   S.win_out));
+  const bool mm = dense_on_mfma(L, S, L.H, L.Hq * L.D);
+  MSK_TRY(launch_x(kPhCombine, k_combine, grid_for_waves((long long)S.T * L.Hq), sizeof(AttnPlan),
+                   st, L, S, S.win_out, mm ? S.a3 : nullptr));
   const int wgrid = grid_for_waves(L.H / DenseRowsHost(nv));
   if (one) {
     const size_t lds = t1_vec_lds(L);
@@ -489,8 +552,8 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
       MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_wo_t1<kF32>), lds));
       MSK_TRY(launch_x(kPhWo, k_wo_t1<kF32>, g, lds, st, L, S, x, h));
     }
-  } else if (L.ddt == kBF16) {
-    MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhWo, k_wo<kBF16, NV>, wgrid, 0, st, L, S, x, h)))
+  } else if (mm) {
+    MSK_TRY(launch_dense(S, L.wo, nullptr, nullptr, 0, 0, L.H, L.Hq * L.D, x, h, kPhWo, st));
   } else {
     MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhWo, k_wo<kF32, NV>, wgrid, 0, st, L, S, x, h)))
   }
@@ -514,8 +577,10 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
       MSK_TRY(launch_x(kPhRouter, k_router_t1<kF32>, g, lds, st, L, S, h, topk_out));
     }
     return hipSuccess;
-  } else if (L.ddt == kBF16) {
-    MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhRouter, k_router<kBF16, NV>, grid, rs_lds, st, L, S, h)))
+  } else if (dense_on_mfma(L, S, L.E, L.H)) {
+    MSK_TRY(launch_x(kPhPrep, k_prep_act, S.T, kWaves * sizeof(float), st, h, L.ffn_norm, S.T, L.H, L.eps, S.u, S.a3));
+    MSK_TRY(launch_dense(S, L.wr, nullptr, nullptr, 0, 0, L.E, L.H, nullptr, S.logits, kPhRouter,
+                         st));
   } else {
     MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhRouter, k_router<kF32, NV>, grid, rs_lds, st, L, S, h)))
   }
@@ -534,17 +599,43 @@ static hipError_t launch_ffn_t1(const LayerArgs& L, const StepArgs& S, const flo
   return hipSuccess;
 }
 
-template <int DT, int NV>
-static hipError_t launch_ffn_t(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
-                               hipStream_t st) {
-  const size_t ulds = sizeof(Union);
-  const size_t dlds = down_lds_bytes(L, S);
-  // the number of distinct experts is known only on the device: size the
-  // gate/up grid for the largest possible union, capped
-  const long long gu_items = (long long)(S.T * L.K < L.E ? S.T * L.K : L.E) * (L.F / 4);
-  MSK_TRY(launch(kPhGateUp, k_gateup<DT, NV>, grid_for_waves(gu_items), ulds, st, L, S));
-  MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_down<DT, NV>), dlds));
-  MSK_TRY(launch_x(kPhDown, k_down<DT, NV>, grid_for_waves(L.H / 4), dlds, st, L, S, h, out));
+
+// Resident workgroups of a kernel at `lds` bytes, times the CU count.
+static int resident_grid(const void* fn, size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kBlockThreads, lds) != hipSuccess ||
+      n < 1)
+    n = 1;
+  return n * cu_count();
+}
+
+constexpr int kGateUpTokens = 2;  // token vectors staged per gate/up pass
+// slot vectors staged per down pass (NVFP4: two, to keep two waves per SIMD)
+template <int DT> constexpr int kDownTokens = DT == kNVFP4 ? 2 : 4;
+
+template <int DT>
+static hipError_t launch_ffn_tn(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
+                                hipStream_t st) {
+  MSK_TRY(launch_x(kPhUnion, k_union, 1, sizeof(Union), st, L, S));
+  {
+    auto fn = k_gateup_tn<DT, kGateUpTokens>;
+    const size_t lds = (size_t)kGateUpTokens * L.H * sizeof(float);
+    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
+    static int grid = 0;
+    if (grid == 0) grid = resident_grid(reinterpret_cast<const void*>(fn), lds);
+    MSK_TRY(launch(kPhGateUp, fn, grid, lds, st, L, S));
+  }
+  {
+    auto fn = k_down_tn<DT, kDownTokens<DT>>;
+    const size_t lds = (size_t)kDownTokens<DT> * L.F * sizeof(float);
+    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
+    static int grid = 0;
+    if (grid == 0) grid = resident_grid(reinterpret_cast<const void*>(fn), lds);
+    MSK_TRY(launch(kPhDown, fn, grid, lds, st, L, S));
+  }
+  const long long n4 = (long long)S.T * L.H / 4;
+  MSK_TRY(launch_x(kPhMoeSum, k_moe_sum, (int)((n4 + kBlockThreads - 1) / kBlockThreads), 0, st,
+                   L, S, h, out));
   return hipSuccess;
 }
 
@@ -557,13 +648,11 @@ hipError_t launch_ffn(const LayerArgs& L, const StepArgs& S, const float* h, flo
       default: return launch_ffn_t1<kNVFP4>(L, S, h, out, st);
     }
   }
-  const int nv = expert_nv(S.T);
   switch (L.edt) {
-    case kF32: MSK_ENV_CASES(nv, return (launch_ffn_t<kF32, NV>(L, S, h, out, st))) break;
-    case kBF16: MSK_ENV_CASES(nv, return (launch_ffn_t<kBF16, NV>(L, S, h, out, st))) break;
-    default: MSK_ENV_CASES(nv, return (launch_ffn_t<kNVFP4, NV>(L, S, h, out, st))) break;
+    case kF32: return launch_ffn_tn<kF32>(L, S, h, out, st);
+    case kBF16: return launch_ffn_tn<kBF16>(L, S, h, out, st);
+    default: return launch_ffn_tn<kNVFP4>(L, S, h, out, st);
   }
-  return hipSuccess;
 }
 
 // Layer l reads `cur` and writes the next buffer; the last layer writes x_out.

@@ -18,7 +18,17 @@ enum Dt : int { kF32 = 0, kBF16 = 1, kE4M3 = 2, kNVFP4 = 3 };
 // Kernel phases, as numbered by the timing calls of the C ABI.
 enum Phase : int {
   kPhQkv = 0, kPhAttn, kPhCombine, kPhWo, kPhRouter, kPhTopk, kPhGateUp, kPhDown, kPhStep,
-  kNumPhases
+  kPhUnion, kPhMoeSum, kPhPrep, kPhDenseSum, kNumPhases
+};
+
+// Distinct selected experts in ascending order, and per expert the slots
+// (t * K + j) routed to it in ascending order.
+struct Union {
+  int n;                       // distinct experts
+  int list[kMaxExperts];       // expert ids
+  int off[kMaxExperts + 1];    // slot ranges in `slots`
+  int start[kMaxExperts];      // per expert id: first position in slots
+  int slots[kMaxTok * kMaxTopK];
 };
 
 // One layer's shapes, weights, cache and attention plan.
@@ -61,9 +71,29 @@ struct StepArgs {
   float *wts;           // [T][K]
   float *act;           // [T*K][F]
   float *xa, *xb;       // [T][H] layer ping-pong
-  unsigned *sync;       // grid barrier words; sync[0] arrive, sync[1] depart, sync[2] error
+  Union *uni;           // distinct selected experts and their slots
+  float *ybuf;          // [T*K][H] per-slot expert outputs (several tokens)
+  unsigned short *a3;   // [3][T][max(H, Hq*D)] bf16 terms of a projection's input
+  float *dpart;         // dense partial tiles
+  unsigned *sync;       // kSyncBytes of barrier and counter words (zero between calls)
   long long *stamps;    // optional timeline [blocks][kStamps] of 100 MHz counter values
 };
+
+// K slices of a matrix-core dense projection with N rows (blocks of 64) and
+// K columns (tiles of 128): about one (row block, slice) item per resident
+// workgroup (two per CU), at least three k-tiles per slice.
+__host__ __device__ inline int dense_slices(int N, int K) {
+  const int n_rb = (N + 63) / 64;
+  const int tiles = K / 128;
+  const int ks = (512 + n_rb - 1) / n_rb;
+  const int most = tiles / 3 > 1 ? tiles / 3 : 1;
+  return ks < 1 ? 1 : (ks > most ? most : ks);
+}
+
+// The workspace starts with kSyncBytes of words that every entry point finds
+// at the same place and that are zero between calls: the grid barrier
+// (words 0, 1 and 64..64+1024) and the router's arrival counter (word 2).
+constexpr int kSyncBytes = 16384;
 
 constexpr int kStamps = 32;  // timeline slots per workgroup (phase ends, per layer)
 

@@ -99,6 +99,16 @@ __device__ __forceinline__ void store_results(const float (&acc)[R][NV], int nv,
       if (v < nv && ln == ((r * NV + v) & 63)) st(r, v, acc[r][v]);
 }
 
+// x = hi + mid + lo to within 2^-24 |x|; bf16 bits, each term the
+// round-to-nearest-even of what the previous terms leave.
+__device__ __forceinline__ void split3_bf16(float x, unsigned& h, unsigned& m, unsigned& l) {
+  h = f2bf16(x);
+  float r = x - bf16_lo(h);
+  m = f2bf16(r);
+  r -= bf16_lo(m);
+  l = f2bf16(r);
+}
+
 // ------------------------------------------------------------- QKV
 // qkv[t][r] = rstd[t] * sum_c W[r][c] * attn_norm[c] * x[t][c] for the rows of
 // wq, wk, wv stacked (r < Hq*D: wq; then wk; then wv).
@@ -472,7 +482,7 @@ __device__ void phase_attn(const LayerArgs& L, const StepArgs& S, const AttnPlan
 // ---------------------------------------------------------- combine
 // attn_o[t][h] = sum_chunks o / sum_chunks l (plain sums, fixed order).
 __device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int* win_out,
-                              int vb, int nvb) {
+                              int vb, int nvb, unsigned short* a3 = nullptr) {
   const int D = L.D, G = L.Hq / L.Hkv;
   const int rows = S.T * L.Hq;
   const int ln = lane_id();
@@ -505,9 +515,26 @@ __device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnP
       if (ln < D) o0 += p[ln];
       if (ln + 64 < D) o1 += p[ln + 64];
     }
-    float* dst = S.attn_o + (size_t)tok * L.Hq * D + (size_t)hh * D;
-    if (ln < D) dst[ln] = o0 / l;
-    if (ln + 64 < D) dst[ln + 64] = o1 / l;
+    const size_t at = (size_t)tok * L.Hq * D + (size_t)hh * D;
+    const float v0 = o0 / l, v1 = o1 / l;
+    if (ln < D) S.attn_o[at + ln] = v0;
+    if (ln + 64 < D) S.attn_o[at + ln + 64] = v1;
+    if (a3 != nullptr) {  // bf16 terms of the output projection's input
+      const size_t plane = (size_t)S.T * L.Hq * D;
+      unsigned h, m, lo;
+      if (ln < D) {
+        split3_bf16(v0, h, m, lo);
+        a3[at + ln] = (unsigned short)h;
+        a3[plane + at + ln] = (unsigned short)m;
+        a3[2 * plane + at + ln] = (unsigned short)lo;
+      }
+      if (ln + 64 < D) {
+        split3_bf16(v1, h, m, lo);
+        a3[at + ln + 64] = (unsigned short)h;
+        a3[plane + at + ln + 64] = (unsigned short)m;
+        a3[2 * plane + at + ln + 64] = (unsigned short)lo;
+      }
+    }
   }
   if (win_out != nullptr && vb == 0) {
     for (int tok = threadIdx.x; tok < S.T; tok += blockDim.x) {
@@ -601,13 +628,6 @@ __device__ void phase_topk(const LayerArgs& L, const StepArgs& S, int* topk_out,
 // Distinct selected experts in ascending order, and per expert the slots
 // (t * K + j) routed to it in ascending order.  Built identically by every
 // workgroup from idx.
-struct Union {
-  int n;                       // distinct experts
-  int list[kMaxExperts];       // expert ids
-  int off[kMaxExperts + 1];    // slot ranges in `slots`
-  int start[kMaxExperts];      // per expert id: first position in slots
-  int slots[kMaxTok * kMaxTopK];
-};
 
 __device__ inline void build_union(const int* idx, int T, int K, int E, Union* U) {
   const int S = T * K;
@@ -662,113 +682,5 @@ __device__ inline void build_union(const int* idx, int T, int K, int E, Union* U
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
-
-// ------------------------------------------------------------ gate/up
-// act[s][f] = silu(gate_e[f] . u[t]) * (up_e[f] . u[t]) for slot s = t*K + j
-// routed to expert e.  Work items: (expert of the union, block of R rows);
-// both matrices' rows stream once for all of the expert's tokens.
-template <int DT, int NVMAX>
-__device__ void phase_gateup(const LayerArgs& L, const StepArgs& S, const Union* U, int vb, int nvb) {
-  constexpr int R = 4;
-  const int nrb = L.F / R;
-  const int n_items = U->n * nrb;
-  const size_t rb = expert_row_bytes(DT, L.H);
-  const size_t sb = (size_t)L.H / 16;
-  for (int item = gwave(vb, nvb); item < n_items; item += nvb * kWaves) {
-    const int ui = item / nrb, rblk = item - (item / nrb) * nrb;
-    const int e = U->list[ui];
-    const int s0 = U->off[ui], ns = U->off[ui + 1] - s0;
-    const int f0 = rblk * R;
-    const float ggs = DT == kNVFP4 ? L.gg[e] : 1.f;
-    const float gus = DT == kNVFP4 ? L.gu[e] : 1.f;
-    for (int sg = 0; sg < ns; sg += NVMAX) {
-      const int nv = ns - sg < NVMAX ? ns - sg : NVMAX;
-      nv_dispatch<NVMAX>(nv, [&](auto nvc) {
-        constexpr int NV = decltype(nvc)::value;
-        const float* vin[NV];
-#pragma unroll
-        for (int v = 0; v < NV; ++v)
-          vin[v] = S.u + (size_t)(U->slots[s0 + sg + (v < nv ? v : 0)] / L.K) * L.H;
-        const uint8_t* wrow[2 * R];
-        const uint8_t* srow[2 * R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const size_t row = (size_t)e * L.F + f0 + r;
-          wrow[r] = L.wg + row * rb;
-          wrow[R + r] = L.wu + row * rb;
-          srow[r] = DT == kNVFP4 ? L.sg + row * sb : nullptr;
-          srow[R + r] = DT == kNVFP4 ? L.su + row * sb : nullptr;
-        }
-        float acc[2 * R][NV];
-        wave_gemv<DT, 2 * R, NV>(wrow, srow, L.H, vin, nv, nullptr, acc);
-        float res[R][NV];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int v = 0; v < NV; ++v) res[r][v] = silu(acc[r][v] * ggs) * (acc[R + r][v] * gus);
-        store_results<R, NV>(res, nv, [&](int r, int v, float val) {
-          S.act[(size_t)U->slots[s0 + sg + v] * L.F + f0 + r] = val;
-        });
-      });
-    }
-  }
-}
-
-// -------------------------------------------------------------- down
-// out[t][c] = h[t][c] + sum_j wts[t][j] * (down_e[c] . act[t*K + j]), e = idx[t][j],
-// summed in slot order.  Work items: blocks of R output rows; each streams
-// those rows of every expert in the union once.
-template <int DT, int NVMAX>
-__device__ void phase_down(const LayerArgs& L, const StepArgs& S, const Union* U, const float* h,
-                           float* out, float* ybuf_all, int vb, int nvb) {
-  constexpr int R = 4;
-  const int TK = S.T * L.K;
-  float* ybuf = ybuf_all + (size_t)wave_id() * TK * R;
-  const size_t rb = expert_row_bytes(DT, L.F);
-  const size_t sb = (size_t)L.F / 16;
-  const int ln = lane_id();
-  for (int blk = gwave(vb, nvb); blk * R < L.H; blk += nvb * kWaves) {
-    const int c0 = blk * R;
-    for (int i = ln; i < TK * R; i += 64) ybuf[i] = 0.f;
-    wave_lds_sync();
-    for (int ui = 0; ui < U->n; ++ui) {
-      const int e = U->list[ui];
-      const int s0 = U->off[ui], ns = U->off[ui + 1] - s0;
-      const float gds = DT == kNVFP4 ? L.gd[e] : 1.f;
-      for (int sg = 0; sg < ns; sg += NVMAX) {
-        const int nv = ns - sg < NVMAX ? ns - sg : NVMAX;
-        nv_dispatch<NVMAX>(nv, [&](auto nvc) {
-          constexpr int NV = decltype(nvc)::value;
-          const float* vin[NV];
-#pragma unroll
-          for (int v = 0; v < NV; ++v)
-            vin[v] = S.act + (size_t)U->slots[s0 + sg + (v < nv ? v : 0)] * L.F;
-          const uint8_t* wrow[R];
-          const uint8_t* srow[R];
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            const size_t row = (size_t)e * L.H + c0 + r;
-            wrow[r] = L.wd + row * rb;
-            srow[r] = DT == kNVFP4 ? L.sd + row * sb : nullptr;
-          }
-          float acc[R][NV];
-          wave_gemv<DT, R, NV>(wrow, srow, L.F, vin, nv, nullptr, acc);
-          store_results<R, NV>(acc, nv, [&](int r, int v, float val) {
-            ybuf[U->slots[s0 + sg + v] * R + r] = val * gds;
-          });
-        });
-      }
-    }
-    wave_lds_sync();
-    for (int i = ln; i < S.T * R; i += 64) {
-      const int t = i / R, r = i - (i / R) * R;
-      const size_t o = (size_t)t * L.H + c0 + r;
-      float acc = h[o];
-      for (int j = 0; j < L.K; ++j) acc += S.wts[t * L.K + j] * ybuf[(t * L.K + j) * R + r];
-      out[o] = acc;
-    }
-    wave_lds_sync();
-  }
-}
 
 }  // namespace msk

@@ -224,8 +224,9 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
   float lsum = 0.f;
 
   fetch(p0);
+  __syncthreads();  // rk is written
   for (int pb = p0; pb < p1; pb += 64) {
-    __syncthreads();  // the previous tile's readers are done; rk is written
+    lds_barrier();  // the previous tile's readers are done
     // K -> kb[pos][d] (bf16)
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
@@ -266,7 +267,7 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
       }
     }
     if (pb + 64 < p1) fetch(pb + 64);
-    __syncthreads();
+    lds_barrier();
 
     // scores of this wave's 16 rows against the tile's 64 positions
     f32x4 sacc[4];

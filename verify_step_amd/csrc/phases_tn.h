@@ -1,0 +1,295 @@
+// Expert FFN for steps of several tokens: only the distinct selected experts
+// are streamed, each once for all the tokens routed to it.
+//
+// The union of selected experts (ascending ids, each with its slots
+// t * K + j in ascending order) is built once per call into the workspace.
+// The (expert, row block) tasks are laid out expert-major and every
+// workgroup takes one contiguous, equally long range of them, so a
+// workgroup meets one or two experts: it stages the input vectors of that
+// expert's tokens in LDS and its four waves stream their share of the rows
+// two buffers deep, as the one-token kernels do.  An expert with more
+// tokens than the staging holds is streamed once per group of tokens.
+//
+// down writes y[slot][c] = down_e[c] . act[slot]; the combine then forms
+// out[t][c] = h[t][c] + sum_j w[t][j] * y[t*K + j][c] in slot order.
+#pragma once
+#include "phases_t1.h"
+
+namespace msk {
+
+// Like stream_t1, for nv <= NV input vectors in LDS: acc[r][v] =
+// sum_c W_r[c] * in_v[c] (NVFP4: with block scales, matrix scale left out).
+template <int DT, int R, int U, int NV, class ActFn, class RowFn, class OutFn, class PreFn>
+__device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& actfn,
+                                          RowFn&& rowfn, OutFn&& out, PreFn&& pre) {
+  using W = WT<DT>;
+  const int ln = lane_id();
+  const int nch = ncols / W::EPL;
+  const int NI = (nch + 64 * U - 1) / (64 * U);
+  const int total = ntask * NI;
+  v4u A[U][R], B[U][R];
+  unsigned sA[U][R], sB[U][R];
+  float acc[R][NV];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc[r][v] = 0.f;
+
+  auto issue = [&](v4u(&w)[U][R], unsigned(&s)[U][R], int f) {
+    const int k = f / NI, i = f - (f / NI) * NI;
+    const uint8_t* wr[R];
+    const uint8_t* sr[R];
+    rowfn(k, wr, sr);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ch = (i * U + u) * 64 + ln;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (ch < nch) {
+          w[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wr[r]) + ch);
+          if constexpr (DT == kNVFP4)
+            s[u][r] = *reinterpret_cast<const unsigned short*>(sr[r] + 2 * ch);
+          else
+            s[u][r] = 0u;
+        } else {
+          w[u][r] = v4u{0u, 0u, 0u, 0u};
+          s[u][r] = 0u;
+        }
+      }
+    }
+  };
+  auto compute = [&](const v4u(&w)[U][R], const unsigned(&s)[U][R], int f) {
+    const int k = f / NI, i = f - (f / NI) * NI;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ch = (i * U + u) * 64 + ln;
+      if (ch < nch) {
+        v2f sc[R];
+        if constexpr (DT == kNVFP4) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) sc[r] = __builtin_amdgcn_cvt_pk_f32_fp8(s[u][r], false);
+        }
+#pragma unroll
+        for (int sub = 0; sub < W::NSUB; ++sub) {
+          float fw[R][W::SUB];
+#pragma unroll
+          for (int r = 0; r < R; ++r) decode_sub<DT>(w[u][r], sub, fw[r]);
+#pragma unroll
+          for (int v = 0; v < NV; ++v) {
+            if (v < nv) {
+              float a[W::SUB];
+              load_act(actfn(v) + ch * W::EPL + sub * W::SUB, a, W::SUB);
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < W::SUB; ++e) d = fmaf(fw[r][e], a[e], d);
+                if constexpr (DT == kNVFP4)
+                  acc[r][v] = fmaf((sub >> 1) ? sc[r].y : sc[r].x, d, acc[r][v]);
+                else
+                  acc[r][v] += d;
+              }
+            }
+          }
+        }
+      }
+    }
+    if (i == NI - 1) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[r][v] = v < nv ? wave_sum(acc[r][v]) : 0.f;
+      out(k, acc);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) acc[r][v] = 0.f;
+    }
+  };
+  if (total > 0) issue(A, sA, 0);
+  if (total > 1) issue(B, sB, 1);
+  pre();
+  for (int f = 0; f < total; f += 2) {
+    compute(A, sA, f);
+    if (f + 2 < total) issue(A, sA, f + 2);
+    if (f + 1 < total) {
+      compute(B, sB, f + 1);
+      if (f + 3 < total) issue(B, sB, f + 3);
+    }
+  }
+}
+
+// The union into global memory (one workgroup).
+__device__ inline void union_to_global(const int* idx, int T, int K, int E, Union* lds, Union* dst) {
+  build_union(idx, T, K, E, lds);
+  const int* s = reinterpret_cast<const int*>(lds);
+  int* d = reinterpret_cast<int*>(dst);
+  for (int i = threadIdx.x; i < (int)(sizeof(Union) / 4); i += blockDim.x) d[i] = s[i];
+}
+
+// This workgroup's contiguous share [t0, t1) of `total` tasks.
+__device__ __forceinline__ void wg_range(long long total, int& t0, int& t1) {
+  t0 = (int)(total * blockIdx.x / gridDim.x);
+  t1 = (int)(total * (blockIdx.x + 1) / gridDim.x);
+}
+
+// Runs body(ui, a, b, s0, nv) for every (expert ui of the union, group of at
+// most NVMAX of its slots starting at slot index s0) that the workgroup's
+// task range meets, with that expert's tasks [a, b) of the range; `stage`
+// fills the LDS inputs for the group.  Every wave calls body for every group.
+template <int NVMAX, class Body>
+__device__ __forceinline__ void for_expert_groups(const Union* U, int nrt, Body&& body) {
+  const int n = U->n;
+  int t0, t1;
+  wg_range((long long)n * nrt, t0, t1);
+  int tau = t0;
+  while (tau < t1) {
+    const int ui = tau / nrt;
+    const int seg_end = (ui + 1) * nrt < t1 ? (ui + 1) * nrt : t1;
+    const int s0 = U->off[ui], ns = U->off[ui + 1] - s0;
+    for (int sg = 0; sg < ns; sg += NVMAX) {
+      const int nv = ns - sg < NVMAX ? ns - sg : NVMAX;
+      body(ui, tau, seg_end, s0 + sg, nv);
+    }
+    tau = seg_end;
+  }
+}
+
+// Rows per task and 16-B chunks per lane per step, as measured best on the
+// GPU: NVFP4's decode needs the registers, so it streams one chunk deep.
+template <int DT> struct TnShape;
+template <> struct TnShape<kF32> { enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2 }; };
+template <> struct TnShape<kBF16> { enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2 }; };
+template <> struct TnShape<kNVFP4> { enum { GU_RW = 2, GU_U = 1, DN_R = 4, DN_U = 1 }; };
+
+// act[s][f] = silu(gate_e[f] . u[t]) * (up_e[f] . u[t]) for slot s = t*K + j.
+// Tasks: (expert, RW rows of gate and the same RW rows of up).
+template <int DT, int NVMAX>
+__device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U, float* act_lds) {
+  constexpr int RW = TnShape<DT>::GU_RW, R = 2 * RW, UU = TnShape<DT>::GU_U;
+  const int nrt = L.F / RW;
+  const size_t rb = expert_row_bytes(DT, L.H);
+  const size_t sb = (size_t)L.H / 16;
+  const int wv = wave_id();
+  for_expert_groups<NVMAX>(U, nrt, [&](int ui, int a, int b, int sidx, int nv) {
+    const int e = U->list[ui];
+    const int nt = b - a;
+    const int w0 = a + nt * wv / kWaves, w1 = a + nt * (wv + 1) / kWaves;
+    const float ggs = DT == kNVFP4 ? L.gg[e] : 1.f;
+    const float gus = DT == kNVFP4 ? L.gu[e] : 1.f;
+    auto pre = [&]() {
+      __syncthreads();  // the previous group's readers are done
+      for (int v = 0; v < nv; ++v) {
+        const float* src = S.u + (size_t)(U->slots[sidx + v] / L.K) * L.H;
+        for (int c = threadIdx.x * 4; c < L.H; c += blockDim.x * 4)
+          *reinterpret_cast<v4f*>(act_lds + v * L.H + c) = *reinterpret_cast<const v4f*>(src + c);
+      }
+      __syncthreads();
+    };
+    nv_dispatch<NVMAX>(nv, [&](auto nvc) {
+      constexpr int NV = decltype(nvc)::value;
+      stream_tn<DT, R, UU, NV>(
+          w1 - w0, L.H, nv, [&](int v) { return act_lds + v * L.H; },
+          [&](int k, auto& wr, auto& sr) {
+            const int f0 = (w0 + k - ui * nrt) * RW;
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+              const size_t row = (size_t)e * L.F + f0 + r;
+              wr[r] = L.wg + row * rb;
+              wr[RW + r] = L.wu + row * rb;
+              sr[r] = DT == kNVFP4 ? L.sg + row * sb : nullptr;
+              sr[RW + r] = DT == kNVFP4 ? L.su + row * sb : nullptr;
+            }
+          },
+          [&](int k, auto& acc) {
+            const int f0 = (w0 + k - ui * nrt) * RW;
+            const int ln = lane_id();
+#pragma unroll
+            for (int r = 0; r < RW; ++r)
+#pragma unroll
+              for (int v = 0; v < NV; ++v)
+                if (v < nv && ln == r * NV + v)
+                  S.act[(size_t)U->slots[sidx + v] * L.F + f0 + r] =
+                      silu(acc[r][v] * ggs) * (acc[RW + r][v] * gus);
+          },
+          pre);
+    });
+  });
+}
+
+// y[s][c] = down_e[c] . act[s] (times the NVFP4 matrix scale) for the slots
+// s routed to expert e.  Tasks: (expert, RD output rows).
+template <int DT, int NVMAX>
+__device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, float* act_lds,
+                        float* y) {
+  constexpr int RD = TnShape<DT>::DN_R, UU = TnShape<DT>::DN_U;
+  const int nrt = L.H / RD;
+  const size_t rb = expert_row_bytes(DT, L.F);
+  const size_t sb = (size_t)L.F / 16;
+  const int wv = wave_id();
+  for_expert_groups<NVMAX>(U, nrt, [&](int ui, int a, int b, int sidx, int nv) {
+    const int e = U->list[ui];
+    const int nt = b - a;
+    const int w0 = a + nt * wv / kWaves, w1 = a + nt * (wv + 1) / kWaves;
+    const float gds = DT == kNVFP4 ? L.gd[e] : 1.f;
+    auto pre = [&]() {
+      __syncthreads();
+      for (int v = 0; v < nv; ++v) {
+        const float* src = S.act + (size_t)U->slots[sidx + v] * L.F;
+        for (int c = threadIdx.x * 4; c < L.F; c += blockDim.x * 4)
+          *reinterpret_cast<v4f*>(act_lds + v * L.F + c) = *reinterpret_cast<const v4f*>(src + c);
+      }
+      __syncthreads();
+    };
+    nv_dispatch<NVMAX>(nv, [&](auto nvc) {
+      constexpr int NV = decltype(nvc)::value;
+      stream_tn<DT, RD, UU, NV>(
+          w1 - w0, L.F, nv, [&](int v) { return act_lds + v * L.F; },
+          [&](int k, auto& wr, auto& sr) {
+            const int c0 = (w0 + k - ui * nrt) * RD;
+#pragma unroll
+            for (int r = 0; r < RD; ++r) {
+              const size_t row = (size_t)e * L.H + c0 + r;
+              wr[r] = L.wd + row * rb;
+              sr[r] = DT == kNVFP4 ? L.sd + row * sb : nullptr;
+            }
+          },
+          [&](int k, auto& acc) {
+            const int c0 = (w0 + k - ui * nrt) * RD;
+            const int ln = lane_id();
+#pragma unroll
+            for (int r = 0; r < RD; ++r)
+#pragma unroll
+              for (int v = 0; v < NV; ++v)
+                if (v < nv && ln == r * NV + v)
+                  y[(size_t)U->slots[sidx + v] * L.H + c0 + r] = acc[r][v] * gds;
+          },
+          pre);
+    });
+  });
+}
+
+// out[t][c] = h[t][c] + sum_j w[t][j] * y[t*K + j][c], j ascending; slots
+// whose expert id is out of range add nothing.
+__device__ inline void down_combine(const LayerArgs& L, const StepArgs& S, const float* h,
+                                    const float* y, float* out) {
+  const int n4 = S.T * L.H / 4;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x) {
+    const int t = (i * 4) / L.H, c = i * 4 - t * L.H;
+    v4f acc = *reinterpret_cast<const v4f*>(h + (size_t)t * L.H + c);
+    for (int j = 0; j < L.K; ++j) {
+      const int s = t * L.K + j;
+      const int e = S.idx[s];
+      if (e < 0 || e >= L.E) continue;
+      const float w = S.wts[s];
+      const v4f yy = *reinterpret_cast<const v4f*>(y + (size_t)s * L.H + c);
+      acc.x = fmaf(w, yy.x, acc.x);
+      acc.y = fmaf(w, yy.y, acc.y);
+      acc.z = fmaf(w, yy.z, acc.z);
+      acc.w = fmaf(w, yy.w, acc.w);
+    }
+    *reinterpret_cast<v4f*>(out + (size_t)t * L.H + c) = acc;
+  }
+}
+
+}  // namespace msk
