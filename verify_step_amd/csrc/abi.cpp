@@ -41,7 +41,7 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 constexpr long long kTargetItems = 2048;
 
 struct AttnSplit {
-  int chunk, n_items, nrg, rows, nw;
+  int chunk, n_items, nrg, rows, nw, nph;
 };
 
 // Query rows of one (request, kv head) pair, G * Tr, go to the matrix cores
@@ -54,10 +54,18 @@ AttnSplit plan_attention(const msk_layer_cfg& c, const msk_batch& b) {
   const bool mfma = (c.kv_dtype == MSK_BF16 || c.kv_dtype == MSK_E4M3) && M > msk::kRowGroup;
   const int m1 = M < 64 ? M : 64;
   int nw = mfma ? cdiv(m1, 16) : 0;
-  // a one-wave item over a bf16 cache of head_dim 128 would prefetch a
-  // whole 32-KB tile per wave, more registers than a wave has: two waves
-  if (nw == 1 && c.kv_dtype == MSK_BF16 && c.head_dim == 128) nw = 2;
-  const int rows = mfma ? 16 * nw : msk::kRowGroup;
+  // head_dim 128: a one-wave item over a bf16 cache would prefetch a whole
+  // 32-KB tile into one wave's registers, so two waves at least; e4m3 items
+  // take four waves, whose smaller per-thread share of the tile lets three
+  // waves per SIMD stay resident
+  if (mfma && c.head_dim == 128 && c.kv_dtype == MSK_BF16 && nw < 2) nw = 2;
+  int nph = 1;
+  if (mfma && c.head_dim == 128 && c.kv_dtype == MSK_E4M3) {
+    // up to two row tiles: pairs of waves split each tile's positions
+    nph = nw <= 2 ? 2 : 1;
+    nw = 4;
+  }
+  const int rows = mfma ? 16 * nw / nph : msk::kRowGroup;
   const int nrg = cdiv(M, rows);
   long long total = 0;
   for (int r = 0; r < b.n_req; ++r) {
@@ -79,7 +87,7 @@ AttnSplit plan_attention(const msk_layer_cfg& c, const msk_batch& b) {
     const int base = lo & ~63, end = L + b.tokens_per_req;
     items += (long long)cdiv(end - base, chunk) * c.n_kv_heads * nrg;
   }
-  return AttnSplit{(int)chunk, (int)items, nrg, rows, nw};
+  return AttnSplit{(int)chunk, (int)items, nrg, rows, nw, nph};
 }
 
 struct Layout {
@@ -291,6 +299,7 @@ msk::LayerArgs make_layer(const msk_layer_cfg& c, const msk_layer_weights* w, co
     L.nrg = a.nrg;
     L.rg_rows = a.rows;
     L.attn_nw = a.nw;
+    L.attn_nph = a.nph;
   }
   return L;
 }

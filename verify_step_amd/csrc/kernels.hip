@@ -38,12 +38,18 @@ __global__ __launch_bounds__(kBlockThreads) void k_attn(LayerArgs L, StepArgs S)
   phase_attn<KDT, D>(L, S, P, msk_smem + align_up(sizeof(AttnPlan), 16), blockIdx.x, gridDim.x);
 }
 
-template <int KDT, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void k_attn_mfma(LayerArgs L, StepArgs S) {
+// The tile fetch is one tile deep per workgroup, so the bytes in flight come
+// from resident workgroups: e4m3 caches (16 KB tiles) run three waves per
+// SIMD; bf16 tiles are twice the registers and keep the compiler's choice.
+template <int KDT> struct AttnWaves { static constexpr int N = KDT == kE4M3 ? 3 : 1; };
+
+template <int KDT, int D, int NW, int NPH>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(AttnWaves<KDT>::N)))
+void k_attn_mfma(LayerArgs L, StepArgs S) {
   AttnPlan* P = reinterpret_cast<AttnPlan*>(msk_smem);
   build_plan(L, S, P);
-  phase_attn_mfma<KDT, D, NW>(L, S, P, msk_smem + align_up(sizeof(AttnPlan), 16), blockIdx.x,
-                              gridDim.x);
+  phase_attn_mfma<KDT, D, NW, NPH>(L, S, P, msk_smem + align_up(sizeof(AttnPlan), 16),
+                                   blockIdx.x, gridDim.x);
 }
 
 // Several tokens: the expert union once, then gate/up and down over it,
@@ -457,10 +463,10 @@ static hipError_t launch_dense(const StepArgs& S, const uint8_t* w0, const uint8
 
 // Matrix-core attention: as many resident workgroups as the CUs hold, each
 // looping over items.
-template <int KDT, int D, int NW>
+template <int KDT, int D, int NW, int NPH = 1>
 static hipError_t launch_attn_mfma_t(const LayerArgs& L, const StepArgs& S, hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&k_attn_mfma<KDT, D, NW>);
-  const size_t lds = align_up(sizeof(AttnPlan), 16) + MfmaGeom<KDT, D, NW>::LDS;
+  const void* fn = reinterpret_cast<const void*>(&k_attn_mfma<KDT, D, NW, NPH>);
+  const size_t lds = align_up(sizeof(AttnPlan), 16) + MfmaGeom<KDT, D, NW, NPH>::LDS;
   MSK_TRY(set_lds_limit(fn, lds));
   static int per_cu = 0;  // one value per instantiation
   if (per_cu == 0) {
@@ -470,19 +476,27 @@ static hipError_t launch_attn_mfma_t(const LayerArgs& L, const StepArgs& S, hipS
   }
   const long long cap = (long long)per_cu * cu_count();
   const int grid = (int)(L.n_items < cap ? L.n_items : cap);
-  return launch_b(kPhAttn, k_attn_mfma<KDT, D, NW>, grid, NW * 64, lds, st, L, S);
+  return launch_b(kPhAttn, k_attn_mfma<KDT, D, NW, NPH>, grid, NW * 64, lds, st, L, S);
 }
 
 template <int KDT, int D>
 static hipError_t launch_attn_mfma_d(const LayerArgs& L, const StepArgs& S, hipStream_t st) {
   switch (L.attn_nw) {
+    // the planner gives bf16 caches of head_dim 128 at least two waves and
+    // e4m3 caches of head_dim 128 four (register budget)
     case 1:
-      // the planner gives this pair two waves (register budget)
-      if constexpr (KDT == kBF16 && D == 128) return hipErrorInvalidValue;
+      if constexpr (D == 128) return hipErrorInvalidValue;
       else return launch_attn_mfma_t<KDT, D, 1>(L, S, st);
-    case 2: return launch_attn_mfma_t<KDT, D, 2>(L, S, st);
-    case 3: return launch_attn_mfma_t<KDT, D, 3>(L, S, st);
-    default: return launch_attn_mfma_t<KDT, D, 4>(L, S, st);
+    case 2:
+      if constexpr (D == 128 && KDT == kE4M3) return hipErrorInvalidValue;
+      else return launch_attn_mfma_t<KDT, D, 2>(L, S, st);
+    case 3:
+      if constexpr (D == 128 && KDT == kE4M3) return hipErrorInvalidValue;
+      else return launch_attn_mfma_t<KDT, D, 3>(L, S, st);
+    default:
+      if constexpr (D == 128 && KDT == kE4M3)
+        if (L.attn_nph == 2) return launch_attn_mfma_t<KDT, D, 4, 2>(L, S, st);
+      return launch_attn_mfma_t<KDT, D, 4>(L, S, st);
   }
 }
 

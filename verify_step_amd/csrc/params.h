@@ -47,7 +47,8 @@ struct LayerArgs {
   int nrg;      // query row groups per kv head: ceil(G * Tr / rg_rows)
   int rg_rows;  // query rows per row group (and per partial-sum block)
   int attn_nw;  // 0: vector attention (rg_rows = kRowGroup); else waves of
-                // the matrix-core attention, rg_rows = 16 * attn_nw
+                // the matrix-core attention, rg_rows = 16 * attn_nw / attn_nph
+  int attn_nph; // matrix-core attention: waves sharing each 16-row tile (1, 2)
 };
 
 // Buffers of one step; the per-layer arrays follow the layer index.

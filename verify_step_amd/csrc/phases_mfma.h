@@ -35,7 +35,7 @@ namespace msk {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int KDT, int D, int NW>
+template <int KDT, int D, int NW, int NPH = 1>
 struct MfmaGeom {
   static constexpr int ES = KV<KDT>::ES;
   static constexpr int RB = D * ES;        // cache row bytes
@@ -53,7 +53,9 @@ struct MfmaGeom {
   static constexpr int LDS_KB = 64 * KBS;
   static constexpr int LDS_VT = D * VTS;
   static constexpr int LDS = LDS_KB + LDS_VT + kMaxTok * 4;
-  static constexpr int ROWS = 16 * NW;     // query rows per item
+  static constexpr int ROWS = 16 * NW / NPH;  // query rows per item
+  static constexpr int NPT = 4 / NPH;      // 16-position tiles per wave
+  static constexpr int NKS = 2 / NPH;      // 32-position k steps per wave
 };
 
 __device__ __forceinline__ unsigned pack_bf16_exact(float a, float b) {
@@ -87,18 +89,21 @@ __device__ __forceinline__ void split_bf16(float x, unsigned& hi, unsigned& lo) 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const v4u& v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <int KDT, int D, int NW>
+// NPH = 2: the waves pair up on the same 16 rows, each taking half of every
+// tile's positions; the pair's sums are added at the end of the item.
+template <int KDT, int D, int NW, int NPH>
 __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int item,
                                uint8_t* wl) {
-  using Gm = MfmaGeom<KDT, D, NW>;
+  using Gm = MfmaGeom<KDT, D, NW, NPH>;
   constexpr int RB = Gm::RB, CPR = Gm::CPR, EPC = Gm::EPC, NT = Gm::NT;
   constexpr int KPT = Gm::KPT, VPT = Gm::VPT, KBS = Gm::KBS, VTS = Gm::VTS;
-  constexpr int DS = Gm::DS, NDT = Gm::NDT, ROWS = Gm::ROWS;
+  constexpr int DS = Gm::DS, NDT = Gm::NDT, ROWS = Gm::ROWS, NPT = Gm::NPT, NKS = Gm::NKS;
   uint8_t* kb = wl;
   uint8_t* vt = wl + Gm::LDS_KB;
   float* rk = reinterpret_cast<float*>(vt + Gm::LDS_VT);
 
   const int tid = threadIdx.x, ln = lane_id(), wv = wave_id();
+  const int rt = wv / NPH, ph = wv - (wv / NPH) * NPH;  // row tile, position half
   int b = 0;
   while (b + 1 < S.n_req && P->item0[b + 1] <= item) ++b;
   const int nch = P->nch[b];
@@ -120,7 +125,7 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
   const bool writer = (rg == 0);
 
   // this lane's query row (lanes l, l^16, l^32, l^48 share it) and its window
-  const int mr = m0 + 16 * wv + (ln & 15);
+  const int mr = m0 + 16 * rt + (ln & 15);
   const bool live = mr < M;
   const int t_me = live ? mr / G : 0;
   const int g_me = live ? mr - t_me * G : 0;
@@ -233,11 +238,8 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
       const int q = tid + u * NT;
       if (q < Gm::NKC) {
         const int row = q / CPR, cc = q % CPR;
-        const int pos = pb + row;
-        v4u raw = kr[u];
-        if (pos >= Lb && pos < p1) raw = new_chunk(pos, cc, false);
         unsigned o[EPC / 2];
-        chunk_to_bf16<KDT>(raw, o);
+        chunk_to_bf16<KDT>(kr[u], o);
         uint8_t* dst = kb + row * KBS + cc * EPC * 2;
 #pragma unroll
         for (int w = 0; w < EPC / 2; w += 4)
@@ -252,12 +254,7 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
         const int pp = q / CPR, cc = q % CPR;
         unsigned o[2][EPC / 2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int pos = pb + 2 * pp + h;
-          v4u raw = vr[u][h];
-          if (pos >= Lb && pos < p1) raw = new_chunk(pos, cc, true);
-          chunk_to_bf16<KDT>(raw, o[h]);
-        }
+        for (int h = 0; h < 2; ++h) chunk_to_bf16<KDT>(vr[u][h], o[h]);
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
           const unsigned a = (e & 1) ? o[0][e >> 1] >> 16 : o[0][e >> 1] & 0xffffu;
@@ -267,46 +264,76 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
       }
     }
     if (pb + 64 < p1) fetch(pb + 64);
+    // the step's own rows in this tile (zero above): rebuilt, stored, converted
+    const int n0 = pb > Lb ? pb : Lb;
+    const int n1 = pb + 64 < p1 ? pb + 64 : p1;
+    if (n0 < n1) {
+      lds_barrier();
+      const int nn = (n1 - n0) * CPR;
+      for (int q = tid; q < 2 * nn; q += NT) {
+        const bool value = q >= nn;
+        const int qq = value ? q - nn : q;
+        const int pos = n0 + qq / CPR, cc = qq % CPR;
+        unsigned o[EPC / 2];
+        chunk_to_bf16<KDT>(new_chunk(pos, cc, value), o);
+        const int row = pos - pb;
+        if (!value) {
+          uint8_t* dst = kb + row * KBS + cc * EPC * 2;
+#pragma unroll
+          for (int w = 0; w < EPC / 2; w += 4)
+            *reinterpret_cast<v4u*>(dst + 4 * w) = v4u{o[w], o[w + 1], o[w + 2], o[w + 3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPC; ++e)
+            *reinterpret_cast<unsigned short*>(vt + (cc * EPC + e) * VTS + 2 * row) =
+                (unsigned short)((e & 1) ? o[e >> 1] >> 16 : o[e >> 1] & 0xffffu);
+        }
+      }
+    }
     lds_barrier();
 
-    // scores of this wave's 16 rows against the tile's 64 positions
-    f32x4 sacc[4];
+    if (m0 + 16 * rt >= M) continue;  // a wave without live rows only fetches
+    // scores of this wave's 16 rows against its NPT 16-position tiles
+    f32x4 sacc[NPT];
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      sacc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int pq = 0; pq < NPT; ++pq) {
+      const int pt = ph * NPT + pq;
+      sacc[pq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < DS; ++ks) {
         const bf16x8 a = as_bf16x8(*reinterpret_cast<const v4u*>(
             kb + (16 * pt + (ln & 15)) * KBS + (32 * ks + 8 * (ln >> 4)) * 2));
-        sacc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], sacc[pt], 0, 0, 0);
-        sacc[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[ks], sacc[pt], 0, 0, 0);
+        sacc[pq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[ks], sacc[pq], 0, 0, 0);
+        sacc[pq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[ks], sacc[pq], 0, 0, 0);
       }
     }
     // weights: lane holds row m, positions 16 pt + 4 (ln >> 4) + i
-    unsigned wh[2][4], wlo[2][4];
+    unsigned wh[NKS][4], wlo[NKS][4];
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
+    for (int pq = 0; pq < NPT; ++pq) {
+      const int pt = ph * NPT + pq;
       unsigned hh[4], ll[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int pos = pb + 16 * pt + 4 * (ln >> 4) + i;
         const bool ok = pos >= w_lo && pos <= w_hi && pos < p1;
-        const float e = ok ? __expf(sacc[pt][i] - L.shift) : 0.f;
+        const float e = ok ? __expf(sacc[pq][i] - L.shift) : 0.f;
         lsum += e;
         split_bf16(e, hh[i], ll[i]);
       }
       // k index 8 (ln >> 4) + 4 (pt & 1) + i of k step pt / 2
-      wh[pt >> 1][2 * (pt & 1)] = hh[0] | hh[1] << 16;
-      wh[pt >> 1][2 * (pt & 1) + 1] = hh[2] | hh[3] << 16;
-      wlo[pt >> 1][2 * (pt & 1)] = ll[0] | ll[1] << 16;
-      wlo[pt >> 1][2 * (pt & 1) + 1] = ll[2] | ll[3] << 16;
+      wh[pq >> 1][2 * (pt & 1)] = hh[0] | hh[1] << 16;
+      wh[pq >> 1][2 * (pt & 1) + 1] = hh[2] | hh[3] << 16;
+      wlo[pq >> 1][2 * (pt & 1)] = ll[0] | ll[1] << 16;
+      wlo[pq >> 1][2 * (pt & 1) + 1] = ll[2] | ll[3] << 16;
     }
     // O^T[d][m] += V^T[d][pos] e[pos][m]; the A operand's k numbering matches
     // the weights': positions 32 ks + 4 (ln >> 4) + {0..3} and + 16 + {0..3}
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 bh = as_bf16x8(v4u{wh[ks][0], wh[ks][1], wh[ks][2], wh[ks][3]});
-      const bf16x8 bl = as_bf16x8(v4u{wlo[ks][0], wlo[ks][1], wlo[ks][2], wlo[ks][3]});
+    for (int kq = 0; kq < NKS; ++kq) {
+      const int ks = ph * NKS + kq;
+      const bf16x8 bh = as_bf16x8(v4u{wh[kq][0], wh[kq][1], wh[kq][2], wh[kq][3]});
+      const bf16x8 bl = as_bf16x8(v4u{wlo[kq][0], wlo[kq][1], wlo[kq][2], wlo[kq][3]});
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const uint8_t* src = vt + (16 * dt + (ln & 15)) * VTS + (32 * ks + 4 * (ln >> 4)) * 2;
@@ -318,10 +345,31 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
       }
     }
   }
-  // partial sums of this wave's rows: part[item][row][d], part[item][row][D] = l
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  float* part = S.part + ((size_t)item * ROWS + 16 * wv + (ln & 15)) * (D + 1);
+  if constexpr (NPH == 2) {
+    // the second half's sums go through LDS (the K tile is free by now) to
+    // the first, which adds them in that order
+    float* xs = reinterpret_cast<float*>(kb) + rt * (NDT * 4 + 1) * 64;
+    lds_barrier();
+    if (ph == 1) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[(dt * 4 + i) * 64 + ln] = oacc[dt][i];
+      xs[NDT * 4 * 64 + ln] = lsum;
+    }
+    lds_barrier();
+    if (ph == 1) return;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[dt][i] += xs[(dt * 4 + i) * 64 + ln];
+    lsum += xs[NDT * 4 * 64 + ln];
+  }
+  // partial sums of this wave's rows: part[item][row][d], part[item][row][D] = l
+  if (m0 + 16 * rt >= M) return;
+  float* part = S.part + ((size_t)item * ROWS + 16 * rt + (ln & 15)) * (D + 1);
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -329,12 +377,12 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
   if (ln < 16) part[D] = lsum;
 }
 
-template <int KDT, int D, int NW>
+template <int KDT, int D, int NW, int NPH>
 __device__ void phase_attn_mfma(const LayerArgs& L, const StepArgs& S, const AttnPlan* P,
                                 uint8_t* lds, int vb, int nvb) {
   const int n_items = P->item0[S.n_req];
   for (int item = vb; item < n_items; item += nvb) {
-    attn_item_mfma<KDT, D, NW>(L, S, P, item, lds);
+    attn_item_mfma<KDT, D, NW, NPH>(L, S, P, item, lds);
     __syncthreads();
   }
 }
