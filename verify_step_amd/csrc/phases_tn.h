@@ -42,17 +42,20 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
     rowfn(k, wr, sr);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      // every lane loads (a clamped chunk past the row end, zeroed after),
+      // so the number of loads in flight is the same on every path and the
+      // waits before each compute step count exactly to that step's loads
       const int ch = (i * U + u) * 64 + ln;
+      const bool in = ch < nch;
+      const int cc = in ? ch : nch - 1;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        if (ch < nch) {
-          w[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wr[r]) + ch);
-          if constexpr (DT == kNVFP4)
-            s[u][r] = *reinterpret_cast<const unsigned short*>(sr[r] + 2 * ch);
-          else
-            s[u][r] = 0u;
+        const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wr[r]) + cc);
+        w[u][r] = in ? x : v4u{0u, 0u, 0u, 0u};
+        if constexpr (DT == kNVFP4) {
+          const unsigned y = *reinterpret_cast<const unsigned short*>(sr[r] + 2 * cc);
+          s[u][r] = in ? y : 0u;
         } else {
-          w[u][r] = v4u{0u, 0u, 0u, 0u};
           s[u][r] = 0u;
         }
       }
@@ -106,16 +109,19 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
         for (int v = 0; v < NV; ++v) acc[r][v] = 0.f;
     }
   };
-  if (total > 0) issue(A, sA, 0);
-  if (total > 1) issue(B, sB, 1);
+  // the refills are issued on every iteration (past the end they repeat the
+  // last step's addresses, unused), for the same reason
+  const int last = total - 1;
+  if (total > 0) {
+    issue(A, sA, 0);
+    issue(B, sB, 1 < last ? 1 : last);
+  }
   pre();
   for (int f = 0; f < total; f += 2) {
     compute(A, sA, f);
-    if (f + 2 < total) issue(A, sA, f + 2);
-    if (f + 1 < total) {
-      compute(B, sB, f + 1);
-      if (f + 3 < total) issue(B, sB, f + 3);
-    }
+    issue(A, sA, f + 2 < last ? f + 2 : last);
+    if (f + 1 < total) compute(B, sB, f + 1);
+    issue(B, sB, f + 3 < last ? f + 3 : last);
   }
 }
 
@@ -177,10 +183,16 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
     const int w0 = a + nt * wv / kWaves, w1 = a + nt * (wv + 1) / kWaves;
     const float ggs = DT == kNVFP4 ? L.gg[e] : 1.f;
     const float gus = DT == kNVFP4 ? L.gu[e] : 1.f;
+    // the group's slots in registers before any weight load is issued: a
+    // global load inside the stream would wait behind the prefetches
+    int slot[NVMAX];
+#pragma unroll
+    for (int v = 0; v < NVMAX; ++v)
+      slot[v] = __builtin_amdgcn_readfirstlane(U->slots[sidx + (v < nv ? v : 0)]);
     auto pre = [&]() {
       __syncthreads();  // the previous group's readers are done
       for (int v = 0; v < nv; ++v) {
-        const float* src = S.u + (size_t)(U->slots[sidx + v] / L.K) * L.H;
+        const float* src = S.u + (size_t)(slot[v] / L.K) * L.H;
         for (int c = threadIdx.x * 4; c < L.H; c += blockDim.x * 4)
           *reinterpret_cast<v4f*>(act_lds + v * L.H + c) = *reinterpret_cast<const v4f*>(src + c);
       }
@@ -209,7 +221,7 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
 #pragma unroll
               for (int v = 0; v < NV; ++v)
                 if (v < nv && ln == r * NV + v)
-                  S.act[(size_t)U->slots[sidx + v] * L.F + f0 + r] =
+                  S.act[(size_t)slot[v] * L.F + f0 + r] =
                       silu(acc[r][v] * ggs) * (acc[RW + r][v] * gus);
           },
           pre);
@@ -232,10 +244,14 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
     const int nt = b - a;
     const int w0 = a + nt * wv / kWaves, w1 = a + nt * (wv + 1) / kWaves;
     const float gds = DT == kNVFP4 ? L.gd[e] : 1.f;
+    int slot[NVMAX];  // in registers before the stream (see gateup_tn)
+#pragma unroll
+    for (int v = 0; v < NVMAX; ++v)
+      slot[v] = __builtin_amdgcn_readfirstlane(U->slots[sidx + (v < nv ? v : 0)]);
     auto pre = [&]() {
       __syncthreads();
       for (int v = 0; v < nv; ++v) {
-        const float* src = S.act + (size_t)U->slots[sidx + v] * L.F;
+        const float* src = S.act + (size_t)slot[v] * L.F;
         for (int c = threadIdx.x * 4; c < L.F; c += blockDim.x * 4)
           *reinterpret_cast<v4f*>(act_lds + v * L.F + c) = *reinterpret_cast<const v4f*>(src + c);
       }
@@ -262,7 +278,7 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
 #pragma unroll
               for (int v = 0; v < NV; ++v)
                 if (v < nv && ln == r * NV + v)
-                  y[(size_t)U->slots[sidx + v] * L.H + c0 + r] = acc[r][v] * gds;
+                  y[(size_t)slot[v] * L.H + c0 + r] = acc[r][v] * gds;
           },
           pre);
     });
