@@ -63,8 +63,11 @@ __device__ __forceinline__ unsigned pack_bf16_exact(float a, float b) {
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 // One 16-B chunk of cache-format data -> its EPC values as bf16, two per
-// word (exact).
+// word (exact: every e4m3 value is a bf16 value; the convert's scale of 1
+// leaves the values unchanged).
 template <int KDT>
 __device__ __forceinline__ void chunk_to_bf16(const v4u& w, unsigned* o) {
   if constexpr (KDT == kBF16) {
@@ -73,18 +76,30 @@ __device__ __forceinline__ void chunk_to_bf16(const v4u& w, unsigned* o) {
     const unsigned ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float f[4];
-      e4m3x4(ws[i], f);
-      o[2 * i] = pack_bf16_exact(f[0], f[1]);
-      o[2 * i + 1] = pack_bf16_exact(f[2], f[3]);
+      o[2 * i] = __builtin_bit_cast(unsigned,
+                                    __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ws[i], 1.0f, false));
+      o[2 * i + 1] = __builtin_bit_cast(unsigned,
+                                        __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ws[i], 1.0f, true));
     }
   }
+}
+
+// Two floats -> two bf16 (round to nearest even), packed a | b << 16.
+__device__ __forceinline__ unsigned cvt_pk_bf16(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f2){a, b}, bf16x2));
 }
 
 // x = hi + lo (+ a residual of at most 2^-16 |x|), both bf16 bits.
 __device__ __forceinline__ void split_bf16(float x, unsigned& hi, unsigned& lo) {
   hi = f2bf16(x);
   lo = f2bf16(x - bf16_lo(hi));
+}
+
+// The same for a pair, packed: hi = (hi_a | hi_b << 16), lo likewise.
+__device__ __forceinline__ void split2_bf16(float a, float b, unsigned& hi, unsigned& lo) {
+  hi = cvt_pk_bf16(a, b);
+  lo = cvt_pk_bf16(a - bf16_lo(hi), b - bf16_hi(hi));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const v4u& v) { return __builtin_bit_cast(bf16x8, v); }
@@ -156,21 +171,30 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
     }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
-    const float rr = 1.0f / sqrtf(ss / (float)D + L.eps);
+    // scores come out in log2 units (times log2(e)), so the weights are
+    // exp2(s - c log2(e)) = exp(s - c) up to rounding
+    const float rr = 1.0f / sqrtf(ss / (float)D + L.eps) * L.qscale * 1.44269504088896341f;
 #pragma unroll
     for (int ks = 0; ks < DS; ++ks) {
-      unsigned h[8], l[8];
+      unsigned h[4], l[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 8; e += 2) {
         const int d = 32 * ks + 8 * (ln >> 4) + e;
-        split_bf16(qf[ks][e] * rr * L.q_norm[d] * L.qscale, h[e], l[e]);
+        split2_bf16(qf[ks][e] * rr * L.q_norm[d], qf[ks][e + 1] * rr * L.q_norm[d + 1], h[e / 2],
+                    l[e / 2]);
       }
-      qh[ks] = as_bf16x8(v4u{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16,
-                             h[6] | h[7] << 16});
-      ql[ks] = as_bf16x8(v4u{l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16,
-                             l[6] | l[7] << 16});
+      qh[ks] = as_bf16x8(v4u{h[0], h[1], h[2], h[3]});
+      ql[ks] = as_bf16x8(v4u{l[0], l[1], l[2], l[3]});
     }
   }
+  // tiles inside every live row's window of this wave need no mask
+  int lo_all = live ? w_lo : 0, hi_all = live ? w_hi : 0x7fffffff;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    lo_all = max(lo_all, __shfl_xor(lo_all, o));
+    hi_all = min(hi_all, __shfl_xor(hi_all, o));
+  }
+  const float shift2 = L.shift * 1.44269504088896341f;
   // 1/rms of the step's new keys that fall in this chunk
   const int tn0 = p0 - Lb > 0 ? p0 - Lb : 0;
   const int tn1 = p1 - Lb < S.Tr ? p1 - Lb : S.Tr;
@@ -257,9 +281,10 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
         for (int h = 0; h < 2; ++h) chunk_to_bf16<KDT>(vr[u][h], o[h]);
 #pragma unroll
         for (int e = 0; e < EPC; ++e) {
-          const unsigned a = (e & 1) ? o[0][e >> 1] >> 16 : o[0][e >> 1] & 0xffffu;
-          const unsigned bb = (e & 1) ? o[1][e >> 1] & 0xffff0000u : o[1][e >> 1] << 16;
-          *reinterpret_cast<unsigned*>(vt + (cc * EPC + e) * VTS + 4 * pp) = a | bb;
+          // element e of positions 2pp (low half) and 2pp + 1 (high half)
+          const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          *reinterpret_cast<unsigned*>(vt + (cc * EPC + e) * VTS + 4 * pp) =
+              __builtin_amdgcn_perm(o[1][e >> 1], o[0][e >> 1], sel);
         }
       }
     }
@@ -308,24 +333,24 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
       }
     }
     // weights: lane holds row m, positions 16 pt + 4 (ln >> 4) + i
+    const bool open = pb >= lo_all && pb + 63 <= hi_all && pb + 64 <= p1;
     unsigned wh[NKS][4], wlo[NKS][4];
 #pragma unroll
     for (int pq = 0; pq < NPT; ++pq) {
       const int pt = ph * NPT + pq;
-      unsigned hh[4], ll[4];
+      float e[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int pos = pb + 16 * pt + 4 * (ln >> 4) + i;
-        const bool ok = pos >= w_lo && pos <= w_hi && pos < p1;
-        const float e = ok ? __expf(sacc[pq][i] - L.shift) : 0.f;
-        lsum += e;
-        split_bf16(e, hh[i], ll[i]);
+        e[i] = __builtin_amdgcn_exp2f(sacc[pq][i] - shift2);
+        if (!open) {
+          const int pos = pb + 16 * pt + 4 * (ln >> 4) + i;
+          e[i] = (pos >= w_lo && pos <= w_hi && pos < p1) ? e[i] : 0.f;
+        }
+        lsum += e[i];
       }
       // k index 8 (ln >> 4) + 4 (pt & 1) + i of k step pt / 2
-      wh[pq >> 1][2 * (pt & 1)] = hh[0] | hh[1] << 16;
-      wh[pq >> 1][2 * (pt & 1) + 1] = hh[2] | hh[3] << 16;
-      wlo[pq >> 1][2 * (pt & 1)] = ll[0] | ll[1] << 16;
-      wlo[pq >> 1][2 * (pt & 1) + 1] = ll[2] | ll[3] << 16;
+      split2_bf16(e[0], e[1], wh[pq >> 1][2 * (pt & 1)], wlo[pq >> 1][2 * (pt & 1)]);
+      split2_bf16(e[2], e[3], wh[pq >> 1][2 * (pt & 1) + 1], wlo[pq >> 1][2 * (pt & 1) + 1]);
     }
     // O^T[d][m] += V^T[d][pos] e[pos][m]; the A operand's k numbering matches
     // the weights': positions 32 ks + 4 (ln >> 4) + {0..3} and + 16 + {0..3}
