@@ -74,19 +74,22 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
         }
 #pragma unroll
         for (int sub = 0; sub < W::NSUB; ++sub) {
-          float fw[R][W::SUB];
+          // the inputs of this sub-block first, then one weight row at a
+          // time: only one row's decoded values are live at once
+          float a[NV][W::SUB];
 #pragma unroll
-          for (int r = 0; r < R; ++r) decode_sub<DT>(w[u][r], sub, fw[r]);
+          for (int v = 0; v < NV; ++v)
+            if (v < nv) load_act(actfn(v) + ch * W::EPL + sub * W::SUB, a[v], W::SUB);
 #pragma unroll
-          for (int v = 0; v < NV; ++v) {
-            if (v < nv) {
-              float a[W::SUB];
-              load_act(actfn(v) + ch * W::EPL + sub * W::SUB, a, W::SUB);
+          for (int r = 0; r < R; ++r) {
+            float fw[W::SUB];
+            decode_sub<DT>(w[u][r], sub, fw);
 #pragma unroll
-              for (int r = 0; r < R; ++r) {
+            for (int v = 0; v < NV; ++v) {
+              if (v < nv) {
                 float d = 0.f;
 #pragma unroll
-                for (int e = 0; e < W::SUB; ++e) d = fmaf(fw[r][e], a[e], d);
+                for (int e = 0; e < W::SUB; ++e) d = fmaf(fw[e], a[v][e], d);
                 if constexpr (DT == kNVFP4)
                   acc[r][v] = fmaf((sub >> 1) ? sc[r].y : sc[r].x, d, acc[r][v]);
                 else
