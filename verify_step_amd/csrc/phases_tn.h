@@ -17,8 +17,43 @@
 
 namespace msk {
 
-// Like stream_t1, for nv <= NV input vectors in LDS: acc[r][v] =
-// sum_c W_r[c] * in_v[c] (NVFP4: with block scales, matrix scale left out).
+// Input vectors staged in LDS are stored in 16-B granules (4 floats) in a
+// rotated order: a lane reads its chunk of EPL consecutive inputs, so in a
+// plain layout the 16 lanes of one LDS read pass would sit EPL * 4 bytes
+// apart and share a few bank groups (NVFP4: two of sixteen).  Rotating each
+// chunk's granules by the chunk index (NVFP4: by half of it) gives the 16
+// lanes of a pass 16 distinct bank groups.  Granule G of a vector is stored
+// at tn_gran<DT>(G), relative to the vector's own start.
+template <int DT>
+__device__ __forceinline__ int tn_gran(int G) {
+  if constexpr (DT == kNVFP4) return (G & ~7) | ((G + (G >> 4)) & 7);
+  else if constexpr (DT == kBF16) return (G & ~1) | ((G ^ (G >> 4)) & 1);
+  else return G;
+}
+
+// n floats from global memory into LDS in that order (all threads).
+template <int DT>
+__device__ __forceinline__ void tn_stage(const float* src, int n, float* dst) {
+  for (int c = threadIdx.x * 4; c < n; c += blockDim.x * 4)
+    *reinterpret_cast<v4f*>(dst + tn_gran<DT>(c >> 2) * 4) = *reinterpret_cast<const v4f*>(src + c);
+}
+
+// The SUB inputs of sub-block `sub` of chunk `ch` of a staged vector.
+template <int DT>
+__device__ __forceinline__ void tn_load(const float* v, int ch, int sub, float* a) {
+  using W = WT<DT>;
+  const int G = (ch * W::EPL + sub * W::SUB) >> 2;
+  const v4f x = *reinterpret_cast<const v4f*>(v + tn_gran<DT>(G) * 4);
+  a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
+  if constexpr (W::SUB == 8) {
+    const v4f y = *reinterpret_cast<const v4f*>(v + tn_gran<DT>(G + 1) * 4);
+    a[4] = y.x; a[5] = y.y; a[6] = y.z; a[7] = y.w;
+  }
+}
+
+// Like stream_t1, for nv <= NV input vectors in LDS (stored by tn_stage):
+// acc[r][v] = sum_c W_r[c] * in_v[c] (NVFP4: with block scales, matrix scale
+// left out).
 template <int DT, int R, int U, int NV, class ActFn, class RowFn, class OutFn, class PreFn>
 __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& actfn,
                                           RowFn&& rowfn, OutFn&& out, PreFn&& pre) {
@@ -79,7 +114,7 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
           float a[NV][W::SUB];
 #pragma unroll
           for (int v = 0; v < NV; ++v)
-            if (v < nv) load_act(actfn(v) + ch * W::EPL + sub * W::SUB, a[v], W::SUB);
+            if (v < nv) tn_load<DT>(actfn(v), ch, sub, a[v]);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             float fw[W::SUB];
@@ -194,11 +229,8 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
       slot[v] = __builtin_amdgcn_readfirstlane(U->slots[sidx + (v < nv ? v : 0)]);
     auto pre = [&]() {
       __syncthreads();  // the previous group's readers are done
-      for (int v = 0; v < nv; ++v) {
-        const float* src = S.u + (size_t)(slot[v] / L.K) * L.H;
-        for (int c = threadIdx.x * 4; c < L.H; c += blockDim.x * 4)
-          *reinterpret_cast<v4f*>(act_lds + v * L.H + c) = *reinterpret_cast<const v4f*>(src + c);
-      }
+      for (int v = 0; v < nv; ++v)
+        tn_stage<DT>(S.u + (size_t)(slot[v] / L.K) * L.H, L.H, act_lds + v * L.H);
       __syncthreads();
     };
     nv_dispatch<NVMAX>(nv, [&](auto nvc) {
@@ -253,11 +285,8 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
       slot[v] = __builtin_amdgcn_readfirstlane(U->slots[sidx + (v < nv ? v : 0)]);
     auto pre = [&]() {
       __syncthreads();
-      for (int v = 0; v < nv; ++v) {
-        const float* src = S.act + (size_t)slot[v] * L.F;
-        for (int c = threadIdx.x * 4; c < L.F; c += blockDim.x * 4)
-          *reinterpret_cast<v4f*>(act_lds + v * L.F + c) = *reinterpret_cast<const v4f*>(src + c);
-      }
+      for (int v = 0; v < nv; ++v)
+        tn_stage<DT>(S.act + (size_t)slot[v] * L.F, L.F, act_lds + v * L.F);
       __syncthreads();
     };
     nv_dispatch<NVMAX>(nv, [&](auto nvc) {
