@@ -14,7 +14,11 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// Wave index within the workgroup, marked wave-uniform so that values
+// derived from it (task and row indices) live in scalar registers and the
+// loads they address are scalar loads, which never queue behind the vector
+// loads of a streaming pipeline.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Wave-wide max / min through DPP row rotations (within rows of 16 lanes)
 // and four lane reads (across rows): no LDS round trips.  Every lane gets

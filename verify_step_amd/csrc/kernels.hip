@@ -161,19 +161,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_wo_t1(LayerArgs L, StepArgs S
 // Router logits, then top-k in the workgroup that finishes last.
 template <int DT>
 __global__ __launch_bounds__(kBlockThreads) void k_router_t1(LayerArgs L, StepArgs S,
-                                                             const float* h, int* topk_out) {
+                                                             const float* h) {
   const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
   router_t1<DT>(L, S, h, reinterpret_cast<float*>(msk_smem + o.act0),
                 reinterpret_cast<float*>(msk_smem + o.red),
                 reinterpret_cast<float*>(msk_smem + o.act1), blockIdx.x, gridDim.x);
-  if (last_workgroup(&S.sync[2], reinterpret_cast<int*>(msk_smem + o.tki))) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (wave_id() == 0) {
-      topk_row(S.logits, L.E, L.K, S.idx, S.wts);
-      if (topk_out != nullptr && lane_id() == 0)
-        for (int k = 0; k < L.K; ++k) topk_out[k] = S.idx[k];
-    }
-  }
 }
 
 template <int DT>
@@ -585,12 +577,15 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
     const int g = L.E < cu_count() ? L.E : cu_count();
     if (L.ddt == kBF16) {
       MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_router_t1<kBF16>), lds));
-      MSK_TRY(launch_x(kPhRouter, k_router_t1<kBF16>, g, lds, st, L, S, h, topk_out));
+      MSK_TRY(launch_x(kPhRouter, k_router_t1<kBF16>, g, lds, st, L, S, h));
     } else {
       MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_router_t1<kF32>), lds));
-      MSK_TRY(launch_x(kPhRouter, k_router_t1<kF32>, g, lds, st, L, S, h, topk_out));
+      MSK_TRY(launch_x(kPhRouter, k_router_t1<kF32>, g, lds, st, L, S, h));
     }
-    return hipSuccess;
+    // top-k in a kernel of its own: finding the last router workgroup in
+    // the router kernel costs every workgroup an agent-scope acquire and
+    // release, which here means L2 writeback and invalidate
+    return launch_x(kPhTopk, k_topk, 1, 0, st, L, S, topk_out);
   } else if (dense_on_mfma(L, S, L.E, L.H)) {
     MSK_TRY(launch_x(kPhPrep, k_prep_act, S.T, kWaves * sizeof(float), st, h, L.ffn_norm, S.T, L.H, L.eps, S.u, S.a3));
     MSK_TRY(launch_dense(S, L.wr, nullptr, nullptr, 0, 0, L.E, L.H, nullptr, S.logits, kPhRouter,
