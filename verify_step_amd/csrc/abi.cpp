@@ -76,7 +76,11 @@ AttnSplit plan_attention(const msk_layer_cfg& c, const msk_batch& b) {
     end = L + b.tokens_per_req;
     total += (long long)(end - base) * c.n_kv_heads * nrg;
   }
-  long long chunk = (total + kTargetItems - 1) / kTargetItems;
+  // matrix-core items: three full rounds of the 768 workgroups (three per CU
+  // on 256 CUs) that its e4m3 head_dim-128 form keeps resident, so the last
+  // round is not left part-empty
+  const long long target = mfma ? 3 * 768 : kTargetItems;
+  long long chunk = (total + target - 1) / target;
   chunk = (chunk + 63) / 64 * 64;
   if (chunk < 64) chunk = 64;
   if (chunk > (1 << 20)) chunk = 1 << 20;
