@@ -98,13 +98,17 @@ struct Layout {
   size_t sync, qkv, part, attn_o, h, u, logits, idx, wts, act, xa, xb, uni, ybuf, a3, dpart, total;
 };
 
-Layout layout(const msk_layer_cfg* cfg, int n_layers, const msk_batch& b) {
+// with_attention = false: the router and expert entry points, which take a
+// flat token count and use no attention partials (nor more workspace than a
+// layer step of the same tokens).
+Layout layout(const msk_layer_cfg* cfg, int n_layers, const msk_batch& b,
+              bool with_attention = true) {
   const msk_layer_cfg& c = cfg[0];
   const size_t T = (size_t)b.n_req * b.tokens_per_req;
   const size_t H = c.hidden, D = c.head_dim;
   const size_t NR = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * D;
   size_t max_rows = 0;
-  for (int l = 0; l < n_layers; ++l) {
+  for (int l = 0; l < n_layers && with_attention; ++l) {
     const AttnSplit a = plan_attention(cfg[l], b);
     const size_t rows_total = (size_t)a.n_items * a.rows;
     if (rows_total > max_rows) max_rows = rows_total;
@@ -420,7 +424,7 @@ msk_status msk_moe_route(const msk_layer_cfg* cfg, const msk_layer_weights* w, i
     return fail(MSK_ERR_INVALID_ARG, "n_tokens %d outside [1, %d]", n_tokens, MSK_MAX_TOKENS);
   if (!h || !u || !topk_idx || !topk_w) return fail(MSK_ERR_INVALID_ARG, "an output or h is null");
   FlatBatch fb(n_tokens);
-  const Layout lay = layout(cfg, 1, fb.b);
+  const Layout lay = layout(cfg, 1, fb.b, false);
   if (!ws || ws_bytes < lay.total)
     return fail(MSK_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, lay.total);
   msk::LayerArgs L = make_layer(*cfg, w, nullptr, nullptr);
@@ -443,7 +447,7 @@ msk_status msk_expert_ffn(const msk_layer_cfg* cfg, const msk_layer_weights* w, 
   if (!u || !topk_idx || !topk_w || !h || !out)
     return fail(MSK_ERR_INVALID_ARG, "an input or output pointer is null");
   FlatBatch fb(n_tokens);
-  const Layout lay = layout(cfg, 1, fb.b);
+  const Layout lay = layout(cfg, 1, fb.b, false);
   if (!ws || ws_bytes < lay.total)
     return fail(MSK_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, lay.total);
   msk::LayerArgs L = make_layer(*cfg, w, nullptr, nullptr);
