@@ -195,12 +195,19 @@ KERNEL_NAMES = {"qkv": "k_qkv", "attn": "k_attn", "combine": "k_combine", "wo": 
 ONE_TOKEN_KERNELS = ("qkv", "wo", "router", "gateup", "down")
 
 
-def kernel_name(phase, T):
+def kernel_name(phase, spec, T, Tr):
+    """The kernel a phase runs as, mirroring the library's choice of path."""
     base = KERNEL_NAMES[phase]
     if T == 1 and phase in ONE_TOKEN_KERNELS:
         return base + "_t1"
     if T > 1 and phase in ("gateup", "down"):
         return base + "_tn"
+    if T > 1 and phase in ("qkv", "wo", "router") and spec["dense_dtype"] == "bf16":
+        return "k_dense_mfma"
+    if phase == "attn":
+        G = spec["n_q_heads"] // spec["n_kv_heads"]
+        if spec["kv_dtype"] in ("bf16", "e4m3") and G * Tr > 8:
+            return "k_attn_mfma"
     return base
 
 
@@ -308,7 +315,7 @@ def main():
     avg_us = d["ms"] * 1e3 / d["launches"]
     bytes_launch = d["bytes"] / d["launches"] if dom != "step" else nbytes
     kgbs = bytes_launch / (avg_us * 1e-6) / 1e9
-    kname = kernel_name(dom, p.T)
+    kname = kernel_name(dom, p.specs[0], p.T, p.tokens_per_req)
     traffic = stored_traffic(kname, args.workload)
 
     out = {
