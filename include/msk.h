@@ -183,8 +183,9 @@ msk_status msk_expert_ffn(const msk_layer_cfg *cfg, const msk_layer_weights *w,
                           const float *topk_w, const float *h, float *out, void *ws,
                           size_t ws_bytes, void *stream);
 
-/* A whole decode/verify step through n_layers (1..MSK_MAX_STACK) layers as one
- * persistent kernel: layer l's output is layer l+1's input.  cfg, w and kv are
+/* A whole decode/verify step through n_layers (1..MSK_MAX_STACK) layers,
+ * enqueued as the per-phase kernels of every layer in order on one stream:
+ * layer l's output is layer l+1's input.  cfg, w and kv are
  * arrays of n_layers entries (shapes must agree; window and dtypes may differ).
  *   x         [T][H] fp32 in/out: the step's input, replaced by its output
  *   layer_out [n_layers][T][H] out, nullable: each layer's output
@@ -195,7 +196,10 @@ msk_status msk_layer_step(const msk_layer_cfg *cfg, const msk_layer_weights *w,
                           float *x, float *layer_out, int32_t *topk_idx, int32_t *win,
                           void *ws, size_t ws_bytes, void *stream);
 
-/* Profiling aid: msk_layer_step (no optional outputs) that also records, for
+/* Profiling aid: msk_layer_step (no optional outputs) run as one persistent
+ * cooperative kernel with grid barriers between dependent phases, where the
+ * stack has one (one token, all fp32); msk_layer_step itself always runs
+ * per-phase kernels, which measure faster on this part.  It records, for
  * every workgroup of the persistent kernel, the GPU's constant 100 MHz
  * real-time counter at the start and after each phase:
  *   stamps  DEVICE int64 [workgroups][32], caller-owned; slot 0 = start, then

@@ -489,7 +489,12 @@ static msk_status layer_step_impl(const msk_layer_cfg* cfg, const msk_layer_weig
   S.topk_out = topk_idx;
   S.win_out = win;
   S.stamps = reinterpret_cast<long long*>(stamps);
-  return device_status(msk::launch_step_fused(Ls, S, static_cast<hipStream_t>(stream)),
+  // Per-phase kernels measure faster than the persistent kernel on this part
+  // (its grid barriers cost more than the kernel boundaries they replace),
+  // so only the timeline call, whose in-kernel stamps need it, runs the
+  // persistent kernel.
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return device_status(stamps ? msk::launch_step_fused(Ls, S, st) : msk::launch_step_unfused(Ls, S, st),
                        "layer-step launch");
 }
 
