@@ -44,10 +44,15 @@ struct MfmaGeom {
   static constexpr int NT = NW * 64;       // threads per workgroup
   static constexpr int NKC = 64 * CPR;     // K chunks per tile
   static constexpr int KPT = (NKC + NT - 1) / NT;
-  static constexpr int NVP = 32 * CPR;     // V (position pair, chunk) tasks per tile
+  static constexpr int NVP = 32 * CPR;     // V (position pair pp = q % 32, chunk q / 32) tasks
   static constexpr int VPT = (NVP + NT - 1) / NT;
   static constexpr int KBS = D * 2 + 16;   // bf16 K tile row stride, bytes
-  static constexpr int VTS = 64 * 2 + 8;   // bf16 V^T tile row stride, bytes
+  // bf16 V^T tile row stride, bytes: a V^T store instruction writes one row
+  // (32 position pairs, 128 B) per half-wave, the halves EPC rows apart; the
+  // stride puts them on opposite halves of the 64 banks (e4m3: 16 rows x 136
+  // B; bf16: 8 rows x 144 B), and keeps the 16 rows of an operand read on
+  // distinct banks
+  static constexpr int VTS = KDT == kE4M3 ? 64 * 2 + 8 : 64 * 2 + 16;
   static constexpr int DS = D / 32;        // k steps of the score product
   static constexpr int NDT = D / 16;       // d tiles of the output product
   static constexpr int LDS_KB = 64 * KBS;
@@ -223,13 +228,13 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
       const int q = tid + u * NT;
-      const int pos = pb + 2 * (q / CPR);
+      const int pos = pb + 2 * (q & 31);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         vr[u][h] = v4u{0u, 0u, 0u, 0u};
         if (q < Gm::NVP && pos + h >= vlo && pos + h < vhi)
           vr[u][h] = __builtin_nontemporal_load(
-              reinterpret_cast<const v4u*>(vc + (size_t)(pos + h) * RB + (q % CPR) * 16));
+              reinterpret_cast<const v4u*>(vc + (size_t)(pos + h) * RB + (q >> 5) * 16));
       }
     }
   };
@@ -275,7 +280,7 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
     for (int u = 0; u < VPT; ++u) {
       const int q = tid + u * NT;
       if (q < Gm::NVP) {
-        const int pp = q / CPR, cc = q % CPR;
+        const int pp = q & 31, cc = q >> 5;
         unsigned o[2][EPC / 2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) chunk_to_bf16<KDT>(vr[u][h], o[h]);
