@@ -19,6 +19,11 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // loads they address are scalar loads, which never queue behind the vector
 // loads of a streaming pipeline.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+// A wave-uniform float moved to a scalar register where it is read: the load
+// that produced it is waited for here, not inside a later streaming loop.
+__device__ __forceinline__ float uniform_f(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
 
 // Wave-wide max / min through DPP row rotations (within rows of 16 lanes)
 // and four lane reads (across rows): no LDS round trips.  Every lane gets
@@ -288,6 +293,11 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
 
+  // Loads are issued on every path (a chunk past the row end is clamped to
+  // the last one and compute adds nothing for it), nothing touches a loaded
+  // value before compute needs it, and compute has no branch on the chunk:
+  // otherwise the compiler's waits for the loads in flight become
+  // conservative and drain the second buffer at every step.
   auto issue = [&](v4u(&w)[U][R], unsigned(&s)[U][R], int f) {
     const int k = f / NI, i = f - (f / NI) * NI;
     const uint8_t* wr[R];
@@ -295,19 +305,17 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
     rowfn(k, wr, sr);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      // a scalar row base plus one 32-bit lane offset shared by the rows
       const int ch = (i * U + u) * 64 + ln;
+      const unsigned cc = (unsigned)(ch < nch ? ch : nch - 1);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        if (ch < nch) {
-          w[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wr[r]) + ch);
-          if constexpr (DT == kNVFP4)
-            s[u][r] = *reinterpret_cast<const unsigned short*>(sr[r] + 2 * ch);
-          else
-            s[u][r] = 0u;
-        } else {
-          w[u][r] = v4u{0u, 0u, 0u, 0u};
+        w[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wr[r] + cc * 16u));
+        // the lane's two scale bytes inside an aligned dword
+        if constexpr (DT == kNVFP4)
+          s[u][r] = *reinterpret_cast<const unsigned*>(sr[r] + (cc * 2u & ~3u));
+        else
           s[u][r] = 0u;
-        }
       }
     }
   };
@@ -317,28 +325,32 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ch = (i * U + u) * 64 + ln;
-      if (ch < nch) {
-        v2f sc[R];
-        if constexpr (DT == kNVFP4) {
+      const bool in = ch < nch;
+      const int cl = in ? ch : nch - 1;
+      v2f sc[R];
+      if constexpr (DT == kNVFP4) {
 #pragma unroll
-          for (int r = 0; r < R; ++r) sc[r] = __builtin_amdgcn_cvt_pk_f32_fp8(s[u][r], false);
+        for (int r = 0; r < R; ++r) {
+          sc[r] = __builtin_amdgcn_cvt_pk_f32_fp8(s[u][r] >> ((cl & 1) * 16), false);
+          sc[r].x = in ? sc[r].x : 0.f;
+          sc[r].y = in ? sc[r].y : 0.f;
         }
+      }
 #pragma unroll
-        for (int sub = 0; sub < W::NSUB; ++sub) {
-          float a[W::SUB];
-          load_act(act + ch * W::EPL + sub * W::SUB, a, W::SUB);
+      for (int sub = 0; sub < W::NSUB; ++sub) {
+        float a[W::SUB];
+        load_act(act + cl * W::EPL + sub * W::SUB, a, W::SUB);
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            float fw[W::SUB];
-            decode_sub<DT>(w[u][r], sub, fw);
-            float d = 0.f;
+        for (int r = 0; r < R; ++r) {
+          float fw[W::SUB];
+          decode_sub<DT>(w[u][r], sub, fw);
+          float d = 0.f;
 #pragma unroll
-            for (int e = 0; e < W::SUB; ++e) d = fmaf(fw[e], a[e], d);
-            if constexpr (DT == kNVFP4)
-              acc[r] = fmaf((sub >> 1) ? sc[r].y : sc[r].x, d, acc[r]);
-            else
-              acc[r] += d;
-          }
+          for (int e = 0; e < W::SUB; ++e) d = fmaf(fw[e], a[e], d);
+          if constexpr (DT == kNVFP4)
+            acc[r] = fmaf((sub >> 1) ? sc[r].y : sc[r].x, d, acc[r]);
+          else  // one sub-block per chunk
+            acc[r] += in ? d : 0.f;
         }
       }
     }
@@ -352,17 +364,32 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
   };
   // the first two buffers go out before the prologue (typically staging the
   // input vector into LDS, which every wave of the workgroup joins), so its
-  // latency overlaps the first weight fetches
-  if (total > 0) issue(A, sA, 0);
-  if (total > 1) issue(B, sB, 1);
+  // latency overlaps the first weight fetches; all of A's loads precede all
+  // of B's, as inside the loop (a single-step task list loads its one step
+  // twice).  The loop issues both refills on every iteration and the last
+  // steps are peeled off, so the loop holds no conditional load.
+  const int last = total - 1;
+  if (total > 0) {
+    issue(A, sA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(B, sB, 1 < last ? 1 : last);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   pre();
-  for (int f = 0; f < total; f += 2) {
+  int f = 0;
+  // steady state: both refills are real steps
+  for (; f + 3 < total; f += 2) {
+    compute(A, sA, f);
+    issue(A, sA, f + 2);
+    compute(B, sB, f + 1);
+    issue(B, sB, f + 3);
+  }
+  // the last one to three steps: A holds step f, B step f + 1
+  if (f < total) {
     compute(A, sA, f);
     if (f + 2 < total) issue(A, sA, f + 2);
-    if (f + 1 < total) {
-      compute(B, sB, f + 1);
-      if (f + 3 < total) issue(B, sB, f + 3);
-    }
+    if (f + 1 < total) compute(B, sB, f + 1);
+    if (f + 2 < total) compute(A, sA, f + 2);
   }
 }
 

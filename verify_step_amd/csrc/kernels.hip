@@ -63,8 +63,13 @@ __global__ __launch_bounds__(kBlockThreads) void k_gateup_tn(LayerArgs L, StepAr
   gateup_tn<DT, NVMAX>(L, S, S.uni, reinterpret_cast<float*>(msk_smem));
 }
 
+// bf16 down streams four slot vectors: held to four waves per SIMD (its
+// registers otherwise come out one over the limit for four)
+template <int DT> struct DownTnWaves { static constexpr int N = DT == kBF16 ? 4 : 1; };
+
 template <int DT, int NVMAX>
-__global__ __launch_bounds__(kBlockThreads) void k_down_tn(LayerArgs L, StepArgs S) {
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(DownTnWaves<DT>::N)))
+void k_down_tn(LayerArgs L, StepArgs S) {
   down_tn<DT, NVMAX>(L, S, S.uni, reinterpret_cast<float*>(msk_smem), S.ybuf);
 }
 

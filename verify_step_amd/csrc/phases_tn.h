@@ -77,22 +77,24 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
     rowfn(k, wr, sr);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      // every lane loads (a clamped chunk past the row end, zeroed after),
-      // so the number of loads in flight is the same on every path and the
-      // waits before each compute step count exactly to that step's loads
+      // every lane loads (a clamped chunk past the row end, which compute
+      // skips), so the number of loads in flight is the same on every path
+      // and the waits before each compute step count exactly to that step's
+      // loads.  Nothing may touch the loaded values here: a select on them
+      // would wait for the refill right after issuing it.
+      // addresses as a scalar row base plus one 32-bit lane offset shared by
+      // the rows (no per-row 64-bit address registers to keep alive)
       const int ch = (i * U + u) * 64 + ln;
-      const bool in = ch < nch;
-      const int cc = in ? ch : nch - 1;
+      const unsigned cc = (unsigned)(ch < nch ? ch : nch - 1);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wr[r]) + cc);
-        w[u][r] = in ? x : v4u{0u, 0u, 0u, 0u};
-        if constexpr (DT == kNVFP4) {
-          const unsigned y = *reinterpret_cast<const unsigned short*>(sr[r] + 2 * cc);
-          s[u][r] = in ? y : 0u;
-        } else {
+        w[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wr[r] + cc * 16u));
+        // the lane's two scale bytes as part of an aligned dword (a 16-bit
+        // load here made the compiler wait for the refills at the next step)
+        if constexpr (DT == kNVFP4)
+          s[u][r] = *reinterpret_cast<const unsigned*>(sr[r] + (cc * 2u & ~3u));
+        else
           s[u][r] = 0u;
-        }
       }
     }
   };
@@ -100,36 +102,43 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
     const int k = f / NI, i = f - (f / NI) * NI;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      // no branch on the chunk: a lane past the row end computes on its
+      // clamped chunk and adds nothing (a branch here would make the
+      // compiler's waits for the loads in flight conservative)
       const int ch = (i * U + u) * 64 + ln;
-      if (ch < nch) {
-        v2f sc[R];
-        if constexpr (DT == kNVFP4) {
+      const bool in = ch < nch;
+      const int cl = in ? ch : nch - 1;
+      v2f sc[R];
+      if constexpr (DT == kNVFP4) {
 #pragma unroll
-          for (int r = 0; r < R; ++r) sc[r] = __builtin_amdgcn_cvt_pk_f32_fp8(s[u][r], false);
+        for (int r = 0; r < R; ++r) {
+          sc[r] = __builtin_amdgcn_cvt_pk_f32_fp8(s[u][r] >> ((cl & 1) * 16), false);
+          sc[r].x = in ? sc[r].x : 0.f;
+          sc[r].y = in ? sc[r].y : 0.f;
         }
+      }
 #pragma unroll
-        for (int sub = 0; sub < W::NSUB; ++sub) {
-          // the inputs of this sub-block first, then one weight row at a
-          // time: only one row's decoded values are live at once
-          float a[NV][W::SUB];
+      for (int sub = 0; sub < W::NSUB; ++sub) {
+        // the inputs of this sub-block first, then one weight row at a
+        // time: only one row's decoded values are live at once
+        float a[NV][W::SUB];
 #pragma unroll
-          for (int v = 0; v < NV; ++v)
-            if (v < nv) tn_load<DT>(actfn(v), ch, sub, a[v]);
+        for (int v = 0; v < NV; ++v)
+          if (v < nv) tn_load<DT>(actfn(v), cl, sub, a[v]);
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            float fw[W::SUB];
-            decode_sub<DT>(w[u][r], sub, fw);
+        for (int r = 0; r < R; ++r) {
+          float fw[W::SUB];
+          decode_sub<DT>(w[u][r], sub, fw);
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-              if (v < nv) {
-                float d = 0.f;
+          for (int v = 0; v < NV; ++v) {
+            if (v < nv) {
+              float d = 0.f;
 #pragma unroll
-                for (int e = 0; e < W::SUB; ++e) d = fmaf(fw[e], a[v][e], d);
-                if constexpr (DT == kNVFP4)
-                  acc[r][v] = fmaf((sub >> 1) ? sc[r].y : sc[r].x, d, acc[r][v]);
-                else
-                  acc[r][v] += d;
-              }
+              for (int e = 0; e < W::SUB; ++e) d = fmaf(fw[e], a[v][e], d);
+              if constexpr (DT == kNVFP4)
+                acc[r][v] = fmaf((sub >> 1) ? sc[r].y : sc[r].x, d, acc[r][v]);
+              else  // one sub-block per chunk
+                acc[r][v] += in ? d : 0.f;
             }
           }
         }
@@ -148,11 +157,16 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
     }
   };
   // the refills are issued on every iteration (past the end they repeat the
-  // last step's addresses, unused), for the same reason
+  // last step's addresses, unused), so the loop holds no conditional load;
+  // peeling the last steps off instead costs registers (and occupancy) here
   const int last = total - 1;
   if (total > 0) {
+    // all of A's loads ahead of all of B's, as inside the loop: the
+    // compiler's waits at the loop head hold for the entry path too
     issue(A, sA, 0);
+    __builtin_amdgcn_sched_barrier(0);
     issue(B, sB, 1 < last ? 1 : last);
+    __builtin_amdgcn_sched_barrier(0);
   }
   pre();
   for (int f = 0; f < total; f += 2) {
@@ -219,8 +233,9 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
     const int e = U->list[ui];
     const int nt = b - a;
     const int w0 = a + nt * wv / kWaves, w1 = a + nt * (wv + 1) / kWaves;
-    const float ggs = DT == kNVFP4 ? L.gg[e] : 1.f;
-    const float gus = DT == kNVFP4 ? L.gu[e] : 1.f;
+    // matrix scales in scalar registers before the stream (see slot below)
+    const float ggs = DT == kNVFP4 ? uniform_f(L.gg[e]) : 1.f;
+    const float gus = DT == kNVFP4 ? uniform_f(L.gu[e]) : 1.f;
     // the group's slots in registers before any weight load is issued: a
     // global load inside the stream would wait behind the prefetches
     int slot[NVMAX];
@@ -278,7 +293,7 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
     const int e = U->list[ui];
     const int nt = b - a;
     const int w0 = a + nt * wv / kWaves, w1 = a + nt * (wv + 1) / kWaves;
-    const float gds = DT == kNVFP4 ? L.gd[e] : 1.f;
+    const float gds = DT == kNVFP4 ? uniform_f(L.gd[e]) : 1.f;
     int slot[NVMAX];  // in registers before the stream (see gateup_tn)
 #pragma unroll
     for (int v = 0; v < NVMAX; ++v)
