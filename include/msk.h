@@ -21,6 +21,8 @@
  * - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
  *   allocates no device memory and keeps no state between calls; scratch space
  *   comes from the caller's workspace (see msk_workspace_size).
+ * - Weight matrices and KV caches are 16-byte aligned, NVFP4 scale arrays
+ *   4-byte aligned; a misaligned pointer is an argument error.
  * - Row-major, innermost dimension last.  T = n_req * tokens_per_req tokens,
  *   request-major: token t of request b is row b * tokens_per_req + t and sits
  *   at cache position p = kv_len[b] + t.

@@ -119,3 +119,33 @@ def test_entry_points_validate_before_enqueue():
                             ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.c_void_p(8),
                             ctypes.c_void_p(8), ctypes.c_void_p(8), 1 << 30, None) == 1
     assert "scales" in msk.last_error()
+
+
+def test_misaligned_pointers_are_argument_errors():
+    # 16-byte weights and caches, 4-byte NVFP4 scale arrays; checked on the
+    # host before anything is enqueued
+    L = msk.lib()
+    cfg = msk.make_cfg(_spec())
+    b = msk.make_batch([10], 1)
+    ptrs = [ctypes.c_void_p(256)] * 18
+    ptrs[4] = ctypes.c_void_p(264)                          # wq 8-byte aligned
+    w = msk.LayerWeights(*ptrs)
+    kv = msk.KV(ctypes.c_void_p(256), ctypes.c_void_p(256), 100)
+    assert L.msk_attn_step(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), ctypes.byref(b),
+                           ctypes.c_void_p(32), ctypes.c_void_p(64), None, None,
+                           ctypes.c_void_p(128), 1 << 30, None) == 1
+    assert "aligned" in msk.last_error()
+    w = msk.LayerWeights(*([ctypes.c_void_p(256)] * 18))
+    kv = msk.KV(ctypes.c_void_p(260), ctypes.c_void_p(256), 100)
+    assert L.msk_attn_step(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), ctypes.byref(b),
+                           ctypes.c_void_p(32), ctypes.c_void_p(64), None, None,
+                           ctypes.c_void_p(128), 1 << 30, None) == 1
+    assert "aligned" in msk.last_error()
+    c4 = msk.make_cfg(_spec(expert_dtype="nvfp4"))
+    ptrs = [ctypes.c_void_p(256)] * 18
+    ptrs[12] = ctypes.c_void_p(258)                         # s_gate 2-byte aligned
+    w4 = msk.LayerWeights(*ptrs)
+    assert L.msk_expert_ffn(ctypes.byref(c4), ctypes.byref(w4), 1, ctypes.c_void_p(8),
+                            ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.c_void_p(8),
+                            ctypes.c_void_p(8), ctypes.c_void_p(8), 1 << 30, None) == 1
+    assert "aligned" in msk.last_error()

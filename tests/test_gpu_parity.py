@@ -43,6 +43,12 @@ CASES = {
     # 12 rows per kv head over a bf16 cache of head_dim 128 (two-wave items)
     "verify-tr2-bf16kv": ("verify-bf16-128k", dict(dims=_SMALL, kv="bf16", kv_len=[200, 129],
                                                    tokens_per_req=2)),
+    # NVFP4 rows whose scale rows start on 2 mod 4 bytes (hidden 480, ffn 96:
+    # 30- and 6-byte scale rows) and rows that end inside a 64-chunk step
+    "decode-odd-nvfp4": ("decode-bf16", dict(dims=dict(_SMALL, hidden=480, ffn_dim=96),
+                                              expert="nvfp4", kv_len=[300], windows=[128])),
+    "stack-odd-nvfp4": ("stack4-nvfp4", dict(dims=dict(_SMALL, hidden=480, ffn_dim=96),
+                                             kv_len=[300], windows=[128, 0])),
 }
 
 

@@ -219,8 +219,12 @@ msk_status check_batch(const msk_batch* b) {
   return ok();
 }
 
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
+
 msk_status check_kv(const msk_kv* kv, const msk_batch* b, int l) {
   if (!kv || !kv->k || !kv->v) return fail(MSK_ERR_INVALID_ARG, "layer %d: kv cache pointer is null", l);
+  if (!aligned(kv->k, 16) || !aligned(kv->v, 16))
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: kv cache is not 16-byte aligned", l);
   for (int r = 0; r < b->n_req; ++r)
     if ((long long)b->kv_len_host[r] + b->tokens_per_req > kv->cap)
       return fail(MSK_ERR_INVALID_ARG, "layer %d: kv_len[%d] + tokens_per_req = %lld > cap %lld", l, r,
@@ -232,6 +236,8 @@ msk_status check_attn_weights(const msk_layer_weights* w, int l) {
   if (!w) return fail(MSK_ERR_INVALID_ARG, "layer %d: weights are null", l);
   if (!w->attn_norm || !w->q_norm || !w->k_norm || !w->wq || !w->wk || !w->wv || !w->wo)
     return fail(MSK_ERR_INVALID_ARG, "layer %d: an attention weight pointer is null", l);
+  if (!aligned(w->wq, 16) || !aligned(w->wk, 16) || !aligned(w->wv, 16) || !aligned(w->wo, 16))
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: an attention weight is not 16-byte aligned", l);
   return ok();
 }
 
@@ -239,6 +245,8 @@ msk_status check_route_weights(const msk_layer_weights* w, int l) {
   if (!w) return fail(MSK_ERR_INVALID_ARG, "layer %d: weights are null", l);
   if (!w->ffn_norm || !w->w_router)
     return fail(MSK_ERR_INVALID_ARG, "layer %d: ffn_norm or w_router is null", l);
+  if (!aligned(w->w_router, 16))
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: w_router is not 16-byte aligned", l);
   return ok();
 }
 
@@ -249,6 +257,11 @@ msk_status check_expert_weights(const msk_layer_cfg* c, const msk_layer_weights*
   if (c->expert_dtype == MSK_NVFP4 &&
       (!w->s_gate || !w->s_up || !w->s_down || !w->g_gate || !w->g_up || !w->g_down))
     return fail(MSK_ERR_INVALID_ARG, "layer %d: NVFP4 experts need block and matrix scales", l);
+  if (!aligned(w->w_gate, 16) || !aligned(w->w_up, 16) || !aligned(w->w_down, 16))
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: an expert weight is not 16-byte aligned", l);
+  if (c->expert_dtype == MSK_NVFP4 &&
+      (!aligned(w->s_gate, 4) || !aligned(w->s_up, 4) || !aligned(w->s_down, 4)))
+    return fail(MSK_ERR_INVALID_ARG, "layer %d: an NVFP4 scale array is not 4-byte aligned", l);
   return ok();
 }
 

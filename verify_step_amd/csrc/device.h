@@ -189,6 +189,18 @@ __device__ __forceinline__ void load_act(const float* p, float* a, int n) {
   }
 }
 
+// NVFP4 block scales of 16-B chunk c of a row: the two e4m3 bytes at
+// srow + 2c, read as the aligned dword holding them (scale arrays are 4-byte
+// aligned and a whole number of dwords long, so the dword never leaves the
+// array), then picked out of it.
+__device__ __forceinline__ unsigned scale_dword(const uint8_t* srow, unsigned c) {
+  const unsigned mis = (unsigned)(uintptr_t)srow & 2u;  // rows start on even bytes
+  return *reinterpret_cast<const unsigned*>(srow - mis + ((c * 2u + mis) & ~3u));
+}
+__device__ __forceinline__ unsigned scale_pair(unsigned dw, const uint8_t* srow, int c) {
+  return dw >> ((((unsigned)(uintptr_t)srow + (unsigned)c * 2u) & 2u) * 8u);
+}
+
 // One wave computes acc[r][v] = sum_c W_r[c] * in_v[c] * gain[c] for R weight
 // rows (any row pointers) and up to NV fp32 input vectors (nv valid).  The
 // rows are streamed once, 16 B per lane per step with two steps in flight;
@@ -311,9 +323,8 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         w[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wr[r] + cc * 16u));
-        // the lane's two scale bytes inside an aligned dword
         if constexpr (DT == kNVFP4)
-          s[u][r] = *reinterpret_cast<const unsigned*>(sr[r] + (cc * 2u & ~3u));
+          s[u][r] = scale_dword(sr[r], cc);
         else
           s[u][r] = 0u;
       }
@@ -322,6 +333,11 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
   auto compute = [&](const v4u(&w)[U][R], const unsigned(&s)[U][R], int f) {
     const int k = f / NI, i = f - (f / NI) * NI;
     const float* act = actfn(k);
+    const uint8_t* sr[R];  // NVFP4: the scale rows again, for their alignment
+    if constexpr (DT == kNVFP4) {
+      const uint8_t* wr[R];
+      rowfn(k, wr, sr);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ch = (i * U + u) * 64 + ln;
@@ -331,7 +347,7 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
       if constexpr (DT == kNVFP4) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          sc[r] = __builtin_amdgcn_cvt_pk_f32_fp8(s[u][r] >> ((cl & 1) * 16), false);
+          sc[r] = __builtin_amdgcn_cvt_pk_f32_fp8(scale_pair(s[u][r], sr[r], cl), false);
           sc[r].x = in ? sc[r].x : 0.f;
           sc[r].y = in ? sc[r].y : 0.f;
         }

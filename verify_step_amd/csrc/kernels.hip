@@ -531,7 +531,10 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
     const int NQ = L.Hq * L.D, NK = L.Hkv * L.D;
     MSK_TRY(launch_dense(S, L.wq, L.wk, L.wv, NQ, NQ + NK, NR, L.H, nullptr, S.qkv, kPhQkv, st));
   } else {
-    MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhQkv, k_qkv<kF32, NV>, qgrid, rs_lds, st, L, S, x)))
+    if (L.ddt == kBF16)
+      MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhQkv, k_qkv<kBF16, NV>, qgrid, rs_lds, st, L, S, x)))
+    else
+      MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhQkv, k_qkv<kF32, NV>, qgrid, rs_lds, st, L, S, x)))
   }
 
   if (L.attn_nw > 0) {
@@ -566,7 +569,10 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
   } else if (mm) {
     MSK_TRY(launch_dense(S, L.wo, nullptr, nullptr, 0, 0, L.H, L.Hq * L.D, x, h, kPhWo, st));
   } else {
-    MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhWo, k_wo<kF32, NV>, wgrid, 0, st, L, S, x, h)))
+    if (L.ddt == kBF16)
+      MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhWo, k_wo<kBF16, NV>, wgrid, 0, st, L, S, x, h)))
+    else
+      MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhWo, k_wo<kF32, NV>, wgrid, 0, st, L, S, x, h)))
   }
   return hipSuccess;
 }
@@ -596,7 +602,10 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
     MSK_TRY(launch_dense(S, L.wr, nullptr, nullptr, 0, 0, L.E, L.H, nullptr, S.logits, kPhRouter,
                          st));
   } else {
-    MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhRouter, k_router<kF32, NV>, grid, rs_lds, st, L, S, h)))
+    if (L.ddt == kBF16)
+      MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhRouter, k_router<kBF16, NV>, grid, rs_lds, st, L, S, h)))
+    else
+      MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhRouter, k_router<kF32, NV>, grid, rs_lds, st, L, S, h)))
   }
   MSK_TRY(launch_x(kPhTopk, k_topk, grid_for_waves(S.T), 0, st, L, S, topk_out));
   return hipSuccess;

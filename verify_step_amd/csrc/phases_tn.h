@@ -89,10 +89,10 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         w[u][r] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wr[r] + cc * 16u));
-        // the lane's two scale bytes as part of an aligned dword (a 16-bit
-        // load here made the compiler wait for the refills at the next step)
+        // the lane's two scale bytes inside an aligned dword (a 16-bit load
+        // here made the compiler wait for the refills at the next step)
         if constexpr (DT == kNVFP4)
-          s[u][r] = *reinterpret_cast<const unsigned*>(sr[r] + (cc * 2u & ~3u));
+          s[u][r] = scale_dword(sr[r], cc);
         else
           s[u][r] = 0u;
       }
@@ -100,6 +100,11 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
   };
   auto compute = [&](const v4u(&w)[U][R], const unsigned(&s)[U][R], int f) {
     const int k = f / NI, i = f - (f / NI) * NI;
+    const uint8_t* sr[R];  // NVFP4: the scale rows again, for their alignment
+    if constexpr (DT == kNVFP4) {
+      const uint8_t* wr[R];
+      rowfn(k, wr, sr);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // no branch on the chunk: a lane past the row end computes on its
@@ -112,7 +117,7 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
       if constexpr (DT == kNVFP4) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          sc[r] = __builtin_amdgcn_cvt_pk_f32_fp8(s[u][r] >> ((cl & 1) * 16), false);
+          sc[r] = __builtin_amdgcn_cvt_pk_f32_fp8(scale_pair(s[u][r], sr[r], cl), false);
           sc[r].x = in ? sc[r].x : 0.f;
           sc[r].y = in ? sc[r].y : 0.f;
         }
