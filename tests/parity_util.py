@@ -40,6 +40,7 @@ def rel_err(gpu, ref, floor=None):
 
 def assert_close(name, gpu, ref, tol, floor=None):
     e = rel_err(gpu, ref, floor)
+    print(f"[err] {name}: max|err|/RMS = {e:.3e} (tolerance {tol:.1e})", flush=True)
     assert e <= tol, f"{name}: max|err|/RMS = {e:.3e} > {tol:.1e}"
     return e
 
@@ -97,18 +98,21 @@ def code_distance(a, b, dtype):
     return np.abs(ordered(a) - ordered(b))
 
 
-def check_appended(p, layer, ref, tol):
+def check_appended(p, layer, ref, tol, tokens=None):
     """K/V written at [L_b, L_b + Tr) equal the oracle's cast values, up to one
     code of the format where the fp32 and fp64 values straddle a rounding
-    boundary."""
+    boundary.  tokens: optional mask over the T tokens to compare."""
     spec = p.specs[layer]
     kd = spec["kv_dtype"]
     Tr = p.tokens_per_req
     for name, bits_key in (("k", "k_new_bits"), ("v", "v_new_bits")):
         cache = p.kv[layer][name]
         for b, L in enumerate(p.kv_len):
-            got = synth.to_numpy(cache[b, :, L:L + Tr])                 # [Hkv][Tr][D]
-            want = np.asarray(ref[bits_key])[b * Tr:(b + 1) * Tr]      # [Tr][Hkv][D]
+            sel = np.ones(Tr, bool) if tokens is None else np.asarray(tokens)[b * Tr:(b + 1) * Tr]
+            if not sel.any():
+                continue
+            got = synth.to_numpy(cache[b, :, L:L + Tr])[:, sel]         # [Hkv][Tr][D]
+            want = np.asarray(ref[bits_key])[b * Tr:(b + 1) * Tr][sel]  # [Tr][Hkv][D]
             want = np.transpose(want, (1, 0, 2))
             if kd == "f32":
                 np.testing.assert_allclose(got, want, rtol=2e-6, atol=2e-6 * np.abs(want).max())
@@ -123,6 +127,50 @@ def routing_margin(logits_ref, k, scale=1e-4):
     if s.shape[1] == k:
         return np.full(s.shape[0], np.inf)
     return s[:, k - 1] - s[:, k]
+
+
+class StackDrift:
+    """Free-running comparison of a layer stack: the oracle runs every layer
+    from the same x, never from a GPU output.  Layer 0 sees identical inputs
+    on both sides; a later layer sees inputs that differ by the earlier
+    layers' rounding, so its routing is compared bit for bit only where the
+    oracle's top-k boundary gap exceeds `drift` x RMS(logits).  A token inside
+    that margin that the GPU routes differently has legitimately left the
+    oracle's trajectory: it is dropped from this layer's comparisons, and it
+    and the later tokens of its request (which attend to its keys) from every
+    later layer's.  At most `max_lost` of the tokens may be dropped."""
+
+    def __init__(self, n_req, Tr, margin0, drift, max_lost=0.25):
+        self.Tr = Tr
+        self.alive = np.ones(n_req * Tr, bool)
+        self.margin0, self.drift, self.max_lost = margin0, drift, max_lost
+
+    def routing(self, layer, idx_gpu, logits_ref, idx_ref, k):
+        """Checks the layer's routing; returns the mask of tokens to compare
+        at this layer."""
+        idx_gpu = np.asarray(idx_gpu)
+        idx_ref = np.asarray(idx_ref)
+        rms = float(np.sqrt(np.mean(np.asarray(logits_ref) ** 2)))
+        delta = (self.margin0 if layer == 0 else self.drift) * rms
+        near = near_mask(logits_ref, k, delta)
+        cmp = self.alive & ~near
+        assert np.array_equal(idx_gpu[cmp], idx_ref[cmp]), \
+            f"layer {layer}: routing differs on {int((idx_gpu[cmp] != idx_ref[cmp]).any(1).sum())} tokens"
+        moved = self.alive & near & (idx_gpu != idx_ref).any(1)
+        here = self.alive & ~moved
+        for t in np.nonzero(moved)[0]:
+            b = t // self.Tr
+            self.alive[t:(b + 1) * self.Tr] = False
+        lost = 1.0 - self.alive.mean()
+        print(f"[gpu-parity] layer {layer}: {int((self.alive & near).sum())} tokens inside the "
+              f"routing margin, {int(moved.sum())} routed differently, {lost:.0%} dropped", flush=True)
+        assert lost <= self.max_lost, f"{lost:.0%} of the tokens left the oracle's trajectory"
+        return here
+
+
+def near_mask(logits_ref, k, delta):
+    """Tokens whose top-k boundary gap is at most delta."""
+    return routing_margin(logits_ref, k) <= delta
 
 
 def check_routing(idx_gpu, logits_ref, idx_ref, k, delta):

@@ -14,11 +14,12 @@ import torch
 import synth
 import verify_step_amd as msk
 from oracle import layer as ol
-from parity_util import (assert_close, check_routing, fill_shift, fp32_store_floor, tol_for)
+from parity_util import (StackDrift, assert_close, fill_shift, fp32_store_floor, tol_for)
 
 pytestmark = pytest.mark.gpu
 
 ROUTE_MARGIN = 1e-5
+DRIFT_MARGIN = 3e-3   # later layers of a stack (see StackDrift)
 
 
 def _run_gpu(p):
@@ -47,28 +48,29 @@ def _check_request(p, gpu, b, n_tok):
     lo, topk, win = gpu
     Tr = p.tokens_per_req
     rows = slice(b * Tr, b * Tr + n_tok)
+    # free-running: the oracle chains its own layers (see StackDrift)
     cur = p.x[rows].double().cpu().numpy()
     gpu_in = cur.copy()
+    drift = StackDrift(1, n_tok, ROUTE_MARGIN, DRIFT_MARGIN)
     for l, spec in enumerate(p.specs):
         w = synth.host_weights(p.weights[l])
         ref = ol.layer_step(spec, w, _sub_kv(p.kv[l], b), [p.kv_len[b]], n_tok, cur)
         tol = tol_for(spec)
+        alive = drift.alive.copy()
         assert np.array_equal(win[l][rows], ref["win"])
-        delta = ROUTE_MARGIN * float(np.sqrt(np.mean(ref["logits"] ** 2)))
-        near = check_routing(topk[l][rows], ref["logits"], ref["idx"], spec["top_k"], delta)
-        print(f"[fullsize] request {b} layer {l}: {near} tokens in the routing margin", flush=True)
-        assert_close(f"req {b} layer {l} out", lo[l][rows], ref["out"], tol)
-        assert_close(f"req {b} layer {l} delta", lo[l][rows] - gpu_in, ref["out"] - cur, tol,
-                     fp32_store_floor(ref["out"]))
+        here = drift.routing(l, topk[l][rows], ref["logits"], ref["idx"], spec["top_k"])
+        assert_close(f"req {b} layer {l} out", lo[l][rows][here], ref["out"][here], tol)
+        assert_close(f"req {b} layer {l} delta", (lo[l][rows] - gpu_in)[here],
+                     (ref["out"] - cur)[here], tol, fp32_store_floor(ref["out"][here]))
         # the appended K/V of these tokens
         for name, key in (("k", "k_new_bits"), ("v", "v_new_bits")):
             L = p.kv_len[b]
-            got = synth.to_numpy(p.kv[l][name][b, :, L:L + n_tok]).astype(np.int64)
-            want = np.transpose(np.asarray(ref[key]), (1, 0, 2)).astype(np.int64)
+            got = synth.to_numpy(p.kv[l][name][b, :, L:L + n_tok]).astype(np.int64)[:, alive]
+            want = np.transpose(np.asarray(ref[key]), (1, 0, 2)).astype(np.int64)[:, alive]
             sign = 0x80
             gv = np.where(got & sign, -(got & 0x7F), got)
             wv = np.where(want & sign, -(want & 0x7F), want)
-            assert np.abs(gv - wv).max() <= 1, f"{name} append differs by more than one code"
+            assert np.abs(gv - wv).max(initial=0) <= 1, f"{name} append differs by more than one code"
         cur = ref["out"]
         gpu_in = lo[l][rows]
 

@@ -10,6 +10,7 @@ import synth
 import verify_step_amd as msk
 from oracle import layer as ol
 from parity_util import (assert_close, check_appended, check_routing, check_topk_of_gpu_logits,
+                         StackDrift, near_mask,
                          fill_shift, fp32_store_floor, oracle_inputs, restore_kv, snapshot_kv,
                          tol_for)
 
@@ -19,6 +20,10 @@ pytestmark = pytest.mark.gpu
 # gap exceeds this fraction of the logits' RMS; fp32 logits carry errors near
 # 1e-6 of it, so only a token closer than that to a tie could flip.
 ROUTE_MARGIN = 1e-5
+# Layers after the first of a stack take inputs that differ from the oracle's
+# chain by the earlier layers' rounding (layer outputs within ~3e-4 of their
+# RMS in the low-precision paths): their logits may move by about as much.
+DRIFT_MARGIN = 3e-3
 
 _SMALL = dict(hidden=512, n_q_heads=12, n_kv_heads=2, head_dim=128, n_experts=32, top_k=8,
               ffn_dim=256)
@@ -85,21 +90,22 @@ def test_layer_step_matches_oracle(prob):
     msk.workspace_status(ws)
     assert torch.equal(x, layer_out[-1])
 
+    # free-running: the oracle chains its own layers from x (see StackDrift)
     cur = p.x.double().cpu().numpy()
     gpu_in = cur.copy()
     lo = layer_out.double().cpu().numpy()
+    drift = StackDrift(len(p.kv_len), p.tokens_per_req, ROUTE_MARGIN, DRIFT_MARGIN)
     for l in range(n):
         spec, w, kv = oracle_inputs(p, l)
         ref = ol.layer_step(spec, w, kv, p.kv_len, p.tokens_per_req, cur)
         tol = tol_for(spec)
-        check_appended(p, l, ref, tol)
+        alive = drift.alive.copy()
+        check_appended(p, l, ref, tol, tokens=alive)
         assert np.array_equal(win[l].cpu().numpy(), ref["win"])
-        delta = ROUTE_MARGIN * float(np.sqrt(np.mean(ref["logits"] ** 2)))
-        near = check_routing(topk[l].cpu().numpy(), ref["logits"], ref["idx"], K, delta)
-        print(f"[gpu-parity] layer {l}: {near} tokens inside the routing margin", flush=True)
-        assert_close(f"layer {l} out", lo[l], ref["out"], tol)
-        assert_close(f"layer {l} delta", lo[l] - gpu_in, ref["out"] - cur, tol,
-                     fp32_store_floor(ref["out"]))
+        here = drift.routing(l, topk[l].cpu().numpy(), ref["logits"], ref["idx"], K)
+        assert_close(f"layer {l} out", lo[l][here], ref["out"][here], tol)
+        assert_close(f"layer {l} delta", (lo[l] - gpu_in)[here], (ref["out"] - cur)[here], tol,
+                     fp32_store_floor(ref["out"][here]))
         cur = ref["out"]
         gpu_in = lo[l]
     restore_kv(p, snaps)
@@ -118,11 +124,7 @@ def test_ops_match_oracle(prob):
     win = torch.empty((T, 2), dtype=torch.int32, device="cuda")
     h, _, _ = msk.attn_step(spec, w, kv, p.kv_len, p.tokens_per_req, p.x, ws, attn_o=attn_o,
                             win=win)
-    logits = torch.empty((T, E), device="cuda")
-    u, idx, wts, _ = msk.moe_route(spec, w, h, ws, logits=logits)
-    out = msk.expert_ffn(spec, w, u, idx, wts, h, ws)
     torch.cuda.synchronize()
-    msk.workspace_status(ws)
 
     so, wo, kvo = oracle_inputs(p, 0)
     x = p.x.double().cpu().numpy()
@@ -133,20 +135,34 @@ def test_ops_match_oracle(prob):
     assert_close("h - x", h.double().cpu().numpy() - x, att["h"] - x, tol,
                  fp32_store_floor(att["h"]))
 
-    # router and experts on the GPU's own h: the oracle consumes the same h
-    # (an input of these two calls), so each call is checked on its own
-    hg = h.double().cpu().numpy()
-    r = ol.route(so, wo, hg)
+    # router and experts each on inputs both sides share: the oracle's h (its
+    # attention output above), then the oracle's routing of it, handed to the
+    # GPU calls as their inputs
+    h32 = np.asarray(att["h"], dtype=np.float32).astype(np.float64)
+    r = ol.route(so, wo, h32)
+    h_dev = torch.from_numpy(h32.astype(np.float32)).to("cuda")
+    logits = torch.empty((T, E), device="cuda")
+    u, idx, wts, _ = msk.moe_route(spec, w, h_dev, ws, logits=logits)
+    u_o = torch.from_numpy(np.asarray(r["u"], dtype=np.float32)).to("cuda")
+    idx_o = torch.from_numpy(np.asarray(r["idx"], dtype=np.int32)).to("cuda")
+    wts_o = torch.from_numpy(np.asarray(r["weights"], dtype=np.float32)).to("cuda")
+    out = msk.expert_ffn(spec, w, u_o, idx_o, wts_o, h_dev, ws)
+    torch.cuda.synchronize()
+    msk.workspace_status(ws)
+
     assert_close("u", u.cpu().numpy(), r["u"], tol)
     assert_close("logits", logits.cpu().numpy(), r["logits"], tol)
     check_topk_of_gpu_logits(idx.cpu().numpy(), logits.cpu().numpy(), K)
     near = check_routing(idx.cpu().numpy(), r["logits"], r["idx"], K,
                          ROUTE_MARGIN * float(np.sqrt(np.mean(r["logits"] ** 2))))
     print(f"[gpu-parity] router: {near} tokens inside the routing margin", flush=True)
-    np.testing.assert_allclose(wts.cpu().numpy(), r["weights"], rtol=1e-5, atol=1e-6)
-    ref_out = ol.expert_ffn(so, wo, u.double().cpu().numpy(), idx.cpu().numpy().astype(np.int64),
-                            wts.double().cpu().numpy(), hg)
-    assert_close("moe delta", out.double().cpu().numpy() - hg, ref_out - hg, tol,
+    far = ~near_mask(r["logits"], K, ROUTE_MARGIN * float(np.sqrt(np.mean(r["logits"] ** 2))))
+    np.testing.assert_allclose(wts.cpu().numpy()[far], np.asarray(r["weights"])[far],
+                               rtol=1e-5, atol=1e-6)
+    ref_out = ol.expert_ffn(so, wo, u_o.double().cpu().numpy(),
+                            np.asarray(r["idx"], dtype=np.int64),
+                            wts_o.double().cpu().numpy(), h32)
+    assert_close("moe delta", out.double().cpu().numpy() - h32, ref_out - h32, tol,
                  fp32_store_floor(ref_out))
     restore_kv(p, snaps)
 

@@ -189,6 +189,25 @@ __device__ __forceinline__ void load_act(const float* p, float* a, int n) {
   }
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const v4u& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Two floats -> two bf16 (round to nearest even), packed a | b << 16.
+__device__ __forceinline__ unsigned cvt_pk_bf16(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f2){a, b}, bf16x2));
+}
+
+// Two floats -> two fp16 (round to nearest even), packed a | b << 16.
+__device__ __forceinline__ unsigned cvt_pk_f16(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f2){a, b}, f16x2));
+}
+
 // NVFP4 block scales of 16-B chunk c of a row: the two e4m3 bytes at
 // srow + 2c, read as the aligned dword holding them (scale arrays are 4-byte
 // aligned and a whole number of dwords long, so the dword never leaves the
@@ -407,6 +426,19 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
     if (f + 1 < total) compute(B, sB, f + 1);
     if (f + 2 < total) compute(A, sA, f + 2);
   }
+}
+
+// Maximum over the block (all waves); every thread gets it.  red is kWaves
+// floats of LDS.
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  lds_barrier();
+  if (lane_id() == 0) red[wave_id()] = v;
+  lds_barrier();
+  float t = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) t = fmaxf(t, red[w]);
+  return t;
 }
 
 // Sum over the block (all waves); every thread gets the total.  red is

@@ -60,7 +60,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_union(LayerArgs L, StepArgs S
 
 template <int DT, int NVMAX>
 __global__ __launch_bounds__(kBlockThreads) void k_gateup_tn(LayerArgs L, StepArgs S) {
-  gateup_tn<DT, NVMAX>(L, S, S.uni, reinterpret_cast<float*>(msk_smem));
+  float* act = reinterpret_cast<float*>(msk_smem);
+  gateup_tn<DT, NVMAX>(L, S, S.uni, act, act + NVMAX * tn_vec_floats<DT>(L.H));
 }
 
 // bf16 down streams four slot vectors: held to four waves per SIMD (its
@@ -70,7 +71,8 @@ template <int DT> struct DownTnWaves { static constexpr int N = DT == kBF16 ? 4 
 template <int DT, int NVMAX>
 __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(DownTnWaves<DT>::N)))
 void k_down_tn(LayerArgs L, StepArgs S) {
-  down_tn<DT, NVMAX>(L, S, S.uni, reinterpret_cast<float*>(msk_smem), S.ybuf);
+  float* act = reinterpret_cast<float*>(msk_smem);
+  down_tn<DT, NVMAX>(L, S, S.uni, act, act + NVMAX * tn_vec_floats<DT>(L.F), S.ybuf);
 }
 
 __global__ __launch_bounds__(kBlockThreads) void k_moe_sum(LayerArgs L, StepArgs S, const float* h,
@@ -642,7 +644,7 @@ static hipError_t launch_ffn_tn(const LayerArgs& L, const StepArgs& S, const flo
   MSK_TRY(launch_x(kPhUnion, k_union, 1, sizeof(Union), st, L, S));
   {
     auto fn = k_gateup_tn<DT, kGateUpTokens>;
-    const size_t lds = (size_t)kGateUpTokens * L.H * sizeof(float);
+    const size_t lds = ((size_t)kGateUpTokens * tn_vec_floats<DT>(L.H) + kWaves) * sizeof(float);
     MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
     static int grid = 0;
     if (grid == 0) grid = resident_grid(reinterpret_cast<const void*>(fn), lds);
@@ -650,7 +652,7 @@ static hipError_t launch_ffn_tn(const LayerArgs& L, const StepArgs& S, const flo
   }
   {
     auto fn = k_down_tn<DT, kDownTokens<DT>>;
-    const size_t lds = (size_t)kDownTokens<DT> * L.F * sizeof(float);
+    const size_t lds = ((size_t)kDownTokens<DT> * tn_vec_floats<DT>(L.F) + kWaves) * sizeof(float);
     MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
     static int grid = 0;
     if (grid == 0) grid = resident_grid(reinterpret_cast<const void*>(fn), lds);

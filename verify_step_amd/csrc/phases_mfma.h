@@ -32,7 +32,6 @@
 
 namespace msk {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int KDT, int D, int NW, int NPH = 1>
@@ -68,8 +67,6 @@ __device__ __forceinline__ unsigned pack_bf16_exact(float a, float b) {
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 // One 16-B chunk of cache-format data -> its EPC values as bf16, two per
 // word (exact: every e4m3 value is a bf16 value; the convert's scale of 1
 // leaves the values unchanged).
@@ -89,12 +86,6 @@ __device__ __forceinline__ void chunk_to_bf16(const v4u& w, unsigned* o) {
   }
 }
 
-// Two floats -> two bf16 (round to nearest even), packed a | b << 16.
-__device__ __forceinline__ unsigned cvt_pk_bf16(float a, float b) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(unsigned, __builtin_convertvector((f2){a, b}, bf16x2));
-}
-
 // x = hi + lo (+ a residual of at most 2^-16 |x|), both bf16 bits.
 __device__ __forceinline__ void split_bf16(float x, unsigned& hi, unsigned& lo) {
   hi = f2bf16(x);
@@ -106,8 +97,6 @@ __device__ __forceinline__ void split2_bf16(float a, float b, unsigned& hi, unsi
   hi = cvt_pk_bf16(a, b);
   lo = cvt_pk_bf16(a - bf16_lo(hi), b - bf16_hi(hi));
 }
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const v4u& v) { return __builtin_bit_cast(bf16x8, v); }
 
 // NPH = 2: the waves pair up on the same 16 rows, each taking half of every
 // tile's positions; the pair's sums are added at the end of the item.

@@ -17,28 +17,65 @@
 
 namespace msk {
 
-// Input vectors staged in LDS are stored in 16-B granules (4 floats) in a
-// rotated order: a lane reads its chunk of EPL consecutive inputs, so in a
-// plain layout the 16 lanes of one LDS read pass would sit EPL * 4 bytes
-// apart and share a few bank groups (NVFP4: two of sixteen).  Rotating each
-// chunk's granules by the chunk index (NVFP4: by half of it) gives the 16
-// lanes of a pass 16 distinct bank groups.  Granule G of a vector is stored
-// at tn_gran<DT>(G), relative to the vector's own start.
+// Input vectors staged in LDS are stored in 16-B granules in a rotated order:
+// a lane reads its chunk of consecutive inputs, so in a plain layout the 16
+// lanes of one LDS read pass would sit a chunk's worth of bytes apart and
+// share a few bank groups.  Rotating each chunk's granules by the chunk index
+// (or a part of it) gives the 16 lanes of a pass 16 distinct bank groups.
+// fp32 and bf16 weights meet fp32 inputs (a granule is 4 floats); NVFP4
+// weights meet fp16 inputs (a granule is 8 halves, a chunk's 32 inputs are 4
+// granules).  Granule G of a vector is stored at tn_gran<DT>(G), relative to
+// the vector's own start.
 template <int DT>
 __device__ __forceinline__ int tn_gran(int G) {
-  if constexpr (DT == kNVFP4) return (G & ~7) | ((G + (G >> 4)) & 7);
+  if constexpr (DT == kNVFP4) return (G & ~3) | ((G + (G >> 4)) & 3);
   else if constexpr (DT == kBF16) return (G & ~1) | ((G ^ (G >> 4)) & 1);
   else return G;
 }
 
-// n floats from global memory into LDS in that order (all threads).
+// LDS floats one staged vector of n inputs takes (fp16 pairs for NVFP4).
 template <int DT>
-__device__ __forceinline__ void tn_stage(const float* src, int n, float* dst) {
-  for (int c = threadIdx.x * 4; c < n; c += blockDim.x * 4)
-    *reinterpret_cast<v4f*>(dst + tn_gran<DT>(c >> 2) * 4) = *reinterpret_cast<const v4f*>(src + c);
+__host__ __device__ constexpr int tn_vec_floats(int n) { return DT == kNVFP4 ? n / 2 : n; }
+
+// n inputs from global memory into LDS in that order (all threads).  NVFP4
+// takes them as fp16 (nearest even, two per word, element 2i low), unscaled
+// when the vector's largest magnitude lies in [2^-8, 2^15) (fp16 then holds
+// every input to its own relative precision unless it is 2^-6 times the
+// largest or smaller); otherwise a second pass stores them times the power of
+// two that brings the largest into [2^13, 2^14).  Returns the factor that
+// undoes the scaling (1 for the other types).  red: kWaves floats of LDS.
+template <int DT>
+__device__ __forceinline__ float tn_stage(const float* src, int n, float* dst, float* red) {
+  if constexpr (DT == kNVFP4) {
+    auto pass = [&](float up) {
+      float m = 0.f;
+      for (int c = threadIdx.x * 8; c < n; c += blockDim.x * 8) {
+        const v4f a = *reinterpret_cast<const v4f*>(src + c);
+        const v4f b = *reinterpret_cast<const v4f*>(src + c + 4);
+        m = fmaxf(m, fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                           fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w)))));
+        *reinterpret_cast<v4u*>(dst + tn_gran<DT>(c >> 3) * 4) =
+            v4u{cvt_pk_f16(a.x * up, a.y * up), cvt_pk_f16(a.z * up, a.w * up),
+                cvt_pk_f16(b.x * up, b.y * up), cvt_pk_f16(b.z * up, b.w * up)};
+      }
+      return m;
+    };
+    const float m = block_max(pass(1.f), red);
+    if (m >= 0x1p-8f && m < 0x1p15f) return 1.f;
+    if (!(m > 0.f) || !(m < __builtin_huge_valf())) return 1.f;  // all zero, or not finite
+    int ex = 0;
+    frexpf(m, &ex);  // m < 2^ex
+    lds_barrier();   // every wave's first-pass stores are done before they are replaced
+    pass(ldexpf(1.f, 14 - ex));
+    return ldexpf(1.f, ex - 14);
+  } else {
+    for (int c = threadIdx.x * 4; c < n; c += blockDim.x * 4)
+      *reinterpret_cast<v4f*>(dst + tn_gran<DT>(c >> 2) * 4) = *reinterpret_cast<const v4f*>(src + c);
+    return 1.f;
+  }
 }
 
-// The SUB inputs of sub-block `sub` of chunk `ch` of a staged vector.
+// The SUB inputs of sub-block `sub` of chunk `ch` of a staged fp32 vector.
 template <int DT>
 __device__ __forceinline__ void tn_load(const float* v, int ch, int sub, float* a) {
   using W = WT<DT>;
@@ -49,6 +86,11 @@ __device__ __forceinline__ void tn_load(const float* v, int ch, int sub, float* 
     const v4f y = *reinterpret_cast<const v4f*>(v + tn_gran<DT>(G + 1) * 4);
     a[4] = y.x; a[5] = y.y; a[6] = y.z; a[7] = y.w;
   }
+}
+
+// NVFP4: the 8 fp16 inputs of sub-block `sub` of chunk `ch` (one granule).
+__device__ __forceinline__ v4u tn_load_f16(const float* v, int ch, int sub) {
+  return *reinterpret_cast<const v4u*>(v + tn_gran<kNVFP4>(ch * 4 + sub) * 4);
 }
 
 // Like stream_t1, for nv <= NV input vectors in LDS (stored by tn_stage):
@@ -122,28 +164,58 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
           sc[r].y = in ? sc[r].y : 0.f;
         }
       }
+      if constexpr (DT == kNVFP4) {
+        // e2m1 pairs -> fp16 pairs (exact), dotted with the fp16 inputs two
+        // products at a time into fp32; the block scale multiplies each
+        // 8-element sum
 #pragma unroll
-      for (int sub = 0; sub < W::NSUB; ++sub) {
-        // the inputs of this sub-block first, then one weight row at a
-        // time: only one row's decoded values are live at once
+        for (int sub = 0; sub < W::NSUB; ++sub) {
+          v4u a[NV];
+#pragma unroll
+          for (int v = 0; v < NV; ++v)
+            if (v < nv) a[v] = tn_load_f16(actfn(v), cl, sub);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const unsigned word = sub == 0 ? w[u][r].x : sub == 1 ? w[u][r].y
+                                : sub == 2 ? w[u][r].z : w[u][r].w;
+            const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0);
+            const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1);
+            const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2);
+            const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+              if (v < nv) {
+                // the pairs are taken out of the 8-vector with a shuffle: a
+                // bit cast of each 32-bit word to a pair compiled to the
+                // first word for all four
+                const f16x8 x = __builtin_bit_cast(f16x8, a[v]);
+                float d = __builtin_amdgcn_fdot2(p0, __builtin_shufflevector(x, x, 0, 1), 0.f, false);
+                d = __builtin_amdgcn_fdot2(p1, __builtin_shufflevector(x, x, 2, 3), d, false);
+                d = __builtin_amdgcn_fdot2(p2, __builtin_shufflevector(x, x, 4, 5), d, false);
+                d = __builtin_amdgcn_fdot2(p3, __builtin_shufflevector(x, x, 6, 7), d, false);
+                acc[r][v] = fmaf((sub >> 1) ? sc[r].y : sc[r].x, d, acc[r][v]);
+              }
+            }
+          }
+        }
+      } else {
+        // the inputs first, then one weight row at a time: only one row's
+        // decoded values are live at once (one sub-block per chunk)
         float a[NV][W::SUB];
 #pragma unroll
         for (int v = 0; v < NV; ++v)
-          if (v < nv) tn_load<DT>(actfn(v), cl, sub, a[v]);
+          if (v < nv) tn_load<DT>(actfn(v), cl, 0, a[v]);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           float fw[W::SUB];
-          decode_sub<DT>(w[u][r], sub, fw);
+          decode_sub<DT>(w[u][r], 0, fw);
 #pragma unroll
           for (int v = 0; v < NV; ++v) {
             if (v < nv) {
               float d = 0.f;
 #pragma unroll
               for (int e = 0; e < W::SUB; ++e) d = fmaf(fw[e], a[v][e], d);
-              if constexpr (DT == kNVFP4)
-                acc[r][v] = fmaf((sub >> 1) ? sc[r].y : sc[r].x, d, acc[r][v]);
-              else  // one sub-block per chunk
-                acc[r][v] += in ? d : 0.f;
+              acc[r][v] += in ? d : 0.f;
             }
           }
         }
@@ -228,7 +300,8 @@ template <> struct TnShape<kNVFP4> { enum { GU_RW = 2, GU_U = 1, DN_R = 4, DN_U 
 // act[s][f] = silu(gate_e[f] . u[t]) * (up_e[f] . u[t]) for slot s = t*K + j.
 // Tasks: (expert, RW rows of gate and the same RW rows of up).
 template <int DT, int NVMAX>
-__device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U, float* act_lds) {
+__device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U, float* act_lds,
+                          float* red) {
   constexpr int RW = TnShape<DT>::GU_RW, R = 2 * RW, UU = TnShape<DT>::GU_U;
   const int nrt = L.F / RW;
   const size_t rb = expert_row_bytes(DT, L.H);
@@ -247,16 +320,19 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
 #pragma unroll
     for (int v = 0; v < NVMAX; ++v)
       slot[v] = __builtin_amdgcn_readfirstlane(U->slots[sidx + (v < nv ? v : 0)]);
+    float down[NVMAX];  // undoes the staging's scaling of each input
     auto pre = [&]() {
-      __syncthreads();  // the previous group's readers are done
+      lds_barrier();  // the previous group's readers are done (LDS only: the
+                      // weight loads just issued stay in flight)
       for (int v = 0; v < nv; ++v)
-        tn_stage<DT>(S.u + (size_t)(slot[v] / L.K) * L.H, L.H, act_lds + v * L.H);
-      __syncthreads();
+        down[v] = tn_stage<DT>(S.u + (size_t)(slot[v] / L.K) * L.H, L.H,
+                               act_lds + v * tn_vec_floats<DT>(L.H), red);
+      lds_barrier();
     };
     nv_dispatch<NVMAX>(nv, [&](auto nvc) {
       constexpr int NV = decltype(nvc)::value;
       stream_tn<DT, R, UU, NV>(
-          w1 - w0, L.H, nv, [&](int v) { return act_lds + v * L.H; },
+          w1 - w0, L.H, nv, [&](int v) { return act_lds + v * tn_vec_floats<DT>(L.H); },
           [&](int k, auto& wr, auto& sr) {
             const int f0 = (w0 + k - ui * nrt) * RW;
 #pragma unroll
@@ -277,7 +353,7 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
               for (int v = 0; v < NV; ++v)
                 if (v < nv && ln == r * NV + v)
                   S.act[(size_t)slot[v] * L.F + f0 + r] =
-                      silu(acc[r][v] * ggs) * (acc[RW + r][v] * gus);
+                      silu(acc[r][v] * (ggs * down[v])) * (acc[RW + r][v] * (gus * down[v]));
           },
           pre);
     });
@@ -288,7 +364,7 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
 // s routed to expert e.  Tasks: (expert, RD output rows).
 template <int DT, int NVMAX>
 __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, float* act_lds,
-                        float* y) {
+                        float* red, float* y) {
   constexpr int RD = TnShape<DT>::DN_R, UU = TnShape<DT>::DN_U;
   const int nrt = L.H / RD;
   const size_t rb = expert_row_bytes(DT, L.F);
@@ -303,16 +379,18 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
 #pragma unroll
     for (int v = 0; v < NVMAX; ++v)
       slot[v] = __builtin_amdgcn_readfirstlane(U->slots[sidx + (v < nv ? v : 0)]);
+    float down[NVMAX];  // undoes the staging's scaling of each input
     auto pre = [&]() {
-      __syncthreads();
+      lds_barrier();
       for (int v = 0; v < nv; ++v)
-        tn_stage<DT>(S.act + (size_t)slot[v] * L.F, L.F, act_lds + v * L.F);
-      __syncthreads();
+        down[v] = tn_stage<DT>(S.act + (size_t)slot[v] * L.F, L.F,
+                               act_lds + v * tn_vec_floats<DT>(L.F), red);
+      lds_barrier();
     };
     nv_dispatch<NVMAX>(nv, [&](auto nvc) {
       constexpr int NV = decltype(nvc)::value;
       stream_tn<DT, RD, UU, NV>(
-          w1 - w0, L.F, nv, [&](int v) { return act_lds + v * L.F; },
+          w1 - w0, L.F, nv, [&](int v) { return act_lds + v * tn_vec_floats<DT>(L.F); },
           [&](int k, auto& wr, auto& sr) {
             const int c0 = (w0 + k - ui * nrt) * RD;
 #pragma unroll
@@ -330,7 +408,7 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
 #pragma unroll
               for (int v = 0; v < NV; ++v)
                 if (v < nv && ln == r * NV + v)
-                  y[(size_t)slot[v] * L.H + c0 + r] = acc[r][v] * gds;
+                  y[(size_t)slot[v] * L.H + c0 + r] = acc[r][v] * (gds * down[v]);
           },
           pre);
     });
