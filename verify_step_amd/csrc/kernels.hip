@@ -510,6 +510,23 @@ static hipError_t launch_attn_mfma(const LayerArgs& L, const StepArgs& S, hipStr
   return launch_attn_mfma_d<kE4M3, 128>(L, S, st);
 }
 
+// The attention partials (matrix-core or vector kernel).
+static hipError_t launch_attn_kernel(const LayerArgs& L, const StepArgs& S, hipStream_t st) {
+  if (L.attn_nw > 0) return launch_attn_mfma(L, S, st);
+  const size_t alds = attn_lds_bytes(L.kdt, L.D);
+  const int agrid = L.n_items < 8 * cu_count() ? L.n_items : 8 * cu_count();
+#define MSK_ATTN(K, DD)                                                           \
+  if (L.kdt == K && L.D == DD) {                                                  \
+    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_attn<K, DD>), alds)); \
+    return launch(kPhAttn, k_attn<K, DD>, agrid, alds, st, L, S);                \
+  }
+  MSK_ATTN(kF32, 32) MSK_ATTN(kF32, 64) MSK_ATTN(kF32, 128)
+  MSK_ATTN(kBF16, 32) MSK_ATTN(kBF16, 64) MSK_ATTN(kBF16, 128)
+  MSK_ATTN(kE4M3, 32) MSK_ATTN(kE4M3, 64) MSK_ATTN(kE4M3, 128)
+#undef MSK_ATTN
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, float* h,
                        hipStream_t st) {
   const int NR = (L.Hq + 2 * L.Hkv) * L.D;
@@ -539,21 +556,7 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
       MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhQkv, k_qkv<kF32, NV>, qgrid, rs_lds, st, L, S, x)))
   }
 
-  if (L.attn_nw > 0) {
-    MSK_TRY(launch_attn_mfma(L, S, st));
-  } else {
-    const size_t alds = attn_lds_bytes(L.kdt, L.D);
-    const int agrid = L.n_items < 8 * cu_count() ? L.n_items : 8 * cu_count();
-#define MSK_ATTN(K, DD)                                                             \
-    if (L.kdt == K && L.D == DD) {                                                  \
-      MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_attn<K, DD>), alds)); \
-      MSK_TRY(launch(kPhAttn, k_attn<K, DD>, agrid, alds, st, L, S));              \
-    }
-    MSK_ATTN(kF32, 32) MSK_ATTN(kF32, 64) MSK_ATTN(kF32, 128)
-    MSK_ATTN(kBF16, 32) MSK_ATTN(kBF16, 64) MSK_ATTN(kBF16, 128)
-    MSK_ATTN(kE4M3, 32) MSK_ATTN(kE4M3, 64) MSK_ATTN(kE4M3, 128)
-#undef MSK_ATTN
-  }
+  MSK_TRY(launch_attn_kernel(L, S, st));
   const bool mm = dense_on_mfma(L, S, L.H, L.Hq * L.D);
   MSK_TRY(launch_x(kPhCombine, k_combine, grid_for_waves((long long)S.T * L.Hq), sizeof(AttnPlan),
                    st, L, S, S.win_out, mm ? S.a3 : nullptr));
@@ -639,9 +642,7 @@ constexpr int kGateUpTokens = 2;  // token vectors staged per gate/up pass
 template <int DT> constexpr int kDownTokens = DT == kNVFP4 ? 2 : 4;
 
 template <int DT>
-static hipError_t launch_ffn_tn(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
-                                hipStream_t st) {
-  MSK_TRY(launch_x(kPhUnion, k_union, 1, sizeof(Union), st, L, S));
+static hipError_t launch_experts_tn(const LayerArgs& L, const StepArgs& S, hipStream_t st) {
   {
     auto fn = k_gateup_tn<DT, kGateUpTokens>;
     const size_t lds = ((size_t)kGateUpTokens * tn_vec_floats<DT>(L.H) + kWaves) * sizeof(float);
@@ -658,10 +659,17 @@ static hipError_t launch_ffn_tn(const LayerArgs& L, const StepArgs& S, const flo
     if (grid == 0) grid = resident_grid(reinterpret_cast<const void*>(fn), lds);
     MSK_TRY(launch(kPhDown, fn, grid, lds, st, L, S));
   }
-  const long long n4 = (long long)S.T * L.H / 4;
-  MSK_TRY(launch_x(kPhMoeSum, k_moe_sum, (int)((n4 + kBlockThreads - 1) / kBlockThreads), 0, st,
-                   L, S, h, out));
   return hipSuccess;
+}
+
+template <int DT>
+static hipError_t launch_ffn_tn(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
+                                hipStream_t st) {
+  MSK_TRY(launch_x(kPhUnion, k_union, 1, sizeof(Union), st, L, S));
+  MSK_TRY(launch_experts_tn<DT>(L, S, st));
+  const long long n4 = (long long)S.T * L.H / 4;
+  return launch_x(kPhMoeSum, k_moe_sum, (int)((n4 + kBlockThreads - 1) / kBlockThreads), 0, st,
+                  L, S, h, out);
 }
 
 hipError_t launch_ffn(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
@@ -687,10 +695,10 @@ hipError_t launch_step_unfused(const LayerArgs* Ls, const StepArgs& S0, hipStrea
   for (int l = 0; l < S.n_layers; ++l) {
     const LayerArgs& L = Ls[l];
     float* nxt = (l == S.n_layers - 1) ? S.x_out : ((l & 1) ? S.xb : S.xa);
+    int* topk = S0.topk_out ? S0.topk_out + (size_t)l * S.T * L.K : nullptr;
     S.win_out = S0.win_out ? S0.win_out + (size_t)l * S.T * 2 : nullptr;
     MSK_TRY(launch_attn(L, S, cur, S.h, st));
-    MSK_TRY(launch_route(L, S, S.h, S0.topk_out ? S0.topk_out + (size_t)l * S.T * L.K : nullptr,
-                         st));
+    MSK_TRY(launch_route(L, S, S.h, topk, st));
     MSK_TRY(launch_ffn(L, S, S.h, nxt, st));
     if (S.layer_out)
       MSK_TRY(hipMemcpyAsync(S.layer_out + (size_t)l * S.T * L.H, nxt,

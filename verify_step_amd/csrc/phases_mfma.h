@@ -9,9 +9,11 @@
 //   weights e = exp(s - c) on the row's window, else 0         (VALU)
 //   output  O^T[d][m]  += sum_pos V^T[d][pos] * e[pos][m]      (MFMA, k = pos)
 // with v_mfma_f32_16x16x32_bf16.  Cached K and V are bf16 or e4m3, both
-// exact in bf16.  qhat and e are fp32; each enters as a sum of two bf16
-// terms (hi = rne(x), lo = rne(x - hi)), so a product is exact to about
-// 2^-16 relative and sums stay in fp32.  The score accumulator's layout (lane
+// exact in bf16.  qhat is fp32 and enters as a sum of two bf16 terms (hi =
+// rne(x), lo = rne(x - hi)), so a score is exact to about 2^-16 relative of
+// its terms; the weights e enter rounded to bf16 once (2^-9 relative each,
+// averaged over many positions), and the normaliser sums those same rounded
+// weights.  Sums stay in fp32.  The score accumulator's layout (lane
 // = column m, four consecutive positions per lane) is used directly as the
 // weight operand of the output product by numbering that product's k index
 // so that a lane's eight k values are its own eight positions of the 32:
@@ -328,7 +330,7 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
     }
     // weights: lane holds row m, positions 16 pt + 4 (ln >> 4) + i
     const bool open = pb >= lo_all && pb + 63 <= hi_all && pb + 64 <= p1;
-    unsigned wh[NKS][4], wlo[NKS][4];
+    unsigned wh[NKS][4];
 #pragma unroll
     for (int pq = 0; pq < NPT; ++pq) {
       const int pt = ph * NPT + pq;
@@ -340,11 +342,13 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
           const int pos = pb + 16 * pt + 4 * (ln >> 4) + i;
           e[i] = (pos >= w_lo && pos <= w_hi && pos < p1) ? e[i] : 0.f;
         }
-        lsum += e[i];
       }
-      // k index 8 (ln >> 4) + 4 (pt & 1) + i of k step pt / 2
-      split2_bf16(e[0], e[1], wh[pq >> 1][2 * (pt & 1)], wlo[pq >> 1][2 * (pt & 1)]);
-      split2_bf16(e[2], e[3], wh[pq >> 1][2 * (pt & 1) + 1], wlo[pq >> 1][2 * (pt & 1) + 1]);
+      // k index 8 (ln >> 4) + 4 (pt & 1) + i of k step pt / 2; the sum of
+      // weights takes the same rounded values the product does
+      const unsigned h0 = cvt_pk_bf16(e[0], e[1]), h1 = cvt_pk_bf16(e[2], e[3]);
+      wh[pq >> 1][2 * (pt & 1)] = h0;
+      wh[pq >> 1][2 * (pt & 1) + 1] = h1;
+      lsum += (bf16_lo(h0) + bf16_hi(h0)) + (bf16_lo(h1) + bf16_hi(h1));
     }
     // O^T[d][m] += V^T[d][pos] e[pos][m]; the A operand's k numbering matches
     // the weights': positions 32 ks + 4 (ln >> 4) + {0..3} and + 16 + {0..3}
@@ -352,7 +356,6 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
     for (int kq = 0; kq < NKS; ++kq) {
       const int ks = ph * NKS + kq;
       const bf16x8 bh = as_bf16x8(v4u{wh[kq][0], wh[kq][1], wh[kq][2], wh[kq][3]});
-      const bf16x8 bl = as_bf16x8(v4u{wlo[kq][0], wlo[kq][1], wlo[kq][2], wlo[kq][3]});
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const uint8_t* src = vt + (16 * dt + (ln & 15)) * VTS + (32 * ks + 4 * (ln >> 4)) * 2;
@@ -360,7 +363,6 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
         const v2u x1 = *reinterpret_cast<const v2u*>(src + 32);
         const bf16x8 a = as_bf16x8(v4u{x0.x, x0.y, x1.x, x1.y});
         oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, oacc[dt], 0, 0, 0);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, oacc[dt], 0, 0, 0);
       }
     }
   }

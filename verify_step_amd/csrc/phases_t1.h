@@ -146,7 +146,8 @@ __device__ void router_t1(const LayerArgs& L, const StepArgs& S, const float* h,
 // Top-k of one token's logits by one wave (value descending, index ascending
 // on ties); idx/w written by lane 0, weights = softmax over the selected.
 // Each round takes the wave-wide maximum, then the lowest index holding it.
-__device__ inline void topk_row(const float* logits, int E, int K, int* idx, float* w) {
+__device__ inline void topk_row(const float* logits, int E, int K, int* idx, float* w,
+                                int* idx2 = nullptr) {
   const int ln = lane_id();
   float v[4];
   bool open[4];  // still selectable
@@ -178,7 +179,11 @@ __device__ inline void topk_row(const float* logits, int E, int K, int* idx, flo
     if (k == 0) v0 = m;
     const float ex = __expf(m - v0);
     den += ex;
-    if (ln == 0) { idx[k] = bi; w[k] = ex; }
+    if (ln == 0) {
+      idx[k] = bi;
+      w[k] = ex;
+      if (idx2) idx2[k] = bi;  // the caller's copy, from the register (no re-read)
+    }
   }
   if (ln == 0) {
     const float inv = 1.0f / den;
@@ -189,9 +194,8 @@ __device__ inline void topk_row(const float* logits, int E, int K, int* idx, flo
 // One wave per token: top-k and gating weights into S.idx / S.wts.
 __device__ void phase_topk(const LayerArgs& L, const StepArgs& S, int* topk_out, int vb, int nvb) {
   for (int t = gwave(vb, nvb); t < S.T; t += nvb * kWaves) {
-    topk_row(S.logits + (size_t)t * L.E, L.E, L.K, S.idx + (size_t)t * L.K, S.wts + (size_t)t * L.K);
-    if (topk_out != nullptr && lane_id() == 0)
-      for (int k = 0; k < L.K; ++k) topk_out[(size_t)t * L.K + k] = S.idx[(size_t)t * L.K + k];
+    topk_row(S.logits + (size_t)t * L.E, L.E, L.K, S.idx + (size_t)t * L.K, S.wts + (size_t)t * L.K,
+             topk_out ? topk_out + (size_t)t * L.K : nullptr);
   }
 }
 
