@@ -465,7 +465,9 @@ static hipError_t launch_dense(const StepArgs& S, const uint8_t* w0, const uint8
 template <int KDT, int D, int NW, int NPH = 1>
 static hipError_t launch_attn_mfma_t(const LayerArgs& L, const StepArgs& S, hipStream_t st) {
   const void* fn = reinterpret_cast<const void*>(&k_attn_mfma<KDT, D, NW, NPH>);
-  const size_t lds = align_up(sizeof(AttnPlan), 16) + MfmaGeom<KDT, D, NW, NPH>::LDS;
+  constexpr size_t item_lds = KDT == kE4M3 && D == 128 && NW == 4 ? (size_t)F8Geom<NPH>::LDS
+                                                                    : (size_t)MfmaGeom<KDT, D, NW, NPH>::LDS;
+  const size_t lds = align_up(sizeof(AttnPlan), 16) + item_lds;
   MSK_TRY(set_lds_limit(fn, lds));
   static int per_cu = 0;  // one value per instantiation
   if (per_cu == 0) {

@@ -398,12 +398,324 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
   if (ln < 16) part[D] = lsum;
 }
 
+// ------------------------------------------- e4m3 caches, head_dim 128
+// The cache bytes are matrix-core operands as they are: the score product
+// runs on v_mfma_scale_f32_16x16x128_f8f6f4 with K straight from a raw tile
+// (A: 16 positions x 128 dims, e4m3) and qhat as three e4m3 terms (B: 128
+// dims x 16 rows).  Each row of qhat is first multiplied by a power of two
+// that puts its largest magnitude in [128, 256); the terms are t1 = rne(x),
+// t2 = rne(x - t1), t3 = rne(x - t1 - t2), so a score carries about 2^-12
+// of its terms' magnitude (the fp8 subnormal step bounds the last term), and
+// the power of two comes back out with the exp2 argument.  The output
+// product stays on bf16 (V converted and transposed once per tile, weights
+// rounded once), as in attn_item_mfma.
+//
+// Raw tiles (64 positions x 128 B of K, then of V) land in a two-slot LDS
+// ring through direct global->LDS loads, the next tile issued as soon as the
+// slot it overwrites is released, so no register holds a tile in flight.  A
+// tile row's 16-B chunk c sits at chunk c ^ ((row >> 1) & 7) of the row:
+// the 16 rows of a score operand read then hit 16 distinct bank groups.
+template <int NPH>
+struct F8Geom {
+  static constexpr int D = 128, NW = 4;
+  static constexpr int RAW = 64 * D;                 // one raw K or V tile, bytes
+  static constexpr int SLOT = 2 * RAW;               // K then V
+  static constexpr int LDS_RING = 2 * SLOT;
+  static constexpr int VTS = 64 * 2 + 8;             // bf16 V^T row stride (as MfmaGeom)
+  static constexpr int LDS_VT = D * VTS;
+  static constexpr int LDS = LDS_RING + LDS_VT + kMaxTok * 4;
+  static constexpr int ROWS = 16 * NW / NPH, NPT = 4 / NPH, NKS = 2 / NPH, NDT = D / 16;
+};
+
+__device__ __forceinline__ int f8_slot(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+template <int NPH>
+__device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int item,
+                             uint8_t* wl) {
+  using Gm = F8Geom<NPH>;
+  constexpr int D = Gm::D, NW = Gm::NW, RB = D, CPR = D / 16, EPC = 16;
+  constexpr int VTS = Gm::VTS, NDT = Gm::NDT, ROWS = Gm::ROWS, NPT = Gm::NPT, NKS = Gm::NKS;
+  uint8_t* ring = wl;
+  uint8_t* vt = wl + Gm::LDS_RING;
+  float* rk = reinterpret_cast<float*>(vt + Gm::LDS_VT);
+
+  const int tid = threadIdx.x, ln = lane_id(), wv = wave_id();
+  const int rt = wv / NPH, ph = wv - (wv / NPH) * NPH;
+  int b = 0;
+  while (b + 1 < S.n_req && P->item0[b + 1] <= item) ++b;
+  const int nch = P->nch[b];
+  int rem = item - P->item0[b];
+  const int j = rem / (L.nrg * nch);
+  rem -= j * L.nrg * nch;
+  const int rg = rem / nch;
+  const int c = rem - rg * nch;
+  const int p0 = P->base[b] + c * L.chunk;
+  const int p1 = p0 + L.chunk < P->end[b] ? p0 + L.chunk : P->end[b];
+  const int Lb = S.kv_len[b];
+  const int G = L.Hq / L.Hkv;
+  const int M = G * S.Tr;
+  const int m0 = rg * ROWS;
+  const int NQ = L.Hq * L.D, NK = L.Hkv * L.D, NR = NQ + 2 * NK;
+  const size_t head_off = ((size_t)b * L.Hkv + j) * (size_t)L.cap;
+  uint8_t* kc = L.kc + head_off * RB;
+  uint8_t* vc = L.vc + head_off * RB;
+  const bool writer = (rg == 0);
+
+  const int mr = m0 + 16 * rt + (ln & 15);
+  const bool live = mr < M;
+  const int t_me = live ? mr / G : 0;
+  const int g_me = live ? mr - t_me * G : 0;
+  const int p_me = Lb + t_me;
+  const int w_lo = live ? (L.window > 0 ? (p_me - L.window + 1 > 0 ? p_me - L.window + 1 : 0) : 0)
+                        : 1;
+  const int w_hi = live ? p_me : 0;
+  const int t_first = m0 / G;
+  const int lo_min = L.window > 0 ? (Lb + t_first - L.window + 1 > 0 ? Lb + t_first - L.window + 1 : 0)
+                                  : 0;
+
+  // raw tile at positions [pb, pb + 64) into a ring slot: rows outside
+  // [vlo, vhi) are not loaded (the step's own rows are rebuilt below; the
+  // rest are masked)
+  auto issue = [&](int pb, uint8_t* slot) {
+    const int vlo = pb > lo_min ? pb : lo_min;
+    const int vhi = p1 < Lb ? p1 : Lb;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int blk = 2 * wv + u;               // 64-granule block of the tile
+      const int row = 8 * blk + (ln >> 3);
+      const int pos = pb + row;
+      const int cg = (ln & 7) ^ ((row >> 1) & 7);  // global chunk that goes to this slot
+      if (pos >= vlo && pos < vhi) {
+        const size_t off = (size_t)pos * RB + cg * 16;
+        __builtin_amdgcn_global_load_lds(kc + off, slot + blk * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vc + off, slot + Gm::RAW + blk * 1024, 16, 0, 0);
+      }
+    }
+  };
+  issue(p0, ring);
+
+  // qhat as three e4m3 terms, lane: row m = ln & 15, dims 32 (ln >> 4) + e
+  v8i qt[3];
+  float qinv;
+  {
+    const float* q = S.qkv + (size_t)(b * S.Tr + t_me) * NR + (size_t)(j * G + g_me) * D;
+    const int d0 = 32 * (ln >> 4);
+    float qf[32];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; e += 4) {
+      const v4f a = live ? *reinterpret_cast<const v4f*>(q + d0 + e) : v4f{0.f, 0.f, 0.f, 0.f};
+      qf[e] = a.x; qf[e + 1] = a.y; qf[e + 2] = a.z; qf[e + 3] = a.w;
+      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float rr = 1.0f / sqrtf(ss / (float)D + L.eps) * L.qscale * 1.44269504088896341f;
+    float mx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      qf[e] *= rr * L.q_norm[d0 + e];
+      mx = fmaxf(mx, fabsf(qf[e]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    int ex = 0;
+    frexpf(mx, &ex);  // mx < 2^ex
+    const float up = mx > 0.f ? ldexpf(1.f, 8 - ex) : 1.f;
+    qinv = mx > 0.f ? ldexpf(1.f, ex - 8) : 1.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) qf[e] *= up;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+#pragma unroll
+      for (int w4 = 0; w4 < 8; ++w4) {
+        const float* x = qf + 4 * w4;
+        const unsigned lo = f2e4m3x2(x[0], x[1]), hi = f2e4m3x2(x[2], x[3]);
+        qt[k][w4] = (int)(lo | (hi << 16));
+        float back[4];
+        e4m3x4(lo | (hi << 16), back);
+        qf[4 * w4] -= back[0]; qf[4 * w4 + 1] -= back[1];
+        qf[4 * w4 + 2] -= back[2]; qf[4 * w4 + 3] -= back[3];
+      }
+    }
+  }
+  int lo_all = live ? w_lo : 0, hi_all = live ? w_hi : 0x7fffffff;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    lo_all = max(lo_all, __shfl_xor(lo_all, o));
+    hi_all = min(hi_all, __shfl_xor(hi_all, o));
+  }
+  const float shift2 = L.shift * 1.44269504088896341f;
+  const int tn0 = p0 - Lb > 0 ? p0 - Lb : 0;
+  const int tn1 = p1 - Lb < S.Tr ? p1 - Lb : S.Tr;
+  for (int t = tn0 + wv; t < tn1; t += NW) {
+    const float* k = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + (size_t)j * D;
+    float ss = 0.f;
+    for (int d = ln; d < D; d += 64) ss += k[d] * k[d];
+    ss = wave_sum(ss);
+    if (ln == 0) rk[t] = 1.0f / sqrtf(ss / (float)D + L.eps);
+  }
+  auto new_chunk = [&](int pos, int cc, bool value) -> v4u {
+    const int t = pos - Lb;
+    const int d0 = cc * EPC;
+    const float* kq = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + (size_t)j * D + d0;
+    float f[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) f[e] = value ? kq[NK + e] : kq[e] * rk[t] * L.k_norm[d0 + e];
+    const v4u enc = encode16<kE4M3>(f);
+    if (writer) *reinterpret_cast<v4u*>((value ? vc : kc) + (size_t)pos * RB + cc * 16) = enc;
+    return enc;
+  };
+
+  f32x4 oacc[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;
+  __syncthreads();  // rk is written
+
+  int it = 0;
+  for (int pb = p0; pb < p1; pb += 64, ++it) {
+    uint8_t* slot = ring + (it & 1) * Gm::SLOT;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the tile have landed
+    lds_barrier();                       // every wave's, and the other slot and vt are free
+    if (pb + 64 < p1) issue(pb + 64, ring + ((it + 1) & 1) * Gm::SLOT);
+    // V -> vt[d][pos] (bf16), rows outside the loaded range as zeros
+    {
+      const int vlo = pb > lo_min ? pb : lo_min;
+      const int vhi = p1 < Lb ? p1 : Lb;
+      const int pp = tid & 31, cc = tid >> 5;
+      unsigned o[2][EPC / 2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 2 * pp + h;
+        const bool ok = pb + row >= vlo && pb + row < vhi;
+        v4u w = *reinterpret_cast<const v4u*>(slot + Gm::RAW + f8_slot(row, cc) * 16);
+        if (!ok) w = v4u{0u, 0u, 0u, 0u};
+        chunk_to_bf16<kE4M3>(w, o[h]);
+      }
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        *reinterpret_cast<unsigned*>(vt + (cc * EPC + e) * VTS + 4 * pp) =
+            __builtin_amdgcn_perm(o[1][e >> 1], o[0][e >> 1], sel);
+      }
+    }
+    // the step's own rows in this tile: K as cache bytes into the raw tile,
+    // V converted into vt
+    const int n0 = pb > Lb ? pb : Lb;
+    const int n1 = pb + 64 < p1 ? pb + 64 : p1;
+    if (n0 < n1) {
+      lds_barrier();  // vt's loaded rows are written before new rows replace theirs
+      const int nn = (n1 - n0) * CPR;
+      for (int q = tid; q < 2 * nn; q += NW * 64) {
+        const bool value = q >= nn;
+        const int qq = value ? q - nn : q;
+        const int pos = n0 + qq / CPR, cc = qq % CPR;
+        const v4u enc = new_chunk(pos, cc, value);
+        const int row = pos - pb;
+        if (!value) {
+          *reinterpret_cast<v4u*>(slot + f8_slot(row, cc) * 16) = enc;
+        } else {
+          unsigned o[EPC / 2];
+          chunk_to_bf16<kE4M3>(enc, o);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e)
+            *reinterpret_cast<unsigned short*>(vt + (cc * EPC + e) * VTS + 2 * row) =
+                (unsigned short)((e & 1) ? o[e >> 1] >> 16 : o[e >> 1] & 0xffffu);
+        }
+      }
+    }
+    lds_barrier();
+
+    if (m0 + 16 * rt >= M) continue;
+    f32x4 sacc[NPT];
+#pragma unroll
+    for (int pq = 0; pq < NPT; ++pq) {
+      const int pt = ph * NPT + pq;
+      const int row = 16 * pt + (ln & 15);
+      const v4u a0 = *reinterpret_cast<const v4u*>(slot + f8_slot(row, 2 * (ln >> 4)) * 16);
+      const v4u a1 = *reinterpret_cast<const v4u*>(slot + f8_slot(row, 2 * (ln >> 4) + 1) * 16);
+      const v8i a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                        (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      sacc[pq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        sacc[pq] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qt[k], sacc[pq], 0, 0, 0,
+                                                                    127, 0, 127);
+    }
+    const bool open = pb >= lo_all && pb + 63 <= hi_all && pb + 64 <= p1;
+    unsigned wh[NKS][4];
+#pragma unroll
+    for (int pq = 0; pq < NPT; ++pq) {
+      const int pt = ph * NPT + pq;
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e[i] = __builtin_amdgcn_exp2f(fmaf(sacc[pq][i], qinv, -shift2));
+        if (!open) {
+          const int pos = pb + 16 * pt + 4 * (ln >> 4) + i;
+          e[i] = (pos >= w_lo && pos <= w_hi && pos < p1) ? e[i] : 0.f;
+        }
+      }
+      const unsigned h0 = cvt_pk_bf16(e[0], e[1]), h1 = cvt_pk_bf16(e[2], e[3]);
+      wh[pq >> 1][2 * (pt & 1)] = h0;
+      wh[pq >> 1][2 * (pt & 1) + 1] = h1;
+      lsum += (bf16_lo(h0) + bf16_hi(h0)) + (bf16_lo(h1) + bf16_hi(h1));
+    }
+#pragma unroll
+    for (int kq = 0; kq < NKS; ++kq) {
+      const int ks = ph * NKS + kq;
+      const bf16x8 bh = as_bf16x8(v4u{wh[kq][0], wh[kq][1], wh[kq][2], wh[kq][3]});
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint8_t* src = vt + (16 * dt + (ln & 15)) * VTS + (32 * ks + 4 * (ln >> 4)) * 2;
+        const v2u x0 = *reinterpret_cast<const v2u*>(src);
+        const v2u x1 = *reinterpret_cast<const v2u*>(src + 32);
+        const bf16x8 a = as_bf16x8(v4u{x0.x, x0.y, x1.x, x1.y});
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, oacc[dt], 0, 0, 0);
+      }
+    }
+  }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if constexpr (NPH == 2) {
+    float* xs = reinterpret_cast<float*>(ring) + rt * (NDT * 4 + 1) * 64;
+    lds_barrier();
+    if (ph == 1) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[(dt * 4 + i) * 64 + ln] = oacc[dt][i];
+      xs[NDT * 4 * 64 + ln] = lsum;
+    }
+    lds_barrier();
+    if (ph == 1) return;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[dt][i] += xs[(dt * 4 + i) * 64 + ln];
+    lsum += xs[NDT * 4 * 64 + ln];
+  }
+  if (m0 + 16 * rt >= M) return;
+  float* part = S.part + ((size_t)item * ROWS + 16 * rt + (ln & 15)) * (D + 1);
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[16 * dt + 4 * (ln >> 4) + i] = oacc[dt][i];
+  if (ln < 16) part[D] = lsum;
+}
+
 template <int KDT, int D, int NW, int NPH>
 __device__ void phase_attn_mfma(const LayerArgs& L, const StepArgs& S, const AttnPlan* P,
                                 uint8_t* lds, int vb, int nvb) {
   const int n_items = P->item0[S.n_req];
   for (int item = vb; item < n_items; item += nvb) {
-    attn_item_mfma<KDT, D, NW, NPH>(L, S, P, item, lds);
+    if constexpr (KDT == kE4M3 && D == 128 && NW == 4)
+      attn_item_f8<NPH>(L, S, P, item, lds);
+    else
+      attn_item_mfma<KDT, D, NW, NPH>(L, S, P, item, lds);
     __syncthreads();
   }
 }
