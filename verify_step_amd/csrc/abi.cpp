@@ -39,6 +39,8 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 // Target number of attention work items (one wave each) per layer: about
 // two rounds of the waves that fit on the chip at once.
 constexpr long long kTargetItems = 2048;
+// Rounds of resident workgroups the matrix-core attention items fill.
+constexpr long long kAttnRounds = 1;
 
 struct AttnSplit {
   int chunk, n_items, nrg, rows, nw, nph;
@@ -76,22 +78,28 @@ AttnSplit plan_attention(const msk_layer_cfg& c, const msk_batch& b) {
     end = L + b.tokens_per_req;
     total += (long long)(end - base) * c.n_kv_heads * nrg;
   }
-  // matrix-core items: three full rounds of the 768 workgroups (three per CU
-  // on 256 CUs) that its e4m3 head_dim-128 form keeps resident, so the last
-  // round is not left part-empty
-  const long long target = mfma ? 3 * 768 : kTargetItems;
+  // matrix-core items: at most kAttnRounds rounds of the 768 workgroups
+  // (three per CU on 256 CUs) that its e4m3 head_dim-128 form keeps resident.
+  // Fewer, longer items mean fewer partials for the combine and less start-up
+  // per item; the chunk grows until every request's partial last chunk still
+  // fits, so no round is left with a handful of full-length items.
+  const long long target = mfma ? kAttnRounds * 768LL : kTargetItems;
+  auto count = [&](long long ch) {
+    long long n = 0;
+    for (int r = 0; r < b.n_req; ++r) {
+      const int L = b.kv_len_host[r], W = c.window;
+      const int lo = W > 0 ? (L - W + 1 > 0 ? L - W + 1 : 0) : 0;
+      const int base = lo & ~63, end = L + b.tokens_per_req;
+      n += (long long)cdiv(end - base, ch) * c.n_kv_heads * nrg;
+    }
+    return n;
+  };
   long long chunk = (total + target - 1) / target;
   chunk = (chunk + 63) / 64 * 64;
   if (chunk < 64) chunk = 64;
+  while (chunk < (1 << 20) && count(chunk) > target) chunk += 64;
   if (chunk > (1 << 20)) chunk = 1 << 20;
-  long long items = 0;
-  for (int r = 0; r < b.n_req; ++r) {
-    const int L = b.kv_len_host[r], W = c.window;
-    const int lo = W > 0 ? (L - W + 1 > 0 ? L - W + 1 : 0) : 0;
-    const int base = lo & ~63, end = L + b.tokens_per_req;
-    items += (long long)cdiv(end - base, chunk) * c.n_kv_heads * nrg;
-  }
-  return AttnSplit{(int)chunk, (int)items, nrg, rows, nw, nph};
+  return AttnSplit{(int)chunk, (int)count(chunk), nrg, rows, nw, nph};
 }
 
 struct Layout {

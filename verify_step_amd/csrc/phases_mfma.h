@@ -415,12 +415,15 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
 // slot it overwrites is released, so no register holds a tile in flight.  A
 // tile row's 16-B chunk c sits at chunk c ^ ((row >> 1) & 7) of the row:
 // the 16 rows of a score operand read then hit 16 distinct bank groups.
+constexpr int kF8Slots = 2;  // ring depth: tiles in flight + 1
+
 template <int NPH>
 struct F8Geom {
   static constexpr int D = 128, NW = 4;
   static constexpr int RAW = 64 * D;                 // one raw K or V tile, bytes
   static constexpr int SLOT = 2 * RAW;               // K then V
-  static constexpr int LDS_RING = 2 * SLOT;
+  static constexpr int NSLOT = kF8Slots;
+  static constexpr int LDS_RING = NSLOT * SLOT;
   static constexpr int VTS = 64 * 2 + 8;             // bf16 V^T row stride (as MfmaGeom)
   static constexpr int LDS_VT = D * VTS;
   static constexpr int LDS = LDS_RING + LDS_VT + kMaxTok * 4;
@@ -475,9 +478,10 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
   const int lo_min = L.window > 0 ? (Lb + t_first - L.window + 1 > 0 ? Lb + t_first - L.window + 1 : 0)
                                   : 0;
 
-  // raw tile at positions [pb, pb + 64) into a ring slot: rows outside
-  // [vlo, vhi) are not loaded (the step's own rows are rebuilt below; the
-  // rest are masked)
+  // raw tile at positions [pb, pb + 64) into a ring slot.  Every lane
+  // loads, so each wave has exactly 4 loads per tile in flight; a row
+  // outside [vlo, vhi) fetches the head's row 0 instead (the step's own rows
+  // are rebuilt below, the other ones are masked)
   auto issue = [&](int pb, uint8_t* slot) {
     const int vlo = pb > lo_min ? pb : lo_min;
     const int vhi = p1 < Lb ? p1 : Lb;
@@ -487,14 +491,14 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
       const int row = 8 * blk + (ln >> 3);
       const int pos = pb + row;
       const int cg = (ln & 7) ^ ((row >> 1) & 7);  // global chunk that goes to this slot
-      if (pos >= vlo && pos < vhi) {
-        const size_t off = (size_t)pos * RB + cg * 16;
-        __builtin_amdgcn_global_load_lds(kc + off, slot + blk * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vc + off, slot + Gm::RAW + blk * 1024, 16, 0, 0);
-      }
+      const size_t off = (size_t)(pos >= vlo && pos < vhi ? pos : 0) * RB + cg * 16;
+      __builtin_amdgcn_global_load_lds(kc + off, slot + blk * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vc + off, slot + Gm::RAW + blk * 1024, 16, 0, 0);
     }
   };
-  issue(p0, ring);
+#pragma unroll
+  for (int k = 0; k + 1 < Gm::NSLOT; ++k)
+    if (p0 + 64 * k < p1) issue(p0 + 64 * k, ring + k * Gm::SLOT);
 
   // qhat as three e4m3 terms, lane: row m = ln & 15, dims 32 (ln >> 4) + e
   v8i qt[3];
@@ -577,10 +581,21 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
 
   int it = 0;
   for (int pb = p0; pb < p1; pb += 64, ++it) {
-    uint8_t* slot = ring + (it & 1) * Gm::SLOT;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the tile have landed
-    lds_barrier();                       // every wave's, and the other slot and vt are free
-    if (pb + 64 < p1) issue(pb + 64, ring + ((it + 1) & 1) * Gm::SLOT);
+    uint8_t* slot = ring + (it % Gm::NSLOT) * Gm::SLOT;
+    // this wave's loads of the tile have landed (the later tiles' 4 loads
+    // each may still be in flight), then every wave's; the slot about to be
+    // refilled and vt are free
+    if constexpr (Gm::NSLOT == 3) {
+      if (pb + 64 < p1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+    lds_barrier();
+    {
+      const int ahead = pb + 64 * (Gm::NSLOT - 1);
+      if (ahead < p1) issue(ahead, ring + ((it + Gm::NSLOT - 1) % Gm::NSLOT) * Gm::SLOT);
+    }
     // V -> vt[d][pos] (bf16), rows outside the loaded range as zeros
     {
       const int vlo = pb > lo_min ? pb : lo_min;
