@@ -64,13 +64,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_gateup_tn(LayerArgs L, StepAr
   gateup_tn<DT, NVMAX>(L, S, S.uni, act, act + NVMAX * tn_vec_floats<DT>(L.H));
 }
 
-// bf16 down streams four slot vectors: held to four waves per SIMD (its
-// registers otherwise come out one over the limit for four)
-template <int DT> struct DownTnWaves { static constexpr int N = DT == kBF16 ? 4 : 1; };
-
 template <int DT, int NVMAX>
-__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(DownTnWaves<DT>::N)))
-void k_down_tn(LayerArgs L, StepArgs S) {
+__global__ __launch_bounds__(kBlockThreads) void k_down_tn(LayerArgs L, StepArgs S) {
   float* act = reinterpret_cast<float*>(msk_smem);
   down_tn<DT, NVMAX>(L, S, S.uni, act, act + NVMAX * tn_vec_floats<DT>(L.F), S.ybuf);
 }
@@ -120,6 +115,20 @@ __global__ __launch_bounds__(kBlockThreads) void k_router(LayerArgs L, StepArgs 
 
 __global__ __launch_bounds__(kBlockThreads) void k_topk(LayerArgs L, StepArgs S, int* topk_out) {
   phase_topk(L, S, topk_out, blockIdx.x, gridDim.x);
+}
+
+// Several tokens in one workgroup of up to 16 waves: the top-k of every
+// token (one wave each: a token's selection is a chain of dependent wave
+// reductions), then the expert union of the selection (what k_topk and
+// k_union do, in one launch).
+constexpr int kTopkUnionThreads = 1024;
+__global__ __launch_bounds__(kTopkUnionThreads) void k_topk_union(LayerArgs L, StepArgs S,
+                                                                  int* topk_out) {
+  for (int t = wave_id(); t < S.T; t += blockDim.x / 64)
+    topk_row(S.logits + (size_t)t * L.E, L.E, L.K, S.idx + (size_t)t * L.K,
+             S.wts + (size_t)t * L.K, topk_out ? topk_out + (size_t)t * L.K : nullptr);
+  __syncthreads();  // the selections are written before the union reads them
+  union_to_global(S.idx, S.T, L.K, L.E, reinterpret_cast<Union*>(msk_smem), S.uni);
 }
 
 
@@ -614,8 +623,10 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
     else
       MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhRouter, k_router<kF32, NV>, grid, rs_lds, st, L, S, h)))
   }
-  MSK_TRY(launch_x(kPhTopk, k_topk, grid_for_waves(S.T), 0, st, L, S, topk_out));
-  return hipSuccess;
+  // the expert union comes with the selection: the multi-token expert
+  // kernels read it (launch_ffn with union_ready)
+  const int waves = S.T < kTopkUnionThreads / 64 ? S.T : kTopkUnionThreads / 64;
+  return launch_b(kPhTopk, k_topk_union, 1, waves * 64, kUnionLds, st, L, S, topk_out);
 }
 
 template <int DT>
@@ -666,8 +677,8 @@ static hipError_t launch_experts_tn(const LayerArgs& L, const StepArgs& S, hipSt
 
 template <int DT>
 static hipError_t launch_ffn_tn(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
-                                hipStream_t st) {
-  MSK_TRY(launch_x(kPhUnion, k_union, 1, sizeof(Union), st, L, S));
+                                hipStream_t st, bool union_ready) {
+  if (!union_ready) MSK_TRY(launch_x(kPhUnion, k_union, 1, kUnionLds, st, L, S));
   MSK_TRY(launch_experts_tn<DT>(L, S, st));
   const long long n4 = (long long)S.T * L.H / 4;
   return launch_x(kPhMoeSum, k_moe_sum, (int)((n4 + kBlockThreads - 1) / kBlockThreads), 0, st,
@@ -675,7 +686,7 @@ static hipError_t launch_ffn_tn(const LayerArgs& L, const StepArgs& S, const flo
 }
 
 hipError_t launch_ffn(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
-                      hipStream_t st) {
+                      hipStream_t st, bool union_ready) {
   if (S.T == 1 && t1_act_lds(L) <= kMaxLds) {
     switch (L.edt) {
       case kF32: return launch_ffn_t1<kF32>(L, S, h, out, st);
@@ -684,9 +695,9 @@ hipError_t launch_ffn(const LayerArgs& L, const StepArgs& S, const float* h, flo
     }
   }
   switch (L.edt) {
-    case kF32: return launch_ffn_tn<kF32>(L, S, h, out, st);
-    case kBF16: return launch_ffn_tn<kBF16>(L, S, h, out, st);
-    default: return launch_ffn_tn<kNVFP4>(L, S, h, out, st);
+    case kF32: return launch_ffn_tn<kF32>(L, S, h, out, st, union_ready);
+    case kBF16: return launch_ffn_tn<kBF16>(L, S, h, out, st, union_ready);
+    default: return launch_ffn_tn<kNVFP4>(L, S, h, out, st, union_ready);
   }
 }
 
@@ -701,7 +712,7 @@ hipError_t launch_step_unfused(const LayerArgs* Ls, const StepArgs& S0, hipStrea
     S.win_out = S0.win_out ? S0.win_out + (size_t)l * S.T * 2 : nullptr;
     MSK_TRY(launch_attn(L, S, cur, S.h, st));
     MSK_TRY(launch_route(L, S, S.h, topk, st));
-    MSK_TRY(launch_ffn(L, S, S.h, nxt, st));
+    MSK_TRY(launch_ffn(L, S, S.h, nxt, st, /*union_ready=*/S.T > 1));
     if (S.layer_out)
       MSK_TRY(hipMemcpyAsync(S.layer_out + (size_t)l * S.T * L.H, nxt,
                              (size_t)S.T * L.H * sizeof(float), hipMemcpyDeviceToDevice, st));

@@ -15,7 +15,8 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
                         hipStream_t st);
 // Experts: out = h + MoE(u).
 hipError_t launch_ffn(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
-                      hipStream_t st);
+                      hipStream_t st,
+                      bool union_ready = false);
 // Whole step over S.n_layers layers as one persistent cooperative kernel.
 hipError_t launch_step_fused(const LayerArgs* Ls, const StepArgs& S, hipStream_t st);
 // Whole step as a sequence of per-phase kernels (the unfused comparison path).

@@ -629,12 +629,13 @@ __device__ void phase_topk(const LayerArgs& L, const StepArgs& S, int* topk_out,
 // (t * K + j) routed to it in ascending order.  Built identically by every
 // workgroup from idx.
 
-__device__ inline void build_union(const int* idx, int T, int K, int E, Union* U) {
+__device__ inline void build_union(const int* idx, int T, int K, int E, Union* U, int* sidx) {
   const int S = T * K;
   for (int e = threadIdx.x; e < E; e += blockDim.x) U->start[e] = 0;
   __syncthreads();
   for (int s = threadIdx.x; s < S; s += blockDim.x) {
     const int e = idx[s];
+    sidx[s] = e;  // the selection in LDS: the ranks below read it many times
     if (e >= 0 && e < E) atomicAdd(&U->start[e], 1);
   }
   __syncthreads();
@@ -672,10 +673,10 @@ __device__ inline void build_union(const int* idx, int T, int K, int E, Union* U
   }
   __syncthreads();
   for (int s = threadIdx.x; s < S; s += blockDim.x) {
-    const int e = idx[s];
+    const int e = sidx[s];
     if (e < 0 || e >= E) continue;
     int rank = 0;
-    for (int q = 0; q < s; ++q) rank += idx[q] == e;
+    for (int q = 0; q < s; ++q) rank += sidx[q] == e;
     U->slots[U->start[e] + rank] = s;
   }
   __syncthreads();

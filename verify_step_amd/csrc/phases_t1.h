@@ -146,7 +146,7 @@ __device__ void router_t1(const LayerArgs& L, const StepArgs& S, const float* h,
 // Top-k of one token's logits by one wave (value descending, index ascending
 // on ties); idx/w written by lane 0, weights = softmax over the selected.
 // Each round takes the wave-wide maximum, then the lowest index holding it.
-__device__ inline void topk_row(const float* logits, int E, int K, int* idx, float* w,
+__device__ __forceinline__ void topk_row(const float* logits, int E, int K, int* idx, float* w,
                                 int* idx2 = nullptr) {
   const int ln = lane_id();
   float v[4];
@@ -159,9 +159,13 @@ __device__ inline void topk_row(const float* logits, int E, int K, int* idx, flo
     open[i] = e < E;
   }
   float v0 = 0.f, den = 0.f;
+  float exs[kMaxTopK];  // kept in registers: the weights are written once,
+  int bis[kMaxTopK];    // normalised, with no read-back of global memory
 #pragma unroll
   for (int k = 0; k < kMaxTopK; ++k) {
-    if (k >= K) break;
+    exs[k] = 0.f;
+    bis[k] = 0;
+    if (k >= K) continue;
     float lm = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -179,15 +183,19 @@ __device__ inline void topk_row(const float* logits, int E, int K, int* idx, flo
     if (k == 0) v0 = m;
     const float ex = __expf(m - v0);
     den += ex;
-    if (ln == 0) {
-      idx[k] = bi;
-      w[k] = ex;
-      if (idx2) idx2[k] = bi;  // the caller's copy, from the register (no re-read)
-    }
+    exs[k] = ex;
+    bis[k] = bi;
   }
   if (ln == 0) {
     const float inv = 1.0f / den;
-    for (int k = 0; k < K; ++k) w[k] *= inv;
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+      if (k < K) {
+        idx[k] = bis[k];
+        w[k] = exs[k] * inv;
+        if (idx2) idx2[k] = bis[k];  // the caller's copy
+      }
+    }
   }
 }
 

@@ -255,8 +255,11 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
 }
 
 // The union into global memory (one workgroup).
+// lds: a Union followed by kUnionIdxInts ints of scratch.
+constexpr int kUnionIdxInts = kMaxTok * kMaxTopK;
+constexpr size_t kUnionLds = sizeof(Union) + kUnionIdxInts * sizeof(int);
 __device__ inline void union_to_global(const int* idx, int T, int K, int E, Union* lds, Union* dst) {
-  build_union(idx, T, K, E, lds);
+  build_union(idx, T, K, E, lds, reinterpret_cast<int*>(lds + 1));
   const int* s = reinterpret_cast<const int*>(lds);
   int* d = reinterpret_cast<int*>(dst);
   for (int i = threadIdx.x; i < (int)(sizeof(Union) / 4); i += blockDim.x) d[i] = s[i];
