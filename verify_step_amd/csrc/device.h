@@ -329,8 +329,15 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
   // value before compute needs it, and compute has no branch on the chunk:
   // otherwise the compiler's waits for the loads in flight become
   // conservative and drain the second buffer at every step.
-  auto issue = [&](v4u(&w)[U][R], unsigned(&s)[U][R], int f) {
-    const int k = f / NI, i = f - (f / NI) * NI;
+  // step f of the stream is (task k, chunk group i); cursors move step by
+  // step with scalar adds (no division per step)
+  struct At { int k, i; };
+  auto next = [&](At a) -> At {
+    if (++a.i == NI) { a.i = 0; ++a.k; }
+    return a;
+  };
+  auto issue = [&](v4u(&w)[U][R], unsigned(&s)[U][R], At at) {
+    const int k = at.k, i = at.i;
     const uint8_t* wr[R];
     const uint8_t* sr[R];
     rowfn(k, wr, sr);
@@ -349,8 +356,8 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
       }
     }
   };
-  auto compute = [&](const v4u(&w)[U][R], const unsigned(&s)[U][R], int f) {
-    const int k = f / NI, i = f - (f / NI) * NI;
+  auto compute = [&](const v4u(&w)[U][R], const unsigned(&s)[U][R], At at) {
+    const int k = at.k, i = at.i;
     const float* act = actfn(k);
     const uint8_t* sr[R];  // NVFP4: the scale rows again, for their alignment
     if constexpr (DT == kNVFP4) {
@@ -404,27 +411,32 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
   // twice).  The loop issues both refills on every iteration and the last
   // steps are peeled off, so the loop holds no conditional load.
   const int last = total - 1;
+  At c0{0, 0}, c1 = next(c0);
   if (total > 0) {
-    issue(A, sA, 0);
+    issue(A, sA, c0);
     __builtin_amdgcn_sched_barrier(0);
-    issue(B, sB, 1 < last ? 1 : last);
+    issue(B, sB, 1 <= last ? c1 : c0);
     __builtin_amdgcn_sched_barrier(0);
   }
   pre();
   int f = 0;
   // steady state: both refills are real steps
   for (; f + 3 < total; f += 2) {
-    compute(A, sA, f);
-    issue(A, sA, f + 2);
-    compute(B, sB, f + 1);
-    issue(B, sB, f + 3);
+    const At c2 = next(c1), c3 = next(c2);
+    compute(A, sA, c0);
+    issue(A, sA, c2);
+    compute(B, sB, c1);
+    issue(B, sB, c3);
+    c0 = c2;
+    c1 = c3;
   }
   // the last one to three steps: A holds step f, B step f + 1
   if (f < total) {
-    compute(A, sA, f);
-    if (f + 2 < total) issue(A, sA, f + 2);
-    if (f + 1 < total) compute(B, sB, f + 1);
-    if (f + 2 < total) compute(A, sA, f + 2);
+    const At c2 = next(c1);
+    compute(A, sA, c0);
+    if (f + 2 < total) issue(A, sA, c2);
+    if (f + 1 < total) compute(B, sB, c1);
+    if (f + 2 < total) compute(A, sA, c2);
   }
 }
 

@@ -112,8 +112,15 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
 #pragma unroll
     for (int v = 0; v < NV; ++v) acc[r][v] = 0.f;
 
-  auto issue = [&](v4u(&w)[U][R], unsigned(&s)[U][R], int f) {
-    const int k = f / NI, i = f - (f / NI) * NI;
+  // step f of the stream is (task k, chunk group i); cursors move step by
+  // step with scalar adds (no division per step)
+  struct At { int k, i; };
+  auto next = [&](At a) -> At {
+    if (++a.i == NI) { a.i = 0; ++a.k; }
+    return a;
+  };
+  auto issue = [&](v4u(&w)[U][R], unsigned(&s)[U][R], At at) {
+    const int k = at.k, i = at.i;
     const uint8_t* wr[R];
     const uint8_t* sr[R];
     rowfn(k, wr, sr);
@@ -140,8 +147,8 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
       }
     }
   };
-  auto compute = [&](const v4u(&w)[U][R], const unsigned(&s)[U][R], int f) {
-    const int k = f / NI, i = f - (f / NI) * NI;
+  auto compute = [&](const v4u(&w)[U][R], const unsigned(&s)[U][R], At at) {
+    const int k = at.k, i = at.i;
     const uint8_t* sr[R];  // NVFP4: the scale rows again, for their alignment
     if constexpr (DT == kNVFP4) {
       const uint8_t* wr[R];
@@ -237,20 +244,25 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
   // last step's addresses, unused), so the loop holds no conditional load;
   // peeling the last steps off instead costs registers (and occupancy) here
   const int last = total - 1;
+  const At at_last{last / NI, last - (last / NI) * NI};
+  At c0{0, 0}, c1 = next(c0);
   if (total > 0) {
     // all of A's loads ahead of all of B's, as inside the loop: the
     // compiler's waits at the loop head hold for the entry path too
-    issue(A, sA, 0);
+    issue(A, sA, c0);
     __builtin_amdgcn_sched_barrier(0);
-    issue(B, sB, 1 < last ? 1 : last);
+    issue(B, sB, 1 <= last ? c1 : at_last);
     __builtin_amdgcn_sched_barrier(0);
   }
   pre();
   for (int f = 0; f < total; f += 2) {
-    compute(A, sA, f);
-    issue(A, sA, f + 2 < last ? f + 2 : last);
-    if (f + 1 < total) compute(B, sB, f + 1);
-    issue(B, sB, f + 3 < last ? f + 3 : last);
+    const At c2 = next(c1), c3 = next(c2);
+    compute(A, sA, c0);
+    issue(A, sA, f + 2 <= last ? c2 : at_last);
+    if (f + 1 < total) compute(B, sB, c1);
+    issue(B, sB, f + 3 <= last ? c3 : at_last);
+    c0 = c2;
+    c1 = c3;
   }
 }
 
