@@ -185,10 +185,40 @@ __global__ __launch_bounds__(kBlockThreads) void k_router_t1(LayerArgs L, StepAr
 }
 
 template <int DT>
-__global__ __launch_bounds__(kBlockThreads) void k_gateup_t1(LayerArgs L, StepArgs S) {
+__global__ __launch_bounds__(kBlockThreads) void k_gateup_t1(LayerArgs L, StepArgs S,
+                                                             int* topk_out, int own_topk) {
   const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
   float* u = reinterpret_cast<float*>(msk_smem + o.act0);
-  gateup_t1<DT>(L, S, S.idx, u, blockIdx.x, gridDim.x, [&]() { stage_copy(S.u, L.H, u); });
+  if (own_topk) {
+    // every wave selects the experts itself from the router logits (into
+    // scalar registers: no launch, no barrier); workgroup 0 records them
+    int sel[kMaxTopK];
+    float ex[kMaxTopK], den;
+    topk_regs(S.logits, L.E, L.K, sel, ex, den);
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) sel[k] = __builtin_amdgcn_readfirstlane(sel[k]);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      const float inv = 1.0f / den;
+#pragma unroll
+      for (int k = 0; k < kMaxTopK; ++k)
+        if (k < L.K) {
+          S.idx[k] = sel[k];
+          S.wts[k] = ex[k] * inv;
+          if (topk_out) topk_out[k] = sel[k];
+        }
+    }
+    // lane k of one vector register holds the k-th id; a wave-uniform slot
+    // index then reads it back with one cross-lane read (no private array)
+    const int lane = threadIdx.x & 63;
+    int selv = sel[0];
+#pragma unroll
+    for (int k = 1; k < kMaxTopK; ++k) selv = lane == k ? sel[k] : selv;
+    auto pick = [selv](int j) { return __builtin_amdgcn_readlane(selv, j); };
+    gateup_t1<DT>(L, S, pick, u, blockIdx.x, gridDim.x, [&]() { stage_copy(S.u, L.H, u); });
+  } else {
+    gateup_t1<DT>(L, S, [&](int j) { return S.idx[j]; }, u, blockIdx.x, gridDim.x,
+                  [&]() { stage_copy(S.u, L.H, u); });
+  }
 }
 
 template <int DT>
@@ -263,7 +293,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_step_t1(StepLayers PK) {
       S.wts[threadIdx.x] = tkw[threadIdx.x];
       if (S.topk_out) S.topk_out[(size_t)l * L.K + threadIdx.x] = tki[threadIdx.x];
     }
-    gateup_t1<EDT>(L, S, tki, act0, vb, nvb, []() {});
+    gateup_t1<EDT>(L, S, [&](int j) { return tki[j]; }, act0, vb, nvb, []() {});
     stamp();
     grid_sync(gs);
 
@@ -594,7 +624,7 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
 }
 
 hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, int* topk_out,
-                        hipStream_t st) {
+                        hipStream_t st, bool defer_topk) {
   const size_t rs_lds = (size_t)S.T * sizeof(float);
   const int nv = dense_nv(S.T);
   const int rows = (L.E + DenseRowsHost(nv) - 1) / DenseRowsHost(nv);
@@ -609,9 +639,11 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
       MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_router_t1<kF32>), lds));
       MSK_TRY(launch_x(kPhRouter, k_router_t1<kF32>, g, lds, st, L, S, h));
     }
-    // top-k in a kernel of its own: finding the last router workgroup in
-    // the router kernel costs every workgroup an agent-scope acquire and
-    // release, which here means L2 writeback and invalidate
+    // top-k outside the router kernel: finding the last router workgroup
+    // costs every workgroup an agent-scope acquire and release, which here
+    // means L2 writeback and invalidate.  Within a layer step the one-token
+    // gate/up kernel selects the experts itself (defer_topk).
+    if (defer_topk) return hipSuccess;
     return launch_x(kPhTopk, k_topk, 1, 0, st, L, S, topk_out);
   } else if (dense_on_mfma(L, S, L.E, L.H)) {
     MSK_TRY(launch_x(kPhPrep, k_prep_act, S.T, kWaves * sizeof(float), st, h, L.ffn_norm, S.T, L.H, L.eps, S.u, S.a3));
@@ -631,10 +663,11 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
 
 template <int DT>
 static hipError_t launch_ffn_t1(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
-                                hipStream_t st) {
+                                hipStream_t st, bool own_topk, int* topk_out) {
   const size_t vlds = t1_vec_lds(L), alds = 256 + (size_t)4 * L.K * L.F;
   MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_gateup_t1<DT>), vlds));
-  MSK_TRY(launch(kPhGateUp, k_gateup_t1<DT>, t1_grid((long long)L.K * (L.F / 2)), vlds, st, L, S));
+  MSK_TRY(launch_x(kPhGateUp, k_gateup_t1<DT>, t1_grid((long long)L.K * (L.F / 2)), vlds, st, L, S,
+                   topk_out, (int)own_topk));
   MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_down_t1<DT>), alds));
   MSK_TRY(launch_x(kPhDown, k_down_t1<DT>, t1_grid((L.H + 3) / 4), alds, st, L, S, h, out));
   return hipSuccess;
@@ -685,13 +718,17 @@ static hipError_t launch_ffn_tn(const LayerArgs& L, const StepArgs& S, const flo
                   L, S, h, out);
 }
 
+bool ffn_one_token(const LayerArgs& L, const StepArgs& S) {
+  return S.T == 1 && t1_act_lds(L) <= kMaxLds;
+}
+
 hipError_t launch_ffn(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
-                      hipStream_t st, bool union_ready) {
-  if (S.T == 1 && t1_act_lds(L) <= kMaxLds) {
+                      hipStream_t st, bool union_ready, bool own_topk, int* topk_out) {
+  if (ffn_one_token(L, S)) {
     switch (L.edt) {
-      case kF32: return launch_ffn_t1<kF32>(L, S, h, out, st);
-      case kBF16: return launch_ffn_t1<kBF16>(L, S, h, out, st);
-      default: return launch_ffn_t1<kNVFP4>(L, S, h, out, st);
+      case kF32: return launch_ffn_t1<kF32>(L, S, h, out, st, own_topk, topk_out);
+      case kBF16: return launch_ffn_t1<kBF16>(L, S, h, out, st, own_topk, topk_out);
+      default: return launch_ffn_t1<kNVFP4>(L, S, h, out, st, own_topk, topk_out);
     }
   }
   switch (L.edt) {
@@ -710,9 +747,12 @@ hipError_t launch_step_unfused(const LayerArgs* Ls, const StepArgs& S0, hipStrea
     float* nxt = (l == S.n_layers - 1) ? S.x_out : ((l & 1) ? S.xb : S.xa);
     int* topk = S0.topk_out ? S0.topk_out + (size_t)l * S.T * L.K : nullptr;
     S.win_out = S0.win_out ? S0.win_out + (size_t)l * S.T * 2 : nullptr;
+    // one token: the gate/up kernel takes the top-k; several: the router's
+    // top-k kernel also builds the expert union
+    const bool own = ffn_one_token(L, S);
     MSK_TRY(launch_attn(L, S, cur, S.h, st));
-    MSK_TRY(launch_route(L, S, S.h, topk, st));
-    MSK_TRY(launch_ffn(L, S, S.h, nxt, st, /*union_ready=*/S.T > 1));
+    MSK_TRY(launch_route(L, S, S.h, topk, st, /*defer_topk=*/own));
+    MSK_TRY(launch_ffn(L, S, S.h, nxt, st, /*union_ready=*/S.T > 1, own, topk));
     if (S.layer_out)
       MSK_TRY(hipMemcpyAsync(S.layer_out + (size_t)l * S.T * L.H, nxt,
                              (size_t)S.T * L.H * sizeof(float), hipMemcpyDeviceToDevice, st));

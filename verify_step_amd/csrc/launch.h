@@ -12,11 +12,13 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
                        hipStream_t st);
 // Router: u, logits, top-k indices and weights.
 hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, int* topk_out,
-                        hipStream_t st);
+                        hipStream_t st, bool defer_topk = false);
 // Experts: out = h + MoE(u).
 hipError_t launch_ffn(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
-                      hipStream_t st,
-                      bool union_ready = false);
+                      hipStream_t st, bool union_ready = false, bool own_topk = false,
+                      int* topk_out = nullptr);
+// The expert phase of S's tokens runs the one-token kernels.
+bool ffn_one_token(const LayerArgs& L, const StepArgs& S);
 // Whole step over S.n_layers layers as one persistent cooperative kernel.
 hipError_t launch_step_fused(const LayerArgs* Ls, const StepArgs& S, hipStream_t st);
 // Whole step as a sequence of per-phase kernels (the unfused comparison path).

@@ -144,10 +144,12 @@ __device__ void router_t1(const LayerArgs& L, const StepArgs& S, const float* h,
 }
 
 // Top-k of one token's logits by one wave (value descending, index ascending
-// on ties); idx/w written by lane 0, weights = softmax over the selected.
-// Each round takes the wave-wide maximum, then the lowest index holding it.
-__device__ __forceinline__ void topk_row(const float* logits, int E, int K, int* idx, float* w,
-                                int* idx2 = nullptr) {
+// on ties) into registers (uniform over the wave): bis[k] the experts,
+// exs[k] / den their softmax weights.  Each round takes the wave-wide
+// maximum, then the lowest index holding it.
+__device__ __forceinline__ void topk_regs(const float* logits, int E, int K,
+                                          int (&bis)[kMaxTopK], float (&exs)[kMaxTopK],
+                                          float& den) {
   const int ln = lane_id();
   float v[4];
   bool open[4];  // still selectable
@@ -158,9 +160,8 @@ __device__ __forceinline__ void topk_row(const float* logits, int E, int K, int*
     v[i] = (x == x) ? x : -INFINITY;  // NaN never wins
     open[i] = e < E;
   }
-  float v0 = 0.f, den = 0.f;
-  float exs[kMaxTopK];  // kept in registers: the weights are written once,
-  int bis[kMaxTopK];    // normalised, with no read-back of global memory
+  float v0 = 0.f;
+  den = 0.f;
 #pragma unroll
   for (int k = 0; k < kMaxTopK; ++k) {
     exs[k] = 0.f;
@@ -186,14 +187,23 @@ __device__ __forceinline__ void topk_row(const float* logits, int E, int K, int*
     exs[k] = ex;
     bis[k] = bi;
   }
-  if (ln == 0) {
+}
+
+// The same, written out by lane 0: idx, w = softmax over the selected, and
+// the caller's copy idx2 when given.
+__device__ __forceinline__ void topk_row(const float* logits, int E, int K, int* idx, float* w,
+                                int* idx2 = nullptr) {
+  int bis[kMaxTopK];
+  float exs[kMaxTopK], den;
+  topk_regs(logits, E, K, bis, exs, den);
+  if (lane_id() == 0) {
     const float inv = 1.0f / den;
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
       if (k < K) {
         idx[k] = bis[k];
         w[k] = exs[k] * inv;
-        if (idx2) idx2[k] = bis[k];  // the caller's copy
+        if (idx2) idx2[k] = bis[k];
       }
     }
   }
@@ -223,8 +233,8 @@ __device__ inline bool last_workgroup(unsigned* counter, int* flag_lds) {
 }
 
 // act[j][f] = silu(gate_e[f] . u) * (up_e[f] . u), e = idx[j]; u staged in LDS.
-template <int DT, class Pre>
-__device__ void gateup_t1(const LayerArgs& L, const StepArgs& S, const int* idx, const float* u,
+template <int DT, class Sel, class Pre>
+__device__ void gateup_t1(const LayerArgs& L, const StepArgs& S, Sel&& idx, const float* u,
                           int vb, int nvb, Pre&& pre) {
   constexpr int R = 2, U = 2;
   const int nrb = L.F / R;
@@ -236,7 +246,7 @@ __device__ void gateup_t1(const LayerArgs& L, const StepArgs& S, const int* idx,
       n, L.H, [&](int) { return u; },
       [&](int k, auto& wr, auto& sr) {
         const int t = gw + k * nw, j = t / nrb, f0 = (t - j * nrb) * R;
-        int e = idx[j];
+        int e = idx(j);
         e = e >= 0 && e < L.E ? e : 0;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -249,7 +259,7 @@ __device__ void gateup_t1(const LayerArgs& L, const StepArgs& S, const int* idx,
       },
       [&](int k, auto& acc) {
         const int t = gw + k * nw, j = t / nrb, f0 = (t - j * nrb) * R;
-        int e = idx[j];
+        int e = idx(j);
         e = e >= 0 && e < L.E ? e : 0;
         const float gs = DT == kNVFP4 ? L.gg[e] : 1.f, us = DT == kNVFP4 ? L.gu[e] : 1.f;
         float res[R];
