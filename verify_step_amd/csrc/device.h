@@ -308,9 +308,12 @@ __device__ __forceinline__ void wave_gemv(const uint8_t* const (&wrow)[R],
 // dotted with one fp32 vector in LDS (actfn(k)).  The weight stream is
 // software-pipelined two buffers deep across row ends and task ends, and the
 // input vector comes from LDS, so no cache load ever waits behind a weight
-// load.  out(k, acc) receives the sums (in every lane); pre() runs once, in
-// every wave, after the first loads are issued.
-template <int DT, int R, int U, class ActFn, class RowFn, class OutFn, class PreFn>
+// load.  out(k, acc) receives the sums (in every lane), or with LANE each
+// lane's partial sum, for a caller that combines tasks linearly before one
+// wave reduction; pre() runs once, in every wave, after the first loads are
+// issued.
+template <int DT, int R, int U, bool LANE = false, class ActFn, class RowFn, class OutFn,
+          class PreFn>
 __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, RowFn&& rowfn,
                                           OutFn&& out, PreFn&& pre) {
   using W = WT<DT>;
@@ -397,8 +400,10 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
       }
     }
     if (i == NI - 1) {
+      if constexpr (!LANE) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+        for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+      }
       out(k, acc);
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[r] = 0.f;

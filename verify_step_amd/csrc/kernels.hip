@@ -89,6 +89,23 @@ __global__ __launch_bounds__(kBlockThreads) void k_prep_act(const float* x, cons
   prep_act(x, g, T, H, eps, a32, a3, reinterpret_cast<float*>(msk_smem));
 }
 
+constexpr int kSumPrepThreads = 1024;
+__global__ __launch_bounds__(kSumPrepThreads) void k_sum_prep(const float* part, int ks,
+                                                              const float* resid, float* h,
+                                                              const float* g, int T, int H,
+                                                              float eps, float* a32,
+                                                              unsigned short* a3) {
+  float* red = reinterpret_cast<float*>(msk_smem);
+  sum_prep_act(part, ks, resid, h, g, T, H, eps, a32, a3, red + 16, red);
+}
+
+__global__ __launch_bounds__(kSumPrepThreads) void k_moe_sum_prep(LayerArgs L, StepArgs S,
+                                                                  const float* h, float* out,
+                                                                  const float* g, float eps) {
+  float* red = reinterpret_cast<float*>(msk_smem);
+  down_combine_prep(L, S, h, S.ybuf, out, g, eps, S.a3, red + 16, red);
+}
+
 template <int CT>
 __global__ __launch_bounds__(kBlockThreads) void k_dense_mfma(DenseArgs A) {
   dense_mfma<CT>(A, msk_smem);
@@ -117,18 +134,75 @@ __global__ __launch_bounds__(kBlockThreads) void k_topk(LayerArgs L, StepArgs S,
   phase_topk(L, S, topk_out, blockIdx.x, gridDim.x);
 }
 
-// Several tokens in one workgroup of up to 16 waves: the top-k of every
-// token (one wave each: a token's selection is a chain of dependent wave
-// reductions), then the expert union of the selection (what k_topk and
-// k_union do, in one launch).
+// Several tokens' routing in one workgroup of up to 16 waves: the router
+// logits (summed here, in slice order, from the dense product's split-K
+// partial tiles when ks > 1, and written out), each token's top-k by one
+// wave (a selection is a chain of dependent wave reductions), then the
+// expert union from the selections kept in LDS (what k_topk and k_union do,
+// in one launch).
 constexpr int kTopkUnionThreads = 1024;
 __global__ __launch_bounds__(kTopkUnionThreads) void k_topk_union(LayerArgs L, StepArgs S,
-                                                                  int* topk_out) {
-  for (int t = wave_id(); t < S.T; t += blockDim.x / 64)
-    topk_row(S.logits + (size_t)t * L.E, L.E, L.K, S.idx + (size_t)t * L.K,
-             S.wts + (size_t)t * L.K, topk_out ? topk_out + (size_t)t * L.K : nullptr);
-  __syncthreads();  // the selections are written before the union reads them
-  union_to_global(S.idx, S.T, L.K, L.E, reinterpret_cast<Union*>(msk_smem), S.uni);
+                                                                  int* topk_out, const float* part,
+                                                                  int ks) {
+  Union* U = reinterpret_cast<Union*>(msk_smem);
+  int* sel = reinterpret_cast<int*>(U + 1);  // [T][K]
+  const int ln = lane_id();
+  for (int t = wave_id(); t < S.T; t += blockDim.x / 64) {
+    // lane: experts e_i = ln + 64 i; every load is issued before any sum
+    // (addresses clamped into range, results past E unused)
+    float x[4];
+    float* lg = S.logits + (size_t)t * L.E;
+    if (ks > 1) {
+      float a[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int q0 = 0; q0 < ks; q0 += 16) {
+        float v[4][16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = ln + 64 * i < L.E ? ln + 64 * i : L.E - 1;
+          // partial tile of row block e / 64, slice q: [q][T][64] within the block
+          const float* src = part + ((size_t)(e >> 6) * ks * S.T + t) * 64 + (e & 63);
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            v[i][q] = src[(size_t)(q0 + q < ks ? q0 + q : ks - 1) * S.T * 64];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            if (q0 + q < ks) a[i] += v[i][q];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = ln + 64 * i;
+        if (e < L.E) lg[e] = a[i];
+        x[i] = e < L.E ? a[i] : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = ln + 64 * i;
+        const float v = lg[e < L.E ? e : L.E - 1];
+        x[i] = e < L.E ? v : -INFINITY;
+      }
+    }
+    int bis[kMaxTopK];
+    float exs[kMaxTopK], den;
+    topk_vals(x, L.E, L.K, bis, exs, den);
+    if (ln == 0) {
+      const float inv = 1.0f / den;
+#pragma unroll
+      for (int k = 0; k < kMaxTopK; ++k)
+        if (k < L.K) {
+          const size_t o = (size_t)t * L.K + k;
+          S.idx[o] = bis[k];
+          S.wts[o] = exs[k] * inv;
+          if (topk_out) topk_out[o] = bis[k];
+          sel[o] = bis[k];
+        }
+    }
+  }
+  __syncthreads();  // every token's selection is in LDS
+  union_to_global(sel, S.T, L.K, L.E, U, S.uni);
 }
 
 
@@ -216,8 +290,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_gateup_t1(LayerArgs L, StepAr
     auto pick = [selv](int j) { return __builtin_amdgcn_readlane(selv, j); };
     gateup_t1<DT>(L, S, pick, u, blockIdx.x, gridDim.x, [&]() { stage_copy(S.u, L.H, u); });
   } else {
-    gateup_t1<DT>(L, S, [&](int j) { return S.idx[j]; }, u, blockIdx.x, gridDim.x,
-                  [&]() { stage_copy(S.u, L.H, u); });
+    const int selv = (threadIdx.x & 63) < L.K ? S.idx[threadIdx.x & 63] : 0;
+    gateup_t1<DT>(L, S, [selv](int j) { return __builtin_amdgcn_readlane(selv, j); }, u,
+                  blockIdx.x, gridDim.x, [&]() { stage_copy(S.u, L.H, u); });
   }
 }
 
@@ -478,9 +553,12 @@ static hipError_t launch_dense_t(const DenseArgs& A, int ph, hipStream_t st) {
 }
 
 // out = resid + W a for the three (QKV) or one weight segments.
+// keep_parts: with K split into several slices the partial tiles are left
+// in S.dpart for the consumer to sum (dense_slices(N, K) of them).
 static hipError_t launch_dense(const StepArgs& S, const uint8_t* w0, const uint8_t* w1,
                                const uint8_t* w2, int seg1, int seg2, int N, int K,
-                               const float* resid, float* out, int ph, hipStream_t st) {
+                               const float* resid, float* out, int ph, hipStream_t st,
+                               bool keep_parts = false) {
   DenseArgs A;
   A.w[0] = w0; A.w[1] = w1 ? w1 : w0; A.w[2] = w2 ? w2 : w0;
   A.seg[0] = 0; A.seg[1] = seg1; A.seg[2] = seg2;
@@ -493,7 +571,7 @@ static hipError_t launch_dense(const StepArgs& S, const uint8_t* w0, const uint8
     case 3: MSK_TRY(launch_dense_t<3>(A, ph, st)); break;
     default: MSK_TRY(launch_dense_t<4>(A, ph, st)); break;
   }
-  if (A.ks == 1) return hipSuccess;
+  if (A.ks == 1 || keep_parts) return hipSuccess;
   const long long n = (long long)S.T * N;
   return launch_x(kPhDenseSum, k_dense_sum, (int)((n + kBlockThreads - 1) / kBlockThreads), 0,
                   st, (const float*)S.dpart, N, S.T, A.ks, resid, out);
@@ -568,8 +646,16 @@ static hipError_t launch_attn_kernel(const LayerArgs& L, const StepArgs& S, hipS
   return hipErrorInvalidValue;
 }
 
+bool wo_sum_in_route(const LayerArgs& L, const StepArgs& S) {
+  return dense_on_mfma(L, S, L.H, L.Hq * L.D) && dense_on_mfma(L, S, L.E, L.H);
+}
+
+bool qkv_on_mfma(const LayerArgs& L, const StepArgs& S) {
+  return dense_on_mfma(L, S, (L.Hq + 2 * L.Hkv) * L.D, L.H);
+}
+
 hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, float* h,
-                       hipStream_t st) {
+                       hipStream_t st, bool wo_parts, bool a3_ready) {
   const int NR = (L.Hq + 2 * L.Hkv) * L.D;
   const size_t rs_lds = (size_t)S.T * sizeof(float);
   const int nv = dense_nv(S.T);
@@ -586,8 +672,9 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
       MSK_TRY(launch_x(kPhQkv, k_qkv_t1<kF32>, g, lds, st, L, S, x));
     }
   } else if (dense_on_mfma(L, S, NR, L.H)) {
-    MSK_TRY(launch_x(kPhPrep, k_prep_act, S.T, kWaves * sizeof(float), st, x, L.attn_norm, S.T, L.H, L.eps,
-                     (float*)nullptr, S.a3));
+    if (!a3_ready)
+      MSK_TRY(launch_x(kPhPrep, k_prep_act, S.T, kWaves * sizeof(float), st, x, L.attn_norm, S.T,
+                       L.H, L.eps, (float*)nullptr, S.a3));
     const int NQ = L.Hq * L.D, NK = L.Hkv * L.D;
     MSK_TRY(launch_dense(S, L.wq, L.wk, L.wv, NQ, NQ + NK, NR, L.H, nullptr, S.qkv, kPhQkv, st));
   } else {
@@ -613,7 +700,8 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
       MSK_TRY(launch_x(kPhWo, k_wo_t1<kF32>, g, lds, st, L, S, x, h));
     }
   } else if (mm) {
-    MSK_TRY(launch_dense(S, L.wo, nullptr, nullptr, 0, 0, L.H, L.Hq * L.D, x, h, kPhWo, st));
+    MSK_TRY(launch_dense(S, L.wo, nullptr, nullptr, 0, 0, L.H, L.Hq * L.D, x, h, kPhWo, st,
+                         wo_parts && wo_sum_in_route(L, S)));
   } else {
     if (L.ddt == kBF16)
       MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhWo, k_wo<kBF16, NV>, wgrid, 0, st, L, S, x, h)))
@@ -624,11 +712,12 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
 }
 
 hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, int* topk_out,
-                        hipStream_t st, bool defer_topk) {
+                        hipStream_t st, bool defer_topk, const float* wo_resid) {
   const size_t rs_lds = (size_t)S.T * sizeof(float);
   const int nv = dense_nv(S.T);
   const int rows = (L.E + DenseRowsHost(nv) - 1) / DenseRowsHost(nv);
   const int grid = grid_for_waves(rows > 64 ? rows : 64);
+  int ks = 1;  // split-K slices of the logits left for the top-k kernel to sum
   if (S.T == 1) {
     const size_t lds = t1_vec_lds(L) + (size_t)kWaves * kRouterRows * sizeof(float);
     const int g = L.E < cu_count() ? L.E : cu_count();
@@ -646,9 +735,20 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
     if (defer_topk) return hipSuccess;
     return launch_x(kPhTopk, k_topk, 1, 0, st, L, S, topk_out);
   } else if (dense_on_mfma(L, S, L.E, L.H)) {
-    MSK_TRY(launch_x(kPhPrep, k_prep_act, S.T, kWaves * sizeof(float), st, h, L.ffn_norm, S.T, L.H, L.eps, S.u, S.a3));
+    if (wo_resid != nullptr && wo_sum_in_route(L, S)) {
+      // h = x + the Wo partial tiles, then the router's input, in one pass
+      const size_t lds = (16 + (size_t)L.H) * sizeof(float);
+      MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_sum_prep), lds));
+      MSK_TRY(launch_b(kPhPrep, k_sum_prep, S.T, kSumPrepThreads, lds, st, (const float*)S.dpart,
+                       dense_slices(L.H, L.Hq * L.D), wo_resid, S.h, L.ffn_norm, S.T, L.H, L.eps,
+                       S.u, S.a3));
+    } else {
+      MSK_TRY(launch_x(kPhPrep, k_prep_act, S.T, kWaves * sizeof(float), st, h, L.ffn_norm, S.T,
+                       L.H, L.eps, S.u, S.a3));
+    }
     MSK_TRY(launch_dense(S, L.wr, nullptr, nullptr, 0, 0, L.E, L.H, nullptr, S.logits, kPhRouter,
-                         st));
+                         st, /*keep_parts=*/true));
+    ks = dense_slices(L.E, L.H);
   } else {
     if (L.ddt == kBF16)
       MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhRouter, k_router<kBF16, NV>, grid, rs_lds, st, L, S, h)))
@@ -658,7 +758,8 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
   // the expert union comes with the selection: the multi-token expert
   // kernels read it (launch_ffn with union_ready)
   const int waves = S.T < kTopkUnionThreads / 64 ? S.T : kTopkUnionThreads / 64;
-  return launch_b(kPhTopk, k_topk_union, 1, waves * 64, kUnionLds, st, L, S, topk_out);
+  return launch_b(kPhTopk, k_topk_union, 1, waves * 64, kUnionLds, st, L, S, topk_out,
+                  (const float*)S.dpart, ks);
 }
 
 template <int DT>
@@ -710,9 +811,17 @@ static hipError_t launch_experts_tn(const LayerArgs& L, const StepArgs& S, hipSt
 
 template <int DT>
 static hipError_t launch_ffn_tn(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
-                                hipStream_t st, bool union_ready) {
+                                hipStream_t st, bool union_ready, const float* next_norm,
+                                float next_eps) {
   if (!union_ready) MSK_TRY(launch_x(kPhUnion, k_union, 1, kUnionLds, st, L, S));
   MSK_TRY(launch_experts_tn<DT>(L, S, st));
+  if (next_norm != nullptr) {
+    // the sum and the next layer's QKV input terms in one pass per token
+    const size_t lds = (16 + (size_t)L.H) * sizeof(float);
+    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_moe_sum_prep), lds));
+    return launch_b(kPhMoeSum, k_moe_sum_prep, S.T, kSumPrepThreads, lds, st, L, S, h, out,
+                    next_norm, next_eps);
+  }
   const long long n4 = (long long)S.T * L.H / 4;
   return launch_x(kPhMoeSum, k_moe_sum, (int)((n4 + kBlockThreads - 1) / kBlockThreads), 0, st,
                   L, S, h, out);
@@ -723,7 +832,8 @@ bool ffn_one_token(const LayerArgs& L, const StepArgs& S) {
 }
 
 hipError_t launch_ffn(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
-                      hipStream_t st, bool union_ready, bool own_topk, int* topk_out) {
+                      hipStream_t st, bool union_ready, bool own_topk, int* topk_out,
+                      const float* next_norm, float next_eps) {
   if (ffn_one_token(L, S)) {
     switch (L.edt) {
       case kF32: return launch_ffn_t1<kF32>(L, S, h, out, st, own_topk, topk_out);
@@ -732,9 +842,9 @@ hipError_t launch_ffn(const LayerArgs& L, const StepArgs& S, const float* h, flo
     }
   }
   switch (L.edt) {
-    case kF32: return launch_ffn_tn<kF32>(L, S, h, out, st, union_ready);
-    case kBF16: return launch_ffn_tn<kBF16>(L, S, h, out, st, union_ready);
-    default: return launch_ffn_tn<kNVFP4>(L, S, h, out, st, union_ready);
+    case kF32: return launch_ffn_tn<kF32>(L, S, h, out, st, union_ready, next_norm, next_eps);
+    case kBF16: return launch_ffn_tn<kBF16>(L, S, h, out, st, union_ready, next_norm, next_eps);
+    default: return launch_ffn_tn<kNVFP4>(L, S, h, out, st, union_ready, next_norm, next_eps);
   }
 }
 
@@ -742,6 +852,7 @@ hipError_t launch_ffn(const LayerArgs& L, const StepArgs& S, const float* h, flo
 hipError_t launch_step_unfused(const LayerArgs* Ls, const StepArgs& S0, hipStream_t st) {
   StepArgs S = S0;
   const float* cur = S.x_in;
+  bool a3_ready = false;  // this layer's QKV input terms came with the previous layer's sum
   for (int l = 0; l < S.n_layers; ++l) {
     const LayerArgs& L = Ls[l];
     float* nxt = (l == S.n_layers - 1) ? S.x_out : ((l & 1) ? S.xb : S.xa);
@@ -750,9 +861,15 @@ hipError_t launch_step_unfused(const LayerArgs* Ls, const StepArgs& S0, hipStrea
     // one token: the gate/up kernel takes the top-k; several: the router's
     // top-k kernel also builds the expert union
     const bool own = ffn_one_token(L, S);
-    MSK_TRY(launch_attn(L, S, cur, S.h, st));
-    MSK_TRY(launch_route(L, S, S.h, topk, st, /*defer_topk=*/own));
-    MSK_TRY(launch_ffn(L, S, S.h, nxt, st, /*union_ready=*/S.T > 1, own, topk));
+    // several tokens: the Wo partial sums join the router's input pass
+    const bool wsr = wo_sum_in_route(L, S);
+    MSK_TRY(launch_attn(L, S, cur, S.h, st, /*wo_parts=*/wsr, a3_ready));
+    MSK_TRY(launch_route(L, S, S.h, topk, st, /*defer_topk=*/own, wsr ? cur : nullptr));
+    // several tokens: the expert sum also prepares the next layer's QKV input
+    const bool pre = l + 1 < S.n_layers && !own && qkv_on_mfma(Ls[l + 1], S);
+    MSK_TRY(launch_ffn(L, S, S.h, nxt, st, /*union_ready=*/S.T > 1, own, topk,
+                       pre ? Ls[l + 1].attn_norm : nullptr, pre ? Ls[l + 1].eps : 0.f));
+    a3_ready = pre;
     if (S.layer_out)
       MSK_TRY(hipMemcpyAsync(S.layer_out + (size_t)l * S.T * L.H, nxt,
                              (size_t)S.T * L.H * sizeof(float), hipMemcpyDeviceToDevice, st));

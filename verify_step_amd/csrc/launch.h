@@ -8,15 +8,29 @@
 namespace msk {
 
 // Attention half: QKV, attention partials, combine, Wo (+ residual).
+// wo_parts: a Wo product split over K leaves its partial tiles for the
+// router launch to sum (launch_route with wo_resid = x).
+// a3_ready: the QKV product's input terms are in S.a3 already (written by
+// the previous layer's expert sum, launch_ffn with next_norm).
 hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, float* h,
-                       hipStream_t st);
-// Router: u, logits, top-k indices and weights.
+                       hipStream_t st, bool wo_parts = false, bool a3_ready = false);
+// Router: u, logits, top-k indices and weights.  wo_resid: h = wo_resid +
+// the Wo partial tiles left by launch_attn(wo_parts) is formed here first.
 hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, int* topk_out,
-                        hipStream_t st, bool defer_topk = false);
-// Experts: out = h + MoE(u).
+                        hipStream_t st, bool defer_topk = false,
+                        const float* wo_resid = nullptr);
+// Several tokens with bf16 Wo and router products on the matrix cores: the
+// Wo partial sums can go to the router's input preparation.
+bool wo_sum_in_route(const LayerArgs& L, const StepArgs& S);
+// Experts: out = h + MoE(u).  next_norm (several tokens only): also write
+// the next layer's QKV input terms of out (RMSNorm with gain next_norm and
+// next_eps) into S.a3.
 hipError_t launch_ffn(const LayerArgs& L, const StepArgs& S, const float* h, float* out,
                       hipStream_t st, bool union_ready = false, bool own_topk = false,
-                      int* topk_out = nullptr);
+                      int* topk_out = nullptr, const float* next_norm = nullptr,
+                      float next_eps = 0.f);
+// Several tokens with a bf16 QKV product on the matrix cores.
+bool qkv_on_mfma(const LayerArgs& L, const StepArgs& S);
 // The expert phase of S's tokens runs the one-token kernels.
 bool ffn_one_token(const LayerArgs& L, const StepArgs& S);
 // Whole step over S.n_layers layers as one persistent cooperative kernel.

@@ -71,6 +71,126 @@ __device__ inline void prep_act(const float* x, const float* g, int T, int H, fl
   }
 }
 
+// src[0] + src[stride] + ... + src[(n - 1) stride] (four consecutive
+// floats each), added in that order, with up to 8 loads in flight at once (a
+// plain loop would wait for each load before issuing the next).
+__device__ __forceinline__ v4f sum_slices4(const float* src, size_t stride, int n) {
+  v4f a = {0.f, 0.f, 0.f, 0.f};
+  for (int q0 = 0; q0 < n; q0 += 8) {
+    v4f v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      v[q] = *reinterpret_cast<const v4f*>(src + (size_t)(q0 + q < n ? q0 + q : n - 1) * stride);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q0 + q < n) {
+        a.x += v[q].x; a.y += v[q].y; a.z += v[q].z; a.w += v[q].w;
+      }
+  }
+  return a;
+}
+
+// Sum over every wave of the workgroup (any size up to 16 waves); every
+// thread gets the total.  red: 16 floats of LDS.
+__device__ __forceinline__ float wg_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int nw = blockDim.x / 64;
+  __syncthreads();
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < nw; ++w) t += red[w];
+  return t;
+}
+
+// One workgroup per token t: h[t] = resid[t] + (the partial tiles of a
+// split-K dense product summed in slice order, as dense_sum does), written
+// out, then a = h[t] * g / sqrt(mean(h[t]^2) + eps) as prep_act writes it.
+// ks <= 1: h is complete already and is only read.  hl: H floats of LDS,
+// red: 16 floats of LDS.
+__device__ inline void sum_prep_act(const float* part, int ks, const float* resid, float* h,
+                                    const float* g, int T, int H, float eps, float* a32,
+                                    unsigned short* a3, float* hl, float* red) {
+  const int t = blockIdx.x;
+  float* hr = h + (size_t)t * H;
+  float s = 0.f;
+  for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
+    v4f v;
+    if (ks > 1) {
+      // four consecutive rows of one 64-row block
+      const v4f a = sum_slices4(part + ((size_t)(c >> 6) * ks * T + t) * 64 + (c & 63),
+                                (size_t)T * 64, ks);
+      const v4f r0 = resid ? *reinterpret_cast<const v4f*>(resid + (size_t)t * H + c)
+                           : v4f{0.f, 0.f, 0.f, 0.f};
+      v = v4f{r0.x + a.x, r0.y + a.y, r0.z + a.z, r0.w + a.w};
+      *reinterpret_cast<v4f*>(hr + c) = v;
+    } else {
+      v = *reinterpret_cast<const v4f*>(hr + c);
+    }
+    *reinterpret_cast<v4f*>(hl + c) = v;
+    s += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  const float r = 1.0f / sqrtf(wg_sum(s, red) / (float)H + eps);  // also orders hl
+  const size_t plane = (size_t)T * H;
+  for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = hl[c + e] * r * g[c + e];
+    if (a32) {
+      *reinterpret_cast<v4f*>(a32 + (size_t)t * H + c) = v4f{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<v4f*>(a32 + (size_t)t * H + c + 4) = v4f{v[4], v[5], v[6], v[7]};
+    }
+    store_split8(a3, plane, (size_t)t * H + c, v);
+  }
+}
+
+// One workgroup per token t: out[t] as down_combine forms it, then the next
+// layer's QKV input terms from it: a3 = bf16 terms of out[t] * g /
+// sqrt(mean(out[t]^2) + eps) (store_split8, as prep_act writes them).
+// ol: H floats of LDS, red: 16 floats of LDS.
+__device__ inline void down_combine_prep(const LayerArgs& L, const StepArgs& S, const float* h,
+                                         const float* y, float* out, const float* g, float eps,
+                                         unsigned short* a3, float* ol, float* red) {
+  const int t = blockIdx.x, H = L.H;
+  float s2 = 0.f;
+  for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
+    v4f acc = *reinterpret_cast<const v4f*>(h + (size_t)t * H + c);
+    // eight slots' loads in flight at once; a slot whose expert id is out of
+    // range adds nothing (its y is not used)
+    for (int j0 = 0; j0 < L.K; j0 += 8) {
+      v4f yy[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = j0 + q < L.K ? j0 + q : L.K - 1;
+        yy[q] = *reinterpret_cast<const v4f*>(y + ((size_t)t * L.K + j) * H + c);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int s = t * L.K + j0 + q;
+        if (j0 + q >= L.K) break;
+        const int e = S.idx[s];
+        if (e < 0 || e >= L.E) continue;
+        const float w = S.wts[s];
+        acc.x = fmaf(w, yy[q].x, acc.x);
+        acc.y = fmaf(w, yy[q].y, acc.y);
+        acc.z = fmaf(w, yy[q].z, acc.z);
+        acc.w = fmaf(w, yy[q].w, acc.w);
+      }
+    }
+    *reinterpret_cast<v4f*>(out + (size_t)t * H + c) = acc;
+    *reinterpret_cast<v4f*>(ol + c) = acc;
+    s2 += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
+  }
+  const float r = 1.0f / sqrtf(wg_sum(s2, red) / (float)H + eps);  // also orders ol
+  const size_t plane = (size_t)S.T * H;
+  for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = ol[c + e] * r * g[c + e];
+    store_split8(a3, plane, (size_t)t * H + c, v);
+  }
+}
+
 // Per 128-column k-tile the weights of a wave's 16 rows (16 x 256 B) and the
 // workgroup's activation terms (3 planes x 16 CT tokens x 256 B) are fetched
 // with direct global->LDS loads, double buffered.  A load instruction moves

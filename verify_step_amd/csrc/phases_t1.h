@@ -145,9 +145,10 @@ __device__ void router_t1(const LayerArgs& L, const StepArgs& S, const float* h,
 
 // Top-k of one token's logits by one wave (value descending, index ascending
 // on ties) into registers (uniform over the wave): bis[k] the experts,
-// exs[k] / den their softmax weights.  Each round takes the wave-wide
-// maximum, then the lowest index holding it.
-__device__ __forceinline__ void topk_regs(const float* logits, int E, int K,
+// exs[k] / den their softmax weights.  Lane l holds the logits of experts
+// l + 64 i in x[i] (i < 4; entries at E or beyond are ignored).  Each round
+// takes the wave-wide maximum, then the lowest index holding it.
+__device__ __forceinline__ void topk_vals(const float (&x)[4], int E, int K,
                                           int (&bis)[kMaxTopK], float (&exs)[kMaxTopK],
                                           float& den) {
   const int ln = lane_id();
@@ -156,8 +157,7 @@ __device__ __forceinline__ void topk_regs(const float* logits, int E, int K,
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = ln + 64 * i;
-    const float x = e < E ? logits[e] : -INFINITY;
-    v[i] = (x == x) ? x : -INFINITY;  // NaN never wins
+    v[i] = (e < E && x[i] == x[i]) ? x[i] : -INFINITY;  // NaN never wins
     open[i] = e < E;
   }
   float v0 = 0.f;
@@ -187,6 +187,20 @@ __device__ __forceinline__ void topk_regs(const float* logits, int E, int K,
     exs[k] = ex;
     bis[k] = bi;
   }
+}
+
+// The same with the logits read from memory.
+__device__ __forceinline__ void topk_regs(const float* logits, int E, int K,
+                                          int (&bis)[kMaxTopK], float (&exs)[kMaxTopK],
+                                          float& den) {
+  const int ln = lane_id();
+  float x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = ln + 64 * i;
+    x[i] = e < E ? logits[e] : -INFINITY;
+  }
+  topk_vals(x, E, K, bis, exs, den);
 }
 
 // The same, written out by lane 0: idx, w = softmax over the selected, and
@@ -272,6 +286,8 @@ __device__ void gateup_t1(const LayerArgs& L, const StepArgs& S, Sel&& idx, cons
 
 // out[c] = h[c] + sum_j w[j] * (down_e[c] . act[j]), e = idx[j], in slot order;
 // act staged in LDS as [K][F].  Entries of idx outside [0, E) add nothing.
+// Each lane folds the weighted partial sums of the K experts of a row block
+// together and the wave reduces once per row block.
 template <int DT, class Pre>
 __device__ void down_t1(const LayerArgs& L, const StepArgs& S, const int* idx, const float* wts,
                         const float* act, const float* h, float* out, float* out2, int vb,
@@ -282,14 +298,31 @@ __device__ void down_t1(const LayerArgs& L, const StepArgs& S, const int* idx, c
   const int gw = gwave(vb, nvb), nw = nvb * kWaves;
   const int K = L.K;
   const int nrb = my_count(gw, nw, (L.H + R - 1) / R);
+  // lane j holds slot j's expert; a wave-uniform slot reads it back with one
+  // cross-lane read
+  const int ev = lane_id() < K ? idx[lane_id()] : -1;
+  // task k = (row block b, slot j): b = k / K by a multiply-high, exact for
+  // k < 2^32 / K (K = 1 would need the multiplier 2^32)
+  const unsigned mK = 0xffffffffu / (unsigned)K + 1u;
+  auto split = [&](int k, int& b, int& j) {
+    b = K == 1 ? k : (int)__umulhi((unsigned)k, mK);
+    j = k - b * K;
+  };
   float o[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) o[r] = 0.f;
-  stream_t1<DT, R, U>(
-      nrb * K, L.F, [&](int k) { return act + (size_t)(k - (k / K) * K) * L.F; },
+  stream_t1<DT, R, U, true>(
+      nrb * K, L.F,
+      [&](int k) {
+        int b, j;
+        split(k, b, j);
+        return act + (size_t)j * L.F;
+      },
       [&](int k, auto& wr, auto& sr) {
-        const int j = k - (k / K) * K, r0 = (gw + (k / K) * nw) * R;
-        int e = idx[j];
+        int b, j;
+        split(k, b, j);
+        const int r0 = (gw + b * nw) * R;
+        int e = __builtin_amdgcn_readlane(ev, j);
         e = e >= 0 && e < L.E ? e : 0;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -300,13 +333,17 @@ __device__ void down_t1(const LayerArgs& L, const StepArgs& S, const int* idx, c
         }
       },
       [&](int k, auto& acc) {
-        const int j = k - (k / K) * K, r0 = (gw + (k / K) * nw) * R;
-        const int e = idx[j];
+        int b, j;
+        split(k, b, j);
+        const int r0 = (gw + b * nw) * R;
+        const int e = __builtin_amdgcn_readlane(ev, j);
         const bool ok = e >= 0 && e < L.E;
         const float s = ok ? wts[j] * (DT == kNVFP4 ? L.gd[e] : 1.f) : 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) o[r] = fmaf(s, acc[r], o[r]);
         if (j == K - 1) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) o[r] = wave_sum(o[r]);
           lane_store<R>(o, [&](int r, float v) {
             const int c = r0 + r;
             if (c < L.H) {
