@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_combine(LayerArgs L, StepArgs
                                                            unsigned short* a3) {
   AttnPlan* P = reinterpret_cast<AttnPlan*>(msk_smem);
   build_plan(L, S, P);
-  phase_combine(L, S, P, win, blockIdx.x, gridDim.x, a3);
+  phase_combine(L, S, P, win, blockIdx.x, gridDim.x,
+                reinterpret_cast<float*>(msk_smem + align_up(sizeof(AttnPlan), 16)), a3);
 }
 
 // Matrix-core dense projections of several tokens and their input terms.
@@ -348,7 +349,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_step_t1(StepLayers PK) {
     phase_attn<KDT, D>(L, S, P, msk_smem + o.attn + align_up(sizeof(AttnPlan), 16), vb, nvb);
     stamp();
     grid_sync(gs);
-    phase_combine(L, S, P, S.win_out ? S.win_out + (size_t)l * 2 * S.T : nullptr, vb, nvb);
+    phase_combine(L, S, P, S.win_out ? S.win_out + (size_t)l * 2 * S.T : nullptr, vb, nvb,
+                  reinterpret_cast<float*>(msk_smem + o.attn + align_up(sizeof(AttnPlan), 16)));
     stamp();
     grid_sync(gs);
 
@@ -686,8 +688,12 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
 
   MSK_TRY(launch_attn_kernel(L, S, st));
   const bool mm = dense_on_mfma(L, S, L.H, L.Hq * L.D);
-  MSK_TRY(launch_x(kPhCombine, k_combine, grid_for_waves((long long)S.T * L.Hq), sizeof(AttnPlan),
-                   st, L, S, S.win_out, mm ? S.a3 : nullptr));
+  {
+    const size_t lds = align_up(sizeof(AttnPlan), 16) + (size_t)kWaves * (L.D + 1) * sizeof(float);
+    const int rows = S.T * L.Hq;  // one workgroup per (token, q head)
+    MSK_TRY(launch_x(kPhCombine, k_combine, rows < 8192 ? rows : 8192, lds, st, L, S, S.win_out,
+                     mm ? S.a3 : nullptr));
+  }
   const int wgrid = grid_for_waves(L.H / DenseRowsHost(nv));
   if (one) {
     const size_t lds = t1_vec_lds(L);

@@ -49,19 +49,29 @@ struct AttnPlan {
 };
 
 __device__ inline void build_plan(const LayerArgs& L, const StepArgs& S, AttnPlan* P) {
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int b = 0; b < S.n_req; ++b) {
-      int base, end;
+  // lane b plans request b (at most 64 requests): one load for all of them,
+  // item offsets by a prefix sum over the lanes
+  if (threadIdx.x < 64) {
+    const int b = threadIdx.x;
+    int base = 0, end = 0, n = 0;
+    if (b < S.n_req) {
       req_span(S.kv_len[b], S.Tr, L.window, base, end);
-      const int n = ceil_div(end - base, L.chunk);
+      n = ceil_div(end - base, L.chunk);
+    }
+    const int cnt = n * L.Hkv * L.nrg;
+    int inc = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int a = __shfl_up(inc, off, 64);
+      if (b >= off) inc += a;
+    }
+    if (b < S.n_req) {
       P->base[b] = base;
       P->end[b] = end;
       P->nch[b] = n;
-      P->item0[b] = acc;
-      acc += n * L.Hkv * L.nrg;
+      P->item0[b] = inc - cnt;
     }
-    P->item0[S.n_req] = acc;
+    if (b == (S.n_req > 0 ? S.n_req - 1 : 0)) P->item0[S.n_req] = S.n_req > 0 ? inc : 0;
   }
   __syncthreads();
 }
@@ -480,13 +490,18 @@ __device__ void phase_attn(const LayerArgs& L, const StepArgs& S, const AttnPlan
 }
 
 // ---------------------------------------------------------- combine
-// attn_o[t][h] = sum_chunks o / sum_chunks l (plain sums, fixed order).
+// attn_o[t][h] = sum_chunks o / sum_chunks l.  One workgroup per row (token,
+// q head): wave w adds the chunks w, w + kWaves, ... (sixteen chunks' loads
+// in flight), then wave 0 adds the waves' sums in wave order.  red: LDS of
+// kWaves * (D + 1) floats.
 __device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int* win_out,
-                              int vb, int nvb, unsigned short* a3 = nullptr) {
+                              int vb, int nvb, float* red, unsigned short* a3 = nullptr) {
   const int D = L.D, G = L.Hq / L.Hkv;
   const int rows = S.T * L.Hq;
-  const int ln = lane_id();
-  for (int row = gwave(vb, nvb); row < rows; row += nvb * kWaves) {
+  const int ln = lane_id(), w = wave_id();
+  // dims ln and ln + 64 (a lane past D loads dim 0 and never stores)
+  const int d0 = ln < D ? ln : 0, d1 = ln + 64 < D ? ln + 64 : 0;
+  for (int row = vb; row < rows; row += nvb) {
     const int tok = row / L.Hq, hh = row - (row / L.Hq) * L.Hq;
     const int b = tok / S.Tr, tt = tok - (tok / S.Tr) * S.Tr;
     const int j = hh / G, g = hh - (hh / G) * G;
@@ -496,45 +511,57 @@ __device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnP
     const float* base = S.part + (size_t)it0 * L.rg_rows * (D + 1) + mm * (D + 1);
     const size_t stride = (size_t)L.rg_rows * (D + 1);
     float l = 0.f, o0 = 0.f, o1 = 0.f;
-    int c = 0;
-    for (; c + 16 <= nch; c += 16) {  // sixteen chunks' loads in flight
+    for (int c0 = w; c0 < nch; c0 += 16 * kWaves) {
       float pl[16], p0[16], p1[16];
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const float* p = base + (c + q) * stride;
+        const int c = c0 + q * kWaves;
+        const float* p = base + (size_t)(c < nch ? c : c0) * stride;
         pl[q] = p[D];
-        p0[q] = ln < D ? p[ln] : 0.f;
-        p1[q] = ln + 64 < D ? p[ln + 64] : 0.f;
+        p0[q] = p[d0];
+        p1[q] = p[d1];
       }
 #pragma unroll
-      for (int q = 0; q < 16; ++q) { l += pl[q]; o0 += p0[q]; o1 += p1[q]; }
+      for (int q = 0; q < 16; ++q)
+        if (c0 + q * kWaves < nch) { l += pl[q]; o0 += p0[q]; o1 += p1[q]; }
     }
-    for (; c < nch; ++c) {
-      const float* p = base + c * stride;
-      l += p[D];
-      if (ln < D) o0 += p[ln];
-      if (ln + 64 < D) o1 += p[ln + 64];
-    }
-    const size_t at = (size_t)tok * L.Hq * D + (size_t)hh * D;
-    const float v0 = o0 / l, v1 = o1 / l;
-    if (ln < D) S.attn_o[at + ln] = v0;
-    if (ln + 64 < D) S.attn_o[at + ln + 64] = v1;
-    if (a3 != nullptr) {  // bf16 terms of the output projection's input
-      const size_t plane = (size_t)S.T * L.Hq * D;
-      unsigned h, m, lo;
-      if (ln < D) {
-        split3_bf16(v0, h, m, lo);
-        a3[at + ln] = (unsigned short)h;
-        a3[plane + at + ln] = (unsigned short)m;
-        a3[2 * plane + at + ln] = (unsigned short)lo;
+    float* rw = red + w * (D + 1);
+    if (ln < D) rw[ln] = o0;
+    if (ln + 64 < D) rw[ln + 64] = o1;
+    if (ln == 0) rw[D] = l;
+    __syncthreads();
+    if (w == 0) {
+      l = red[D];
+      o0 = ln < D ? red[ln] : 0.f;
+      o1 = ln + 64 < D ? red[ln + 64] : 0.f;
+      for (int q = 1; q < kWaves; ++q) {
+        const float* rq = red + q * (D + 1);
+        l += rq[D];
+        if (ln < D) o0 += rq[ln];
+        if (ln + 64 < D) o1 += rq[ln + 64];
       }
-      if (ln + 64 < D) {
-        split3_bf16(v1, h, m, lo);
-        a3[at + ln + 64] = (unsigned short)h;
-        a3[plane + at + ln + 64] = (unsigned short)m;
-        a3[2 * plane + at + ln + 64] = (unsigned short)lo;
+      const size_t at = (size_t)tok * L.Hq * D + (size_t)hh * D;
+      const float v0 = o0 / l, v1 = o1 / l;
+      if (ln < D) S.attn_o[at + ln] = v0;
+      if (ln + 64 < D) S.attn_o[at + ln + 64] = v1;
+      if (a3 != nullptr) {  // bf16 terms of the output projection's input
+        const size_t plane = (size_t)S.T * L.Hq * D;
+        unsigned h, m, lo;
+        if (ln < D) {
+          split3_bf16(v0, h, m, lo);
+          a3[at + ln] = (unsigned short)h;
+          a3[plane + at + ln] = (unsigned short)m;
+          a3[2 * plane + at + ln] = (unsigned short)lo;
+        }
+        if (ln + 64 < D) {
+          split3_bf16(v1, h, m, lo);
+          a3[at + ln + 64] = (unsigned short)h;
+          a3[plane + at + ln + 64] = (unsigned short)m;
+          a3[2 * plane + at + ln + 64] = (unsigned short)lo;
+        }
       }
     }
+    __syncthreads();  // red is reused by the next row
   }
   if (win_out != nullptr && vb == 0) {
     for (int tok = threadIdx.x; tok < S.T; tok += blockDim.x) {
