@@ -656,6 +656,7 @@ __device__ void phase_topk(const LayerArgs& L, const StepArgs& S, int* topk_out,
 // (t * K + j) routed to it in ascending order.  Built identically by every
 // workgroup from idx.
 
+// sidx: LDS for T * K + 16 ints, 8-byte aligned.
 __device__ inline void build_union(const int* idx, int T, int K, int E, Union* U, int* sidx) {
   const int S = T * K;
   for (int e = threadIdx.x; e < E; e += blockDim.x) U->start[e] = 0;
@@ -702,8 +703,21 @@ __device__ inline void build_union(const int* idx, int T, int K, int E, Union* U
   for (int s = threadIdx.x; s < S; s += blockDim.x) {
     const int e = sidx[s];
     if (e < 0 || e >= E) continue;
+    // rank among the earlier slots of the same expert: sixteen slots per
+    // step, read as eight pairs together (entries at s or beyond, up to 15
+    // past the end of the selection, are read and not counted)
     int rank = 0;
-    for (int q = 0; q < s; ++q) rank += sidx[q] == e;
+    const int2* sp = reinterpret_cast<const int2*>(sidx);
+    for (int q0 = 0; q0 < s; q0 += 16) {
+      int2 a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = sp[(q0 >> 1) + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        rank += (q0 + 2 * u < s && a[u].x == e) ? 1 : 0;
+        rank += (q0 + 2 * u + 1 < s && a[u].y == e) ? 1 : 0;
+      }
+    }
     U->slots[U->start[e] + rank] = s;
   }
   __syncthreads();

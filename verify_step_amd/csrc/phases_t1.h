@@ -143,49 +143,90 @@ __device__ void router_t1(const LayerArgs& L, const StepArgs& S, const float* h,
   }
 }
 
+// Order key of logit x of expert e < 256: a larger value gives a larger
+// key (NaN counts as -inf, -0 as +0), and among equal values the lower index
+// gives the larger key (low 8 bits 255 - e).  Keys are distinct and nonzero.
+__device__ __forceinline__ unsigned long long topk_key(float x, int e) {
+  float v = (x == x) ? x : -INFINITY;
+  if (v == 0.f) v = 0.f;
+  const unsigned b = __float_as_uint(v);
+  const unsigned k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)k << 8) | (unsigned)(255 - e);
+}
+__device__ __forceinline__ float topk_key_value(unsigned long long key) {
+  const unsigned k = (unsigned)(key >> 8);
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Wave-wide maximum of a 64-bit key (DPP within rows of 16 lanes, then four
+// lane reads); every lane gets it.
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  auto mx = [](unsigned long long a, unsigned long long b) { return a > b ? a : b; };
+  auto sh = [](unsigned long long a, unsigned lo, unsigned hi) {
+    return ((unsigned long long)hi << 32) | lo;
+  };
+  v = mx(v, sh(v, dpp_i<kDppXor1>((int)v), dpp_i<kDppXor1>((int)(v >> 32))));
+  v = mx(v, sh(v, dpp_i<kDppXor2>((int)v), dpp_i<kDppXor2>((int)(v >> 32))));
+  v = mx(v, sh(v, dpp_i<kDppRor4>((int)v), dpp_i<kDppRor4>((int)(v >> 32))));
+  v = mx(v, sh(v, dpp_i<kDppRor8>((int)v), dpp_i<kDppRor8>((int)(v >> 32))));
+  const unsigned lo = (unsigned)v, hi = (unsigned)(v >> 32);
+  unsigned long long r = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const unsigned long long t =
+        sh(0, __builtin_amdgcn_readlane(lo, 16 * q), __builtin_amdgcn_readlane(hi, 16 * q));
+    r = mx(r, t);
+  }
+  return r;
+}
+
 // Top-k of one token's logits by one wave (value descending, index ascending
 // on ties) into registers (uniform over the wave): bis[k] the experts,
 // exs[k] / den their softmax weights.  Lane l holds the logits of experts
-// l + 64 i in x[i] (i < 4; entries at E or beyond are ignored).  Each round
-// takes the wave-wide maximum, then the lowest index holding it.
+// l + 64 i in x[i] (i < 4; entries at E or beyond are never selected; E <=
+// 256).  Each lane sorts its four keys once; a round takes the wave-wide
+// maximum of the lanes' first keys and the lane holding it moves to its next.
 __device__ __forceinline__ void topk_vals(const float (&x)[4], int E, int K,
                                           int (&bis)[kMaxTopK], float (&exs)[kMaxTopK],
                                           float& den) {
+  typedef unsigned long long u64;
   const int ln = lane_id();
-  float v[4];
-  bool open[4];  // still selectable
+  u64 k[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = ln + 64 * i;
-    v[i] = (e < E && x[i] == x[i]) ? x[i] : -INFINITY;  // NaN never wins
-    open[i] = e < E;
+    k[i] = e < E ? topk_key(x[i], e) : 0ull;
   }
+  auto cs = [](u64& a, u64& b) {  // a >= b afterwards
+    const u64 hi = a > b ? a : b, lo = a > b ? b : a;
+    a = hi;
+    b = lo;
+  };
+  cs(k[0], k[1]);
+  cs(k[2], k[3]);
+  cs(k[0], k[2]);
+  cs(k[1], k[3]);
+  cs(k[1], k[2]);
   float v0 = 0.f;
   den = 0.f;
 #pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) {
-    exs[k] = 0.f;
-    bis[k] = 0;
-    if (k >= K) continue;
-    float lm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (open[i]) lm = fmaxf(lm, v[i]);
-    const float m = wave_max(lm);
-    int cand = 0x7fffffff;
-#pragma unroll
-    for (int i = 3; i >= 0; --i)
-      if (open[i] && v[i] == m) cand = ln + 64 * i;
-    int bi = wave_min_i(cand);
-    if (bi == 0x7fffffff) bi = 0;  // fewer selectable logits than k
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (ln + 64 * i == bi) { v[i] = -INFINITY; open[i] = false; }
-    if (k == 0) v0 = m;
-    const float ex = __expf(m - v0);
+  for (int r = 0; r < kMaxTopK; ++r) {
+    exs[r] = 0.f;
+    bis[r] = 0;
+    if (r >= K) continue;
+    const u64 m = wave_max_u64(k[0]);
+    const bool win = k[0] == m;  // one lane (keys are distinct)
+    k[0] = win ? k[1] : k[0];
+    k[1] = win ? k[2] : k[1];
+    k[2] = win ? k[3] : k[2];
+    k[3] = win ? 0ull : k[3];
+    if (m == 0ull) continue;  // fewer selectable logits than k: expert 0, weight 0
+    const float val = topk_key_value(m);
+    if (r == 0) v0 = val;
+    const float ex = __expf(val - v0);
     den += ex;
-    exs[k] = ex;
-    bis[k] = bi;
+    exs[r] = ex;
+    bis[r] = 255 - (int)(m & 0xffu);
   }
 }
 

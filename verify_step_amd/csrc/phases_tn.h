@@ -96,7 +96,8 @@ __device__ __forceinline__ v4u tn_load_f16(const float* v, int ch, int sub) {
 // Like stream_t1, for nv <= NV input vectors in LDS (stored by tn_stage):
 // acc[r][v] = sum_c W_r[c] * in_v[c] (NVFP4: with block scales, matrix scale
 // left out).
-template <int DT, int R, int U, int NV, class ActFn, class RowFn, class OutFn, class PreFn>
+template <int DT, int R, int U, int NV, int NB = 2, class ActFn, class RowFn, class OutFn,
+          class PreFn>
 __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& actfn,
                                           RowFn&& rowfn, OutFn&& out, PreFn&& pre) {
   using W = WT<DT>;
@@ -104,8 +105,8 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
   const int nch = ncols / W::EPL;
   const int NI = (nch + 64 * U - 1) / (64 * U);
   const int total = ntask * NI;
-  v4u A[U][R], B[U][R];
-  unsigned sA[U][R], sB[U][R];
+  v4u Wb[NB][U][R];
+  unsigned Sb[NB][U][R];
   float acc[R][NV];
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -240,36 +241,48 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
         for (int v = 0; v < NV; ++v) acc[r][v] = 0.f;
     }
   };
-  // the refills are issued on every iteration (past the end they repeat the
-  // last step's addresses, unused), so the loop holds no conditional load;
-  // peeling the last steps off instead costs registers (and occupancy) here
+  // NB buffers rotate: step f computes in buffer f % NB, whose refill (step
+  // f + NB) goes out right after, so NB - 1 buffers stay in flight while one
+  // is computed.  The refills are issued on every iteration (past the end
+  // they repeat the last step's addresses, unused), so the loop holds no
+  // conditional load; peeling the last steps off instead costs registers
+  // (and occupancy) here
   const int last = total - 1;
   const At at_last{last / NI, last - (last / NI) * NI};
-  At c0{0, 0}, c1 = next(c0);
+  At c[NB];
+  c[0] = At{0, 0};
+#pragma unroll
+  for (int b = 1; b < NB; ++b) c[b] = next(c[b - 1]);
   if (total > 0) {
-    // all of A's loads ahead of all of B's, as inside the loop: the
-    // compiler's waits at the loop head hold for the entry path too
-    issue(A, sA, c0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(B, sB, 1 <= last ? c1 : at_last);
-    __builtin_amdgcn_sched_barrier(0);
+    // every buffer's loads ahead of the next buffer's, as inside the loop:
+    // the compiler's waits at the loop head hold for the entry path too
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      issue(Wb[b], Sb[b], b <= last ? c[b] : at_last);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   pre();
-  for (int f = 0; f < total; f += 2) {
-    const At c2 = next(c1), c3 = next(c2);
-    compute(A, sA, c0);
-    issue(A, sA, f + 2 <= last ? c2 : at_last);
-    if (f + 1 < total) compute(B, sB, c1);
-    issue(B, sB, f + 3 <= last ? c3 : at_last);
-    c0 = c2;
-    c1 = c3;
+  for (int f = 0; f < total; f += NB) {
+    At n[NB];
+    n[0] = next(c[NB - 1]);
+#pragma unroll
+    for (int b = 1; b < NB; ++b) n[b] = next(n[b - 1]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b == 0 || f + b < total) compute(Wb[b], Sb[b], c[b]);
+      issue(Wb[b], Sb[b], f + NB + b <= last ? n[b] : at_last);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) c[b] = n[b];
   }
 }
 
 // The union into global memory (one workgroup).
 // lds: a Union followed by kUnionIdxInts ints of scratch.
-constexpr int kUnionIdxInts = kMaxTok * kMaxTopK;
+constexpr int kUnionIdxInts = kMaxTok * kMaxTopK + 16;
 constexpr size_t kUnionLds = sizeof(Union) + kUnionIdxInts * sizeof(int);
+static_assert(sizeof(Union) % 8 == 0, "the selection after the union is read as int pairs");
 __device__ inline void union_to_global(const int* idx, int T, int K, int E, Union* lds, Union* dst) {
   build_union(idx, T, K, E, lds, reinterpret_cast<int*>(lds + 1));
   const int* s = reinterpret_cast<const int*>(lds);
