@@ -289,6 +289,11 @@ def main():
         step(stream)
     torch.cuda.synchronize()
     msk.workspace_status(ws)
+    # Each step takes the previous step's output as its input, so the routing
+    # (and with it the distinct experts a step streams) changes from step to
+    # step.  The timed steps and the per-kernel pass below both start from
+    # this state, so the bytes counted in the second are those of the first.
+    x_start = x.clone()
 
     # the timed region: K steps back to back, nothing else on the stream
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -304,6 +309,8 @@ def main():
     us_layer = ms_step * 1e3 / n_layers
 
     # the same K steps again, each kernel bracketed by dispatch-stamped events
+    x.copy_(x_start)
+    torch.cuda.synchronize()
     kp, step_bytes = kernel_pass(p, x, ws, args.steps, stream)
     msk.workspace_status(ws)
     nbytes = int(np.mean([b for b, _ in step_bytes]))

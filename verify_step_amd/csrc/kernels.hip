@@ -58,10 +58,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_union(LayerArgs L, StepArgs S
   union_to_global(S.idx, S.T, L.K, L.E, reinterpret_cast<Union*>(msk_smem), S.uni);
 }
 
-template <int DT, int NVMAX>
-__global__ __launch_bounds__(kBlockThreads) void k_gateup_tn(LayerArgs L, StepArgs S) {
+template <int DT, int NVMAX, int NWV>
+__global__ __launch_bounds__(NWV * 64) void k_gateup_tn(LayerArgs L, StepArgs S) {
   float* act = reinterpret_cast<float*>(msk_smem);
-  gateup_tn<DT, NVMAX>(L, S, S.uni, act, act + NVMAX * tn_vec_floats<DT>(L.H));
+  gateup_tn<DT, NVMAX, NWV>(L, S, S.uni, act, act + NVMAX * tn_vec_floats<DT>(L.H));
 }
 
 template <int DT, int NVMAX>
@@ -782,27 +782,30 @@ static hipError_t launch_ffn_t1(const LayerArgs& L, const StepArgs& S, const flo
 
 
 // Resident workgroups of a kernel at `lds` bytes, times the CU count.
-static int resident_grid(const void* fn, size_t lds) {
+static int resident_grid(const void* fn, size_t lds, int threads = kBlockThreads) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kBlockThreads, lds) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, lds) != hipSuccess ||
       n < 1)
     n = 1;
   return n * cu_count();
 }
 
 constexpr int kGateUpTokens = 2;  // token vectors staged per gate/up pass
+// waves per gate/up workgroup (sharing its staged inputs)
+template <int DT> constexpr int kGateUpWaves = 4;
 // slot vectors staged per down pass (NVFP4: two, to keep two waves per SIMD)
 template <int DT> constexpr int kDownTokens = DT == kNVFP4 ? 2 : 4;
 
 template <int DT>
 static hipError_t launch_experts_tn(const LayerArgs& L, const StepArgs& S, hipStream_t st) {
   {
-    auto fn = k_gateup_tn<DT, kGateUpTokens>;
-    const size_t lds = ((size_t)kGateUpTokens * tn_vec_floats<DT>(L.H) + kWaves) * sizeof(float);
+    constexpr int nwv = kGateUpWaves<DT>;
+    auto fn = k_gateup_tn<DT, kGateUpTokens, nwv>;
+    const size_t lds = ((size_t)kGateUpTokens * tn_vec_floats<DT>(L.H) + nwv) * sizeof(float);
     MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
     static int grid = 0;
-    if (grid == 0) grid = resident_grid(reinterpret_cast<const void*>(fn), lds);
-    MSK_TRY(launch(kPhGateUp, fn, grid, lds, st, L, S));
+    if (grid == 0) grid = resident_grid(reinterpret_cast<const void*>(fn), lds, nwv * 64);
+    MSK_TRY(launch_b(kPhGateUp, fn, grid, nwv * 64, lds, st, L, S));
   }
   {
     auto fn = k_down_tn<DT, kDownTokens<DT>>;

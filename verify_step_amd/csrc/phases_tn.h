@@ -326,8 +326,9 @@ template <> struct TnShape<kBF16> { enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U =
 template <> struct TnShape<kNVFP4> { enum { GU_RW = 2, GU_U = 1, DN_R = 4, DN_U = 1 }; };
 
 // act[s][f] = silu(gate_e[f] . u[t]) * (up_e[f] . u[t]) for slot s = t*K + j.
-// Tasks: (expert, RW rows of gate and the same RW rows of up).
-template <int DT, int NVMAX>
+// Tasks: (expert, RW rows of gate and the same RW rows of up); NWV waves per
+// workgroup share the staged inputs.
+template <int DT, int NVMAX, int NWV = kWaves>
 __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U, float* act_lds,
                           float* red) {
   constexpr int RW = TnShape<DT>::GU_RW, R = 2 * RW, UU = TnShape<DT>::GU_U;
@@ -338,7 +339,7 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
   for_expert_groups<NVMAX>(U, nrt, [&](int ui, int a, int b, int sidx, int nv) {
     const int e = U->list[ui];
     const int nt = b - a;
-    const int w0 = a + nt * wv / kWaves, w1 = a + nt * (wv + 1) / kWaves;
+    const int w0 = a + nt * wv / NWV, w1 = a + nt * (wv + 1) / NWV;
     // matrix scales in scalar registers before the stream (see slot below)
     const float ggs = DT == kNVFP4 ? uniform_f(L.gg[e]) : 1.f;
     const float gus = DT == kNVFP4 ? uniform_f(L.gu[e]) : 1.f;
