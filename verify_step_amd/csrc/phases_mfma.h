@@ -407,15 +407,17 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
 // t2 = rne(x - t1), t3 = rne(x - t1 - t2), so a score carries about 2^-12
 // of its terms' magnitude (the fp8 subnormal step bounds the last term), and
 // the power of two comes back out with the exp2 argument.  The output
-// product stays on bf16 (V converted and transposed once per tile, weights
-// rounded once), as in attn_item_mfma.
+// product stays on bf16 (weights rounded once, as in attn_item_mfma), with
+// its V^T operand read from the raw V tile by the gfx950 transpose load
+// (ds_read_b64_tr_b8) and converted in registers: no converted copy of V.
 //
-// Raw tiles (64 positions x 128 B of K, then of V) land in a two-slot LDS
-// ring through direct global->LDS loads, the next tile issued as soon as the
-// slot it overwrites is released, so no register holds a tile in flight.  A
-// tile row's 16-B chunk c sits at chunk c ^ ((row >> 1) & 7) of the row:
-// the 16 rows of a score operand read then hit 16 distinct bank groups.
-constexpr int kF8Slots = 2;  // ring depth: tiles in flight + 1
+// Raw tiles (64 positions x 128 B of K, then of V) land in a three-slot LDS
+// ring through direct global->LDS loads, two tiles ahead, each issued as
+// soon as the slot it overwrites is released, so no register holds a tile in
+// flight.  A tile row's 16-B chunk c sits at chunk c ^ ((row >> 1) & 7) of
+// the row: the 16 rows of a score operand read then hit 16 distinct bank
+// groups, and so do the 16 lanes of a transpose load.
+constexpr int kF8Slots = 3;  // ring depth: tiles in flight + 1
 
 template <int NPH>
 struct F8Geom {
@@ -424,25 +426,29 @@ struct F8Geom {
   static constexpr int SLOT = 2 * RAW;               // K then V
   static constexpr int NSLOT = kF8Slots;
   static constexpr int LDS_RING = NSLOT * SLOT;
-  static constexpr int VTS = 64 * 2 + 8;             // bf16 V^T row stride (as MfmaGeom)
-  static constexpr int LDS_VT = D * VTS;
-  static constexpr int LDS = LDS_RING + LDS_VT + kMaxTok * 4;
+  static constexpr int LDS = LDS_RING + kMaxTok * 4;
   static constexpr int ROWS = 16 * NW / NPH, NPT = 4 / NPH, NKS = 2 / NPH, NDT = D / 16;
 };
 
 __device__ __forceinline__ int f8_slot(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+// Two e4m3 bytes of w (bytes 0, 1, or 2, 3 with HI) as a bf16 pair (exact).
+template <bool HI>
+__device__ __forceinline__ unsigned e4m3x2_bf16(unsigned w) {
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
 
 template <int NPH>
 __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int item,
                              uint8_t* wl) {
   using Gm = F8Geom<NPH>;
   constexpr int D = Gm::D, NW = Gm::NW, RB = D, CPR = D / 16, EPC = 16;
-  constexpr int VTS = Gm::VTS, NDT = Gm::NDT, ROWS = Gm::ROWS, NPT = Gm::NPT, NKS = Gm::NKS;
+  constexpr int NDT = Gm::NDT, ROWS = Gm::ROWS, NPT = Gm::NPT, NKS = Gm::NKS;
   uint8_t* ring = wl;
-  uint8_t* vt = wl + Gm::LDS_RING;
-  float* rk = reinterpret_cast<float*>(vt + Gm::LDS_VT);
+  float* rk = reinterpret_cast<float*>(wl + Gm::LDS_RING);
 
   const int tid = threadIdx.x, ln = lane_id(), wv = wave_id();
   const int rt = wv / NPH, ph = wv - (wv / NPH) * NPH;
@@ -584,7 +590,7 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
     uint8_t* slot = ring + (it % Gm::NSLOT) * Gm::SLOT;
     // this wave's loads of the tile have landed (the later tiles' 4 loads
     // each may still be in flight), then every wave's; the slot about to be
-    // refilled and vt are free
+    // refilled is free
     if constexpr (Gm::NSLOT == 3) {
       if (pb + 64 < p1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
       else __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -596,53 +602,31 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
       const int ahead = pb + 64 * (Gm::NSLOT - 1);
       if (ahead < p1) issue(ahead, ring + ((it + Gm::NSLOT - 1) % Gm::NSLOT) * Gm::SLOT);
     }
-    // V -> vt[d][pos] (bf16), rows outside the loaded range as zeros
+    // V rows outside the loaded range become zeros (their loads fetched the
+    // head's row 0, and a masked weight times a NaN would still be NaN); the
+    // step's own rows take their K and V as cache bytes
     {
       const int vlo = pb > lo_min ? pb : lo_min;
       const int vhi = p1 < Lb ? p1 : Lb;
-      const int pp = tid & 31, cc = tid >> 5;
-      unsigned o[2][EPC / 2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = 2 * pp + h;
-        const bool ok = pb + row >= vlo && pb + row < vhi;
-        v4u w = *reinterpret_cast<const v4u*>(slot + Gm::RAW + f8_slot(row, cc) * 16);
-        if (!ok) w = v4u{0u, 0u, 0u, 0u};
-        chunk_to_bf16<kE4M3>(w, o[h]);
-      }
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        *reinterpret_cast<unsigned*>(vt + (cc * EPC + e) * VTS + 4 * pp) =
-            __builtin_amdgcn_perm(o[1][e >> 1], o[0][e >> 1], sel);
-      }
-    }
-    // the step's own rows in this tile: K as cache bytes into the raw tile,
-    // V converted into vt
-    const int n0 = pb > Lb ? pb : Lb;
-    const int n1 = pb + 64 < p1 ? pb + 64 : p1;
-    if (n0 < n1) {
-      lds_barrier();  // vt's loaded rows are written before new rows replace theirs
-      const int nn = (n1 - n0) * CPR;
-      for (int q = tid; q < 2 * nn; q += NW * 64) {
-        const bool value = q >= nn;
-        const int qq = value ? q - nn : q;
-        const int pos = n0 + qq / CPR, cc = qq % CPR;
-        const v4u enc = new_chunk(pos, cc, value);
-        const int row = pos - pb;
-        if (!value) {
-          *reinterpret_cast<v4u*>(slot + f8_slot(row, cc) * 16) = enc;
-        } else {
-          unsigned o[EPC / 2];
-          chunk_to_bf16<kE4M3>(enc, o);
-#pragma unroll
-          for (int e = 0; e < EPC; ++e)
-            *reinterpret_cast<unsigned short*>(vt + (cc * EPC + e) * VTS + 2 * row) =
-                (unsigned short)((e & 1) ? o[e >> 1] >> 16 : o[e >> 1] & 0xffffu);
+      const int n0 = pb > Lb ? pb : Lb;
+      const int n1 = pb + 64 < p1 ? pb + 64 : p1;
+      if (pb < vlo || pb + 64 > vhi) {
+        for (int q = tid; q < 64 * CPR; q += NW * 64) {
+          const int row = q / CPR, cc = q - (q / CPR) * CPR;
+          const int pos = pb + row;
+          if (pos >= vlo && pos < vhi) continue;
+          if (pos >= n0 && pos < n1) {
+            *reinterpret_cast<v4u*>(slot + f8_slot(row, cc) * 16) = new_chunk(pos, cc, false);
+            *reinterpret_cast<v4u*>(slot + Gm::RAW + f8_slot(row, cc) * 16) =
+                new_chunk(pos, cc, true);
+          } else {
+            *reinterpret_cast<v4u*>(slot + Gm::RAW + f8_slot(row, cc) * 16) =
+                v4u{0u, 0u, 0u, 0u};
+          }
         }
+        lds_barrier();
       }
     }
-    lds_barrier();
 
     if (m0 + 16 * rt >= M) continue;
     f32x4 sacc[NPT];
@@ -683,12 +667,26 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
     for (int kq = 0; kq < NKS; ++kq) {
       const int ks = ph * NKS + kq;
       const bf16x8 bh = as_bf16x8(v4u{wh[kq][0], wh[kq][1], wh[kq][2], wh[kq][3]});
+      // V^T operand (16 dims x 32 positions, the k order of the weights:
+      // slot m < 4 is position 4 g + m, slot m >= 4 position 16 + 4 g + m - 4
+      // of the k-step, g = ln >> 4).  Within each 16 lanes the transpose load
+      // gives lane 8 j + b byte b of the 8 bytes addressed by lane j + 2 m as
+      // its byte m, so lane q addresses slot m = q >> 1's row at dims
+      // 8 (q & 1) .. + 7 of the 16-dim tile, and lane i ends up with dim i
+      // of the tile at the eight positions in k order.
+      const int q = ln & 15, m = q >> 1;
+      const int vrow = 32 * ks + 4 * (ln >> 4) + (m & 3) + 16 * (m >> 2);
+      const uint8_t* vr = slot + Gm::RAW + vrow * 128 + 8 * (q & 1);
+      const int sw = (vrow >> 1) & 7;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const uint8_t* src = vt + (16 * dt + (ln & 15)) * VTS + (32 * ks + 4 * (ln >> 4)) * 2;
-        const v2u x0 = *reinterpret_cast<const v2u*>(src);
-        const v2u x1 = *reinterpret_cast<const v2u*>(src + 32);
-        const bf16x8 a = as_bf16x8(v4u{x0.x, x0.y, x1.x, x1.y});
+        typedef __attribute__((address_space(3))) v2i lds_v2i;
+        const v2i raw =
+            __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vr + ((dt ^ sw) << 4)));
+        const bf16x8 a = as_bf16x8(v4u{e4m3x2_bf16<false>((unsigned)raw.x),
+                                       e4m3x2_bf16<true>((unsigned)raw.x),
+                                       e4m3x2_bf16<false>((unsigned)raw.y),
+                                       e4m3x2_bf16<true>((unsigned)raw.y)});
         oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, oacc[dt], 0, 0, 0);
       }
     }
