@@ -6,8 +6,9 @@
 // The (expert, row block) tasks are laid out expert-major and every
 // workgroup takes one contiguous, equally long range of them, so a
 // workgroup meets one or two experts: it stages the input vectors of that
-// expert's tokens in LDS and its four waves stream their share of the rows
-// two buffers deep, as the one-token kernels do.  An expert with more
+// expert's tokens in LDS and its waves take the range's tasks in turn (wave
+// w the tasks w, w + 4, ..., so the waves read neighbouring rows together),
+// each streaming its rows two buffers deep, as the one-token kernels do.  An expert with more
 // tokens than the staging holds is streamed once per group of tokens.
 //
 // down writes y[slot][c] = down_e[c] . act[slot]; the combine then forms
@@ -339,7 +340,7 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
   for_expert_groups<NVMAX>(U, nrt, [&](int ui, int a, int b, int sidx, int nv) {
     const int e = U->list[ui];
     const int nt = b - a;
-    const int w0 = a + nt * wv / NWV, w1 = a + nt * (wv + 1) / NWV;
+    const int nmine = my_count(wv, NWV, nt);
     // matrix scales in scalar registers before the stream (see slot below)
     const float ggs = DT == kNVFP4 ? uniform_f(L.gg[e]) : 1.f;
     const float gus = DT == kNVFP4 ? uniform_f(L.gu[e]) : 1.f;
@@ -361,9 +362,9 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
     nv_dispatch<NVMAX>(nv, [&](auto nvc) {
       constexpr int NV = decltype(nvc)::value;
       stream_tn<DT, R, UU, NV>(
-          w1 - w0, L.H, nv, [&](int v) { return act_lds + v * tn_vec_floats<DT>(L.H); },
+          nmine, L.H, nv, [&](int v) { return act_lds + v * tn_vec_floats<DT>(L.H); },
           [&](int k, auto& wr, auto& sr) {
-            const int f0 = (w0 + k - ui * nrt) * RW;
+            const int f0 = (a + wv + k * NWV - ui * nrt) * RW;
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
               const size_t row = (size_t)e * L.F + f0 + r;
@@ -374,7 +375,7 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
             }
           },
           [&](int k, auto& acc) {
-            const int f0 = (w0 + k - ui * nrt) * RW;
+            const int f0 = (a + wv + k * NWV - ui * nrt) * RW;
             const int ln = lane_id();
 #pragma unroll
             for (int r = 0; r < RW; ++r)
@@ -402,7 +403,7 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
   for_expert_groups<NVMAX>(U, nrt, [&](int ui, int a, int b, int sidx, int nv) {
     const int e = U->list[ui];
     const int nt = b - a;
-    const int w0 = a + nt * wv / kWaves, w1 = a + nt * (wv + 1) / kWaves;
+    const int nmine = my_count(wv, kWaves, nt);
     const float gds = DT == kNVFP4 ? uniform_f(L.gd[e]) : 1.f;
     int slot[NVMAX];  // in registers before the stream (see gateup_tn)
 #pragma unroll
@@ -419,9 +420,9 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
     nv_dispatch<NVMAX>(nv, [&](auto nvc) {
       constexpr int NV = decltype(nvc)::value;
       stream_tn<DT, RD, UU, NV>(
-          w1 - w0, L.F, nv, [&](int v) { return act_lds + v * tn_vec_floats<DT>(L.F); },
+          nmine, L.F, nv, [&](int v) { return act_lds + v * tn_vec_floats<DT>(L.F); },
           [&](int k, auto& wr, auto& sr) {
-            const int c0 = (w0 + k - ui * nrt) * RD;
+            const int c0 = (a + wv + k * kWaves - ui * nrt) * RD;
 #pragma unroll
             for (int r = 0; r < RD; ++r) {
               const size_t row = (size_t)e * L.H + c0 + r;
@@ -430,7 +431,7 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
             }
           },
           [&](int k, auto& acc) {
-            const int c0 = (w0 + k - ui * nrt) * RD;
+            const int c0 = (a + wv + k * kWaves - ui * nrt) * RD;
             const int ln = lane_id();
 #pragma unroll
             for (int r = 0; r < RD; ++r)
