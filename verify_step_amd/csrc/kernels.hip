@@ -107,9 +107,9 @@ __global__ __launch_bounds__(kSumPrepThreads) void k_moe_sum_prep(LayerArgs L, S
   down_combine_prep(L, S, h, S.ybuf, out, g, eps, S.a3, red + 16, red);
 }
 
-template <int CT>
+template <int CT, int NT>
 __global__ __launch_bounds__(kBlockThreads) void k_dense_mfma(DenseArgs A) {
-  dense_mfma<CT>(A, msk_smem);
+  dense_mfma<CT, NT>(A, msk_smem);
 }
 
 __global__ __launch_bounds__(kBlockThreads) void k_dense_sum(const float* part, int N, int T,
@@ -538,10 +538,10 @@ static bool dense_on_mfma(const LayerArgs& L, const StepArgs& S, int N, int K) {
   return S.T > 1 && L.ddt == kBF16 && N % 16 == 0 && K % 128 == 0;
 }
 
-template <int CT>
+template <int CT, int NT>
 static hipError_t launch_dense_t(const DenseArgs& A, int ph, hipStream_t st) {
-  const void* fn = reinterpret_cast<const void*>(&k_dense_mfma<CT>);
-  const size_t lds = DenseLds<CT>::BYTES;
+  const void* fn = reinterpret_cast<const void*>(&k_dense_mfma<CT, NT>);
+  const size_t lds = DenseLds<CT, NT>::BYTES;
   MSK_TRY(set_lds_limit(fn, lds));
   static int per_cu = 0;
   if (per_cu == 0) {
@@ -551,27 +551,37 @@ static hipError_t launch_dense_t(const DenseArgs& A, int ph, hipStream_t st) {
   }
   const long long items = (long long)((A.N + 63) / 64) * A.ks;
   const long long cap = (long long)per_cu * cu_count();
-  return launch_x(ph, k_dense_mfma<CT>, (int)(items < cap ? items : cap), lds, st, A);
+  return launch_x(ph, k_dense_mfma<CT, NT>, (int)(items < cap ? items : cap), lds, st, A);
 }
 
 // out = resid + W a for the three (QKV) or one weight segments.
 // keep_parts: with K split into several slices the partial tiles are left
-// in S.dpart for the consumer to sum (dense_slices(N, K) of them).
+// in S.dpart for the consumer to sum (dense_slices(N, K) of them).  terms:
+// how many of the input's bf16 terms the product takes (2 or 3).
 static hipError_t launch_dense(const StepArgs& S, const uint8_t* w0, const uint8_t* w1,
                                const uint8_t* w2, int seg1, int seg2, int N, int K,
                                const float* resid, float* out, int ph, hipStream_t st,
-                               bool keep_parts = false) {
+                               bool keep_parts = false, int terms = 3) {
   DenseArgs A;
   A.w[0] = w0; A.w[1] = w1 ? w1 : w0; A.w[2] = w2 ? w2 : w0;
   A.seg[0] = 0; A.seg[1] = seg1; A.seg[2] = seg2;
   A.N = N; A.K = K; A.T = S.T;
   A.ks = dense_slices(N, K);
   A.a3 = S.a3; A.resid = resid; A.out = out; A.part = S.dpart;
-  switch ((S.T + 15) / 16) {
-    case 1: MSK_TRY(launch_dense_t<1>(A, ph, st)); break;
-    case 2: MSK_TRY(launch_dense_t<2>(A, ph, st)); break;
-    case 3: MSK_TRY(launch_dense_t<3>(A, ph, st)); break;
-    default: MSK_TRY(launch_dense_t<4>(A, ph, st)); break;
+  if (terms == 2) {
+    switch ((S.T + 15) / 16) {
+      case 1: MSK_TRY((launch_dense_t<1, 2>(A, ph, st))); break;
+      case 2: MSK_TRY((launch_dense_t<2, 2>(A, ph, st))); break;
+      case 3: MSK_TRY((launch_dense_t<3, 2>(A, ph, st))); break;
+      default: MSK_TRY((launch_dense_t<4, 2>(A, ph, st))); break;
+    }
+  } else {
+    switch ((S.T + 15) / 16) {
+      case 1: MSK_TRY((launch_dense_t<1, 3>(A, ph, st))); break;
+      case 2: MSK_TRY((launch_dense_t<2, 3>(A, ph, st))); break;
+      case 3: MSK_TRY((launch_dense_t<3, 3>(A, ph, st))); break;
+      default: MSK_TRY((launch_dense_t<4, 3>(A, ph, st))); break;
+    }
   }
   if (A.ks == 1 || keep_parts) return hipSuccess;
   const long long n = (long long)S.T * N;
@@ -707,7 +717,7 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
     }
   } else if (mm) {
     MSK_TRY(launch_dense(S, L.wo, nullptr, nullptr, 0, 0, L.H, L.Hq * L.D, x, h, kPhWo, st,
-                         wo_parts && wo_sum_in_route(L, S)));
+                         wo_parts && wo_sum_in_route(L, S), /*terms=*/2));
   } else {
     if (L.ddt == kBF16)
       MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhWo, k_wo<kBF16, NV>, wgrid, 0, st, L, S, x, h)))

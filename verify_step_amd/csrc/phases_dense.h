@@ -5,11 +5,14 @@
 // v_mfma_f32_16x16x32_bf16 takes the weight rows as the A operand (16 rows,
 // eight consecutive k per lane) and the activations as the B operand (16
 // tokens), both read from LDS tiles (below).  Each
-// activation enters as three bf16 terms a = hi + mid + lo (each the
-// round-to-nearest-even of what the previous terms leave), so the
-// products are as exact as fp32 ones and the sums stay in fp32.  The terms
-// are written once per call, [3][T][K] bf16, by the kernel that produces the
-// activations.
+// activation is written as three bf16 terms a = hi + mid + lo (each the
+// round-to-nearest-even of what the previous terms leave), [3][T][K], once
+// per call by the kernel that produces the activations.  A product takes the
+// first NT of them: QKV and the router all three (products as exact as fp32
+// ones: the new K and V rows are rounded to the cache format, where a
+// difference at a rounding boundary moves a value by a whole fp8 step, and
+// routing is compared bit for bit), Wo two (hi + mid leaves at most 2^-17
+// of each input out).  The sums stay in fp32.
 //
 // Work item: (block of 64 output rows, one of KS slices of K); each of the
 // four waves owns 16 of the rows.  With KS > 1 each item writes a partial
@@ -192,7 +195,7 @@ __device__ inline void down_combine_prep(const LayerArgs& L, const StepArgs& S, 
 }
 
 // Per 128-column k-tile the weights of a wave's 16 rows (16 x 256 B) and the
-// workgroup's activation terms (3 planes x 16 CT tokens x 256 B) are fetched
+// workgroup's activation terms (NT planes x 16 CT tokens x 256 B) are fetched
 // with direct global->LDS loads, double buffered.  A load instruction moves
 // 1 KB: four rows x 256 B, each row's 16-B pieces stored at piece ^ (row &
 // 15), so the MFMA operand reads (16 rows, one piece each) hit 16 distinct
@@ -200,28 +203,24 @@ __device__ inline void down_combine_prep(const LayerArgs& L, const StepArgs& S, 
 constexpr int kDenseKT = 128;       // columns per k-tile
 constexpr int kDenseATile = 16 * 256;  // one wave's weight tile, bytes
 
-template <int CT>
+template <int CT, int NT>
 struct DenseLds {
-  static constexpr int BT = 3 * 16 * CT * 256;  // activation tile, bytes
+  static constexpr int BT = NT * 16 * CT * 256;  // activation tile, bytes
   static constexpr int A0 = 0;
   static constexpr int B0 = A0 + 2 * kWaves * kDenseATile;
   static constexpr int BYTES = B0 + 2 * BT;  // weight tiles [2][4 waves], term tiles [2]
 };
 
-__device__ __forceinline__ void wait_vm(int n) {
-  // vmcnt <= n (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
-  switch (n) {
-    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
-    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
-    case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;
-    default: __builtin_amdgcn_s_waitcnt(0); break;
-  }
+// vmcnt <= N (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int CT>
+template <int CT, int NT>
 __device__ void dense_mfma(const DenseArgs& A, uint8_t* lds) {
-  using G = DenseLds<CT>;
+  using G = DenseLds<CT, NT>;
   const int ln = lane_id(), wv = wave_id();
   const int r = ln & 15, g = ln >> 4;
   const int n_rb = (A.N + 63) / 64;
@@ -256,8 +255,8 @@ __device__ void dense_mfma(const DenseArgs& A, uint8_t* lds) {
       }
       uint8_t* bt = lds + G::B0 + buf * G::BT;
 #pragma unroll
-      for (int k = 0; k < 3 * CT; ++k) {
-        const int i = wv + kWaves * k;       // instruction of the 12 CT in the B tile
+      for (int k = 0; k < NT * CT; ++k) {
+        const int i = wv + kWaves * k;       // instruction of the 4 NT CT in the B tile
         const int brow = 4 * i + g;          // plane-major row: p3 * 16 CT + t
         const int p3 = brow / (16 * CT), t = brow - p3 * 16 * CT;
         const int tt = t < A.T ? t : 0;
@@ -275,10 +274,11 @@ __device__ void dense_mfma(const DenseArgs& A, uint8_t* lds) {
       const int buf = (tau - t0) & 1;
       if (tau + 1 < t1) {
         issue(tau + 1, buf ^ 1);
-        // this tile's loads are the older ones: 4 (weights) + 3 CT (terms) per lane remain
-        wait_vm(active ? 4 + 3 * CT : 3 * CT);
+        // this tile's loads are the older ones: 4 (weights) + NT CT (terms) per lane remain
+        if (active) wait_vm<4 + NT * CT>();
+        else wait_vm<NT * CT>();
       } else {
-        wait_vm(0);
+        wait_vm<0>();
       }
       lds_barrier();
       if (active) {
@@ -291,7 +291,7 @@ __device__ void dense_mfma(const DenseArgs& A, uint8_t* lds) {
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int p3 = 0; p3 < 3; ++p3) {
+            for (int p3 = 0; p3 < NT; ++p3) {
               const bf16x8 bb = as_bf16x8(*reinterpret_cast<const v4u*>(
                   bt + (p3 * 16 * CT + 16 * ct + r) * 256 + slot * 16));
               acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, acc[ct], 0, 0, 0);
