@@ -84,11 +84,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_combine(LayerArgs L, StepArgs
 }
 
 // Matrix-core dense projections of several tokens and their input terms.
-__global__ __launch_bounds__(kBlockThreads) void k_prep_act(const float* x, const float* g, int T,
-                                                            int H, float eps, float* a32,
-                                                            unsigned short* a3) {
-  prep_act(x, g, T, H, eps, a32, a3, reinterpret_cast<float*>(msk_smem));
-}
 
 constexpr int kSumPrepThreads = 1024;
 __global__ __launch_bounds__(kSumPrepThreads) void k_sum_prep(const float* part, int ks,
@@ -555,6 +550,16 @@ static hipError_t launch_dense_t(const DenseArgs& A, int ph, hipStream_t st) {
 }
 
 // out = resid + W a for the three (QKV) or one weight segments.
+// a = RMSNorm(x) * g of T rows as bf16 terms (and as fp32 when a32 is
+// given): one 1024-thread workgroup per row, the row loaded once.
+static hipError_t launch_prep(const float* x, const float* g, int T, int H, float eps, float* a32,
+                              unsigned short* a3, hipStream_t st) {
+  const size_t lds = (16 + (size_t)H) * sizeof(float);
+  MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_sum_prep), lds));
+  return launch_b(kPhPrep, k_sum_prep, T, kSumPrepThreads, lds, st, (const float*)nullptr, 0,
+                  (const float*)nullptr, const_cast<float*>(x), g, T, H, eps, a32, a3);
+}
+
 // keep_parts: with K split into several slices the partial tiles are left
 // in S.dpart for the consumer to sum (dense_slices(N, K) of them).  terms:
 // how many of the input's bf16 terms the product takes (2 or 3).
@@ -685,8 +690,7 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
     }
   } else if (dense_on_mfma(L, S, NR, L.H)) {
     if (!a3_ready)
-      MSK_TRY(launch_x(kPhPrep, k_prep_act, S.T, kWaves * sizeof(float), st, x, L.attn_norm, S.T,
-                       L.H, L.eps, (float*)nullptr, S.a3));
+      MSK_TRY(launch_prep(x, L.attn_norm, S.T, L.H, L.eps, nullptr, S.a3, st));
     const int NQ = L.Hq * L.D, NK = L.Hkv * L.D;
     MSK_TRY(launch_dense(S, L.wq, L.wk, L.wv, NQ, NQ + NK, NR, L.H, nullptr, S.qkv, kPhQkv, st));
   } else {
@@ -759,8 +763,7 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
                        dense_slices(L.H, L.Hq * L.D), wo_resid, S.h, L.ffn_norm, S.T, L.H, L.eps,
                        S.u, S.a3));
     } else {
-      MSK_TRY(launch_x(kPhPrep, k_prep_act, S.T, kWaves * sizeof(float), st, h, L.ffn_norm, S.T,
-                       L.H, L.eps, S.u, S.a3));
+      MSK_TRY(launch_prep(h, L.ffn_norm, S.T, L.H, L.eps, S.u, S.a3, st));
     }
     MSK_TRY(launch_dense(S, L.wr, nullptr, nullptr, 0, 0, L.E, L.H, nullptr, S.logits, kPhRouter,
                          st, /*keep_parts=*/true));

@@ -49,31 +49,6 @@ __device__ __forceinline__ void store_split8(unsigned short* a3, size_t plane, s
       v4u{l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16};
 }
 
-// One workgroup per token: a = x * g / sqrt(mean(x^2) + eps) as fp32 (if
-// a32) and as bf16 terms.
-__device__ inline void prep_act(const float* x, const float* g, int T, int H, float eps,
-                                float* a32, unsigned short* a3, float* red) {
-  const int t = blockIdx.x;
-  const float* xr = x + (size_t)t * H;
-  float s = 0.f;
-  for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
-    const v4f a = *reinterpret_cast<const v4f*>(xr + c);
-    s += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
-  }
-  const float r = 1.0f / sqrtf(block_sum(s, red) / (float)H + eps);
-  const size_t plane = (size_t)T * H;
-  for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = xr[c + e] * r * g[c + e];
-    if (a32) {
-      *reinterpret_cast<v4f*>(a32 + (size_t)t * H + c) = v4f{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<v4f*>(a32 + (size_t)t * H + c + 4) = v4f{v[4], v[5], v[6], v[7]};
-    }
-    store_split8(a3, plane, (size_t)t * H + c, v);
-  }
-}
-
 // src[0] + src[stride] + ... + src[(n - 1) stride] (four consecutive
 // floats each), added in that order, with up to 8 loads in flight at once (a
 // plain loop would wait for each load before issuing the next).
@@ -108,9 +83,10 @@ __device__ __forceinline__ float wg_sum(float v, float* red) {
 
 // One workgroup per token t: h[t] = resid[t] + (the partial tiles of a
 // split-K dense product summed in slice order, as dense_sum does), written
-// out, then a = h[t] * g / sqrt(mean(h[t]^2) + eps) as prep_act writes it.
-// ks <= 1: h is complete already and is only read.  hl: H floats of LDS,
-// red: 16 floats of LDS.
+// out, then a = h[t] * g / sqrt(mean(h[t]^2) + eps) as bf16 terms
+// (store_split8) and, when a32 is given, as fp32.  ks <= 1: h is complete
+// already and is only read (the plain RMSNorm of an input row).  hl: H
+// floats of LDS, red: 16 floats of LDS.
 __device__ inline void sum_prep_act(const float* part, int ks, const float* resid, float* h,
                                     const float* g, int T, int H, float eps, float* a32,
                                     unsigned short* a3, float* hl, float* red) {
@@ -149,7 +125,7 @@ __device__ inline void sum_prep_act(const float* part, int ks, const float* resi
 
 // One workgroup per token t: out[t] as down_combine forms it, then the next
 // layer's QKV input terms from it: a3 = bf16 terms of out[t] * g /
-// sqrt(mean(out[t]^2) + eps) (store_split8, as prep_act writes them).
+// sqrt(mean(out[t]^2) + eps) (store_split8, as sum_prep_act writes them).
 // ol: H floats of LDS, red: 16 floats of LDS.
 __device__ inline void down_combine_prep(const LayerArgs& L, const StepArgs& S, const float* h,
                                          const float* y, float* out, const float* g, float eps,
@@ -332,8 +308,16 @@ __device__ inline void dense_sum(const float* part, int N, int T, int ks, const 
     const int t = q / N, row = q - (q / N) * N;
     const int rb = row >> 6, rr = row & 63;
     const float* src = part + (size_t)rb * ks * T * 64 + t * 64 + rr;
+    // the slices' loads issued together, eight at a time, then added in order
     float v = 0.f;
-    for (int s = 0; s < ks; ++s) v += src[(size_t)s * T * 64];
+    for (int s0 = 0; s0 < ks; s0 += 8) {
+      float pv[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) pv[s] = src[(size_t)(s0 + s < ks ? s0 + s : ks - 1) * T * 64];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        if (s0 + s < ks) v += pv[s];
+    }
     out[q] = (resid ? resid[q] : 0.f) + v;
   }
 }

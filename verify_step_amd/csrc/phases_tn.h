@@ -453,16 +453,26 @@ __device__ inline void down_combine(const LayerArgs& L, const StepArgs& S, const
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x) {
     const int t = (i * 4) / L.H, c = i * 4 - t * L.H;
     v4f acc = *reinterpret_cast<const v4f*>(h + (size_t)t * L.H + c);
-    for (int j = 0; j < L.K; ++j) {
-      const int s = t * L.K + j;
-      const int e = S.idx[s];
-      if (e < 0 || e >= L.E) continue;
-      const float w = S.wts[s];
-      const v4f yy = *reinterpret_cast<const v4f*>(y + (size_t)s * L.H + c);
-      acc.x = fmaf(w, yy.x, acc.x);
-      acc.y = fmaf(w, yy.y, acc.y);
-      acc.z = fmaf(w, yy.z, acc.z);
-      acc.w = fmaf(w, yy.w, acc.w);
+    // eight slots' loads in flight at once, then added in slot order
+    for (int j0 = 0; j0 < L.K; j0 += 8) {
+      v4f yy[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = j0 + q < L.K ? j0 + q : L.K - 1;
+        yy[q] = *reinterpret_cast<const v4f*>(y + ((size_t)t * L.K + j) * L.H + c);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (j0 + q >= L.K) break;
+        const int s = t * L.K + j0 + q;
+        const int e = S.idx[s];
+        if (e < 0 || e >= L.E) continue;
+        const float w = S.wts[s];
+        acc.x = fmaf(w, yy[q].x, acc.x);
+        acc.y = fmaf(w, yy[q].y, acc.y);
+        acc.z = fmaf(w, yy[q].z, acc.z);
+        acc.w = fmaf(w, yy[q].w, acc.w);
+      }
     }
     *reinterpret_cast<v4f*>(out + (size_t)t * L.H + c) = acc;
   }
