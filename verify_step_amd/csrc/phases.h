@@ -677,13 +677,22 @@ __device__ inline void build_union(const int* idx, int T, int K, int E, Union* U
       nz += c[i] > 0;
       tot += c[i];
     }
-    int inz = nz, itot = tot;  // inclusive scans over lanes
+    // exclusive prefix sums over the lanes and wave totals, one ballot per
+    // bit (nz <= 4, tot <= S <= 1024): no cross-lane data movement
+    const unsigned long long below = (1ull << ln) - 1ull;
+    int pnz = 0, ptot = 0, inz = 0, itot = 0;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int a = __shfl_up(inz, off, 64), bsum = __shfl_up(itot, off, 64);
-      if (ln >= off) { inz += a; itot += bsum; }
+    for (int b = 0; b < 3; ++b) {
+      const unsigned long long m = __ballot((nz >> b) & 1);
+      pnz += __popcll(m & below) << b;
+      inz += __popcll(m) << b;
     }
-    int pnz = inz - nz, ptot = itot - tot;
+#pragma unroll
+    for (int b = 0; b < 11; ++b) {
+      const unsigned long long m = __ballot((tot >> b) & 1);
+      ptot += __popcll(m & below) << b;
+      itot += __popcll(m) << b;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = ln * 4 + i;
@@ -697,7 +706,7 @@ __device__ inline void build_union(const int* idx, int T, int K, int E, Union* U
         ptot += c[i];
       }
     }
-    if (ln == 63) { U->n = inz; U->off[inz] = itot; }
+    if (ln == 0) { U->n = inz; U->off[inz] = itot; }
   }
   __syncthreads();
   for (int s = threadIdx.x; s < S; s += blockDim.x) {
