@@ -64,10 +64,10 @@ __global__ __launch_bounds__(NWV * 64) void k_gateup_tn(LayerArgs L, StepArgs S)
   gateup_tn<DT, NVMAX, NWV>(L, S, S.uni, act, act + NVMAX * tn_vec_floats<DT>(L.H));
 }
 
-template <int DT, int NVMAX>
-__global__ __launch_bounds__(kBlockThreads) void k_down_tn(LayerArgs L, StepArgs S) {
+template <int DT, int NVMAX, int NWV>
+__global__ __launch_bounds__(NWV * 64) void k_down_tn(LayerArgs L, StepArgs S) {
   float* act = reinterpret_cast<float*>(msk_smem);
-  down_tn<DT, NVMAX>(L, S, S.uni, act, act + NVMAX * tn_vec_floats<DT>(L.F), S.ybuf);
+  down_tn<DT, NVMAX, NWV>(L, S, S.uni, act, act + NVMAX * tn_vec_floats<DT>(L.F), S.ybuf);
 }
 
 __global__ __launch_bounds__(kBlockThreads) void k_moe_sum(LayerArgs L, StepArgs S, const float* h,
@@ -803,30 +803,40 @@ static int resident_grid(const void* fn, size_t lds, int threads = kBlockThreads
   return n * cu_count();
 }
 
-constexpr int kGateUpTokens = 2;  // token vectors staged per gate/up pass
-// waves per gate/up workgroup (sharing its staged inputs)
-template <int DT> constexpr int kGateUpWaves = 4;
+// token vectors staged per gate/up pass: four fp32 vectors (96 KB at
+// H = 6144, one workgroup per CU) for fp32 and bf16 experts, two fp16 ones
+// for NVFP4 (register pressure of its decode).  Measured on verify-bf16-128k:
+// four per pass 10% faster than two, and two with one workgroup per CU much
+// slower than either.
+template <int DT> constexpr int kGateUpTokens = DT == kNVFP4 ? 2 : 4;
+// waves per gate/up workgroup (sharing its staged inputs): eight for the
+// one-per-CU fp32 and bf16 workgroups (4% faster than four on
+// verify-bf16-128k)
+template <int DT> constexpr int kGateUpWaves = DT == kNVFP4 ? 4 : 8;
 // slot vectors staged per down pass (NVFP4: two, to keep two waves per SIMD)
 template <int DT> constexpr int kDownTokens = DT == kNVFP4 ? 2 : 4;
+// waves per down workgroup
+template <int DT> constexpr int kDownWaves = 4;
 
 template <int DT>
 static hipError_t launch_experts_tn(const LayerArgs& L, const StepArgs& S, hipStream_t st) {
   {
     constexpr int nwv = kGateUpWaves<DT>;
-    auto fn = k_gateup_tn<DT, kGateUpTokens, nwv>;
-    const size_t lds = ((size_t)kGateUpTokens * tn_vec_floats<DT>(L.H) + nwv) * sizeof(float);
+    auto fn = k_gateup_tn<DT, kGateUpTokens<DT>, nwv>;
+    const size_t lds = ((size_t)kGateUpTokens<DT> * tn_vec_floats<DT>(L.H) + nwv) * sizeof(float);
     MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
     static int grid = 0;
     if (grid == 0) grid = resident_grid(reinterpret_cast<const void*>(fn), lds, nwv * 64);
     MSK_TRY(launch_b(kPhGateUp, fn, grid, nwv * 64, lds, st, L, S));
   }
   {
-    auto fn = k_down_tn<DT, kDownTokens<DT>>;
-    const size_t lds = ((size_t)kDownTokens<DT> * tn_vec_floats<DT>(L.F) + kWaves) * sizeof(float);
+    constexpr int nwv = kDownWaves<DT>;
+    auto fn = k_down_tn<DT, kDownTokens<DT>, nwv>;
+    const size_t lds = ((size_t)kDownTokens<DT> * tn_vec_floats<DT>(L.F) + nwv) * sizeof(float);
     MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
     static int grid = 0;
-    if (grid == 0) grid = resident_grid(reinterpret_cast<const void*>(fn), lds);
-    MSK_TRY(launch(kPhDown, fn, grid, lds, st, L, S));
+    if (grid == 0) grid = resident_grid(reinterpret_cast<const void*>(fn), lds, nwv * 64);
+    MSK_TRY(launch_b(kPhDown, fn, grid, nwv * 64, lds, st, L, S));
   }
   return hipSuccess;
 }

@@ -392,7 +392,7 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
 
 // y[s][c] = down_e[c] . act[s] (times the NVFP4 matrix scale) for the slots
 // s routed to expert e.  Tasks: (expert, RD output rows).
-template <int DT, int NVMAX>
+template <int DT, int NVMAX, int NWV = kWaves>
 __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, float* act_lds,
                         float* red, float* y) {
   constexpr int RD = TnShape<DT>::DN_R, UU = TnShape<DT>::DN_U;
@@ -403,7 +403,7 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
   for_expert_groups<NVMAX>(U, nrt, [&](int ui, int a, int b, int sidx, int nv) {
     const int e = U->list[ui];
     const int nt = b - a;
-    const int nmine = my_count(wv, kWaves, nt);
+    const int nmine = my_count(wv, NWV, nt);
     const float gds = DT == kNVFP4 ? uniform_f(L.gd[e]) : 1.f;
     int slot[NVMAX];  // in registers before the stream (see gateup_tn)
 #pragma unroll
@@ -422,7 +422,7 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
       stream_tn<DT, RD, UU, NV>(
           nmine, L.F, nv, [&](int v) { return act_lds + v * tn_vec_floats<DT>(L.F); },
           [&](int k, auto& wr, auto& sr) {
-            const int c0 = (a + wv + k * kWaves - ui * nrt) * RD;
+            const int c0 = (a + wv + k * NWV - ui * nrt) * RD;
 #pragma unroll
             for (int r = 0; r < RD; ++r) {
               const size_t row = (size_t)e * L.H + c0 + r;
@@ -431,7 +431,7 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
             }
           },
           [&](int k, auto& acc) {
-            const int c0 = (a + wv + k * kWaves - ui * nrt) * RD;
+            const int c0 = (a + wv + k * NWV - ui * nrt) * RD;
             const int ln = lane_id();
 #pragma unroll
             for (int r = 0; r < RD; ++r)
