@@ -804,11 +804,12 @@ static int resident_grid(const void* fn, size_t lds, int threads = kBlockThreads
 }
 
 // token vectors staged per gate/up pass: four fp32 vectors (96 KB at
-// H = 6144, one workgroup per CU) for fp32 and bf16 experts, two fp16 ones
-// for NVFP4 (register pressure of its decode).  Measured on verify-bf16-128k:
-// four per pass 10% faster than two, and two with one workgroup per CU much
-// slower than either.
-template <int DT> constexpr int kGateUpTokens = DT == kNVFP4 ? 2 : 4;
+// H = 6144, one workgroup per CU) for fp32 and bf16 experts, three fp16 ones
+// for NVFP4 (register pressure of its decode).  Measured: bf16 four per
+// pass 10% faster than two on verify-bf16-128k (two with one workgroup per
+// CU much slower than either); NVFP4 three 3% faster than two on
+// stack4-nvfp4, four slower.
+template <int DT> constexpr int kGateUpTokens = DT == kNVFP4 ? 3 : 4;
 // waves per gate/up workgroup (sharing its staged inputs): eight for the
 // one-per-CU fp32 and bf16 workgroups (4% faster than four on
 // verify-bf16-128k)
