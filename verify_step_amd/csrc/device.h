@@ -13,6 +13,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
+template <int N> struct IC { static constexpr int value = N; };
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // Wave index within the workgroup, marked wave-uniform so that values
 // derived from it (task and row indices) live in scalar registers and the
@@ -40,6 +42,8 @@ constexpr int kDppXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppRor4 = 0x124;   // row_ror:4
 constexpr int kDppRor8 = 0x128;   // row_ror:8
+constexpr int kDppMirror = 0x140;      // row_mirror: lane j of a row <- 15 - j
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane j of 8 <- 7 - j
 
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f<kDppXor1>(v));
@@ -85,6 +89,57 @@ __device__ __forceinline__ float add_xor16(float v) {
 __device__ __forceinline__ float add_xor32(float v) {
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Wave sums of P per-lane values (P = 1, 2, 4, 8 or 16) with fewer
+// cross-lane steps than P separate sums: each of the first log2 P steps
+// trades half of a lane's values with the lane at distance 32, 16, 8, 4
+// (lane swaps, a DPP rotation, a swizzle) and adds the other half, so
+// afterwards every lane holds one value; the remaining lane bits are summed
+// as in wave_sum.  Lane l returns the total of value l >> (6 - log2 P) (of
+// value 0 for P = 1).
+template <int P>
+__device__ __forceinline__ float reduce_scatter(const float (&a)[P]) {
+  static_assert(P == 1 || P == 2 || P == 4 || P == 8 || P == 16, "P is a power of two <= 16");
+  constexpr int L = P == 1 ? 0 : P == 2 ? 1 : P == 4 ? 2 : P == 8 ? 3 : 4;
+  const int ln = lane_id();
+  float b[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) b[j] = a[j];
+  auto halve = [&](auto n_c, int d, auto partner) {
+    constexpr int N = decltype(n_c)::value;
+    const bool up = (ln & d) != 0;
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) {
+      const float keep = up ? b[j + N / 2] : b[j];
+      const float give = up ? b[j] : b[j + N / 2];
+      b[j] = keep + partner(give);
+    }
+  };
+  auto p32 = [&](float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(ln < 32 ? p[1] : p[0]);
+  };
+  auto p16 = [&](float x) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((ln & 16) ? p[0] : p[1]);
+  };
+  auto p8 = [&](float x) { return dpp_f<kDppRor8>(x); };  // lane j <-> j ^ 8 in a row
+  auto p4 = [&](float x) {  // xor 4 within 32 lanes (swizzle bit mode)
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
+  };
+  if constexpr (L >= 1) halve(IC<P>{}, 32, p32);
+  if constexpr (L >= 2) halve(IC<P / 2>{}, 16, p16);
+  if constexpr (L >= 3) halve(IC<P / 4>{}, 8, p8);
+  if constexpr (L >= 4) halve(IC<P / 8>{}, 4, p4);
+  float v = b[0];
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  if constexpr (L < 4) v += dpp_f<kDppHalfMirror>(v);  // quads uniform: the other quad of 8
+  if constexpr (L < 3) v += dpp_f<kDppMirror>(v);      // halves uniform: the other 8 of 16
+  if constexpr (L < 2) v = add_xor16(v);
+  if constexpr (L < 1) v = add_xor32(v);
+  return v;
 }
 
 // Sum of v over the lanes congruent to this one modulo LPP (LPP = 4, 8, 16

@@ -8,7 +8,6 @@
 
 namespace msk {
 
-template <int N> struct IC { static constexpr int value = N; };
 
 // Global index of this wave when waves are numbered across workgroups first,
 // so that a phase with fewer tasks than waves still spreads over every CU.
