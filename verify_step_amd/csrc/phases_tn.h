@@ -94,11 +94,17 @@ __device__ __forceinline__ v4u tn_load_f16(const float* v, int ch, int sub) {
   return *reinterpret_cast<const v4u*>(v + tn_gran<kNVFP4>(ch * 4 + sub) * 4);
 }
 
+// NV padded to a power of two, and log2 of a power of two up to 16.
+constexpr int tn_nvp(int nv) { return nv <= 1 ? 1 : nv <= 2 ? 2 : nv <= 4 ? 4 : 8; }
+constexpr int tn_log2(int p) { return p <= 1 ? 0 : p == 2 ? 1 : p == 4 ? 2 : p == 8 ? 3 : 4; }
+
 // Like stream_t1, for nv <= NV input vectors in LDS (stored by tn_stage):
-// acc[r][v] = sum_c W_r[c] * in_v[c] (NVFP4: with block scales, matrix scale
-// left out).
-template <int DT, int R, int U, int NV, int NB = 2, bool SCATTER = false, class ActFn,
-          class RowFn, class OutFn, class PreFn>
+// the sums W_r . in_v (NVFP4: with block scales, matrix scale left out) of a
+// task's R rows and nv vectors, reduced over the wave together
+// (reduce_scatter): out(k, sum) gets in lane l the sum of index
+// l >> (6 - log2 P), index r NVP + v, P = R NVP, NVP = tn_nvp(NV).
+template <int DT, int R, int U, int NV, int NB = 2, class ActFn, class RowFn, class OutFn,
+          class PreFn>
 __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& actfn,
                                           RowFn&& rowfn, OutFn&& out, PreFn&& pre) {
   using W = WT<DT>;
@@ -231,23 +237,15 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
       }
     }
     if (i == NI - 1) {
-      if constexpr (SCATTER) {
-        // value (r, v) at index r * NVP + v (NV padded to a power of two);
-        // out(k, red) gets in each lane the total of index lane >> (6 - log2 P)
-        constexpr int NVP = NV <= 1 ? 1 : NV <= 2 ? 2 : NV <= 4 ? 4 : 8;
-        float a[R * NVP];
+      // value (r, v) at index r * NVP + v (NV padded to a power of two);
+      // out(k, sum) gets in each lane the total of index lane >> (6 - log2 P)
+      constexpr int NVP = tn_nvp(NV);
+      float a[R * NVP];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-          for (int v = 0; v < NVP; ++v) a[r * NVP + v] = (v < NV && v < nv) ? acc[r][v] : 0.f;
-        out(k, reduce_scatter<R * NVP>(a));
-      } else {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int v = 0; v < NV; ++v) acc[r][v] = v < nv ? wave_sum(acc[r][v]) : 0.f;
-        out(k, acc);
-      }
+        for (int v = 0; v < NVP; ++v) a[r * NVP + v] = (v < NV && v < nv) ? acc[r][v] : 0.f;
+      out(k, reduce_scatter<R * NVP>(a));
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -334,9 +332,9 @@ __device__ __forceinline__ void for_expert_groups(const Union* U, int nrt, Body&
 // Rows per task and 16-B chunks per lane per step, as measured best on the
 // GPU: NVFP4's decode needs the registers, so it streams one chunk deep.
 template <int DT> struct TnShape;
-template <> struct TnShape<kF32> { enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2, SC = 0 }; };
-template <> struct TnShape<kBF16> { enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2, SC = 0 }; };
-template <> struct TnShape<kNVFP4> { enum { GU_RW = 2, GU_U = 1, DN_R = 4, DN_U = 1, SC = 1 }; };
+template <> struct TnShape<kF32> { enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2 }; };
+template <> struct TnShape<kBF16> { enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2 }; };
+template <> struct TnShape<kNVFP4> { enum { GU_RW = 2, GU_U = 1, DN_R = 4, DN_U = 1 }; };
 
 // act[s][f] = silu(gate_e[f] . u[t]) * (up_e[f] . u[t]) for slot s = t*K + j.
 // Tasks: (expert, RW rows of gate and the same RW rows of up); NWV waves per
@@ -373,7 +371,7 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
     };
     nv_dispatch<NVMAX>(nv, [&](auto nvc) {
       constexpr int NV = decltype(nvc)::value;
-      stream_tn<DT, R, UU, NV, 2, (bool)TnShape<DT>::SC>(
+      stream_tn<DT, R, UU, NV>(
           nmine, L.H, nv, [&](int v) { return act_lds + v * tn_vec_floats<DT>(L.H); },
           [&](int k, auto& wr, auto& sr) {
             const int f0 = (a + wv + k * NWV - ui * nrt) * RW;
@@ -386,33 +384,22 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
               sr[RW + r] = DT == kNVFP4 ? L.su + row * sb : nullptr;
             }
           },
-          [&](int k, auto&& acc) {
+          [&](int k, float sum) {
+            // gate value (r, v) at index r NVP + v, its up value P / 2 later:
+            // 32 lanes on
             const int f0 = (a + wv + k * NWV - ui * nrt) * RW;
             const int ln = lane_id();
-            if constexpr (TnShape<DT>::SC) {
-              // gate value (r, v) at index r NVP + v, its up value P / 2
-              // later: 32 lanes on
-              constexpr int NVP = NV <= 1 ? 1 : NV <= 2 ? 2 : NV <= 4 ? 4 : 8;
-              constexpr int LP = R * NVP == 4 ? 2 : R * NVP == 8 ? 3 : 4;
-              auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc),
-                                                         __float_as_uint(acc), false, false);
-              const float upv = __uint_as_float(sw[1]);  // lanes < 32: lane + 32's value
-              const int idx = ln >> (6 - LP), r = idx / NVP, v = idx - (idx / NVP) * NVP;
-              const bool lead = ln < 32 && (ln & ((64 >> LP) - 1)) == 0;
+            constexpr int NVP = tn_nvp(NV), LP = tn_log2(R * NVP);
+            auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum),
+                                                       false, false);
+            const float upv = __uint_as_float(sw[1]);  // lanes < 32: lane + 32's value
+            const int idx = ln >> (6 - LP), r = idx / NVP, v = idx - (idx / NVP) * NVP;
+            const bool lead = ln < 32 && (ln & ((64 >> LP) - 1)) == 0;
 #pragma unroll
-              for (int q = 0; q < NV; ++q)  // constant slot indices (no private array)
-                if (lead && v == q && q < nv)
-                  S.act[(size_t)slot[q] * L.F + f0 + r] =
-                      silu(acc * (ggs * down[q])) * (upv * (gus * down[q]));
-            } else {
-#pragma unroll
-              for (int r = 0; r < RW; ++r)
-#pragma unroll
-                for (int v = 0; v < NV; ++v)
-                  if (v < nv && ln == r * NV + v)
-                    S.act[(size_t)slot[v] * L.F + f0 + r] =
-                        silu(acc[r][v] * (ggs * down[v])) * (acc[RW + r][v] * (gus * down[v]));
-            }
+            for (int q = 0; q < NV; ++q)  // constant slot indices (no private array)
+              if (lead && v == q && q < nv)
+                S.act[(size_t)slot[q] * L.F + f0 + r] =
+                    silu(sum * (ggs * down[q])) * (upv * (gus * down[q]));
           },
           pre);
     });
@@ -448,7 +435,7 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
     };
     nv_dispatch<NVMAX>(nv, [&](auto nvc) {
       constexpr int NV = decltype(nvc)::value;
-      stream_tn<DT, RD, UU, NV, 2, (bool)TnShape<DT>::SC>(
+      stream_tn<DT, RD, UU, NV>(
           nmine, L.F, nv, [&](int v) { return act_lds + v * tn_vec_floats<DT>(L.F); },
           [&](int k, auto& wr, auto& sr) {
             const int c0 = (a + wv + k * NWV - ui * nrt) * RD;
@@ -459,26 +446,16 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
               sr[r] = DT == kNVFP4 ? L.sd + row * sb : nullptr;
             }
           },
-          [&](int k, auto&& acc) {
+          [&](int k, float sum) {
             const int c0 = (a + wv + k * NWV - ui * nrt) * RD;
             const int ln = lane_id();
-            if constexpr (TnShape<DT>::SC) {
-              constexpr int NVP = NV <= 1 ? 1 : NV <= 2 ? 2 : NV <= 4 ? 4 : 8;
-              constexpr int LP = RD * NVP == 4 ? 2 : RD * NVP == 8 ? 3 : 4;
-              const int idx = ln >> (6 - LP), r = idx / NVP, v = idx - (idx / NVP) * NVP;
-              const bool lead = (ln & ((64 >> LP) - 1)) == 0;
+            constexpr int NVP = tn_nvp(NV), LP = tn_log2(RD * NVP);
+            const int idx = ln >> (6 - LP), r = idx / NVP, v = idx - (idx / NVP) * NVP;
+            const bool lead = (ln & ((64 >> LP) - 1)) == 0;
 #pragma unroll
-              for (int q = 0; q < NV; ++q)  // constant slot indices (no private array)
-                if (lead && v == q && q < nv)
-                  y[(size_t)slot[q] * L.H + c0 + r] = acc * (gds * down[q]);
-            } else {
-#pragma unroll
-              for (int r = 0; r < RD; ++r)
-#pragma unroll
-                for (int v = 0; v < NV; ++v)
-                  if (v < nv && ln == r * NV + v)
-                    y[(size_t)slot[v] * L.H + c0 + r] = acc[r][v] * (gds * down[v]);
-            }
+            for (int q = 0; q < NV; ++q)  // constant slot indices (no private array)
+              if (lead && v == q && q < nv)
+                y[(size_t)slot[q] * L.H + c0 + r] = sum * (gds * down[q]);
           },
           pre);
     });
