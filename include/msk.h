@@ -220,19 +220,25 @@ msk_status msk_layer_step_timeline(const msk_layer_cfg *cfg, const msk_layer_wei
  *   MSK_PH_ATTN     split-KV no-max attention partials
  *   MSK_PH_COMBINE  sum of the partials, window bounds
  *   MSK_PH_WO       output projection + residual
- *   MSK_PH_ROUTER   FFN RMSNorm + router logits (+ top-k for one token)
- *   MSK_PH_TOPK     top-k and gating weights (more than one token)
+ *   MSK_PH_ROUTER   FFN RMSNorm + router logits (one token; with several,
+ *                   the router's product on the matrix cores)
+ *   MSK_PH_TOPK     top-k and gating weights (one token: msk_moe_route
+ *                   alone; within msk_layer_step the gate/up kernel selects
+ *                   itself).  Several tokens: the router's K-slice sums,
+ *                   the top-k and the expert union in one kernel
  *   MSK_PH_GATEUP   expert gate/up + SwiGLU
  *   MSK_PH_DOWN     expert down + weighted combine + residual
  *   MSK_PH_STEP     the persistent whole-step kernel, where it runs
  *   MSK_PH_UNION    distinct selected experts and their slots (more than
- *                   one token)
+ *                   one token, msk_expert_ffn alone)
  *   MSK_PH_MOE_SUM  weighted sum of the per-slot expert outputs + residual
- *                   (more than one token)
+ *                   (more than one token; between layers of a stack it also
+ *                   writes the next layer's QKV input terms)
  *   MSK_PH_PREP     RMSNorm of a projection's input into bf16 terms for the
- *                   matrix cores (more than one token, bf16 dense weights)
+ *                   matrix cores (more than one token, bf16 dense weights);
+ *                   before the router it also forms h from Wo's K-slice sums
  *   MSK_PH_DENSE_SUM  sum of a matrix-core projection's K-slice partials
- *                   (+ residual)
+ *                   (+ residual; the QKV product within msk_layer_step)
  * msk_timer_start(mask) forgets earlier records and, from then on, brackets
  * every launch of each phase whose bit (1 << phase) is set in mask with a
  * pair of HIP events that the dispatch itself stamps (hipExtLaunchKernel),
