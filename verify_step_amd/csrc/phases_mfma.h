@@ -502,6 +502,19 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
       __builtin_amdgcn_global_load_lds(vc + off, slot + Gm::RAW + blk * 1024, 16, 0, 0);
     }
   };
+  // this lane's query values and q-norm gains are loaded before the first
+  // tiles are issued: issued after them, they would wait for the tiles on
+  // the in-order load counter (a lane past M reads row 0 and zeroes it)
+  const int d0 = 32 * (ln >> 4);
+  v4f qa[8], qn[8];
+  {
+    const float* q = S.qkv + (size_t)(b * S.Tr + t_me) * NR + (size_t)(j * G + g_me) * D;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qa[e] = *reinterpret_cast<const v4f*>(q + d0 + 4 * e);
+      qn[e] = *reinterpret_cast<const v4f*>(L.q_norm + d0 + 4 * e);
+    }
+  }
 #pragma unroll
   for (int k = 0; k + 1 < Gm::NSLOT; ++k)
     if (p0 + 64 * k < p1) issue(p0 + 64 * k, ring + k * Gm::SLOT);
@@ -510,13 +523,11 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
   v8i qt[3];
   float qinv;
   {
-    const float* q = S.qkv + (size_t)(b * S.Tr + t_me) * NR + (size_t)(j * G + g_me) * D;
-    const int d0 = 32 * (ln >> 4);
     float qf[32];
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; e += 4) {
-      const v4f a = live ? *reinterpret_cast<const v4f*>(q + d0 + e) : v4f{0.f, 0.f, 0.f, 0.f};
+      const v4f a = live ? qa[e >> 2] : v4f{0.f, 0.f, 0.f, 0.f};
       qf[e] = a.x; qf[e + 1] = a.y; qf[e + 2] = a.z; qf[e + 3] = a.w;
       ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
     }
@@ -526,7 +537,7 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
     float mx = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      qf[e] *= rr * L.q_norm[d0 + e];
+      qf[e] *= rr * qn[e >> 2][e & 3];
       mx = fmaxf(mx, fabsf(qf[e]));
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
