@@ -226,12 +226,62 @@ __host__ __device__ inline T1Lds t1_lds(int H, int HqD, int K, int F) {
   return o;
 }
 
+// The input vector of a one-token GEMV is loaded into registers before the
+// weight stream's first loads are issued (up to kT1Regs four-float pieces
+// per thread): loaded after them, it would wait for them on the in-order
+// load counter before the staging could start.  Longer vectors take the
+// plain staging.
+constexpr int kT1Regs = 8;
+struct T1Vec {
+  v4f v[kT1Regs], g[kT1Regs];
+};
+__device__ __forceinline__ void t1_load(const float* x, const float* g, int n, T1Vec& r) {
+#pragma unroll
+  for (int i = 0; i < kT1Regs; ++i) {
+    const int c = (int)threadIdx.x * 4 + i * kBlockThreads * 4;
+    const int cl = c < n ? c : 0;
+    r.v[i] = *reinterpret_cast<const v4f*>(x + cl);
+    if (g) r.g[i] = *reinterpret_cast<const v4f*>(g + cl);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+// act = v * g / sqrt(mean(v^2) + eps) (g given) or act = v, from registers.
+__device__ __forceinline__ void t1_stage(const T1Vec& r, bool norm, int n, float eps, float* act,
+                                         float* red) {
+  float rr = 1.f;
+  if (norm) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kT1Regs; ++i) {
+      const int c = (int)threadIdx.x * 4 + i * kBlockThreads * 4;
+      if (c < n) s += r.v[i].x * r.v[i].x + r.v[i].y * r.v[i].y + r.v[i].z * r.v[i].z + r.v[i].w * r.v[i].w;
+    }
+    rr = 1.0f / sqrtf(block_sum(s, red) / (float)n + eps);
+  }
+#pragma unroll
+  for (int i = 0; i < kT1Regs; ++i) {
+    const int c = (int)threadIdx.x * 4 + i * kBlockThreads * 4;
+    if (c < n) {
+      const v4f a = r.v[i];
+      *reinterpret_cast<v4f*>(act + c) =
+          norm ? v4f{a.x * rr * r.g[i].x, a.y * rr * r.g[i].y, a.z * rr * r.g[i].z, a.w * rr * r.g[i].w}
+               : a;
+    }
+  }
+  __syncthreads();
+}
+
 template <int DT>
 __global__ __launch_bounds__(kBlockThreads) void k_qkv_t1(LayerArgs L, StepArgs S, const float* x) {
   const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
   float* act = reinterpret_cast<float*>(msk_smem + o.act0);
+  float* red = reinterpret_cast<float*>(msk_smem + o.red);
+  const bool regs = L.H <= kT1Regs * kBlockThreads * 4;
+  T1Vec r;
+  if (regs) t1_load(x, L.attn_norm, L.H, r);
   qkv_t1<DT>(L, S, act, blockIdx.x, gridDim.x, [&]() {
-    stage_norm_t1(x, L.attn_norm, L.H, L.eps, act, reinterpret_cast<float*>(msk_smem + o.red));
+    if (regs) t1_stage(r, true, L.H, L.eps, act, red);
+    else stage_norm_t1(x, L.attn_norm, L.H, L.eps, act, red);
   });
 }
 
@@ -240,8 +290,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_wo_t1(LayerArgs L, StepArgs S
                                                          float* h) {
   const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
   float* act = reinterpret_cast<float*>(msk_smem + o.act0);
-  wo_t1<DT>(L, S, x, h, act, blockIdx.x, gridDim.x,
-            [&]() { stage_copy(S.attn_o, L.Hq * L.D, act); });
+  const int n = L.Hq * L.D;
+  const bool regs = n <= kT1Regs * kBlockThreads * 4;
+  T1Vec r;
+  if (regs) t1_load(S.attn_o, nullptr, n, r);
+  wo_t1<DT>(L, S, x, h, act, blockIdx.x, gridDim.x, [&]() {
+    if (regs) t1_stage(r, false, n, 0.f, act, nullptr);
+    else stage_copy(S.attn_o, n, act);
+  });
 }
 
 // Router logits, then top-k in the workgroup that finishes last.
@@ -259,6 +315,15 @@ __global__ __launch_bounds__(kBlockThreads) void k_gateup_t1(LayerArgs L, StepAr
                                                              int* topk_out, int own_topk) {
   const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
   float* u = reinterpret_cast<float*>(msk_smem + o.act0);
+  // u into registers first: its loads then overlap the selection and never
+  // wait behind the expert rows' loads
+  const bool regs = L.H <= kT1Regs * kBlockThreads * 4;
+  T1Vec ur;
+  if (regs) t1_load(S.u, nullptr, L.H, ur);
+  auto stage_u = [&]() {
+    if (regs) t1_stage(ur, false, L.H, 0.f, u, nullptr);
+    else stage_copy(S.u, L.H, u);
+  };
   if (own_topk) {
     // every wave selects the experts itself from the router logits (into
     // scalar registers: no launch, no barrier); workgroup 0 records them
@@ -284,11 +349,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_gateup_t1(LayerArgs L, StepAr
 #pragma unroll
     for (int k = 1; k < kMaxTopK; ++k) selv = lane == k ? sel[k] : selv;
     auto pick = [selv](int j) { return __builtin_amdgcn_readlane(selv, j); };
-    gateup_t1<DT>(L, S, pick, u, blockIdx.x, gridDim.x, [&]() { stage_copy(S.u, L.H, u); });
+    gateup_t1<DT>(L, S, pick, u, blockIdx.x, gridDim.x, stage_u);
   } else {
     const int selv = (threadIdx.x & 63) < L.K ? S.idx[threadIdx.x & 63] : 0;
     gateup_t1<DT>(L, S, [selv](int j) { return __builtin_amdgcn_readlane(selv, j); }, u,
-                  blockIdx.x, gridDim.x, [&]() { stage_copy(S.u, L.H, u); });
+                  blockIdx.x, gridDim.x, stage_u);
   }
 }
 
