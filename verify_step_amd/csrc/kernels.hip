@@ -305,9 +305,16 @@ template <int DT>
 __global__ __launch_bounds__(kBlockThreads) void k_router_t1(LayerArgs L, StepArgs S,
                                                              const float* h) {
   const T1Lds o = t1_lds(L.H, L.Hq * L.D, L.K, L.F);
-  router_t1<DT>(L, S, h, reinterpret_cast<float*>(msk_smem + o.act0),
-                reinterpret_cast<float*>(msk_smem + o.red),
-                reinterpret_cast<float*>(msk_smem + o.act1), blockIdx.x, gridDim.x);
+  float* act = reinterpret_cast<float*>(msk_smem + o.act0);
+  float* red = reinterpret_cast<float*>(msk_smem + o.red);
+  const bool regs = L.H <= kT1Regs * kBlockThreads * 4;
+  T1Vec r;
+  if (regs) t1_load(h, L.ffn_norm, L.H, r);
+  router_t1<DT>(L, S, act, reinterpret_cast<float*>(msk_smem + o.act1), blockIdx.x, gridDim.x,
+                [&]() {
+                  if (regs) t1_stage(r, true, L.H, L.eps, act, red);
+                  else stage_norm_t1(h, L.ffn_norm, L.H, L.eps, act, red);
+                });
 }
 
 template <int DT>
@@ -419,7 +426,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_step_t1(StepLayers PK) {
     stamp();
     grid_sync(gs);
 
-    router_t1<DDT>(L, S, S.h, act0, red, act1, vb, nvb);
+    router_t1<DDT>(L, S, act0, act1, vb, nvb,
+                   [&]() { stage_norm_t1(S.h, L.ffn_norm, L.H, L.eps, act0, red); });
     stamp();
     grid_sync(gs);
 

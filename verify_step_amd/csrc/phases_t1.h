@@ -103,15 +103,15 @@ __device__ void wo_t1(const LayerArgs& L, const StepArgs& S, const float* x, flo
       pre);
 }
 
-// u = RMSNorm(h) * ffn_norm into LDS (workgroup vb also writes its slice of
-// u to global memory); logits[e] = w_router[e] . u.  Workgroup vb owns rows
+// u = RMSNorm(h) * ffn_norm into LDS by stage() (workgroup vb then writes its
+// slice of u to global memory); logits[e] = w_router[e] . u.  Workgroup vb owns rows
 // vb, vb + nvb, ...; each of its waves streams one quarter of every row and
 // the quarters are added in fixed order.  part: LDS [kWaves][kRouterRows].
 constexpr int kRouterRows = 16;
 
-template <int DT>
-__device__ void router_t1(const LayerArgs& L, const StepArgs& S, const float* h, float* act,
-                          float* red, float* part, int vb, int nvb) {
+template <int DT, class Stage>
+__device__ void router_t1(const LayerArgs& L, const StepArgs& S, float* act, float* part, int vb,
+                          int nvb, Stage stage) {
   constexpr int R = 1, U = 2;
   const int w = wave_id();
   const int cols = L.H / kWaves;
@@ -128,7 +128,7 @@ __device__ void router_t1(const LayerArgs& L, const StepArgs& S, const float* h,
         if (lane_id() == 0) part[w * kRouterRows + k] = acc[0];
       },
       [&]() {
-        stage_norm_t1(h, L.ffn_norm, L.H, L.eps, act, red);
+        stage();
         const int per = ((L.H / 4 + nvb - 1) / nvb) * 4;
         const int c0 = vb * per, c1 = c0 + per < L.H ? c0 + per : L.H;
         for (int c = c0 + threadIdx.x * 4; c < c1; c += blockDim.x * 4)
