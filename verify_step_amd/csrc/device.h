@@ -517,9 +517,9 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 // kWaves floats of LDS.
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
-  __syncthreads();
+  lds_barrier();
   if (lane_id() == 0) red[wave_id()] = v;
-  __syncthreads();
+  lds_barrier();
   float t = 0.f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) t += red[w];

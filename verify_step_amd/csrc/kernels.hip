@@ -229,8 +229,9 @@ __host__ __device__ inline T1Lds t1_lds(int H, int HqD, int K, int F) {
 // The input vector of a one-token GEMV is loaded into registers before the
 // weight stream's first loads are issued (up to kT1Regs four-float pieces
 // per thread): loaded after them, it would wait for them on the in-order
-// load counter before the staging could start.  Longer vectors take the
-// plain staging.
+// load counter before the staging could start.  The staging meets the other
+// waves at an LDS-only barrier, which leaves the weight loads in flight.
+// Longer vectors take the plain staging.
 constexpr int kT1Regs = 8;
 struct T1Vec {
   v4f v[kT1Regs], g[kT1Regs];
@@ -268,7 +269,7 @@ __device__ __forceinline__ void t1_stage(const T1Vec& r, bool norm, int n, float
                : a;
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 template <int DT>
@@ -369,8 +370,22 @@ __global__ __launch_bounds__(kBlockThreads) void k_down_t1(LayerArgs L, StepArgs
                                                            float* out) {
   // only the expert activations are staged here: [K][F] after the scratch words
   float* act = reinterpret_cast<float*>(msk_smem + 256);
-  down_t1<DT>(L, S, S.idx, S.wts, act, h, out, nullptr, blockIdx.x, gridDim.x,
-              [&]() { stage_copy(S.act, L.K * L.F, act); });
+  const int n = L.K * L.F;
+  constexpr int kPart = kT1Regs * kBlockThreads * 4;
+  const bool regs = n <= 2 * kPart;
+  T1Vec r0, r1;
+  if (regs) {
+    t1_load(S.act, nullptr, n, r0);
+    if (n > kPart) t1_load(S.act + kPart, nullptr, n - kPart, r1);
+  }
+  down_t1<DT>(L, S, S.idx, S.wts, act, h, out, nullptr, blockIdx.x, gridDim.x, [&]() {
+    if (regs) {
+      t1_stage(r0, false, n, 0.f, act, nullptr);
+      if (n > kPart) t1_stage(r1, false, n - kPart, 0.f, act + kPart, nullptr);
+    } else {
+      stage_copy(S.act, n, act);
+    }
+  });
 }
 
 // The whole one-token step through every layer in one persistent launch.

@@ -342,6 +342,14 @@ __device__ void down_t1(const LayerArgs& L, const StepArgs& S, const int* idx, c
   // lane j holds slot j's expert; a wave-uniform slot reads it back with one
   // cross-lane read
   const int ev = lane_id() < K ? idx[lane_id()] : -1;
+  // and slot j's weight (times the expert's global scale for NVFP4), complete
+  // before the first weight row is issued, so the loop waits for nothing but
+  // the weight rows
+  const float wv = lane_id() < K ? wts[lane_id()] : 0.f;
+  const bool okv = ev >= 0 && ev < L.E;
+  float sv = okv ? wv : 0.f;
+  if (DT == kNVFP4) sv *= okv ? L.gd[ev] : 0.f;
+  asm volatile("" ::"v"(sv));
   // task k = (row block b, slot j): b = k / K by a multiply-high, exact for
   // k < 2^32 / K (K = 1 would need the multiplier 2^32)
   const unsigned mK = 0xffffffffu / (unsigned)K + 1u;
@@ -377,9 +385,7 @@ __device__ void down_t1(const LayerArgs& L, const StepArgs& S, const int* idx, c
         int b, j;
         split(k, b, j);
         const int r0 = (gw + b * nw) * R;
-        const int e = __builtin_amdgcn_readlane(ev, j);
-        const bool ok = e >= 0 && e < L.E;
-        const float s = ok ? wts[j] * (DT == kNVFP4 ? L.gd[e] : 1.f) : 0.f;
+        const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), j));
 #pragma unroll
         for (int r = 0; r < R; ++r) o[r] = fmaf(s, acc[r], o[r]);
         if (j == K - 1) {
