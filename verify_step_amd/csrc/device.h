@@ -501,14 +501,16 @@ __device__ __forceinline__ void stream_t1(int ntask, int ncols, ActFn&& actfn, R
 }
 
 // Maximum over the block (all waves, at most 16); every thread gets it.
-// red is one float of LDS per wave.
+// red is one float of LDS per wave.  NW: the number of waves, if known at
+// compile time (0: read from blockDim).
+template <int NW = 0>
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
   lds_barrier();
   if (lane_id() == 0) red[wave_id()] = v;
   lds_barrier();
   float t = red[0];
-  const int nw = blockDim.x >> 6;
+  const int nw = NW ? NW : (int)(blockDim.x >> 6);
   for (int w = 1; w < nw; ++w) t = fmaxf(t, red[w]);
   return t;
 }

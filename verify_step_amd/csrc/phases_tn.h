@@ -76,6 +76,128 @@ __device__ __forceinline__ float tn_stage(const float* src, int n, float* dst, f
   }
 }
 
+// The nv <= NVMAX input vectors of a group into LDS, vector v from src(v)
+// (src must give a readable vector for every v < NVMAX) to dst + v *
+// tn_vec_floats(n), in tn_stage's format; down[v] gets the factor that undoes
+// the scaling.  Each thread issues the loads of VB vectors times C chunks
+// before it stores any of them: a loop that stored each chunk as it arrived
+// would wait for every load in turn, and, the load counter being in order,
+// for every weight load issued before it.  The LDS stores start after a
+// barrier, so the previous group's readers may still be running at entry.
+// NT is the workgroup size as a constant: blockDim.x is read from the
+// dispatch packet by a global load, which would wait behind the weight loads.
+template <int DT, int NVMAX, int VB, int C, int NT, class Src>
+__device__ __forceinline__ void tn_stage_group(int nv, int n, Src&& src, float* dst, float* red,
+                                               float (&down)[NVMAX]) {
+  constexpr int EPC = DT == kNVFP4 ? 8 : 4;  // inputs per thread per chunk
+  constexpr int step = NT * EPC;
+  const int stride = tn_vec_floats<DT>(n);
+#pragma unroll
+  for (int v = 0; v < NVMAX; ++v) down[v] = 1.f;
+  if constexpr (C == 0) {  // vector by vector, as tn_stage goes
+    lds_barrier();
+#pragma unroll
+    for (int v = 0; v < NVMAX; ++v)
+      if (v < nv) down[v] = tn_stage<DT>(src(v), n, dst + v * stride, red);
+  } else if constexpr (DT == kNVFP4) {
+    if (n > C * step) {  // longer than one batch: the two-pass staging
+      lds_barrier();
+#pragma unroll
+      for (int v = 0; v < NVMAX; ++v)
+        if (v < nv) down[v] = tn_stage<DT>(src(v), n, dst + v * stride, red);
+      return;
+    }
+#pragma unroll
+    for (int v0 = 0; v0 < NVMAX; v0 += VB) {
+      if (v0 >= nv) break;
+      v4f x[VB][C][2];
+#pragma unroll
+      for (int b = 0; b < VB; ++b) {
+        const float* sp = src(v0 + b < NVMAX ? v0 + b : 0);
+#pragma unroll
+        for (int q = 0; q < C; ++q) {
+          const int c = (int)threadIdx.x * 8 + q * step;
+          const int cl = c < n ? c : 0;
+          x[b][q][0] = *reinterpret_cast<const v4f*>(sp + cl);
+          x[b][q][1] = *reinterpret_cast<const v4f*>(sp + cl + 4);
+        }
+      }
+      if (v0 == 0) lds_barrier();
+#pragma unroll
+      for (int b = 0; b < VB; ++b) {
+        const int v = v0 + b;
+        if (v >= NVMAX || v >= nv) break;
+        float m = 0.f;
+#pragma unroll
+        for (int q = 0; q < C; ++q)
+          if ((int)threadIdx.x * 8 + q * step < n)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              m = fmaxf(m, fmaxf(fmaxf(fabsf(x[b][q][h].x), fabsf(x[b][q][h].y)),
+                                 fmaxf(fabsf(x[b][q][h].z), fabsf(x[b][q][h].w))));
+        m = block_max<NT / 64>(m, red);
+        float up = 1.f;
+        if (!(m >= 0x1p-8f && m < 0x1p15f) && m > 0.f && m < __builtin_huge_valf()) {
+          int ex = 0;
+          frexpf(m, &ex);  // m < 2^ex
+          up = ldexpf(1.f, 14 - ex);
+          down[v] = ldexpf(1.f, ex - 14);
+        }
+#pragma unroll
+        for (int q = 0; q < C; ++q) {
+          const int c = (int)threadIdx.x * 8 + q * step;
+          if (c < n) {
+            const v4f a = x[b][q][0], bb = x[b][q][1];
+            *reinterpret_cast<v4u*>(dst + v * stride + tn_gran<DT>(c >> 3) * 4) =
+                v4u{cvt_pk_f16(a.x * up, a.y * up), cvt_pk_f16(a.z * up, a.w * up),
+                    cvt_pk_f16(bb.x * up, bb.y * up), cvt_pk_f16(bb.z * up, bb.w * up)};
+          }
+        }
+      }
+    }
+  } else {
+    // one batch: loads, a barrier (which also keeps the compiler from moving
+    // any load down to its store), stores; a chunk past the end reloads and
+    // rewrites chunk 0 with the same value
+    auto batch = [&](int c0) {
+#pragma unroll
+      for (int v0 = 0; v0 < NVMAX; v0 += VB) {
+        if (v0 >= nv) break;
+        v4f x[VB][C];
+#pragma unroll
+        for (int b = 0; b < VB; ++b) {
+          const float* sp = src(v0 + b < NVMAX ? v0 + b : 0);
+#pragma unroll
+          for (int q = 0; q < C; ++q) {
+            const int c = c0 + q * step;
+            x[b][q] = *reinterpret_cast<const v4f*>(sp + (c < n ? c : 0));
+          }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int b = 0; b < VB; ++b) {
+          const int v = v0 + b;
+          if (v >= NVMAX || v >= nv) break;
+#pragma unroll
+          for (int q = 0; q < C; ++q) {
+            const int c = c0 + q * step;
+            *reinterpret_cast<v4f*>(dst + v * stride + tn_gran<DT>((c < n ? c : 0) >> 2) * 4) =
+                x[b][q];
+          }
+        }
+      }
+    };
+    if (n <= C * step) {
+      batch((int)threadIdx.x * 4);  // straight-line: no loop to merge wait states over
+    } else {
+      lds_barrier();
+#pragma unroll
+      for (int v = 0; v < NVMAX; ++v)
+        if (v < nv) tn_stage<DT>(src(v), n, dst + v * stride, red);
+    }
+  }
+}
+
 // The SUB inputs of sub-block `sub` of chunk `ch` of a staged fp32 vector.
 template <int DT>
 __device__ __forceinline__ void tn_load(const float* v, int ch, int sub, float* a) {
@@ -332,9 +454,20 @@ __device__ __forceinline__ void for_expert_groups(const Union* U, int nrt, Body&
 // Rows per task and 16-B chunks per lane per step, as measured best on the
 // GPU: NVFP4's decode needs the registers, so it streams one chunk deep.
 template <int DT> struct TnShape;
-template <> struct TnShape<kF32> { enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2 }; };
-template <> struct TnShape<kBF16> { enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2 }; };
-template <> struct TnShape<kNVFP4> { enum { GU_RW = 2, GU_U = 1, DN_R = 4, DN_U = 1 }; };
+// Staging: GU_VB / DN_VB input vectors of GU_C / DN_C chunks per thread are
+// loaded per batch (C = 0: vector by vector with tn_stage).  Batched loads
+// measured faster only for NVFP4's down projection (a single batch of three
+// fp32 vectors at expert width 2048); elsewhere they measured the same or
+// slower, and NVFP4's gate/up would lose a wave per SIMD to the registers.
+template <> struct TnShape<kF32> {
+  enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2, GU_VB = 1, GU_C = 0, DN_VB = 1, DN_C = 0 };
+};
+template <> struct TnShape<kBF16> {
+  enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2, GU_VB = 1, GU_C = 0, DN_VB = 1, DN_C = 0 };
+};
+template <> struct TnShape<kNVFP4> {
+  enum { GU_RW = 2, GU_U = 1, DN_R = 4, DN_U = 1, GU_VB = 1, GU_C = 0, DN_VB = 3, DN_C = 1 };
+};
 
 // act[s][f] = silu(gate_e[f] . u[t]) * (up_e[f] . u[t]) for slot s = t*K + j.
 // Tasks: (expert, RW rows of gate and the same RW rows of up); NWV waves per
@@ -362,11 +495,10 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
       slot[v] = __builtin_amdgcn_readfirstlane(U->slots[sidx + (v < nv ? v : 0)]);
     float down[NVMAX];  // undoes the staging's scaling of each input
     auto pre = [&]() {
-      lds_barrier();  // the previous group's readers are done (LDS only: the
-                      // weight loads just issued stay in flight)
-      for (int v = 0; v < nv; ++v)
-        down[v] = tn_stage<DT>(S.u + (size_t)(slot[v] / L.K) * L.H, L.H,
-                               act_lds + v * tn_vec_floats<DT>(L.H), red);
+      // LDS-only barriers: the weight loads just issued stay in flight
+      tn_stage_group<DT, NVMAX, TnShape<DT>::GU_VB, TnShape<DT>::GU_C, NWV * 64>(
+          nv, L.H, [&](int v) { return S.u + (size_t)(slot[v] / L.K) * L.H; }, act_lds, red,
+          down);
       lds_barrier();
     };
     nv_dispatch<NVMAX>(nv, [&](auto nvc) {
@@ -427,10 +559,8 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
       slot[v] = __builtin_amdgcn_readfirstlane(U->slots[sidx + (v < nv ? v : 0)]);
     float down[NVMAX];  // undoes the staging's scaling of each input
     auto pre = [&]() {
-      lds_barrier();
-      for (int v = 0; v < nv; ++v)
-        down[v] = tn_stage<DT>(S.act + (size_t)slot[v] * L.F, L.F,
-                               act_lds + v * tn_vec_floats<DT>(L.F), red);
+      tn_stage_group<DT, NVMAX, TnShape<DT>::DN_VB, TnShape<DT>::DN_C, NWV * 64>(
+          nv, L.F, [&](int v) { return S.act + (size_t)slot[v] * L.F; }, act_lds, red, down);
       lds_barrier();
     };
     nv_dispatch<NVMAX>(nv, [&](auto nvc) {
