@@ -799,7 +799,7 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
   const int wgrid = grid_for_waves(L.H / DenseRowsHost(nv));
   if (one) {
     const size_t lds = t1_vec_lds(L);
-    const int g = t1_grid((L.H + 3) / 4);
+    const int g = t1_grid((L.H + 1) / 2);
     if (L.ddt == kBF16) {
       MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_wo_t1<kBF16>), lds));
       MSK_TRY(launch_x(kPhWo, k_wo_t1<kBF16>, g, lds, st, L, S, x, h));
@@ -877,7 +877,7 @@ static hipError_t launch_ffn_t1(const LayerArgs& L, const StepArgs& S, const flo
   MSK_TRY(launch_x(kPhGateUp, k_gateup_t1<DT>, t1_grid((long long)L.K * (L.F / 2)), vlds, st, L, S,
                    topk_out, (int)own_topk));
   MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_down_t1<DT>), alds));
-  MSK_TRY(launch_x(kPhDown, k_down_t1<DT>, t1_grid((L.H + 3) / 4), alds, st, L, S, h, out));
+  MSK_TRY(launch_x(kPhDown, k_down_t1<DT>, t1_grid((L.H + 2) / 3), alds, st, L, S, h, out));
   return hipSuccess;
 }
 

@@ -78,7 +78,10 @@ __device__ void qkv_t1(const LayerArgs& L, const StepArgs& S, const float* act, 
 template <int DT, class Pre>
 __device__ void wo_t1(const LayerArgs& L, const StepArgs& S, const float* x, float* h,
                       const float* act, int vb, int nvb, Pre&& pre) {
-  constexpr int R = 4, U = 2;
+  // two rows per task: at hidden 6144 one task per wave then gives twice the
+  // waves of four-row tasks, and with them twice the rows in flight (Wo went
+  // from 15.3 to 13.6 us; QKV, which has 2048 four-row tasks, did not gain)
+  constexpr int R = 2, U = 2;
   const int NI = L.Hq * L.D;
   const size_t rb = dense_row_bytes(DT, NI);
   const int gw = gwave(vb, nvb), nw = nvb * kWaves;
@@ -333,7 +336,9 @@ template <int DT, class Pre>
 __device__ void down_t1(const LayerArgs& L, const StepArgs& S, const int* idx, const float* wts,
                         const float* act, const float* h, float* out, float* out2, int vb,
                         int nvb, Pre&& pre) {
-  constexpr int R = 4, U = 2;
+  // three rows per task: at hidden 6144 that is 2048 row blocks, one per
+  // wave of the 512 workgroups whose staged activations fit in LDS at once
+  constexpr int R = 3, U = 2;
   const size_t rb = expert_row_bytes(DT, L.F);
   const size_t sb = (size_t)L.F / 16;
   const int gw = gwave(vb, nvb), nw = nvb * kWaves;
