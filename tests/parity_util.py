@@ -138,12 +138,15 @@ class StackDrift:
     that margin that the GPU routes differently has legitimately left the
     oracle's trajectory: it is dropped from this layer's comparisons, and it
     and the later tokens of its request (which attend to its keys) from every
-    later layer's.  At most `max_lost` of the tokens may be dropped."""
+    later layer's.  At most `max_moved` tokens over the whole stack may be
+    routed differently this way (the committed runs moved none; one allows a
+    single genuine near-tie without hiding a systematic drift)."""
 
-    def __init__(self, n_req, Tr, margin0, drift, max_lost=0.25):
+    def __init__(self, n_req, Tr, margin0, drift, max_moved=1):
         self.Tr = Tr
         self.alive = np.ones(n_req * Tr, bool)
-        self.margin0, self.drift, self.max_lost = margin0, drift, max_lost
+        self.margin0, self.drift, self.max_moved = margin0, drift, max_moved
+        self.moved = 0
 
     def routing(self, layer, idx_gpu, logits_ref, idx_ref, k):
         """Checks the layer's routing; returns the mask of tokens to compare
@@ -161,10 +164,12 @@ class StackDrift:
         for t in np.nonzero(moved)[0]:
             b = t // self.Tr
             self.alive[t:(b + 1) * self.Tr] = False
+        self.moved += int(moved.sum())
         lost = 1.0 - self.alive.mean()
         print(f"[gpu-parity] layer {layer}: {int((self.alive & near).sum())} tokens inside the "
               f"routing margin, {int(moved.sum())} routed differently, {lost:.0%} dropped", flush=True)
-        assert lost <= self.max_lost, f"{lost:.0%} of the tokens left the oracle's trajectory"
+        assert self.moved <= self.max_moved, \
+            f"{self.moved} tokens left the oracle's trajectory (at most {self.max_moved})"
         return here
 
 

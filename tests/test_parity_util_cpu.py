@@ -34,7 +34,7 @@ def test_layer0_flip_inside_margin0_fails():
 
 def test_later_layer_flip_inside_drift_margin_drops_the_request_tail():
     lg, idx = _logits()
-    d = StackDrift(2, 3, margin0=1e-5, drift=1e-3, max_lost=0.5)
+    d = StackDrift(2, 3, margin0=1e-5, drift=1e-3, max_moved=1)
     here = d.routing(0, idx, lg, idx, 2)
     assert here.all()
     gpu = idx.copy()
@@ -49,10 +49,16 @@ def test_later_layer_flip_inside_drift_margin_drops_the_request_tail():
         d.routing(2, gpu, lg, idx, 2)
 
 
-def test_too_many_dropped_tokens_fail():
+def test_a_second_moved_token_fails():
     lg, idx = _logits()
-    d = StackDrift(2, 3, margin0=1e-5, drift=1e-3, max_lost=0.25)
+    lg = lg.copy()
+    lg[4] = [3.0, 1.0, 0.9999, -1.0]       # a second near tie, in request 1
+    idx = np.argsort(-lg, axis=1, kind="stable")[:, :2]
+    d = StackDrift(2, 3, margin0=1e-5, drift=1e-3)
     gpu = idx.copy()
-    gpu[1] = [0, 2]                        # drops tokens 1 and 2: a third of all
+    gpu[1] = [0, 2]
+    d.routing(1, gpu, lg, idx, 2)          # one genuine near-tie is allowed
+    gpu = idx.copy()
+    gpu[4] = [0, 2]
     with pytest.raises(AssertionError):
-        d.routing(1, gpu, lg, idx, 2)
+        d.routing(2, gpu, lg, idx, 2)      # a second one is not
