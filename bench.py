@@ -14,7 +14,12 @@ inputs already resident in HBM.  Prints one JSON line:
   kernels        the same figures for every phase
   cpu_baseline   the CPU oracle timed on the same workload on this host
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+With no --workload, every workload is measured and printed on a line of its
+own; the largest single-GPU workload (verify-bf16-128k: 2 x 8 draft tokens
+over 131072 e4m3 positions per request, bf16 experts) comes last and carries
+the CPU baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
 """
 import argparse
 import json
@@ -121,26 +126,44 @@ def stored_traffic(kernel, workload):
     return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
 
 
+def _blas_threads():
+    """Threads the host BLAS actually runs with (what the oracle's products use)."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(p, budget_s=30.0):
-    """Time the CPU oracle on the same workload: the whole layer step when it
-    fits the budget (it does for one decode token), else one layer."""
+    """Time the CPU oracle on the same workload: whole layers of the step
+    until the budget is spent (at least one).  Every weight and cache byte a
+    layer can read is copied to host memory before its timer starts, so the
+    figure is the oracle's arithmetic, not the device-to-host copies."""
     from oracle import layer as ol
     specs = p.specs
-    cores = len(os.sched_getaffinity(0))
     cur = p.x.double().cpu().numpy()
-    t0 = time.perf_counter()
+    spent = 0.0
     done = 0
     for l in range(len(specs)):
-        w = synth.host_weights(p.weights[l])
-        kv = synth.host_kv(p.kv[l])
+        w = synth.host_weights(p.weights[l], lazy_experts=False)
+        kv = dict(k=synth.to_numpy(p.kv[l]["k"]), v=synth.to_numpy(p.kv[l]["v"]),
+                  cap=p.kv[l]["cap"])
+        t0 = time.perf_counter()
         ol.layer_step(specs[l], w, kv, p.kv_len, p.tokens_per_req, cur)
+        spent += time.perf_counter() - t0
         done += 1
-        if time.perf_counter() - t0 > budget_s:
+        del w, kv
+        if spent > budget_s:
             break
-    dt = time.perf_counter() - t0
-    return dict(value=dt / done * 1e6, unit="us per layer-step", cores=cores, kind="oracle",
+    return dict(value=spent / done * 1e6, unit="us per layer-step", cores=_blas_threads(),
+                kind="oracle",
                 sample=f"{done} of {len(specs)} layer step(s) of the benchmarked workload, "
-                       f"float64 NumPy, including the host copies of the selected experts")
+                       f"float64 NumPy on host copies of the weights and cache (copies "
+                       f"made before the timer starts)")
 
 
 def unfused_step(p, x, ws):
@@ -249,34 +272,16 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode-bf16")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
-                    help="fused: msk_layer_step; unfused: the msk_attn_step -> msk_moe_route "
-                         "-> msk_expert_ffn calls per layer")
-    ap.add_argument("--timeline", action="store_true",
-                    help="also print per-phase times of the persistent kernel")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a 1 GiB device copy (counter calibration) and exit")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this layer step runs on a single MI355X "
-              "(no multi-GPU path is built)", file=sys.stderr)
-        sys.exit(2)
-    if args.calibrate_copy:
-        copy_calibration()
-        return
+HEADLINE = "verify-bf16-128k"
+ALL_WORKLOADS = ["tiny-fp32", "decode-bf16", "stack4-nvfp4", "longctx-nvfp4", HEADLINE]
 
+
+def measure(name, args, with_cpu):
+    """Time one workload: returns its JSON record."""
     dev = "cuda:0"
-    torch.cuda.set_device(0)
-    p = synth.make_problem(args.workload, device=dev)
-    for spec, w in zip(p.specs, p.weights):
-        spec["softmax_shift"] = msk.softmax_shift(w["q_norm"], w["k_norm"], spec["head_dim"])
+    p = synth.make_problem(name, device=dev)
+    for spec in p.specs:
+        spec["softmax_shift"] = 0.0     # the library derives the score bound from the gains
     n_layers = len(p.specs)
     ws = msk.new_workspace(p.specs, p.kv_len, p.tokens_per_req, device=dev)
     x = p.x.clone()
@@ -323,7 +328,10 @@ def main():
     bytes_launch = d["bytes"] / d["launches"] if dom != "step" else nbytes
     kgbs = bytes_launch / (avg_us * 1e-6) / 1e9
     kname = kernel_name(dom, p.specs[0], p.T, p.tokens_per_req)
-    traffic = stored_traffic(kname, args.workload)
+    traffic = stored_traffic(kname, name)
+    # weight-streaming time of the step: its distinct dense, router and
+    # expert bytes at the HBM peak (the pages' denominator, without KV)
+    stream_us = (parts["dense"] + parts["experts"]) / (HBM_PEAK_GBS * 1e3)
 
     out = {
         "metric": METRIC,
@@ -338,7 +346,7 @@ def main():
         "vs_baseline": None,
         "dtype": p.specs[0]["dense_dtype"],
         "data": "synthetic",
-        "config": {"workload": args.workload, "n_layers": n_layers, "n_req": p.n_req,
+        "config": {"workload": name, "n_layers": n_layers, "n_req": p.n_req,
                    "tokens_per_req": p.tokens_per_req, "kv_len": p.kv_len,
                    "dense": p.specs[0]["dense_dtype"], "experts": p.specs[0]["expert_dtype"],
                    "kv": p.specs[0]["kv_dtype"]},
@@ -346,6 +354,7 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "algorithmic_bytes": nbytes,
         "bytes_breakdown": parts,
+        "step_over_weight_streaming": round(ms_step * 1e3 / stream_us, 3),
         "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": kname, "phase": dom,
@@ -356,13 +365,47 @@ def main():
                          "gbs": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1)
                          if ph != "step" else None}
                     for ph, r in timed.items()},
-        "path": args.path,
+        "path": "layer_step" if args.path == "fused" else "per_op_calls",
     }
     if args.timeline and args.path == "fused":
         out["timeline"] = timeline(p, ws, x)
-    if not args.no_cpu_baseline:
+    if with_cpu:
         out["cpu_baseline"] = cpu_baseline(p)
-    print(json.dumps(out), flush=True)
+    del p, ws, x, step
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="all",
+                    help="one workload name, or 'all': every workload, each on a line of its "
+                         f"own, the largest ({HEADLINE}) last")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
+                    help="fused: msk_layer_step; unfused: the msk_attn_step -> msk_moe_route "
+                         "-> msk_expert_ffn calls per layer")
+    ap.add_argument("--timeline", action="store_true",
+                    help="also print per-phase times of the persistent kernel")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this layer step runs on a single MI355X "
+              "(no multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        copy_calibration()
+        return
+    torch.cuda.set_device(0)
+    names = ALL_WORKLOADS if args.workload == "all" else [args.workload]
+    for name in names:
+        # the CPU oracle is timed once, beside the headline workload
+        with_cpu = not args.no_cpu_baseline and name == names[-1]
+        print(json.dumps(measure(name, args, with_cpu)), flush=True)
 
 
 if __name__ == "__main__":

@@ -87,8 +87,9 @@ typedef struct {
   float softmax_shift; /* c: fixed score bound; attention weights are
                           exp(s - c) summed without a running maximum.  Any c
                           with s - c < 88 for every score gives the same result
-                          up to rounding; sqrt(D)*max|g_q|*max|g_k| bounds the
-                          scores of QK-normalised keys                            */
+                          up to rounding.  0: the library takes the bound of
+                          QK-normalised scores from the gains on the device,
+                          c = sqrt(D) * max|q_norm| * max|k_norm|             */
   int32_t dense_dtype;  /* MSK_F32 | MSK_BF16: wq, wk, wv, wo, w_router          */
   int32_t expert_dtype; /* MSK_F32 | MSK_BF16 | MSK_NVFP4: w_gate, w_up, w_down  */
   int32_t kv_dtype;     /* MSK_F32 (head_dim <= 64) | MSK_BF16 | MSK_E4M3        */
@@ -153,7 +154,11 @@ msk_status msk_workspace_status(void *ws, size_t ws_bytes, void *stream);
 
 /* Attention half of a layer (steps: attention RMSNorm, QKV projection,
  * QK-norm, KV append, windowed no-max split-KV attention, output projection
- * with residual).
+ * with residual).  Defined by: QK-norm and softmax without a running maximum,
+ * chunks reduced independently (brifing.si page, "Removing Attention
+ * Bottlenecks"); sliding-window 2,048 or full-context attention (ainewsbites
+ * page, "One program replaces many kernel boundaries"; brifing.si page, "Model
+ * Architecture Details"); the fp8 cache (aitop.news page, opening paragraphs).
  *   x      [T][H] fp32 in
  *   h      [T][H] fp32 out: x + wo . attn
  *   attn_o [T][Hq*D] fp32 out, nullable: attention output before wo
@@ -168,7 +173,9 @@ msk_status msk_attn_step(const msk_layer_cfg *cfg, const msk_layer_weights *w,
 
 /* Router: u = RMSNorm(h) * ffn_norm; logits = w_router . u (fp32); per token the
  * top_k experts by logit (descending; the lower index wins a tie) and their
- * weights (softmax over the selected logits).
+ * weights (softmax over the selected logits).  Defined by: every layer routes
+ * each token to 8 of 256 experts (ainewsbites page, "One program replaces many
+ * kernel boundaries"; brifing.si page, "Model Architecture Details").
  *   h [T][H] in; u [T][H] out; topk_idx [T][k] int32 out; topk_w [T][k] out;
  *   logits [T][E] out, nullable. */
 msk_status msk_moe_route(const msk_layer_cfg *cfg, const msk_layer_weights *w,
@@ -178,16 +185,26 @@ msk_status msk_moe_route(const msk_layer_cfg *cfg, const msk_layer_weights *w,
 
 /* Experts: out[t] = h[t] + sum_j topk_w[t][j] * down_e(silu(gate_e u[t]) * up_e u[t])
  * with e = topk_idx[t][j], summed in slot order j = 0..k-1.  Only the distinct
- * selected experts are read, each once for all tokens routed to it.
+ * selected experts are read, each once for all tokens routed to it.  Defined
+ * by: the selected experts' weights are fetched once routing is known, and a
+ * verify step streams the step's distinct experts (ainewsbites page, "One
+ * program replaces many kernel boundaries" and "Reported decode and
+ * verification gains"); NVFP4 experts with one scale per 16 values (brifing.si
+ * page, "Expert Weight Quantization").
  *   u, h [T][H] in; topk_idx, topk_w [T][k] in; out [T][H] out (may equal h). */
 msk_status msk_expert_ffn(const msk_layer_cfg *cfg, const msk_layer_weights *w,
                           int32_t n_tokens, const float *u, const int32_t *topk_idx,
                           const float *topk_w, const float *h, float *out, void *ws,
                           size_t ws_bytes, void *stream);
 
-/* A whole decode/verify step through n_layers (1..MSK_MAX_STACK) layers,
- * enqueued as the per-phase kernels of every layer in order on one stream:
- * layer l's output is layer l+1's input.  cfg, w and kv are
+/* A whole decode/verify step through n_layers (1..MSK_MAX_STACK) layers.
+ * Defined by: one program runs every layer of a decode or verify step
+ * (ainewsbites page, "One program replaces many kernel boundaries"; brifing.si
+ * page, "Megakernel Architecture Benefits"), and a verify step checks all
+ * draft tokens of a request in one pass (brifing.si page, "Speculative
+ * Decoding Integration").  The step is enqueued on one stream as the
+ * per-phase kernels of every layer in order: layer l's output is layer l+1's
+ * input.  cfg, w and kv are
  * arrays of n_layers entries (shapes must agree; window and dtypes may differ).
  *   x         [T][H] fp32 in/out: the step's input, replaced by its output
  *   layer_out [n_layers][T][H] out, nullable: each layer's output

@@ -155,7 +155,8 @@ def attention_block(spec, w, kv, kv_len, tokens_per_req, x, kv_block=65536):
     H, Hq, Hkv, D = spec["hidden"], spec["n_q_heads"], spec["n_kv_heads"], spec["head_dim"]
     G = Hq // Hkv
     eps = spec["rms_eps"]
-    shift = spec["softmax_shift"]
+    # a given shift of 0 stands for the score bound taken from the gains
+    shift = spec["softmax_shift"] or score_shift(w["q_norm"], w["k_norm"], D)
     dd, kd = spec["dense_dtype"], spec["kv_dtype"]
     Tr = tokens_per_req
     n_req = len(kv_len)

@@ -54,6 +54,34 @@ CASES = {
                                               expert="nvfp4", kv_len=[300], windows=[128])),
     "stack-odd-nvfp4": ("stack4-nvfp4", dict(dims=dict(_SMALL, hidden=480, ffn_dim=96),
                                              kv_len=[300], windows=[128, 0])),
+    # one token over an fp8 cache (the vector attention kernel on e4m3
+    # bytes), head_dim 128 with a sliding window and head_dim 64 full
+    "decode-e4m3-d128": ("decode-bf16", dict(dims=_SMALL, kv="e4m3", kv_len=[3000],
+                                             windows=[2048])),
+    "decode-e4m3-d64": ("decode-bf16", dict(dims=dict(_SMALL, head_dim=64, n_q_heads=8),
+                                            kv="e4m3", kv_len=[700, 3], n_req=2, windows=[0])),
+    # matrix-core attention over e4m3 caches at head_dim 64 (one wave per
+    # item) and head_dim 32 (two waves)
+    "verify-e4m3-d64": ("verify-bf16-128k", dict(dims=dict(_SMALL, head_dim=64, n_q_heads=8),
+                                                 kv_len=[900, 65], tokens_per_req=4)),
+    "verify-e4m3-d32": ("verify-bf16-128k", dict(dims=dict(_SMALL, head_dim=32, n_q_heads=8),
+                                                 kv_len=[500, 31])),
+    # fp32 weights and cache with several tokens: the vector dense kernels
+    # and the fp32 multi-token expert kernels
+    "tiny-fp32-t4": ("tiny-fp32", dict(tokens_per_req=4, n_req=2, kv_len=[512, 100])),
+    # histories long enough that each attention item runs many 64-position
+    # tiles through the LDS ring: e4m3 at 48 rows per kv head (about 11 tiles
+    # per item), e4m3 at 24 rows (position-split wave pairs, about 7), bf16
+    # at 48 rows (about 5)
+    "verify-longchunk": ("verify-bf16-128k", dict(dims=dict(_SMALL, n_kv_heads=2),
+                                                  kv_len=[200000, 70000])),
+    "longctx-longchunk": ("longctx-nvfp4", dict(dims=dict(_SMALL, top_k=4, n_experts=16),
+                                                kv_len=[150000, 20000, 5, 0])),
+    "verify-bf16kv-longchunk": ("verify-bf16-128k", dict(dims=_SMALL, kv="bf16",
+                                                         kv_len=[100000], n_req=1)),
+    # one token over a long e4m3 history: vector attention items of five tiles
+    "decode-e4m3-long": ("decode-bf16", dict(dims=_SMALL, kv="e4m3", kv_len=[300000],
+                                             windows=[0])),
 }
 
 

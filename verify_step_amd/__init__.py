@@ -7,12 +7,13 @@ raises instead of computing anything elsewhere.
 
 Layer specs are dicts with the keys hidden, n_q_heads, n_kv_heads, head_dim,
 n_experts, top_k, ffn_dim, window, rms_eps, softmax_shift, dense_dtype,
-expert_dtype, kv_dtype (dtype strings 'f32', 'bf16', 'e4m3', 'nvfp4').
+expert_dtype, kv_dtype (dtype strings 'f32', 'bf16', 'e4m3', 'nvfp4');
+softmax_shift 0 (or None) lets the library derive the score bound from the
+QK-norm gains on the device.
 Weights are dicts of device tensors named as in the C header; a KV cache is a
 dict with tensors 'k', 'v' of shape [n_req][Hkv][cap][D].
 """
 import ctypes
-import math
 import os
 
 import torch
@@ -127,16 +128,10 @@ def _stream(stream=None):
 
 # ----------------------------------------------------------- marshalling
 
-def softmax_shift(q_norm, k_norm, head_dim):
-    """Fixed softmax shift from the QK-norm gains: sqrt(D) max|g_q| max|g_k|
-    bounds every score of a normalised query against a normalised key."""
-    return float(math.sqrt(head_dim) * float(q_norm.abs().max()) * float(k_norm.abs().max()))
-
-
 def make_cfg(spec):
     return LayerCfg(spec["hidden"], spec["n_q_heads"], spec["n_kv_heads"], spec["head_dim"],
                     spec["n_experts"], spec["top_k"], spec["ffn_dim"], spec["window"],
-                    spec["rms_eps"], spec["softmax_shift"], DTYPE[spec["dense_dtype"]],
+                    spec["rms_eps"], spec["softmax_shift"] or 0.0, DTYPE[spec["dense_dtype"]],
                     DTYPE[spec["expert_dtype"]], DTYPE[spec["kv_dtype"]])
 
 

@@ -528,6 +528,23 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+// Fixed softmax shift of a layer: the given value, or (given 0) the score
+// bound sqrt(D) * max|q_norm| * max|k_norm| of a QK-normalised query against
+// a QK-normalised key.  The softmax does not depend on it; it only keeps
+// exp(s - c) in range.  The gains are read as two values per lane (D <= 128)
+// by gain_pair, issued together with a kernel's other prologue loads, and
+// reduced over the wave by layer_shift where the loads have landed anyway.
+__device__ __forceinline__ v2f gain_pair(const float* g, int D) {
+  const int ln = lane_id();
+  return v2f{ln < D ? g[ln] : 0.f, ln + 64 < D ? g[ln + 64] : 0.f};
+}
+__device__ __forceinline__ float layer_shift(float given, v2f gq, v2f gk, int D) {
+  if (given != 0.f) return given;
+  const float mq = wave_max(fmaxf(fabsf(gq.x), fabsf(gq.y)));
+  const float mk = wave_max(fmaxf(fabsf(gk.x), fabsf(gk.y)));
+  return sqrtf((float)D) * mq * mk;
+}
+
 // ---------------------------------------------------- grid-wide barrier
 // Barrier words in the caller's workspace (zero before first use):
 //   words[0]            generation, advanced by workgroup 0 at each barrier

@@ -301,7 +301,8 @@ __global__ __launch_bounds__(kBlockThreads) void k_wo_t1(LayerArgs L, StepArgs S
   });
 }
 
-// Router logits, then top-k in the workgroup that finishes last.
+// Router logits of one token (the top-k is taken by the kernel that reads
+// them: k_topk, or every wave of k_gateup_t1 within a layer step).
 template <int DT>
 __global__ __launch_bounds__(kBlockThreads) void k_router_t1(LayerArgs L, StepArgs S,
                                                              const float* h) {
@@ -882,13 +883,22 @@ static hipError_t launch_ffn_t1(const LayerArgs& L, const StepArgs& S, const flo
 }
 
 
-// Resident workgroups of a kernel at `lds` bytes, times the CU count.
+// Resident workgroups of a kernel at `lds` bytes, times the CU count,
+// remembered per (kernel, LDS size): the expert kernels' LDS depends on the
+// hidden and FFN sizes of the call.
 static int resident_grid(const void* fn, size_t lds, int threads = kBlockThreads) {
+  struct Entry { const void* fn; size_t lds; int threads, grid; };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  std::lock_guard<std::mutex> g(mu);
+  for (const Entry& e : cache)
+    if (e.fn == fn && e.lds == lds && e.threads == threads) return e.grid;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, lds) != hipSuccess ||
       n < 1)
     n = 1;
-  return n * cu_count();
+  cache.push_back(Entry{fn, lds, threads, n * cu_count()});
+  return cache.back().grid;
 }
 
 // token vectors staged per gate/up pass: four fp32 vectors (96 KB at
@@ -915,8 +925,7 @@ static hipError_t launch_experts_tn(const LayerArgs& L, const StepArgs& S, hipSt
     auto fn = k_gateup_tn<DT, kGateUpTokens<DT>, nwv>;
     const size_t lds = ((size_t)kGateUpTokens<DT> * tn_vec_floats<DT>(L.H) + nwv) * sizeof(float);
     MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
-    static int grid = 0;
-    if (grid == 0) grid = resident_grid(reinterpret_cast<const void*>(fn), lds, nwv * 64);
+    const int grid = resident_grid(reinterpret_cast<const void*>(fn), lds, nwv * 64);
     MSK_TRY(launch_b(kPhGateUp, fn, grid, nwv * 64, lds, st, L, S));
   }
   {
@@ -924,8 +933,7 @@ static hipError_t launch_experts_tn(const LayerArgs& L, const StepArgs& S, hipSt
     auto fn = k_down_tn<DT, kDownTokens<DT>, nwv>;
     const size_t lds = ((size_t)kDownTokens<DT> * tn_vec_floats<DT>(L.F) + nwv) * sizeof(float);
     MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
-    static int grid = 0;
-    if (grid == 0) grid = resident_grid(reinterpret_cast<const void*>(fn), lds, nwv * 64);
+    const int grid = resident_grid(reinterpret_cast<const void*>(fn), lds, nwv * 64);
     MSK_TRY(launch_b(kPhDown, fn, grid, nwv * 64, lds, st, L, S));
   }
   return hipSuccess;

@@ -287,6 +287,7 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
 
   // this wave's query rows, normalised and pre-scaled, and their windows
   constexpr int QD = (D + 63) / 64;
+  const v2f gq2 = gain_pair(L.q_norm, D), gk2 = gain_pair(L.k_norm, D);
   {
     float qv[RPW][QD];
 #pragma unroll
@@ -352,6 +353,7 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
   __syncthreads();
   // positions before the group's earliest window start are never visible
   const int lo_min = win[0];
+  const float shift = layer_shift(L.shift, gq2, gk2, D);
 
   float lsum[RPW];
   float o[RPW][EPLV];
@@ -438,7 +440,7 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
       for (int r = 0; r < RPW; ++r) {
         const int mm = wv * RPW + r;
         const bool ok = ln < npos && pos >= win[2 * mm] && pos <= win[2 * mm + 1];
-        const float e = ok ? __expf(s[r] - L.shift) : 0.f;
+        const float e = ok ? __expf(s[r] - shift) : 0.f;
         et[mm * 64 + ln] = e;
         lsum[r] += e;
       }

@@ -27,8 +27,8 @@
 // are rebuilt from the QKV output as stored (QK-norm on k, cast to the cache
 // format), and the row-group-0 item writes them into the cache.
 //
-// Cite: no-max softmax with a fixed score bound (ainewsbites, "Removing
-// attention bottlenecks"), split-KV partials combined by plain sums.
+// Cite: no-max softmax with a fixed score bound (brifing.si page, "Removing
+// Attention Bottlenecks"), split-KV partials combined by plain sums.
 #pragma once
 #include "phases.h"
 
@@ -151,6 +151,7 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
 
   // qhat as the B operand of the score product: lane holds row m, d = 32 ks + 8 (ln >> 4) + e
   bf16x8 qh[DS], ql[DS];
+  const v2f gq2 = gain_pair(L.q_norm, D), gk2 = gain_pair(L.k_norm, D);
   {
     const float* q = S.qkv + (size_t)(b * S.Tr + t_me) * NR + (size_t)(j * G + g_me) * D;
     float qf[DS][8];
@@ -190,7 +191,7 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
     lo_all = max(lo_all, __shfl_xor(lo_all, o));
     hi_all = min(hi_all, __shfl_xor(hi_all, o));
   }
-  const float shift2 = L.shift * 1.44269504088896341f;
+  const float shift2 = layer_shift(L.shift, gq2, gk2, D) * 1.44269504088896341f;
   // 1/rms of the step's new keys that fall in this chunk
   const int tn0 = p0 - Lb > 0 ? p0 - Lb : 0;
   const int tn1 = p1 - Lb < S.Tr ? p1 - Lb : S.Tr;
@@ -507,6 +508,7 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
   // the in-order load counter (a lane past M reads row 0 and zeroes it)
   const int d0 = 32 * (ln >> 4);
   v4f qa[8], qn[8];
+  const v2f gq2 = gain_pair(L.q_norm, D), gk2 = gain_pair(L.k_norm, D);
   {
     const float* q = S.qkv + (size_t)(b * S.Tr + t_me) * NR + (size_t)(j * G + g_me) * D;
 #pragma unroll
@@ -568,7 +570,7 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
     lo_all = max(lo_all, __shfl_xor(lo_all, o));
     hi_all = min(hi_all, __shfl_xor(hi_all, o));
   }
-  const float shift2 = L.shift * 1.44269504088896341f;
+  const float shift2 = layer_shift(L.shift, gq2, gk2, D) * 1.44269504088896341f;
   const int tn0 = p0 - Lb > 0 ? p0 - Lb : 0;
   const int tn1 = p1 - Lb < S.Tr ? p1 - Lb : S.Tr;
   for (int t = tn0 + wv; t < tn1; t += NW) {

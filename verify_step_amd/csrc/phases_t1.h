@@ -275,21 +275,6 @@ __device__ void phase_topk(const LayerArgs& L, const StepArgs& S, int* topk_out,
   }
 }
 
-// The workgroup that finishes last (counter in the workspace) gets true; the
-// counter is returned to zero by that workgroup.  No workgroup waits.
-__device__ inline bool last_workgroup(unsigned* counter, int* flag_lds) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev =
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = prev == gridDim.x - 1;
-    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag_lds = last;
-  }
-  __syncthreads();
-  return *flag_lds != 0;
-}
-
 // act[j][f] = silu(gate_e[f] . u) * (up_e[f] . u), e = idx[j]; u staged in LDS.
 template <int DT, class Sel, class Pre>
 __device__ void gateup_t1(const LayerArgs& L, const StepArgs& S, Sel&& idx, const float* u,
