@@ -215,6 +215,26 @@ msk_status msk_layer_step(const msk_layer_cfg *cfg, const msk_layer_weights *w,
                           float *x, float *layer_out, int32_t *topk_idx, int32_t *win,
                           void *ws, size_t ws_bytes, void *stream);
 
+/* msk_layer_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same step and outputs, with its scratch in an array the library keeps
+ * on every GPU it runs on (msk_noalloc_scratch_bytes() bytes per GPU, 64 MiB,
+ * held until the process ends) instead of a caller workspace.  It calls no
+ * hipMalloc, hipFree or other allocating routine (no host allocation either).
+ * Arguments as msk_layer_step, minus the workspace.  Errors: as
+ * msk_layer_step; MSK_ERR_WORKSPACE if the step needs more scratch than the
+ * array holds (msk_workspace_size above msk_noalloc_scratch_bytes()).  Every
+ * call on one GPU shares that GPU's array: calls that may overlap on one GPU
+ * (several streams or threads) race and must not be issued.  The array keeps
+ * the previous call's contents; each call zeroes the words it needs zeroed.
+ * Kernel timing (msk_timer_start) does not record these calls. */
+msk_status msk_layer_step_noalloc(const msk_layer_cfg *cfg, const msk_layer_weights *w,
+                                  const msk_kv *kv, int32_t n_layers, const msk_batch *batch,
+                                  float *x, float *layer_out, int32_t *topk_idx, int32_t *win,
+                                  void *stream);
+/* Bytes of the per-GPU scratch array of msk_layer_step_noalloc. */
+size_t msk_noalloc_scratch_bytes(void);
+
 /* Profiling aid: msk_layer_step (no optional outputs) run as one persistent
  * cooperative kernel with grid barriers between dependent phases, where the
  * stack has one (one token, all fp32); msk_layer_step itself always runs

@@ -149,3 +149,20 @@ def test_misaligned_pointers_are_argument_errors():
                             ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.c_void_p(8),
                             ctypes.c_void_p(8), ctypes.c_void_p(8), 1 << 30, None) == 1
     assert "aligned" in msk.last_error()
+
+
+def test_noalloc_rejects_a_step_larger_than_its_scratch():
+    """The allocation-free step refuses, before anything is enqueued, a step
+    whose workspace exceeds the per-GPU scratch array (host-side check)."""
+    big = _spec(hidden=65536, n_experts=16, top_k=16, ffn_dim=128)
+    n = msk.workspace_size(big, [10] * 8, 8)
+    assert n > msk.noalloc_scratch_bytes() == 64 << 20
+    fake = ctypes.c_void_p(1 << 20)           # never dereferenced: rejected first
+    cfg = msk.make_cfg(big)
+    w = msk.LayerWeights(*([fake.value] * len(msk._WEIGHT_FIELDS)))
+    kv = msk.KV(fake.value, fake.value, 64)
+    b = msk.make_batch([10] * 8, 8)
+    st = msk.lib().msk_layer_step_noalloc(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), 1,
+                                          ctypes.byref(b), fake, None, None, None, None)
+    assert st == 3, msk.last_error()
+    assert "scratch" in msk.last_error()

@@ -95,6 +95,11 @@ def lib():
         L.msk_layer_step.restype = i32
         L.msk_layer_step.argtypes = [P(LayerCfg), P(LayerWeights), P(KV), i32, P(Batch), vp, vp,
                                      vp, vp, vp, sz, vp]
+        L.msk_layer_step_noalloc.restype = i32
+        L.msk_layer_step_noalloc.argtypes = [P(LayerCfg), P(LayerWeights), P(KV), i32, P(Batch),
+                                             vp, vp, vp, vp, vp]
+        L.msk_noalloc_scratch_bytes.restype = sz
+        L.msk_noalloc_scratch_bytes.argtypes = []
         L.msk_timer_start.restype = i32
         L.msk_timer_start.argtypes = [ctypes.c_uint32]
         L.msk_timer_read.restype = i32
@@ -228,6 +233,25 @@ def layer_step(specs, weights, kvs, kv_len, tokens_per_req, x, ws, layer_out=Non
                                 _ptr(topk_idx), _ptr(win), _ptr(ws), ws.numel(),
                                 _stream(stream)))
     return x
+
+
+def layer_step_noalloc(specs, weights, kvs, kv_len, tokens_per_req, x, layer_out=None,
+                       topk_idx=None, win=None, stream=None):
+    """layer_step without a workspace: the library's per-GPU scratch array is
+    used (msk_layer_step_noalloc); x is updated in place."""
+    n = len(specs)
+    cfgs = _array(LayerCfg, [make_cfg(s) for s in specs])
+    wts = _array(LayerWeights, [make_weights(w) for w in weights])
+    kva = _array(KV, [make_kv(k) for k in kvs])
+    b = make_batch(kv_len, tokens_per_req)
+    _check(lib().msk_layer_step_noalloc(cfgs, wts, kva, n, ctypes.byref(b), _ptr(x),
+                                        _ptr(layer_out), _ptr(topk_idx), _ptr(win),
+                                        _stream(stream)))
+    return x
+
+
+def noalloc_scratch_bytes():
+    return lib().msk_noalloc_scratch_bytes()
 
 
 PHASES = ("qkv", "attn", "combine", "wo", "router", "topk", "gateup", "down", "step", "union",

@@ -7,7 +7,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <string>
 
 #include "../../include/msk.h"
 #include "launch.h"
@@ -15,20 +14,20 @@
 
 namespace {
 
-thread_local std::string g_err;
+// The last error text of this thread, in a fixed buffer: no entry point
+// allocates host memory, on its error paths either.
+thread_local char g_err[512];
 
 msk_status fail(msk_status s, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
   va_end(ap);
-  g_err = buf;
   return s;
 }
 
 msk_status ok() {
-  g_err.clear();
+  g_err[0] = '\0';
   return MSK_OK;
 }
 
@@ -381,7 +380,7 @@ extern "C" {
 
 int32_t msk_abi_version(void) { return MSK_ABI_VERSION; }
 
-const char* msk_last_error(void) { return g_err.c_str(); }
+const char* msk_last_error(void) { return g_err; }
 
 size_t msk_workspace_size(const msk_layer_cfg* cfg, int32_t n_layers, const msk_batch* batch) {
   if (!cfg || n_layers < 1 || n_layers > MSK_MAX_STACK) {
@@ -480,10 +479,13 @@ msk_status msk_expert_ffn(const msk_layer_cfg* cfg, const msk_layer_weights* w, 
                        "expert launch");
 }
 
+// noalloc: the workspace is the library's per-GPU scratch array (ws and
+// ws_bytes unused), and the call allocates nothing.
 static msk_status layer_step_impl(const msk_layer_cfg* cfg, const msk_layer_weights* w,
                                   const msk_kv* kv, int32_t n_layers, const msk_batch* batch,
                                   float* x, float* layer_out, int32_t* topk_idx, int32_t* win,
-                                  int64_t* stamps, void* ws, size_t ws_bytes, void* stream) {
+                                  int64_t* stamps, void* ws, size_t ws_bytes, void* stream,
+                                  bool noalloc = false) {
   if (!cfg || !w || !kv) return fail(MSK_ERR_INVALID_ARG, "cfg, w or kv is null");
   if (n_layers < 1 || n_layers > MSK_MAX_STACK)
     return fail(MSK_ERR_INVALID_ARG, "n_layers %d outside [1, %d]", n_layers, MSK_MAX_STACK);
@@ -498,6 +500,16 @@ static msk_status layer_step_impl(const msk_layer_cfg* cfg, const msk_layer_weig
   }
   if (!x) return fail(MSK_ERR_INVALID_ARG, "x is null");
   const Layout lay = layout(cfg, n_layers, *batch);
+  if (noalloc) {
+    if (lay.total > msk::kScratchBytes)
+      return fail(MSK_ERR_WORKSPACE,
+                  "this step needs %zu B of scratch; the allocation-free entry point holds "
+                  "%zu B per GPU",
+                  lay.total, msk::kScratchBytes);
+    const hipError_t e = msk::scratch_address(&ws);
+    if (e != hipSuccess) return device_status(e, "scratch address");
+    ws_bytes = msk::kScratchBytes;
+  }
   if (!ws || ws_bytes < lay.total)
     return fail(MSK_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, lay.total);
   msk::LayerArgs Ls[msk::kMaxLayers];
@@ -515,6 +527,7 @@ static msk_status layer_step_impl(const msk_layer_cfg* cfg, const msk_layer_weig
   // so only the timeline call, whose in-kernel stamps need it, runs the
   // persistent kernel.
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (noalloc) return device_status(msk::launch_step_noalloc(Ls, S, st), "layer-step launch");
   return device_status(stamps ? msk::launch_step_fused(Ls, S, st) : msk::launch_step_unfused(Ls, S, st),
                        "layer-step launch");
 }
@@ -526,6 +539,16 @@ msk_status msk_layer_step(const msk_layer_cfg* cfg, const msk_layer_weights* w, 
   return layer_step_impl(cfg, w, kv, n_layers, batch, x, layer_out, topk_idx, win, nullptr, ws,
                          ws_bytes, stream);
 }
+
+msk_status msk_layer_step_noalloc(const msk_layer_cfg* cfg, const msk_layer_weights* w,
+                                  const msk_kv* kv, int32_t n_layers, const msk_batch* batch,
+                                  float* x, float* layer_out, int32_t* topk_idx, int32_t* win,
+                                  void* stream) {
+  return layer_step_impl(cfg, w, kv, n_layers, batch, x, layer_out, topk_idx, win, nullptr,
+                         nullptr, 0, stream, /*noalloc=*/true);
+}
+
+size_t msk_noalloc_scratch_bytes(void) { return msk::kScratchBytes; }
 
 msk_status msk_layer_step_timeline(const msk_layer_cfg* cfg, const msk_layer_weights* w,
                                    const msk_kv* kv, int32_t n_layers, const msk_batch* batch,

@@ -533,9 +533,13 @@ struct PhaseTimer {
   size_t used[kNumPhases] = {};
 };
 static PhaseTimer g_timer;
+// Set for the duration of an allocation-free call: no event is created or
+// recorded then (event creation allocates).
+static thread_local bool g_timer_off = false;
 
 static hipError_t timer_pair(int ph, hipEvent_t* a, hipEvent_t* b) {
   *a = *b = nullptr;
+  if (g_timer_off) return hipSuccess;
   std::lock_guard<std::mutex> g(g_timer.mu);
   if (!(g_timer.mask >> ph & 1u)) return hipSuccess;
   auto& v = g_timer.ev[ph];
@@ -887,18 +891,24 @@ static hipError_t launch_ffn_t1(const LayerArgs& L, const StepArgs& S, const flo
 // remembered per (kernel, LDS size): the expert kernels' LDS depends on the
 // hidden and FFN sizes of the call.
 static int resident_grid(const void* fn, size_t lds, int threads = kBlockThreads) {
-  struct Entry { const void* fn; size_t lds; int threads, grid; };
+  struct Entry { const void* fn; size_t lds; int threads, grid, dev; };
   static std::mutex mu;
-  static std::vector<Entry> cache;
+  static Entry cache[64];
+  static int used = 0;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
   std::lock_guard<std::mutex> g(mu);
-  for (const Entry& e : cache)
-    if (e.fn == fn && e.lds == lds && e.threads == threads) return e.grid;
+  for (int i = 0; i < used; ++i) {
+    const Entry& e = cache[i];
+    if (e.fn == fn && e.lds == lds && e.threads == threads && e.dev == dev) return e.grid;
+  }
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, lds) != hipSuccess ||
       n < 1)
     n = 1;
-  cache.push_back(Entry{fn, lds, threads, n * cu_count()});
-  return cache.back().grid;
+  const int grid = n * cu_count();
+  if (used < 64) cache[used++] = Entry{fn, lds, threads, grid, dev};
+  return grid;
 }
 
 // token vectors staged per gate/up pass: four fp32 vectors (96 KB at
@@ -1061,6 +1071,52 @@ hipError_t launch_step_fused(const LayerArgs* Ls, const StepArgs& S, hipStream_t
     MSK_TRY((launch_fused_t1<kF32, kF32, kF32, 32>(Ls, S, st, &launched)));
     if (launched) return hipSuccess;
   }
+  return launch_step_unfused(Ls, S, st);
+}
+
+// ------------------------------------------- allocation-free scratch
+// Scratch of the allocation-free entry point: one array per GPU, allocated
+// by the code object loader with the library and held until the process
+// ends.  Host code never uses this name as an address (in host code it is a
+// stand-in, not the device address): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_address(void** out) {
+  *out = nullptr;
+  int dev = 0;
+  MSK_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> g(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    MSK_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+// Zero n words with a plain kernel (no memset node, so the call can sit in a
+// captured graph).
+__global__ __launch_bounds__(kBlockThreads) void k_clear_words(unsigned* w, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) w[i] = 0u;
+}
+
+hipError_t launch_step_noalloc(const LayerArgs* Ls, const StepArgs& S, hipStream_t st) {
+  struct Off {
+    Off() { g_timer_off = true; }
+    ~Off() { g_timer_off = false; }
+  } off;
+  // the array keeps the previous call's contents: the barrier and counter
+  // words must start at zero
+  const int n = kSyncBytes / 4;
+  hipLaunchKernelGGL(k_clear_words, dim3((n + kBlockThreads - 1) / kBlockThreads),
+                     dim3(kBlockThreads), 0, st, S.sync, n);
+  MSK_TRY(hipGetLastError());
   return launch_step_unfused(Ls, S, st);
 }
 

@@ -38,6 +38,16 @@ hipError_t launch_step_fused(const LayerArgs* Ls, const StepArgs& S, hipStream_t
 // Whole step as a sequence of per-phase kernels (the unfused comparison path).
 hipError_t launch_step_unfused(const LayerArgs* Ls, const StepArgs& S, hipStream_t st);
 
+// Scratch of the allocation-free entry point: kScratchBytes per GPU, at the
+// address scratch_address gives for the current device (looked up once per
+// device).  launch_step_noalloc runs the per-phase step on S, whose
+// workspace pointers lie in that scratch, after zeroing its barrier and
+// counter words; it creates and records no timing events.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t scratch_address(void** out);
+hipError_t launch_step_noalloc(const LayerArgs* Ls, const StepArgs& S, hipStream_t st);
+
 // Kernel timing (msk_timer_start / msk_timer_read): arm the phases in
 // `mask`, forget earlier records; read the summed milliseconds and launch
 // count of one phase, waiting for its last recorded launch.
