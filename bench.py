@@ -273,7 +273,8 @@ def copy_calibration(nbytes=1 << 30, reps=3):
 
 
 HEADLINE = "verify-bf16-128k"
-ALL_WORKLOADS = ["tiny-fp32", "decode-bf16", "stack4-nvfp4", "longctx-nvfp4", HEADLINE]
+ALL_WORKLOADS = ["tiny-fp32", "decode-bf16", "stack4-nvfp4", "longctx-nvfp4", "deep32-nvfp4",
+                 HEADLINE]
 
 
 def measure(name, args, with_cpu):

@@ -51,7 +51,7 @@ extern "C" {
 #define MSK_ABI_VERSION 1
 #define MSK_MAX_REQ 64       /* requests per call                          */
 #define MSK_MAX_TOKENS 64    /* T = n_req * tokens_per_req per call         */
-#define MSK_MAX_STACK 4      /* layers per msk_layer_step call             */
+#define MSK_MAX_STACK 64     /* layers per msk_layer_step call             */
 
 typedef enum {
   MSK_OK = 0,

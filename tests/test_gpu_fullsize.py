@@ -17,6 +17,7 @@ import torch
 
 import synth
 import verify_step_amd as msk
+from oracle import formats as fm
 from oracle import layer as ol
 from parity_util import (StackDrift, assert_close, fill_shift, fp32_store_floor, tol_for)
 
@@ -81,7 +82,8 @@ def _check_request(p, gpu, b, n_tok, attn=None):
             assert_close(f"req {b} attn_o", o_a[rows], ref["attn_o"], tol)
             assert_close(f"req {b} attn h - x", h_a[rows] - cur, ref["h"] - cur, tol,
                          fp32_store_floor(ref["h"]))
-        here = drift.routing(l, topk[l][rows], ref["logits"], ref["idx"], spec["top_k"])
+        in_err = drift.input_error(gpu_in, cur) if l > 0 else 0.0
+        here = drift.routing(l, topk[l][rows], ref["logits"], ref["idx"], spec["top_k"], in_err)
         assert_close(f"req {b} layer {l} out", lo[l][rows][here], ref["out"][here], tol)
         assert_close(f"req {b} layer {l} delta", (lo[l][rows] - gpu_in)[here],
                      (ref["out"] - cur)[here], tol, fp32_store_floor(ref["out"][here]))
@@ -93,7 +95,14 @@ def _check_request(p, gpu, b, n_tok, attn=None):
             sign = 0x80
             gv = np.where(got & sign, -(got & 0x7F), got)
             wv = np.where(want & sign, -(want & 0x7F), want)
-            assert np.abs(gv - wv).max(initial=0) <= 1, f"{name} append differs by more than one code"
+            far = np.abs(gv - wv) > 1
+            if in_err > 0:
+                # a free-running later layer: values may move further within the drift
+                # (see check_appended)
+                gval = fm.decode(got.astype(np.uint8), "e4m3")
+                wval = fm.decode(want.astype(np.uint8), "e4m3")
+                far &= np.abs(gval - wval) > 10.0 * in_err * float(np.sqrt(np.mean(wval * wval)))
+            assert not far.any(), f"{name} append differs by more than one code"
         cur = ref["out"]
         gpu_in = lo[l][rows]
 

@@ -79,6 +79,10 @@ CASES = {
                                                 kv_len=[150000, 20000, 5, 0])),
     "verify-bf16kv-longchunk": ("verify-bf16-128k", dict(dims=_SMALL, kv="bf16",
                                                          kv_len=[100000], n_req=1)),
+    # a 16-layer hybrid stack (three sliding-window layers to one full-context
+    # layer), several tokens, NVFP4 experts: layer l + 1 reads layer l's output
+    "deep16-small": ("deep32-nvfp4", dict(dims=_SMALL, kv_len=[500], tokens_per_req=4,
+                                          windows=[128, 128, 128, 0] * 4)),
     # one token over a long e4m3 history: vector attention items of five tiles
     "decode-e4m3-long": ("decode-bf16", dict(dims=_SMALL, kv="e4m3", kv_len=[300000],
                                              windows=[0])),
@@ -128,14 +132,58 @@ def test_layer_step_matches_oracle(prob):
         ref = ol.layer_step(spec, w, kv, p.kv_len, p.tokens_per_req, cur)
         tol = tol_for(spec)
         alive = drift.alive.copy()
-        check_appended(p, l, ref, tol, tokens=alive)
+        in_err = drift.input_error(gpu_in, cur) if l > 0 else 0.0
+        check_appended(p, l, ref, tol, tokens=alive, in_err=in_err)
         assert np.array_equal(win[l].cpu().numpy(), ref["win"])
-        here = drift.routing(l, topk[l].cpu().numpy(), ref["logits"], ref["idx"], K)
+        here = drift.routing(l, topk[l].cpu().numpy(), ref["logits"], ref["idx"], K, in_err)
         assert_close(f"layer {l} out", lo[l][here], ref["out"][here], tol)
         assert_close(f"layer {l} delta", (lo[l] - gpu_in)[here], (ref["out"] - cur)[here], tol,
                      fp32_store_floor(ref["out"][here]))
         cur = ref["out"]
         gpu_in = lo[l]
+    restore_kv(p, snaps)
+
+
+def test_stack_layers_teacher_forced(prob):
+    """Every layer of a stack run alone on the GPU, fed the oracle's input of
+    that layer (the oracle chains its own layers; its outputs become GPU
+    inputs, never the reverse): routing bit exact, appended KV, windows and
+    outputs as for a single layer.  The chaining itself is what
+    test_layer_step_matches_oracle checks."""
+    case, p = prob
+    n = len(p.specs)
+    if n == 1:
+        pytest.skip("one layer: test_layer_step_matches_oracle feeds both sides the same input")
+    print(f"[gpu-parity] teacher-forced {case}", flush=True)
+    T, K = p.T, p.specs[0]["top_k"]
+    snaps = snapshot_kv(p)
+    cur = p.x.double().cpu().numpy()
+    for l in range(n):
+        x32 = cur.astype(np.float32)
+        cur = x32.astype(np.float64)          # both sides start from the same fp32 values
+        spec, w, kv = oracle_inputs(p, l)
+        ref = ol.layer_step(spec, w, kv, p.kv_len, p.tokens_per_req, cur)
+        tol = tol_for(spec)
+        ws = msk.new_workspace(p.specs[l:l + 1], p.kv_len, p.tokens_per_req)
+        x = torch.from_numpy(x32).to("cuda")
+        topk = torch.empty((1, T, K), dtype=torch.int32, device="cuda")
+        win = torch.empty((1, T, 2), dtype=torch.int32, device="cuda")
+        msk.layer_step(p.specs[l:l + 1], p.weights[l:l + 1], p.kv[l:l + 1], p.kv_len,
+                       p.tokens_per_req, x, ws, topk_idx=topk, win=win)
+        torch.cuda.synchronize()
+        msk.workspace_status(ws)
+        check_appended(p, l, ref, tol)
+        assert np.array_equal(win[0].cpu().numpy(), ref["win"])
+        rms = float(np.sqrt(np.mean(ref["logits"] ** 2)))
+        near = check_routing(topk[0].cpu().numpy(), ref["logits"], ref["idx"], K,
+                             ROUTE_MARGIN * rms)
+        far = ~near_mask(ref["logits"], K, ROUTE_MARGIN * rms)
+        out = x.double().cpu().numpy()
+        assert_close(f"layer {l} out (teacher-forced)", out[far], ref["out"][far], tol)
+        assert_close(f"layer {l} delta (teacher-forced)", (out - cur)[far], (ref["out"] - cur)[far],
+                     tol, fp32_store_floor(ref["out"][far]))
+        print(f"[gpu-parity] layer {l}: {near} tokens inside the routing margin", flush=True)
+        cur = ref["out"]
     restore_kv(p, snaps)
 
 

@@ -32,7 +32,7 @@ def test_layer0_flip_inside_margin0_fails():
         d.routing(0, gpu, lg, idx, 2)     # gap 1e-4 exceeds the layer-0 margin
 
 
-def test_later_layer_flip_inside_drift_margin_drops_the_request_tail():
+def test_later_layer_flip_drops_the_request_tail():
     lg, idx = _logits()
     d = StackDrift(2, 3, margin0=1e-5, drift=1e-3, max_moved=1)
     here = d.routing(0, idx, lg, idx, 2)
@@ -42,7 +42,7 @@ def test_later_layer_flip_inside_drift_margin_drops_the_request_tail():
     here = d.routing(1, gpu, lg, idx, 2)
     assert here.tolist() == [True, False, True, True, True, True]
     assert d.alive.tolist() == [True, False, False, True, True, True]
-    # a far token routed differently still fails
+    # a second token routed differently, near or far, exceeds max_moved
     gpu = idx.copy()
     gpu[3] = [1, 0]
     with pytest.raises(AssertionError):
@@ -62,3 +62,14 @@ def test_a_second_moved_token_fails():
     gpu[4] = [0, 2]
     with pytest.raises(AssertionError):
         d.routing(2, gpu, lg, idx, 2)      # a second one is not
+
+
+def test_layer0_far_flip_fails_and_input_error_is_relative():
+    lg, idx = _logits()
+    gpu = idx.copy()
+    gpu[3] = [1, 0]                        # a clear boundary: never excused at layer 0
+    d = StackDrift(2, 3, margin0=1e-5, drift=1e-3)
+    with pytest.raises(AssertionError):
+        d.routing(0, gpu, lg, idx, 2)
+    x = np.ones((6, 4))
+    assert d.input_error(x * (1 + 1e-3), x) == pytest.approx(1e-3)

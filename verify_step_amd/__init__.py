@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(HERE, "libmsk.so")
 DTYPE = {"f32": 0, "bf16": 1, "e4m3": 2, "nvfp4": 3}
 MAX_REQ = 64
 MAX_TOKENS = 64
-MAX_STACK = 4
+MAX_STACK = 64
 
 STATUS = {0: "MSK_OK", 1: "MSK_ERR_INVALID_ARG", 2: "MSK_ERR_UNSUPPORTED",
           3: "MSK_ERR_WORKSPACE", 4: "MSK_ERR_DEVICE", 5: "MSK_ERR_TIMEOUT"}

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kTopkUnionThreads) void k_topk_union(LayerArgs L, S
 // the attention phase of the persistent kernel reuses the same space.
 struct StepLayers {
   StepArgs S;
-  LayerArgs L[kMaxLayers];
+  LayerArgs L[kMaxFusedLayers];
 };
 
 struct T1Lds {
@@ -1043,7 +1043,7 @@ static hipError_t launch_fused_t1(const LayerArgs* Ls, const StepArgs& S, hipStr
   const int grid = cu_count();
   StepLayers P;
   P.S = S;
-  for (int l = 0; l < kMaxLayers; ++l) P.L[l] = Ls[l < S.n_layers ? l : 0];
+  for (int l = 0; l < kMaxFusedLayers; ++l) P.L[l] = Ls[l < S.n_layers ? l : 0];
   void* args[] = {&P};
   *launched = true;
   hipEvent_t e0, e1;
@@ -1065,7 +1065,7 @@ hipError_t launch_step_fused(const LayerArgs* Ls, const StepArgs& S, hipStream_t
   for (int l = 1; l < S.n_layers; ++l)
     same = same && Ls[l].ddt == Ls[0].ddt && Ls[l].edt == Ls[0].edt && Ls[l].kdt == Ls[0].kdt;
   const LayerArgs& L = Ls[0];
-  const bool fits = t1_act_lds(L) <= kMaxLds;
+  const bool fits = t1_act_lds(L) <= kMaxLds && S.n_layers <= kMaxFusedLayers;
   if (S.T == 1 && same && fits && L.ddt == kF32 && L.edt == kF32 && L.kdt == kF32 && L.D == 32) {
     bool launched = false;
     MSK_TRY((launch_fused_t1<kF32, kF32, kF32, 32>(Ls, S, st, &launched)));

@@ -6,7 +6,8 @@ namespace msk {
 
 constexpr int kMaxReq = 64;
 constexpr int kMaxTok = 64;
-constexpr int kMaxLayers = 4;
+constexpr int kMaxLayers = 64;      // layers per whole-step call
+constexpr int kMaxFusedLayers = 4;  // layers of the persistent timeline kernel (kernel arguments)
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 256;
 constexpr int kRowGroup = 8;       // query rows handled together by attention

@@ -3,6 +3,7 @@
   python3 -m verify_step_amd.profsum stats  STATS_CSV  --workload W --cmd "..." --out FILE
   python3 -m verify_step_amd.profsum traffic --kernel K --workload W \
       --fetch CSV --write CSV --copy-fetch CSV --copy-write CSV --cmds "..." --out FILE
+  python3 -m verify_step_amd.profsum util CSV --workload W --cmd "..." --out FILE
 
 `stats` reads the kernel_stats CSV of a `rocprofv3 --kernel-trace --stats
 --output-format csv` run and tabulates the library's kernels.  `traffic`
@@ -12,6 +13,11 @@ device copy) and converts the kernel's mean KiB per dispatch into bytes
 with the factor that makes the copy's readings equal its known size.  The
 traffic summary carries the SHA-256 of the kernel sources it was taken
 with; bench.py reports its figure only while the sources still match.
+`util` reads the counter_collection CSV of a `--pmc MfmaUtil VALUBusy` run
+(rocprofv3's derived metrics: the matrix-core busy cycles per SIMD, and the
+cycles with a vector ALU instruction in flight per CU, both as a percentage
+of the GPU's busy cycles over each dispatch) and tabulates their mean per
+kernel.
 """
 import argparse
 import csv
@@ -112,6 +118,31 @@ def traffic_md(kernel, workload, fetch, write, cfetch, cwrite, cmds):
     return "\n".join(out)
 
 
+def util_md(path, workload, cmd):
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] not in ("MfmaUtil", "VALUBusy"):
+            continue
+        if "msk::" not in r["Kernel_Name"]:
+            continue
+        k = short_name(r["Kernel_Name"])
+        vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = [f"# Matrix-core and vector-ALU utilisation: {workload}", "",
+           "One `rocprofv3 --pmc` run of the benchmark (from the repository root, on one "
+           "MI355X):", "", "```", cmd, "```", "",
+           "MfmaUtil: matrix-core busy cycles over all SIMDs / (GPU busy cycles x SIMDs), %.  "
+           "VALUBusy: cycles with a vector-ALU instruction in flight per CU / GPU busy "
+           "cycles, %.  Means over the dispatches of each kernel.", "",
+           "| kernel | dispatches | MfmaUtil % | VALUBusy % |", "|---|---:|---:|---:|"]
+    def mean(v):
+        return sum(v) / len(v) if v else float("nan")
+    for k in sorted(vals, key=lambda k: -mean(vals[k].get("VALUBusy", [0]))):
+        m, v = vals[k].get("MfmaUtil", []), vals[k].get("VALUBusy", [])
+        out.append(f"| `{k}` | {max(len(m), len(v))} | {mean(m):.1f} | {mean(v):.1f} |")
+    out.append("")
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -124,8 +155,15 @@ def main(argv=None):
     for a in ("--kernel", "--workload", "--fetch", "--write", "--copy-fetch", "--copy-write",
               "--cmds", "--out"):
         t.add_argument(a, required=True)
+    u = sub.add_parser("util")
+    u.add_argument("csv")
+    u.add_argument("--workload", required=True)
+    u.add_argument("--cmd", required=True)
+    u.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    if a.what == "stats":
+    if a.what == "util":
+        text = util_md(a.csv, a.workload, a.cmd)
+    elif a.what == "stats":
         text = stats_md(read_stats(a.csv), a.workload, a.cmd)
     else:
         text = traffic_md(a.kernel, a.workload, a.fetch, a.write, a.copy_fetch, a.copy_write,
