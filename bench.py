@@ -186,34 +186,9 @@ def unfused_step(p, x, ws):
     return run
 
 
-def timeline(p, ws, x):
-    """Per-phase times of one persistent-kernel step from the in-kernel
-    real-time counter (100 MHz): phase k ends when the last workgroup has
-    finished it; its time is measured from the previous phase's end."""
-    nblk = torch.cuda.get_device_properties(0).multi_processor_count
-    stamps = torch.zeros((nblk, 32), dtype=torch.int64, device=x.device)
-    msk.layer_step_timeline(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws, stamps)
-    torch.cuda.synchronize()
-    st = stamps.cpu().numpy().astype(np.float64) * 0.01      # us
-    names = ["qkv", "attn", "combine", "wo", "router", "gateup", "down"]
-    out = []
-    t0 = st[:, 0].min()
-    prev = t0
-    for l in range(len(p.specs)):
-        for i, nm in enumerate(names):
-            k = 1 + l * len(names) + i
-            if k >= 32 or st[:, k].max() == 0:
-                break
-            end = st[:, k].max()
-            out.append(dict(layer=l, phase=nm, us=round(end - prev, 2),
-                            spread_us=round(end - st[:, k].min(), 2)))
-            prev = end
-    return dict(total_us=round(prev - t0, 2), phases=out)
-
-
 KERNEL_NAMES = {"qkv": "k_qkv", "attn": "k_attn", "combine": "k_combine", "wo": "k_wo",
                 "router": "k_router", "topk": "k_topk", "gateup": "k_gateup", "down": "k_down",
-                "step": "k_step_t1", "union": "k_union", "moe_sum": "k_moe_sum",
+                "step": "k_step_p", "union": "k_union", "moe_sum": "k_moe_sum",
                 "prep": "k_prep_act", "dense_sum": "k_dense_sum"}
 ONE_TOKEN_KERNELS = ("qkv", "wo", "router", "gateup", "down")
 
@@ -234,7 +209,7 @@ def kernel_name(phase, spec, T, Tr):
     return base
 
 
-def kernel_pass(p, x, ws, steps, stream):
+def kernel_pass(p, x, ws, steps, stream, stamps=None):
     """Run `steps` more steps with every phase kernel bracketed by HIP events
     (msk_timer_start), each step recording its routing.  Returns per phase
     the summed kernel time, the launch count and the algorithmic bytes of
@@ -242,7 +217,7 @@ def kernel_pass(p, x, ws, steps, stream):
     n_layers, K = len(p.specs), p.specs[0]["top_k"]
     topk = torch.zeros((steps, n_layers, p.T, K), dtype=torch.int32, device=x.device)
     runs = [msk.Step(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws,
-                     topk_idx=topk[i]) for i in range(steps)]
+                     topk_idx=topk[i], stamps=stamps) for i in range(steps)]
     msk.timer_start()
     for r in runs:
         r(stream)
@@ -286,7 +261,11 @@ def measure(name, args, with_cpu):
     n_layers = len(p.specs)
     ws = msk.new_workspace(p.specs, p.kv_len, p.tokens_per_req, device=dev)
     x = p.x.clone()
-    step = msk.Step(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws)
+    stamps = None
+    if args.path == "persistent":
+        n_wg = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+        stamps = torch.zeros((n_wg, 32), dtype=torch.int64, device=dev)
+    step = msk.Step(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws, stamps=stamps)
     if args.path == "unfused":
         step = unfused_step(p, x, ws)
 
@@ -317,7 +296,7 @@ def measure(name, args, with_cpu):
     # the same K steps again, each kernel bracketed by dispatch-stamped events
     x.copy_(x_start)
     torch.cuda.synchronize()
-    kp, step_bytes = kernel_pass(p, x, ws, args.steps, stream)
+    kp, step_bytes = kernel_pass(p, x, ws, args.steps, stream, stamps)
     msk.workspace_status(ws)
     nbytes = int(np.mean([b for b, _ in step_bytes]))
     parts = {k: int(np.mean([pp[k] for _, pp in step_bytes])) for k in step_bytes[0][1]}
@@ -366,10 +345,9 @@ def measure(name, args, with_cpu):
                          "gbs": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1)
                          if ph != "step" else None}
                     for ph, r in timed.items()},
-        "path": "layer_step" if args.path == "fused" else "per_op_calls",
+        "path": {"fused": "layer_step", "unfused": "per_op_calls",
+                 "persistent": "persistent_kernel"}[args.path],
     }
-    if args.timeline and args.path == "fused":
-        out["timeline"] = timeline(p, ws, x)
     if with_cpu:
         out["cpu_baseline"] = cpu_baseline(p)
     del p, ws, x, step
@@ -386,11 +364,10 @@ def main():
                     help="one workload name, or 'all': every workload, each on a line of its "
                          f"own, the largest ({HEADLINE}) last")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=["fused", "unfused"], default="fused",
+    ap.add_argument("--path", choices=["fused", "unfused", "persistent"], default="fused",
                     help="fused: msk_layer_step; unfused: the msk_attn_step -> msk_moe_route "
-                         "-> msk_expert_ffn calls per layer")
-    ap.add_argument("--timeline", action="store_true",
-                    help="also print per-phase times of the persistent kernel")
+                         "-> msk_expert_ffn calls per layer; persistent: "
+                         "msk_layer_step_timeline, the persistent step kernel where one exists")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()

@@ -235,21 +235,25 @@ msk_status msk_layer_step_noalloc(const msk_layer_cfg *cfg, const msk_layer_weig
 /* Bytes of the per-GPU scratch array of msk_layer_step_noalloc. */
 size_t msk_noalloc_scratch_bytes(void);
 
-/* Profiling aid: msk_layer_step (no optional outputs) run as one persistent
- * cooperative kernel with grid barriers between dependent phases, where the
- * stack has one (one token, all fp32); msk_layer_step itself always runs
- * per-phase kernels, which measure faster on this part.  It records, for
- * every workgroup of the persistent kernel, the GPU's constant 100 MHz
- * real-time counter at the start and after each phase:
- *   stamps  DEVICE int64 [workgroups][32], caller-owned; slot 0 = start, then
- *           per layer: QKV, attention, combine, Wo, router, gate/up, down.
- * The number of workgroups is the GPU's compute-unit count.  Stacks that run
- * as per-phase kernels (more than one token, or dtype combinations without a
- * persistent kernel) leave stamps untouched. */
+/* Profiling aid: msk_layer_step run as the persistent
+ * step kernel where one exists for the stack (one token per step; bf16 dense
+ * and experts over a bf16 cache, bf16 dense with NVFP4 experts over an e4m3
+ * cache, or all fp32; head_dim 128, 128 and 32): every phase of up to four
+ * layers in one launch, its workgroups meeting at device-wide barriers
+ * where a phase needs the whole result of the one before.  Other stacks run
+ * as per-phase kernels and leave stamps untouched.  It records, for every
+ * workgroup of the persistent kernel, the GPU's constant 100 MHz real-time
+ * counter at the start and after each phase:
+ *   stamps  DEVICE int64 [4 * CUs][32], caller-owned and zero-filled; slot 0
+ *           = start, then per layer: QKV, attention, combine, Wo, router,
+ *           gate/up, down (the first four layers).  Rows of workgroups that
+ *           did not run stay zero.
+ * A barrier wait that gives up sets the workspace's error flag, which
+ * msk_workspace_status reports. */
 msk_status msk_layer_step_timeline(const msk_layer_cfg *cfg, const msk_layer_weights *w,
                                    const msk_kv *kv, int32_t n_layers, const msk_batch *batch,
-                                   float *x, int64_t *stamps, void *ws, size_t ws_bytes,
-                                   void *stream);
+                                   float *x, float *layer_out, int32_t *topk_idx, int32_t *win,
+                                   int64_t *stamps, void *ws, size_t ws_bytes, void *stream);
 
 /* Kernel timing for measurement harnesses.  The step's kernels fall into
  * phases:

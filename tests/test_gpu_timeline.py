@@ -1,6 +1,9 @@
 """The persistent whole-step kernel (the timeline call, which runs it for
-one-token all-fp32 stacks) on the small fp32 workload: the same result as
-the oracle, and every workgroup's phase stamps present and in order."""
+one-token steps where an instantiation exists) against the oracle, and its
+per-workgroup phase stamps present and in order.  Cases: the small fp32
+layer, the full-size bf16 decode layer, a reduced-width layer with NVFP4
+experts over an e4m3 cache, and a six-layer fp32 stack, which the kernel runs
+as two launches (four layers, then two)."""
 import numpy as np
 import pytest
 import torch
@@ -14,15 +17,27 @@ from parity_util import (assert_close, fill_shift, fp32_store_floor, oracle_inpu
 pytestmark = pytest.mark.gpu
 
 PHASES_PER_LAYER = 7  # QKV, attention, combine, Wo, router, gate/up, down
+_SMALL = dict(hidden=512, n_q_heads=12, n_kv_heads=2, head_dim=128, n_experts=32, top_k=8,
+              ffn_dim=256)
+
+CASES = {
+    "tiny-fp32": ("tiny-fp32", None),
+    "decode-bf16": ("decode-bf16", None),
+    "decode-nvfp4-e4m3": ("decode-bf16", dict(dims=_SMALL, expert="nvfp4", kv="e4m3",
+                                              kv_len=[3000], windows=[2048])),
+    "tiny-fp32-6layers": ("tiny-fp32", dict(windows=[128, 0, 128, 0, 128, 0])),
+}
 
 
-def test_timeline_persistent_kernel_matches_oracle():
-    print("[gpu-timeline] tiny-fp32", flush=True)
-    p = synth.make_problem("tiny-fp32", device="cuda")
+@pytest.mark.parametrize("case", list(CASES))
+def test_persistent_kernel_matches_oracle(case):
+    name, ov = CASES[case]
+    print(f"[gpu-timeline] {case}", flush=True)
+    p = synth.make_problem(name, device="cuda", overrides=ov)
     fill_shift(p)
     snaps = snapshot_kv(p)
     ws = msk.new_workspace(p.specs, p.kv_len, p.tokens_per_req)
-    n_wg = torch.cuda.get_device_properties(0).multi_processor_count
+    n_wg = 4 * torch.cuda.get_device_properties(0).multi_processor_count
     stamps = torch.zeros((n_wg, 32), dtype=torch.int64, device="cuda")
     x = p.x.clone()
     msk.layer_step_timeline(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws, stamps)
@@ -42,7 +57,9 @@ def test_timeline_persistent_kernel_matches_oracle():
     # the persistent kernel ran (stamps written) and each workgroup's stamps
     # follow the phase order
     st = stamps.cpu().numpy()
-    n = 1 + PHASES_PER_LAYER * len(p.specs)
-    assert (st[:, 0] > 0).all(), "persistent kernel did not run"
-    assert (np.diff(st[:, :n], axis=1) >= 0).all()
+    ran = st[:, 0] > 0
+    assert ran.sum() >= torch.cuda.get_device_properties(0).multi_processor_count, \
+        "persistent kernel did not run"
+    n = min(32, 1 + PHASES_PER_LAYER * len(p.specs))
+    assert (np.diff(st[ran, :n], axis=1) >= 0).all()
     restore_kv(p, snaps)

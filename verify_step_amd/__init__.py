@@ -106,7 +106,7 @@ def lib():
         L.msk_timer_read.argtypes = [i32, P(ctypes.c_double), P(ctypes.c_int64)]
         L.msk_layer_step_timeline.restype = i32
         L.msk_layer_step_timeline.argtypes = [P(LayerCfg), P(LayerWeights), P(KV), i32, P(Batch),
-                                              vp, vp, vp, sz, vp]
+                                              vp, vp, vp, vp, vp, vp, sz, vp]
         if L.msk_abi_version() != 1:
             raise RuntimeError("libmsk.so ABI version mismatch")
         _lib = L
@@ -274,15 +274,18 @@ def timer_read(phase):
     return ms.value, n.value
 
 
-def layer_step_timeline(specs, weights, kvs, kv_len, tokens_per_req, x, ws, stamps, stream=None):
-    """layer_step that records per-workgroup phase timestamps into `stamps`
-    (int64 device tensor [n_workgroups][32])."""
+def layer_step_timeline(specs, weights, kvs, kv_len, tokens_per_req, x, ws, stamps,
+                        layer_out=None, topk_idx=None, win=None, stream=None):
+    """layer_step run as the persistent step kernel where one exists, recording
+    per-workgroup phase timestamps into `stamps` (int64 device tensor
+    [4 * CUs][32], zero-filled)."""
     n = len(specs)
     cfgs = _array(LayerCfg, [make_cfg(s) for s in specs])
     wts = _array(LayerWeights, [make_weights(w) for w in weights])
     kva = _array(KV, [make_kv(k) for k in kvs])
     b = make_batch(kv_len, tokens_per_req)
-    _check(lib().msk_layer_step_timeline(cfgs, wts, kva, n, ctypes.byref(b), _ptr(x), _ptr(stamps),
+    _check(lib().msk_layer_step_timeline(cfgs, wts, kva, n, ctypes.byref(b), _ptr(x),
+                                         _ptr(layer_out), _ptr(topk_idx), _ptr(win), _ptr(stamps),
                                          _ptr(ws), ws.numel(), _stream(stream)))
     return x
 
@@ -290,18 +293,24 @@ def layer_step_timeline(specs, weights, kvs, kv_len, tokens_per_req, x, ws, stam
 class Step:
     """Pre-marshalled arguments of one whole-step call, for repeated launches
     (timing loops): building ctypes structs once keeps Python overhead out of
-    the launch path."""
+    the launch path.  With `stamps` the call is msk_layer_step_timeline (the
+    persistent step kernel where one exists)."""
 
     def __init__(self, specs, weights, kvs, kv_len, tokens_per_req, x, ws, layer_out=None,
-                 topk_idx=None, win=None):
+                 topk_idx=None, win=None, stamps=None):
         self.n = len(specs)
         self.cfgs = _array(LayerCfg, [make_cfg(s) for s in specs])
         self.wts = _array(LayerWeights, [make_weights(w) for w in weights])
         self.kva = _array(KV, [make_kv(k) for k in kvs])
         self.batch = make_batch(kv_len, tokens_per_req)
-        self.args = (self.cfgs, self.wts, self.kva, self.n, ctypes.byref(self.batch), _ptr(x),
-                     _ptr(layer_out), _ptr(topk_idx), _ptr(win), _ptr(ws), ws.numel())
-        self.fn = lib().msk_layer_step
+        head = (self.cfgs, self.wts, self.kva, self.n, ctypes.byref(self.batch), _ptr(x),
+                _ptr(layer_out), _ptr(topk_idx), _ptr(win))
+        if stamps is None:
+            self.args = head + (_ptr(ws), ws.numel())
+            self.fn = lib().msk_layer_step
+        else:
+            self.args = head + (_ptr(stamps), _ptr(ws), ws.numel())
+            self.fn = lib().msk_layer_step_timeline
 
     def __call__(self, stream=None):
         _check(self.fn(*self.args, _stream(stream)))

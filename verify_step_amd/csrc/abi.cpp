@@ -552,10 +552,10 @@ size_t msk_noalloc_scratch_bytes(void) { return msk::kScratchBytes; }
 
 msk_status msk_layer_step_timeline(const msk_layer_cfg* cfg, const msk_layer_weights* w,
                                    const msk_kv* kv, int32_t n_layers, const msk_batch* batch,
-                                   float* x, int64_t* stamps, void* ws, size_t ws_bytes,
-                                   void* stream) {
+                                   float* x, float* layer_out, int32_t* topk_idx, int32_t* win,
+                                   int64_t* stamps, void* ws, size_t ws_bytes, void* stream) {
   if (!stamps) return fail(MSK_ERR_INVALID_ARG, "stamps is null");
-  return layer_step_impl(cfg, w, kv, n_layers, batch, x, nullptr, nullptr, nullptr, stamps, ws,
+  return layer_step_impl(cfg, w, kv, n_layers, batch, x, layer_out, topk_idx, win, stamps, ws,
                          ws_bytes, stream);
 }
 

@@ -528,6 +528,36 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
+// How a phase reads data that another workgroup wrote, and writes data that
+// another workgroup reads, within the step.  Plain: the producer ran in an
+// earlier kernel, whose end made its stores visible everywhere.  Coh: the
+// producer runs in the same (persistent) launch, possibly on another XCD,
+// whose L2 is not kept coherent with this one's: relaxed agent-scope atomic
+// loads and stores, which the hardware keeps coherent across the device
+// without the cost of an L2 writeback or invalidate.  Together with a
+// barrier whose arrival follows the stores' completion, a Coh load after the
+// barrier sees the Coh stores made before it.
+struct Plain {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ v4f ld4(const float* p) { return *reinterpret_cast<const v4f*>(p); }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+  static __device__ __forceinline__ void st4(float* p, v4f v) { *reinterpret_cast<v4f*>(p) = v; }
+};
+struct Coh {
+  static __device__ __forceinline__ float ld(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  static __device__ __forceinline__ v4f ld4(const float* p) {
+    return v4f{ld(p), ld(p + 1), ld(p + 2), ld(p + 3)};
+  }
+  static __device__ __forceinline__ void st(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  static __device__ __forceinline__ void st4(float* p, v4f v) {
+    st(p, v.x); st(p + 1, v.y); st(p + 2, v.z); st(p + 3, v.w);
+  }
+};
+
 // Fixed softmax shift of a layer: the given value, or (given 0) the score
 // bound sqrt(D) * max|q_norm| * max|k_norm| of a QK-normalised query against
 // a QK-normalised key.  The softmax does not depend on it; it only keeps
@@ -545,76 +575,8 @@ __device__ __forceinline__ float layer_shift(float given, v2f gq, v2f gk, int D)
   return sqrtf((float)D) * mq * mk;
 }
 
-// ---------------------------------------------------- grid-wide barrier
-// Barrier words in the caller's workspace (zero before first use):
-//   words[0]            generation, advanced by workgroup 0 at each barrier
-//   words[1]            error flag (a wait gave up)
-//   words[64 + b]       arrival epoch of workgroup b
-// Epochs only grow, across launches too: a launch starts from the
-// generation the previous one left, so nothing needs resetting.  Arrivals
-// are plain per-workgroup stores (no contended atomic); workgroup 0 checks
-// them with one thread per workgroup and publishes the new generation.
-// Every wait is bounded: a missing arrival sets the error flag instead of
-// hanging the GPU.
-constexpr int kSyncFlags = 64;
+// Bound of every device-side wait: past it a wait gives up and sets the
+// workspace's error flag instead of hanging the GPU.
 constexpr unsigned kSpinLimit = 1u << 22;
-
-struct GridSync {
-  unsigned* words;
-  unsigned base;   // generation at launch
-  unsigned k;      // barriers passed in this launch
-};
-
-__device__ __forceinline__ GridSync grid_sync_begin(unsigned* words) {
-  // every thread reads the same generation: it cannot advance before all
-  // workgroups have arrived at this launch's first barrier
-  GridSync g{words, __hip_atomic_load(&words[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0u};
-  return g;
-}
-
-__device__ __forceinline__ bool epoch_before(unsigned a, unsigned b) { return (int)(a - b) < 0; }
-
-__device__ __forceinline__ void grid_sync(GridSync& g) {
-  __syncthreads();
-  ++g.k;
-  const unsigned target = g.base + g.k;
-  unsigned* gen = &g.words[0];
-  unsigned* err = &g.words[1];
-  unsigned* flags = &g.words[kSyncFlags];
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_store(&flags[blockIdx.x], target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (blockIdx.x == 0) {
-    for (int b = threadIdx.x; b < (int)gridDim.x; b += blockDim.x) {
-      unsigned spins = 0;
-      while (epoch_before(__hip_atomic_load(&flags[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                          target)) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > kSpinLimit) {
-          __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
-      __hip_atomic_store(gen, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  if (threadIdx.x == 0) {
-    unsigned spins = 0;
-    while (epoch_before(__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), target)) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  __syncthreads();
-}
 
 }  // namespace msk

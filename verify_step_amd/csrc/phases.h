@@ -251,7 +251,7 @@ __device__ __forceinline__ void decode_v(const uint8_t* p, float* f) {
 
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0); }
 
-template <int KDT, int D>
+template <int KDT, int D, class MP = Plain>
 __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int item,
                           uint8_t* wl) {
   using Gm = AttnGeom<KDT, D>;
@@ -299,7 +299,7 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
 #pragma unroll
       for (int i = 0; i < QD; ++i) {
         const int d = ln + 64 * i;
-        qv[r][i] = (m0 + mm < M && d < D) ? q[d] : 0.f;
+        qv[r][i] = (m0 + mm < M && d < D) ? MP::ld(&q[d]) : 0.f;
       }
     }
 #pragma unroll
@@ -337,7 +337,7 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
 #pragma unroll
         for (int i = 0; i < QD; ++i) {
           const int d = ln + 64 * i;
-          kv[q][i] = (t0 + q < tn1 && d < D) ? k[d] : 0.f;
+          kv[q][i] = (t0 + q < tn1 && d < D) ? MP::ld(&k[d]) : 0.f;
         }
       }
 #pragma unroll
@@ -394,8 +394,8 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
           float fk[16], fv[16];
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            fk[e] = e < EPC ? kq[e] * rk[t] * L.k_norm[d0 + e] : 0.f;
-            fv[e] = e < EPC ? vq[e] : 0.f;
+            fk[e] = e < EPC ? MP::ld(&kq[e]) * rk[t] * L.k_norm[d0 + e] : 0.f;
+            fv[e] = e < EPC ? MP::ld(&vq[e]) : 0.f;
           }
           const v4u ek = encode16<KDT>(fk), ev = encode16<KDT>(fv);
           *reinterpret_cast<v4u*>(kt + row * RB + col * 16) = ek;
@@ -474,18 +474,18 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
     for (int k = 0; k < EPLV; ++k) o[r][k] = sum_groups<LPP>(o[r][k]);
     if (pg == 0) {
 #pragma unroll
-      for (int k = 0; k < EPLV; ++k) part[mm * (D + 1) + dc * EPLV + k] = o[r][k];
+      for (int k = 0; k < EPLV; ++k) MP::st(&part[mm * (D + 1) + dc * EPLV + k], o[r][k]);
     }
-    if (ln == 0) part[mm * (D + 1) + D] = l;
+    if (ln == 0) MP::st(&part[mm * (D + 1) + D], l);
   }
 }
 
-template <int KDT, int D>
+template <int KDT, int D, class MP = Plain>
 __device__ void phase_attn(const LayerArgs& L, const StepArgs& S, const AttnPlan* P,
                            uint8_t* lds, int vb, int nvb) {
   const int n_items = P->item0[S.n_req];
   for (int item = vb; item < n_items; item += nvb) {
-    attn_item<KDT, D>(L, S, P, item, lds);
+    attn_item<KDT, D, MP>(L, S, P, item, lds);
     __syncthreads();
   }
 }
@@ -495,6 +495,7 @@ __device__ void phase_attn(const LayerArgs& L, const StepArgs& S, const AttnPlan
 // q head): wave w adds the chunks w, w + kWaves, ... (sixteen chunks' loads
 // in flight), then wave 0 adds the waves' sums in wave order.  red: LDS of
 // kWaves * (D + 1) floats.
+template <class MP = Plain>
 __device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int* win_out,
                               int vb, int nvb, float* red, unsigned short* a3 = nullptr) {
   const int D = L.D, G = L.Hq / L.Hkv;
@@ -518,9 +519,9 @@ __device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnP
       for (int q = 0; q < 16; ++q) {
         const int c = c0 + q * kWaves;
         const float* p = base + (size_t)(c < nch ? c : c0) * stride;
-        pl[q] = p[D];
-        p0[q] = p[d0];
-        p1[q] = p[d1];
+        pl[q] = MP::ld(&p[D]);
+        p0[q] = MP::ld(&p[d0]);
+        p1[q] = MP::ld(&p[d1]);
       }
 #pragma unroll
       for (int q = 0; q < 16; ++q)
@@ -543,8 +544,8 @@ __device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnP
       }
       const size_t at = (size_t)tok * L.Hq * D + (size_t)hh * D;
       const float v0 = o0 / l, v1 = o1 / l;
-      if (ln < D) S.attn_o[at + ln] = v0;
-      if (ln + 64 < D) S.attn_o[at + ln + 64] = v1;
+      if (ln < D) MP::st(&S.attn_o[at + ln], v0);
+      if (ln + 64 < D) MP::st(&S.attn_o[at + ln + 64], v1);
       if (a3 != nullptr) {  // bf16 terms of the output projection's input
         const size_t plane = (size_t)S.T * L.Hq * D;
         unsigned h, m, lo;

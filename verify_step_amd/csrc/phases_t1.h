@@ -14,16 +14,17 @@ __device__ __forceinline__ int my_count(int gw, int nw, int ntask) {
 }
 
 // act[c] = x[c] * g[c] / sqrt(mean(x^2) + eps) into LDS (g may be null).
+template <class M = Plain>
 __device__ inline void stage_norm_t1(const float* x, const float* g, int H, float eps, float* act,
                                      float* red) {
   float s = 0.f;
   for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
-    v4f a = *reinterpret_cast<const v4f*>(x + c);
+    v4f a = M::ld4(x + c);
     s += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
   }
   const float r = 1.0f / sqrtf(block_sum(s, red) / (float)H + eps);
   for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
-    v4f a = *reinterpret_cast<const v4f*>(x + c);
+    v4f a = M::ld4(x + c);
     v4f gg = *reinterpret_cast<const v4f*>(g + c);
     *reinterpret_cast<v4f*>(act + c) = v4f{a.x * r * gg.x, a.y * r * gg.y, a.z * r * gg.z, a.w * r * gg.w};
   }
@@ -31,9 +32,10 @@ __device__ inline void stage_norm_t1(const float* x, const float* g, int H, floa
 }
 
 // Plain copy of n floats (n % 4 == 0) into LDS.
+template <class M = Plain>
 __device__ inline void stage_copy(const float* src, int n, float* dst) {
   for (int c = threadIdx.x * 4; c < n; c += blockDim.x * 4)
-    *reinterpret_cast<v4f*>(dst + c) = *reinterpret_cast<const v4f*>(src + c);
+    *reinterpret_cast<v4f*>(dst + c) = M::ld4(src + c);
   __syncthreads();
 }
 
@@ -47,7 +49,7 @@ __device__ __forceinline__ void lane_store(const float (&acc)[R], F&& st) {
 }
 
 // qkv[r] = sum_c W[r][c] act[c] over the stacked rows of wq, wk, wv.
-template <int DT, class Pre>
+template <int DT, class M = Plain, class Pre>
 __device__ void qkv_t1(const LayerArgs& L, const StepArgs& S, const float* act, int vb, int nvb,
                        Pre&& pre) {
   constexpr int R = 4, U = 2;
@@ -69,13 +71,13 @@ __device__ void qkv_t1(const LayerArgs& L, const StepArgs& S, const float* act, 
       },
       [&](int k, auto& acc) {
         const int r0 = (gw + k * nw) * R;
-        lane_store<R>(acc, [&](int r, float v) { S.qkv[r0 + r] = v; });
+        lane_store<R>(acc, [&](int r, float v) { M::st(&S.qkv[r0 + r], v); });
       },
       pre);
 }
 
 // h[r] = x[r] + sum_c wo[r][c] act[c]  (act = staged attention output)
-template <int DT, class Pre>
+template <int DT, class M = Plain, class Pre>
 __device__ void wo_t1(const LayerArgs& L, const StepArgs& S, const float* x, float* h,
                       const float* act, int vb, int nvb, Pre&& pre) {
   // two rows per task: at hidden 6144 one task per wave then gives twice the
@@ -100,7 +102,7 @@ __device__ void wo_t1(const LayerArgs& L, const StepArgs& S, const float* x, flo
       [&](int k, auto& acc) {
         const int r0 = (gw + k * nw) * R;
         lane_store<R>(acc, [&](int r, float v) {
-          if (r0 + r < L.H) h[r0 + r] = x[r0 + r] + v;
+          if (r0 + r < L.H) M::st(&h[r0 + r], M::ld(&x[r0 + r]) + v);
         });
       },
       pre);
@@ -112,7 +114,7 @@ __device__ void wo_t1(const LayerArgs& L, const StepArgs& S, const float* x, flo
 // the quarters are added in fixed order.  part: LDS [kWaves][kRouterRows].
 constexpr int kRouterRows = 16;
 
-template <int DT, class Stage>
+template <int DT, class M = Plain, class Stage>
 __device__ void router_t1(const LayerArgs& L, const StepArgs& S, float* act, float* part, int vb,
                           int nvb, Stage stage) {
   constexpr int R = 1, U = 2;
@@ -135,14 +137,14 @@ __device__ void router_t1(const LayerArgs& L, const StepArgs& S, float* act, flo
         const int per = ((L.H / 4 + nvb - 1) / nvb) * 4;
         const int c0 = vb * per, c1 = c0 + per < L.H ? c0 + per : L.H;
         for (int c = c0 + threadIdx.x * 4; c < c1; c += blockDim.x * 4)
-          *reinterpret_cast<v4f*>(S.u + c) = *reinterpret_cast<const v4f*>(act + c);
+          M::st4(S.u + c, *reinterpret_cast<const v4f*>(act + c));
       });
   __syncthreads();
   for (int k = threadIdx.x; k < n; k += blockDim.x) {
     float v = 0.f;
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) v += part[q * kRouterRows + k];
-    S.logits[vb + k * nvb] = v;
+    M::st(&S.logits[vb + k * nvb], v);
   }
 }
 
@@ -234,6 +236,7 @@ __device__ __forceinline__ void topk_vals(const float (&x)[4], int E, int K,
 }
 
 // The same with the logits read from memory.
+template <class M = Plain>
 __device__ __forceinline__ void topk_regs(const float* logits, int E, int K,
                                           int (&bis)[kMaxTopK], float (&exs)[kMaxTopK],
                                           float& den) {
@@ -242,7 +245,7 @@ __device__ __forceinline__ void topk_regs(const float* logits, int E, int K,
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = ln + 64 * i;
-    x[i] = e < E ? logits[e] : -INFINITY;
+    x[i] = e < E ? M::ld(&logits[e]) : -INFINITY;
   }
   topk_vals(x, E, K, bis, exs, den);
 }
@@ -276,7 +279,7 @@ __device__ void phase_topk(const LayerArgs& L, const StepArgs& S, int* topk_out,
 }
 
 // act[j][f] = silu(gate_e[f] . u) * (up_e[f] . u), e = idx[j]; u staged in LDS.
-template <int DT, class Sel, class Pre>
+template <int DT, class M = Plain, class Sel, class Pre>
 __device__ void gateup_t1(const LayerArgs& L, const StepArgs& S, Sel&& idx, const float* u,
                           int vb, int nvb, Pre&& pre) {
   constexpr int R = 2, U = 2;
@@ -308,7 +311,7 @@ __device__ void gateup_t1(const LayerArgs& L, const StepArgs& S, Sel&& idx, cons
         float res[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) res[r] = silu(acc[r] * gs) * (acc[R + r] * us);
-        lane_store<R>(res, [&](int r, float v) { S.act[(size_t)j * L.F + f0 + r] = v; });
+        lane_store<R>(res, [&](int r, float v) { M::st(&S.act[(size_t)j * L.F + f0 + r], v); });
       },
       pre);
 }
@@ -317,7 +320,7 @@ __device__ void gateup_t1(const LayerArgs& L, const StepArgs& S, Sel&& idx, cons
 // act staged in LDS as [K][F].  Entries of idx outside [0, E) add nothing.
 // Each lane folds the weighted partial sums of the K experts of a row block
 // together and the wave reduces once per row block.
-template <int DT, class Pre>
+template <int DT, class M = Plain, class Pre>
 __device__ void down_t1(const LayerArgs& L, const StepArgs& S, const int* idx, const float* wts,
                         const float* act, const float* h, float* out, float* out2, int vb,
                         int nvb, Pre&& pre) {
@@ -384,8 +387,8 @@ __device__ void down_t1(const LayerArgs& L, const StepArgs& S, const int* idx, c
           lane_store<R>(o, [&](int r, float v) {
             const int c = r0 + r;
             if (c < L.H) {
-              const float y = h[c] + v;
-              out[c] = y;
+              const float y = M::ld(&h[c]) + v;
+              M::st(&out[c], y);
               if (out2) out2[c] = y;
             }
           });
