@@ -271,3 +271,33 @@ def test_determinism_and_untouched_slots(prob):
                 bb = b[mask].view(torch.uint8) if b.dtype != torch.uint8 else b[mask]
                 assert torch.equal(aa, bb)
     restore_kv(p, snaps)
+
+
+def test_expert_ffn_with_repeated_experts_in_a_token():
+    """msk_expert_ffn on selections where some token lists an expert twice
+    (the caller's selection, not the router's): every slot still counts, as
+    in the oracle's sum over slots."""
+    print("[gpu-parity] repeated experts", flush=True)
+    p = synth.make_problem("stack4-nvfp4", device="cuda",
+                           overrides=dict(dims=_SMALL, kv_len=[300], windows=[128]))
+    fill_shift(p)
+    spec, w = p.specs[0], p.weights[0]
+    T, H, K = p.T, spec["hidden"], spec["top_k"]
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(spec["n_experts"], K, replace=False) for _ in range(T)])
+    idx[1, 3] = idx[1, 0]                 # token 1 repeats its first expert
+    idx[4, 5] = idx[4, 2] = idx[2, 0]     # token 4 twice the expert token 2 starts with
+    wts = rng.random((T, K))
+    wts /= wts.sum(1, keepdims=True)
+    u = rng.standard_normal((T, H)).astype(np.float32)
+    h = rng.standard_normal((T, H)).astype(np.float32)
+    ws = msk.new_workspace(p.specs[:1], p.kv_len, p.tokens_per_req)
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt)  # noqa: E731
+    out = msk.expert_ffn(spec, w, dev(u), dev(idx, torch.int32), dev(wts.astype(np.float32)),
+                         dev(h), ws)
+    torch.cuda.synchronize()
+    so, wo, _ = oracle_inputs(p, 0)
+    ref = ol.expert_ffn(so, wo, u.astype(np.float64), idx.astype(np.int64),
+                        wts.astype(np.float32).astype(np.float64), h.astype(np.float64))
+    assert_close("moe delta (repeated experts)", out.double().cpu().numpy() - h, ref - h,
+                 tol_for(spec), fp32_store_floor(ref))

@@ -658,15 +658,30 @@ __device__ void phase_topk(const LayerArgs& L, const StepArgs& S, int* topk_out,
 // (t * K + j) routed to it in ascending order.  Built identically by every
 // workgroup from idx.
 
-// sidx: LDS for T * K + 16 ints, 8-byte aligned.
+// sidx: LDS for T * K + 16 ints followed by kMaxExperts + 1 64-bit words,
+// 8-byte aligned.  A slot's place among its expert's slots is the number of
+// earlier slots of that expert.  When no token lists an expert twice (the
+// router's selections never do) that is the number of earlier tokens that
+// selected it: a popcount of the expert's token mask.  Otherwise the earlier
+// slots are counted one by one.
 __device__ inline void build_union(const int* idx, int T, int K, int E, Union* U, int* sidx) {
   const int S = T * K;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) U->start[e] = 0;
+  unsigned long long* mask = reinterpret_cast<unsigned long long*>(sidx + kMaxTok * kMaxTopK + 16);
+  unsigned long long* repeat = mask + kMaxExperts;  // nonzero: some token repeats an expert
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    U->start[e] = 0;
+    mask[e] = 0ull;
+  }
+  if (threadIdx.x == 0) *repeat = 0ull;
   __syncthreads();
   for (int s = threadIdx.x; s < S; s += blockDim.x) {
     const int e = idx[s];
-    sidx[s] = e;  // the selection in LDS: the ranks below read it many times
-    if (e >= 0 && e < E) atomicAdd(&U->start[e], 1);
+    sidx[s] = e;
+    if (e >= 0 && e < E) {
+      atomicAdd(&U->start[e], 1);
+      const unsigned long long bit = 1ull << (s / K);
+      if (atomicOr(&mask[e], bit) & bit) atomicOr(repeat, 1ull);
+    }
   }
   __syncthreads();
   if (wave_id() == 0) {
@@ -711,23 +726,15 @@ __device__ inline void build_union(const int* idx, int T, int K, int E, Union* U
     if (ln == 0) { U->n = inz; U->off[inz] = itot; }
   }
   __syncthreads();
+  const bool repeats = *repeat != 0ull;
   for (int s = threadIdx.x; s < S; s += blockDim.x) {
     const int e = sidx[s];
     if (e < 0 || e >= E) continue;
-    // rank among the earlier slots of the same expert: sixteen slots per
-    // step, read as eight pairs together (entries at s or beyond, up to 15
-    // past the end of the selection, are read and not counted)
     int rank = 0;
-    const int2* sp = reinterpret_cast<const int2*>(sidx);
-    for (int q0 = 0; q0 < s; q0 += 16) {
-      int2 a[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) a[u] = sp[(q0 >> 1) + u];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        rank += (q0 + 2 * u < s && a[u].x == e) ? 1 : 0;
-        rank += (q0 + 2 * u + 1 < s && a[u].y == e) ? 1 : 0;
-      }
+    if (!repeats) {
+      rank = __popcll(mask[e] & ((1ull << (s / K)) - 1ull));
+    } else {
+      for (int q = 0; q < s; ++q) rank += sidx[q] == e ? 1 : 0;
     }
     U->slots[U->start[e] + rank] = s;
   }

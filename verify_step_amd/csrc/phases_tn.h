@@ -16,6 +16,13 @@
 #pragma once
 #include "phases_t1.h"
 
+#ifndef MSK_TN_BF16_NB
+#define MSK_TN_BF16_NB 2
+#endif
+#ifndef MSK_TN_FP4_NB
+#define MSK_TN_FP4_NB 2
+#endif
+
 namespace msk {
 
 // Input vectors staged in LDS are stored in 16-B granules in a rotated order:
@@ -412,9 +419,10 @@ __device__ __forceinline__ void stream_tn(int ntask, int ncols, int nv, ActFn&& 
 }
 
 // The union into global memory (one workgroup).
-// lds: a Union followed by kUnionIdxInts ints of scratch.
+// lds: a Union followed by kUnionIdxInts ints and kMaxExperts + 1 64-bit
+// words of scratch.
 constexpr int kUnionIdxInts = kMaxTok * kMaxTopK + 16;
-constexpr size_t kUnionLds = sizeof(Union) + kUnionIdxInts * sizeof(int);
+constexpr size_t kUnionLds = sizeof(Union) + kUnionIdxInts * sizeof(int) + (kMaxExperts + 1) * 8;
 static_assert(sizeof(Union) % 8 == 0, "the selection after the union is read as int pairs");
 __device__ inline void union_to_global(const int* idx, int T, int K, int E, Union* lds, Union* dst) {
   build_union(idx, T, K, E, lds, reinterpret_cast<int*>(lds + 1));
@@ -460,13 +468,16 @@ template <int DT> struct TnShape;
 // fp32 vectors at expert width 2048); elsewhere they measured the same or
 // slower, and NVFP4's gate/up would lose a wave per SIMD to the registers.
 template <> struct TnShape<kF32> {
-  enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2, GU_VB = 1, GU_C = 0, DN_VB = 1, DN_C = 0 };
+  enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2, GU_VB = 1, GU_C = 0, DN_VB = 1, DN_C = 0,
+         GU_NB = 2, DN_NB = 2 };
 };
 template <> struct TnShape<kBF16> {
-  enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2, GU_VB = 1, GU_C = 0, DN_VB = 1, DN_C = 0 };
+  enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2, GU_VB = 1, GU_C = 0, DN_VB = 1, DN_C = 0,
+         GU_NB = MSK_TN_BF16_NB, DN_NB = MSK_TN_BF16_NB };
 };
 template <> struct TnShape<kNVFP4> {
-  enum { GU_RW = 2, GU_U = 1, DN_R = 4, DN_U = 1, GU_VB = 1, GU_C = 0, DN_VB = 3, DN_C = 1 };
+  enum { GU_RW = 2, GU_U = 1, DN_R = 4, DN_U = 1, GU_VB = 1, GU_C = 0, DN_VB = 3, DN_C = 1,
+         GU_NB = MSK_TN_FP4_NB, DN_NB = MSK_TN_FP4_NB };
 };
 
 // act[s][f] = silu(gate_e[f] . u[t]) * (up_e[f] . u[t]) for slot s = t*K + j.
@@ -503,7 +514,7 @@ __device__ void gateup_tn(const LayerArgs& L, const StepArgs& S, const Union* U,
     };
     nv_dispatch<NVMAX>(nv, [&](auto nvc) {
       constexpr int NV = decltype(nvc)::value;
-      stream_tn<DT, R, UU, NV>(
+      stream_tn<DT, R, UU, NV, TnShape<DT>::GU_NB>(
           nmine, L.H, nv, [&](int v) { return act_lds + v * tn_vec_floats<DT>(L.H); },
           [&](int k, auto& wr, auto& sr) {
             const int f0 = (a + wv + k * NWV - ui * nrt) * RW;
@@ -565,7 +576,7 @@ __device__ void down_tn(const LayerArgs& L, const StepArgs& S, const Union* U, f
     };
     nv_dispatch<NVMAX>(nv, [&](auto nvc) {
       constexpr int NV = decltype(nvc)::value;
-      stream_tn<DT, RD, UU, NV>(
+      stream_tn<DT, RD, UU, NV, TnShape<DT>::DN_NB>(
           nmine, L.F, nv, [&](int v) { return act_lds + v * tn_vec_floats<DT>(L.F); },
           [&](int k, auto& wr, auto& sr) {
             const int c0 = (a + wv + k * NWV - ui * nrt) * RD;
