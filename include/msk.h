@@ -59,7 +59,8 @@ typedef enum {
   MSK_ERR_UNSUPPORTED = 2, /* valid but outside what this library handles   */
   MSK_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
   MSK_ERR_DEVICE = 4,      /* a HIP call or launch failed                   */
-  MSK_ERR_TIMEOUT = 5      /* a device-side wait gave up (see msk_workspace_status) */
+  MSK_ERR_TIMEOUT = 5      /* a device-side wait of an earlier call on the same
+                              workspace gave up (see msk_workspace_status) */
 } msk_status;
 
 typedef enum {
@@ -146,10 +147,12 @@ const char *msk_last_error(void);
 size_t msk_workspace_size(const msk_layer_cfg *cfg, int32_t n_layers,
                           const msk_batch *batch);
 
-/* Synchronises `stream`, then reports whether a device-side wait in a call
- * that used `ws` gave up (MSK_ERR_TIMEOUT; the workspace's synchronisation
- * words are then reset so the next call starts clean) or MSK_OK.
- * MSK_ERR_DEVICE if the stream reports an error. */
+/* Synchronises `stream` and the device, then reports whether a device-side
+ * wait in a call that used `ws` gave up (MSK_ERR_TIMEOUT; the workspace's
+ * synchronisation words are then reset so the next call starts clean) or
+ * MSK_OK.  MSK_ERR_DEVICE if the stream reports an error.  Without this call
+ * the next call on `ws` reports such a wait the same way, after its argument
+ * checks and before it enqueues anything (see msk_layer_step_timeline). */
 msk_status msk_workspace_status(void *ws, size_t ws_bytes, void *stream);
 
 /* Attention half of a layer (steps: attention RMSNorm, QKV projection,
@@ -248,12 +251,24 @@ size_t msk_noalloc_scratch_bytes(void);
  *           = start, then per layer: QKV, attention, combine, Wo, router,
  *           gate/up, down (the first four layers).  Rows of workgroups that
  *           did not run stay zero.
- * A barrier wait that gives up sets the workspace's error flag, which
- * msk_workspace_status reports. */
+ * Every barrier wait is bounded (msk_set_spin_limit): one that gives up sets
+ * the workspace's error flag, and the next call on the workspace (any entry
+ * point that takes it, or msk_workspace_status) synchronises the device
+ * before it enqueues anything, resets the flag and returns MSK_ERR_TIMEOUT.
+ * The library remembers the last 64 workspaces this call ran the persistent
+ * kernel on; the flag of an older one is reported by msk_workspace_status
+ * alone.  The outputs of a call whose wait gave up are undefined. */
 msk_status msk_layer_step_timeline(const msk_layer_cfg *cfg, const msk_layer_weights *w,
                                    const msk_kv *kv, int32_t n_layers, const msk_batch *batch,
                                    float *x, float *layer_out, int32_t *topk_idx, int32_t *win,
                                    int64_t *stamps, void *ws, size_t ws_bytes, void *stream);
+
+/* Test aid: the number of polls after which a device-side barrier wait of
+ * msk_layer_step_timeline gives up (0 restores the default, 2^22 polls, of
+ * seconds).  Process-wide; read by each call when it launches.  A small
+ * bound makes waits give up on purpose, so that the error path can be
+ * exercised with every kernel still running to its end. */
+msk_status msk_set_spin_limit(uint32_t polls);
 
 /* Kernel timing for measurement harnesses.  The step's kernels fall into
  * phases:

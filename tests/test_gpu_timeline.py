@@ -63,3 +63,43 @@ def test_persistent_kernel_matches_oracle(case):
     n = min(32, 1 + PHASES_PER_LAYER * len(p.specs))
     assert (np.diff(st[ran, :n], axis=1) >= 0).all()
     restore_kv(p, snaps)
+
+
+def test_a_wait_that_gives_up_is_reported_by_the_next_call():
+    """The barrier waits of the persistent kernel bounded to one poll give up
+    (forced from the host: every kernel still runs to its end, on whatever
+    its inputs hold).  The next call on the same workspace returns
+    MSK_ERR_TIMEOUT before it enqueues anything, and the call after that runs
+    clean and matches the oracle."""
+    print("[gpu-timeline] watchdog", flush=True)
+    p = synth.make_problem("tiny-fp32", device="cuda")
+    fill_shift(p)
+    snaps = snapshot_kv(p)
+    ws = msk.new_workspace(p.specs, p.kv_len, p.tokens_per_req)
+    n_wg = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    stamps = torch.zeros((n_wg, 32), dtype=torch.int64, device="cuda")
+    x = p.x.clone()
+    msk.set_spin_limit(1)
+    try:
+        msk.layer_step_timeline(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws,
+                                stamps)
+    finally:
+        msk.set_spin_limit(0)
+    torch.cuda.synchronize()
+    assert (stamps[:, 0] > 0).any(), "persistent kernel did not run"
+    restore_kv(p, snaps)
+
+    x = p.x.clone()
+    with pytest.raises(msk.MskError) as e:
+        msk.layer_step(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws)
+    assert e.value.status == 5, e.value
+    torch.cuda.synchronize()
+    assert torch.equal(x, p.x), "the reporting call enqueued work"
+
+    msk.layer_step(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws)
+    torch.cuda.synchronize()
+    msk.workspace_status(ws)
+    spec, w, kv = oracle_inputs(p, 0)
+    ref = ol.layer_step(spec, w, kv, p.kv_len, p.tokens_per_req, p.x.double().cpu().numpy())["out"]
+    assert_close("out after the report", x.double().cpu().numpy(), ref, tol_for(spec))
+    restore_kv(p, snaps)

@@ -100,6 +100,8 @@ def lib():
                                              vp, vp, vp, vp, vp]
         L.msk_noalloc_scratch_bytes.restype = sz
         L.msk_noalloc_scratch_bytes.argtypes = []
+        L.msk_set_spin_limit.restype = i32
+        L.msk_set_spin_limit.argtypes = [ctypes.c_uint32]
         L.msk_timer_start.restype = i32
         L.msk_timer_start.argtypes = [ctypes.c_uint32]
         L.msk_timer_read.restype = i32
@@ -252,6 +254,12 @@ def layer_step_noalloc(specs, weights, kvs, kv_len, tokens_per_req, x, layer_out
 
 def noalloc_scratch_bytes():
     return lib().msk_noalloc_scratch_bytes()
+
+
+def set_spin_limit(polls):
+    """Polls before a barrier wait of the timeline call gives up (0: the
+    default)."""
+    _check(lib().msk_set_spin_limit(polls))
 
 
 PHASES = ("qkv", "attn", "combine", "wo", "router", "topk", "gateup", "down", "step", "union",

@@ -3,10 +3,12 @@
 // call, so invalid arguments return with nothing enqueued.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/msk.h"
 #include "launch.h"
@@ -363,6 +365,61 @@ msk_status device_status(hipError_t e, const char* what) {
   return fail(MSK_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Polls before a device-side wait gives up (msk_set_spin_limit).
+std::atomic<unsigned> g_spin_limit{msk::kSpinLimit};
+
+// Reads the workspace's error word once the device is idle; a set word is
+// reported as MSK_ERR_TIMEOUT and the synchronisation words are reset, so
+// the next call starts clean.
+msk_status read_watchdog(void* ws) {
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return device_status(e, "hipDeviceSynchronize");
+  unsigned words[2] = {0, 0};
+  e = hipMemcpy(words, ws, sizeof(words), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return device_status(e, "hipMemcpy");
+  if (words[1] == 0) return ok();
+  e = hipMemset(ws, 0, msk::kSyncBytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return device_status(e, "hipMemset");
+  return fail(MSK_ERR_TIMEOUT, "a device-side wait of an earlier call on this workspace gave up "
+                               "(barrier watchdog)");
+}
+
+// Workspaces whose latest launch was the persistent step kernel, the one
+// kernel with device-side waits.  The next call on such a workspace reads its
+// error word before it enqueues anything (a device synchronisation, paid only
+// after such a launch).  At most kWatched are remembered; past that the
+// oldest is forgotten, and a trip of its launch stays in the workspace for
+// msk_workspace_status to report.
+constexpr int kWatched = 64;
+std::mutex g_watch_mu;
+void* g_watch[kWatched];
+int g_watch_n = 0;
+
+void watch(void* ws) {
+  std::lock_guard<std::mutex> g(g_watch_mu);
+  for (int i = 0; i < g_watch_n; ++i)
+    if (g_watch[i] == ws) return;
+  if (g_watch_n == kWatched) {
+    for (int i = 1; i < kWatched; ++i) g_watch[i - 1] = g_watch[i];
+    --g_watch_n;
+  }
+  g_watch[g_watch_n++] = ws;
+}
+
+bool unwatch(void* ws) {
+  std::lock_guard<std::mutex> g(g_watch_mu);
+  for (int i = 0; i < g_watch_n; ++i)
+    if (g_watch[i] == ws) {
+      g_watch[i] = g_watch[--g_watch_n];
+      return true;
+    }
+  return false;
+}
+
+// The watchdog check every call on a workspace makes after its argument checks.
+msk_status watchdog(void* ws) { return unwatch(ws) ? read_watchdog(ws) : MSK_OK; }
+
 // A one-token batch description for the calls that take only a token count.
 struct FlatBatch {
   int32_t zero[MSK_MAX_TOKENS] = {};
@@ -399,19 +456,10 @@ size_t msk_workspace_size(const msk_layer_cfg* cfg, int32_t n_layers, const msk_
 msk_status msk_workspace_status(void* ws, size_t ws_bytes, void* stream) {
   if (!ws || ws_bytes < (size_t)msk::kSyncBytes)
     return fail(MSK_ERR_WORKSPACE, "workspace missing or too small");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = hipStreamSynchronize(st);
+  const hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_status(e, "hipStreamSynchronize");
-  unsigned words[2] = {0, 0};
-  e = hipMemcpy(words, ws, sizeof(words), hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return device_status(e, "hipMemcpy");
-  if (words[1] != 0) {
-    // a barrier wait gave up: epochs may be inconsistent, start them over
-    e = hipMemset(ws, 0, msk::kSyncBytes);
-    if (e != hipSuccess) return device_status(e, "hipMemset");
-    return fail(MSK_ERR_TIMEOUT, "a device-side wait gave up (barrier watchdog)");
-  }
-  return ok();
+  unwatch(ws);
+  return read_watchdog(ws);
 }
 
 msk_status msk_attn_step(const msk_layer_cfg* cfg, const msk_layer_weights* w, const msk_kv* kv,
@@ -426,6 +474,7 @@ msk_status msk_attn_step(const msk_layer_cfg* cfg, const msk_layer_weights* w, c
   const Layout lay = layout(cfg, 1, *batch);
   if (!ws || ws_bytes < lay.total)
     return fail(MSK_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, lay.total);
+  CHECK(watchdog(ws));
   msk::LayerArgs L = make_layer(*cfg, w, kv, batch);
   msk::StepArgs S = make_step(lay, ws, batch->n_req, batch->tokens_per_req, batch->kv_len_host);
   S.n_layers = 1;
@@ -447,6 +496,7 @@ msk_status msk_moe_route(const msk_layer_cfg* cfg, const msk_layer_weights* w, i
   const Layout lay = layout(cfg, 1, fb.b, false);
   if (!ws || ws_bytes < lay.total)
     return fail(MSK_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, lay.total);
+  CHECK(watchdog(ws));
   msk::LayerArgs L = make_layer(*cfg, w, nullptr, nullptr);
   msk::StepArgs S = make_step(lay, ws, n_tokens, 1, nullptr);
   S.u = u;
@@ -470,6 +520,7 @@ msk_status msk_expert_ffn(const msk_layer_cfg* cfg, const msk_layer_weights* w, 
   const Layout lay = layout(cfg, 1, fb.b, false);
   if (!ws || ws_bytes < lay.total)
     return fail(MSK_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, lay.total);
+  CHECK(watchdog(ws));
   msk::LayerArgs L = make_layer(*cfg, w, nullptr, nullptr);
   msk::StepArgs S = make_step(lay, ws, n_tokens, 1, nullptr);
   S.u = const_cast<float*>(u);
@@ -512,6 +563,7 @@ static msk_status layer_step_impl(const msk_layer_cfg* cfg, const msk_layer_weig
   }
   if (!ws || ws_bytes < lay.total)
     return fail(MSK_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, lay.total);
+  if (!noalloc) CHECK(watchdog(ws));
   msk::LayerArgs Ls[msk::kMaxLayers];
   for (int l = 0; l < n_layers; ++l) Ls[l] = make_layer(cfg[l], &w[l], &kv[l], batch);
   msk::StepArgs S = make_step(lay, ws, batch->n_req, batch->tokens_per_req, batch->kv_len_host);
@@ -522,14 +574,18 @@ static msk_status layer_step_impl(const msk_layer_cfg* cfg, const msk_layer_weig
   S.topk_out = topk_idx;
   S.win_out = win;
   S.stamps = reinterpret_cast<long long*>(stamps);
+  S.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   // Per-phase kernels measure faster than the persistent kernel on this part
   // (its grid barriers cost more than the kernel boundaries they replace),
   // so only the timeline call, whose in-kernel stamps need it, runs the
   // persistent kernel.
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (noalloc) return device_status(msk::launch_step_noalloc(Ls, S, st), "layer-step launch");
-  return device_status(stamps ? msk::launch_step_fused(Ls, S, st) : msk::launch_step_unfused(Ls, S, st),
-                       "layer-step launch");
+  if (!stamps) return device_status(msk::launch_step_unfused(Ls, S, st), "layer-step launch");
+  bool persistent = false;
+  const hipError_t e = msk::launch_step_fused(Ls, S, st, &persistent);
+  if (e == hipSuccess && persistent) watch(ws);
+  return device_status(e, "layer-step launch");
 }
 
 msk_status msk_layer_step(const msk_layer_cfg* cfg, const msk_layer_weights* w, const msk_kv* kv,
@@ -549,6 +605,11 @@ msk_status msk_layer_step_noalloc(const msk_layer_cfg* cfg, const msk_layer_weig
 }
 
 size_t msk_noalloc_scratch_bytes(void) { return msk::kScratchBytes; }
+
+msk_status msk_set_spin_limit(uint32_t polls) {
+  g_spin_limit.store(polls ? polls : msk::kSpinLimit, std::memory_order_relaxed);
+  return ok();
+}
 
 msk_status msk_layer_step_timeline(const msk_layer_cfg* cfg, const msk_layer_weights* w,
                                    const msk_kv* kv, int32_t n_layers, const msk_batch* batch,

@@ -575,8 +575,4 @@ __device__ __forceinline__ float layer_shift(float given, v2f gq, v2f gk, int D)
   return sqrtf((float)D) * mq * mk;
 }
 
-// Bound of every device-side wait: past it a wait gives up and sets the
-// workspace's error flag instead of hanging the GPU.
-constexpr unsigned kSpinLimit = 1u << 22;
-
 }  // namespace msk

@@ -402,12 +402,17 @@ __global__ __launch_bounds__(kBlockThreads) void k_down_t1(LayerArgs L, StepArgs
 // loads and stores, so no barrier needs an L2 writeback or invalidate
 // (measured here: 2.1 us per barrier over 256 workgroups and 2.6 us over
 // 512, against 5.6-9.3 us with agent-scope fences, and 3.9-6.8 us with one
-// counter for all workgroups).  Every wait is bounded: a missing arrival
-// sets the error flag (reported by msk_workspace_status) instead of hanging.
+// counter for all workgroups).  Every wait is bounded (StepArgs::spin_limit
+// polls): a missing arrival sets the workspace's error flag instead of
+// hanging, and the next call on that workspace reports it.  A workgroup whose
+// wait gave up runs on with whatever its inputs hold: every index it derives
+// from data is clamped to its range, so its accesses stay in bounds, and its
+// later waits are bounded the same way.
 constexpr int kTreeGroups = 8;
 struct TreeSync {
   unsigned* w;
   unsigned epoch;
+  unsigned limit;  // polls before a wait gives up
 };
 
 __device__ __forceinline__ unsigned a_ld(unsigned* p) {
@@ -420,10 +425,10 @@ __device__ __forceinline__ unsigned a_add(unsigned* p, unsigned v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ TreeSync tree_begin(unsigned* w) {
+__device__ __forceinline__ TreeSync tree_begin(unsigned* w, unsigned limit) {
   // every workgroup reads the same generation: it cannot advance before all
   // of this launch's workgroups have arrived at its first barrier
-  return TreeSync{w, a_ld(&w[0])};
+  return TreeSync{w, a_ld(&w[0]), limit};
 }
 
 __device__ __forceinline__ void tree_sync(TreeSync& ts) {
@@ -446,7 +451,7 @@ __device__ __forceinline__ void tree_sync(TreeSync& ts) {
     unsigned spins = 0;
     while ((int)(a_ld(&w[0]) - ts.epoch) < 0) {
       __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
+      if (++spins > ts.limit) {
         a_st(&w[1], 1u);
         break;
       }
@@ -502,7 +507,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_step_p(StepLayers PK) {
       S.stamps[(size_t)vb * kStamps + slot] = (long long)__builtin_amdgcn_s_memrealtime();
   };
   if (PK.l0 == 0) stamp(0);
-  TreeSync ts = tree_begin(S.sync);
+  TreeSync ts = tree_begin(S.sync, S.spin_limit);
   float* red = reinterpret_cast<float*>(msk_smem + PLds::red);
   int* tki = reinterpret_cast<int*>(msk_smem + PLds::tki);
   float* tkw = reinterpret_cast<float*>(msk_smem + PLds::tkw);
@@ -1186,8 +1191,10 @@ bool persistent_supported(const LayerArgs* Ls, const StepArgs& S) {
 
 // The whole one-token step as the persistent kernel where an instantiation
 // exists and its workgroups fit; otherwise the per-phase kernels.
-hipError_t launch_step_fused(const LayerArgs* Ls, const StepArgs& S, hipStream_t st) {
+hipError_t launch_step_fused(const LayerArgs* Ls, const StepArgs& S, hipStream_t st,
+                             bool* persistent) {
   bool launched = false;
+  *persistent = false;
   if (persistent_supported(Ls, S)) {
     const LayerArgs& L = Ls[0];
     if (L.ddt == kBF16 && L.edt == kBF16)
@@ -1197,6 +1204,7 @@ hipError_t launch_step_fused(const LayerArgs* Ls, const StepArgs& S, hipStream_t
     else
       MSK_TRY((launch_persistent<kF32, kF32, kF32, 32>(Ls, S, st, &launched)));
   }
+  *persistent = launched;
   if (launched) return hipSuccess;
   return launch_step_unfused(Ls, S, st);
 }

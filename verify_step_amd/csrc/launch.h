@@ -33,9 +33,12 @@ hipError_t launch_ffn(const LayerArgs& L, const StepArgs& S, const float* h, flo
 bool qkv_on_mfma(const LayerArgs& L, const StepArgs& S);
 // The expert phase of S's tokens runs the one-token kernels.
 bool ffn_one_token(const LayerArgs& L, const StepArgs& S);
-// Whole step over S.n_layers layers as one persistent cooperative kernel.
-hipError_t launch_step_fused(const LayerArgs* Ls, const StepArgs& S, hipStream_t st);
-// Whole step as a sequence of per-phase kernels (the unfused comparison path).
+// Whole step over S.n_layers layers as the persistent step kernel (one launch
+// per kMaxFusedLayers layers) where an instantiation covers the shape, else
+// as launch_step_unfused; *persistent says which ran.
+hipError_t launch_step_fused(const LayerArgs* Ls, const StepArgs& S, hipStream_t st,
+                             bool* persistent);
+// Whole step as a sequence of per-phase kernels.
 hipError_t launch_step_unfused(const LayerArgs* Ls, const StepArgs& S, hipStream_t st);
 
 // Scratch of the allocation-free entry point: kScratchBytes per GPU, at the

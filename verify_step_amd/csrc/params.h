@@ -52,6 +52,10 @@ struct LayerArgs {
   int attn_nph; // matrix-core attention: waves sharing each 16-row tile (1, 2)
 };
 
+// Default bound, in polls, of every device-side wait: past it a wait gives up
+// and sets the workspace's error flag instead of hanging the GPU.
+constexpr unsigned kSpinLimit = 1u << 22;
+
 // Buffers of one step; the per-layer arrays follow the layer index.
 struct StepArgs {
   int n_req, Tr, T, n_layers;
@@ -79,6 +83,7 @@ struct StepArgs {
   float *dpart;         // dense partial tiles
   unsigned *sync;       // kSyncBytes of barrier and counter words (zero between calls)
   long long *stamps;    // optional timeline [blocks][kStamps] of 100 MHz counter values
+  unsigned spin_limit;  // polls before a device-side wait gives up
 };
 
 // K slices of a matrix-core dense projection with N rows (blocks of 64) and
