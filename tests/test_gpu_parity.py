@@ -83,6 +83,13 @@ CASES = {
     # layer), several tokens, NVFP4 experts: layer l + 1 reads layer l's output
     "deep16-small": ("deep32-nvfp4", dict(dims=_SMALL, kv_len=[500], tokens_per_req=4,
                                           windows=[128, 128, 128, 0] * 4)),
+    # e4m3 matrix-core attention over three row tiles (one wave of the item
+    # idle): 40 rows per kv head (the third tile half live), full context; and
+    # 36 rows with each draft's own sliding window
+    "verify-m40-e4m3": ("verify-bf16-128k", dict(dims=dict(_SMALL, n_q_heads=10),
+                                                 kv_len=[20000, 130])),
+    "verify-m36-e4m3-swa": ("verify-bf16-128k", dict(dims=_SMALL, tokens_per_req=6,
+                                                     kv_len=[3000, 2100], windows=[2048])),
     # one token over a long e4m3 history: vector attention items of five tiles
     "decode-e4m3-long": ("decode-bf16", dict(dims=_SMALL, kv="e4m3", kv_len=[300000],
                                              windows=[0])),

@@ -50,7 +50,7 @@ struct AttnSplit {
 // Query rows of one (request, kv head) pair, G * Tr, go to the matrix cores
 // when they fill more than one row group of the vector path and the cache
 // values are exact in bf16 (bf16 or e4m3 caches); each wave then takes 16
-// rows, at most four waves per item.
+// rows (or half the positions of 16 rows), at most 64 rows per item.
 AttnSplit plan_attention(const msk_layer_cfg& c, const msk_batch& b) {
   const int G = c.n_q_heads / c.n_kv_heads;
   const int M = G * b.tokens_per_req;
@@ -83,7 +83,9 @@ AttnSplit plan_attention(const msk_layer_cfg& c, const msk_batch& b) {
   // (three per CU on 256 CUs) that its e4m3 head_dim-128 form keeps resident.
   // Fewer, longer items mean fewer partials for the combine and less start-up
   // per item; the chunk grows until every request's partial last chunk still
-  // fits, so no round is left with a handful of full-length items.
+  // fits, so no round is left with a handful of full-length items.  (The
+  // e4m3 head_dim-128 items take their head's 64-position tiles round-robin
+  // rather than as one range; the count of items is the same.)
   const long long target = mfma ? kAttnRounds * 768LL : kTargetItems;
   auto count = [&](long long ch) {
     long long n = 0;

@@ -412,23 +412,28 @@ __device__ void attn_item_mfma(const LayerArgs& L, const StepArgs& S, const Attn
 // its V^T operand read from the raw V tile by the gfx950 transpose load
 // (ds_read_b64_tr_b8) and converted in registers: no converted copy of V.
 //
-// Raw tiles (64 positions x 128 B of K, then of V) land in a three-slot LDS
-// ring through direct global->LDS loads, two tiles ahead, each issued as
-// soon as the slot it overwrites is released, so no register holds a tile in
-// flight.  A tile row's 16-B chunk c sits at chunk c ^ ((row >> 1) & 7) of
+// Raw tiles (64 positions x 128 B of K, then of V) land in an NSLOT-slot LDS
+// ring through direct global->LDS loads, NSLOT - 1 tiles ahead, each issued
+// as soon as the slot it overwrites is released, so no register holds a tile
+// in flight.  A tile row's 16-B chunk c sits at chunk c ^ ((row >> 1) & 7) of
 // the row: the 16 rows of a score operand read then hit 16 distinct bank
 // groups, and so do the 16 lanes of a transpose load.
-constexpr int kF8Slots = 3;  // ring depth: tiles in flight + 1
-
+//
+// Item shapes (waves per 16-row tile NPH): four row tiles (NPH 1), or up to
+// two with wave pairs splitting each tile's positions (NPH 2); four waves,
+// three workgroups per CU.  One tile ahead per workgroup (NSLOT 2) measures
+// as fast as two or three on this part: with 48 KB in flight per CU the
+// cache stream is as close to its ceiling as deeper rings bring it.
 template <int NPH>
 struct F8Geom {
   static constexpr int D = 128, NW = 4;
   static constexpr int RAW = 64 * D;                 // one raw K or V tile, bytes
   static constexpr int SLOT = 2 * RAW;               // K then V
-  static constexpr int NSLOT = kF8Slots;
+  static constexpr int NSLOT = 2;
   static constexpr int LDS_RING = NSLOT * SLOT;
-  static constexpr int LDS = LDS_RING + kMaxTok * 4;
+  static constexpr int LDS = 128 + LDS_RING + kMaxTok * 4;  // ring aligned to 128 B
   static constexpr int ROWS = 16 * NW / NPH, NPT = 4 / NPH, NKS = 2 / NPH, NDT = D / 16;
+  static_assert(NSLOT >= 2 && NSLOT <= 4, "vmcnt waits cover up to two tiles ahead");
 };
 
 __device__ __forceinline__ int f8_slot(int row, int c) { return row * 8 + (c ^ ((row >> 1) & 7)); }
@@ -442,14 +447,54 @@ __device__ __forceinline__ unsigned e4m3x2_bf16(unsigned w) {
   return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
+// The eight transpose reads of one k-step's V^T operands (one per 16-dim
+// tile dt, at LDS byte (base ^ (dt << 4)) + OFF), issued together and waited
+// for in the same asm block.  Written with the builtin, each read made the compiler
+// wait for every global->LDS load in flight first (it cannot tell the slot
+// being read from the slots being filled), which drained the tile prefetch
+// once per tile.  The reads here only touch a slot whose loads the loop has
+// already waited for.
+template <int OFF>
+__device__ __forceinline__ void v_tr_reads(unsigned base, v2i (&r)[8]) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  // the seven other addresses are formed inside the block, so that they are
+  // not kept live across the tile loop
+  unsigned t[7];
+  asm volatile(
+      "v_xor_b32 %8, 16, %15\n\t"
+      "v_xor_b32 %9, 32, %15\n\t"
+      "v_xor_b32 %10, 48, %15\n\t"
+      "v_xor_b32 %11, 64, %15\n\t"
+      "v_xor_b32 %12, 0x50, %15\n\t"
+      "v_xor_b32 %13, 0x60, %15\n\t"
+      "v_xor_b32 %14, 0x70, %15\n\t"
+      "ds_read_b64_tr_b8 %0, %15 offset:%16\n\t"
+      "ds_read_b64_tr_b8 %1, %8 offset:%16\n\t"
+      "ds_read_b64_tr_b8 %2, %9 offset:%16\n\t"
+      "ds_read_b64_tr_b8 %3, %10 offset:%16\n\t"
+      "ds_read_b64_tr_b8 %4, %11 offset:%16\n\t"
+      "ds_read_b64_tr_b8 %5, %12 offset:%16\n\t"
+      "ds_read_b64_tr_b8 %6, %13 offset:%16\n\t"
+      "ds_read_b64_tr_b8 %7, %14 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]),
+        "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6])
+      : "v"(base), "i"(OFF)
+      : "memory");
+}
+
+// A ring slot index as a type (the tile loop is unrolled over the slots).
+template <int N> struct F8Slot { static constexpr int v = N; };
+
 template <int NPH>
 __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPlan* P, int item,
                              uint8_t* wl) {
   using Gm = F8Geom<NPH>;
   constexpr int D = Gm::D, NW = Gm::NW, RB = D, CPR = D / 16, EPC = 16;
   constexpr int NDT = Gm::NDT, ROWS = Gm::ROWS, NPT = Gm::NPT, NKS = Gm::NKS;
-  uint8_t* ring = wl;
-  float* rk = reinterpret_cast<float*>(wl + Gm::LDS_RING);
+  uint8_t* ring = wl + ((128 - ((unsigned)(size_t)(__attribute__((address_space(3))) uint8_t*)wl & 127)) & 127);
+  float* rk = reinterpret_cast<float*>(ring + Gm::LDS_RING);
 
   const int tid = threadIdx.x, ln = lane_id(), wv = wave_id();
   const int rt = wv / NPH, ph = wv - (wv / NPH) * NPH;
@@ -461,8 +506,13 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
   rem -= j * L.nrg * nch;
   const int rg = rem / nch;
   const int c = rem - rg * nch;
-  const int p0 = P->base[b] + c * L.chunk;
-  const int p1 = p0 + L.chunk < P->end[b] ? p0 + L.chunk : P->end[b];
+  // the head's 64-position tiles in [base, pe) go round-robin to its nch
+  // items: item c takes tiles c, c + nch, ...  The items of a head then
+  // stream neighbouring tiles at any one time, rather than nch regions far
+  // apart.
+  const int pe = P->end[b];
+  const int ts = 64 * nch;               // positions between this item's tiles
+  const int pb0 = P->base[b] + 64 * c;   // its first tile
   const int Lb = S.kv_len[b];
   const int G = L.Hq / L.Hkv;
   const int M = G * S.Tr;
@@ -491,7 +541,7 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
   // are rebuilt below, the other ones are masked)
   auto issue = [&](int pb, uint8_t* slot) {
     const int vlo = pb > lo_min ? pb : lo_min;
-    const int vhi = p1 < Lb ? p1 : Lb;
+    const int vhi = Lb;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int blk = 2 * wv + u;               // 64-granule block of the tile
@@ -519,7 +569,7 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
   }
 #pragma unroll
   for (int k = 0; k + 1 < Gm::NSLOT; ++k)
-    if (p0 + 64 * k < p1) issue(p0 + 64 * k, ring + k * Gm::SLOT);
+    if (pb0 + ts * k < pe) issue(pb0 + ts * k, ring + k * Gm::SLOT);
 
   // qhat as three e4m3 terms, lane: row m = ln & 15, dims 32 (ln >> 4) + e
   v8i qt[3];
@@ -571,9 +621,7 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
     hi_all = min(hi_all, __shfl_xor(hi_all, o));
   }
   const float shift2 = layer_shift(L.shift, gq2, gk2, D) * 1.44269504088896341f;
-  const int tn0 = p0 - Lb > 0 ? p0 - Lb : 0;
-  const int tn1 = p1 - Lb < S.Tr ? p1 - Lb : S.Tr;
-  for (int t = tn0 + wv; t < tn1; t += NW) {
+  for (int t = wv; t < S.Tr; t += NW) {
     const float* k = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + (size_t)j * D;
     float ss = 0.f;
     for (int d = ln; d < D; d += 64) ss += k[d] * k[d];
@@ -595,34 +643,62 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
   f32x4 oacc[NDT];
 #pragma unroll
   for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;
+  // row sums of the rounded weights, on the matrix cores: an all-ones V^T
+  // operand (every entry of the product is the sum of its row's weights)
+  f32x4 sacc_l = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8 ones = as_bf16x8(v4u{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   __syncthreads();  // rk is written
 
-  int it = 0;
-  for (int pb = p0; pb < p1; pb += 64, ++it) {
-    uint8_t* slot = ring + (it % Gm::NSLOT) * Gm::SLOT;
+  // Per-lane LDS offsets within a ring slot, fixed for the item (a slot's
+  // own offset is a constant of each unrolled tile below).  Score operand:
+  // row 16 pt + r16 of the K tile, chunks 2 (ln >> 4) and + 1; the chunk
+  // swizzle depends only on r16.  Transpose reads: slot byte
+  // vr + ((dt ^ sw) << 4) = (vr | sw << 4) ^ (dt << 4), as bits 4..6 of vr
+  // are zero; sw does not depend on the k-step, whose rows sit 4096 B apart.
+  const int r16 = ln & 15, swr = (r16 >> 1) & 7;
+  const unsigned ring_lds = (unsigned)(size_t)(__attribute__((address_space(3))) uint8_t*)ring;
+  const int ka0 = (r16 * 8 + ((2 * (ln >> 4)) ^ swr)) * 16 + ph * NPT * 2048;
+  const int ka1 = (r16 * 8 + ((2 * (ln >> 4) + 1) ^ swr)) * 16 + ph * NPT * 2048;
+  unsigned tra;  // LDS address of dim tile 0's transpose read; tile dt: tra ^ (dt << 4)
+  {
+    const int q = ln & 15, m = q >> 1;
+    const int vrow = 32 * ph * NKS + 4 * (ln >> 4) + (m & 3) + 16 * (m >> 2);
+    const unsigned vr = Gm::RAW + vrow * 128 + 8 * (q & 1);  // within the slot
+    const unsigned sw = (unsigned)((vrow >> 1) & 7);
+    tra = ring_lds + (vr | (sw << 4));  // the ring is 128-B aligned: bits 4..6 are sw
+  }
+  // the rows' common window, uniform over the wave, in scalar registers
+  const int lo_s = __builtin_amdgcn_readfirstlane(lo_all);
+  const int hi_s = __builtin_amdgcn_readfirstlane(hi_all);
+  const bool dead = m0 + 16 * rt >= M;
+
+  // One tile at positions [pb, pb + 64) in ring slot SC::v.
+  auto tile = [&](auto SC, int pb) {
+    constexpr int SL = decltype(SC)::v;
+    uint8_t* slot = ring + SL * Gm::SLOT;
     // this wave's loads of the tile have landed (the later tiles' 4 loads
-    // each may still be in flight), then every wave's; the slot about to be
-    // refilled is free
-    if constexpr (Gm::NSLOT == 3) {
-      if (pb + 64 < p1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-      else __builtin_amdgcn_s_waitcnt(0x0F70);
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // each may still be in flight: those issued so far, up to NSLOT - 2
+    // tiles ahead), then every wave's; the slot about to be refilled is free
+    {
+      const int later = (pe - pb - 1) / ts;  // this item's tiles after this one
+      const int ahead = later < Gm::NSLOT - 2 ? later : Gm::NSLOT - 2;
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F78);       // vmcnt(8)
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+      else __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
     }
     lds_barrier();
     {
-      const int ahead = pb + 64 * (Gm::NSLOT - 1);
-      if (ahead < p1) issue(ahead, ring + ((it + Gm::NSLOT - 1) % Gm::NSLOT) * Gm::SLOT);
+      const int ahead = pb + ts * (Gm::NSLOT - 1);
+      if (ahead < pe) issue(ahead, ring + ((SL + Gm::NSLOT - 1) % Gm::NSLOT) * Gm::SLOT);
     }
     // V rows outside the loaded range become zeros (their loads fetched the
     // head's row 0, and a masked weight times a NaN would still be NaN); the
     // step's own rows take their K and V as cache bytes
     {
       const int vlo = pb > lo_min ? pb : lo_min;
-      const int vhi = p1 < Lb ? p1 : Lb;
+      const int vhi = Lb;
       const int n0 = pb > Lb ? pb : Lb;
-      const int n1 = pb + 64 < p1 ? pb + 64 : p1;
+      const int n1 = pb + 64 < pe ? pb + 64 : pe;
       if (pb < vlo || pb + 64 > vhi) {
         for (int q = tid; q < 64 * CPR; q += NW * 64) {
           const int row = q / CPR, cc = q - (q / CPR) * CPR;
@@ -641,14 +717,12 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
       }
     }
 
-    if (m0 + 16 * rt >= M) continue;
+    if (dead) return;
     f32x4 sacc[NPT];
 #pragma unroll
     for (int pq = 0; pq < NPT; ++pq) {
-      const int pt = ph * NPT + pq;
-      const int row = 16 * pt + (ln & 15);
-      const v4u a0 = *reinterpret_cast<const v4u*>(slot + f8_slot(row, 2 * (ln >> 4)) * 16);
-      const v4u a1 = *reinterpret_cast<const v4u*>(slot + f8_slot(row, 2 * (ln >> 4) + 1) * 16);
+      const v4u a0 = *reinterpret_cast<const v4u*>(slot + pq * 2048 + ka0);
+      const v4u a1 = *reinterpret_cast<const v4u*>(slot + pq * 2048 + ka1);
       const v8i a = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                         (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
       sacc[pq] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -657,28 +731,28 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
         sacc[pq] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qt[k], sacc[pq], 0, 0, 0,
                                                                     127, 0, 127);
     }
-    const bool open = pb >= lo_all && pb + 63 <= hi_all && pb + 64 <= p1;
+    // a tile inside every row's window and the chunk needs no mask (the
+    // bounds are uniform: a scalar branch)
+    const bool full = pb >= lo_s && pb + 63 <= hi_s && pb + 64 <= pe;
     unsigned wh[NKS][4];
 #pragma unroll
     for (int pq = 0; pq < NPT; ++pq) {
       const int pt = ph * NPT + pq;
       float e[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        e[i] = __builtin_amdgcn_exp2f(fmaf(sacc[pq][i], qinv, -shift2));
-        if (!open) {
+      for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(sacc[pq][i], qinv, -shift2));
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
           const int pos = pb + 16 * pt + 4 * (ln >> 4) + i;
-          e[i] = (pos >= w_lo && pos <= w_hi && pos < p1) ? e[i] : 0.f;
+          e[i] = (pos >= w_lo && pos <= w_hi && pos < pe) ? e[i] : 0.f;
         }
       }
-      const unsigned h0 = cvt_pk_bf16(e[0], e[1]), h1 = cvt_pk_bf16(e[2], e[3]);
-      wh[pq >> 1][2 * (pt & 1)] = h0;
-      wh[pq >> 1][2 * (pt & 1) + 1] = h1;
-      lsum += (bf16_lo(h0) + bf16_hi(h0)) + (bf16_lo(h1) + bf16_hi(h1));
+      wh[pq >> 1][2 * (pt & 1)] = cvt_pk_bf16(e[0], e[1]);
+      wh[pq >> 1][2 * (pt & 1) + 1] = cvt_pk_bf16(e[2], e[3]);
     }
-#pragma unroll
-    for (int kq = 0; kq < NKS; ++kq) {
-      const int ks = ph * NKS + kq;
+    auto pv = [&](auto KQ) {
+      constexpr int kq = decltype(KQ)::v;
       const bf16x8 bh = as_bf16x8(v4u{wh[kq][0], wh[kq][1], wh[kq][2], wh[kq][3]});
       // V^T operand (16 dims x 32 positions, the k order of the weights:
       // slot m < 4 is position 4 g + m, slot m >= 4 position 16 + 4 g + m - 4
@@ -687,25 +761,32 @@ __device__ void attn_item_f8(const LayerArgs& L, const StepArgs& S, const AttnPl
       // its byte m, so lane q addresses slot m = q >> 1's row at dims
       // 8 (q & 1) .. + 7 of the 16-dim tile, and lane i ends up with dim i
       // of the tile at the eight positions in k order.
-      const int q = ln & 15, m = q >> 1;
-      const int vrow = 32 * ks + 4 * (ln >> 4) + (m & 3) + 16 * (m >> 2);
-      const uint8_t* vr = slot + Gm::RAW + vrow * 128 + 8 * (q & 1);
-      const int sw = (vrow >> 1) & 7;
+      v2i vt[NDT];
+      v_tr_reads<SL * Gm::SLOT + 4096 * kq>(tra, vt);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        typedef __attribute__((address_space(3))) v2i lds_v2i;
-        const v2i raw =
-            __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vr + ((dt ^ sw) << 4)));
+        const v2i raw = vt[dt];
         const bf16x8 a = as_bf16x8(v4u{e4m3x2_bf16<false>((unsigned)raw.x),
                                        e4m3x2_bf16<true>((unsigned)raw.x),
                                        e4m3x2_bf16<false>((unsigned)raw.y),
                                        e4m3x2_bf16<true>((unsigned)raw.y)});
         oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, oacc[dt], 0, 0, 0);
       }
-    }
+      sacc_l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bh, sacc_l, 0, 0, 0);
+    };
+    pv(F8Slot<0>());
+    if constexpr (NKS > 1) pv(F8Slot<1>());
+  };
+  // the ring slot of a tile is a constant of each unrolled step
+  for (int pb = pb0; pb < pe; pb += ts * Gm::NSLOT) {
+    tile(F8Slot<0>(), pb);
+    if (pb + ts < pe) tile(F8Slot<1>(), pb + ts);
+    if constexpr (Gm::NSLOT > 2)
+      if (pb + 2 * ts < pe) tile(F8Slot<2>(), pb + 2 * ts);
+    if constexpr (Gm::NSLOT > 3)
+      if (pb + 3 * ts < pe) tile(F8Slot<3>(), pb + 3 * ts);
   }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  float lsum = sacc_l[0];
   if constexpr (NPH == 2) {
     float* xs = reinterpret_cast<float*>(ring) + rt * (NDT * 4 + 1) * 64;
     lds_barrier();
