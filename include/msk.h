@@ -151,7 +151,7 @@ size_t msk_workspace_size(const msk_layer_cfg *cfg, int32_t n_layers,
  * wait in a call that used `ws` gave up (MSK_ERR_TIMEOUT; the workspace's
  * synchronisation words are then reset so the next call starts clean) or
  * MSK_OK.  MSK_ERR_DEVICE if the stream reports an error.  Without this call
- * the next call on `ws` reports such a wait the same way, after its argument
+ * a later call on `ws` reports such a wait the same way, after its argument
  * checks and before it enqueues anything (see msk_layer_step_timeline). */
 msk_status msk_workspace_status(void *ws, size_t ws_bytes, void *stream);
 
@@ -252,12 +252,18 @@ size_t msk_noalloc_scratch_bytes(void);
  *           gate/up, down (the first four layers).  Rows of workgroups that
  *           did not run stay zero.
  * Every barrier wait is bounded (msk_set_spin_limit): one that gives up sets
- * the workspace's error flag, and the next call on the workspace (any entry
- * point that takes it, or msk_workspace_status) synchronises the device
- * before it enqueues anything, resets the flag and returns MSK_ERR_TIMEOUT.
- * The library remembers the last 64 workspaces this call ran the persistent
- * kernel on; the flag of an older one is reported by msk_workspace_status
- * alone.  The outputs of a call whose wait gave up are undefined. */
+ * the workspace's error flag.  Behind the launch the library copies the flag
+ * to pinned host memory and records an event on `stream`; the first call on
+ * the workspace (any entry point that takes it) that starts after the launch
+ * has finished finds the flag without waiting, resets the workspace's
+ * synchronisation words and returns MSK_ERR_TIMEOUT before it enqueues
+ * anything.  A call made while the launch still runs cannot know yet and
+ * leaves the check to a later one; msk_workspace_status, which synchronises,
+ * always reports it.  The library tracks the last 64 workspaces this call ran
+ * the persistent kernel on; the flag of an older one is reported by
+ * msk_workspace_status alone.  The outputs of a call whose wait gave up are
+ * undefined.  The first persistent launch allocates the pinned words and
+ * each tracked workspace one event. */
 msk_status msk_layer_step_timeline(const msk_layer_cfg *cfg, const msk_layer_weights *w,
                                    const msk_kv *kv, int32_t n_layers, const msk_batch *batch,
                                    float *x, float *layer_out, int32_t *topk_idx, int32_t *win,

@@ -68,9 +68,9 @@ def test_persistent_kernel_matches_oracle(case):
 def test_a_wait_that_gives_up_is_reported_by_the_next_call():
     """The barrier waits of the persistent kernel bounded to one poll give up
     (forced from the host: every kernel still runs to its end, on whatever
-    its inputs hold).  The next call on the same workspace returns
-    MSK_ERR_TIMEOUT before it enqueues anything, and the call after that runs
-    clean and matches the oracle."""
+    its inputs hold).  The next call on the same workspace, made after the
+    launch has finished, returns MSK_ERR_TIMEOUT before it enqueues anything,
+    and the call after that runs clean and matches the oracle."""
     print("[gpu-timeline] watchdog", flush=True)
     p = synth.make_problem("tiny-fp32", device="cuda")
     fill_shift(p)

@@ -373,6 +373,11 @@ std::atomic<unsigned> g_spin_limit{msk::kSpinLimit};
 // Reads the workspace's error word once the device is idle; a set word is
 // reported as MSK_ERR_TIMEOUT and the synchronisation words are reset, so
 // the next call starts clean.
+#define MSK_TRY_HOST(x)                \
+  do {                                 \
+    const hipError_t e_ = (x);         \
+    if (e_ != hipSuccess) return e_;   \
+  } while (0)
 msk_status read_watchdog(void* ws) {
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return device_status(e, "hipDeviceSynchronize");
@@ -388,39 +393,83 @@ msk_status read_watchdog(void* ws) {
 }
 
 // Workspaces whose latest launch was the persistent step kernel, the one
-// kernel with device-side waits.  The next call on such a workspace reads its
-// error word before it enqueues anything (a device synchronisation, paid only
-// after such a launch).  At most kWatched are remembered; past that the
-// oldest is forgotten, and a trip of its launch stays in the workspace for
-// msk_workspace_status to report.
+// kernel with device-side waits.  Behind such a launch the library copies the
+// workspace's error word to pinned host memory on the launch's stream and
+// records an event.  Every later call on the workspace looks at the event
+// without waiting: once it has completed, the call reads the copied word
+// before it enqueues anything and reports a wait that gave up.  So the first
+// call that starts after the launch has finished reports its trip (a call
+// made while it still runs cannot know), and msk_workspace_status, which
+// synchronises, always does.  At most kWatched workspaces are tracked; past
+// that the oldest is dropped, and a trip of its launch stays in the workspace
+// for msk_workspace_status to report.
+struct Watch {
+  void* ws;       // nullptr: free
+  hipEvent_t ev;  // created on first use, on device `dev`
+  int dev;
+};
 constexpr int kWatched = 64;
 std::mutex g_watch_mu;
-void* g_watch[kWatched];
-int g_watch_n = 0;
+Watch g_watch[kWatched];
+int g_watch_next = 0;            // the slot a full table gives up next
+unsigned* g_flag = nullptr;      // pinned host copies of the error words [kWatched]
 
-void watch(void* ws) {
+hipError_t watch(void* ws, hipStream_t st) {
   std::lock_guard<std::mutex> g(g_watch_mu);
-  for (int i = 0; i < g_watch_n; ++i)
-    if (g_watch[i] == ws) return;
-  if (g_watch_n == kWatched) {
-    for (int i = 1; i < kWatched; ++i) g_watch[i - 1] = g_watch[i];
-    --g_watch_n;
+  if (!g_flag) {
+    MSK_TRY_HOST(hipHostMalloc(reinterpret_cast<void**>(&g_flag), kWatched * sizeof(unsigned),
+                               hipHostMallocDefault));
+    for (int i = 0; i < kWatched; ++i) g_flag[i] = 0;
   }
-  g_watch[g_watch_n++] = ws;
+  int i = -1;
+  for (int k = 0; k < kWatched && i < 0; ++k)
+    if (g_watch[k].ws == ws) i = k;
+  for (int k = 0; k < kWatched && i < 0; ++k)
+    if (g_watch[k].ws == nullptr) i = k;
+  if (i < 0) {
+    i = g_watch_next;
+    g_watch_next = (g_watch_next + 1) % kWatched;
+  }
+  int dev = 0;
+  MSK_TRY_HOST(hipGetDevice(&dev));
+  Watch& w = g_watch[i];
+  if (w.ev == nullptr || w.dev != dev) {
+    if (w.ev != nullptr) MSK_TRY_HOST(hipEventDestroy(w.ev));
+    w.ev = nullptr;
+    MSK_TRY_HOST(hipEventCreateWithFlags(&w.ev, hipEventDisableTiming));
+    w.dev = dev;
+  }
+  w.ws = ws;
+  MSK_TRY_HOST(hipMemcpyAsync(&g_flag[i], static_cast<uint8_t*>(ws) + sizeof(unsigned),
+                              sizeof(unsigned), hipMemcpyDeviceToHost, st));
+  return hipEventRecord(w.ev, st);
 }
 
-bool unwatch(void* ws) {
+// Forgets the workspace (msk_workspace_status reads its word itself).
+void unwatch(void* ws) {
   std::lock_guard<std::mutex> g(g_watch_mu);
-  for (int i = 0; i < g_watch_n; ++i)
-    if (g_watch[i] == ws) {
-      g_watch[i] = g_watch[--g_watch_n];
-      return true;
-    }
-  return false;
+  for (int k = 0; k < kWatched; ++k)
+    if (g_watch[k].ws == ws) g_watch[k].ws = nullptr;
 }
 
-// The watchdog check every call on a workspace makes after its argument checks.
-msk_status watchdog(void* ws) { return unwatch(ws) ? read_watchdog(ws) : MSK_OK; }
+// The watchdog check every call on a workspace makes after its argument
+// checks (see Watch).
+msk_status watchdog(void* ws) {
+  unsigned flag = 0;
+  {
+    std::lock_guard<std::mutex> g(g_watch_mu);
+    int i = -1;
+    for (int k = 0; k < kWatched && i < 0; ++k)
+      if (g_watch[k].ws == ws) i = k;
+    if (i < 0) return MSK_OK;
+    const hipError_t e = hipEventQuery(g_watch[i].ev);
+    if (e == hipErrorNotReady) return MSK_OK;  // still running: a later call looks again
+    if (e != hipSuccess) return device_status(e, "hipEventQuery");
+    flag = *static_cast<volatile unsigned*>(&g_flag[i]);
+    g_watch[i].ws = nullptr;
+  }
+  return flag == 0 ? MSK_OK : read_watchdog(ws);
+}
 
 // A one-token batch description for the calls that take only a token count.
 struct FlatBatch {
@@ -585,8 +634,8 @@ static msk_status layer_step_impl(const msk_layer_cfg* cfg, const msk_layer_weig
   if (noalloc) return device_status(msk::launch_step_noalloc(Ls, S, st), "layer-step launch");
   if (!stamps) return device_status(msk::launch_step_unfused(Ls, S, st), "layer-step launch");
   bool persistent = false;
-  const hipError_t e = msk::launch_step_fused(Ls, S, st, &persistent);
-  if (e == hipSuccess && persistent) watch(ws);
+  hipError_t e = msk::launch_step_fused(Ls, S, st, &persistent);
+  if (e == hipSuccess && persistent) e = watch(ws, st);
   return device_status(e, "layer-step launch");
 }
 
