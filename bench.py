@@ -189,7 +189,7 @@ def unfused_step(p, x, ws):
 KERNEL_NAMES = {"qkv": "k_qkv", "attn": "k_attn", "combine": "k_combine", "wo": "k_wo",
                 "router": "k_router", "topk": "k_topk", "gateup": "k_gateup", "down": "k_down",
                 "step": "k_step_p", "union": "k_union", "moe_sum": "k_moe_sum",
-                "prep": "k_prep_act", "dense_sum": "k_dense_sum"}
+                "prep": "k_sum_prep", "dense_sum": "k_dense_sum"}
 ONE_TOKEN_KERNELS = ("qkv", "wo", "router", "gateup", "down")
 
 
