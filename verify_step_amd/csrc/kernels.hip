@@ -24,6 +24,17 @@ constexpr size_t kMaxLds = 160 * 1024;
 __host__ __device__ constexpr size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ------------------------------------------------------------ kernels
+// Device-coherent (agent-scope) word operations for counters and barriers.
+__device__ __forceinline__ unsigned a_ld(unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void a_st(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned a_add(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int DT, int NV>
 __global__ __launch_bounds__(kBlockThreads) void k_qkv(LayerArgs L, StepArgs S, const float* x) {
   float* rs = reinterpret_cast<float*>(msk_smem);
@@ -130,20 +141,25 @@ __global__ __launch_bounds__(kBlockThreads) void k_topk(LayerArgs L, StepArgs S,
   phase_topk(L, S, topk_out, blockIdx.x, gridDim.x);
 }
 
-// Several tokens' routing in one workgroup of up to 16 waves: the router
-// logits (summed here, in slice order, from the dense product's split-K
-// partial tiles when ks > 1, and written out), each token's top-k by one
-// wave (a selection is a chain of dependent wave reductions), then the
-// expert union from the selections kept in LDS (what k_topk and k_union do,
-// in one launch).
-constexpr int kTopkUnionThreads = 1024;
-__global__ __launch_bounds__(kTopkUnionThreads) void k_topk_union(LayerArgs L, StepArgs S,
-                                                                  int* topk_out, const float* part,
-                                                                  int ks) {
+// Several tokens' routing: one wave per token sums the router logits (in
+// slice order, from the dense product's split-K partial tiles when ks > 1)
+// and writes them out, then takes the token's top-k (a selection is a chain of
+// dependent wave reductions, so the tokens go to waves of kTopkWaves-wave
+// workgroups, all at once).  The workgroup that arrives last, counted on a
+// word of the workspace, reads every token's selection and builds the expert
+// union (what k_topk and k_union do, in one launch).  The selections travel
+// between workgroups through device-coherent stores and loads, written and
+// waited for before the arrival is counted: no cache flush is needed.
+constexpr int kTopkWaves = 4;
+__global__ __launch_bounds__(kTopkWaves * 64) void k_topk_union(LayerArgs L, StepArgs S,
+                                                                int* topk_out, const float* part,
+                                                                int ks) {
   Union* U = reinterpret_cast<Union*>(msk_smem);
   int* sel = reinterpret_cast<int*>(U + 1);  // [T][K]
+  __shared__ int last;
   const int ln = lane_id();
-  for (int t = wave_id(); t < S.T; t += blockDim.x / 64) {
+  const int t = blockIdx.x * kTopkWaves + wave_id();
+  if (t < S.T) {
     // lane: experts e_i = ln + 64 i; every load is issued before any sum
     // (addresses clamped into range, results past E unused)
     float x[4];
@@ -190,14 +206,25 @@ __global__ __launch_bounds__(kTopkUnionThreads) void k_topk_union(LayerArgs L, S
       for (int k = 0; k < kMaxTopK; ++k)
         if (k < L.K) {
           const size_t o = (size_t)t * L.K + k;
-          S.idx[o] = bis[k];
+          __hip_atomic_store(&S.idx[o], bis[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           S.wts[o] = exs[k] * inv;
           if (topk_out) topk_out[o] = bis[k];
-          sel[o] = bis[k];
         }
     }
   }
-  __syncthreads();  // every token's selection is in LDS
+  // this workgroup's selections have landed before its arrival is counted
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* cnt = S.sync + kTopkCountWord;
+    last = a_add(cnt, 1u) == gridDim.x - 1;
+    if (last) a_st(cnt, 0u);  // zero again for the next launch
+  }
+  __syncthreads();
+  if (!last) return;
+  for (int i = threadIdx.x; i < S.T * L.K; i += blockDim.x)
+    sel[i] = __hip_atomic_load(&S.idx[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
   union_to_global(sel, S.T, L.K, L.E, U, S.uni);
 }
 
@@ -415,15 +442,6 @@ struct TreeSync {
   unsigned limit;  // polls before a wait gives up
 };
 
-__device__ __forceinline__ unsigned a_ld(unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void a_st(unsigned* p, unsigned v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned a_add(unsigned* p, unsigned v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 __device__ __forceinline__ TreeSync tree_begin(unsigned* w, unsigned limit) {
   // every workgroup reads the same generation: it cannot advance before all
@@ -990,9 +1008,8 @@ hipError_t launch_route(const LayerArgs& L, const StepArgs& S, const float* h, i
   }
   // the expert union comes with the selection: the multi-token expert
   // kernels read it (launch_ffn with union_ready)
-  const int waves = S.T < kTopkUnionThreads / 64 ? S.T : kTopkUnionThreads / 64;
-  return launch_b(kPhTopk, k_topk_union, 1, waves * 64, kUnionLds, st, L, S, topk_out,
-                  (const float*)S.dpart, ks);
+  return launch_b(kPhTopk, k_topk_union, (S.T + kTopkWaves - 1) / kTopkWaves, kTopkWaves * 64,
+                  kUnionLds, st, L, S, topk_out, (const float*)S.dpart, ks);
 }
 
 template <int DT>

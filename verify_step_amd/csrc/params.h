@@ -98,9 +98,12 @@ __host__ __device__ inline int dense_slices(int N, int K) {
 }
 
 // The workspace starts with kSyncBytes of words that every entry point finds
-// at the same place and that are zero between calls: the grid barrier
-// (words 0, 1 and 64..64+1024) and the router's arrival counter (word 2).
+// at the same place and that are zero between calls: the persistent kernel's
+// tree barrier (word 0 its generation, word 1 the error flag, word 32 and
+// words 64 + 32 g for g < 8 its arrival counters) and, at kTopkCountWord, the
+// arrival counter of the several-token top-k kernel.
 constexpr int kSyncBytes = 16384;
+constexpr int kTopkCountWord = 1024;
 
 constexpr int kStamps = 32;  // timeline slots per workgroup (phase ends, per layer)
 

@@ -148,70 +148,60 @@ __device__ void router_t1(const LayerArgs& L, const StepArgs& S, float* act, flo
   }
 }
 
-// Order key of logit x of expert e < 256: a larger value gives a larger
-// key (NaN counts as -inf, -0 as +0), and among equal values the lower index
-// gives the larger key (low 8 bits 255 - e).  Keys are distinct and nonzero.
-__device__ __forceinline__ unsigned long long topk_key(float x, int e) {
+// Order key of a logit: a larger value gives a larger key (NaN counts as
+// -inf, -0 as +0).  Every logit's key is nonzero; 0 marks no expert.
+__device__ __forceinline__ unsigned topk_key(float x) {
   float v = (x == x) ? x : -INFINITY;
   if (v == 0.f) v = 0.f;
   const unsigned b = __float_as_uint(v);
-  const unsigned k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((unsigned long long)k << 8) | (unsigned)(255 - e);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-__device__ __forceinline__ float topk_key_value(unsigned long long key) {
-  const unsigned k = (unsigned)(key >> 8);
+__device__ __forceinline__ float topk_key_value(unsigned k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Wave-wide maximum of a 64-bit key (DPP within rows of 16 lanes, then four
-// lane reads); every lane gets it.
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-  auto mx = [](unsigned long long a, unsigned long long b) { return a > b ? a : b; };
-  auto sh = [](unsigned long long a, unsigned lo, unsigned hi) {
-    return ((unsigned long long)hi << 32) | lo;
-  };
-  v = mx(v, sh(v, dpp_i<kDppXor1>((int)v), dpp_i<kDppXor1>((int)(v >> 32))));
-  v = mx(v, sh(v, dpp_i<kDppXor2>((int)v), dpp_i<kDppXor2>((int)(v >> 32))));
-  v = mx(v, sh(v, dpp_i<kDppRor4>((int)v), dpp_i<kDppRor4>((int)(v >> 32))));
-  v = mx(v, sh(v, dpp_i<kDppRor8>((int)v), dpp_i<kDppRor8>((int)(v >> 32))));
-  const unsigned lo = (unsigned)v, hi = (unsigned)(v >> 32);
-  unsigned long long r = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const unsigned long long t =
-        sh(0, __builtin_amdgcn_readlane(lo, 16 * q), __builtin_amdgcn_readlane(hi, 16 * q));
-    r = mx(r, t);
-  }
-  return r;
+// Wave-wide maximum of an unsigned key (DPP within rows of 16 lanes, then
+// four lane reads); every lane gets it.
+__device__ __forceinline__ unsigned wave_max_u(unsigned v) {
+  v = max(v, (unsigned)dpp_i<kDppXor1>((int)v));
+  v = max(v, (unsigned)dpp_i<kDppXor2>((int)v));
+  v = max(v, (unsigned)dpp_i<kDppRor4>((int)v));
+  v = max(v, (unsigned)dpp_i<kDppRor8>((int)v));
+  const unsigned a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const unsigned c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
 }
 
 // Top-k of one token's logits by one wave (value descending, index ascending
 // on ties) into registers (uniform over the wave): bis[k] the experts,
 // exs[k] / den their softmax weights.  Lane l holds the logits of experts
 // l + 64 i in x[i] (i < 4; entries at E or beyond are never selected; E <=
-// 256).  Each lane sorts its four keys once; a round takes the wave-wide
-// maximum of the lanes' first keys and the lane holding it moves to its next.
+// 256).  Each lane sorts its four (key, expert) pairs once; a round takes the
+// wave-wide maximum of the lanes' first keys, and the lane holding it (among
+// equal keys the one whose expert index is lowest) moves to its next.
 __device__ __forceinline__ void topk_vals(const float (&x)[4], int E, int K,
                                           int (&bis)[kMaxTopK], float (&exs)[kMaxTopK],
                                           float& den) {
-  typedef unsigned long long u64;
   const int ln = lane_id();
-  u64 k[4];
+  unsigned kv[4];
+  int ke[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = ln + 64 * i;
-    k[i] = e < E ? topk_key(x[i], e) : 0ull;
+    kv[i] = e < E ? topk_key(x[i]) : 0u;
+    ke[i] = e;
   }
-  auto cs = [](u64& a, u64& b) {  // a >= b afterwards
-    const u64 hi = a > b ? a : b, lo = a > b ? b : a;
-    a = hi;
-    b = lo;
+  auto cs = [](unsigned& ka, int& ea, unsigned& kb, int& eb) {  // (ka, ea) ranks first afterwards
+    const bool sw = kb > ka || (kb == ka && eb < ea);
+    const unsigned k0 = sw ? kb : ka, k1 = sw ? ka : kb;
+    const int e0 = sw ? eb : ea, e1 = sw ? ea : eb;
+    ka = k0; kb = k1; ea = e0; eb = e1;
   };
-  cs(k[0], k[1]);
-  cs(k[2], k[3]);
-  cs(k[0], k[2]);
-  cs(k[1], k[3]);
-  cs(k[1], k[2]);
+  cs(kv[0], ke[0], kv[1], ke[1]);
+  cs(kv[2], ke[2], kv[3], ke[3]);
+  cs(kv[0], ke[0], kv[2], ke[2]);
+  cs(kv[1], ke[1], kv[3], ke[3]);
+  cs(kv[1], ke[1], kv[2], ke[2]);
   float v0 = 0.f;
   den = 0.f;
 #pragma unroll
@@ -219,19 +209,31 @@ __device__ __forceinline__ void topk_vals(const float (&x)[4], int E, int K,
     exs[r] = 0.f;
     bis[r] = 0;
     if (r >= K) continue;
-    const u64 m = wave_max_u64(k[0]);
-    const bool win = k[0] == m;  // one lane (keys are distinct)
-    k[0] = win ? k[1] : k[0];
-    k[1] = win ? k[2] : k[1];
-    k[2] = win ? k[3] : k[2];
-    k[3] = win ? 0ull : k[3];
-    if (m == 0ull) continue;  // fewer selectable logits than k: expert 0, weight 0
+    const unsigned m = wave_max_u(kv[0]);
+    if (m == 0u) continue;  // fewer selectable logits than k: expert 0, weight 0
+    // the lane holding the maximum: the only one, or among lanes whose first
+    // keys are equal, the one whose first expert index is lowest
+    const unsigned long long tied = __ballot(kv[0] == m);
+    int wl;
+    if (__popcll(tied) == 1)
+      wl = __ffsll((long long)tied) - 1;
+    else
+      wl = wave_min_i(kv[0] == m ? ke[0] : 0x7fffffff) & 63;
+    const int ew = __builtin_amdgcn_readlane(ke[0], wl);
+    const bool win = ln == wl;
+    kv[0] = win ? kv[1] : kv[0];
+    kv[1] = win ? kv[2] : kv[1];
+    kv[2] = win ? kv[3] : kv[2];
+    kv[3] = win ? 0u : kv[3];
+    ke[0] = win ? ke[1] : ke[0];
+    ke[1] = win ? ke[2] : ke[1];
+    ke[2] = win ? ke[3] : ke[2];
     const float val = topk_key_value(m);
     if (r == 0) v0 = val;
     const float ex = __expf(val - v0);
     den += ex;
     exs[r] = ex;
-    bis[r] = 255 - (int)(m & 0xffu);
+    bis[r] = ew;
   }
 }
 
