@@ -308,3 +308,43 @@ def test_expert_ffn_with_repeated_experts_in_a_token():
                         wts.astype(np.float32).astype(np.float64), h.astype(np.float64))
     assert_close("moe delta (repeated experts)", out.double().cpu().numpy() - h, ref - h,
                  tol_for(spec), fp32_store_floor(ref))
+
+
+TIED = [3, 17, 64, 65, 100, 128, 129, 191, 192, 255]
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_router_ties_go_to_the_lower_index(T):
+    """Ten experts with identical router rows, made the largest logits of
+    every token: the selection is the eight lowest of those indices, as the
+    oracle takes it (value descending, index ascending).  The tied experts sit
+    in one lane, in neighbouring lanes and across the four experts a lane
+    holds, so every branch of the tie-break runs (one token: the top-k kernel
+    of msk_moe_route; several: the top-k and union kernel)."""
+    print(f"[gpu-parity] router ties T={T}", flush=True)
+    p = synth.make_problem("verify-bf16-128k", device="cuda",
+                           overrides=dict(dims=dict(_SMALL, n_experts=256), kv_len=[64, 64]))
+    spec, w = dict(p.specs[0]), dict(p.weights[0])
+    H, K = spec["hidden"], spec["top_k"]
+    wr = w["w_router"].clone()
+    row = wr[TIED[0]].float() * 8.0          # exact in bf16
+    for e in TIED:
+        wr[e] = row.to(wr.dtype)
+    w["w_router"] = wr
+    # tokens leaning towards the tied row, so its logit leads for each of them
+    g = w["ffn_norm"].float()
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    h = torch.randn((T, H), generator=gen, device="cuda") + 20.0 * row / row.norm() / g
+    ws = msk.new_workspace([spec], [64] * T, 1)
+    logits = torch.empty((T, spec["n_experts"]), device="cuda")
+    _, idx, wts, _ = msk.moe_route(spec, w, h, ws, logits=logits)
+    torch.cuda.synchronize()
+    msk.workspace_status(ws)
+    lg = logits.cpu().numpy()
+    # identical rows are reduced in the same order: bit-identical logits
+    assert (lg[:, TIED] == lg[:, TIED[:1]]).all()
+    r = ol.route(spec, synth.host_weights(w), h.double().cpu().numpy())
+    assert (np.asarray(r["idx"]) == TIED[:K]).all(), "the oracle's ties"
+    assert np.array_equal(idx.cpu().numpy(), np.asarray(r["idx"]))
+    np.testing.assert_allclose(wts.cpu().numpy(), 1.0 / K, rtol=1e-6)
+    check_topk_of_gpu_logits(idx.cpu().numpy(), lg, K)
