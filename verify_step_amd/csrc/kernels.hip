@@ -1,7 +1,8 @@
 // Kernels of the MoE decode/verify layer step for gfx950, and their host
-// launchers.  Each phase of the step is also a kernel of its own (the
-// unfused path); the fused path runs every phase of every layer in one
-// persistent cooperative launch with grid barriers between dependent phases.
+// launchers.  Each phase of the step is a kernel of its own, launched in
+// order on one stream; the persistent kernel k_step_p runs every phase of up
+// to four layers in one launch of resident workgroups, with tree barriers
+// between dependent phases (the timeline call).
 #include <hip/hip_ext.h>
 
 #include <mutex>

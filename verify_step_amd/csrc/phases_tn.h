@@ -16,12 +16,6 @@
 #pragma once
 #include "phases_t1.h"
 
-#ifndef MSK_TN_BF16_NB
-#define MSK_TN_BF16_NB 2
-#endif
-#ifndef MSK_TN_FP4_NB
-#define MSK_TN_FP4_NB 2
-#endif
 
 namespace msk {
 
@@ -461,6 +455,8 @@ __device__ __forceinline__ void for_expert_groups(const Union* U, int nrt, Body&
 
 // Rows per task and 16-B chunks per lane per step, as measured best on the
 // GPU: NVFP4's decode needs the registers, so it streams one chunk deep.
+// Buffers per stream (NB): two; three measured no faster for either type, nor
+// did other row and chunk counts, nor fewer NVFP4 workgroups per CU.
 template <int DT> struct TnShape;
 // Staging: GU_VB / DN_VB input vectors of GU_C / DN_C chunks per thread are
 // loaded per batch (C = 0: vector by vector with tn_stage).  Batched loads
@@ -473,11 +469,11 @@ template <> struct TnShape<kF32> {
 };
 template <> struct TnShape<kBF16> {
   enum { GU_RW = 2, GU_U = 2, DN_R = 2, DN_U = 2, GU_VB = 1, GU_C = 0, DN_VB = 1, DN_C = 0,
-         GU_NB = MSK_TN_BF16_NB, DN_NB = MSK_TN_BF16_NB };
+         GU_NB = 2, DN_NB = 2 };
 };
 template <> struct TnShape<kNVFP4> {
   enum { GU_RW = 2, GU_U = 1, DN_R = 4, DN_U = 1, GU_VB = 1, GU_C = 0, DN_VB = 3, DN_C = 1,
-         GU_NB = MSK_TN_FP4_NB, DN_NB = MSK_TN_FP4_NB };
+         GU_NB = 2, DN_NB = 2 };
 };
 
 // act[s][f] = silu(gate_e[f] . u[t]) * (up_e[f] . u[t]) for slot s = t*K + j.
