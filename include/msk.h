@@ -51,6 +51,7 @@ extern "C" {
 #define MSK_ABI_VERSION 1
 #define MSK_MAX_REQ 64       /* requests per call                          */
 #define MSK_MAX_TOKENS 64    /* T = n_req * tokens_per_req per call         */
+#define MSK_MAX_PREFILL_TOKENS 8192 /* tokens per msk_moe_prefill call        */
 #define MSK_MAX_STACK 64     /* layers per msk_layer_step call             */
 
 typedef enum {
@@ -275,6 +276,32 @@ msk_status msk_layer_step_timeline(const msk_layer_cfg *cfg, const msk_layer_wei
  * bound makes waits give up on purpose, so that the error path can be
  * exercised with every kernel still running to its end. */
 msk_status msk_set_spin_limit(uint32_t polls);
+
+/* Experts of a prefill batch: the same result as msk_expert_ffn, for up to
+ * MSK_MAX_PREFILL_TOKENS tokens.  With many tokens per expert the gate/up and
+ * down products are matrix products on the matrix cores: the slots (t, j) are
+ * grouped by expert, and each group of up to 64 of an expert's slots meets
+ * that expert's weights as a bf16 matrix product with fp32 accumulation (u and
+ * the SwiGLU activations as two bf16 terms each, exact to about 2^-17; NVFP4
+ * weights decoded exactly to bf16).  Defined by: a fused MoE kernel among the
+ * prefill optimisations
+ * (ainewsbites page, "Agentic coding benchmark and serving tradeoffs");
+ * NVFP4 experts with one scale per 16 values (brifing.si page, "Expert Weight
+ * Quantization").
+ *   u, h [T][H] in (16-byte aligned); topk_idx, topk_w [T][k] in (an index
+ *   outside [0, E) makes its slot add nothing); out [T][H] out (may equal h).
+ *   Experts bf16 or NVFP4, hidden and ffn_dim multiples of 128, else
+ *   MSK_ERR_UNSUPPORTED.  ws: msk_moe_prefill_workspace_size() bytes.
+ *   Results do not depend on the order the slots of an expert are grouped in. */
+msk_status msk_moe_prefill(const msk_layer_cfg *cfg, const msk_layer_weights *w,
+                           int32_t n_tokens, const float *u, const int32_t *topk_idx,
+                           const float *topk_w, const float *h, float *out, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* Workspace bytes of msk_moe_prefill for n_tokens tokens (grouped inputs,
+ * products and per-slot outputs: about n_tokens * k * (8 H + 12 F) bytes);
+ * 0 and msk_last_error() on invalid or unsupported arguments. */
+size_t msk_moe_prefill_workspace_size(const msk_layer_cfg *cfg, int32_t n_tokens);
 
 /* Kernel timing for measurement harnesses.  The step's kernels fall into
  * phases:

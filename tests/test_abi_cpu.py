@@ -166,3 +166,20 @@ def test_noalloc_rejects_a_step_larger_than_its_scratch():
                                           ctypes.byref(b), fake, None, None, None, None)
     assert st == 3, msk.last_error()
     assert "scratch" in msk.last_error()
+
+
+def test_prefill_validates_before_enqueue():
+    """msk_moe_prefill: sizes, token counts and expert formats are checked on
+    the host; nothing is dereferenced (all pointers fake) when they fail."""
+    L = msk.lib()
+    ok = _spec(hidden=256, ffn_dim=128, expert_dtype="bf16", dense_dtype="bf16")
+    assert L.msk_moe_prefill_workspace_size(ctypes.byref(msk.make_cfg(ok)), 100) > 0
+    for bad, n, status in [(ok, 0, 1), (ok, 8193, 1), (dict(ok, expert_dtype="f32"), 4, 2),
+                           (dict(ok, ffn_dim=96), 4, 2)]:
+        cfg = msk.make_cfg(bad)
+        assert L.msk_moe_prefill_workspace_size(ctypes.byref(cfg), n) == 0
+        fake = ctypes.c_void_p(1 << 20)
+        w = msk.LayerWeights(*([fake.value] * len(msk._WEIGHT_FIELDS)))
+        st = L.msk_moe_prefill(ctypes.byref(cfg), ctypes.byref(w), n, fake, fake, fake, fake, fake,
+                               fake, 1 << 40, None)
+        assert st == status, msk.last_error()

@@ -100,6 +100,11 @@ def lib():
                                              vp, vp, vp, vp, vp]
         L.msk_noalloc_scratch_bytes.restype = sz
         L.msk_noalloc_scratch_bytes.argtypes = []
+        L.msk_moe_prefill.restype = i32
+        L.msk_moe_prefill.argtypes = [P(LayerCfg), P(LayerWeights), i32, vp, vp, vp, vp, vp, vp,
+                                      sz, vp]
+        L.msk_moe_prefill_workspace_size.restype = sz
+        L.msk_moe_prefill_workspace_size.argtypes = [P(LayerCfg), i32]
         L.msk_set_spin_limit.restype = i32
         L.msk_set_spin_limit.argtypes = [ctypes.c_uint32]
         L.msk_timer_start.restype = i32
@@ -254,6 +259,26 @@ def layer_step_noalloc(specs, weights, kvs, kv_len, tokens_per_req, x, layer_out
 
 def noalloc_scratch_bytes():
     return lib().msk_noalloc_scratch_bytes()
+
+
+def prefill_workspace(spec, n_tokens, device="cuda"):
+    """A workspace for msk_moe_prefill of n_tokens tokens."""
+    cfg = make_cfg(spec)
+    n = lib().msk_moe_prefill_workspace_size(ctypes.byref(cfg), n_tokens)
+    if n == 0:
+        raise MskError(1, last_error())
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_prefill(spec, w, u, idx, wts, h, ws, out=None, stream=None):
+    """Experts of a prefill batch: returns out = h + MoE(u)."""
+    T, H = h.shape
+    out = torch.empty_like(h) if out is None else out
+    cfg, wt = make_cfg(spec), make_weights(w)
+    _check(lib().msk_moe_prefill(ctypes.byref(cfg), ctypes.byref(wt), T, _ptr(u), _ptr(idx),
+                                 _ptr(wts), _ptr(h), _ptr(out), _ptr(ws), ws.numel(),
+                                 _stream(stream)))
+    return out
 
 
 def set_spin_limit(polls):

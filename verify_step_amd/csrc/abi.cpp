@@ -471,6 +471,44 @@ msk_status watchdog(void* ws) {
   return flag == 0 ? MSK_OK : read_watchdog(ws);
 }
 
+// Workspace of the prefill expert FFN for n tokens (see msk::PfArgs).
+struct PfLayout {
+  size_t off, nblk, blk, perm, pe, a, gu, act, y, total;
+};
+PfLayout pf_layout(const msk_layer_cfg& c, int n) {
+  const size_t S = (size_t)n * c.top_k, E = c.n_experts, H = c.hidden, F = c.ffn_dim;
+  PfLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += up(bytes);
+    return at;
+  };
+  L.off = take((E + 1) * sizeof(int));
+  L.nblk = take(sizeof(int));
+  L.blk = take((S / 64 + E + 1) * sizeof(msk::PfBlock));
+  L.perm = take(S * sizeof(int));
+  L.pe = take(S * sizeof(int));
+  L.a = take(2 * S * H * 2);
+  L.gu = take(S * 2 * F * sizeof(float));
+  L.act = take(2 * S * F * 2);
+  L.y = take(S * H * sizeof(float));
+  L.total = o;
+  return L;
+}
+
+msk_status check_prefill(const msk_layer_cfg* cfg, const msk_layer_weights* w, int32_t n) {
+  CHECK(check_cfg(cfg, 0));
+  if (n < 1 || n > MSK_MAX_PREFILL_TOKENS)
+    return fail(MSK_ERR_INVALID_ARG, "n_tokens %d outside [1, %d]", n, MSK_MAX_PREFILL_TOKENS);
+  if (cfg->expert_dtype != MSK_BF16 && cfg->expert_dtype != MSK_NVFP4)
+    return fail(MSK_ERR_UNSUPPORTED, "prefill experts are bf16 or NVFP4");
+  if (cfg->hidden % 128 || cfg->ffn_dim % 128)
+    return fail(MSK_ERR_UNSUPPORTED, "prefill needs hidden and ffn_dim multiples of 128");
+  if (w) CHECK(check_expert_weights(cfg, w, 0));
+  return ok();
+}
+
 // A one-token batch description for the calls that take only a token count.
 struct FlatBatch {
   int32_t zero[MSK_MAX_TOKENS] = {};
@@ -656,6 +694,48 @@ msk_status msk_layer_step_noalloc(const msk_layer_cfg* cfg, const msk_layer_weig
 }
 
 size_t msk_noalloc_scratch_bytes(void) { return msk::kScratchBytes; }
+
+size_t msk_moe_prefill_workspace_size(const msk_layer_cfg* cfg, int32_t n_tokens) {
+  if (!cfg) {
+    fail(MSK_ERR_INVALID_ARG, "cfg is null");
+    return 0;
+  }
+  if (check_prefill(cfg, nullptr, n_tokens) != MSK_OK) return 0;
+  ok();
+  return pf_layout(*cfg, n_tokens).total;
+}
+
+msk_status msk_moe_prefill(const msk_layer_cfg* cfg, const msk_layer_weights* w, int32_t n_tokens,
+                           const float* u, const int32_t* topk_idx, const float* topk_w,
+                           const float* h, float* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!cfg || !w) return fail(MSK_ERR_INVALID_ARG, "cfg or w is null");
+  CHECK(check_prefill(cfg, w, n_tokens));
+  if (!u || !topk_idx || !topk_w || !h || !out)
+    return fail(MSK_ERR_INVALID_ARG, "an input or output pointer is null");
+  if (!aligned(u, 16) || !aligned(h, 16) || !aligned(out, 16))
+    return fail(MSK_ERR_INVALID_ARG, "u, h and out must be 16-byte aligned");
+  const PfLayout lay = pf_layout(*cfg, n_tokens);
+  if (!ws || ws_bytes < lay.total)
+    return fail(MSK_ERR_WORKSPACE, "workspace %zu B < required %zu B", ws_bytes, lay.total);
+  CHECK(watchdog(ws));
+  msk::LayerArgs L = make_layer(*cfg, w, nullptr, nullptr);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  msk::PfArgs P{};
+  P.T = n_tokens;
+  P.idx = topk_idx;
+  P.u = u;
+  P.off = reinterpret_cast<int*>(base + lay.off);
+  P.nblk = reinterpret_cast<int*>(base + lay.nblk);
+  P.blk = reinterpret_cast<msk::PfBlock*>(base + lay.blk);
+  P.perm = reinterpret_cast<int*>(base + lay.perm);
+  P.pe = reinterpret_cast<int*>(base + lay.pe);
+  P.a = reinterpret_cast<unsigned short*>(base + lay.a);
+  P.gu = reinterpret_cast<float*>(base + lay.gu);
+  P.act = reinterpret_cast<unsigned short*>(base + lay.act);
+  P.y = reinterpret_cast<float*>(base + lay.y);
+  return device_status(msk::launch_prefill(L, P, topk_w, h, out, static_cast<hipStream_t>(stream)),
+                       "prefill launch");
+}
 
 msk_status msk_set_spin_limit(uint32_t polls) {
   g_spin_limit.store(polls ? polls : msk::kSpinLimit, std::memory_order_relaxed);

@@ -14,6 +14,7 @@
 #include "phases_mfma.h"
 #include "phases_t1.h"
 #include "phases_tn.h"
+#include "phases_prefill.h"
 
 namespace msk {
 
@@ -806,6 +807,7 @@ static hipError_t launch_dense(const StepArgs& S, const uint8_t* w0, const uint8
   A.N = N; A.K = K; A.T = S.T;
   A.ks = dense_slices(N, K);
   A.a3 = S.a3; A.resid = resid; A.out = out; A.part = S.dpart;
+  A.tmap = nullptr; A.oscale = 1.f; A.a3_plane = 0;
   if (terms == 2) {
     switch ((S.T + 15) / 16) {
       case 1: MSK_TRY((launch_dense_t<1, 2>(A, ph, st))); break;
@@ -1102,6 +1104,71 @@ static hipError_t launch_ffn_tn(const LayerArgs& L, const StepArgs& S, const flo
                     next_norm, next_eps);
   }
   const long long n4 = (long long)S.T * L.H / 4;
+  return launch_x(kPhMoeSum, k_moe_sum, (int)((n4 + kBlockThreads - 1) / kBlockThreads), 0, st,
+                  L, S, h, out);
+}
+
+// ------------------------------------------------- prefill expert FFN
+__global__ __launch_bounds__(1024) void k_pf_route(LayerArgs L, PfArgs P) {
+  pf_route(L, P, reinterpret_cast<int*>(msk_smem));
+}
+__global__ __launch_bounds__(kBlockThreads) void k_pf_gather(LayerArgs L, PfArgs P) {
+  pf_gather(L, P);
+}
+__global__ __launch_bounds__(kBlockThreads) void k_pf_swiglu(LayerArgs L, PfArgs P) {
+  pf_swiglu(L, P);
+}
+template <bool FP4, bool GU>
+__global__ __launch_bounds__(kBlockThreads) void k_pf_dense(LayerArgs L, PfArgs P) {
+  pf_dense<FP4, GU>(L, P, msk_smem);
+}
+
+template <bool FP4>
+static hipError_t launch_pf_products(const LayerArgs& L, const PfArgs& P, hipStream_t st) {
+  const size_t lds = DenseLds<4, 2>::BYTES;
+  const long long slots = (long long)P.T * L.K;
+  auto grid_for = [&](long long n) {
+    const long long g = (n + kBlockThreads - 1) / kBlockThreads;
+    const long long cap = 8LL * cu_count();
+    return (int)(g < 1 ? 1 : (g < cap ? g : cap));
+  };
+  {
+    auto fn = k_pf_dense<FP4, true>;
+    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
+    const int grid = resident_grid(reinterpret_cast<const void*>(fn), lds);
+    MSK_TRY(launch_x(kPhGateUp, fn, grid, lds, st, L, P));
+  }
+  MSK_TRY(launch_x(kPhPrep, k_pf_swiglu, grid_for(slots * L.F / 8), 0, st, L, P));
+  {
+    auto fn = k_pf_dense<FP4, false>;
+    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
+    const int grid = resident_grid(reinterpret_cast<const void*>(fn), lds);
+    MSK_TRY(launch_x(kPhDown, fn, grid, lds, st, L, P));
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_prefill(const LayerArgs& L, const PfArgs& P, const float* wts, const float* h,
+                          float* out, hipStream_t st) {
+  const size_t rl = (3 * kMaxExperts + 1) * sizeof(int);
+  MSK_TRY(launch_b(kPhUnion, k_pf_route, 1, 1024, rl, st, L, P));
+  const long long slots = (long long)P.T * L.K;
+  {
+    const long long g = (slots * L.H / 8 + kBlockThreads - 1) / kBlockThreads;
+    const long long cap = 8LL * cu_count();
+    MSK_TRY(launch_x(kPhPrep, k_pf_gather, (int)(g < cap ? g : cap), 0, st, L, P));
+  }
+  if (L.edt == kNVFP4)
+    MSK_TRY(launch_pf_products<true>(L, P, st));
+  else
+    MSK_TRY(launch_pf_products<false>(L, P, st));
+  // out[t] = h[t] + sum_j w[t][j] y[t K + j], the decode path's weighted combine
+  StepArgs S{};
+  S.T = P.T;
+  S.idx = const_cast<int*>(P.idx);
+  S.wts = const_cast<float*>(wts);
+  S.ybuf = P.y;
+  const long long n4 = (long long)P.T * L.H / 4;
   return launch_x(kPhMoeSum, k_moe_sum, (int)((n4 + kBlockThreads - 1) / kBlockThreads), 0, st,
                   L, S, h, out);
 }

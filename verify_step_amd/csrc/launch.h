@@ -38,6 +38,10 @@ bool ffn_one_token(const LayerArgs& L, const StepArgs& S);
 // as launch_step_unfused; *persistent says which ran.
 hipError_t launch_step_fused(const LayerArgs* Ls, const StepArgs& S, hipStream_t st,
                              bool* persistent);
+// Expert FFN of a prefill batch (see phases_prefill.h): route, gather,
+// gate/up, SwiGLU, down, weighted sum, on `st`.
+hipError_t launch_prefill(const LayerArgs& L, const PfArgs& P, const float* wts, const float* h,
+                          float* out, hipStream_t st);
 // Whole step as a sequence of per-phase kernels.
 hipError_t launch_step_unfused(const LayerArgs* Ls, const StepArgs& S, hipStream_t st);
 

@@ -105,6 +105,26 @@ __host__ __device__ inline int dense_slices(int N, int K) {
 constexpr int kSyncBytes = 16384;
 constexpr int kTopkCountWord = 1024;
 
+// Buffers of the prefill expert FFN (msk_moe_prefill; see phases_prefill.h).
+struct PfBlock {
+  int e, pos0, n;  // expert, first grouped position, slots (1..64)
+};
+
+struct PfArgs {
+  int T;                 // tokens
+  const int* idx;        // [T][K] selected experts (out of range: the slot adds nothing)
+  const float* u;        // [T][H] expert input
+  int* off;              // [E + 1] first grouped position of each expert; off[E] = slots placed
+  int* nblk;             // blocks listed
+  PfBlock* blk;          // [T K / 64 + E] blocks
+  int* perm;             // [T K] slot at grouped position pos
+  int* pe;               // [T K] expert at grouped position pos
+  unsigned short* a;     // [2][T K][H] bf16 terms of the inputs by position
+  float* gu;             // [T K][2 F] gate and up products by position
+  unsigned short* act;   // [2][T K][F] bf16 terms of the activations by position
+  float* y;              // [T K][H] expert outputs by slot
+};
+
 constexpr int kStamps = 32;  // timeline slots per workgroup (phase ends, per layer)
 
 }  // namespace msk
