@@ -14,8 +14,13 @@ inputs already resident in HBM.  Prints one JSON line:
   kernels        the same figures for every phase
   cpu_baseline   the CPU oracle timed on the same workload on this host
 
+The prefill workloads (prefill-nvfp4, prefill-bf16) time msk_moe_prefill
+instead: one layer's expert FFN over 4096 tokens on the matrix cores; their
+line gives µs per call, achieved TFLOP/s of the two products (2 x slots x
+3 x hidden x FFN flops) and a roofline against the 2.5 PFLOP/s bf16 peak.
+
 With no --workload, every workload is measured and printed on a line of its
-own; the largest single-GPU workload (verify-bf16-128k: 2 x 8 draft tokens
+own; the largest single-GPU decode/verify workload (verify-bf16-128k: 2 x 8 draft tokens
 over 131072 e4m3 positions per request, bf16 experts) comes last and carries
 the CPU baseline.
 
@@ -248,8 +253,97 @@ def copy_calibration(nbytes=1 << 30, reps=3):
 
 
 HEADLINE = "verify-bf16-128k"
+# the prefill expert FFN of one layer at full width (hidden 6144, 256 experts
+# top-8, FFN 2048) over 4096 tokens: 32768 slots, about 128 per expert
+PREFILL = {"prefill-nvfp4": dict(expert="nvfp4", tokens=4096, seed=6),
+           "prefill-bf16": dict(expert="bf16", tokens=4096, seed=7)}
 ALL_WORKLOADS = ["tiny-fp32", "decode-bf16", "stack4-nvfp4", "longctx-nvfp4", "deep32-nvfp4",
-                 HEADLINE]
+                 "prefill-nvfp4", "prefill-bf16", HEADLINE]
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PREFILL_METRIC = "µs per MoE layer prefill expert FFN + achieved TFLOP/s (% of bf16 matrix peak)"
+
+
+def measure_prefill(name, args):
+    """Time msk_moe_prefill on one layer's experts: returns its JSON record.
+    Routing: each token's top-8 of 256 synthetic unit logits."""
+    cfg = PREFILL[name]
+    dev = "cuda:0"
+    p = synth.make_problem("decode-bf16", device=dev,
+                           overrides=dict(expert=cfg["expert"], kv_len=[64], windows=[128],
+                                          seed=cfg["seed"]))
+    spec, w = p.specs[0], p.weights[0]
+    T, H, F, E, K = (cfg["tokens"], spec["hidden"], spec["ffn_dim"], spec["n_experts"],
+                     spec["top_k"])
+    g = torch.Generator(device=dev).manual_seed(cfg["seed"])
+    u = torch.randn((T, H), generator=g, device=dev)
+    h = torch.randn((T, H), generator=g, device=dev)
+    logits = torch.randn((T, E), generator=g, device=dev)
+    top, idx = torch.topk(logits, K, dim=1)
+    idx = idx.to(torch.int32).contiguous()
+    wts = torch.softmax(top, dim=1).contiguous()
+    ws = msk.prefill_workspace(spec, T, device=dev)
+    out = torch.empty_like(h)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        msk.moe_prefill(spec, w, u, idx, wts, h, ws, out=out, stream=stream)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        msk.moe_prefill(spec, w, u, idx, wts, h, ws, out=out, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    # the same calls again with every kernel bracketed by dispatch-stamped events
+    msk.timer_start()
+    for _ in range(args.steps):
+        msk.moe_prefill(spec, w, u, idx, wts, h, ws, out=out, stream=stream)
+    torch.cuda.synchronize()
+    kt = {ph: msk.timer_read(ph) for ph in msk.PHASES}
+    msk.timer_start(())
+    slots = T * K
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=E)
+    gu_b, dn_b = expert_bytes(spec)
+    distinct = int((counts > 0).sum()) * (gu_b + dn_b)
+    # each group of up to 64 of an expert's slots reads the expert's rows again
+    streamed = int(((counts + 63) // 64).sum()) * (gu_b + dn_b)
+    flops = {"gateup": 2.0 * slots * 2 * F * H, "down": 2.0 * slots * H * F}
+    total_flops = sum(flops.values())
+    timed = {ph: v for ph, v in kt.items() if v[1]}
+    dom = max(("gateup", "down"), key=lambda ph: timed[ph][0])
+    avg_us = timed[dom][0] * 1e3 / timed[dom][1]
+    achieved = flops[dom] / (avg_us * 1e-6) / 1e12
+    return {
+        "metric": PREFILL_METRIC,
+        "value": round(ms * 1e3, 3),
+        "unit": "us per prefill expert FFN",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "tokens": T, "slots": slots, "hidden": H, "ffn": F,
+                   "experts": E, "top_k": K, "expert_format": spec["expert_dtype"],
+                   "distinct_experts": int((counts > 0).sum())},
+        "tflops": round(total_flops / (ms * 1e-3) / 1e12, 1),
+        "tflops_frac": round(total_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "hbm_gbs_distinct_weights": round(distinct / (ms * 1e-3) / 1e9, 1),
+        "weight_bytes_distinct": distinct,
+        "weight_bytes_streamed": streamed,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_pf_dense", "phase": dom,
+                     "flops_per_launch": flops[dom], "avg_launch_us": round(avg_us, 3),
+                     "launches": timed[dom][1]},
+        "kernels": {ph: {"avg_us": round(v[0] * 1e3 / v[1], 3), "launches": v[1]}
+                    for ph, v in timed.items()},
+        "path": "moe_prefill",
+    }
 
 
 def measure(name, args, with_cpu):
@@ -381,6 +475,9 @@ def main():
     torch.cuda.set_device(0)
     names = ALL_WORKLOADS if args.workload == "all" else [args.workload]
     for name in names:
+        if name in PREFILL:
+            print(json.dumps(measure_prefill(name, args)), flush=True)
+            continue
         # the CPU oracle is timed once, beside the headline workload
         with_cpu = not args.no_cpu_baseline and name == names[-1]
         print(json.dumps(measure(name, args, with_cpu)), flush=True)

@@ -1,8 +1,9 @@
 """GPU parity of the prefill expert FFN (msk_moe_prefill, through the C ABI)
 against the oracle's expert FFN on the same seeded inputs: many tokens, the
-slots grouped by expert into blocks of up to 64 for the matrix cores.  Same
-tolerance as the other bf16/fp4 paths: the MoE delta out - h within 2e-2 of
-its RMS (plus one fp32 ulp of out)."""
+slots grouped by expert into chunks of up to 128 for the matrix cores (inputs
+as fp16 with a power of two per row for NVFP4 experts, bf16 for bf16
+experts).  Same tolerance as the other bf16/fp4 paths: the MoE delta out - h
+within 2e-2 of its RMS (plus one fp32 ulp of out)."""
 import numpy as np
 import pytest
 import torch
@@ -16,6 +17,10 @@ pytestmark = pytest.mark.gpu
 
 _SMALL = dict(hidden=512, n_q_heads=12, n_kv_heads=2, head_dim=128, n_experts=32, top_k=8,
               ffn_dim=256)
+# five k-tiles of the gate/up product and three of the down product (an odd
+# count ends the two-tile pipeline early); the down product's last 256-row
+# block has 128 rows, so two of its four waves hold no rows
+_ODD = dict(_SMALL, hidden=640, ffn_dim=384)
 
 
 def _layer(expert, dims):
@@ -53,19 +58,25 @@ def _check(name, out, h, ref, rows=None):
     assert_close(f"{name} moe delta", got - h0, ref - h0, LOWP_TOL, fp32_store_floor(ref))
 
 
+# slots per expert: random 300 -> about 75 (chunks of 5 to 8 16-slot tiles),
+# 200 -> 50 (4 tiles), 100 -> 25 (2), 1 -> 1; skewed 300 -> 300 for each of 8
+# experts (three chunks of 100); repeats 70 -> 210, 210, 140 (two chunks each)
 CASES = [
-    ("bf16", "random", 300),
-    ("nvfp4", "random", 300),
-    ("nvfp4", "skewed", 300),
-    ("bf16", "repeats", 70),
-    ("nvfp4", "random", 1),
+    ("bf16", "random", 300, "small"),
+    ("nvfp4", "random", 300, "small"),
+    ("nvfp4", "skewed", 300, "small"),
+    ("bf16", "repeats", 70, "small"),
+    ("nvfp4", "random", 1, "small"),
+    ("nvfp4", "random", 200, "odd"),
+    ("bf16", "random", 100, "odd"),
+    ("bf16", "skewed", 40, "odd"),
 ]
 
 
-@pytest.mark.parametrize("expert,routing,T", CASES)
-def test_prefill_matches_oracle(expert, routing, T):
-    print(f"[gpu-prefill] {expert} {routing} T={T}", flush=True)
-    spec, w = _layer(expert, _SMALL)
+@pytest.mark.parametrize("expert,routing,T,dims", CASES)
+def test_prefill_matches_oracle(expert, routing, T, dims):
+    print(f"[gpu-prefill] {expert} {routing} T={T} {dims}", flush=True)
+    spec, w = _layer(expert, _SMALL if dims == "small" else _ODD)
     u, h, idx, wts = _inputs(spec, T, 11, routing)
     ws = msk.prefill_workspace(spec, T)
     out = msk.moe_prefill(spec, w, u, idx, wts, h, ws)

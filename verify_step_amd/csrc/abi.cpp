@@ -473,7 +473,7 @@ msk_status watchdog(void* ws) {
 
 // Workspace of the prefill expert FFN for n tokens (see msk::PfArgs).
 struct PfLayout {
-  size_t off, nblk, blk, perm, pe, a, gu, act, y, total;
+  size_t off, nchunk, chunk, perm, pos, pe, ue, ae, a, gu, act, y, total;
 };
 PfLayout pf_layout(const msk_layer_cfg& c, int n) {
   const size_t S = (size_t)n * c.top_k, E = c.n_experts, H = c.hidden, F = c.ffn_dim;
@@ -485,11 +485,14 @@ PfLayout pf_layout(const msk_layer_cfg& c, int n) {
     return at;
   };
   L.off = take((E + 1) * sizeof(int));
-  L.nblk = take(sizeof(int));
-  L.blk = take((S / 64 + E + 1) * sizeof(msk::PfBlock));
+  L.nchunk = take(sizeof(int));
+  L.chunk = take((S / msk::kPfChunk + E + 1) * sizeof(msk::PfChunk));
   L.perm = take(S * sizeof(int));
+  L.pos = take(S * sizeof(int));
   L.pe = take(S * sizeof(int));
-  L.a = take(2 * S * H * 2);
+  L.ue = take(S * sizeof(int));
+  L.ae = take(S * sizeof(int));
+  L.a = take(2 * S * H * 2);    // fp16, or two bf16 term planes
   L.gu = take(S * 2 * F * sizeof(float));
   L.act = take(2 * S * F * 2);
   L.y = take(S * H * sizeof(float));
@@ -725,10 +728,13 @@ msk_status msk_moe_prefill(const msk_layer_cfg* cfg, const msk_layer_weights* w,
   P.idx = topk_idx;
   P.u = u;
   P.off = reinterpret_cast<int*>(base + lay.off);
-  P.nblk = reinterpret_cast<int*>(base + lay.nblk);
-  P.blk = reinterpret_cast<msk::PfBlock*>(base + lay.blk);
+  P.nchunk = reinterpret_cast<int*>(base + lay.nchunk);
+  P.chunk = reinterpret_cast<msk::PfChunk*>(base + lay.chunk);
   P.perm = reinterpret_cast<int*>(base + lay.perm);
+  P.pos = reinterpret_cast<int*>(base + lay.pos);
   P.pe = reinterpret_cast<int*>(base + lay.pe);
+  P.ue = reinterpret_cast<int*>(base + lay.ue);
+  P.ae = reinterpret_cast<int*>(base + lay.ae);
   P.a = reinterpret_cast<unsigned short*>(base + lay.a);
   P.gu = reinterpret_cast<float*>(base + lay.gu);
   P.act = reinterpret_cast<unsigned short*>(base + lay.act);

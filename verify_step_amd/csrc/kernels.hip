@@ -807,7 +807,6 @@ static hipError_t launch_dense(const StepArgs& S, const uint8_t* w0, const uint8
   A.N = N; A.K = K; A.T = S.T;
   A.ks = dense_slices(N, K);
   A.a3 = S.a3; A.resid = resid; A.out = out; A.part = S.dpart;
-  A.tmap = nullptr; A.oscale = 1.f; A.a3_plane = 0;
   if (terms == 2) {
     switch ((S.T + 15) / 16) {
       case 1: MSK_TRY((launch_dense_t<1, 2>(A, ph, st))); break;
@@ -1112,56 +1111,44 @@ static hipError_t launch_ffn_tn(const LayerArgs& L, const StepArgs& S, const flo
 __global__ __launch_bounds__(1024) void k_pf_route(LayerArgs L, PfArgs P) {
   pf_route(L, P, reinterpret_cast<int*>(msk_smem));
 }
+template <bool FP4>
 __global__ __launch_bounds__(kBlockThreads) void k_pf_gather(LayerArgs L, PfArgs P) {
-  pf_gather(L, P);
+  pf_gather<FP4>(L, P);
 }
+template <bool FP4>
 __global__ __launch_bounds__(kBlockThreads) void k_pf_swiglu(LayerArgs L, PfArgs P) {
-  pf_swiglu(L, P);
+  pf_swiglu<FP4>(L, P);
 }
 template <bool FP4, bool GU>
-__global__ __launch_bounds__(kBlockThreads) void k_pf_dense(LayerArgs L, PfArgs P) {
-  pf_dense<FP4, GU>(L, P, msk_smem);
+__global__ __launch_bounds__(kBlockThreads) void k_pf_gemm(LayerArgs L, PfArgs P) {
+  pf_gemm<FP4, GU>(L, P, msk_smem);
 }
 
 template <bool FP4>
-static hipError_t launch_pf_products(const LayerArgs& L, const PfArgs& P, hipStream_t st) {
-  const size_t lds = DenseLds<4, 2>::BYTES;
-  const long long slots = (long long)P.T * L.K;
-  auto grid_for = [&](long long n) {
-    const long long g = (n + kBlockThreads - 1) / kBlockThreads;
-    const long long cap = 8LL * cu_count();
-    return (int)(g < 1 ? 1 : (g < cap ? g : cap));
+static hipError_t launch_pf(const LayerArgs& L, const PfArgs& P, hipStream_t st) {
+  const int slots = P.T * L.K;
+  // one wave per token, then per grouped position
+  MSK_TRY(launch_x(kPhPrep, k_pf_gather<FP4>, (P.T + kWaves - 1) / kWaves, 0, st, L, P));
+  auto gemm = [&](auto fn, int ph) -> hipError_t {
+    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), kPfLds));
+    // a multiple of 8 workgroups: the items are split by XCD
+    int grid = resident_grid(reinterpret_cast<const void*>(fn), kPfLds) & ~7;
+    if (grid < 8) grid = 8;
+    return launch_x(ph, fn, grid, kPfLds, st, L, P);
   };
-  {
-    auto fn = k_pf_dense<FP4, true>;
-    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
-    const int grid = resident_grid(reinterpret_cast<const void*>(fn), lds);
-    MSK_TRY(launch_x(kPhGateUp, fn, grid, lds, st, L, P));
-  }
-  MSK_TRY(launch_x(kPhPrep, k_pf_swiglu, grid_for(slots * L.F / 8), 0, st, L, P));
-  {
-    auto fn = k_pf_dense<FP4, false>;
-    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
-    const int grid = resident_grid(reinterpret_cast<const void*>(fn), lds);
-    MSK_TRY(launch_x(kPhDown, fn, grid, lds, st, L, P));
-  }
-  return hipSuccess;
+  MSK_TRY(gemm(k_pf_gemm<FP4, true>, kPhGateUp));
+  MSK_TRY(launch_x(kPhPrep, k_pf_swiglu<FP4>, (slots + kWaves - 1) / kWaves, 0, st, L, P));
+  return gemm(k_pf_gemm<FP4, false>, kPhDown);
 }
 
 hipError_t launch_prefill(const LayerArgs& L, const PfArgs& P, const float* wts, const float* h,
                           float* out, hipStream_t st) {
   const size_t rl = (3 * kMaxExperts + 1) * sizeof(int);
   MSK_TRY(launch_b(kPhUnion, k_pf_route, 1, 1024, rl, st, L, P));
-  const long long slots = (long long)P.T * L.K;
-  {
-    const long long g = (slots * L.H / 8 + kBlockThreads - 1) / kBlockThreads;
-    const long long cap = 8LL * cu_count();
-    MSK_TRY(launch_x(kPhPrep, k_pf_gather, (int)(g < cap ? g : cap), 0, st, L, P));
-  }
   if (L.edt == kNVFP4)
-    MSK_TRY(launch_pf_products<true>(L, P, st));
+    MSK_TRY(launch_pf<true>(L, P, st));
   else
-    MSK_TRY(launch_pf_products<false>(L, P, st));
+    MSK_TRY(launch_pf<false>(L, P, st));
   // out[t] = h[t] + sum_j w[t][j] y[t K + j], the decode path's weighted combine
   StepArgs S{};
   S.T = P.T;

@@ -106,8 +106,10 @@ constexpr int kSyncBytes = 16384;
 constexpr int kTopkCountWord = 1024;
 
 // Buffers of the prefill expert FFN (msk_moe_prefill; see phases_prefill.h).
-struct PfBlock {
-  int e, pos0, n;  // expert, first grouped position, slots (1..64)
+constexpr int kPfChunk = 128;  // most slots of one expert in one matrix-product item
+
+struct PfChunk {
+  int e, pos0, n;  // expert, first grouped position, slots (1..kPfChunk)
 };
 
 struct PfArgs {
@@ -115,13 +117,17 @@ struct PfArgs {
   const int* idx;        // [T][K] selected experts (out of range: the slot adds nothing)
   const float* u;        // [T][H] expert input
   int* off;              // [E + 1] first grouped position of each expert; off[E] = slots placed
-  int* nblk;             // blocks listed
-  PfBlock* blk;          // [T K / 64 + E] blocks
+  int* nchunk;           // chunks listed
+  PfChunk* chunk;        // [T K / kPfChunk + E] chunks, by expert
   int* perm;             // [T K] slot at grouped position pos
+  int* pos;              // [T K] grouped position of slot s (-1: not placed)
   int* pe;               // [T K] expert at grouped position pos
-  unsigned short* a;     // [2][T K][H] bf16 terms of the inputs by position
+  int* ue;               // [T K] input row pos holds u * 2^-ue[pos]
+  int* ae;               // [T K] activation row pos holds act * 2^-ae[pos]
+  unsigned short* a;     // [T K][H] inputs by position: fp16 (NVFP4 experts), or
+                         // [2][T K][H] two bf16 terms (bf16 experts)
   float* gu;             // [T K][2 F] gate and up products by position
-  unsigned short* act;   // [2][T K][F] bf16 terms of the activations by position
+  unsigned short* act;   // [T K][F] activations by position, as a
   float* y;              // [T K][H] expert outputs by slot
 };
 

@@ -33,11 +33,6 @@ struct DenseArgs {
   const float* resid;    // [T][N] or null
   float* out;            // [T][N]
   float* part;           // [n_rb][ks][T][64] partial tiles (ks > 1)
-  const int* tmap;       // ks == 1: output row of token t is tmap[t] (null: t)
-  float oscale;          // ks == 1: outputs are resid + oscale * W a
-  const uint8_t* s[3];   // NVFP4 weights (dense_item_fp4): e4m3 block scales of
-                         // each segment, [rows][K / 16]; w then holds the codes
-  size_t a3_plane;       // elements between the input term planes (0: T * K)
 };
 
 // a3[p][t][k] for eight consecutive k of one token from fp32 values.
@@ -199,17 +194,16 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// One work item of the product: output rows rb * 64 .. + 63 over K slice sl
-// (ks == 1: the whole of K, written to out; otherwise the slice's partial
-// tile).  Ends with the workgroup's LDS free for the next item.
 template <int CT, int NT>
-__device__ void dense_item(const DenseArgs& A, int item, uint8_t* lds) {
+__device__ void dense_mfma(const DenseArgs& A, uint8_t* lds) {
   using G = DenseLds<CT, NT>;
   const int ln = lane_id(), wv = wave_id();
   const int r = ln & 15, g = ln >> 4;
+  const int n_rb = (A.N + 63) / 64;
   const int tiles = A.K / kDenseKT;
-  const size_t plane = A.a3_plane ? A.a3_plane : (size_t)A.T * A.K;
-  {
+  const size_t plane = (size_t)A.T * A.K;
+  const int n_items = n_rb * A.ks;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int rb = item / A.ks, sl = item - (item / A.ks) * A.ks;
     const int t0 = (int)((long long)tiles * sl / A.ks);
     const int t1 = (int)((long long)tiles * (sl + 1) / A.ks);
@@ -293,8 +287,8 @@ __device__ void dense_item(const DenseArgs& A, int item, uint8_t* lds) {
           for (int i = 0; i < 4; ++i) {
             const int row = r0 + 4 * g + i;
             if (A.ks == 1) {
-              const size_t o = (size_t)(A.tmap ? A.tmap[t] : t) * A.N + row;
-              A.out[o] = (A.resid ? A.resid[o] : 0.f) + A.oscale * acc[ct][i];
+              const size_t o = (size_t)t * A.N + row;
+              A.out[o] = (A.resid ? A.resid[o] : 0.f) + acc[ct][i];
             } else {
               dst[t * 64 + 16 * wv + 4 * g + i] = acc[ct][i];
             }
@@ -303,144 +297,6 @@ __device__ void dense_item(const DenseArgs& A, int item, uint8_t* lds) {
       }
     }
   }
-}
-
-// dense_item with NVFP4 weights (ks == 1, NT bf16 terms of the inputs):
-// each k-tile of a wave's 16 rows (16 x 64 B of e2m1 codes, 16 x 8 scale
-// bytes) is loaded into registers one tile ahead, decoded exactly to bf16
-// (an e2m1 value times its e4m3 scale has at most six significant bits) and
-// written into the same swizzled LDS tile the bf16 rows arrive in, so the
-// matrix-core loop is dense_item's.  The token tiles still arrive by direct
-// global->LDS loads.
-template <int CT, int NT>
-__device__ void dense_item_fp4(const DenseArgs& A, int item, uint8_t* lds) {
-  using G = DenseLds<CT, NT>;
-  const int ln = lane_id(), wv = wave_id();
-  const int r = ln & 15, g = ln >> 4;
-  const int tiles = A.K / kDenseKT;
-  const int rb = item;
-  const int r0 = rb * 64 + 16 * wv;    // this wave's first row
-  const bool active = r0 < A.N;
-  const size_t cb = (size_t)A.K / 2, sb = (size_t)A.K / 16;  // code and scale bytes per row
-  const uint8_t* wr[4];
-  const uint8_t* sr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = active ? r0 + 4 * i + g : 0;
-    const int sg = row >= A.seg[2] && A.seg[2] > 0 ? 2 : (row >= A.seg[1] && A.seg[1] > 0 ? 1 : 0);
-    const size_t lr = (size_t)(row - (sg ? A.seg[sg] : 0));
-    wr[i] = A.w[sg] + lr * cb;
-    sr[i] = A.s[sg] + lr * sb;
-  }
-  // lane (g, r) fills slot r of local row 4 i + g with piece p = r ^ (4 i + g):
-  // columns 8 p .. 8 p + 7 of the k-tile, codes at byte 4 p, scale byte p / 2
-  unsigned cw[4], sw[4];
-  auto load = [&](int tau) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = r ^ (4 * i + g);
-      cw[i] = *reinterpret_cast<const unsigned*>(wr[i] + (size_t)tau * 64 + 4 * p);
-      sw[i] = *reinterpret_cast<const unsigned*>(sr[i] + (((size_t)tau * 8 + (p >> 1)) & ~(size_t)3));
-    }
-  };
-  auto store = [&](int tau, int buf) {
-    uint8_t* at = lds + G::A0 + (buf * kWaves + wv) * kDenseATile;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = r ^ (4 * i + g);
-      const int byte = (tau * 8 + (p >> 1)) & 3;
-      const float sc = __builtin_amdgcn_cvt_f32_fp8((int)(sw[i] >> (8 * byte)), 0);
-      const unsigned c = cw[i];
-      unsigned q[4];
-#define MSK_FP4_PAIR(SEL)                                                                   \
-  {                                                                                          \
-    const unsigned pr = __builtin_bit_cast(unsigned,                                         \
-                                           __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, SEL)); \
-    q[SEL] = cvt_pk_bf16(bf16_lo(pr) * sc, bf16_hi(pr) * sc);                               \
-  }
-      MSK_FP4_PAIR(0) MSK_FP4_PAIR(1) MSK_FP4_PAIR(2) MSK_FP4_PAIR(3)
-#undef MSK_FP4_PAIR
-      *reinterpret_cast<v4u*>(at + i * 1024 + ln * 16) = v4u{q[0], q[1], q[2], q[3]};
-    }
-  };
-  const size_t plane = A.a3_plane ? A.a3_plane : (size_t)A.T * A.K;
-  auto issue_b = [&](int tau, int buf) {
-    uint8_t* bt = lds + G::B0 + buf * G::BT;
-#pragma unroll
-    for (int k = 0; k < NT * CT; ++k) {
-      const int i = wv + kWaves * k;       // instruction of the 4 NT CT in the B tile
-      const int brow = 4 * i + g;          // plane-major row: p3 * 16 CT + t
-      const int p3 = brow / (16 * CT), t = brow - p3 * 16 * CT;
-      const int tt = t < A.T ? t : 0;
-      const int p = r ^ (t & 15);
-      __builtin_amdgcn_global_load_lds(
-          A.a3 + p3 * plane + (size_t)tt * A.K + (size_t)tau * kDenseKT + p * 8, bt + i * 1024,
-          16, 0, 0);
-    }
-  };
-  f32x4 acc[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (tiles > 0) {
-    load(0);
-    issue_b(0, 0);
-    wait_vm<0>();
-    if (active) store(0, 0);
-  }
-  for (int tau = 0; tau < tiles; ++tau) {
-    const int buf = tau & 1;
-    if (tau + 1 < tiles) {
-      load(tau + 1);
-      issue_b(tau + 1, buf ^ 1);
-      wait_vm<8 + NT * CT>();  // this tile's token loads (older) have landed
-    } else {
-      wait_vm<0>();
-    }
-    lds_barrier();
-    if (active) {
-      const uint8_t* at = lds + G::A0 + (buf * kWaves + wv) * kDenseATile;
-      const uint8_t* bt = lds + G::B0 + buf * G::BT;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int slot = (4 * q + g) ^ r;
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const v4u*>(at + r * 256 + slot * 16));
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int p3 = 0; p3 < NT; ++p3) {
-            const bf16x8 bb = as_bf16x8(*reinterpret_cast<const v4u*>(
-                bt + (p3 * 16 * CT + 16 * ct + r) * 256 + slot * 16));
-            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, acc[ct], 0, 0, 0);
-          }
-      }
-    }
-    if (tau + 1 < tiles) {
-      wait_vm<NT * CT>();  // the next tile's codes and scales (older than its token loads)
-      if (active) store(tau + 1, buf ^ 1);
-    }
-    lds_barrier();  // the buffers are refilled on the next tile
-  }
-  // lane: token 16 ct + r, rows r0 + 4 g + i
-  if (active) {
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int t = 16 * ct + r;
-      if (t < A.T) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = r0 + 4 * g + i;
-          const size_t o = (size_t)(A.tmap ? A.tmap[t] : t) * A.N + row;
-          A.out[o] = (A.resid ? A.resid[o] : 0.f) + A.oscale * acc[ct][i];
-        }
-      }
-    }
-  }
-}
-
-template <int CT, int NT>
-__device__ void dense_mfma(const DenseArgs& A, uint8_t* lds) {
-  const int n_items = ((A.N + 63) / 64) * A.ks;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) dense_item<CT, NT>(A, item, lds);
 }
 
 // out[t][r] = resid[t][r] + sum over slices s (ascending) of the partial

@@ -6,31 +6,58 @@
 // on the matrix cores: the fused MoE kernel the ainewsbites page lists among
 // the prefill optimisations ("Agentic coding benchmark and serving
 // tradeoffs"), over NVFP4 or bf16 experts (brifing.si page, "Expert Weight
-// Quantization").  The slots (token t,
-// choice j) are grouped by expert; each expert's slots form blocks of up to
-// 64, and a block times 64 weight rows is one work item of the dense
-// matrix-core loop (dense_item / dense_item_fp4):
+// Quantization").  The slots (token t, choice j) are grouped by expert and
+// each expert's slots split into chunks of at most kPfChunk:
 //   route    count the slots per expert, place them grouped by expert (the
-//            order within an expert does not change any result), list blocks;
-//   gather   each position's token input u as two bf16 terms (hi, then the
-//            rest, together exact to about 2^-17 of u);
+//            order within an expert does not change any result), list chunks;
+//   gather   each position's input row u[t], in the matrix-product format;
 //   gate/up  gu[pos] = [W_g; W_u]_e u  (fp32), e the position's expert;
-//   swiglu   act[pos] = silu(g_g gu_gate) * (g_u gu_up) as two bf16 terms
+//   swiglu   act[pos] = silu(g_g gu_gate) * (g_u gu_up), in the same format
 //            (g: NVFP4 matrix scales, else 1);
 //   down     y[slot] = g_d W_d,e act[pos];
 //   sum      out[t] = h[t] + sum_j w[t][j] y[t k + j], j ascending (the
 //            decode path's weighted combine, k_moe_sum).
+//
+// Number formats.  An e2m1 code times its e4m3 block scale has at most six
+// significant bits and lies in [2^-10, 2688], so NVFP4 weights are exact in
+// fp16; their products run as v_mfma_f32_16x16x32_f16 with fp16 inputs, each
+// input row multiplied by a power of two that puts its largest magnitude in
+// [2^14, 2^15) (11 significant bits per input, no overflow; the power is
+// undone on the fp32 result).  bf16 weights are not exact in fp16, so those
+// products run as v_mfma_f32_16x16x32_bf16 with each input as two bf16 terms
+// (hi = rne(x), lo = rne(x - hi): about 2^-17 relative left out).  The pages
+// run the experts in FP8; both formats keep far more of each input.  Sums are
+// fp32.
+//
+// Matrix product item: (chunk of up to 128 slots of expert e, 256 output
+// rows); each of the four waves owns 64 rows x all the chunk's slots
+// (4 x 8 accumulator tiles of 16 x 16).  Per k-tile (128 columns for NVFP4,
+// 64 for bf16, so that either tile of inputs is 32 KB):
+//   - the chunk's input rows arrive in LDS by direct global->LDS loads, three
+//     tiles in the ring (two in flight while one is used), each row's 16-B
+//     pieces stored at piece ^ (row & 15) (bf16: row & 7) so an operand read
+//     (16 rows, one piece each) meets no bank conflict; every wave reads all
+//     of them;
+//   - each wave's weight rows go straight to registers two tiles ahead (they
+//     are used by that wave alone): a lane holds KT / 4 consecutive columns
+//     of one row, which serve every k-step of the tile.  The k index of step
+//     j, lane group g is numbered (KT / 4) g + 8 j + (0..7) on both operands,
+//     which keeps every lane's weight load one contiguous run of bytes.
+// The weights are streamed once per chunk (once per expert when it has at
+// most 128 slots); the items of one chunk are consecutive and an XCD runs a
+// contiguous range of items, so the chunk's inputs and the weights shared by
+// an expert's chunks are re-read from that XCD's L2.
 #pragma once
 #include "phases_dense.h"
 
 namespace msk {
 
-// One workgroup: counts per expert (LDS atomics), offsets, placement, blocks.
+// One workgroup: counts per expert (LDS atomics), offsets, chunks, placement.
 // lds: 3 * kMaxExperts + 1 ints.
 __device__ inline void pf_route(const LayerArgs& L, const PfArgs& P, int* lds) {
   int* cnt = lds;
   int* cur = lds + kMaxExperts;
-  int* bo = lds + 2 * kMaxExperts;  // [E + 1] first block of each expert
+  int* co = lds + 2 * kMaxExperts;  // [E + 1] first chunk of each expert
   const int S = P.T * L.K;
   for (int e = threadIdx.x; e < L.E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
@@ -40,137 +67,409 @@ __device__ inline void pf_route(const LayerArgs& L, const PfArgs& P, int* lds) {
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int o = 0, b = 0;
+    int o = 0, c = 0;
     for (int e = 0; e < L.E; ++e) {
       cur[e] = o;
-      bo[e] = b;
+      co[e] = c;
       P.off[e] = o;
       o += cnt[e];
-      b += (cnt[e] + 63) / 64;
+      c += (cnt[e] + kPfChunk - 1) / kPfChunk;
     }
-    bo[L.E] = b;
+    co[L.E] = c;
     P.off[L.E] = o;
-    *P.nblk = b;
+    *P.nchunk = c;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < L.E; e += blockDim.x)
-    for (int b = 0; 64 * b < cnt[e]; ++b) {
-      const int n = cnt[e] - 64 * b;
-      P.blk[bo[e] + b] = PfBlock{e, cur[e] + 64 * b, n < 64 ? n : 64};
+  // an expert's slots in nc near-equal chunks
+  for (int e = threadIdx.x; e < L.E; e += blockDim.x) {
+    const int n = cnt[e], nc = (n + kPfChunk - 1) / kPfChunk;
+    for (int c = 0; c < nc; ++c) {
+      const int lo = n * c / nc, hi = n * (c + 1) / nc;
+      P.chunk[co[e] + c] = PfChunk{e, cur[e] + lo, hi - lo};
     }
+  }
   __syncthreads();
   for (int s = threadIdx.x; s < S; s += blockDim.x) {
     const int e = P.idx[s];
-    if (e < 0 || e >= L.E) continue;
+    if (e < 0 || e >= L.E) {
+      P.pos[s] = -1;
+      continue;
+    }
     const int p = atomicAdd(&cur[e], 1);
     P.perm[p] = s;
     P.pe[p] = e;
+    P.pos[s] = p;
   }
 }
 
-// Eight fp32 values as two bf16 terms: hi = bf16(x), lo = bf16(x - hi), at
-// element off of the two planes that are `plane` elements apart.
-__device__ __forceinline__ void store_split2(unsigned short* dst, size_t plane, size_t off,
-                                             const float (&v)[8]) {
+// Power of two s such that m * 2^-s lies in [2^14, 2^15) (0 when m is zero
+// or not finite).
+__device__ __forceinline__ int pf_shift(float m) {
+  if (!(m > 0.f) || !isfinite(m)) return 0;
+  int x;
+  frexpf(m, &x);  // m = f 2^x, f in [0.5, 1)
+  return x - 15;
+}
+
+// Eight values stored at element off of the input planes (plane elements
+// apart): fp16 of v * 2^-sh (FP4), or the two bf16 terms of v.
+template <bool FP4>
+__device__ __forceinline__ void pf_store8(unsigned short* dst, size_t plane, size_t off,
+                                          const float (&v)[8], int sh) {
   unsigned hi[4], lo[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    hi[i] = cvt_pk_bf16(v[2 * i], v[2 * i + 1]);
-    lo[i] = cvt_pk_bf16(v[2 * i] - bf16_lo(hi[i]), v[2 * i + 1] - bf16_hi(hi[i]));
+    if constexpr (FP4) {
+      hi[i] = cvt_pk_f16(ldexpf(v[2 * i], -sh), ldexpf(v[2 * i + 1], -sh));
+    } else {
+      hi[i] = cvt_pk_bf16(v[2 * i], v[2 * i + 1]);
+      lo[i] = cvt_pk_bf16(v[2 * i] - bf16_lo(hi[i]), v[2 * i + 1] - bf16_hi(hi[i]));
+    }
   }
   *reinterpret_cast<v4u*>(dst + off) = v4u{hi[0], hi[1], hi[2], hi[3]};
-  *reinterpret_cast<v4u*>(dst + plane + off) = v4u{lo[0], lo[1], lo[2], lo[3]};
+  if constexpr (!FP4) *reinterpret_cast<v4u*>(dst + plane + off) = v4u{lo[0], lo[1], lo[2], lo[3]};
 }
 
-// a[pos] = u[token of pos] as two bf16 terms, eight inputs per thread and step.
+// One wave per token t: its input row u[t] in the product format, written to
+// the grouped position of each of its placed slots, with its power of two.
+template <bool FP4>
 __device__ inline void pf_gather(const LayerArgs& L, const PfArgs& P) {
-  const int n = P.off[L.E];
-  const int per = L.H / 8;
-  const size_t plane = (size_t)P.T * L.K * L.H;
-  const long long total = (long long)n * per;
-  for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < total;
-       q += (long long)gridDim.x * blockDim.x) {
-    const int pos = (int)(q / per), c = (int)(q - (long long)pos * per) * 8;
-    const int t = P.perm[pos] / L.K;
-    const float* src = P.u + (size_t)t * L.H + c;
-    const v4f x0 = *reinterpret_cast<const v4f*>(src);
-    const v4f x1 = *reinterpret_cast<const v4f*>(src + 4);
+  const int t = blockIdx.x * kWaves + wave_id();
+  if (t >= P.T) return;
+  const int ln = lane_id();
+  const float* src = P.u + (size_t)t * L.H;
+  int sh = 0;
+  if constexpr (FP4) {
+    float m = 0.f;
+    for (int c = 8 * ln; c < L.H; c += 512) {
+      const v4f x0 = *reinterpret_cast<const v4f*>(src + c);
+      const v4f x1 = *reinterpret_cast<const v4f*>(src + c + 4);
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(x0.x), fabsf(x0.y)), fmaxf(fabsf(x0.z), fabsf(x0.w))));
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(x1.x), fabsf(x1.y)), fmaxf(fabsf(x1.z), fabsf(x1.w))));
+    }
+    sh = pf_shift(wave_max(m));
+  }
+  if (ln < L.K) {
+    const int p = P.pos[t * L.K + ln];
+    if (p >= 0) P.ue[p] = sh;
+  }
+  for (int c = 8 * ln; c < L.H; c += 512) {
+    const v4f x0 = *reinterpret_cast<const v4f*>(src + c);
+    const v4f x1 = *reinterpret_cast<const v4f*>(src + c + 4);
     const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    store_split2(P.a, plane, (size_t)pos * L.H + c, v);
+    for (int j = 0; j < L.K; ++j) {
+      const int p = P.pos[t * L.K + j];
+      if (p >= 0) pf_store8<FP4>(P.a, (size_t)P.T * L.K * L.H, (size_t)p * L.H + c, v, sh);
+    }
   }
 }
 
-// act[pos][f] = silu(g_g gu[pos][f]) * (g_u gu[pos][F + f]) as two bf16 terms.
+// One wave per grouped position: act = silu(g_g gate) * (g_u up) in the
+// product format, with its power of two.
+template <bool FP4>
 __device__ inline void pf_swiglu(const LayerArgs& L, const PfArgs& P) {
-  const int n = P.off[L.E];
-  const int per = L.F / 8;
-  const size_t plane = (size_t)P.T * L.K * L.F;
-  const long long total = (long long)n * per;
-  for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < total;
-       q += (long long)gridDim.x * blockDim.x) {
-    const int pos = (int)(q / per), c = (int)(q - (long long)pos * per) * 8;
-    const int e = P.pe[pos];
-    const float gs = L.edt == kNVFP4 ? L.gg[e] : 1.f;
-    const float us = L.edt == kNVFP4 ? L.gu[e] : 1.f;
-    const float* g = P.gu + (size_t)pos * 2 * L.F + c;
-    const float* up = g + L.F;
-    float v[8];
+  const int pos = blockIdx.x * kWaves + wave_id();
+  if (pos >= P.off[L.E]) return;
+  const int ln = lane_id();
+  const int e = P.pe[pos];
+  const float gs = FP4 ? L.gg[e] : 1.f;
+  const float us = FP4 ? L.gu[e] : 1.f;
+  const float* g = P.gu + (size_t)pos * 2 * L.F;
+  const float* up = g + L.F;
+  auto act8 = [&](int c, float (&v)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; i += 4) {
-      const v4f a = *reinterpret_cast<const v4f*>(g + i);
-      const v4f b = *reinterpret_cast<const v4f*>(up + i);
+      const v4f a = *reinterpret_cast<const v4f*>(g + c + i);
+      const v4f b = *reinterpret_cast<const v4f*>(up + c + i);
       v[i] = silu(gs * a.x) * (us * b.x);
       v[i + 1] = silu(gs * a.y) * (us * b.y);
       v[i + 2] = silu(gs * a.z) * (us * b.z);
       v[i + 3] = silu(gs * a.w) * (us * b.w);
     }
-    store_split2(P.act, plane, (size_t)pos * L.F + c, v);
+  };
+  int sh = 0;
+  if constexpr (FP4) {
+    float m = 0.f;
+    for (int c = 8 * ln; c < L.F; c += 512) {
+      float v[8];
+      act8(c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
+    sh = pf_shift(wave_max(m));
+  }
+  if (ln == 0) P.ae[pos] = sh;
+  for (int c = 8 * ln; c < L.F; c += 512) {
+    float v[8];
+    act8(c, v);
+    pf_store8<FP4>(P.act, (size_t)P.T * L.K * L.F, (size_t)pos * L.F + c, v, sh);
   }
 }
 
-// The gate/up (GU) or down product of every block: item = (block, 64-row
-// block of the expert's rows).
-template <bool FP4, bool GU>
-__device__ void pf_dense(const LayerArgs& L, const PfArgs& P, uint8_t* lds) {
+constexpr int kPfRows = 4 * 64;             // output rows per item
+constexpr int kPfStage = kPfChunk * 256;     // bytes of one k-tile of inputs
+constexpr int kPfStages = 3;                 // k-tiles in the LDS ring
+constexpr int kPfLds = kPfStages * kPfStage;
+
+// Per format: input terms, k columns per tile, weight registers of a tile
+// (lane (r, g) holds columns (KT / 4) g .. + KT / 4 - 1 of rows 16 rf + r).
+template <bool FP4>
+struct PfW;
+template <>
+struct PfW<true> {
+  static constexpr int NTERM = 1, KT = 128, LOADS = 8;
+  v4u c[4];           // e2m1 codes, low nibble first
+  unsigned s[4];      // e4m3 block scales 4 (g / 2) .. + 3 of the tile; the
+                      // lane's two are the half (g & 1)
+};
+template <>
+struct PfW<false> {
+  static constexpr int NTERM = 2, KT = 64, LOADS = 8;
+  v4u w[4][2];        // bf16 values
+};
+
+// The weight operand of row tile rf, k-step j.
+__device__ __forceinline__ f16x8 pf_weights(const PfW<true>& W, int rf, int j, f16x2 sc) {
+  const unsigned d = W.c[rf][j];
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * sc;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * sc;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * sc;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * sc;
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  const f16x4 lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  const f16x4 hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// One item: rows rb * 256 .. + 255 of the product for chunk ch, TF 16-slot
+// tiles of the chunk (16 (TF - 1) < ch.n <= 16 TF).  Ends with the LDS free.
+template <bool FP4, bool GU, int TF>
+__device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, int rb,
+                        uint8_t* lds) {
+  using W_ = PfW<FP4>;
+  constexpr int KT = W_::KT, NTERM = W_::NTERM, J = KT / 32;
+  constexpr int RB = KT * 2, PR = RB / 16, RPI = 1024 / RB;  // row bytes, pieces, rows per 1 KB
+  constexpr int LPP = 16 * TF * RB / 1024;                     // 1-KB loads per term plane
+  constexpr int PLANE = kPfChunk * RB;                         // LDS bytes per term plane
   const int N = GU ? 2 * L.F : L.H, K = GU ? L.H : L.F;
-  const int n_rb = N / 64;
-  const long long items = (long long)(*P.nblk) * n_rb;
-  const size_t rbytes = FP4 ? (size_t)K / 2 : (size_t)K * 2;  // weight bytes per row
-  const size_t sbytes = (size_t)K / 16;                         // NVFP4 scale bytes per row
-  for (long long item = blockIdx.x; item < items; item += gridDim.x) {
-    const PfBlock b = P.blk[item / n_rb];
-    const int rb = (int)(item - (item / n_rb) * n_rb);
-    DenseArgs D{};
-    D.K = K;
-    D.N = N;
-    D.T = b.n;
-    D.ks = 1;
-    D.oscale = 1.f;
-    D.a3_plane = (size_t)P.T * L.K * K;  // the two terms' planes span every slot
+  const int ln = lane_id(), wv = wave_id(), r = ln & 15, g = ln >> 4;
+  const int tiles = K / KT;
+  const int r0 = rb * kPfRows + 64 * wv;  // this wave's first row (64 never straddle W_g / W_u)
+  const bool active = r0 < N;
+  const uint8_t* wp[4];
+  const uint8_t* sp[4];
+#pragma unroll
+  for (int rf = 0; rf < 4; ++rf) {
+    const int row = active ? r0 + 16 * rf + r : 0;
+    const uint8_t* m;
+    const uint8_t* sm;
+    size_t gr;
     if constexpr (GU) {
-      const size_t r0 = (size_t)b.e * L.F;
-      D.w[0] = L.wg + r0 * rbytes;
-      D.w[1] = L.wu + r0 * rbytes;
-      D.w[2] = D.w[0];
-      D.s[0] = FP4 ? L.sg + r0 * sbytes : nullptr;
-      D.s[1] = FP4 ? L.su + r0 * sbytes : nullptr;
-      D.s[2] = D.s[0];
-      D.seg[1] = L.F;
-      D.a3 = P.a + (size_t)b.pos0 * K;
-      D.out = P.gu + (size_t)b.pos0 * N;
+      const bool up = row >= L.F;
+      m = up ? L.wu : L.wg;
+      sm = up ? L.su : L.sg;
+      gr = (size_t)ch.e * L.F + (up ? row - L.F : row);
     } else {
-      const size_t r0 = (size_t)b.e * L.H;
-      D.w[0] = D.w[1] = D.w[2] = L.wd + r0 * rbytes;
-      D.s[0] = D.s[1] = D.s[2] = FP4 ? L.sd + r0 * sbytes : nullptr;
-      D.a3 = P.act + (size_t)b.pos0 * K;
-      D.out = P.y;
-      D.tmap = P.perm + b.pos0;
-      D.oscale = FP4 ? L.gd[b.e] : 1.f;
+      m = L.wd;
+      sm = L.sd;
+      gr = (size_t)ch.e * L.H + row;
     }
-    if constexpr (FP4)
-      dense_item_fp4<4, 2>(D, rb, lds);
+    if constexpr (FP4) {
+      wp[rf] = m + gr * (K / 2) + 16 * g;
+      sp[rf] = sm + gr * (K / 16) + 4 * (g >> 1);
+    } else {
+      wp[rf] = m + gr * K * 2 + 32 * g;
+      sp[rf] = nullptr;
+    }
+  }
+  auto load_w = [&](int tau, W_& W) {
+#pragma unroll
+    for (int rf = 0; rf < 4; ++rf) {
+      if constexpr (FP4) {
+        W.c[rf] = *reinterpret_cast<const v4u*>(wp[rf] + (size_t)tau * 64);
+        W.s[rf] = *reinterpret_cast<const unsigned*>(sp[rf] + (size_t)tau * 8);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          W.w[rf][q] = *reinterpret_cast<const v4u*>(wp[rf] + (size_t)tau * 128 + 16 * q);
+      }
+    }
+  };
+  const unsigned short* in = GU ? P.a : P.act;
+  const size_t in_plane = (size_t)P.T * L.K * K;
+  auto issue_in = [&](int tau, int buf) {
+    uint8_t* bt = lds + buf * kPfStage;
+#pragma unroll
+    for (int m = 0; m < TF; ++m) {
+      const int q = wv + 4 * m;          // 1-KB load q of the NTERM LPP
+      const int pl = q / LPP, ql = q - pl * LPP;
+      const int R = ql * RPI + ln / PR;  // chunk row this lane fills, slot ln % PR
+      const int tk = R < ch.n ? R : ch.n - 1;
+      const int p = (ln % PR) ^ (R & (PR - 1));  // the piece that belongs in that slot
+      __builtin_amdgcn_global_load_lds(
+          in + pl * in_plane + (size_t)(ch.pos0 + tk) * K + (size_t)tau * KT + p * 8,
+          bt + pl * PLANE + ql * 1024, 16, 0, 0);
+    }
+  };
+  f32x4 acc[4][TF];
+#pragma unroll
+  for (int rf = 0; rf < 4; ++rf)
+#pragma unroll
+    for (int tf = 0; tf < TF; ++tf) acc[rf][tf] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const W_& W, int buf) {
+    const uint8_t* bt = lds + buf * kPfStage;
+    f16x2 sc[4][2];
+    if constexpr (FP4) {
+#pragma unroll
+      for (int rf = 0; rf < 4; ++rf) {
+        const int sv = (int)(W.s[rf] >> (16 * (g & 1)));
+        const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sv, 0);
+        const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sv, 1);
+        sc[rf][0] = f16x2{s0, s0};
+        sc[rf][1] = f16x2{s1, s1};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      v4u b[NTERM][TF];
+#pragma unroll
+      for (int pl = 0; pl < NTERM; ++pl)
+#pragma unroll
+        for (int tf = 0; tf < TF; ++tf)
+          b[pl][tf] = *reinterpret_cast<const v4u*>(
+              bt + pl * PLANE + (16 * tf + r) * RB + (((J * g + j) ^ (r & (PR - 1))) * 16));
+#pragma unroll
+      for (int rf = 0; rf < 4; ++rf) {
+        if constexpr (FP4) {
+          const f16x8 a = pf_weights(W, rf, j, sc[rf][j >> 1]);
+#pragma unroll
+          for (int tf = 0; tf < TF; ++tf)
+            acc[rf][tf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                a, __builtin_bit_cast(f16x8, b[0][tf]), acc[rf][tf], 0, 0, 0);
+        } else {
+          const bf16x8 a = as_bf16x8(W.w[rf][j]);
+#pragma unroll
+          for (int tf = 0; tf < TF; ++tf)
+#pragma unroll
+            for (int pl = 0; pl < NTERM; ++pl)
+              acc[rf][tf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(b[pl][tf]),
+                                                                    acc[rf][tf], 0, 0, 0);
+        }
+      }
+    }
+  };
+  // Tile tau, ring slot S = tau % 3: wait for its loads (tile tau + 1's may
+  // stay in flight), meet the other waves (so every wave is done with tile
+  // tau - 1, whose slot is refilled), fetch tile tau + 2 (LA) and use tile
+  // tau.  Every wave issues the same loads at every step (idle waves fetch
+  // rows they never use) and the loads are never conditional inside the
+  // loop, so the compiler's own counter bookkeeping stays exact and adds no
+  // wait that would drain the loads in flight.
+  W_ W[kPfStages];
+  constexpr int PER = TF + W_::LOADS;  // loads per tile of every wave
+  auto fetch = [&](auto S_, int tau) {
+    constexpr int S = decltype(S_)::value;
+    issue_in(tau, S);
+    load_w(tau, W[S]);
+  };
+  auto step = [&](auto S_, auto LA_, auto LAST_, int tau) {
+    constexpr int S = decltype(S_)::value;
+    if constexpr (decltype(LAST_)::value)
+      wait_vm<0>();
     else
-      dense_item<4, 2>(D, rb, lds);
+      wait_vm<PER>();
+    lds_barrier();
+    if constexpr (decltype(LA_)::value) fetch(IC<(S + 2) % kPfStages>{}, tau + 2);
+    if (active) compute(W[S], S);
+  };
+  using T_ = IC<1>;
+  using F_ = IC<0>;
+  fetch(IC<0>{}, 0);
+  fetch(IC<1>{}, tiles > 1 ? 1 : 0);  // one tile: a second copy, never used
+  if (tiles >= 2) {
+    const int nla = tiles - 2;  // steps that fetch ahead: 0 .. tiles - 3
+    int tau = 0;
+    for (; tau + 3 <= nla; tau += 3) {
+      step(IC<0>{}, T_{}, F_{}, tau);
+      step(IC<1>{}, T_{}, F_{}, tau + 1);
+      step(IC<2>{}, T_{}, F_{}, tau + 2);
+    }
+    if (tau < nla) {
+      step(IC<0>{}, T_{}, F_{}, tau);
+      if (tau + 1 < nla) step(IC<1>{}, T_{}, F_{}, tau + 1);
+    }
+    // the last two tiles, in ring slots (tiles - 2) % 3 and (tiles - 1) % 3
+    switch (nla % kPfStages) {
+      case 0:
+        step(IC<0>{}, F_{}, F_{}, tiles - 2);
+        step(IC<1>{}, F_{}, T_{}, tiles - 1);
+        break;
+      case 1:
+        step(IC<1>{}, F_{}, F_{}, tiles - 2);
+        step(IC<2>{}, F_{}, T_{}, tiles - 1);
+        break;
+      default:
+        step(IC<2>{}, F_{}, F_{}, tiles - 2);
+        step(IC<0>{}, F_{}, T_{}, tiles - 1);
+        break;
+    }
+  } else {
+    step(IC<0>{}, F_{}, T_{}, 0);
+  }
+  lds_barrier();  // every wave is done with the ring before the next item fills it
+  if (!active) return;
+  // lane (r, g): slot 16 tf + r, rows r0 + 16 rf + 4 g + i
+#pragma unroll
+  for (int tf = 0; tf < TF; ++tf) {
+    const int tk = 16 * tf + r;
+    if (tk >= ch.n) continue;
+    const int pos = ch.pos0 + tk;
+    float* o;
+    int sh;
+    float osc = 1.f;
+    if constexpr (GU) {
+      sh = P.ue[pos];
+      o = P.gu + (size_t)pos * N + r0 + 4 * g;
+    } else {
+      sh = P.ae[pos];
+      if constexpr (FP4) osc = L.gd[ch.e];
+      o = P.y + (size_t)P.perm[pos] * N + r0 + 4 * g;
+    }
+#pragma unroll
+    for (int rf = 0; rf < 4; ++rf) {
+      const f32x4 a = acc[rf][tf];
+      *reinterpret_cast<v4f*>(o + 16 * rf) =
+          v4f{ldexpf(osc * a[0], sh), ldexpf(osc * a[1], sh), ldexpf(osc * a[2], sh),
+              ldexpf(osc * a[3], sh)};
+    }
+  }
+}
+
+// Every item of the gate/up (GU) or down product: item = chunk * n_rb + row
+// block.  Workgroup b runs on XCD b % 8 (gridDim.x is a multiple of 8); XCD
+// x takes the contiguous items [x per, (x + 1) per) in order.
+template <bool FP4, bool GU>
+__device__ void pf_gemm(const LayerArgs& L, const PfArgs& P, uint8_t* lds) {
+  const int N = GU ? 2 * L.F : L.H;
+  const int n_rb = (N + kPfRows - 1) / kPfRows;
+  const long long items = (long long)(*P.nchunk) * n_rb;
+  const long long per = (items + 7) >> 3;
+  const int x = blockIdx.x & 7, v = blockIdx.x >> 3, gx = gridDim.x >> 3;
+  for (long long i = v; i < per; i += gx) {
+    const long long item = x * per + i;
+    if (item >= items) break;
+    const long long c = item / n_rb;
+    const PfChunk ch = P.chunk[c];
+    const int rb = (int)(item - c * n_rb);
+    const int ntf = (ch.n + 15) >> 4;
+    if (ntf > 4)
+      pf_item<FP4, GU, 8>(L, P, ch, rb, lds);
+    else if (ntf > 2)
+      pf_item<FP4, GU, 4>(L, P, ch, rb, lds);
+    else if (ntf > 1)
+      pf_item<FP4, GU, 2>(L, P, ch, rb, lds);
+    else
+      pf_item<FP4, GU, 1>(L, P, ch, rb, lds);
   }
 }
 
