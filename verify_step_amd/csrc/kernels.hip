@@ -1130,11 +1130,12 @@ static hipError_t launch_pf(const LayerArgs& L, const PfArgs& P, hipStream_t st)
   // one wave per token, then per grouped position
   MSK_TRY(launch_x(kPhPrep, k_pf_gather<FP4>, (P.T + kWaves - 1) / kWaves, 0, st, L, P));
   auto gemm = [&](auto fn, int ph) -> hipError_t {
-    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), kPfLds));
+    constexpr size_t lds = pf_lds<FP4>();
+    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(fn), lds));
     // a multiple of 8 workgroups: the items are split by XCD
-    int grid = resident_grid(reinterpret_cast<const void*>(fn), kPfLds) & ~7;
+    int grid = resident_grid(reinterpret_cast<const void*>(fn), lds) & ~7;
     if (grid < 8) grid = 8;
-    return launch_x(ph, fn, grid, kPfLds, st, L, P);
+    return launch_x(ph, fn, grid, lds, st, L, P);
   };
   MSK_TRY(gemm(k_pf_gemm<FP4, true>, kPhGateUp));
   MSK_TRY(launch_x(kPhPrep, k_pf_swiglu<FP4>, (slots + kWaves - 1) / kWaves, 0, st, L, P));

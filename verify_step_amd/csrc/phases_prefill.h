@@ -32,17 +32,18 @@
 // Matrix product item: (chunk of up to 128 slots of expert e, 256 output
 // rows); each of the four waves owns 64 rows x all the chunk's slots
 // (4 x 8 accumulator tiles of 16 x 16).  Per k-tile (128 columns for NVFP4,
-// 64 for bf16, so that either tile of inputs is 32 KB):
-//   - the chunk's input rows arrive in LDS by direct global->LDS loads, three
-//     tiles in the ring (two in flight while one is used), each row's 16-B
-//     pieces stored at piece ^ (row & 15) (bf16: row & 7) so an operand read
-//     (16 rows, one piece each) meets no bank conflict; every wave reads all
-//     of them;
-//   - each wave's weight rows go straight to registers two tiles ahead (they
-//     are used by that wave alone): a lane holds KT / 4 consecutive columns
-//     of one row, which serve every k-step of the tile.  The k index of step
-//     j, lane group g is numbered (KT / 4) g + 8 j + (0..7) on both operands,
-//     which keeps every lane's weight load one contiguous run of bytes.
+// 64 for bf16, so that either tile of inputs is 32 KB), in a ring of three
+// tiles (two in flight while one is used):
+//   - the chunk's input rows arrive in LDS by direct global->LDS loads, each
+//     row's 16-B pieces stored at piece ^ (row & 15) (bf16: row & 7) so an
+//     operand read (16 rows, one piece each) meets no bank conflict; every
+//     wave reads all of them;
+//   - NVFP4 weight rows (codes and block scales) arrive in the same ring slot
+//     by direct loads as well, each wave's own rows, and are decoded from LDS;
+//     bf16 weight rows go straight to registers (a lane holds 16 consecutive
+//     columns of one row, which serve both k-steps of the tile).  The k index
+//     of step j, lane group g is numbered (KT / 4) g + 8 j + (0..7) on both
+//     operands, which keeps every lane's part of a row one contiguous run.
 // The weights are streamed once per chunk (once per expert when it has at
 // most 128 slots); the items of one chunk are consecutive and an XCD runs a
 // contiguous range of items, so the chunk's inputs and the weights shared by
@@ -207,30 +208,41 @@ __device__ inline void pf_swiglu(const LayerArgs& L, const PfArgs& P) {
 }
 
 constexpr int kPfRows = 4 * 64;             // output rows per item
-constexpr int kPfStage = kPfChunk * 256;     // bytes of one k-tile of inputs
+constexpr int kPfIn = kPfChunk * 256;        // bytes of one k-tile of inputs
 constexpr int kPfStages = 3;                 // k-tiles in the LDS ring
-constexpr int kPfLds = kPfStages * kPfStage;
 
-// Per format: input terms, k columns per tile, weight registers of a tile
-// (lane (r, g) holds columns (KT / 4) g .. + KT / 4 - 1 of rows 16 rf + r).
+// Per format: input terms, k columns per tile, loads per tile of one wave
+// besides its share of the input tile, bytes of one ring slot.
+//   NVFP4: a wave's 64 weight rows of a tile (64 x 64 B of e2m1 codes and
+//   64 x 8 B of e4m3 scales) come into the slot by direct global->LDS loads
+//   too: four 1-KB loads of codes (16 rows x 64 B each; a row's 16-B pieces
+//   stored at piece ^ ((row >> 2) & 3), so an operand read of 16 rows meets
+//   no bank conflict) and two 256-B loads of scales.
+//   bf16: a lane's 16 columns of four rows (32 B each) go straight to
+//   registers, two tiles ahead.
 template <bool FP4>
-struct PfW;
+struct PfFmt;
 template <>
-struct PfW<true> {
-  static constexpr int NTERM = 1, KT = 128, LOADS = 8;
-  v4u c[4];           // e2m1 codes, low nibble first
-  unsigned s[4];      // e4m3 block scales 4 (g / 2) .. + 3 of the tile; the
-                      // lane's two are the half (g & 1)
+struct PfFmt<true> {
+  static constexpr int NTERM = 1, KT = 128, LOADS = 6;
+  static constexpr int CODES = kPfIn, SCALES = CODES + 4 * 4096, STAGE = SCALES + 4 * 512;
 };
 template <>
-struct PfW<false> {
-  static constexpr int NTERM = 2, KT = 64, LOADS = 8;
-  v4u w[4][2];        // bf16 values
+struct PfFmt<false> {
+  static constexpr int NTERM = 2, KT = 64, LOADS = 8, STAGE = kPfIn;
+};
+template <bool FP4>
+constexpr int pf_lds() { return kPfStages * PfFmt<FP4>::STAGE; }
+
+// bf16 weight registers of one tile: lane (r, g) holds columns 16 g .. + 15
+// of rows 16 rf + r.
+struct PfWbf {
+  v4u w[4][2];
 };
 
-// The weight operand of row tile rf, k-step j.
-__device__ __forceinline__ f16x8 pf_weights(const PfW<true>& W, int rf, int j, f16x2 sc) {
-  const unsigned d = W.c[rf][j];
+// The NVFP4 weight operand of k-step j from a lane's 16 B of codes (32
+// columns) and its block scale for those 8 columns.
+__device__ __forceinline__ f16x8 pf_weights(unsigned d, f16x2 sc) {
   const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * sc;
   const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * sc;
   const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * sc;
@@ -246,8 +258,8 @@ __device__ __forceinline__ f16x8 pf_weights(const PfW<true>& W, int rf, int j, f
 template <bool FP4, bool GU, int TF>
 __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, int rb,
                         uint8_t* lds) {
-  using W_ = PfW<FP4>;
-  constexpr int KT = W_::KT, NTERM = W_::NTERM, J = KT / 32;
+  using Fm = PfFmt<FP4>;
+  constexpr int KT = Fm::KT, NTERM = Fm::NTERM, J = KT / 32;
   constexpr int RB = KT * 2, PR = RB / 16, RPI = 1024 / RB;  // row bytes, pieces, rows per 1 KB
   constexpr int LPP = 16 * TF * RB / 1024;                     // 1-KB loads per term plane
   constexpr int PLANE = kPfChunk * RB;                         // LDS bytes per term plane
@@ -256,11 +268,9 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
   const int tiles = K / KT;
   const int r0 = rb * kPfRows + 64 * wv;  // this wave's first row (64 never straddle W_g / W_u)
   const bool active = r0 < N;
-  const uint8_t* wp[4];
-  const uint8_t* sp[4];
-#pragma unroll
-  for (int rf = 0; rf < 4; ++rf) {
-    const int row = active ? r0 + 16 * rf + r : 0;
+  // first byte of weight row `row` (global row index of the product) and of
+  // its NVFP4 scales
+  auto wrow = [&](int row, const uint8_t*& w, const uint8_t*& sc) {
     const uint8_t* m;
     const uint8_t* sm;
     size_t gr;
@@ -275,30 +285,59 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
       gr = (size_t)ch.e * L.H + row;
     }
     if constexpr (FP4) {
-      wp[rf] = m + gr * (K / 2) + 16 * g;
-      sp[rf] = sm + gr * (K / 16) + 4 * (g >> 1);
+      w = m + gr * (K / 2);
+      sc = sm + gr * (K / 16);
     } else {
-      wp[rf] = m + gr * K * 2 + 32 * g;
-      sp[rf] = nullptr;
+      w = m + gr * K * 2;
+      sc = nullptr;
+    }
+  };
+  const int wr0 = active ? r0 : 0;  // idle waves fetch rows they never use
+  // NVFP4: this lane's rows in the code loads (16 i + ln / 4) and the scale
+  // loads (32 q + ln / 2); bf16: rows 16 rf + r
+  const uint8_t* wp[4];
+  const uint8_t* sp[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint8_t* sc;
+    wrow(wr0 + 16 * i + (FP4 ? ln >> 2 : r), wp[i], sc);
+    if constexpr (FP4)
+      wp[i] += 16 * ((ln & 3) ^ ((ln >> 4) & 3));  // the piece that belongs in this lane's slot
+    else
+      wp[i] += 32 * g;
+  }
+  if constexpr (FP4) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint8_t* w;
+      wrow(wr0 + 32 * q + (ln >> 1), w, sp[q]);
+      sp[q] += 4 * (ln & 1);
     }
   }
-  auto load_w = [&](int tau, W_& W) {
+  auto load_w = [&](int tau, PfWbf& W) {
 #pragma unroll
-    for (int rf = 0; rf < 4; ++rf) {
-      if constexpr (FP4) {
-        W.c[rf] = *reinterpret_cast<const v4u*>(wp[rf] + (size_t)tau * 64);
-        W.s[rf] = *reinterpret_cast<const unsigned*>(sp[rf] + (size_t)tau * 8);
-      } else {
+    for (int rf = 0; rf < 4; ++rf)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-          W.w[rf][q] = *reinterpret_cast<const v4u*>(wp[rf] + (size_t)tau * 128 + 16 * q);
-      }
+      for (int q = 0; q < 2; ++q)
+        W.w[rf][q] = *reinterpret_cast<const v4u*>(wp[rf] + (size_t)tau * 128 + 16 * q);
+  };
+  auto dma_w = [&](int tau, int buf) {
+    if constexpr (FP4) {
+      uint8_t* st = lds + buf * Fm::STAGE;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(wp[i] + (size_t)tau * 64,
+                                         st + Fm::CODES + wv * 4096 + i * 1024, 16, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_global_load_lds(sp[q] + (size_t)tau * 8,
+                                         st + Fm::SCALES + wv * 512 + q * 256, 4, 0, 0);
     }
   };
   const unsigned short* in = GU ? P.a : P.act;
   const size_t in_plane = (size_t)P.T * L.K * K;
   auto issue_in = [&](int tau, int buf) {
-    uint8_t* bt = lds + buf * kPfStage;
+    uint8_t* bt = lds + buf * Fm::STAGE;
 #pragma unroll
     for (int m = 0; m < TF; ++m) {
       const int q = wv + 4 * m;          // 1-KB load q of the NTERM LPP
@@ -316,13 +355,20 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
   for (int rf = 0; rf < 4; ++rf)
 #pragma unroll
     for (int tf = 0; tf < TF; ++tf) acc[rf][tf] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const W_& W, int buf) {
-    const uint8_t* bt = lds + buf * kPfStage;
+  auto compute = [&](const PfWbf& W, int buf) {
+    const uint8_t* bt = lds + buf * Fm::STAGE;
+    v4u cw[4];
     f16x2 sc[4][2];
     if constexpr (FP4) {
+      // this wave's codes and scales of the tile
 #pragma unroll
       for (int rf = 0; rf < 4; ++rf) {
-        const int sv = (int)(W.s[rf] >> (16 * (g & 1)));
+        const int row = 16 * rf + r;
+        cw[rf] = *reinterpret_cast<const v4u*>(bt + Fm::CODES + wv * 4096 + row * 64 +
+                                               ((g ^ ((r >> 2) & 3)) * 16));
+        const int sv = (int)(*reinterpret_cast<const unsigned*>(
+                                 bt + Fm::SCALES + wv * 512 + row * 8 + 4 * (g >> 1)) >>
+                             (16 * (g & 1)));
         const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sv, 0);
         const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sv, 1);
         sc[rf][0] = f16x2{s0, s0};
@@ -341,7 +387,7 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
 #pragma unroll
       for (int rf = 0; rf < 4; ++rf) {
         if constexpr (FP4) {
-          const f16x8 a = pf_weights(W, rf, j, sc[rf][j >> 1]);
+          const f16x8 a = pf_weights(cw[rf][j], sc[rf][j >> 1]);
 #pragma unroll
           for (int tf = 0; tf < TF; ++tf)
             acc[rf][tf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -365,12 +411,15 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
   // rows they never use) and the loads are never conditional inside the
   // loop, so the compiler's own counter bookkeeping stays exact and adds no
   // wait that would drain the loads in flight.
-  W_ W[kPfStages];
-  constexpr int PER = TF + W_::LOADS;  // loads per tile of every wave
+  PfWbf W[kPfStages];  // bf16 weight registers (unused for NVFP4)
+  constexpr int PER = TF + Fm::LOADS;  // loads per tile of every wave
   auto fetch = [&](auto S_, int tau) {
     constexpr int S = decltype(S_)::value;
     issue_in(tau, S);
-    load_w(tau, W[S]);
+    if constexpr (FP4)
+      dma_w(tau, S);
+    else
+      load_w(tau, W[S]);
   };
   auto step = [&](auto S_, auto LA_, auto LAST_, int tau) {
     constexpr int S = decltype(S_)::value;
@@ -384,6 +433,12 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
   };
   using T_ = IC<1>;
   using F_ = IC<0>;
+  // The previous item's output stores are still counted: until a wait for
+  // zero, the compiler treats the counter as out of order and turns every
+  // wait it adds for a weight register into a wait for zero (a full drain
+  // at a step of the loop below).  One drain here, before anything of this
+  // item is in flight, costs only the stores' round trip.
+  wait_vm<0>();
   fetch(IC<0>{}, 0);
   fetch(IC<1>{}, tiles > 1 ? 1 : 0);  // one tile: a second copy, never used
   if (tiles >= 2) {
