@@ -81,7 +81,8 @@ __device__ inline void pf_route(const LayerArgs& L, const PfArgs& P, int* lds) {
     *P.nchunk = c;
   }
   __syncthreads();
-  // an expert's slots in nc near-equal chunks
+  // an expert's slots in nc near-equal chunks (measured faster than chunks
+  // of kPfChunk and a last one with the rest)
   for (int e = threadIdx.x; e < L.E; e += blockDim.x) {
     const int n = cnt[e], nc = (n + kPfChunk - 1) / kPfChunk;
     for (int c = 0; c < nc; ++c) {
@@ -253,8 +254,9 @@ __device__ __forceinline__ f16x8 pf_weights(unsigned d, f16x2 sc) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// One item: rows rb * 256 .. + 255 of the product for chunk ch, TF 16-slot
-// tiles of the chunk (16 (TF - 1) < ch.n <= 16 TF).  Ends with the LDS free.
+// One item: rows rb * 256 .. + 255 of the product for chunk ch, in TF 16-slot
+// tiles (ch.n <= 16 TF; slots past ch.n repeat its last one and are not
+// written).  Ends with the LDS free.
 template <bool FP4, bool GU, int TF>
 __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, int rb,
                         uint8_t* lds) {
@@ -517,8 +519,10 @@ __device__ void pf_gemm(const LayerArgs& L, const PfArgs& P, uint8_t* lds) {
     const PfChunk ch = P.chunk[c];
     const int rb = (int)(item - c * n_rb);
     const int ntf = (ch.n + 15) >> 4;
-    if (ntf > 4)
+    if (ntf > 6)
       pf_item<FP4, GU, 8>(L, P, ch, rb, lds);
+    else if (ntf > 4)
+      pf_item<FP4, GU, 6>(L, P, ch, rb, lds);
     else if (ntf > 2)
       pf_item<FP4, GU, 4>(L, P, ch, rb, lds);
     else if (ntf > 1)
