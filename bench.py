@@ -263,6 +263,20 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 PREFILL_METRIC = "µs per MoE layer prefill expert FFN + achieved TFLOP/s (% of bf16 matrix peak)"
 
 
+def prefill_accounting(spec, counts):
+    """Algorithmic flops of the two products ({"gateup", "down"}), the bytes
+    of the distinct experts' weights, and the weight bytes the chunked
+    products stream, for counts[e] slots routed to expert e."""
+    H, F = spec["hidden"], spec["ffn_dim"]
+    slots = int(np.sum(counts))
+    gu_b, dn_b = expert_bytes(spec)
+    distinct = int((np.asarray(counts) > 0).sum()) * (gu_b + dn_b)
+    # each chunk of up to 128 of an expert's slots streams the expert's rows
+    streamed = int(((np.asarray(counts) + 127) // 128).sum()) * (gu_b + dn_b)
+    flops = {"gateup": 2.0 * slots * 2 * F * H, "down": 2.0 * slots * H * F}
+    return flops, distinct, streamed
+
+
 def measure_prefill(name, args):
     """Time msk_moe_prefill on one layer's experts: returns its JSON record.
     Routing: each token's top-8 of 256 synthetic unit logits."""
@@ -303,11 +317,7 @@ def measure_prefill(name, args):
     msk.timer_start(())
     slots = T * K
     counts = np.bincount(idx.cpu().numpy().ravel(), minlength=E)
-    gu_b, dn_b = expert_bytes(spec)
-    distinct = int((counts > 0).sum()) * (gu_b + dn_b)
-    # each group of up to 64 of an expert's slots reads the expert's rows again
-    streamed = int(((counts + 63) // 64).sum()) * (gu_b + dn_b)
-    flops = {"gateup": 2.0 * slots * 2 * F * H, "down": 2.0 * slots * H * F}
+    flops, distinct, streamed = prefill_accounting(spec, counts)
     total_flops = sum(flops.values())
     timed = {ph: v for ph, v in kt.items() if v[1]}
     dom = max(("gateup", "down"), key=lambda ph: timed[ph][0])
@@ -337,7 +347,7 @@ def measure_prefill(name, args):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "k_pf_dense", "phase": dom,
+                     "kernel": "k_pf_gemm", "phase": dom,
                      "flops_per_launch": flops[dom], "avg_launch_us": round(avg_us, 3),
                      "launches": timed[dom][1]},
         "kernels": {ph: {"avg_us": round(v[0] * 1e3 / v[1], 3), "launches": v[1]}

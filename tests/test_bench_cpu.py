@@ -68,6 +68,21 @@ def test_distinct_experts_counted_once():
     assert parts["experts"] == 8 * sum(bench.expert_bytes(spec))
 
 
+def test_prefill_accounting_by_hand():
+    """Hidden 6144, FFN 2048, NVFP4 experts: 300 slots on expert 0 (three
+    chunks), 128 on expert 1 (one), 129 on expert 5 (two), none elsewhere."""
+    spec = _spec_only("stack4-nvfp4")
+    counts = np.zeros(256, dtype=np.int64)
+    counts[[0, 1, 5]] = [300, 128, 129]
+    flops, distinct, streamed = bench.prefill_accounting(spec, counts)
+    # gate and up: 2 flops x 557 slots x 4096 rows x 6144; down: x 6144 x 2048
+    assert flops["gateup"] == 2 * 557 * 4096 * 6144
+    assert flops["down"] == 2 * 557 * 6144 * 2048
+    one = 6_291_456 + 786_432 + 4          # one NVFP4 matrix of 2048 x 6144
+    assert distinct == 3 * 3 * one
+    assert streamed == (3 + 1 + 2) * 3 * one
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)
