@@ -323,6 +323,8 @@ def measure_prefill(name, args):
     dom = max(("gateup", "down"), key=lambda ph: timed[ph][0])
     avg_us = timed[dom][0] * 1e3 / timed[dom][1]
     achieved = flops[dom] / (avg_us * 1e-6) / 1e12
+    # HBM bytes per gate/up launch (its counter summary covers that kernel)
+    traffic = stored_traffic("k_pf_gemm", name) if dom == "gateup" else None
     return {
         "metric": PREFILL_METRIC,
         "value": round(ms * 1e3, 3),
@@ -346,7 +348,7 @@ def measure_prefill(name, args):
         "weight_bytes_streamed": streamed,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "kernel": "k_pf_gemm", "phase": dom,
                      "flops_per_launch": flops[dom], "avg_launch_us": round(avg_us, 3),
                      "launches": timed[dom][1]},
