@@ -119,3 +119,21 @@ def test_prefill_full_size(expert):
     torch.cuda.synchronize()
     rows = np.array([0, 1, 257, 511, 900, 1023])
     _check(f"full {expert}", out, h, _oracle(spec, w, u, h, idx, wts, rows), rows)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("expert,routing", [("nvfp4", "random"), ("bf16", "skewed")])
+def test_prefill_max_tokens(expert, routing):
+    """The largest call: 8192 tokens (65536 slots) at hidden 6144, 256 experts,
+    FFN 2048.  Random routing gives about 256 slots per expert (two or three
+    chunks each); skewed routing puts every token on experts 0..7 (64 chunks
+    of 128 each).  The oracle recomputes six tokens."""
+    print(f"[gpu-prefill] max tokens {expert} {routing}", flush=True)
+    spec, w = _layer(expert, synth._BIG)
+    T = 8192
+    u, h, idx, wts = _inputs(spec, T, 14, routing)
+    ws = msk.prefill_workspace(spec, T)
+    out = msk.moe_prefill(spec, w, u, idx, wts, h, ws)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 4095, 4096, 8000, 8191])
+    _check(f"max {expert} {routing}", out, h, _oracle(spec, w, u, h, idx, wts, rows), rows)
