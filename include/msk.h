@@ -280,10 +280,12 @@ msk_status msk_set_spin_limit(uint32_t polls);
 /* Experts of a prefill batch: the same result as msk_expert_ffn, for up to
  * MSK_MAX_PREFILL_TOKENS tokens.  With many tokens per expert the gate/up and
  * down products are matrix products on the matrix cores: the slots (t, j) are
- * grouped by expert, and each group of up to 64 of an expert's slots meets
- * that expert's weights as a bf16 matrix product with fp32 accumulation (u and
- * the SwiGLU activations as two bf16 terms each, exact to about 2^-17; NVFP4
- * weights decoded exactly to bf16).  Defined by: a fused MoE kernel among the
+ * grouped by expert, and each chunk of up to 128 of an expert's slots meets
+ * that expert's weights in one product with fp32 accumulation.  NVFP4 weights
+ * are decoded exactly to fp16 and meet fp16 inputs (u and the SwiGLU
+ * activations, each slot's row scaled by a power of two: 11 significant
+ * bits); bf16 weights meet two bf16 terms of each input (exact to about
+ * 2^-17).  Defined by: a fused MoE kernel among the
  * prefill optimisations
  * (ainewsbites page, "Agentic coding benchmark and serving tradeoffs");
  * NVFP4 experts with one scale per 16 values (brifing.si page, "Expert Weight
