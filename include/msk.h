@@ -301,7 +301,8 @@ msk_status msk_moe_prefill(const msk_layer_cfg *cfg, const msk_layer_weights *w,
                            size_t ws_bytes, void *stream);
 
 /* Workspace bytes of msk_moe_prefill for n_tokens tokens (grouped inputs,
- * products and per-slot outputs: about n_tokens * k * (8 H + 12 F) bytes);
+ * products and per-slot outputs: about n_tokens * (k * (4 H + 12 F) + 4 H)
+ * bytes);
  * 0 and msk_last_error() on invalid or unsupported arguments. */
 size_t msk_moe_prefill_workspace_size(const msk_layer_cfg *cfg, int32_t n_tokens);
 

@@ -492,7 +492,7 @@ PfLayout pf_layout(const msk_layer_cfg& c, int n) {
   L.pe = take(S * sizeof(int));
   L.ue = take(S * sizeof(int));
   L.ae = take(S * sizeof(int));
-  L.a = take(2 * S * H * 2);    // fp16, or two bf16 term planes
+  L.a = take(2 * (size_t)n * H * 2);  // by token: fp16, or two bf16 term planes
   L.gu = take(S * 2 * F * sizeof(float));
   L.act = take(2 * S * F * 2);
   L.y = take(S * H * sizeof(float));

@@ -122,10 +122,10 @@ struct PfArgs {
   int* perm;             // [T K] slot at grouped position pos
   int* pos;              // [T K] grouped position of slot s (-1: not placed)
   int* pe;               // [T K] expert at grouped position pos
-  int* ue;               // [T K] input row pos holds u * 2^-ue[pos]
+  int* ue;               // [T K] the input row of pos's token holds u * 2^-ue[pos]
   int* ae;               // [T K] activation row pos holds act * 2^-ae[pos]
-  unsigned short* a;     // [T K][H] inputs by position: fp16 (NVFP4 experts), or
-                         // [2][T K][H] two bf16 terms (bf16 experts)
+  unsigned short* a;     // [T][H] inputs by token: fp16 (NVFP4 experts), or
+                         // [2][T][H] two bf16 terms (bf16 experts)
   float* gu;             // [T K][2 F] gate and up products by position
   unsigned short* act;   // [T K][F] activations by position, as a
   float* y;              // [T K][H] expert outputs by slot

@@ -10,7 +10,8 @@
 // each expert's slots split into chunks of at most kPfChunk:
 //   route    count the slots per expert, place them grouped by expert (the
 //            order within an expert does not change any result), list chunks;
-//   gather   each position's input row u[t], in the matrix-product format;
+//   gather   each token's input row u[t] in the matrix-product format, once
+//            (the gate/up product reads it through the slot's token);
 //   gate/up  gu[pos] = [W_g; W_u]_e u  (fp32), e the position's expert;
 //   swiglu   act[pos] = silu(g_g gu_gate) * (g_u gu_up), in the same format
 //            (g: NVFP4 matrix scales, else 1);
@@ -132,8 +133,8 @@ __device__ __forceinline__ void pf_store8(unsigned short* dst, size_t plane, siz
   if constexpr (!FP4) *reinterpret_cast<v4u*>(dst + plane + off) = v4u{lo[0], lo[1], lo[2], lo[3]};
 }
 
-// One wave per token t: its input row u[t] in the product format, written to
-// the grouped position of each of its placed slots, with its power of two.
+// One wave per token t: its input row u[t] in the product format, and its
+// power of two at the grouped position of each of its placed slots.
 template <bool FP4>
 __device__ inline void pf_gather(const LayerArgs& L, const PfArgs& P) {
   const int t = blockIdx.x * kWaves + wave_id();
@@ -159,10 +160,7 @@ __device__ inline void pf_gather(const LayerArgs& L, const PfArgs& P) {
     const v4f x0 = *reinterpret_cast<const v4f*>(src + c);
     const v4f x1 = *reinterpret_cast<const v4f*>(src + c + 4);
     const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    for (int j = 0; j < L.K; ++j) {
-      const int p = P.pos[t * L.K + j];
-      if (p >= 0) pf_store8<FP4>(P.a, (size_t)P.T * L.K * L.H, (size_t)p * L.H + c, v, sh);
-    }
+    pf_store8<FP4>(P.a, (size_t)P.T * L.H, (size_t)t * L.H + c, v, sh);
   }
 }
 
@@ -336,20 +334,28 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
                                          st + Fm::SCALES + wv * 512 + q * 256, 4, 0, 0);
     }
   };
+  // input rows: u by token (gate/up), act by grouped position (down)
   const unsigned short* in = GU ? P.a : P.act;
-  const size_t in_plane = (size_t)P.T * L.K * K;
+  const size_t in_plane = GU ? (size_t)P.T * L.H : (size_t)P.T * L.K * L.F;
+  const unsigned short* isrc[TF];  // this lane's row and piece in 1-KB load m
+#pragma unroll
+  for (int m = 0; m < TF; ++m) {
+    const int q = wv + 4 * m;          // 1-KB load q of the NTERM LPP
+    const int pl = q / LPP, ql = q - pl * LPP;
+    const int R = ql * RPI + ln / PR;  // chunk row this lane fills, slot ln % PR
+    const int tk = R < ch.n ? R : ch.n - 1;
+    const int p = (ln % PR) ^ (R & (PR - 1));  // the piece that belongs in that slot
+    const int row = GU ? P.perm[ch.pos0 + tk] / L.K : ch.pos0 + tk;
+    isrc[m] = in + pl * in_plane + (size_t)row * K + p * 8;
+  }
   auto issue_in = [&](int tau, int buf) {
     uint8_t* bt = lds + buf * Fm::STAGE;
 #pragma unroll
     for (int m = 0; m < TF; ++m) {
-      const int q = wv + 4 * m;          // 1-KB load q of the NTERM LPP
+      const int q = wv + 4 * m;
       const int pl = q / LPP, ql = q - pl * LPP;
-      const int R = ql * RPI + ln / PR;  // chunk row this lane fills, slot ln % PR
-      const int tk = R < ch.n ? R : ch.n - 1;
-      const int p = (ln % PR) ^ (R & (PR - 1));  // the piece that belongs in that slot
-      __builtin_amdgcn_global_load_lds(
-          in + pl * in_plane + (size_t)(ch.pos0 + tk) * K + (size_t)tau * KT + p * 8,
-          bt + pl * PLANE + ql * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(isrc[m] + (size_t)tau * KT, bt + pl * PLANE + ql * 1024,
+                                       16, 0, 0);
     }
   };
   f32x4 acc[4][TF];
