@@ -137,3 +137,22 @@ def test_prefill_max_tokens(expert, routing):
     torch.cuda.synchronize()
     rows = np.array([0, 1, 4095, 4096, 8000, 8191])
     _check(f"max {expert} {routing}", out, h, _oracle(spec, w, u, h, idx, wts, rows), rows)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("expert", ["nvfp4", "bf16"])
+def test_prefill_long_rows(expert):
+    """Hidden 6272 and FFN 4224: rows longer than the gather (6144) and SwiGLU
+    (4096) keep in registers, so both convert their rows in two passes; 49
+    and 33 k-tiles, and a last 256-row block of the down product with 128
+    rows.  16 experts top-4 over 64 tokens."""
+    print(f"[gpu-prefill] long rows {expert}", flush=True)
+    dims = dict(_SMALL, hidden=6272, ffn_dim=4224, n_experts=16, top_k=4)
+    spec, w = _layer(expert, dims)
+    T = 64
+    u, h, idx, wts = _inputs(spec, T, 15)
+    ws = msk.prefill_workspace(spec, T)
+    out = msk.moe_prefill(spec, w, u, idx, wts, h, ws)
+    torch.cuda.synchronize()
+    rows = np.array([0, 7, 31, 63])
+    _check(f"long rows {expert}", out, h, _oracle(spec, w, u, h, idx, wts, rows), rows)

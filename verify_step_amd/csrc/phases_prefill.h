@@ -133,6 +133,54 @@ __device__ __forceinline__ void pf_store8(unsigned short* dst, size_t plane, siz
   if constexpr (!FP4) *reinterpret_cast<v4u*>(dst + plane + off) = v4u{lo[0], lo[1], lo[2], lo[3]};
 }
 
+// A wave converts one row of n values (eight per lane per 512 columns) to the
+// product format: for FP4 the power of two of its largest magnitude comes
+// first (pf_shift), so the row is needed twice.  Rows of up to 512 NR values
+// stay in registers in between (one read); longer rows are produced twice.
+// produce8(c, v) forms columns c .. c + 7; store8(c, v, sh) writes them.
+// Returns the power of two.
+template <bool FP4, int NR, class Produce, class Store>
+__device__ __forceinline__ int pf_convert_row(int n, Produce&& produce8, Store&& store8) {
+  const int ln = lane_id();
+  if (n <= 512 * NR) {
+    float v[NR][8];
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int c = 8 * ln + 512 * i;
+      if (c < n) {
+        produce8(c, v[i]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[i][k]));
+      }
+    }
+    const int sh = FP4 ? pf_shift(wave_max(m)) : 0;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int c = 8 * ln + 512 * i;
+      if (c < n) store8(c, v[i], sh);
+    }
+    return sh;
+  }
+  int sh = 0;
+  if constexpr (FP4) {
+    float m = 0.f;
+    for (int c = 8 * ln; c < n; c += 512) {
+      float v[8];
+      produce8(c, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+    }
+    sh = pf_shift(wave_max(m));
+  }
+  for (int c = 8 * ln; c < n; c += 512) {
+    float v[8];
+    produce8(c, v);
+    store8(c, v, sh);
+  }
+  return sh;
+}
+
 // One wave per token t: its input row u[t] in the product format, and its
 // power of two at the grouped position of each of its placed slots.
 template <bool FP4>
@@ -141,26 +189,20 @@ __device__ inline void pf_gather(const LayerArgs& L, const PfArgs& P) {
   if (t >= P.T) return;
   const int ln = lane_id();
   const float* src = P.u + (size_t)t * L.H;
-  int sh = 0;
-  if constexpr (FP4) {
-    float m = 0.f;
-    for (int c = 8 * ln; c < L.H; c += 512) {
-      const v4f x0 = *reinterpret_cast<const v4f*>(src + c);
-      const v4f x1 = *reinterpret_cast<const v4f*>(src + c + 4);
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(x0.x), fabsf(x0.y)), fmaxf(fabsf(x0.z), fabsf(x0.w))));
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(x1.x), fabsf(x1.y)), fmaxf(fabsf(x1.z), fabsf(x1.w))));
-    }
-    sh = pf_shift(wave_max(m));
-  }
+  const int sh = pf_convert_row<FP4, 12>(
+      L.H,
+      [&](int c, float (&v)[8]) {
+        const v4f x0 = *reinterpret_cast<const v4f*>(src + c);
+        const v4f x1 = *reinterpret_cast<const v4f*>(src + c + 4);
+        v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+        v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+      },
+      [&](int c, const float (&v)[8], int sh) {
+        pf_store8<FP4>(P.a, (size_t)P.T * L.H, (size_t)t * L.H + c, v, sh);
+      });
   if (ln < L.K) {
     const int p = P.pos[t * L.K + ln];
     if (p >= 0) P.ue[p] = sh;
-  }
-  for (int c = 8 * ln; c < L.H; c += 512) {
-    const v4f x0 = *reinterpret_cast<const v4f*>(src + c);
-    const v4f x1 = *reinterpret_cast<const v4f*>(src + c + 4);
-    const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    pf_store8<FP4>(P.a, (size_t)P.T * L.H, (size_t)t * L.H + c, v, sh);
   }
 }
 
@@ -170,40 +212,28 @@ template <bool FP4>
 __device__ inline void pf_swiglu(const LayerArgs& L, const PfArgs& P) {
   const int pos = blockIdx.x * kWaves + wave_id();
   if (pos >= P.off[L.E]) return;
-  const int ln = lane_id();
   const int e = P.pe[pos];
   const float gs = FP4 ? L.gg[e] : 1.f;
   const float us = FP4 ? L.gu[e] : 1.f;
   const float* g = P.gu + (size_t)pos * 2 * L.F;
   const float* up = g + L.F;
-  auto act8 = [&](int c, float (&v)[8]) {
+  const int sh = pf_convert_row<FP4, 8>(
+      L.F,
+      [&](int c, float (&v)[8]) {
 #pragma unroll
-    for (int i = 0; i < 8; i += 4) {
-      const v4f a = *reinterpret_cast<const v4f*>(g + c + i);
-      const v4f b = *reinterpret_cast<const v4f*>(up + c + i);
-      v[i] = silu(gs * a.x) * (us * b.x);
-      v[i + 1] = silu(gs * a.y) * (us * b.y);
-      v[i + 2] = silu(gs * a.z) * (us * b.z);
-      v[i + 3] = silu(gs * a.w) * (us * b.w);
-    }
-  };
-  int sh = 0;
-  if constexpr (FP4) {
-    float m = 0.f;
-    for (int c = 8 * ln; c < L.F; c += 512) {
-      float v[8];
-      act8(c, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-    }
-    sh = pf_shift(wave_max(m));
-  }
-  if (ln == 0) P.ae[pos] = sh;
-  for (int c = 8 * ln; c < L.F; c += 512) {
-    float v[8];
-    act8(c, v);
-    pf_store8<FP4>(P.act, (size_t)P.T * L.K * L.F, (size_t)pos * L.F + c, v, sh);
-  }
+        for (int i = 0; i < 8; i += 4) {
+          const v4f a = *reinterpret_cast<const v4f*>(g + c + i);
+          const v4f b = *reinterpret_cast<const v4f*>(up + c + i);
+          v[i] = silu(gs * a.x) * (us * b.x);
+          v[i + 1] = silu(gs * a.y) * (us * b.y);
+          v[i + 2] = silu(gs * a.z) * (us * b.z);
+          v[i + 3] = silu(gs * a.w) * (us * b.w);
+        }
+      },
+      [&](int c, const float (&v)[8], int sh) {
+        pf_store8<FP4>(P.act, (size_t)P.T * L.K * L.F, (size_t)pos * L.F + c, v, sh);
+      });
+  if (lane_id() == 0) P.ae[pos] = sh;
 }
 
 constexpr int kPfRows = 4 * 64;             // output rows per item
