@@ -45,10 +45,10 @@
 //     columns of one row, which serve both k-steps of the tile).  The k index
 //     of step j, lane group g is numbered (KT / 4) g + 8 j + (0..7) on both
 //     operands, which keeps every lane's part of a row one contiguous run.
-// The weights are streamed once per chunk (once per expert when it has at
-// most 128 slots); the items of one chunk are consecutive and an XCD runs a
-// contiguous range of items, so the chunk's inputs and the weights shared by
-// an expert's chunks are re-read from that XCD's L2.
+// The weights are streamed from HBM once per chunk (once per expert when it
+// has at most 128 slots).  The items of one chunk are consecutive and an XCD
+// runs a contiguous range of items, so the chunk's inputs, which every row
+// block of the chunk reads, are re-read from that XCD's L2.
 #pragma once
 #include "phases_dense.h"
 
