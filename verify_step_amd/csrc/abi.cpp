@@ -473,7 +473,7 @@ msk_status watchdog(void* ws) {
 
 // Workspace of the prefill expert FFN for n tokens (see msk::PfArgs).
 struct PfLayout {
-  size_t off, nchunk, chunk, perm, pos, pe, ue, ae, a, gu, act, y, total;
+  size_t off, nchunk, chunk, cur, perm, pos, pe, ue, ae, a, gu, act, y, total;
 };
 PfLayout pf_layout(const msk_layer_cfg& c, int n) {
   const size_t S = (size_t)n * c.top_k, E = c.n_experts, H = c.hidden, F = c.ffn_dim;
@@ -487,6 +487,7 @@ PfLayout pf_layout(const msk_layer_cfg& c, int n) {
   L.off = take((E + 1) * sizeof(int));
   L.nchunk = take(sizeof(int));
   L.chunk = take((S / msk::kPfChunk + E + 1) * sizeof(msk::PfChunk));
+  L.cur = take(E * sizeof(int));
   L.perm = take(S * sizeof(int));
   L.pos = take(S * sizeof(int));
   L.pe = take(S * sizeof(int));
@@ -730,6 +731,7 @@ msk_status msk_moe_prefill(const msk_layer_cfg* cfg, const msk_layer_weights* w,
   P.off = reinterpret_cast<int*>(base + lay.off);
   P.nchunk = reinterpret_cast<int*>(base + lay.nchunk);
   P.chunk = reinterpret_cast<msk::PfChunk*>(base + lay.chunk);
+  P.cur = reinterpret_cast<int*>(base + lay.cur);
   P.perm = reinterpret_cast<int*>(base + lay.perm);
   P.pos = reinterpret_cast<int*>(base + lay.pos);
   P.pe = reinterpret_cast<int*>(base + lay.pe);

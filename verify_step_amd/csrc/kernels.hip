@@ -1144,7 +1144,7 @@ static hipError_t launch_pf(const LayerArgs& L, const PfArgs& P, hipStream_t st)
 
 hipError_t launch_prefill(const LayerArgs& L, const PfArgs& P, const float* wts, const float* h,
                           float* out, hipStream_t st) {
-  const size_t rl = (3 * kMaxExperts + 1) * sizeof(int);
+  const size_t rl = (3 * kMaxExperts + 8) * sizeof(int);
   MSK_TRY(launch_b(kPhUnion, k_pf_route, 1, 1024, rl, st, L, P));
   if (L.edt == kNVFP4)
     MSK_TRY(launch_pf<true>(L, P, st));

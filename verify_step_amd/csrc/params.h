@@ -119,6 +119,7 @@ struct PfArgs {
   int* off;              // [E + 1] first grouped position of each expert; off[E] = slots placed
   int* nchunk;           // chunks listed
   PfChunk* chunk;        // [T K / kPfChunk + E] chunks, by expert
+  int* cur;              // [E] next grouped position of each expert (placement cursor)
   int* perm;             // [T K] slot at grouped position pos
   int* pos;              // [T K] grouped position of slot s (-1: not placed)
   int* pe;               // [T K] expert at grouped position pos

@@ -8,10 +8,12 @@
 // tradeoffs"), over NVFP4 or bf16 experts (brifing.si page, "Expert Weight
 // Quantization").  The slots (token t, choice j) are grouped by expert and
 // each expert's slots split into chunks of at most kPfChunk:
-//   route    count the slots per expert, place them grouped by expert (the
-//            order within an expert does not change any result), list chunks;
-//   gather   each token's input row u[t] in the matrix-product format, once
-//            (the gate/up product reads it through the slot's token);
+//   route    count the slots per expert, lay out their grouped positions by
+//            expert, list the chunks;
+//   gather   place each token's slots (a per-expert cursor: the order within
+//            an expert does not change any result) and write the token's
+//            input row u[t] in the matrix-product format, once (the gate/up
+//            product reads it through the slot's token);
 //   gate/up  gu[pos] = [W_g; W_u]_e u  (fp32), e the position's expert;
 //   swiglu   act[pos] = silu(g_g gu_gate) * (g_u gu_up), in the same format
 //            (g: NVFP4 matrix scales, else 1);
@@ -54,12 +56,14 @@
 
 namespace msk {
 
-// One workgroup: counts per expert (LDS atomics), offsets, chunks, placement.
-// lds: 3 * kMaxExperts + 1 ints.
+// One workgroup: counts per expert (LDS atomics), offsets and chunk counts
+// (prefix sums over the experts, one expert per thread of the first four
+// waves), the chunk list, and each expert's placement cursor.
+// lds: 3 * kMaxExperts + 8 ints.
 __device__ inline void pf_route(const LayerArgs& L, const PfArgs& P, int* lds) {
   int* cnt = lds;
   int* cur = lds + kMaxExperts;
-  int* co = lds + 2 * kMaxExperts;  // [E + 1] first chunk of each expert
+  int* co = lds + 2 * kMaxExperts;  // [E] first chunk of each expert
   const int S = P.T * L.K;
   for (int e = threadIdx.x; e < L.E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
@@ -68,18 +72,44 @@ __device__ inline void pf_route(const LayerArgs& L, const PfArgs& P, int* lds) {
     if (e >= 0 && e < L.E) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int o = 0, c = 0;
-    for (int e = 0; e < L.E; ++e) {
-      cur[e] = o;
-      co[e] = c;
-      P.off[e] = o;
-      o += cnt[e];
-      c += (cnt[e] + kPfChunk - 1) / kPfChunk;
+  static_assert(kMaxExperts <= 256, "one expert per thread of four waves");
+  int* wsum = lds + 3 * kMaxExperts;  // [4] slots, [4] chunks of each wave
+  const int x = threadIdx.x, ln = lane_id(), w = threadIdx.x >> 6;
+  int ps = 0, pc = 0;  // prefix sums of slots and of chunks
+  if (x < kMaxExperts) {
+    ps = x < L.E ? cnt[x] : 0;
+    pc = (ps + kPfChunk - 1) / kPfChunk;
+    // inclusive sums within the wave
+    for (int d = 1; d < 64; d <<= 1) {
+      const int a = __shfl_up(ps, d), b = __shfl_up(pc, d);
+      if (ln >= d) {
+        ps += a;
+        pc += b;
+      }
     }
-    co[L.E] = c;
-    P.off[L.E] = o;
-    *P.nchunk = c;
+    if (ln == 63) {
+      wsum[w] = ps;
+      wsum[4 + w] = pc;
+    }
+  }
+  __syncthreads();
+  if (x < kMaxExperts) {
+    for (int v = 0; v < w; ++v) {
+      ps += wsum[v];
+      pc += wsum[4 + v];
+    }
+    if (x < L.E) {
+      const int c0 = cnt[x];
+      const int o = ps - c0;  // first grouped position of expert x
+      cur[x] = o;
+      co[x] = pc - (c0 + kPfChunk - 1) / kPfChunk;
+      P.off[x] = o;
+      P.cur[x] = o;
+      if (x == L.E - 1) {
+        P.off[L.E] = ps;
+        *P.nchunk = pc;
+      }
+    }
   }
   __syncthreads();
   // an expert's slots in nc near-equal chunks (measured faster than chunks
@@ -90,18 +120,6 @@ __device__ inline void pf_route(const LayerArgs& L, const PfArgs& P, int* lds) {
       const int lo = n * c / nc, hi = n * (c + 1) / nc;
       P.chunk[co[e] + c] = PfChunk{e, cur[e] + lo, hi - lo};
     }
-  }
-  __syncthreads();
-  for (int s = threadIdx.x; s < S; s += blockDim.x) {
-    const int e = P.idx[s];
-    if (e < 0 || e >= L.E) {
-      P.pos[s] = -1;
-      continue;
-    }
-    const int p = atomicAdd(&cur[e], 1);
-    P.perm[p] = s;
-    P.pe[p] = e;
-    P.pos[s] = p;
   }
 }
 
@@ -181,8 +199,9 @@ __device__ __forceinline__ int pf_convert_row(int n, Produce&& produce8, Store&&
   return sh;
 }
 
-// One wave per token t: its input row u[t] in the product format, and its
-// power of two at the grouped position of each of its placed slots.
+// One wave per token t: its slots' grouped positions (lane j < k takes slot
+// j's from its expert's cursor), its input row u[t] in the product format,
+// and its power of two at each of those positions.
 template <bool FP4>
 __device__ inline void pf_gather(const LayerArgs& L, const PfArgs& P) {
   const int t = blockIdx.x * kWaves + wave_id();
@@ -200,9 +219,18 @@ __device__ inline void pf_gather(const LayerArgs& L, const PfArgs& P) {
       [&](int c, const float (&v)[8], int sh) {
         pf_store8<FP4>(P.a, (size_t)P.T * L.H, (size_t)t * L.H + c, v, sh);
       });
+  static_assert(kMaxTopK <= 64, "one lane per slot of a token");
   if (ln < L.K) {
-    const int p = P.pos[t * L.K + ln];
-    if (p >= 0) P.ue[p] = sh;
+    const int s = t * L.K + ln;
+    const int e = P.idx[s];
+    int p = -1;
+    if (e >= 0 && e < L.E) {
+      p = __hip_atomic_fetch_add(P.cur + e, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      P.perm[p] = s;
+      P.pe[p] = e;
+      P.ue[p] = sh;
+    }
+    P.pos[s] = p;
   }
 }
 
