@@ -17,7 +17,8 @@ inputs already resident in HBM.  Prints one JSON line:
 The prefill workloads (prefill-nvfp4, prefill-bf16) time msk_moe_prefill
 instead: one layer's expert FFN over 4096 tokens on the matrix cores; their
 line gives µs per call, achieved TFLOP/s of the two products (2 x slots x
-3 x hidden x FFN flops) and a roofline against the 2.5 PFLOP/s bf16 peak.
+3 x hidden x FFN flops) and a roofline against the 2.5 PFLOP/s dense fp16/bf16
+peak; dtype is fp16 for NVFP4 experts (decoded exactly to fp16), bf16 otherwise.
 
 With no --workload, every workload is measured and printed on a line of its
 own; the largest single-GPU decode/verify workload (verify-bf16-128k: 2 x 8 draft tokens
@@ -259,8 +260,9 @@ PREFILL = {"prefill-nvfp4": dict(expert="nvfp4", tokens=4096, seed=6),
            "prefill-bf16": dict(expert="bf16", tokens=4096, seed=7)}
 ALL_WORKLOADS = ["tiny-fp32", "decode-bf16", "stack4-nvfp4", "longctx-nvfp4", "deep32-nvfp4",
                  "prefill-nvfp4", "prefill-bf16", HEADLINE]
-MFMA_BF16_PEAK_TFLOPS = 2500.0
-PREFILL_METRIC = "µs per MoE layer prefill expert FFN + achieved TFLOP/s (% of bf16 matrix peak)"
+MFMA_F16_PEAK_TFLOPS = 2500.0
+PREFILL_METRIC = ("µs per MoE layer prefill expert FFN + achieved TFLOP/s "
+                  "(% of the dense fp16/bf16 matrix peak)")
 
 
 def prefill_accounting(spec, counts):
@@ -336,19 +338,20 @@ def measure_prefill(name, args):
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        # the products' input type: NVFP4 weights decoded to fp16, else bf16
+        "dtype": "fp16" if spec["expert_dtype"] == "nvfp4" else "bf16",
         "data": "synthetic",
         "config": {"workload": name, "tokens": T, "slots": slots, "hidden": H, "ffn": F,
                    "experts": E, "top_k": K, "expert_format": spec["expert_dtype"],
                    "distinct_experts": int((counts > 0).sum())},
         "tflops": round(total_flops / (ms * 1e-3) / 1e12, 1),
-        "tflops_frac": round(total_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "tflops_frac": round(total_flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
         "hbm_gbs_distinct_weights": round(distinct / (ms * 1e-3) / 1e9, 1),
         "weight_bytes_distinct": distinct,
         "weight_bytes_streamed": streamed,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "kernel": "k_pf_gemm", "phase": dom,
                      "flops_per_launch": flops[dom], "avg_launch_us": round(avg_us, 3),
                      "launches": timed[dom][1]},
