@@ -273,8 +273,10 @@ def prefill_accounting(spec, counts):
     slots = int(np.sum(counts))
     gu_b, dn_b = expert_bytes(spec)
     distinct = int((np.asarray(counts) > 0).sum()) * (gu_b + dn_b)
-    # each chunk of up to 128 of an expert's slots streams the expert's rows
-    streamed = int(((np.asarray(counts) + 127) // 128).sum()) * (gu_b + dn_b)
+    # each chunk of an expert's slots (up to 160 for NVFP4 experts, 128 for
+    # bf16 experts) streams the expert's rows
+    cmax = 160 if spec["expert_dtype"] == "nvfp4" else 128
+    streamed = int(((np.asarray(counts) + cmax - 1) // cmax).sum()) * (gu_b + dn_b)
     flops = {"gateup": 2.0 * slots * 2 * F * H, "down": 2.0 * slots * H * F}
     return flops, distinct, streamed
 

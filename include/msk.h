@@ -280,8 +280,9 @@ msk_status msk_set_spin_limit(uint32_t polls);
 /* Experts of a prefill batch: the same result as msk_expert_ffn, for up to
  * MSK_MAX_PREFILL_TOKENS tokens.  With many tokens per expert the gate/up and
  * down products are matrix products on the matrix cores: the slots (t, j) are
- * grouped by expert, and each chunk of up to 128 of an expert's slots meets
- * that expert's weights in one product with fp32 accumulation.  NVFP4 weights
+ * grouped by expert, and each chunk of an expert's slots (up to 160 for NVFP4
+ * experts, 128 for bf16 experts) meets that expert's weights in one product
+ * with fp32 accumulation.  NVFP4 weights
  * are decoded exactly to fp16 and meet fp16 inputs (u and the SwiGLU
  * activations, each slot's row scaled by a power of two: 11 significant
  * bits); bf16 weights meet two bf16 terms of each input (exact to about

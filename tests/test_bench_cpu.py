@@ -69,16 +69,23 @@ def test_distinct_experts_counted_once():
 
 
 def test_prefill_accounting_by_hand():
-    """Hidden 6144, FFN 2048, NVFP4 experts: 300 slots on expert 0 (three
-    chunks), 128 on expert 1 (one), 129 on expert 5 (two), none elsewhere."""
+    """Hidden 6144, FFN 2048: 300 slots on expert 0, 128 on expert 1, 161 on
+    expert 5, none elsewhere.  NVFP4 experts take chunks of up to 160 slots
+    (two, one and two chunks), bf16 experts chunks of up to 128 (three, one,
+    two)."""
     spec = _spec_only("stack4-nvfp4")
     counts = np.zeros(256, dtype=np.int64)
-    counts[[0, 1, 5]] = [300, 128, 129]
+    counts[[0, 1, 5]] = [300, 128, 161]
     flops, distinct, streamed = bench.prefill_accounting(spec, counts)
-    # gate and up: 2 flops x 557 slots x 4096 rows x 6144; down: x 6144 x 2048
-    assert flops["gateup"] == 2 * 557 * 4096 * 6144
-    assert flops["down"] == 2 * 557 * 6144 * 2048
+    # gate and up: 2 flops x 589 slots x 4096 rows x 6144; down: x 6144 x 2048
+    assert flops["gateup"] == 2 * 589 * 4096 * 6144
+    assert flops["down"] == 2 * 589 * 6144 * 2048
     one = 6_291_456 + 786_432 + 4          # one NVFP4 matrix of 2048 x 6144
+    assert distinct == 3 * 3 * one
+    assert streamed == (2 + 1 + 2) * 3 * one
+    spec = dict(spec, expert_dtype="bf16")
+    one = 2048 * 6144 * 2                  # one bf16 matrix
+    _, distinct, streamed = bench.prefill_accounting(spec, counts)
     assert distinct == 3 * 3 * one
     assert streamed == (3 + 1 + 2) * 3 * one
 

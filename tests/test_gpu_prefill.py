@@ -1,6 +1,7 @@
 """GPU parity of the prefill expert FFN (msk_moe_prefill, through the C ABI)
 against the oracle's expert FFN on the same seeded inputs: many tokens, the
-slots grouped by expert into chunks of up to 128 for the matrix cores (inputs
+slots grouped by expert into chunks of up to 160 (NVFP4 experts) or 128
+(bf16 experts) for the matrix cores (inputs
 as fp16 with a power of two per row for NVFP4 experts, bf16 for bf16
 experts).  Same tolerance as the other bf16/fp4 paths: the MoE delta out - h
 within 2e-2 of its RMS (plus one fp32 ulp of out)."""
@@ -59,12 +60,16 @@ def _check(name, out, h, ref, rows=None):
 
 
 # slots per expert: random 300 -> about 75 (chunks of 5 to 8 16-slot tiles),
-# 200 -> 50 (4 tiles), 100 -> 25 (2), 1 -> 1; skewed 300 -> 300 for each of 8
-# experts (three chunks of 100); repeats 70 -> 210, 210, 140 (two chunks each)
+# 200 -> 50 (4 tiles), 100 -> 25 (2), 1 -> 1; skewed T -> T for each of 8
+# experts: 300 -> two NVFP4 chunks of 150 (ten tiles, the last one ragged),
+# 160 -> one full chunk of ten tiles, 161 -> two chunks of 80 and 81, 40 -> one
+# bf16 chunk; repeats 70 -> 210, 210, 140 (two bf16 chunks each)
 CASES = [
     ("bf16", "random", 300, "small"),
     ("nvfp4", "random", 300, "small"),
     ("nvfp4", "skewed", 300, "small"),
+    ("nvfp4", "skewed", 160, "small"),
+    ("nvfp4", "skewed", 161, "odd"),
     ("bf16", "repeats", 70, "small"),
     ("nvfp4", "random", 1, "small"),
     ("nvfp4", "random", 200, "odd"),
@@ -125,8 +130,8 @@ def test_prefill_full_size(expert):
 @pytest.mark.parametrize("expert,routing", [("nvfp4", "random"), ("bf16", "skewed")])
 def test_prefill_max_tokens(expert, routing):
     """The largest call: 8192 tokens (65536 slots) at hidden 6144, 256 experts,
-    FFN 2048.  Random routing gives about 256 slots per expert (two or three
-    chunks each); skewed routing puts every token on experts 0..7 (64 chunks
+    FFN 2048.  Random routing gives about 256 slots per expert (two chunks
+    each); skewed routing puts every token on experts 0..7 (bf16: 64 chunks
     of 128 each).  The oracle recomputes six tokens."""
     print(f"[gpu-prefill] max tokens {expert} {routing}", flush=True)
     spec, w = _layer(expert, synth._BIG)

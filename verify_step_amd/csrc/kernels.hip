@@ -1108,8 +1108,8 @@ static hipError_t launch_ffn_tn(const LayerArgs& L, const StepArgs& S, const flo
 }
 
 // ------------------------------------------------- prefill expert FFN
-__global__ __launch_bounds__(1024) void k_pf_route(LayerArgs L, PfArgs P) {
-  pf_route(L, P, reinterpret_cast<int*>(msk_smem));
+__global__ __launch_bounds__(1024) void k_pf_route(LayerArgs L, PfArgs P, int cmax) {
+  pf_route(L, P, cmax, reinterpret_cast<int*>(msk_smem));
 }
 template <bool FP4>
 __global__ __launch_bounds__(kBlockThreads) void k_pf_gather(LayerArgs L, PfArgs P) {
@@ -1145,7 +1145,8 @@ static hipError_t launch_pf(const LayerArgs& L, const PfArgs& P, hipStream_t st)
 hipError_t launch_prefill(const LayerArgs& L, const PfArgs& P, const float* wts, const float* h,
                           float* out, hipStream_t st) {
   const size_t rl = (3 * kMaxExperts + 8) * sizeof(int);
-  MSK_TRY(launch_b(kPhUnion, k_pf_route, 1, 1024, rl, st, L, P));
+  const int cmax = L.edt == kNVFP4 ? PfFmt<true>::CHUNK : PfFmt<false>::CHUNK;
+  MSK_TRY(launch_b(kPhUnion, k_pf_route, 1, 1024, rl, st, L, P, cmax));
   if (L.edt == kNVFP4)
     MSK_TRY(launch_pf<true>(L, P, st));
   else

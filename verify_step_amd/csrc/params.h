@@ -106,10 +106,13 @@ constexpr int kSyncBytes = 16384;
 constexpr int kTopkCountWord = 1024;
 
 // Buffers of the prefill expert FFN (msk_moe_prefill; see phases_prefill.h).
-constexpr int kPfChunk = 128;  // most slots of one expert in one matrix-product item
+// Most slots of one expert in one matrix-product item: kPfChunkFp4 for NVFP4
+// experts, kPfChunk for bf16 experts (the smaller one sizes the chunk list).
+constexpr int kPfChunk = 128;
+constexpr int kPfChunkFp4 = 160;
 
 struct PfChunk {
-  int e, pos0, n;  // expert, first grouped position, slots (1..kPfChunk)
+  int e, pos0, n;  // expert, first grouped position, slots (1 .. the chunk limit)
 };
 
 struct PfArgs {

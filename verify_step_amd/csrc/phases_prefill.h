@@ -7,7 +7,8 @@
 // the prefill optimisations ("Agentic coding benchmark and serving
 // tradeoffs"), over NVFP4 or bf16 experts (brifing.si page, "Expert Weight
 // Quantization").  The slots (token t, choice j) are grouped by expert and
-// each expert's slots split into chunks of at most kPfChunk:
+// each expert's slots split into near-equal chunks of at most 160 (NVFP4
+// experts) or 128 (bf16 experts):
 //   route    count the slots per expert, lay out their grouped positions by
 //            expert, list the chunks;
 //   gather   place each token's slots (a per-expert cursor: the order within
@@ -32,15 +33,16 @@
 // run the experts in FP8; both formats keep far more of each input.  Sums are
 // fp32.
 //
-// Matrix product item: (chunk of up to 128 slots of expert e, 256 output
-// rows); each of the four waves owns 64 rows x all the chunk's slots
-// (4 x 8 accumulator tiles of 16 x 16).  Per k-tile (128 columns for NVFP4,
-// 64 for bf16, so that either tile of inputs is 32 KB), in a ring of three
-// tiles (two in flight while one is used):
+// Matrix product item: (chunk of expert e, 256 output rows); each of the
+// four waves owns 64 rows x all the chunk's slots (4 x TF accumulator tiles
+// of 16 x 16, TF 16-slot tiles: at most 10 for NVFP4, 8 for bf16, which is
+// what the register file holds).  Per k-tile of 64 columns, in a ring of
+// three tiles (two in flight while one is used; deeper rings measured
+// slower, as more loads in flight per CU lower what each one gets):
 //   - the chunk's input rows arrive in LDS by direct global->LDS loads, each
-//     row's 16-B pieces stored at piece ^ (row & 15) (bf16: row & 7) so an
-//     operand read (16 rows, one piece each) meets no bank conflict; every
-//     wave reads all of them;
+//     row's 16-B pieces stored at piece ^ (row & 7) so an operand read (16
+//     rows, one piece each) meets no bank conflict; every wave reads all of
+//     them;
 //   - NVFP4 weight rows (codes and block scales) arrive in the same ring slot
 //     by direct loads as well, each wave's own rows, and are decoded from LDS;
 //     bf16 weight rows go straight to registers (a lane holds 16 consecutive
@@ -48,10 +50,12 @@
 //     of step j, lane group g is numbered (KT / 4) g + 8 j + (0..7) on both
 //     operands, which keeps every lane's part of a row one contiguous run.
 // The weights are streamed from HBM once per chunk (once per expert when it
-// has at most 128 slots).  The items of one chunk are consecutive and an XCD
+// has at most 160 slots: at 4096 tokens, top-8 of 256, nearly every expert).  The items of one chunk are consecutive and an XCD
 // runs a contiguous range of items, so the chunk's inputs, which every row
 // block of the chunk reads, are re-read from that XCD's L2.
 #pragma once
+#include <utility>
+
 #include "phases_dense.h"
 
 namespace msk {
@@ -59,8 +63,8 @@ namespace msk {
 // One workgroup: counts per expert (LDS atomics), offsets and chunk counts
 // (prefix sums over the experts, one expert per thread of the first four
 // waves), the chunk list, and each expert's placement cursor.
-// lds: 3 * kMaxExperts + 8 ints.
-__device__ inline void pf_route(const LayerArgs& L, const PfArgs& P, int* lds) {
+// cmax: most slots per chunk.  lds: 3 * kMaxExperts + 8 ints.
+__device__ inline void pf_route(const LayerArgs& L, const PfArgs& P, int cmax, int* lds) {
   int* cnt = lds;
   int* cur = lds + kMaxExperts;
   int* co = lds + 2 * kMaxExperts;  // [E] first chunk of each expert
@@ -78,7 +82,7 @@ __device__ inline void pf_route(const LayerArgs& L, const PfArgs& P, int* lds) {
   int ps = 0, pc = 0;  // prefix sums of slots and of chunks
   if (x < kMaxExperts) {
     ps = x < L.E ? cnt[x] : 0;
-    pc = (ps + kPfChunk - 1) / kPfChunk;
+    pc = (ps + cmax - 1) / cmax;
     // inclusive sums within the wave
     for (int d = 1; d < 64; d <<= 1) {
       const int a = __shfl_up(ps, d), b = __shfl_up(pc, d);
@@ -102,7 +106,7 @@ __device__ inline void pf_route(const LayerArgs& L, const PfArgs& P, int* lds) {
       const int c0 = cnt[x];
       const int o = ps - c0;  // first grouped position of expert x
       cur[x] = o;
-      co[x] = pc - (c0 + kPfChunk - 1) / kPfChunk;
+      co[x] = pc - (c0 + cmax - 1) / cmax;
       P.off[x] = o;
       P.cur[x] = o;
       if (x == L.E - 1) {
@@ -113,9 +117,9 @@ __device__ inline void pf_route(const LayerArgs& L, const PfArgs& P, int* lds) {
   }
   __syncthreads();
   // an expert's slots in nc near-equal chunks (measured faster than chunks
-  // of kPfChunk and a last one with the rest)
+  // of cmax and a last one with the rest)
   for (int e = threadIdx.x; e < L.E; e += blockDim.x) {
-    const int n = cnt[e], nc = (n + kPfChunk - 1) / kPfChunk;
+    const int n = cnt[e], nc = (n + cmax - 1) / cmax;
     for (int c = 0; c < nc; ++c) {
       const int lo = n * c / nc, hi = n * (c + 1) / nc;
       P.chunk[co[e] + c] = PfChunk{e, cur[e] + lo, hi - lo};
@@ -265,31 +269,40 @@ __device__ inline void pf_swiglu(const LayerArgs& L, const PfArgs& P) {
 }
 
 constexpr int kPfRows = 4 * 64;             // output rows per item
-constexpr int kPfIn = kPfChunk * 256;        // bytes of one k-tile of inputs
-constexpr int kPfStages = 3;                 // k-tiles in the LDS ring
-
-// Per format: input terms, k columns per tile, loads per tile of one wave
-// besides its share of the input tile, bytes of one ring slot.
-//   NVFP4: a wave's 64 weight rows of a tile (64 x 64 B of e2m1 codes and
-//   64 x 8 B of e4m3 scales) come into the slot by direct global->LDS loads
-//   too: four 1-KB loads of codes (16 rows x 64 B each; a row's 16-B pieces
-//   stored at piece ^ ((row >> 2) & 3), so an operand read of 16 rows meets
-//   no bank conflict) and two 256-B loads of scales.
+// Per format: input terms, k columns per tile, ring slots, loads per tile of
+// one wave besides its share of the input tile, bytes of one ring slot.
+//   NVFP4: a wave's 64 weight rows of a tile (64 x 32 B of e2m1 codes and
+//   64 x 4 B of e4m3 scales) come into the slot by direct global->LDS loads
+//   too: two 1-KB loads of codes (32 rows each, row-major: an operand read of
+//   16 rows x 8 B is one contiguous 512 B, free of bank conflicts) and one
+//   256-B load of scales.
 //   bf16: a lane's 16 columns of four rows (32 B each) go straight to
 //   registers, two tiles ahead.
 template <bool FP4>
 struct PfFmt;
 template <>
 struct PfFmt<true> {
-  static constexpr int NTERM = 1, KT = 128, LOADS = 6;
-  static constexpr int CODES = kPfIn, SCALES = CODES + 4 * 4096, STAGE = SCALES + 4 * 512;
+  static constexpr int CHUNK = kPfChunkFp4, NTERM = 1, KT = 64, STAGES = 3, LOADS = 3;
+  static constexpr int IN = CHUNK * KT * 2 * NTERM;  // bytes of one k-tile of inputs
+  static constexpr int CODES = IN, SCALES = CODES + 4 * 2048, STAGE = SCALES + 4 * 256;
 };
 template <>
 struct PfFmt<false> {
-  static constexpr int NTERM = 2, KT = 64, LOADS = 8, STAGE = kPfIn;
+  static constexpr int CHUNK = kPfChunk, NTERM = 2, KT = 64, STAGES = 3, LOADS = 8;
+  static constexpr int IN = CHUNK * KT * 2 * NTERM, STAGE = IN;
 };
 template <bool FP4>
-constexpr int pf_lds() { return kPfStages * PfFmt<FP4>::STAGE; }
+constexpr int pf_lds() { return PfFmt<FP4>::STAGES * PfFmt<FP4>::STAGE; }
+
+// f(IC<0>{}), ..., f(IC<N - 1>{})
+template <class F, int... I>
+__device__ __forceinline__ void pf_unroll(F&& f, std::integer_sequence<int, I...>) {
+  (f(IC<I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void pf_for(F&& f) {
+  pf_unroll(f, std::make_integer_sequence<int, N>{});
+}
 
 // bf16 weight registers of one tile: lane (r, g) holds columns 16 g .. + 15
 // of rows 16 rf + r.
@@ -317,10 +330,11 @@ template <bool FP4, bool GU, int TF>
 __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, int rb,
                         uint8_t* lds) {
   using Fm = PfFmt<FP4>;
-  constexpr int KT = Fm::KT, NTERM = Fm::NTERM, J = KT / 32;
+  constexpr int KT = Fm::KT, NTERM = Fm::NTERM, J = KT / 32, NS = Fm::STAGES, LA = NS - 1;
   constexpr int RB = KT * 2, PR = RB / 16, RPI = 1024 / RB;  // row bytes, pieces, rows per 1 KB
   constexpr int LPP = 16 * TF * RB / 1024;                     // 1-KB loads per term plane
-  constexpr int PLANE = kPfChunk * RB;                         // LDS bytes per term plane
+  constexpr int NL = NTERM * LPP, NLW = (NL + 3) / 4;          // 1-KB input loads: all, per wave
+  constexpr int PLANE = Fm::CHUNK * RB;                        // LDS bytes per term plane
   const int N = GU ? 2 * L.F : L.H, K = GU ? L.H : L.F;
   const int ln = lane_id(), wv = wave_id(), r = ln & 15, g = ln >> 4;
   const int tiles = K / KT;
@@ -351,25 +365,25 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
     }
   };
   const int wr0 = active ? r0 : 0;  // idle waves fetch rows they never use
-  // NVFP4: this lane's rows in the code loads (16 i + ln / 4) and the scale
-  // loads (32 q + ln / 2); bf16: rows 16 rf + r
+  // NVFP4: this lane's rows in the two code loads (32 i + ln / 2, 16-B
+  // piece ln & 1) and in the scale load (ln); bf16: rows 16 rf + r
   const uint8_t* wp[4];
-  const uint8_t* sp[2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint8_t* sc;
-    wrow(wr0 + 16 * i + (FP4 ? ln >> 2 : r), wp[i], sc);
-    if constexpr (FP4)
-      wp[i] += 16 * ((ln & 3) ^ ((ln >> 4) & 3));  // the piece that belongs in this lane's slot
-    else
-      wp[i] += 32 * g;
-  }
+  const uint8_t* sp = nullptr;
   if constexpr (FP4) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint8_t* w;
-      wrow(wr0 + 32 * q + (ln >> 1), w, sp[q]);
-      sp[q] += 4 * (ln & 1);
+    for (int i = 0; i < 2; ++i) {
+      const uint8_t* sc;
+      wrow(wr0 + 32 * i + (ln >> 1), wp[i], sc);
+      wp[i] += 16 * (ln & 1);
+    }
+    const uint8_t* w;
+    wrow(wr0 + ln, w, sp);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint8_t* sc;
+      wrow(wr0 + 16 * i + r, wp[i], sc);
+      wp[i] += 32 * g;
     }
   }
   auto load_w = [&](int tau, PfWbf& W) {
@@ -383,22 +397,22 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
     if constexpr (FP4) {
       uint8_t* st = lds + buf * Fm::STAGE;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds(wp[i] + (size_t)tau * 64,
-                                         st + Fm::CODES + wv * 4096 + i * 1024, 16, 0, 0);
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        __builtin_amdgcn_global_load_lds(sp[q] + (size_t)tau * 8,
-                                         st + Fm::SCALES + wv * 512 + q * 256, 4, 0, 0);
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(wp[i] + (size_t)tau * (KT / 2),
+                                         st + Fm::CODES + wv * 2048 + i * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(sp + (size_t)tau * (KT / 16), st + Fm::SCALES + wv * 256,
+                                       4, 0, 0);
     }
   };
   // input rows: u by token (gate/up), act by grouped position (down)
   const unsigned short* in = GU ? P.a : P.act;
   const size_t in_plane = GU ? (size_t)P.T * L.H : (size_t)P.T * L.K * L.F;
-  const unsigned short* isrc[TF];  // this lane's row and piece in 1-KB load m
+  // 1-KB input load m of this wave is load (wv + 4 m) % NL of the tile
+  // (with two loads, waves 2 and 3 repeat those of waves 0 and 1)
+  const unsigned short* isrc[NLW];  // this lane's row and piece in its load m
 #pragma unroll
-  for (int m = 0; m < TF; ++m) {
-    const int q = wv + 4 * m;          // 1-KB load q of the NTERM LPP
+  for (int m = 0; m < NLW; ++m) {
+    const int q = (wv + 4 * m) % NL;
     const int pl = q / LPP, ql = q - pl * LPP;
     const int R = ql * RPI + ln / PR;  // chunk row this lane fills, slot ln % PR
     const int tk = R < ch.n ? R : ch.n - 1;
@@ -409,8 +423,8 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
   auto issue_in = [&](int tau, int buf) {
     uint8_t* bt = lds + buf * Fm::STAGE;
 #pragma unroll
-    for (int m = 0; m < TF; ++m) {
-      const int q = wv + 4 * m;
+    for (int m = 0; m < NLW; ++m) {
+      const int q = (wv + 4 * m) % NL;
       const int pl = q / LPP, ql = q - pl * LPP;
       __builtin_amdgcn_global_load_lds(isrc[m] + (size_t)tau * KT, bt + pl * PLANE + ql * 1024,
                                        16, 0, 0);
@@ -423,22 +437,19 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
     for (int tf = 0; tf < TF; ++tf) acc[rf][tf] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const PfWbf& W, int buf) {
     const uint8_t* bt = lds + buf * Fm::STAGE;
-    v4u cw[4];
-    f16x2 sc[4][2];
+    v2u cw[4];
+    f16x2 sc[4];
     if constexpr (FP4) {
-      // this wave's codes and scales of the tile
+      // this wave's codes and scales of the tile: lane group g holds columns
+      // 16 g .. 16 g + 15 of its row (8 B of codes, block scale g)
 #pragma unroll
       for (int rf = 0; rf < 4; ++rf) {
         const int row = 16 * rf + r;
-        cw[rf] = *reinterpret_cast<const v4u*>(bt + Fm::CODES + wv * 4096 + row * 64 +
-                                               ((g ^ ((r >> 2) & 3)) * 16));
-        const int sv = (int)(*reinterpret_cast<const unsigned*>(
-                                 bt + Fm::SCALES + wv * 512 + row * 8 + 4 * (g >> 1)) >>
-                             (16 * (g & 1)));
-        const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sv, 0);
-        const _Float16 s1 = (_Float16)__builtin_amdgcn_cvt_f32_fp8(sv, 1);
-        sc[rf][0] = f16x2{s0, s0};
-        sc[rf][1] = f16x2{s1, s1};
+        cw[rf] = *reinterpret_cast<const v2u*>(bt + Fm::CODES + wv * 2048 + row * 32 + g * 8);
+        const unsigned sv =
+            *reinterpret_cast<const unsigned*>(bt + Fm::SCALES + wv * 256 + row * 4);
+        const _Float16 s0 = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)(sv >> (8 * g)), 0);
+        sc[rf] = f16x2{s0, s0};
       }
     }
 #pragma unroll
@@ -453,7 +464,7 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
 #pragma unroll
       for (int rf = 0; rf < 4; ++rf) {
         if constexpr (FP4) {
-          const f16x8 a = pf_weights(cw[rf][j], sc[rf][j >> 1]);
+          const f16x8 a = pf_weights(cw[rf][j], sc[rf]);
 #pragma unroll
           for (int tf = 0; tf < TF; ++tf)
             acc[rf][tf] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -470,15 +481,16 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
       }
     }
   };
-  // Tile tau, ring slot S = tau % 3: wait for its loads (tile tau + 1's may
-  // stay in flight), meet the other waves (so every wave is done with tile
-  // tau - 1, whose slot is refilled), fetch tile tau + 2 (LA) and use tile
-  // tau.  Every wave issues the same loads at every step (idle waves fetch
-  // rows they never use) and the loads are never conditional inside the
-  // loop, so the compiler's own counter bookkeeping stays exact and adds no
-  // wait that would drain the loads in flight.
-  PfWbf W[kPfStages];  // bf16 weight registers (unused for NVFP4)
-  constexpr int PER = TF + Fm::LOADS;  // loads per tile of every wave
+  // Tile tau, ring slot S = tau % NS: wait for its loads (those of the
+  // LA - 1 tiles after it may stay in flight), meet the other waves (so every
+  // wave is done with tile tau - 1, whose slot is refilled), fetch tile
+  // tau + LA and use tile tau.  Every wave issues the same loads at every
+  // step (idle waves fetch rows they never use) and the loads are never
+  // conditional inside the loop, so the compiler's own counter bookkeeping
+  // stays exact and adds no wait that would drain the loads in flight.
+  PfWbf W[NS];  // bf16 weight registers (unused for NVFP4)
+  constexpr int PER = NLW + Fm::LOADS;  // loads per tile of every wave
+  static_assert((LA - 1) * PER < 64, "loads in flight within the counter's range");
   auto fetch = [&](auto S_, int tau) {
     constexpr int S = decltype(S_)::value;
     issue_in(tau, S);
@@ -487,14 +499,13 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
     else
       load_w(tau, W[S]);
   };
-  auto step = [&](auto S_, auto LA_, auto LAST_, int tau) {
+  // FETCH: whether this step fetches ahead; AFTER: tiles whose loads may
+  // still be in flight after this one's
+  auto step = [&](auto S_, auto FETCH_, auto AFTER_, int tau) {
     constexpr int S = decltype(S_)::value;
-    if constexpr (decltype(LAST_)::value)
-      wait_vm<0>();
-    else
-      wait_vm<PER>();
+    wait_vm<decltype(AFTER_)::value * PER>();
     lds_barrier();
-    if constexpr (decltype(LA_)::value) fetch(IC<(S + 2) % kPfStages>{}, tau + 2);
+    if constexpr (decltype(FETCH_)::value) fetch(IC<(S + LA) % NS>{}, tau + LA);
     if (active) compute(W[S], S);
   };
   using T_ = IC<1>;
@@ -505,37 +516,30 @@ __device__ void pf_item(const LayerArgs& L, const PfArgs& P, const PfChunk ch, i
   // at a step of the loop below).  One drain here, before anything of this
   // item is in flight, costs only the stores' round trip.
   wait_vm<0>();
-  fetch(IC<0>{}, 0);
-  fetch(IC<1>{}, tiles > 1 ? 1 : 0);  // one tile: a second copy, never used
-  if (tiles >= 2) {
-    const int nla = tiles - 2;  // steps that fetch ahead: 0 .. tiles - 3
+  // tiles 0 .. LA - 1 (fewer tiles: copies of the last, never used)
+  pf_for<LA>([&](auto I) { fetch(I, decltype(I)::value < tiles ? decltype(I)::value : tiles - 1); });
+  if (tiles >= LA) {
+    const int nla = tiles - LA;  // steps that fetch ahead: 0 .. nla - 1
     int tau = 0;
-    for (; tau + 3 <= nla; tau += 3) {
-      step(IC<0>{}, T_{}, F_{}, tau);
-      step(IC<1>{}, T_{}, F_{}, tau + 1);
-      step(IC<2>{}, T_{}, F_{}, tau + 2);
-    }
-    if (tau < nla) {
-      step(IC<0>{}, T_{}, F_{}, tau);
-      if (tau + 1 < nla) step(IC<1>{}, T_{}, F_{}, tau + 1);
-    }
-    // the last two tiles, in ring slots (tiles - 2) % 3 and (tiles - 1) % 3
-    switch (nla % kPfStages) {
-      case 0:
-        step(IC<0>{}, F_{}, F_{}, tiles - 2);
-        step(IC<1>{}, F_{}, T_{}, tiles - 1);
-        break;
-      case 1:
-        step(IC<1>{}, F_{}, F_{}, tiles - 2);
-        step(IC<2>{}, F_{}, T_{}, tiles - 1);
-        break;
-      default:
-        step(IC<2>{}, F_{}, F_{}, tiles - 2);
-        step(IC<0>{}, F_{}, T_{}, tiles - 1);
-        break;
-    }
+    for (; tau + NS <= nla; tau += NS)
+      pf_for<NS>([&](auto I) { step(I, T_{}, IC<LA - 1>{}, tau + decltype(I)::value); });
+    // R more steps that fetch ahead, in slots 0 .. R - 1, then the last LA
+    // tiles, in slots R .. R + LA - 1 (mod NS)
+    const int rem = nla - tau;
+    pf_for<NS>([&](auto R_) {
+      constexpr int R = decltype(R_)::value;
+      if (rem == R) {
+        pf_for<R>([&](auto I) { step(I, T_{}, IC<LA - 1>{}, tau + decltype(I)::value); });
+        pf_for<LA>([&](auto I) {
+          constexpr int i = decltype(I)::value;
+          step(IC<(R + i) % NS>{}, F_{}, IC<LA - 1 - i>{}, tau + R + i);
+        });
+      }
+    });
   } else {
-    step(IC<0>{}, F_{}, T_{}, 0);
+    pf_for<LA>([&](auto I) {
+      if (decltype(I)::value < tiles) step(I, F_{}, IC<0>{}, decltype(I)::value);
+    });
   }
   lds_barrier();  // every wave is done with the ring before the next item fills it
   if (!active) return;
@@ -583,7 +587,9 @@ __device__ void pf_gemm(const LayerArgs& L, const PfArgs& P, uint8_t* lds) {
     const PfChunk ch = P.chunk[c];
     const int rb = (int)(item - c * n_rb);
     const int ntf = (ch.n + 15) >> 4;
-    if (ntf > 6)
+    if (FP4 && ntf > 8)
+      pf_item<FP4, GU, FP4 ? 10 : 8>(L, P, ch, rb, lds);
+    else if (ntf > 6)
       pf_item<FP4, GU, 8>(L, P, ch, rb, lds);
     else if (ntf > 4)
       pf_item<FP4, GU, 6>(L, P, ch, rb, lds);
