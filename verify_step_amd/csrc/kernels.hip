@@ -51,6 +51,23 @@ __global__ __launch_bounds__(kBlockThreads) void k_attn(LayerArgs L, StepArgs S)
   phase_attn<KDT, D>(L, S, P, msk_smem + align_up(sizeof(AttnPlan), 16), blockIdx.x, gridDim.x);
 }
 
+// Vector attention items whose group's last arrival also sums the group's
+// partials into attn_o (no combine launch); workgroup 0 writes the windows.
+template <int KDT, int D>
+__global__ __launch_bounds__(kBlockThreads) void k_attn_c(LayerArgs L, StepArgs S) {
+  static_assert(CombineLds<D>::BYTES <= AttnGeom<KDT, D>::LDS_ITEM, "combine LDS");
+  AttnPlan* P = reinterpret_cast<AttnPlan*>(msk_smem);
+  build_plan(L, S, P);
+  uint8_t* lds = msk_smem + align_up(sizeof(AttnPlan), 16);
+  const int n_items = P->item0[S.n_req];
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    attn_item<KDT, D, CohSt>(L, S, P, item, lds);
+    combine_if_last<D>(L, S, P, item, S.sync + kAttnCountWord, lds);
+    __syncthreads();
+  }
+  if (blockIdx.x == 0 && S.win_out != nullptr) write_windows(L, S, S.win_out);
+}
+
 // The tile fetch is one tile deep per workgroup, so the bytes in flight come
 // from resident workgroups: e4m3 caches (16 KB tiles) run three waves per
 // SIMD; bf16 tiles are twice the registers and keep the compiler's choice.
@@ -880,15 +897,25 @@ static hipError_t launch_attn_mfma(const LayerArgs& L, const StepArgs& S, hipStr
   return launch_attn_mfma_d<kE4M3, 128>(L, S, st);
 }
 
-// The attention partials (matrix-core or vector kernel).
-static hipError_t launch_attn_kernel(const LayerArgs& L, const StepArgs& S, hipStream_t st) {
+// Most chunks per group for which the vector attention items sum their own
+// partials.
+constexpr int kFuseChunks = 8;
+
+// The attention partials (matrix-core or vector kernel); with `fused` the
+// vector kernel also sums them (k_attn_c).
+static hipError_t launch_attn_kernel(const LayerArgs& L, const StepArgs& S, hipStream_t st,
+                                     bool fused) {
   if (L.attn_nw > 0) return launch_attn_mfma(L, S, st);
   const size_t alds = attn_lds_bytes(L.kdt, L.D);
   const int agrid = L.n_items < 8 * cu_count() ? L.n_items : 8 * cu_count();
-#define MSK_ATTN(K, DD)                                                           \
-  if (L.kdt == K && L.D == DD) {                                                  \
-    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_attn<K, DD>), alds)); \
-    return launch(kPhAttn, k_attn<K, DD>, agrid, alds, st, L, S);                \
+#define MSK_ATTN(K, DD)                                                             \
+  if (L.kdt == K && L.D == DD) {                                                    \
+    if (fused) {                                                                    \
+      MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_attn_c<K, DD>), alds)); \
+      return launch(kPhAttn, k_attn_c<K, DD>, agrid, alds, st, L, S);                \
+    }                                                                               \
+    MSK_TRY(set_lds_limit(reinterpret_cast<const void*>(&k_attn<K, DD>), alds));   \
+    return launch(kPhAttn, k_attn<K, DD>, agrid, alds, st, L, S);                  \
   }
   MSK_ATTN(kF32, 32) MSK_ATTN(kF32, 64) MSK_ATTN(kF32, 128)
   MSK_ATTN(kBF16, 32) MSK_ATTN(kBF16, 64) MSK_ATTN(kBF16, 128)
@@ -934,9 +961,25 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
       MSK_NV_CASES(nv, MSK_TRY(launch_x(kPhQkv, k_qkv<kF32, NV>, qgrid, rs_lds, st, L, S, x)))
   }
 
-  MSK_TRY(launch_attn_kernel(L, S, st));
   const bool mm = dense_on_mfma(L, S, L.H, L.Hq * L.D);
-  {
+  // Vector items (a group holds at most kRowGroup rows) over a few chunks per
+  // group: the last item of a group sums its partials.  Its tail (waiting
+  // for the partial stores, the counter's round trip, then reading every
+  // chunk back) grows with the chunks: over 33 chunks of six rows it cost
+  // more than a combine launch.  Matrix-core items, whose groups hold up to
+  // 64 rows, and groups of more chunks leave the sums to a combine launch
+  // spread over every (token, q head).
+  int most = 0;
+  for (int b = 0; b < S.n_req; ++b) {
+    int base, end;
+    req_span(S.kv_len[b], S.Tr, L.window, base, end);
+    const int n = ceil_div(end - base, L.chunk);
+    most = n > most ? n : most;
+  }
+  const bool fused = L.attn_nw == 0 && !mm && most <= kFuseChunks &&
+                     S.n_req * L.Hkv * L.nrg <= kAttnCountMax;
+  MSK_TRY(launch_attn_kernel(L, S, st, fused));
+  if (!fused) {
     const size_t lds = align_up(sizeof(AttnPlan), 16) + (size_t)kWaves * (L.D + 1) * sizeof(float);
     const int rows = S.T * L.Hq;  // one workgroup per (token, q head)
     MSK_TRY(launch_x(kPhCombine, k_combine, rows < 8192 ? rows : 8192, lds, st, L, S, S.win_out,
@@ -1252,6 +1295,9 @@ static hipError_t launch_persistent(const LayerArgs* Ls, const StepArgs& S, hipS
 
 bool persistent_supported(const LayerArgs* Ls, const StepArgs& S) {
   if (S.T != 1) return false;
+  // its attention phase runs the vector items
+  for (int l = 0; l < S.n_layers; ++l)
+    if (Ls[l].attn_nw != 0) return false;
   for (int l = 1; l < S.n_layers; ++l)
     if (Ls[l].ddt != Ls[0].ddt || Ls[l].edt != Ls[0].edt || Ls[l].kdt != Ls[0].kdt ||
         Ls[l].D != Ls[0].D)

@@ -100,10 +100,16 @@ __host__ __device__ inline int dense_slices(int N, int K) {
 // The workspace starts with kSyncBytes of words that every entry point finds
 // at the same place and that are zero between calls: the persistent kernel's
 // tree barrier (word 0 its generation, word 1 the error flag, word 32 and
-// words 64 + 32 g for g < 8 its arrival counters) and, at kTopkCountWord, the
-// arrival counter of the several-token top-k kernel.
+// words 64 + 32 g for g < 8 its arrival counters), at kTopkCountWord, the
+// arrival counter of the several-token top-k kernel, and the attention
+// counters below.
 constexpr int kSyncBytes = 16384;
 constexpr int kTopkCountWord = 1024;
+// Words kAttnCountWord .. + kAttnCountMax: the attention items' arrival
+// counters, one per (request, kv head, row group), when the last item of a
+// group sums the group's partials.
+constexpr int kAttnCountWord = 2048;
+constexpr int kAttnCountMax = kSyncBytes / 4 - kAttnCountWord;
 
 // Buffers of the prefill expert FFN (msk_moe_prefill; see phases_prefill.h).
 // Most slots of one expert in one matrix-product item: kPfChunkFp4 for NVFP4

@@ -188,14 +188,13 @@ struct AttnGeom {
   static constexpr int LPP = D / EPLV;        // lanes per position (V)
   static constexpr int PPI = 64 / LPP;        // positions per V step
   static constexpr int NVL = 64 / PPI;        // V steps per block
-  // per-workgroup LDS: q rows, K tile, V tile, weights, new-key norms, windows
+  // per-workgroup LDS: q rows, K tile, V tile, weights, windows
   static constexpr int LDS_Q = kRowGroup * D * 4;
   static constexpr int LDS_K = TILE;
   static constexpr int LDS_V = TILE;
   static constexpr int LDS_E = kRowGroup * 64 * 4;
-  static constexpr int LDS_RK = kMaxTok * 4;
   static constexpr int LDS_WIN = kRowGroup * 8;
-  static constexpr int LDS_ITEM = LDS_Q + LDS_K + LDS_V + LDS_E + LDS_RK + LDS_WIN;
+  static constexpr int LDS_ITEM = LDS_Q + LDS_K + LDS_V + LDS_E + LDS_WIN;
   static constexpr int RPW = kRowGroup / kWaves;  // query rows per wave
 };
 
@@ -261,8 +260,7 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
   uint8_t* kt = wl + Gm::LDS_Q;
   uint8_t* vt = kt + Gm::LDS_K;
   float* et = reinterpret_cast<float*>(vt + Gm::LDS_V);
-  float* rk = et + kRowGroup * 64;
-  int* win = reinterpret_cast<int*>(rk + kMaxTok);
+  int* win = reinterpret_cast<int*>(et + kRowGroup * 64);
 
   const int ln = lane_id(), wv = wave_id();
   int b = 0;
@@ -285,7 +283,77 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
   uint8_t* vc = L.vc + head_off * RB;
   const bool writer = (rg == 0);
 
-  // this wave's query rows, normalised and pre-scaled, and their windows
+  // positions before the group's earliest window start (that of its first
+  // row's token) are never visible
+  const int lo_min = L.window > 0 ? (Lb + m0 / G - L.window + 1 > 0 ? Lb + m0 / G - L.window + 1 : 0)
+                                  : 0;
+  // cached rows of one 64-position block straight into the LDS tiles, the
+  // 1-KB loads dealt over the waves.  Lane l of load i carries tile bytes
+  // [i KB + 16 l, +16), i.e. row (1024 i + 16 l) / RB; only rows that are
+  // visible and already cached are fetched.
+  auto issue_tiles = [&](int pb, int npos) {
+#pragma unroll
+    for (int i0 = 0; i0 < NLD; i0 += kWaves) {
+      const int i = i0 + wv;
+      const int off = i * 1024 + ln * 16;
+      const int pos = pb + off / RB;
+      if (i < NLD && pos < pb + npos && pos >= lo_min && pos < Lb) {
+        __builtin_amdgcn_global_load_lds(kc + (size_t)pb * RB + off, kt + i * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vc + (size_t)pb * RB + off, vt + i * 1024, 16, 0, 0);
+      }
+    }
+  };
+
+  // The step's own rows in block [pb, pb + npos) (positions >= kv_len),
+  // rebuilt from the QKV output into the LDS tiles: k QK-normalised, both
+  // cast to the cache format.  Wave w takes the tokens t = w mod kWaves, lane
+  // l < CPR the row's 16-byte chunk l.  Their loads follow the block's tile
+  // loads, so one wait covers both.
+  auto own_rows = [&](int pb, int npos) {
+    const int t0 = pb > Lb ? pb - Lb : 0;
+    const int t1 = pb + npos - Lb < S.Tr ? pb + npos - Lb : S.Tr;
+    const int d0 = ln * EPC;
+    const bool act = ln < CPR;
+    for (int t = t0 + wv; t < t1; t += kWaves) {
+      const float* kq = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + (size_t)j * D + (act ? d0 : 0);
+      const float* vq = kq + NK;
+      float fk[EPC], fv[EPC], gk[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        fk[e] = act ? MP::ld(&kq[e]) : 0.f;
+        fv[e] = act ? MP::ld(&vq[e]) : 0.f;
+        gk[e] = act ? L.k_norm[d0 + e] : 0.f;
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) ss += fk[e] * fk[e];
+      const float r = 1.0f / sqrtf(wave_sum(ss) / (float)D + L.eps);
+      if (act) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) gk[e] = fk[e] * r * gk[e];
+        const int row = Lb + t - pb;
+        *reinterpret_cast<v4u*>(kt + row * RB + ln * 16) = encode16<KDT>(gk);
+        *reinterpret_cast<v4u*>(vt + row * RB + ln * 16) = encode16<KDT>(fv);
+      }
+    }
+  };
+  // ... and, by the row-group-0 item, from the LDS tiles into the cache
+  auto store_own_rows = [&](int pb, int npos) {
+    const int t0 = pb > Lb ? pb - Lb : 0;
+    const int t1 = pb + npos - Lb < S.Tr ? pb + npos - Lb : S.Tr;
+    if (!writer || ln >= CPR) return;
+    for (int t = t0 + wv; t < t1; t += kWaves) {
+      const int row = Lb + t - pb;
+      *reinterpret_cast<v4u*>(kc + (size_t)(Lb + t) * RB + ln * 16) =
+          *reinterpret_cast<const v4u*>(kt + row * RB + ln * 16);
+      *reinterpret_cast<v4u*>(vc + (size_t)(Lb + t) * RB + ln * 16) =
+          *reinterpret_cast<const v4u*>(vt + row * RB + ln * 16);
+    }
+  };
+
+  // this wave's query rows, normalised and pre-scaled, and their windows.
+  // The first block's tiles and own rows are loaded right after the query
+  // values, so the three arrive in one round trip.
   constexpr int QD = (D + 63) / 64;
   const v2f gq2 = gain_pair(L.q_norm, D), gk2 = gain_pair(L.k_norm, D);
   {
@@ -302,6 +370,10 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
         qv[r][i] = (m0 + mm < M && d < D) ? MP::ld(&q[d]) : 0.f;
       }
     }
+    if (p0 < p1) {
+      issue_tiles(p0, p1 - p0 < 64 ? p1 - p0 : 64);
+      own_rows(p0, p1 - p0 < 64 ? p1 - p0 : 64);
+    }
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const int mm = wv * RPW + r;
@@ -314,7 +386,7 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
 #pragma unroll
       for (int i = 0; i < QD; ++i) {
         const int d = ln + 64 * i;
-        if (d < D) qs[mm * D + d] = m < M ? qv[r][i] * rr * L.q_norm[d] * L.qscale : 0.f;
+        if (d < D) qs[mm * D + d] = m < M ? qv[r][i] * rr * (i == 0 ? gq2.x : gq2.y) * L.qscale : 0.f;
       }
       if (ln == 0) {
         const int t = m / G;
@@ -324,35 +396,7 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
       }
     }
   }
-  // 1/rms of the step's new keys that fall in this chunk (wave 0)
-  const int tn0 = p0 - Lb > 0 ? p0 - Lb : 0;
-  const int tn1 = p1 - Lb < S.Tr ? p1 - Lb : S.Tr;
-  if (wv == 0) {
-    for (int t0 = tn0; t0 < tn1; t0 += 8) {
-      float kv[8][QD];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int tq = t0 + q < tn1 ? t0 + q : tn1 - 1;
-        const float* k = S.qkv + (size_t)(b * S.Tr + tq) * NR + NQ + (size_t)j * D;
-#pragma unroll
-        for (int i = 0; i < QD; ++i) {
-          const int d = ln + 64 * i;
-          kv[q][i] = (t0 + q < tn1 && d < D) ? MP::ld(&k[d]) : 0.f;
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < QD; ++i) ss += kv[q][i] * kv[q][i];
-        ss = wave_sum(ss);
-        if (ln == 0 && t0 + q < tn1) rk[t0 + q] = 1.0f / sqrtf(ss / (float)D + L.eps);
-      }
-    }
-  }
-  __syncthreads();
-  // positions before the group's earliest window start are never visible
-  const int lo_min = win[0];
+  lds_barrier();
   const float shift = layer_shift(L.shift, gq2, gk2, D);
 
   float lsum[RPW];
@@ -367,45 +411,9 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
 
   for (int pb = p0; pb < p1; pb += 64) {
     const int npos = p1 - pb < 64 ? p1 - pb : 64;
-    // cached rows of this block straight into the LDS tiles, the 1-KB loads
-    // dealt over the waves.  Lane l of load i carries tile bytes
-    // [i KB + 16 l, +16), i.e. row (1024 i + 16 l) / RB; only rows that are
-    // visible and already cached are fetched.
-#pragma unroll
-    for (int i0 = 0; i0 < NLD; i0 += kWaves) {
-      const int i = i0 + wv;
-      const int off = i * 1024 + ln * 16;
-      const int pos = pb + off / RB;
-      if (i < NLD && pos < pb + npos && pos >= lo_min && pos < Lb) {
-        __builtin_amdgcn_global_load_lds(kc + (size_t)pb * RB + off, kt + i * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vc + (size_t)pb * RB + off, vt + i * 1024, 16, 0, 0);
-      }
-    }
-    // the step's own rows (positions >= kv_len): rebuilt and stored
-    if (pb + npos > Lb) {
-      for (int q = threadIdx.x; q < 64 * CPR; q += blockDim.x) {
-        const int row = q / CPR, col = q - (q / CPR) * CPR;
-        const int pos = pb + row;
-        if (row < npos && pos >= Lb) {
-          const int t = pos - Lb;
-          const int d0 = col * EPC;
-          const float* kq = S.qkv + (size_t)(b * S.Tr + t) * NR + NQ + (size_t)j * D + d0;
-          const float* vq = kq + NK;
-          float fk[16], fv[16];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            fk[e] = e < EPC ? MP::ld(&kq[e]) * rk[t] * L.k_norm[d0 + e] : 0.f;
-            fv[e] = e < EPC ? MP::ld(&vq[e]) : 0.f;
-          }
-          const v4u ek = encode16<KDT>(fk), ev = encode16<KDT>(fv);
-          *reinterpret_cast<v4u*>(kt + row * RB + col * 16) = ek;
-          *reinterpret_cast<v4u*>(vt + row * RB + col * 16) = ev;
-          if (writer) {
-            *reinterpret_cast<v4u*>(kc + (size_t)pos * RB + col * 16) = ek;
-            *reinterpret_cast<v4u*>(vc + (size_t)pos * RB + col * 16) = ev;
-          }
-        }
-      }
+    if (pb != p0) {
+      issue_tiles(pb, npos);
+      own_rows(pb, npos);
     }
     wait_vm_all();
     __syncthreads();
@@ -462,6 +470,7 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
         }
       }
     }
+    store_own_rows(pb, npos);
     __syncthreads();  // tiles are refilled by the next block
   }
   // reduce over lanes and write this wave's partial sums
@@ -487,6 +496,90 @@ __device__ void phase_attn(const LayerArgs& L, const StepArgs& S, const AttnPlan
   for (int item = vb; item < n_items; item += nvb) {
     attn_item<KDT, D, MP>(L, S, P, item, lds);
     __syncthreads();
+  }
+}
+
+// ------------------------------------------- combine by the last item
+// Variant of the attention items for the per-phase kernel: each item writes
+// its partial sums with agent-coherent stores (Coh) and waits for them to
+// complete before counting itself in on its group's counter; the last of a
+// group's items to arrive reads the group's partials back with agent-coherent
+// loads, sums them in chunk order and writes attn_o.  This takes the separate
+// combine launch off the path where a group holds few rows (the vector items).
+struct CohSt {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { Coh::st(p, v); }
+};
+
+// Bytes of LDS combine_if_last uses at the start of the item area.
+template <int D> struct CombineLds {
+  static constexpr int RED = kRowGroup * (D + 1) * 4 + 16;
+  static constexpr int BYTES = RED + 16;
+};
+
+// ctr: one zero-initialised word per (request, kv head, row group), left at
+// zero again by the group's last item.
+template <int D>
+__device__ void combine_if_last(const LayerArgs& L, const StepArgs& S, const AttnPlan* P,
+                                int item, unsigned* ctr, uint8_t* lds) {
+  float* red = reinterpret_cast<float*>(lds);
+  int* flag = reinterpret_cast<int*>(lds + CombineLds<D>::RED);
+  wait_vm_all();  // this thread's partial stores have completed ...
+  __syncthreads();  // ... and every other thread's
+  int b = 0;
+  while (b + 1 < S.n_req && P->item0[b + 1] <= item) ++b;
+  const int nch = P->nch[b];
+  const int gi = (item - P->item0[b]) / nch;  // j * nrg + rg
+  const int grp = b * L.Hkv * L.nrg + gi;
+  if (threadIdx.x == 0) {
+    const unsigned seen = __hip_atomic_fetch_add(&ctr[grp], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    const int last = seen + 1 == (unsigned)nch;
+    if (last) __hip_atomic_store(&ctr[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  if (!*flag) return;
+  const int j = gi / L.nrg, rg = gi - (gi / L.nrg) * L.nrg;
+  const int G = L.Hq / L.Hkv, M = G * S.Tr;
+  const int rows = L.rg_rows, m0 = rg * rows;
+  const int live = M - m0 < rows ? M - m0 : rows;
+  const int nf4 = (live * (D + 1) + 3) / 4;
+  const int stride = rows * (D + 1) * 4;  // bytes from one item's partials to the next
+  const float* base = S.part + (size_t)(P->item0[b] + gi * nch) * rows * (D + 1);
+  // raw buffer over the group's partials: loads past the last chunk return 0;
+  // cache policy sc1, the agent-coherent policy of Coh's loads
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(base), 0, nch * stride, 0x00020000);
+  constexpr int CB = 40;  // chunks in flight per thread
+  for (int f = threadIdx.x; f < nf4; f += blockDim.x) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < nch; c0 += CB) {
+      v4f t[CB];
+#pragma unroll
+      for (int q = 0; q < CB; ++q)
+        t[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, (c0 + q) * stride + f * 16, 0, 16);
+#pragma unroll
+      for (int q = 0; q < CB; ++q) acc += t[q];
+    }
+    *reinterpret_cast<v4f*>(red + 4 * f) = acc;
+  }
+  __syncthreads();
+  for (int v = threadIdx.x; v < live * D; v += blockDim.x) {
+    const int mm = v / D, d = v - (v / D) * D;
+    const int m = m0 + mm, t = m / G, g = m - (m / G) * G;
+    S.attn_o[((size_t)(b * S.Tr + t) * L.Hq + j * G + g) * D + d] =
+        red[mm * (D + 1) + d] / red[mm * (D + 1) + D];
+  }
+}
+
+// Cache windows of the step's tokens, [T][2] (lo, hi).
+__device__ inline void write_windows(const LayerArgs& L, const StepArgs& S, int* win_out) {
+  for (int tok = threadIdx.x; tok < S.T; tok += blockDim.x) {
+    const int b = tok / S.Tr, t = tok - (tok / S.Tr) * S.Tr;
+    const int p = S.kv_len[b] + t;
+    win_out[2 * tok] = L.window > 0 ? (p - L.window + 1 > 0 ? p - L.window + 1 : 0) : 0;
+    win_out[2 * tok + 1] = p;
   }
 }
 
@@ -565,14 +658,7 @@ __device__ void phase_combine(const LayerArgs& L, const StepArgs& S, const AttnP
     }
     __syncthreads();  // red is reused by the next row
   }
-  if (win_out != nullptr && vb == 0) {
-    for (int tok = threadIdx.x; tok < S.T; tok += blockDim.x) {
-      const int b = tok / S.Tr, t = tok - (tok / S.Tr) * S.Tr;
-      const int p = S.kv_len[b] + t;
-      win_out[2 * tok] = L.window > 0 ? (p - L.window + 1 > 0 ? p - L.window + 1 : 0) : 0;
-      win_out[2 * tok + 1] = p;
-    }
-  }
+  if (win_out != nullptr && vb == 0) write_windows(L, S, win_out);
 }
 
 // ------------------------------------------------------------- Wo
