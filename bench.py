@@ -172,7 +172,7 @@ def cpu_baseline(p, budget_s=30.0):
                        f"made before the timer starts)")
 
 
-def unfused_step(p, x, ws):
+def per_op_step(p, x, ws):
     """The same step as separate per-op calls (attention, router, experts)
     per layer: one launch sequence per phase group, no persistent kernel."""
     H = p.specs[0]["hidden"]
@@ -377,8 +377,8 @@ def measure(name, args, with_cpu):
         n_wg = 4 * torch.cuda.get_device_properties(0).multi_processor_count
         stamps = torch.zeros((n_wg, 32), dtype=torch.int64, device=dev)
     step = msk.Step(p.specs, p.weights, p.kv, p.kv_len, p.tokens_per_req, x, ws, stamps=stamps)
-    if args.path == "unfused":
-        step = unfused_step(p, x, ws)
+    if args.path == "per_op":
+        step = per_op_step(p, x, ws)
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -456,7 +456,7 @@ def measure(name, args, with_cpu):
                          "gbs": round(r["bytes"] / (r["ms"] * 1e-3) / 1e9, 1)
                          if ph != "step" else None}
                     for ph, r in timed.items()},
-        "path": {"fused": "layer_step", "unfused": "per_op_calls",
+        "path": {"layer_step": "layer_step", "per_op": "per_op_calls",
                  "persistent": "persistent_kernel"}[args.path],
     }
     if with_cpu:
@@ -475,10 +475,12 @@ def main():
                     help="one workload name, or 'all': every workload, each on a line of its "
                          f"own, the largest ({HEADLINE}) last")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=["fused", "unfused", "persistent"], default="fused",
-                    help="fused: msk_layer_step; unfused: the msk_attn_step -> msk_moe_route "
-                         "-> msk_expert_ffn calls per layer; persistent: "
-                         "msk_layer_step_timeline, the persistent step kernel where one exists")
+    ap.add_argument("--path", choices=["layer_step", "per_op", "persistent"],
+                    default="layer_step",
+                    help="layer_step: msk_layer_step (per-phase kernels); per_op: the "
+                         "msk_attn_step -> msk_moe_route -> msk_expert_ffn calls per layer; "
+                         "persistent: msk_layer_step_timeline, the persistent step kernel "
+                         "where one exists")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()

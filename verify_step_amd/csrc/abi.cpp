@@ -73,10 +73,7 @@ AttnSplit plan_attention(const msk_layer_cfg& c, const msk_batch& b) {
   long long total = 0;
   for (int r = 0; r < b.n_req; ++r) {
     int base, end;
-    const int L = b.kv_len_host[r], W = c.window;
-    const int lo = W > 0 ? (L - W + 1 > 0 ? L - W + 1 : 0) : 0;
-    base = lo & ~63;
-    end = L + b.tokens_per_req;
+    msk::req_span(b.kv_len_host[r], b.tokens_per_req, c.window, mfma, base, end);
     total += (long long)(end - base) * c.n_kv_heads * nrg;
   }
   // matrix-core items: at most kAttnRounds rounds of the 768 workgroups
@@ -90,9 +87,8 @@ AttnSplit plan_attention(const msk_layer_cfg& c, const msk_batch& b) {
   auto count = [&](long long ch) {
     long long n = 0;
     for (int r = 0; r < b.n_req; ++r) {
-      const int L = b.kv_len_host[r], W = c.window;
-      const int lo = W > 0 ? (L - W + 1 > 0 ? L - W + 1 : 0) : 0;
-      const int base = lo & ~63, end = L + b.tokens_per_req;
+      int base, end;
+      msk::req_span(b.kv_len_host[r], b.tokens_per_req, c.window, mfma, base, end);
       n += (long long)cdiv(end - base, ch) * c.n_kv_heads * nrg;
     }
     return n;

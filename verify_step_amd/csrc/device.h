@@ -40,6 +40,7 @@ __device__ __forceinline__ int dpp_i(int v) {
 }
 constexpr int kDppXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRor2 = 0x122;   // row_ror:2
 constexpr int kDppRor4 = 0x124;   // row_ror:4
 constexpr int kDppRor8 = 0x128;   // row_ror:8
 constexpr int kDppMirror = 0x140;      // row_mirror: lane j of a row <- 15 - j
@@ -142,10 +143,11 @@ __device__ __forceinline__ float reduce_scatter(const float (&a)[P]) {
   return v;
 }
 
-// Sum of v over the lanes congruent to this one modulo LPP (LPP = 4, 8, 16
-// or 32): the lanes that hold the same slice for different positions.
+// Sum of v over the lanes congruent to this one modulo LPP (LPP = 2, 4, 8,
+// 16 or 32): the lanes that hold the same slice for different positions.
 template <int LPP>
 __device__ __forceinline__ float sum_groups(float v) {
+  if constexpr (LPP <= 2) v += dpp_f<kDppRor2>(v);
   if constexpr (LPP <= 4) v += dpp_f<kDppRor4>(v);
   if constexpr (LPP <= 8) v += dpp_f<kDppRor8>(v);
   if constexpr (LPP <= 16) v = add_xor16(v);
@@ -154,6 +156,18 @@ __device__ __forceinline__ float sum_groups(float v) {
 }
 
 
+
+// Sum of v over the aligned group of N consecutive lanes holding this one
+// (N = 1, 2, 4, 8, 16 or 32); every lane of the group gets the sum.
+template <int N>
+__device__ __forceinline__ float sum_within(float v) {
+  if constexpr (N >= 2) v += dpp_f<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp_f<kDppXor2>(v);
+  if constexpr (N >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_f<kDppMirror>(v);
+  if constexpr (N >= 32) v = add_xor16(v);
+  return v;
+}
 
 // Orders LDS traffic of one wave: its earlier LDS writes are complete before
 // its later LDS reads (used for wave-private tiles, no workgroup barrier).

@@ -972,7 +972,7 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
   int most = 0;
   for (int b = 0; b < S.n_req; ++b) {
     int base, end;
-    req_span(S.kv_len[b], S.Tr, L.window, base, end);
+    req_span(S.kv_len[b], S.Tr, L.window, L.attn_nw != 0, base, end);
     const int n = ceil_div(end - base, L.chunk);
     most = n > most ? n : most;
   }

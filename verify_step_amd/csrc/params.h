@@ -52,6 +52,17 @@ struct LayerArgs {
   int attn_nph; // matrix-core attention: waves sharing each 16-row tile (1, 2)
 };
 
+// Cache range one request's tokens read in one layer: from the window start of
+// its first draft token (rounded down to 64 positions for the matrix-core
+// items, align64) to one past its last draft token's own position.  The
+// vector items start at the window itself, so that a window of 64 k
+// positions is k items per kv head, not k + 1.
+__host__ __device__ inline void req_span(int L, int Tr, int W, bool align64, int& base, int& end) {
+  const int lo = W > 0 ? (L - W + 1 > 0 ? L - W + 1 : 0) : 0;
+  base = align64 ? lo & ~63 : lo;
+  end = L + Tr;
+}
+
 // Default bound, in polls, of every device-side wait: past it a wait gives up
 // and sets the workspace's error flag instead of hanging the GPU.
 constexpr unsigned kSpinLimit = 1u << 22;

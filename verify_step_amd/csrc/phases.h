@@ -30,14 +30,6 @@ template <int NV> struct DenseRows { static constexpr int R = NV >= 16 ? 2 : 4; 
 
 __host__ __device__ inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Cache range one request's tokens read in one layer: from the window start of
-// its first draft token (rounded down to 64 positions) to one past its last
-// draft token's own position.
-__host__ __device__ inline void req_span(int L, int Tr, int W, int& base, int& end) {
-  const int lo = W > 0 ? (L - W + 1 > 0 ? L - W + 1 : 0) : 0;
-  base = lo & ~63;
-  end = L + Tr;
-}
 
 // Attention work split of one layer, kept in LDS by every workgroup.
 struct AttnPlan {
@@ -54,7 +46,7 @@ __device__ inline void build_plan(const LayerArgs& L, const StepArgs& S, AttnPla
     const int b = threadIdx.x;
     int base = 0, end = 0, n = 0;
     if (b < S.n_req) {
-      req_span(S.kv_len[b], S.Tr, L.window, base, end);
+      req_span(S.kv_len[b], S.Tr, L.window, L.attn_nw != 0, base, end);
       n = ceil_div(end - base, L.chunk);
     }
     const int cnt = n * L.Hkv * L.nrg;
@@ -161,19 +153,21 @@ __device__ void phase_qkv(const LayerArgs& L, const StepArgs& S, const float* x,
 //  - the K and V rows go straight from HBM into the workgroup's LDS tiles
 //    (direct global->LDS loads, shared by the four waves; no registers are
 //    held while they fly);
-//  - a lane then owns one cache position and computes its eight scores
-//    in-lane, reading its K row in a lane-rotated chunk order so the
-//    unpadded tile is read without bank conflicts;
+//  - a step of a wave covers whole rows: each lane takes one 16-byte chunk
+//    of K and of V at one position, forms its part of the two rows' scores
+//    against query values held in registers, and a sum over the position's
+//    lanes gives the scores;
 //  - e = exp(s - shift) inside the token's window, else 0 (no running max);
-//  - o += e * V with each lane owning a slice of head_dim for a few positions.
+//  - the lane adds e times its V chunk to its own accumulators, which are
+//    summed over the positions' lanes once, at the end of the item.
 // Positions at or past kv_len[b] are the step's own draft tokens: their K/V
 // are rebuilt from the QKV output (QK-norm on k, cast to the cache format),
 // and the row-group-0 item also writes them into the cache.
 // The item writes its plain partial sums (o[8][D], l[8]).
 template <int KDT> struct KV;
-template <> struct KV<kF32> { enum { ES = 4, EPLV = 4 }; };
-template <> struct KV<kBF16> { enum { ES = 2, EPLV = 8 }; };
-template <> struct KV<kE4M3> { enum { ES = 1, EPLV = 8 }; };
+template <> struct KV<kF32> { enum { ES = 4 }; };
+template <> struct KV<kBF16> { enum { ES = 2 }; };
+template <> struct KV<kE4M3> { enum { ES = 1 }; };
 
 template <int KDT, int D>
 struct AttnGeom {
@@ -183,18 +177,12 @@ struct AttnGeom {
   static constexpr int EPC = 16 / ES;         // elements per 16-B chunk
   static constexpr int TILE = 64 * RB;        // one 64-position tile
   static constexpr int NLD = TILE / 1024;     // 1-KB wave loads per tile
-  static constexpr int EPLV = KV<KDT>::EPLV;  // V elements per lane
-  static constexpr int VB = EPLV * ES;        // V bytes per lane
-  static constexpr int LPP = D / EPLV;        // lanes per position (V)
-  static constexpr int PPI = 64 / LPP;        // positions per V step
-  static constexpr int NVL = 64 / PPI;        // V steps per block
-  // per-workgroup LDS: q rows, K tile, V tile, weights, windows
+  // per-workgroup LDS: q rows, K tile, V tile, windows
   static constexpr int LDS_Q = kRowGroup * D * 4;
   static constexpr int LDS_K = TILE;
   static constexpr int LDS_V = TILE;
-  static constexpr int LDS_E = kRowGroup * 64 * 4;
   static constexpr int LDS_WIN = kRowGroup * 8;
-  static constexpr int LDS_ITEM = LDS_Q + LDS_K + LDS_V + LDS_E + LDS_WIN;
+  static constexpr int LDS_ITEM = LDS_Q + LDS_K + LDS_V + LDS_WIN;
   static constexpr int RPW = kRowGroup / kWaves;  // query rows per wave
 };
 
@@ -232,22 +220,6 @@ __device__ __forceinline__ void decode16(const v4u& w, float* f) {
   }
 }
 
-// Decode the first EPLV elements of a V slice (16 B, or 8 B for e4m3).
-template <int KDT>
-__device__ __forceinline__ void decode_v(const uint8_t* p, float* f) {
-  if constexpr (KDT == kF32) {
-    v4f a = *reinterpret_cast<const v4f*>(p);
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-  } else if constexpr (KDT == kBF16) {
-    v4u w = *reinterpret_cast<const v4u*>(p);
-    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
-    f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
-  } else {
-    v2u w = *reinterpret_cast<const v2u*>(p);
-    e4m3x4(w.x, f); e4m3x4(w.y, f + 4);
-  }
-}
-
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0); }
 
 template <int KDT, int D, class MP = Plain>
@@ -255,12 +227,10 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
                           uint8_t* wl) {
   using Gm = AttnGeom<KDT, D>;
   constexpr int RB = Gm::RB, CPR = Gm::CPR, EPC = Gm::EPC, NLD = Gm::NLD, RPW = Gm::RPW;
-  constexpr int EPLV = Gm::EPLV, VB = Gm::VB, LPP = Gm::LPP, PPI = Gm::PPI, NVL = Gm::NVL;
   float* qs = reinterpret_cast<float*>(wl);
   uint8_t* kt = wl + Gm::LDS_Q;
   uint8_t* vt = kt + Gm::LDS_K;
-  float* et = reinterpret_cast<float*>(vt + Gm::LDS_V);
-  int* win = reinterpret_cast<int*>(et + kRowGroup * 64);
+  int* win = reinterpret_cast<int*>(vt + Gm::LDS_V);
 
   const int ln = lane_id(), wv = wave_id();
   int b = 0;
@@ -399,15 +369,33 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
   lds_barrier();
   const float shift = layer_shift(L.shift, gq2, gk2, D);
 
+  // Lane (g, c) = (ln / CPR, ln % CPR) takes 16-byte chunk c of position
+  // PG i + g of the block at step i: a step's loads cover PG whole rows.  A
+  // score is summed over the CPR lanes of its position, and the lane adds
+  // its weighted V chunk to its own accumulators, so weights never pass
+  // through LDS; the position groups are summed once at the end.  The
+  // query values of this wave's rows stay in registers.
+  constexpr int PG = 64 / CPR;
+  const int cq = ln % CPR, gq = ln / CPR;
+  const bool live = m0 + wv * RPW < M;  // a wave without live rows skips the products
+  float qr[RPW][EPC];
+  int wlo[RPW], whi[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int mm = wv * RPW + r;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) qr[r][e] = qs[mm * D + cq * EPC + e];
+    wlo[r] = win[2 * mm];
+    whi[r] = win[2 * mm + 1];
+  }
   float lsum[RPW];
-  float o[RPW][EPLV];
+  float o[RPW][EPC];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     lsum[r] = 0.f;
 #pragma unroll
-    for (int i = 0; i < EPLV; ++i) o[r][i] = 0.f;
+    for (int e = 0; e < EPC; ++e) o[r][e] = 0.f;
   }
-  const int pg = ln / LPP, dc = ln - (ln / LPP) * LPP;
 
   for (int pb = p0; pb < p1; pb += 64) {
     const int npos = p1 - pb < 64 ? p1 - pb : 64;
@@ -417,73 +405,50 @@ __device__ void attn_item(const LayerArgs& L, const StepArgs& S, const AttnPlan*
     }
     wait_vm_all();
     __syncthreads();
-    // scores of this wave's rows: lane = position, K row read in a
-    // lane-rotated chunk order
-    {
-      float s[RPW];
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) s[r] = 0.f;
-      const uint8_t* krow = kt + ln * RB;
-      const float* qw = qs + wv * RPW * D;
+    if (live) {
+      const int nit = (npos + PG - 1) / PG;  // steps holding positions of the block
 #pragma unroll 4
       for (int i = 0; i < CPR; ++i) {
-        const int cc = (i + ln) & (CPR - 1);
-        float kf[EPC];
-        decode16<KDT>(*reinterpret_cast<const v4u*>(krow + cc * 16), kf);
-        const int d0 = cc * EPC;
+        if (i >= nit) break;
+        const int pp = i * PG + gq;
+        const int pos = pb + pp;
+        float kf[EPC], vf[EPC];
+        decode16<KDT>(*reinterpret_cast<const v4u*>(kt + pp * RB + cq * 16), kf);
+        decode16<KDT>(*reinterpret_cast<const v4u*>(vt + pp * RB + cq * 16), vf);
+        // rows that were not fetched hold stale bytes: their V is zeroed so
+        // that a zero weight never meets a NaN
+        const bool loaded = pp < npos && pos >= lo_min;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) vf[e] = loaded ? vf[e] : 0.f;
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
+          float sc = 0.f;
 #pragma unroll
-          for (int e4 = 0; e4 < EPC; e4 += 4) {
-            v4f qa = *reinterpret_cast<const v4f*>(qw + r * D + d0 + e4);
-            s[r] = fmaf(qa.x, kf[e4], s[r]);
-            s[r] = fmaf(qa.y, kf[e4 + 1], s[r]);
-            s[r] = fmaf(qa.z, kf[e4 + 2], s[r]);
-            s[r] = fmaf(qa.w, kf[e4 + 3], s[r]);
-          }
-        }
-      }
-      const int pos = pb + ln;
+          for (int e = 0; e < EPC; ++e) sc = fmaf(qr[r][e], kf[e], sc);
+          sc = sum_within<CPR>(sc);
+          const bool ok = loaded && pos >= wlo[r] && pos <= whi[r];
+          const float w = ok ? __expf(sc - shift) : 0.f;
+          lsum[r] += w;
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const int mm = wv * RPW + r;
-        const bool ok = ln < npos && pos >= win[2 * mm] && pos <= win[2 * mm + 1];
-        const float e = ok ? __expf(s[r] - shift) : 0.f;
-        et[mm * 64 + ln] = e;
-        lsum[r] += e;
-      }
-    }
-    wave_lds_sync();
-    // o += e * V for this wave's rows, from the V tile
-#pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-      const int pp = pg + i * PPI;
-      const int pos = pb + pp;
-      if (pp < npos && pos >= lo_min) {
-        float vf[EPLV];
-        decode_v<KDT>(vt + pp * RB + dc * VB, vf);
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-          const float e = et[(wv * RPW + r) * 64 + pp];
-#pragma unroll
-          for (int k = 0; k < EPLV; ++k) o[r][k] = fmaf(e, vf[k], o[r][k]);
+          for (int e = 0; e < EPC; ++e) o[r][e] = fmaf(w, vf[e], o[r][e]);
         }
       }
     }
     store_own_rows(pb, npos);
     __syncthreads();  // tiles are refilled by the next block
   }
-  // reduce over lanes and write this wave's partial sums
+  // sum over the position groups and write this wave's partial sums
+  if (!live) return;
   float* part = S.part + (size_t)item * kRowGroup * (D + 1);
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const int mm = wv * RPW + r;
-    const float l = wave_sum(lsum[r]);
+    const float l = sum_groups<CPR>(lsum[r]);  // lanes of a position hold equal sums
 #pragma unroll
-    for (int k = 0; k < EPLV; ++k) o[r][k] = sum_groups<LPP>(o[r][k]);
-    if (pg == 0) {
+    for (int e = 0; e < EPC; ++e) o[r][e] = sum_groups<CPR>(o[r][e]);
+    if (gq == 0) {
 #pragma unroll
-      for (int k = 0; k < EPLV; ++k) MP::st(&part[mm * (D + 1) + dc * EPLV + k], o[r][k]);
+      for (int e = 0; e < EPC; ++e) MP::st(&part[mm * (D + 1) + cq * EPC + e], o[r][e]);
     }
     if (ln == 0) MP::st(&part[mm * (D + 1) + D], l);
   }
