@@ -965,8 +965,9 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
   // Vector items (a group holds at most kRowGroup rows) over a few chunks per
   // group: the last item of a group sums its partials.  Its tail (waiting
   // for the partial stores, the counter's round trip, then reading every
-  // chunk back) grows with the chunks: over 33 chunks of six rows it cost
-  // more than a combine launch.  Matrix-core items, whose groups hold up to
+  // chunk back) grows with the chunks: over 32 chunks of six rows (a
+  // 2048-position window at head_dim 128) it added 6.2 us to the attention
+  // kernel, against 4.2 us for a combine launch.  Matrix-core items, whose groups hold up to
   // 64 rows, and groups of more chunks leave the sums to a combine launch
   // spread over every (token, q head).
   int most = 0;
