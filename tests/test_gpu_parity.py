@@ -93,6 +93,13 @@ CASES = {
     # one token over a long e4m3 history: vector attention items of five tiles
     "decode-e4m3-long": ("decode-bf16", dict(dims=_SMALL, kv="e4m3", kv_len=[300000],
                                              windows=[0])),
+    # one token with a long sliding window whose first position (50000) is
+    # not on a 64-position boundary: vector items start at the window itself
+    # and each runs three blocks that start off the boundary (bf16 and e4m3)
+    "decode-bf16-longwin": ("decode-bf16", dict(dims=_SMALL, kv="bf16", kv_len=[200000],
+                                                windows=[150001])),
+    "decode-e4m3-longwin": ("decode-bf16", dict(dims=_SMALL, kv="e4m3", kv_len=[200000],
+                                                windows=[150001])),
 }
 
 
