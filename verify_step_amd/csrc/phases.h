@@ -516,7 +516,7 @@ __device__ void combine_if_last(const LayerArgs& L, const StepArgs& S, const Att
   // cache policy sc1, the agent-coherent policy of Coh's loads
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(base), 0, nch * stride, 0x00020000);
-  constexpr int CB = 40;  // chunks in flight per thread
+  constexpr int CB = 8;  // chunks in flight per thread (one round for the fused groups)
   for (int f = threadIdx.x; f < nf4; f += blockDim.x) {
     v4f acc = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < nch; c0 += CB) {
