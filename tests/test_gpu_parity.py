@@ -100,6 +100,15 @@ CASES = {
                                                 windows=[150001])),
     "decode-e4m3-longwin": ("decode-bf16", dict(dims=_SMALL, kv="e4m3", kv_len=[200000],
                                                 windows=[150001])),
+    # one token with a window of at most eight 64-position chunks: the last
+    # item of each group sums the partials (e4m3 at head_dim 128 and 64, bf16
+    # at head_dim 64)
+    "decode-e4m3-shortwin": ("decode-bf16", dict(dims=_SMALL, kv="e4m3", kv_len=[1000],
+                                                 windows=[200])),
+    "decode-e4m3-d64-shortwin": ("decode-bf16", dict(dims=dict(_SMALL, head_dim=64, n_q_heads=8),
+                                                     kv="e4m3", kv_len=[500], windows=[100])),
+    "decode-bf16-d64-shortwin": ("decode-bf16", dict(dims=dict(_SMALL, head_dim=64, n_q_heads=8),
+                                                     kv="bf16", kv_len=[300], windows=[130])),
 }
 
 
