@@ -310,7 +310,11 @@ size_t msk_moe_prefill_workspace_size(const msk_layer_cfg *cfg, int32_t n_tokens
 /* Kernel timing for measurement harnesses.  The step's kernels fall into
  * phases:
  *   MSK_PH_QKV      RMSNorm + QKV projection + QK-norm + KV append
- *   MSK_PH_ATTN     split-KV no-max attention partials
+ *   MSK_PH_ATTN     split-KV no-max attention partials (and their sums and
+ *                   the window bounds, with no combine launch, where the
+ *                   vector kernel runs, the output projection does not run
+ *                   on the matrix cores, and every group spans at most
+ *                   eight chunks)
  *   MSK_PH_COMBINE  sum of the partials, window bounds
  *   MSK_PH_WO       output projection + residual
  *   MSK_PH_ROUTER   FFN RMSNorm + router logits (one token; with several,

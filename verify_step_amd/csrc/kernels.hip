@@ -967,8 +967,10 @@ hipError_t launch_attn(const LayerArgs& L, const StepArgs& S, const float* x, fl
   // for the partial stores, the counter's round trip, then reading every
   // chunk back) grows with the chunks: over 32 chunks of six rows (a
   // 2048-position window at head_dim 128) it added 6.2 us to the attention
-  // kernel, against 4.2 us for a combine launch.  Matrix-core items, whose groups hold up to
-  // 64 rows, and groups of more chunks leave the sums to a combine launch
+  // kernel, against 4.2 us for a combine launch.  Matrix-core items, whose
+  // groups hold up to 64 rows, groups of more chunks, and steps whose output
+  // projection runs on the matrix cores (it reads attn_o as bf16 terms,
+  // which the combine launch writes) leave the sums to a combine launch
   // spread over every (token, q head).
   int most = 0;
   for (int b = 0; b < S.n_req; ++b) {
